@@ -1,0 +1,201 @@
+"""CPU oracle for MLA decode — TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  It wraps liboracle.so (oracle.c: plain float64 C) with
+numpy marshalling and shares nothing with the GPU library.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .build import LIB, build
+
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
+_DT = {"f32": F32, "bf16": BF16, "fp8": E4M3, "e4m3": E4M3, "f64": F64}
+_NP = {F32: np.float32, BF16: np.uint16, E4M3: np.uint8, F64: np.float64}
+
+_lib = None
+
+
+class _Problem(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("H", C.c_int32), ("d_nope", C.c_int32), ("d_rope", C.c_int32),
+        ("d_latent", C.c_int32), ("d_v", C.c_int32), ("scale", C.c_double),
+        ("q_nope", C.c_void_p), ("q_rope", C.c_void_p), ("q_dtype", C.c_int32),
+        ("w_uk", C.c_void_p), ("w_uv", C.c_void_p), ("w_dtype", C.c_int32),
+        ("rows", C.c_void_p), ("row_scale", C.c_void_p), ("cache_dtype", C.c_int32),
+        ("page_size", C.c_int32), ("seq_stride", C.c_int64), ("block_table", C.c_void_p),
+        ("max_pages", C.c_int32), ("seq_lens", C.c_void_p),
+    ]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = C.CDLL(LIB)
+        L.oracle_mla_decode.restype = C.c_int
+        L.oracle_mla_decode.argtypes = [C.POINTER(_Problem), C.c_void_p, C.c_void_p, C.c_int32,
+                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_void_p]
+        L.oracle_absorb_q.restype = C.c_int
+        L.oracle_absorb_q.argtypes = [C.c_int32] * 5 + [C.c_void_p, C.c_void_p, C.c_int32,
+                                                        C.c_void_p, C.c_int32, C.c_void_p]
+        L.oracle_combine.restype = C.c_int
+        L.oracle_combine.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 4
+        L.oracle_up_proj.restype = C.c_int
+        L.oracle_up_proj.argtypes = [C.c_int32] * 4 + [C.c_void_p, C.c_void_p, C.c_int32,
+                                                       C.c_void_p]
+        L.oracle_decode_bf16.restype = C.c_double
+        L.oracle_decode_bf16.argtypes = [C.c_uint16]
+        L.oracle_decode_e4m3.restype = C.c_double
+        L.oracle_decode_e4m3.argtypes = [C.c_uint8]
+        L.oracle_decode_array.restype = None
+        L.oracle_decode_array.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_void_p]
+        L.oracle_mla_cache_bytes_per_token.restype = C.c_int64
+        L.oracle_mla_cache_bytes_per_token.argtypes = [C.c_int32] * 4
+        L.oracle_mha_cache_bytes.restype = C.c_int64
+        L.oracle_mha_cache_bytes.argtypes = [C.c_int64] * 5
+        L.oracle_num_threads.restype = C.c_int
+        L.oracle_num_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _dt(x) -> int:
+    return _DT[x] if isinstance(x, str) else int(x)
+
+
+def _arr(a, dtype_code) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=_NP[dtype_code])
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def decode(q_nope, q_rope, q_dtype, w_uk, w_uv, w_dtype, rows, cache_dtype, seq_lens, *,
+           row_scale=None, page_size: int = 0, seq_stride: Optional[int] = None,
+           block_table=None, scale: Optional[float] = None,
+           sel: Optional[Sequence[tuple]] = None, t_begin=None, t_end=None,
+           want_u: bool = False):
+    """Naive MLA decode.  Arrays hold stored bits (float32 / uint16 bf16 /
+    uint8 e4m3 / float64).  Returns (o [n, d_v], lse [n], u [n, d_latent] or
+    None) as float64, for the selected (b, h) pairs or all B*H in order."""
+    qd, wd, cd = _dt(q_dtype), _dt(w_dtype), _dt(cache_dtype)
+    q_nope = _arr(q_nope, qd)
+    q_rope = _arr(q_rope, qd)
+    w_uk = _arr(w_uk, wd)
+    w_uv = _arr(w_uv, wd)
+    rows = _arr(rows, cd)
+    B, H, dn = q_nope.shape
+    dr = q_rope.shape[2]
+    dl = w_uk.shape[2]
+    dv = w_uv.shape[1]
+    assert rows.shape[-1] == dl + dr
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    rs = None if row_scale is None else np.ascontiguousarray(row_scale, dtype=np.float32)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    if seq_stride is None:
+        seq_stride = int(seq_lens.max()) if B else 0
+    P = _Problem(B, H, dn, dr, dl, dv, float(scale) if scale else 0.0,
+                 _ptr(q_nope), _ptr(q_rope), qd, _ptr(w_uk), _ptr(w_uv), wd,
+                 _ptr(rows), _ptr(rs), cd, int(page_size), int(seq_stride), _ptr(bt),
+                 0 if bt is None else int(bt.shape[1]), _ptr(seq_lens))
+    if sel is None:
+        n = B * H
+        sb = sh = None
+    else:
+        sel = list(sel)
+        n = len(sel)
+        sb = np.ascontiguousarray([s[0] for s in sel], dtype=np.int32)
+        sh = np.ascontiguousarray([s[1] for s in sel], dtype=np.int32)
+    tb = None if t_begin is None else np.ascontiguousarray(t_begin, dtype=np.int32)
+    te = None if t_end is None else np.ascontiguousarray(t_end, dtype=np.int32)
+    o = np.zeros((n, dv), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    u = np.zeros((n, dl), dtype=np.float64) if want_u else None
+    rc = lib().oracle_mla_decode(C.byref(P), _ptr(sb), _ptr(sh), n, _ptr(tb), _ptr(te),
+                                 _ptr(o), _ptr(lse), _ptr(u))
+    if rc != 0:
+        raise ValueError(f"oracle_mla_decode failed: {rc}")
+    return o, lse, u
+
+
+def decode_inputs(inp, sel=None, want_u=False, t_begin=None, t_end=None, scale=None):
+    """decode() on a synth.MLAInputs-like object (duck-typed)."""
+    wl = inp.wl
+    return decode(inp.q_nope, inp.q_rope, wl.act_dtype, inp.w_uk, inp.w_uv, wl.act_dtype,
+                  inp.rows, wl.cache_dtype, inp.seq_lens, row_scale=inp.row_scale,
+                  page_size=wl.page_size, seq_stride=inp.seq_stride,
+                  block_table=inp.block_table, scale=scale, sel=sel, t_begin=t_begin,
+                  t_end=t_end, want_u=want_u)
+
+
+def absorb_q(q_nope, q_rope, q_dtype, w_uk, w_dtype):
+    """q_abs [B, H, d_latent + d_rope] float64."""
+    qd, wd = _dt(q_dtype), _dt(w_dtype)
+    q_nope, q_rope, w_uk = _arr(q_nope, qd), _arr(q_rope, qd), _arr(w_uk, wd)
+    B, H, dn = q_nope.shape
+    dr, dl = q_rope.shape[2], w_uk.shape[2]
+    out = np.zeros((B, H, dl + dr), dtype=np.float64)
+    rc = lib().oracle_absorb_q(B, H, dn, dr, dl, _ptr(q_nope), _ptr(q_rope), qd, _ptr(w_uk),
+                               wd, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_absorb_q failed: {rc}")
+    return out
+
+
+def combine(u_part, lse_part):
+    """u_part [B, S, H, D], lse_part [B, S, H] (float64) -> (u [B, H, D], lse [B, H])."""
+    u_part = np.ascontiguousarray(u_part, dtype=np.float64)
+    lse_part = np.ascontiguousarray(lse_part, dtype=np.float64)
+    B, S, H, D = u_part.shape
+    u = np.zeros((B, H, D), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    rc = lib().oracle_combine(B, S, H, D, _ptr(u_part), _ptr(lse_part), _ptr(u), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_combine failed: {rc}")
+    return u, lse
+
+
+def up_proj(u, w_uv, w_dtype):
+    """u [B, H, d_latent] float64, W_UV [H, d_v, d_latent] -> o [B, H, d_v]."""
+    wd = _dt(w_dtype)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    w_uv = _arr(w_uv, wd)
+    B, H, dl = u.shape
+    dv = w_uv.shape[1]
+    o = np.zeros((B, H, dv), dtype=np.float64)
+    rc = lib().oracle_up_proj(B, H, dv, dl, _ptr(u), _ptr(w_uv), wd, _ptr(o))
+    if rc != 0:
+        raise ValueError(f"oracle_up_proj failed: {rc}")
+    return o
+
+
+def decode_array(a, dtype) -> np.ndarray:
+    """Decode stored bits to float64 with the oracle's own decoder."""
+    d = _dt(dtype)
+    a = _arr(a, d)
+    out = np.empty(a.shape, dtype=np.float64)
+    lib().oracle_decode_array(_ptr(a), d, a.size, _ptr(out))
+    return out
+
+
+def mla_cache_bytes_per_token(d_latent, d_rope, elem_bytes, scale_bytes=0) -> int:
+    return int(lib().oracle_mla_cache_bytes_per_token(d_latent, d_rope, elem_bytes,
+                                                      scale_bytes))
+
+
+def mha_cache_bytes(layers, seq_len, heads, head_dim, elem_bytes) -> int:
+    return int(lib().oracle_mha_cache_bytes(layers, seq_len, heads, head_dim, elem_bytes))
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())

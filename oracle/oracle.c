@@ -1,0 +1,322 @@
+/*
+ * CPU oracle for MLA decode — TEST INFRASTRUCTURE ONLY.
+ *
+ * Callers: the tests, the smoke check and the benchmark's CPU-baseline leg.
+ * Nothing on the product path may load it.  It shares no code, header, table
+ * or helper with the GPU library.
+ *
+ * What it computes is the plain, non-absorbed MLA decode, in float64:
+ * for every cached token the full key and value of each head are rebuilt from
+ * the token's latent, then textbook softmax attention runs over them.  The
+ * pages:
+ *   [V2]  "DeepSeek V2的MLA注意力机制：如何用低秩压缩技术降低KV Cache显存消耗？"
+ *         (snabindia.com) — §2.1 low-rank reconstruction K = W_U^K·KV_comp,
+ *         V = W_U^V·KV_comp; §2.2 decoupled RoPE: a content query q_C, a
+ *         positional query q_R and ONE positional key k_R shared by all heads;
+ *         §2.3 only KV_comp and k_R are cached, the score is the product of the
+ *         concatenations (q_C q_R)(K_C K_R)^T over sqrt(d), and absorbing W_U^K
+ *         into the query / W_U^V into the output is exact algebra;
+ *         §1.1 MHA cache size 2 x layers x seq x h x d (x bytes).
+ *   [LAT] "Multi-Head Latent Attention（MLA）：大模型KV Cache显存优化原理与实操"
+ *         (CSDN mirror) — §2.1 Attention(Q,K,V) = softmax(QK^T/sqrt(d_k)) V and
+ *         the MHA cache bytes per token; §3.2 the latent cache is a 2-D
+ *         [seq, latent] array per sequence, read by slicing.
+ *   [DSA] "engineering DeepSeek sparse attention long context inference"
+ *         (blog.hotdry.top) — the MLA module listing: cache the latent, rebuild
+ *         k and v with the up-projections, then attention.
+ * Readings taken where the pages are silent (the softmax scale is
+ * 1/sqrt(d_nope + d_rope); W_UK is [h][d_nope][d_latent] and W_UV is
+ * [h][d_v][d_latent], the nn.Linear layout of the [DSA] listing; one 576-wide
+ * row per token holds [c_KV | k_R]; e4m3 rows carry one fp32 factor; every
+ * cached token is attended, no mask) are listed with the tests that pin them.
+ *
+ * Pins (tests/test_oracle_*.py): library SDPA over explicitly rebuilt K/V,
+ * the absorbed-form identity, closed forms (one token, zero query, dominant
+ * key), invariants (score shift, token and head permutation, split+merge,
+ * paged vs contiguous, unread NaN slots, linearity in W_UV), exhaustive codec
+ * tables against torch's bfloat16 / float8_e4m3fn, and the pages' printed
+ * cache sizes.  No function here is "parity unpinned".
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- decoders */
+
+double oracle_decode_bf16(uint16_t bits) {
+  /* bfloat16 is the upper half of an IEEE-754 binary32 */
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+double oracle_decode_e4m3(uint8_t code) {
+  /* OCP 8-bit floating point spec, E4M3: 1 sign, 4 exponent (bias 7),
+   * 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN;
+   * there are no infinities. */
+  int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, 1 - 7);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+static double load_elem(const void* base, int32_t dtype, int64_t i) {
+  switch (dtype) {
+    case ORACLE_F32: return (double)((const float*)base)[i];
+    case ORACLE_BF16: return oracle_decode_bf16(((const uint16_t*)base)[i]);
+    case ORACLE_E4M3: return oracle_decode_e4m3(((const uint8_t*)base)[i]);
+    case ORACLE_F64: return ((const double*)base)[i];
+    default: return NAN;
+  }
+}
+
+void oracle_decode_array(const void* src, int32_t dtype, int64_t n, double* dst) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, dtype, i);
+}
+
+static int valid_dtype(int32_t d) { return d >= ORACLE_F32 && d <= ORACLE_F64; }
+
+/* --------------------------------------------------------- cache addressing */
+
+/* physical row of token t of sequence b: contiguous [b][seq_stride] rows, or a
+ * page of page_size rows named by the block table ([V2] §1.2/§3.3 paging) */
+static int64_t row_of(const oracle_mla_problem* P, int32_t b, int64_t t) {
+  if (P->page_size > 0) {
+    int64_t page = P->block_table[(int64_t)b * P->max_pages + t / P->page_size];
+    return page * P->page_size + t % P->page_size;
+  }
+  return (int64_t)b * P->seq_stride + t;
+}
+
+/* decode one cached row [c_KV | k_R] to float64; e4m3 rows are multiplied by
+ * their per-row factor */
+static void load_row(const oracle_mla_problem* P, int64_t r, double* c) {
+  const int32_t w = P->d_latent + P->d_rope;
+  double f = 1.0;
+  if (P->cache_dtype == ORACLE_E4M3) f = (double)P->row_scale[r];
+  for (int32_t j = 0; j < w; ++j) c[j] = load_elem(P->rows, P->cache_dtype, r * w + j) * f;
+}
+
+/* ----------------------------------------------------------- naive decode */
+
+int oracle_mla_decode(const oracle_mla_problem* P, const int32_t* sel_b,
+                      const int32_t* sel_h, int32_t n_sel, const int32_t* t_begin,
+                      const int32_t* t_end, double* o, double* lse, double* u) {
+  if (!P || !o || !lse) return -1;
+  if (P->B < 0 || P->H <= 0 || P->d_nope <= 0 || P->d_rope < 0 || P->d_latent <= 0 ||
+      P->d_v <= 0)
+    return -2;
+  if (!valid_dtype(P->q_dtype) || !valid_dtype(P->w_dtype) || !valid_dtype(P->cache_dtype))
+    return -3;
+  if (P->cache_dtype == ORACLE_E4M3 && !P->row_scale) return -4;
+  if (P->page_size > 0 && !P->block_table) return -5;
+  const int32_t all = (sel_b == NULL);
+  const int64_t n = all ? (int64_t)P->B * P->H : n_sel;
+  const double scale =
+      P->scale > 0 ? P->scale : 1.0 / sqrt((double)(P->d_nope + P->d_rope));
+  const int32_t dn = P->d_nope, dr = P->d_rope, dl = P->d_latent, dv = P->d_v;
+  int err = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t idx = 0; idx < n; ++idx) {
+    const int32_t b = all ? (int32_t)(idx / P->H) : sel_b[idx];
+    const int32_t h = all ? (int32_t)(idx % P->H) : sel_h[idx];
+    if (b < 0 || b >= P->B || h < 0 || h >= P->H) {
+      err = -6;
+      continue;
+    }
+    int64_t L = P->seq_lens[b];
+    int64_t t0 = t_begin ? t_begin[b] : 0;
+    int64_t t1 = t_end ? t_end[b] : L;
+    if (t0 < 0) t0 = 0;
+    if (t1 > L) t1 = L;
+    double* out_o = o + idx * dv;
+    double* out_u = u ? u + idx * dl : NULL;
+    for (int32_t v = 0; v < dv; ++v) out_o[v] = 0.0;
+    if (out_u)
+      for (int32_t j = 0; j < dl; ++j) out_u[j] = 0.0;
+    if (t1 <= t0) {
+      lse[idx] = -INFINITY;
+      continue;
+    }
+    const int64_t nt = t1 - t0;
+    double* Wk = malloc(sizeof(double) * dn * dl);
+    double* Wv = malloc(sizeof(double) * dv * dl);
+    double* qc = malloc(sizeof(double) * dn);
+    double* qr = malloc(sizeof(double) * (dr > 0 ? dr : 1));
+    double* c = malloc(sizeof(double) * (dl + dr));
+    double* k = malloc(sizeof(double) * dn);
+    double* vv = malloc(sizeof(double) * dv);
+    double* s = malloc(sizeof(double) * nt);
+    for (int64_t i = 0; i < (int64_t)dn * dl; ++i)
+      Wk[i] = load_elem(P->w_uk, P->w_dtype, (int64_t)h * dn * dl + i);
+    for (int64_t i = 0; i < (int64_t)dv * dl; ++i)
+      Wv[i] = load_elem(P->w_uv, P->w_dtype, (int64_t)h * dv * dl + i);
+    for (int32_t i = 0; i < dn; ++i)
+      qc[i] = load_elem(P->q_nope, P->q_dtype, ((int64_t)b * P->H + h) * dn + i);
+    for (int32_t i = 0; i < dr; ++i)
+      qr[i] = load_elem(P->q_rope, P->q_dtype, ((int64_t)b * P->H + h) * dr + i);
+
+    /* pass 1: scores.  The key of head h for token t is the concatenation of
+     * the rebuilt content key W_UK[h]·c_t ([V2] §2.1) and the shared
+     * positional key k_R,t ([V2] §2.2); the query is [q_C ; q_R]; the score is
+     * their dot product times the softmax scale ([V2] §2.3, [LAT] §2.1). */
+    for (int64_t t = 0; t < nt; ++t) {
+      load_row(P, row_of(P, b, t0 + t), c);
+      for (int32_t i = 0; i < dn; ++i) {
+        double acc = 0.0;
+        const double* wr = Wk + (int64_t)i * dl;
+        for (int32_t j = 0; j < dl; ++j) acc += wr[j] * c[j];
+        k[i] = acc;
+      }
+      double dot = 0.0;
+      for (int32_t i = 0; i < dn; ++i) dot += qc[i] * k[i];
+      for (int32_t i = 0; i < dr; ++i) dot += qr[i] * c[dl + i];
+      s[t] = scale * dot;
+    }
+    /* softmax over the attended tokens ([LAT] §2.1) */
+    double m = -INFINITY;
+    for (int64_t t = 0; t < nt; ++t)
+      if (s[t] > m) m = s[t];
+    double l = 0.0;
+    for (int64_t t = 0; t < nt; ++t) {
+      s[t] = exp(s[t] - m);
+      l += s[t];
+    }
+    /* pass 2: weighted sum of the rebuilt values W_UV[h]·c_t ([V2] §2.1) */
+    for (int64_t t = 0; t < nt; ++t) {
+      load_row(P, row_of(P, b, t0 + t), c);
+      for (int32_t i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        const double* wr = Wv + (int64_t)i * dl;
+        for (int32_t j = 0; j < dl; ++j) acc += wr[j] * c[j];
+        vv[i] = acc;
+      }
+      for (int32_t i = 0; i < dv; ++i) out_o[i] += s[t] * vv[i];
+      if (out_u)
+        for (int32_t j = 0; j < dl; ++j) out_u[j] += s[t] * c[j];
+    }
+    for (int32_t i = 0; i < dv; ++i) out_o[i] /= l;
+    if (out_u)
+      for (int32_t j = 0; j < dl; ++j) out_u[j] /= l;
+    lse[idx] = m + log(l);
+    free(Wk); free(Wv); free(qc); free(qr); free(c); free(k); free(vv); free(s);
+  }
+  return err;
+}
+
+/* ------------------------------------------------------- the other calls */
+
+/* Absorbing W_UK into the query ([V2] §2.3, §4.1): the content score
+ * q_C·(W_UK c) equals (W_UK^T q_C)·c, so the absorbed query is
+ * sum_n q_C[n] W_UK[n][:]; the RoPE part is carried unchanged. */
+int oracle_absorb_q(int32_t B, int32_t H, int32_t d_nope, int32_t d_rope,
+                    int32_t d_latent, const void* q_nope, const void* q_rope,
+                    int32_t q_dtype, const void* w_uk, int32_t w_dtype,
+                    double* q_abs) {
+  if (B < 0 || H <= 0 || d_nope <= 0 || d_rope < 0 || d_latent <= 0 || !q_abs) return -1;
+  if (!valid_dtype(q_dtype) || !valid_dtype(w_dtype)) return -3;
+  const int32_t w = d_latent + d_rope;
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    const int64_t h = bh % H;
+    double* out = q_abs + bh * w;
+    for (int32_t j = 0; j < d_latent; ++j) out[j] = 0.0;
+    for (int32_t n = 0; n < d_nope; ++n) {
+      const double q = load_elem(q_nope, q_dtype, bh * d_nope + n);
+      for (int32_t j = 0; j < d_latent; ++j)
+        out[j] += q * load_elem(w_uk, w_dtype, (h * d_nope + n) * d_latent + j);
+    }
+    for (int32_t j = 0; j < d_rope; ++j)
+      out[d_latent + j] = load_elem(q_rope, q_dtype, bh * d_rope + j);
+  }
+  return 0;
+}
+
+/* Merging softmax results computed over disjoint token sets: each part p
+ * holds u_p = sum_{t in p} e^{s_t} x_t / Z_p with lse_p = log Z_p; the whole
+ * is Z = sum_p Z_p and u = sum_p (Z_p / Z) u_p.  Parts with lse_p = -inf
+ * attended nothing and carry no weight. */
+int oracle_combine(int32_t B, int32_t S, int32_t H, int32_t D,
+                   const double* u_part, const double* lse_part, double* u,
+                   double* lse) {
+  if (B < 0 || S <= 0 || H <= 0 || D <= 0 || !u_part || !lse_part || !u) return -1;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h) {
+      double m = -INFINITY;
+      for (int64_t p = 0; p < S; ++p) {
+        double x = lse_part[(b * S + p) * H + h];
+        if (x > m) m = x;
+      }
+      double* out = u + (b * H + h) * D;
+      for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
+      if (m == -INFINITY) {
+        if (lse) lse[b * H + h] = -INFINITY;
+        continue;
+      }
+      double z = 0.0;
+      for (int64_t p = 0; p < S; ++p) z += exp(lse_part[(b * S + p) * H + h] - m);
+      const double L = m + log(z);
+      for (int64_t p = 0; p < S; ++p) {
+        const double wgt = exp(lse_part[(b * S + p) * H + h] - L);
+        if (wgt == 0.0) continue;
+        const double* up = u_part + ((b * S + p) * H + h) * D;
+        for (int32_t d = 0; d < D; ++d) out[d] += wgt * up[d];
+      }
+      if (lse) lse[b * H + h] = L;
+    }
+  return 0;
+}
+
+/* Applying W_UV after the weighted sum ([V2] §2.3): the attention output of
+ * head h is W_UV[h] · (sum_t p_t c_t). */
+int oracle_up_proj(int32_t B, int32_t H, int32_t d_v, int32_t d_latent,
+                   const double* u, const void* w_uv, int32_t w_dtype, double* o) {
+  if (B < 0 || H <= 0 || d_v <= 0 || d_latent <= 0 || !u || !o) return -1;
+  if (!valid_dtype(w_dtype)) return -3;
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    const int64_t h = bh % H;
+    for (int32_t v = 0; v < d_v; ++v) {
+      double acc = 0.0;
+      for (int32_t c = 0; c < d_latent; ++c)
+        acc += load_elem(w_uv, w_dtype, (h * d_v + v) * d_latent + c) * u[bh * d_latent + c];
+      o[bh * d_v + v] = acc;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------ size arithmetic */
+
+/* [V2] §2.3: per token and layer only KV_comp (d_latent) and k_R (d_rope)
+ * are cached; an e4m3 row adds its scale factor. */
+int64_t oracle_mla_cache_bytes_per_token(int32_t d_latent, int32_t d_rope,
+                                         int32_t elem_bytes, int32_t scale_bytes) {
+  return (int64_t)(d_latent + d_rope) * elem_bytes + scale_bytes;
+}
+
+/* [V2] §1.1: MHA caches K and V of every head: 2 x layers x seq x h x d
+ * elements. */
+int64_t oracle_mha_cache_bytes(int64_t layers, int64_t seq_len, int64_t heads,
+                               int64_t head_dim, int64_t elem_bytes) {
+  return 2 * layers * seq_len * heads * head_dim * elem_bytes;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

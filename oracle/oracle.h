@@ -1,0 +1,91 @@
+/*
+ * CPU oracle for MLA decode — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It is a plain, slow, float64 implementation of what an
+ * MLA decode step computes, written from the pages' statement of the method,
+ * and it shares no code with the GPU library.
+ *
+ * Parity status of every function is listed in oracle.c's header.
+ */
+#ifndef MLA_ORACLE_H
+#define MLA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage formats understood by the oracle's element decoder */
+enum {
+  ORACLE_F32 = 0,  /* IEEE-754 binary32 */
+  ORACLE_BF16 = 1, /* upper 16 bits of binary32 */
+  ORACLE_E4M3 = 2, /* OCP FP8 E4M3 (bias 7, no Inf, S.1111.111 = NaN) */
+  ORACLE_F64 = 3   /* IEEE-754 binary64 */
+};
+
+typedef struct {
+  int32_t B, H, d_nope, d_rope, d_latent, d_v;
+  double scale; /* softmax scale; <= 0 selects 1/sqrt(d_nope + d_rope) */
+  const void* q_nope; /* [B][H][d_nope] */
+  const void* q_rope; /* [B][H][d_rope] */
+  int32_t q_dtype;
+  const void* w_uk; /* [H][d_nope][d_latent] */
+  const void* w_uv; /* [H][d_v][d_latent] */
+  int32_t w_dtype;
+  const void* rows; /* cache rows of d_latent + d_rope elements: [c_KV | k_R] */
+  const float* row_scale; /* E4M3 cache: one factor per row, else NULL */
+  int32_t cache_dtype;
+  int32_t page_size;          /* 0: row of token t of seq b = b*seq_stride + t */
+  int64_t seq_stride;
+  const int32_t* block_table; /* paged: row = block_table[b*max_pages + t/ps]*ps + t%ps */
+  int32_t max_pages;
+  const int32_t* seq_lens; /* [B] */
+} oracle_mla_problem;
+
+/* Naive decode: rebuild K and V per cached token, then textbook attention.
+ * sel_b/sel_h (n_sel pairs) choose the outputs; NULL computes all B*H in
+ * (b, h) order.  t_begin/t_end (per sequence, may be NULL) restrict the
+ * attended tokens to [t_begin[b], t_end[b]).  Outputs per selected pair:
+ * o [d_v], lse (natural log; -inf when no token is attended), and optionally
+ * u [d_latent] = softmax-weighted mean of the cached latents.  Returns 0, or
+ * a negative value on a bad argument. */
+int oracle_mla_decode(const oracle_mla_problem* P, const int32_t* sel_b,
+                      const int32_t* sel_h, int32_t n_sel, const int32_t* t_begin,
+                      const int32_t* t_end, double* o, double* lse, double* u);
+
+/* q_abs[b][h][:d_latent] = sum_n q_nope[b][h][n] * W_UK[h][n][:] ;
+ * q_abs[b][h][d_latent:] = q_rope[b][h][:]  (float64 out) */
+int oracle_absorb_q(int32_t B, int32_t H, int32_t d_nope, int32_t d_rope,
+                    int32_t d_latent, const void* q_nope, const void* q_rope,
+                    int32_t q_dtype, const void* w_uk, int32_t w_dtype,
+                    double* q_abs);
+
+/* Merge S partial softmax results: lse = log sum_p exp(lse_p),
+ * u = sum_p exp(lse_p - lse) u_p.  u_part [B][S][H][D], lse_part [B][S][H]. */
+int oracle_combine(int32_t B, int32_t S, int32_t H, int32_t D,
+                   const double* u_part, const double* lse_part, double* u,
+                   double* lse);
+
+/* o[b][h][v] = sum_c W_UV[h][v][c] * u[b][h][c] */
+int oracle_up_proj(int32_t B, int32_t H, int32_t d_v, int32_t d_latent,
+                   const double* u, const void* w_uv, int32_t w_dtype, double* o);
+
+/* element decoders (exact) */
+double oracle_decode_bf16(uint16_t bits);
+double oracle_decode_e4m3(uint8_t code);
+void oracle_decode_array(const void* src, int32_t dtype, int64_t n, double* dst);
+
+/* cache-size arithmetic */
+int64_t oracle_mla_cache_bytes_per_token(int32_t d_latent, int32_t d_rope,
+                                         int32_t elem_bytes, int32_t scale_bytes);
+int64_t oracle_mha_cache_bytes(int64_t layers, int64_t seq_len, int64_t heads,
+                               int64_t head_dim, int64_t elem_bytes);
+
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,89 @@
+"""Plants plausible mistakes in a copy of the oracle (on the CPU, in a temp
+dir) and checks that the pins of test_oracle_pins / test_oracle_codecs catch
+every one of them."""
+
+import ctypes
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from oracle.build import CFLAGS
+
+from . import test_oracle_codecs as codecs
+from . import test_oracle_pins as pins
+
+HERE = os.path.dirname(os.path.abspath(oracle.__file__))
+
+MUTANTS = {
+    "drop_rope_term": ("for (int32_t i = 0; i < dr; ++i) dot += qr[i] * c[dl + i];", ""),
+    "scale_over_latent_width": ("1.0 / sqrt((double)(P->d_nope + P->d_rope))",
+                                "1.0 / sqrt((double)(P->d_latent + P->d_rope))"),
+    "transposed_w_uk": ("const double* wr = Wk + (int64_t)i * dl;\n        for (int32_t j = 0; j < dl; ++j) acc += wr[j] * c[j];\n        k[i] = acc;",
+                        "for (int32_t j = 0; j < dl; ++j) acc += Wk[(int64_t)j * dn + i] * c[j];\n        k[i] = acc;"),
+    "missing_normalisation": ("for (int32_t i = 0; i < dv; ++i) out_o[i] /= l;", ""),
+    "values_from_w_uk": ("Wv[i] = load_elem(P->w_uv, P->w_dtype, (int64_t)h * dv * dl + i);",
+                         "Wv[i] = load_elem(P->w_uk, P->w_dtype, (int64_t)h * dv * dl + i);"),
+    "last_token_dropped": ("/* pass 2: weighted sum of the rebuilt values W_UV[h]·c_t ([V2] §2.1) */\n    for (int64_t t = 0; t < nt; ++t) {",
+                           "/* pass 2 */\n    for (int64_t t = 0; t < nt - 1; ++t) {"),
+    "e4m3_bias_8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "paged_offset_wrong": ("return page * P->page_size + t % P->page_size;",
+                           "return page * P->page_size + (t + 1) % P->page_size;"),
+    "lse_base2": ("lse[idx] = m + log(l);", "lse[idx] = m + log2(l);"),
+    "combine_ignores_weights": ("out[d] += wgt * up[d];", "out[d] += up[d] / S;"),
+    "row_scale_ignored": ("if (P->cache_dtype == ORACLE_E4M3) f = (double)P->row_scale[r];", ""),
+}
+
+PIN_CHECKS = [
+    lambda: pins.test_matches_library_attention_on_rebuilt_kv((16, 8, 32, 12)),
+    lambda: pins.test_matches_library_attention_on_rebuilt_kv((128, 64, 512, 128)),
+    pins.test_identity_weights_reduce_to_one_kv_head_attention,
+    pins.test_absorbed_form_identity,
+    pins.test_single_token_returns_its_value,
+    pins.test_zero_query_is_uniform_average,
+    pins.test_one_dominant_key_two_level_weights,
+    pins.test_common_score_shift,
+    lambda: pins.test_split_and_merge_equals_whole((0, 13, 40, 61)),
+    pins.test_default_scale_is_one_over_sqrt_nope_plus_rope,
+    pins.test_paged_equals_contiguous_and_poison_is_unread,
+    pins.test_fp8_rows_are_decoded_codes_times_row_scale,
+    codecs.test_e4m3_decode_all_codes,
+]
+
+
+def _build_mutant(tmp, name):
+    src = open(os.path.join(HERE, "oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not found in oracle.c"
+    d = tmp / name
+    d.mkdir()
+    (d / "oracle.c").write_text(src.replace(old, new))
+    shutil.copy(os.path.join(HERE, "oracle.h"), d / "oracle.h")
+    lib = d / "liboracle.so"
+    subprocess.run(["gcc", *CFLAGS, "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+                    str(d / "oracle.c"), "-o", str(lib), "-lm"], check=True)
+    return str(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(tmp_path, name, monkeypatch):
+    path = _build_mutant(tmp_path, name)
+    good = oracle.lib()
+    # a library with the same entry points and signatures, different arithmetic
+    mut = ctypes.CDLL(path)
+    for fn in ("oracle_mla_decode", "oracle_absorb_q", "oracle_combine", "oracle_up_proj",
+               "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_array",
+               "oracle_mla_cache_bytes_per_token", "oracle_mha_cache_bytes",
+               "oracle_num_threads"):
+        getattr(mut, fn).restype = getattr(good, fn).restype
+        getattr(mut, fn).argtypes = getattr(good, fn).argtypes
+    monkeypatch.setattr(oracle, "_lib", mut)
+    caught = 0
+    for check in PIN_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError):
+            caught += 1
+    assert caught > 0, f"no pin catches mutant {name}"
