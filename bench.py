@@ -1,0 +1,234 @@
+"""Benchmark: MLA decode step (absorb -> decode -> combine -> up-projection) on
+one MI355X, synthetic inputs, printed as one JSON line.
+
+Timed workload (default): DeepSeek-V2 geometry, bf16 cache and weights with
+fp32 accumulation, batch 32, one query token per sequence, 128 heads,
+d_nope 128, d_rope 64, d_c 512, d_v 128, uniform cache length 2048, 8 split
+ranges per sequence.  A "step" is one decode step of one layer for the whole
+batch; tokens/s = batch / step time.
+
+The inputs of R independent replicas (cache rows, queries, weights; >= 1 GiB
+in total) are resident in HBM before timing starts and the steps rotate over
+them, so the 256 MB Infinity Cache cannot serve the cache stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "mla_latent_kv_15_amd", "csrc", "mla_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv2_b32_l2k")
+    ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
+    ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--replica-bytes", type=float, default=1.25 * 2**30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE,):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(launch_cache_bytes):
+    """HBM bytes per decode launch measured by rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n,
+                      "launches": 5}), flush=True)
+
+
+def cpu_baseline(inp, n_seq: int):
+    """The oracle timed on the host cores on n_seq whole sequences (all heads,
+    all cached tokens) of the same workload; tokens/s = n_seq / seconds."""
+    import oracle
+    wl = inp.wl
+    pairs = [(b, h) for b in range(n_seq) for h in range(wl.heads)]
+    t = time.perf_counter()
+    oracle.decode_inputs(inp, sel=pairs)
+    dt = time.perf_counter() - t
+    return {"value": n_seq / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences, all {wl.heads} heads, "
+                      f"{int(inp.seq_lens[0])} cached tokens each (naive float64 rebuild of "
+                      f"K and V), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_15_amd as mla
+    import synth
+    from tests.mla_cases import DeviceInputs
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    wl = synth.workload(args.workload)
+    S = args.splits or wl.num_splits
+    print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(wl)
+    dev = DeviceInputs(inp)
+    cache_bytes = synth.cache_bytes(wl, inp.seq_lens)
+    per_replica = (cache_bytes + dev.w_uk.numel() * dev.w_uk.element_size() * 2
+                   + dev.q_nope.numel() * 2 * 2)
+    R = max(1, math.ceil(args.replica_bytes / per_replica))
+
+    # replicas: same values at different addresses
+    reps = []
+    for r in range(R):
+        c = dev.cache
+        reps.append(dict(
+            q_nope=dev.q_nope.clone(), q_rope=dev.q_rope.clone(), w_uk=dev.w_uk.clone(),
+            w_uv=dev.w_uv.clone(),
+            cache=mla.Cache(rows=c.rows.clone(), seq_lens=c.seq_lens.clone(),
+                            max_seq_len=c.max_seq_len,
+                            row_scale=None if c.row_scale is None else c.row_scale.clone(),
+                            block_table=None if c.block_table is None else c.block_table.clone(),
+                            seq_stride=c.seq_stride, page_size=c.page_size)))
+    act = torch.float32 if wl.cache_dtype == "f32" else torch.bfloat16
+    part = torch.float32 if args.part_dtype == "f32" else act
+    out = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    step = mla.DecodeStep(dev.geo, wl.batch, S, act_dtype=act, part_dtype=part, out_dtype=out)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def one(i, ev=None):
+        rp = reps[i % R]
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_absorb_q(step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs,
+                         stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.mla_decode(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
+                       stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        if S > 1:
+            mla.mla_combine(step.geo, step.u_part, step.lse_part, step.u, step.lse, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        mla.mla_up_proj(step.geo, step.u, rp["w_uv"], step.o, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    print(f"[bench] warmup {args.warmup}, R={R} replicas", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing: K steps between two synchronisations
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel timing with HIP events on the launch stream (a separate pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        one(i, evs[i])
+    torch.cuda.synchronize()
+    ker = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(4)]
+                    for i in range(args.steps)])  # ms
+    k_mean = ker.mean(axis=0)
+    k_med = np.median(ker, axis=0)
+    t_decode = float(k_mean[1]) * 1e-3
+    t_dc = float(k_mean[1] + k_mean[2]) * 1e-3
+
+    launch_bytes = cache_bytes  # algorithmic bytes of one mla_decode launch
+    achieved = launch_bytes / t_decode / 1e9
+    traffic = stored_traffic(launch_bytes)
+    tokens_per_s = wl.batch / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, 2 if wl.batch >= 2 else 1)
+
+    rec = {
+        "metric": "MLA decode tokens/s + latent-KV HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.cache_dtype == "bf16" else wl.cache_dtype,
+        "data": "synthetic (seeded N(0,1) activations/cache, N(0,1/512) weights)",
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads,
+                   "d_nope": wl.d_nope, "d_rope": wl.d_rope, "d_latent": wl.d_latent,
+                   "d_v": wl.d_v, "seq_len": int(inp.max_seq_len), "splits": S,
+                   "cache": f"{wl.cache_dtype} {'paged' if wl.page_size else 'contiguous'}",
+                   "partials": args.part_dtype, "replicas": R, "parallelism": "none (1 GPU)"},
+        "cache_GBps": cache_bytes / t_dc / 1e9,
+        "cache_pct_hbm_peak": 100.0 * cache_bytes / t_dc / 1e9 / HBM_PEAK_GBPS,
+        "kernel_us_mean": {"absorb_q": k_mean[0] * 1e3, "decode": k_mean[1] * 1e3,
+                           "combine": k_mean[2] * 1e3, "up_proj": k_mean[3] * 1e3},
+        "kernel_us_median": {"absorb_q": k_med[0] * 1e3, "decode": k_med[1] * 1e3,
+                             "combine": k_med[2] * 1e3, "up_proj": k_med[3] * 1e3},
+        "roofline": {"kernel": "mla_decode", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * mla.h — C ABI of the MLA (multi-head latent attention) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What one decode step computes, for every sequence b and query head i, over
+ * the L_b cached tokens of b (no mask: every cached token is attended):
+ *
+ *     o[b,i] = W_UV[i] · softmax_t( scale · ( q̃[b,i]·c_t + q_R[b,i]·k_R,t ) ) · c_t
+ *     q̃[b,i] = W_UK[i]ᵀ · q_C[b,i]
+ *
+ * where c_t (d_latent wide) is the cached joint KV latent of token t and k_R,t
+ * (d_rope wide) is its decoupled RoPE key, shared by all heads.  Sources:
+ *  - "DeepSeek V2的MLA注意力机制…低秩压缩技术…" (snabindia.com):
+ *    §2.1 the keys and values are rebuilt from one latent, K = W_U^K·KV_comp
+ *    and V = W_U^V·KV_comp; §2.2 the decoupled query (content part q_C,
+ *    position part q_R) and the single position key shared by all heads;
+ *    §2.3 only KV_comp and k_R are cached, the score is the dot product of
+ *    the concatenated query and key over sqrt(d), and W_U^K can be absorbed
+ *    into the query and W_U^V applied after the weighted sum (§4.1
+ *    optimize_for_inference);  §3.1 the DeepSeek-V2 geometry (128 heads,
+ *    head dim 128, d_c = 512, RoPE dim 64).
+ *  - "Multi-Head Latent Attention（MLA）：大模型KV Cache显存优化原理与实操"
+ *    (CSDN): §2.1 textbook attention softmax(QKᵀ/sqrt(d_k))·V; §3.2 the
+ *    latent cache is a [seq, latent] array per sequence.
+ *  - "engineering DeepSeek sparse attention long context inference"
+ *    (hotdry.top): FP8 KV cache for 128K contexts; the nn.Linear weight
+ *    layout [h·d, d_c] of the up-projections.
+ *
+ * The step is four calls, each only enqueued on the caller's HIP stream:
+ *     mla_absorb_q  ->  mla_decode  ->  mla_combine  ->  mla_up_proj
+ * mla_decode splits every sequence into num_splits token ranges and writes one
+ * normalised partial result per range; mla_combine merges them exactly with
+ * log-sum-exp weights; with num_splits == 1 the partial already is the final
+ * u and mla_combine may be skipped.
+ *
+ * Conventions for every call
+ *  - Pointers named as tensors are DEVICE pointers, owned by the caller,
+ *    row-major and contiguous, with the shapes given at each argument.  The
+ *    library never allocates, frees, retains or synchronises: each call
+ *    validates its arguments on the host, enqueues kernels on `stream`
+ *    (a hipStream_t; NULL = the default stream) and returns.
+ *  - Errors: argument problems are reported synchronously, before any launch,
+ *    as a status code (nothing is printed, no exception crosses the ABI).
+ *    A failed launch returns MLA_E_HIP.  Faults inside a kernel surface at the
+ *    caller's next synchronisation, as with any asynchronous HIP work.
+ *  - Thread safety: no mutable global state; calls on different streams are
+ *    independent.
+ *  - dtype codes: MLA_F32 (IEEE binary32), MLA_BF16 (upper half of binary32),
+ *    MLA_FP8_E4M3 (OCP 8-bit E4M3, bias 7, no infinities, max 448).
+ *  - Compiled geometry: d_latent = 512 and d_rope = 64 (the DeepSeek-V2
+ *    values); d_nope and d_v may be 1..256 in mla_absorb_q / mla_up_proj.
+ *  - Data: a sequence of length 0 yields u = 0, lse = -inf and o = 0.
+ *    Cache slots that hold no token of the sequence being read (past its
+ *    length, the tail of its last page) are never read and may hold anything,
+ *    including NaN.  NaN or Inf in read inputs propagate.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_E_ARG = 1,         /* null pointer, negative size, bad enum value */
+  MLA_E_DTYPE = 2,       /* dtype combination not provided */
+  MLA_E_SHAPE = 3,       /* dimension outside the compiled geometry */
+  MLA_E_ALIGN = 4,       /* a pointer or stride violates the stated alignment */
+  MLA_E_HIP = 5,         /* the HIP runtime reported an error at launch */
+  MLA_E_UNSUPPORTED = 6  /* valid request the library does not provide */
+} mla_status_t;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype_t;
+
+/* Model geometry of one attention layer.
+ * softmax_scale <= 0 selects 1/sqrt(d_nope + d_rope): the scale belongs to the
+ * per-head query/key width of the non-absorbed form (DeepSeek V2 page §2.3),
+ * not to the 576-wide absorbed dot product. */
+typedef struct {
+  int32_t heads;     /* h >= 1 */
+  int32_t d_nope;    /* content (non-RoPE) query/key width per head */
+  int32_t d_rope;    /* decoupled RoPE width (64) */
+  int32_t d_latent;  /* latent width d_c (512) */
+  int32_t d_v;       /* value width per head */
+  float softmax_scale;
+} mla_dims_t;
+
+/* The latent KV cache of one layer.  Every cached token is one row of
+ * d_latent + d_rope elements, [c_KV | k_R] (DeepSeek V2 page §2.3: only the
+ * latent and the RoPE key are cached).
+ *
+ * Contiguous (page_size == 0): token t of sequence b is row b*seq_stride + t.
+ * Paged (page_size == 64): token t of sequence b is row
+ *   block_table[b*max_pages + t/64]*64 + t%64  (pages of 64 rows; the DeepSeek
+ * V2 page §1.2 / §3.3 lists paged KV memory as the companion optimisation).
+ *
+ * rows must be 16-byte aligned.  An FP8_E4M3 cache carries one fp32 factor per
+ * row in row_scale (same row index): value = decode(code) * row_scale[row]. */
+typedef struct {
+  int32_t dtype;               /* mla_dtype_t of rows */
+  const void* rows;            /* device, [n_rows][d_latent + d_rope] */
+  const float* row_scale;      /* device, [n_rows]; FP8 only, else NULL */
+  int32_t page_size;           /* 0 or 64 */
+  int64_t seq_stride;          /* contiguous: rows between sequences (>= max length) */
+  const int32_t* block_table;  /* device, [B][max_pages]; paged only */
+  int32_t max_pages;
+  const int32_t* seq_lens;     /* device, [B], each in [0, max_seq_len] */
+  int32_t max_seq_len;         /* host-side bound on every seq_lens[b] */
+} mla_cache_t;
+
+/* Absorb W_UK into the query (DeepSeek V2 page §2.3 and §4.1):
+ *   q_abs[b][i][0:d_latent]        = sum_n q_nope[b][i][n] * W_UK[i][n][:]
+ *   q_abs[b][i][d_latent:+d_rope]  = q_rope[b][i][:]
+ * q_nope [B][h][d_nope], q_rope [B][h][d_rope] (dtype q_dt, F32 or BF16);
+ * w_uk [h][d_nope][d_latent] (w_dt, F32 or BF16); fp32 accumulation.
+ * q_abs [B][h][d_latent+d_rope] in q_abs_dt: F32, BF16 (round to nearest
+ * even) or FP8_E4M3, in which case q_abs_scale [B][h] receives one fp32
+ * factor per (b, i) (amax/448) and q_abs holds RNE(x / factor); otherwise
+ * q_abs_scale must be NULL. */
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* q_nope,
+                          const void* q_rope, int32_t q_dt, const void* w_uk,
+                          int32_t w_dt, void* q_abs, int32_t q_abs_dt,
+                          float* q_abs_scale, void* stream);
+
+/* Attention of every head over the latent cache, split into num_splits token
+ * ranges per sequence.  Split p of sequence b covers tokens
+ *   [p*C, min((p+1)*C, L_b)),  C = 32 * ceil(max_seq_len / (32*num_splits)),
+ * so every range is a whole number of 32-token tiles; empty ranges write
+ * u = 0 and lse = -inf.  For each (b, p, i) over that range R:
+ *   s_t  = scale * (q_abs[b][i][0:d_latent]·c_t + q_abs[b][i][d_latent:]·k_R,t)
+ *   u_part[b][p][i][:] = sum_{t in R} e^{s_t} c_t / sum_{t in R} e^{s_t}
+ *   lse_part[b][p][i]  = ln sum_{t in R} e^{s_t}      (natural log)
+ * q_abs [B][h][d_latent+d_rope] (q_abs_dt); q_abs_scale [B][h] when q_abs is
+ * FP8, else NULL.  u_part [B][num_splits][h][d_latent] in part_dt (F32 or
+ * BF16); lse_part [B][num_splits][h] fp32.  1 <= num_splits <= 1024.
+ * Provided dtype pairs (cache / q_abs): F32/F32, BF16/BF16, FP8/BF16,
+ * FP8/FP8.  The BF16 and FP8 paths need h to be a multiple of 32. */
+mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
+                        int32_t q_abs_dt, const float* q_abs_scale,
+                        const mla_cache_t* cache, int32_t num_splits, void* u_part,
+                        int32_t part_dt, float* lse_part, void* stream);
+
+/* Merge the split partials of mla_decode with log-sum-exp weights:
+ *   lse[b][i] = ln sum_p e^{lse_part[b][p][i]}
+ *   u[b][i][:] = sum_p e^{lse_part[b][p][i] - lse[b][i]} * u_part[b][p][i][:]
+ * Parts with lse = -inf carry no weight; if every part is empty, u = 0 and
+ * lse = -inf.  u_part/lse_part as written by mla_decode; u [B][h][d_latent]
+ * in u_dt (F32 or BF16); lse [B][h] fp32 or NULL. */
+mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t num_splits,
+                         const void* u_part, int32_t part_dt, const float* lse_part,
+                         void* u, int32_t u_dt, float* lse, void* stream);
+
+/* Apply W_UV after the weighted sum (DeepSeek V2 page §2.3):
+ *   o[b][i][v] = sum_c W_UV[i][v][c] * u[b][i][c]
+ * u [B][h][d_latent] (u_dt, F32 or BF16); w_uv [h][d_v][d_latent] (w_dt, F32
+ * or BF16); o [B][h][d_v] in o_dt (F32 or BF16, round to nearest even);
+ * fp32 accumulation. */
+mla_status_t mla_up_proj(const mla_dims_t* dims, int32_t B, const void* u,
+                         int32_t u_dt, const void* w_uv, int32_t w_dt, void* o,
+                         int32_t o_dt, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mla_status_str(mla_status_t status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

@@ -1,0 +1,231 @@
+"""Python binding of libmla.so, the MI355X (gfx950) MLA decode library.
+
+Argument marshalling only: every function here takes torch tensors that live
+on the GPU, checks their dtype/shape/contiguity, and passes raw device
+pointers plus the current HIP stream to the C entry point of the same name
+declared in include/mla.h.  All arithmetic runs in the library's kernels.
+There is no CPU fallback: importing this module without the built library
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_F32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
+MLA_OK = 0
+
+D_LATENT = 512
+D_ROPE = 64
+TILE_TOKENS = 32
+PAGE_SIZE = 64
+MAX_SPLITS = 1024
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class Dims(C.Structure):
+    _fields_ = [("heads", C.c_int32), ("d_nope", C.c_int32), ("d_rope", C.c_int32),
+                ("d_latent", C.c_int32), ("d_v", C.c_int32), ("softmax_scale", C.c_float)]
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("rows", C.c_void_p), ("row_scale", C.c_void_p),
+                ("page_size", C.c_int32), ("seq_stride", C.c_int64),
+                ("block_table", C.c_void_p), ("max_pages", C.c_int32),
+                ("seq_lens", C.c_void_p), ("max_seq_len", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, f32p = C.c_void_p, C.c_int32, C.c_void_p
+        L.mla_absorb_q.restype = C.c_int
+        L.mla_absorb_q.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp, i32, vp, i32, f32p, vp]
+        L.mla_decode.restype = C.c_int
+        L.mla_decode.argtypes = [C.POINTER(Dims), i32, vp, i32, f32p, C.POINTER(CacheDesc), i32,
+                                 vp, i32, f32p, vp]
+        L.mla_combine.restype = C.c_int
+        L.mla_combine.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, f32p, vp, i32, f32p, vp]
+        L.mla_up_proj.restype = C.c_int
+        L.mla_up_proj.argtypes = [C.POINTER(Dims), i32, vp, i32, vp, i32, vp, i32, vp]
+        L.mla_status_str.restype = C.c_char_p
+        L.mla_status_str.argtypes = [C.c_int]
+        L.mla_version.restype = C.c_int32
+        L.mla_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_up_proj", "mla_status_str",
+            "mla_version")
+
+
+def status_str(status: int) -> str:
+    return lib().mla_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MLA_OK:
+        raise MLAError(fn, status)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MLA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MLA library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+@dataclass
+class Geometry:
+    heads: int
+    d_nope: int = 128
+    d_rope: int = D_ROPE
+    d_latent: int = D_LATENT
+    d_v: int = 128
+    softmax_scale: float = 0.0  # <= 0: 1/sqrt(d_nope + d_rope)
+
+    def c(self) -> Dims:
+        return Dims(self.heads, self.d_nope, self.d_rope, self.d_latent, self.d_v,
+                    float(self.softmax_scale))
+
+
+@dataclass
+class Cache:
+    """Latent cache of one layer (see mla_cache_t).  rows: [n_rows, 576]
+    (float32 / bfloat16 / uint8 e4m3 codes); row_scale: float32 [n_rows] for
+    e4m3; seq_lens: int32 [B] on the device; block_table: int32 [B, max_pages]
+    for the paged layout."""
+    rows: torch.Tensor
+    seq_lens: torch.Tensor
+    max_seq_len: int
+    row_scale: Optional[torch.Tensor] = None
+    block_table: Optional[torch.Tensor] = None
+    seq_stride: int = 0
+    page_size: int = 0
+
+    def c(self) -> CacheDesc:
+        mp = 0 if self.block_table is None else int(self.block_table.shape[1])
+        return CacheDesc(dtype_code(self.rows), _ptr(self.rows), _ptr(self.row_scale),
+                         int(self.page_size), int(self.seq_stride), _ptr(self.block_table), mp,
+                         _ptr(self.seq_lens), int(self.max_seq_len))
+
+
+def mla_absorb_q(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor,
+                 q_abs: torch.Tensor, q_abs_scale: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    B = int(q_nope.shape[0])
+    d = geo.c()
+    st = lib().mla_absorb_q(C.byref(d), B, _ptr(q_nope), _ptr(q_rope), dtype_code(q_nope),
+                            _ptr(w_uk), dtype_code(w_uk), _ptr(q_abs), dtype_code(q_abs),
+                            _ptr(q_abs_scale), _stream(stream))
+    _check("mla_absorb_q", st)
+
+
+def mla_decode(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int,
+               u_part: torch.Tensor, lse_part: torch.Tensor,
+               q_abs_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    B = int(q_abs.shape[0])
+    d = geo.c()
+    cd = cache.c()
+    st = lib().mla_decode(C.byref(d), B, _ptr(q_abs), dtype_code(q_abs), _ptr(q_abs_scale),
+                          C.byref(cd), int(num_splits), _ptr(u_part), dtype_code(u_part),
+                          _ptr(lse_part), _stream(stream))
+    _check("mla_decode", st)
+
+
+def mla_combine(geo: Geometry, u_part: torch.Tensor, lse_part: torch.Tensor, u: torch.Tensor,
+                lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    B, S = int(u_part.shape[0]), int(u_part.shape[1])
+    d = geo.c()
+    st = lib().mla_combine(C.byref(d), B, S, _ptr(u_part), dtype_code(u_part), _ptr(lse_part),
+                           _ptr(u), dtype_code(u), _ptr(lse), _stream(stream))
+    _check("mla_combine", st)
+
+
+def mla_up_proj(geo: Geometry, u: torch.Tensor, w_uv: torch.Tensor, o: torch.Tensor,
+                stream=None) -> None:
+    B = int(u.shape[0])
+    d = geo.c()
+    st = lib().mla_up_proj(C.byref(d), B, _ptr(u), dtype_code(u), _ptr(w_uv), dtype_code(w_uv),
+                           _ptr(o), dtype_code(o), _stream(stream))
+    _check("mla_up_proj", st)
+
+
+def split_chunk(max_seq_len: int, num_splits: int) -> int:
+    """Tokens per split range (mirrors the rule stated in include/mla.h)."""
+    if max_seq_len <= 0:
+        return 0
+    per = TILE_TOKENS * num_splits
+    return -(-max_seq_len // per) * TILE_TOKENS
+
+
+class DecodeStep:
+    """One MLA decode step of one layer: the four library calls in order, with
+    the intermediate buffers allocated once (torch allocator) and reused.
+
+    q_nope [B, h, d_nope], q_rope [B, h, d_rope], w_uk [h, d_nope, 512],
+    w_uv [h, d_v, 512] (float32 or bfloat16); the cache as `Cache`.
+    act_dtype is the dtype of q_abs / u; part_dtype of the split partials."""
+
+    def __init__(self, geo: Geometry, batch: int, num_splits: int, device="cuda",
+                 act_dtype=torch.bfloat16, part_dtype=torch.bfloat16, out_dtype=torch.bfloat16):
+        self.geo = geo
+        self.B = batch
+        self.S = int(num_splits)
+        h = geo.heads
+        w = geo.d_latent + geo.d_rope
+        self.q_abs = torch.empty(batch, h, w, dtype=act_dtype, device=device)
+        self.u_part = torch.empty(batch, self.S, h, geo.d_latent, dtype=part_dtype, device=device)
+        self.lse_part = torch.empty(batch, self.S, h, dtype=torch.float32, device=device)
+        self.u = (self.u_part.view(batch, h, geo.d_latent) if self.S == 1
+                  else torch.empty(batch, h, geo.d_latent, dtype=part_dtype, device=device))
+        self.lse = (self.lse_part.view(batch, h) if self.S == 1
+                    else torch.empty(batch, h, dtype=torch.float32, device=device))
+        self.o = torch.empty(batch, h, geo.d_v, dtype=out_dtype, device=device)
+
+    def run(self, q_nope, q_rope, w_uk, w_uv, cache: Cache, stream=None) -> torch.Tensor:
+        mla_absorb_q(self.geo, q_nope, q_rope, w_uk, self.q_abs, stream=stream)
+        mla_decode(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part, stream=stream)
+        if self.S > 1:
+            mla_combine(self.geo, self.u_part, self.lse_part, self.u, self.lse, stream=stream)
+        mla_up_proj(self.geo, self.u, w_uv, self.o, stream=stream)
+        return self.o

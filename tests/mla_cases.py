@@ -1,0 +1,113 @@
+"""Shared helpers of the GPU tests: upload seeded synthetic inputs, run one
+decode step through the library's C ABI, and compare with the CPU oracle on
+chosen (sequence, head) pairs."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mla_latent_kv_15_amd as mla
+import oracle
+import synth
+
+# max|gpu - oracle| <= TOL * max|oracle| per compared quantity
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def bits_to_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "f32":
+        t = torch.from_numpy(a.astype(np.float32, copy=False))
+    elif dtype == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "fp8":
+        t = torch.from_numpy(a.astype(np.uint8, copy=False))
+    else:
+        raise ValueError(dtype)
+    return t.to(device)
+
+
+class DeviceInputs:
+    """The stored inputs of one synthetic workload, resident on the GPU."""
+
+    def __init__(self, inp: synth.MLAInputs, device="cuda"):
+        wl = inp.wl
+        self.inp = inp
+        self.wl = wl
+        self.q_nope = bits_to_tensor(inp.q_nope, wl.act_dtype, device)
+        self.q_rope = bits_to_tensor(inp.q_rope, wl.act_dtype, device)
+        self.w_uk = bits_to_tensor(inp.w_uk, wl.act_dtype, device)
+        self.w_uv = bits_to_tensor(inp.w_uv, wl.act_dtype, device)
+        rows = bits_to_tensor(inp.rows, wl.cache_dtype, device)
+        row_scale = (None if inp.row_scale is None
+                     else torch.from_numpy(inp.row_scale).to(device))
+        bt = (None if inp.block_table is None
+              else torch.from_numpy(np.ascontiguousarray(inp.block_table, np.int32)).to(device))
+        self.cache = mla.Cache(rows=rows, seq_lens=torch.from_numpy(inp.seq_lens).to(device),
+                               max_seq_len=int(inp.max_seq_len), row_scale=row_scale,
+                               block_table=bt, seq_stride=int(inp.seq_stride),
+                               page_size=int(wl.page_size))
+        self.geo = mla.Geometry(heads=wl.heads, d_nope=wl.d_nope, d_rope=wl.d_rope,
+                                d_latent=wl.d_latent, d_v=wl.d_v)
+
+
+def act_torch_dtype(wl) -> torch.dtype:
+    return torch.float32 if wl.cache_dtype == "f32" else torch.bfloat16
+
+
+def run_step(dev: DeviceInputs, num_splits: int, part_dtype=None, out_dtype=None):
+    """absorb -> decode -> combine -> up_proj.  Returns the DecodeStep (its
+    buffers hold q_abs, u_part, lse_part, u, lse, o)."""
+    wl = dev.wl
+    act = act_torch_dtype(wl)
+    step = mla.DecodeStep(dev.geo, wl.batch, num_splits, act_dtype=act,
+                          part_dtype=part_dtype or act,
+                          out_dtype=out_dtype or TORCH_DT[wl.out_dtype])
+    step.run(dev.q_nope, dev.q_rope, dev.w_uk, dev.w_uv, dev.cache)
+    torch.cuda.synchronize()
+    return step
+
+
+def sample_pairs(B: int, H: int, n_b: int = 4, n_h: int = 4, seq_lens=None):
+    """A deterministic spread of (b, h) pairs: first/last sequences and heads
+    plus interior ones; sequences of length 0 are kept (they must give 0)."""
+    bs = sorted(set(np.linspace(0, B - 1, n_b).round().astype(int).tolist()))
+    hs = sorted(set(np.linspace(0, H - 1, n_h).round().astype(int).tolist()))
+    return [(b, h) for b in bs for h in hs]
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), "non-finite GPU output"
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    diff = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if scale == 0.0:
+        return diff
+    return diff / scale
+
+
+def check_against_oracle(dev: DeviceInputs, step: mla.DecodeStep, pairs, tol: float):
+    """o, u and lse of the selected pairs against the oracle.  Returns the
+    three relative errors."""
+    o_ref, lse_ref, u_ref = oracle.decode_inputs(dev.inp, sel=pairs, want_u=True)
+    o = step.o.float().cpu().numpy()
+    u = step.u.float().cpu().numpy()
+    lse = step.lse.float().cpu().numpy()
+    o_got = np.stack([o[b, h] for b, h in pairs])
+    u_got = np.stack([u[b, h] for b, h in pairs])
+    lse_got = np.array([lse[b, h] for b, h in pairs])
+    e_o = rel_err(o_got, o_ref)
+    e_u = rel_err(u_got, u_ref)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_got), fin), "empty-sequence lse must be -inf"
+    assert np.all(lse_got[~fin] == -np.inf)
+    e_l = float(np.max(np.abs(lse_got[fin] - lse_ref[fin]))) if fin.any() else 0.0
+    assert e_o <= tol, f"o: max err {e_o:.3e} > {tol:g} of max|o|"
+    assert e_u <= tol, f"u: max err {e_u:.3e} > {tol:g} of max|u|"
+    # lse is a log: an absolute error of tol is a relative error of tol in exp(lse)
+    assert e_l <= tol, f"lse: max abs err {e_l:.3e} > {tol:g}"
+    return e_o, e_u, e_l

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP decode path (absorb -> decode -> combine -> up-projection,
+called through the C ABI) against the CPU oracle (naive rebuild of K and V,
+textbook softmax) on seeded synthetic inputs.
+
+Tolerances: max|o_gpu - o_oracle| <= tol * max|o_oracle| with tol 1e-4 for an
+fp32 cache, 2e-2 for bf16 and 6e-2 for an fp8-e4m3 cache; the same bound is
+applied to the attention-weighted latent u, and tol as an absolute bound on
+lse (natural log).  Cache slots that hold no token are NaN-poisoned by the
+generator, so reading one fails the finiteness check.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.mla_cases import (TOL, DeviceInputs, check_against_oracle, run_step, sample_pairs)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- small cases
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_tiny_f32_every_output(splits):
+    """fp32 cache, B=1, h=16, L=512: every (b, h) against the oracle at 1e-4."""
+    wl = synth.workload("tiny_f32")
+    dev = DeviceInputs(synth.make_inputs(wl))
+    step = run_step(dev, splits)
+    pairs = [(0, h) for h in range(wl.heads)]
+    e = check_against_oracle(dev, step, pairs, TOL["f32"])
+    _log(f"tiny_f32 S={splits}: err o/u/lse = {e}")
+
+
+RAGGED = [0, 1, 31, 32, 45, 300, 257]
+
+
+@pytest.mark.parametrize("heads", [32, 128, 160])
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_ragged_bf16(heads, splits):
+    """bf16, several tiles plus ragged tails, empty and 1-token sequences, a
+    partial head group (160 = 128 + 32) and waves without heads (32)."""
+    wl = synth.workload("dsv2_b32_l2k").with_(batch=len(RAGGED), heads=heads, seq_len=None,
+                                             seed=synth.workloads.BASE_SEED + 101)
+    dev = DeviceInputs(synth.make_inputs(wl, lengths=RAGGED))
+    step = run_step(dev, splits)
+    pairs = [(b, h) for b in range(wl.batch) for h in sorted({0, 1, heads // 2, heads - 1})]
+    e = check_against_oracle(dev, step, pairs, TOL["bf16"])
+    _log(f"ragged h={heads} S={splits}: err o/u/lse = {e}")
+
+
+@pytest.mark.parametrize("part", ["f32", "bf16"])
+def test_ragged_fp32_partials(part):
+    """The same bf16 problem with fp32 or bf16 split partials."""
+    wl = synth.workload("dsv2_b32_l2k").with_(batch=len(RAGGED), seq_len=None,
+                                             seed=synth.workloads.BASE_SEED + 102)
+    dev = DeviceInputs(synth.make_inputs(wl, lengths=RAGGED))
+    step = run_step(dev, 5, part_dtype=torch.float32 if part == "f32" else torch.bfloat16)
+    pairs = [(b, h) for b in range(wl.batch) for h in (0, 77, 127)]
+    check_against_oracle(dev, step, pairs, TOL["bf16"])
+
+
+def test_fp8_small():
+    """fp8-e4m3 cache with per-row scales, ragged lengths, 3 splits."""
+    wl = synth.workload("fp8_b1_l128k").with_(batch=4, seq_len=None,
+                                             seed=synth.workloads.BASE_SEED + 103)
+    lens = [300, 77, 1, 0]
+    dev = DeviceInputs(synth.make_inputs(wl, lengths=lens))
+    step = run_step(dev, 3)
+    pairs = [(b, h) for b in range(4) for h in (0, 31, 64, 127)]
+    e = check_against_oracle(dev, step, pairs, TOL["fp8"])
+    _log(f"fp8 small: err o/u/lse = {e}")
+
+
+def test_paged_matches_contiguous_bitwise():
+    """The same tokens in a shuffled paged pool and in contiguous rows give
+    bit-identical partials (the tiles see the same rows in the same order)."""
+    base = synth.workload("paged_b64_ragged").with_(batch=6, seed=synth.workloads.BASE_SEED + 104)
+    lens = [1, 64, 65, 700, 129, 0]
+    paged = DeviceInputs(synth.make_inputs(base, lengths=lens))
+    contig = DeviceInputs(synth.make_inputs(base.with_(page_size=0), lengths=lens))
+    a = run_step(paged, 3)
+    b = run_step(contig, 3)
+    assert torch.equal(a.u_part.view(torch.int16), b.u_part.view(torch.int16))
+    assert torch.equal(a.lse_part, b.lse_part)
+    assert torch.equal(a.o.view(torch.int16), b.o.view(torch.int16))
+    pairs = [(bb, h) for bb in range(6) for h in (0, 127)]
+    check_against_oracle(paged, a, pairs, TOL["bf16"])
+
+
+def test_split_count_invariance():
+    """Different split counts give the same result within rounding."""
+    wl = synth.workload("dsv2_b32_l2k").with_(batch=3, seq_len=1000,
+                                             seed=synth.workloads.BASE_SEED + 105)
+    dev = DeviceInputs(synth.make_inputs(wl))
+    ref = run_step(dev, 1, part_dtype=torch.float32).o.float()
+    for s in (2, 3, 7, 32):
+        got = run_step(dev, s, part_dtype=torch.float32).o.float()
+        err = (got - ref).abs().max().item() / ref.abs().max().item()
+        assert err < 5e-3, (s, err)
+
+
+def test_repeat_is_deterministic():
+    wl = synth.workload("dsv2_b32_l2k").with_(batch=2, seq_len=333,
+                                             seed=synth.workloads.BASE_SEED + 106)
+    dev = DeviceInputs(synth.make_inputs(wl))
+    a = run_step(dev, 4).o.clone()
+    b = run_step(dev, 4).o.clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------- full sizes
+
+FULL = [
+    ("dsv2_b32_l2k", "bf16", 4, 4),
+    ("long_b4_l32k", "bf16", 4, 3),
+    ("paged_b64_ragged", "bf16", 4, 3),
+    ("fp8_b1_l128k", "fp8", 1, 4),
+    ("fp8_b8_l128k", "fp8", 2, 2),
+]
+
+
+@pytest.mark.parametrize("name,kind,nb,nh", FULL)
+def test_full_size_sampled(name, kind, nb, nh):
+    """Each workload at its full size with its stated split count, checked on a
+    spread of (b, h) pairs that the oracle computes one by one."""
+    wl = synth.workload(name)
+    _log(f"{name}: generating inputs")
+    dev = DeviceInputs(synth.make_inputs(wl))
+    _log(f"{name}: running S={wl.num_splits}")
+    step = run_step(dev, wl.num_splits)
+    pairs = sample_pairs(wl.batch, wl.heads, nb, nh)
+    e = check_against_oracle(dev, step, pairs, TOL[kind])
+    _log(f"{name}: err o/u/lse = {e}")
+    o = step.o.float()
+    assert torch.isfinite(o).all()
