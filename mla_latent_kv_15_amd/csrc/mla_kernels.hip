@@ -134,6 +134,9 @@ constexpr int kDmaPerWave = kBf16Chunks / 64 / kWaves;  // 9 wave-loads of 1 KB
 constexpr int kFp8RowChunks = kRowElems / 16;           // 36 x 16 B per fp8 row
 constexpr int kFp8Chunks = kTileTokens * kFp8RowChunks;               // 1152
 constexpr int kFp8PerThread = (kFp8Chunks + kThreads - 1) / kThreads;  // 5
+constexpr int kNBuf = 4;  // bf16 LDS tile buffers: up to 3 tiles in flight
+constexpr int kPBufBytes = 4 * 2048;
+constexpr int kQkAhead = 8;  // QK operand reads in flight  // bf16 probabilities of 4 head blocks x 32 tokens
 constexpr float kRefSlack = 64.0f;  // log2 units, see the softmax reference note
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -154,16 +157,31 @@ struct DecodeParams {
   float* lse_part;
 };
 
-// byte offset in an LDS tile of 16-byte chunk c of token t
-__device__ inline int lds_chunk(int t, int c) { return t * kRowBytes + ((c ^ (t & 7)) << 4); }
+// 16-byte chunk c of token t sits at chunk position c ^ swz(t) of the token's
+// row (the XOR stays inside the aligned group of 8 chunks).  swz maps
+// t = 0..7 to 0,2,4,6,1,3,5,7: the QK operand reads (8 consecutive tokens, one
+// chunk) and the transposing reads (4 consecutive tokens, two neighbouring
+// chunks) both touch 8 different chunk positions, i.e. all 32 banks once.
+__device__ inline int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
-// bf16 tile: wave w fills LDS chunk slots [(4i + w)*64, +64) for i = 0..8;
-// slot s holds chunk (s % 72) ^ (t & 7) of token t = s / 72.  The per-lane
-// source offsets are recomputed for every tile from an opaque copy of the lane
-// id, so the compiler does not keep nine of them alive across the loop.
-__device__ inline void tile_dma_bf16(const DecodeParams& P, uint8_t* T, int b, int t0, int nvalid,
-                                     int wave, int lane) {
-  const int64_t row0 = tile_row0(P.block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
+// byte offset in an LDS tile of 16-byte chunk c of token t
+__device__ inline int lds_chunk(int t, int c) { return t * kRowBytes + ((c ^ swz(t)) << 4); }
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+}
+
+// bf16 tile: wave w fills LDS chunk slots [(4i + w)*64, +64) for i = 0..8; slot
+// s of token t = s / 72 holds chunk (s % 72) ^ swz(t).  The loads are issued as
+// inline asm: the compiler then does not know they write LDS and does not wait
+// for them before every LDS read (it cannot prove the reads do not alias); the
+// kernel waits for them itself.  The per-lane source offsets are recomputed
+// for every tile from an opaque copy of the lane id, so the compiler does not
+// keep nine of them alive across the loop.
+__device__ inline void tile_dma_bf16(const DecodeParams& P, const int32_t* __restrict__ block_table,
+                                     uint32_t lds_tile, int b, int t0, int nvalid, int wave,
+                                     int lane) {
+  const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
   const uint8_t* base = P.rows + row0 * kRowBytes;
   int ln = lane;
   asm volatile("" : "+v"(ln));
@@ -171,10 +189,11 @@ __device__ inline void tile_dma_bf16(const DecodeParams& P, uint8_t* T, int b, i
   for (int i = 0; i < kDmaPerWave; ++i) {
     const int slot = (i * kWaves + wave) * 64 + ln;
     const int t = slot / kRowChunks;
-    const int c = (slot - t * kRowChunks) ^ (t & 7);
+    const int c = (slot - t * kRowChunks) ^ swz(t);
     const uint32_t off = static_cast<uint32_t>(((t < nvalid) ? t : 0) * kRowBytes + c * 16);
-    __builtin_amdgcn_global_load_lds(base + off, (lds_void_t*)(T + (i * kWaves + wave) * 1024),
-                                     16, 0, 0);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (i * kWaves + wave) * 1024);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0)
+                 : "memory");
   }
 }
 
@@ -183,9 +202,10 @@ struct Fp8Regs {
   float scale;
 };
 
-__device__ inline void tile_load_fp8(Fp8Regs& R, const DecodeParams& P, int b, int t0, int nvalid,
-                                     int tid) {
-  const int64_t row0 = tile_row0(P.block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
+__device__ inline void tile_load_fp8(Fp8Regs& R, const DecodeParams& P,
+                                     const int32_t* __restrict__ block_table, int b, int t0,
+                                     int nvalid, int tid) {
+  const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
   const uint8_t* base = P.rows + row0 * kRowElems;
 #pragma unroll
   for (int i = 0; i < kFp8PerThread; ++i) {
@@ -217,9 +237,14 @@ __device__ inline void tile_store_fp8(const Fp8Regs& R, uint8_t* T, float* tscal
 template <bool FP8, int PART_DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1)))
-void decode_mfma_kernel(DecodeParams P) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) float sscale[2][kTileTokens];
+void decode_mfma_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
+  constexpr int kBufs = FP8 ? 2 : kNBuf;
+  // tiles, then two probability buffers of 4 head blocks x 2 KiB
+  // (fp8: then the two tiles' row scales).  The bf16 layout uses all 160 KiB.
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t smem[kBufs * kTileBytes + 2 * kPBufBytes + (FP8 ? 2 * kTileTokens * 4 : 0)];
+  uint8_t* pbuf = smem + kBufs * kTileBytes;
+  float (*sscale)[kTileTokens] = reinterpret_cast<float (*)[kTileTokens]>(pbuf + 2 * kPBufBytes);
 
   const int nwork = P.B * P.S * P.HG;
   const int wid = xcd_remap(blockIdx.x, nwork);
@@ -230,41 +255,35 @@ void decode_mfma_kernel(DecodeParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hl = lane & 31;  // head within the wave (column of Sᵀ and Uᵀ)
+  const int hl = lane & 31;  // head within a 32-head block (column of Sᵀ and Uᵀ)
   const int g = lane >> 5;   // k-slot half
-  const int h0 = hg * kHeadsPerBlock + wave * kHeadsPerWave;
-  const bool active = h0 < P.H;  // wave-uniform
-  const int h = h0 + hl;
+  const int hbase = hg * kHeadsPerBlock;
+  // head blocks of this group: wave w computes QK/softmax for block w, and PV
+  // for every block over latent columns [128 w, 128 w + 128)
+  const int nhb = min(kWaves, (P.H - hbase) / kHeadsPerWave);  // workgroup-uniform
+  const bool qk_wave = wave < nhb;                              // wave-uniform
+  const int h = hbase + wave * kHeadsPerWave + hl;              // this lane's QK head
 
   // lengths are clamped to [0, max_seq_len]: the cache is never read past it
   const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
   const int t_begin = p * P.chunk;
   const int t_end = min(t_begin + P.chunk, L);
-  const int64_t out_row = (static_cast<int64_t>(b) * P.S + p) * P.H + h;
+  const int64_t row_base = (static_cast<int64_t>(b) * P.S + p) * P.H + hbase;  // u_part row of head hbase
 
   if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
-    if (active) {
-      for (int c = g; c < kDLatent; c += 2) store_elem<PART_DT>(P.u_part, out_row * kDLatent + c, 0.0f);
-      if (g == 0) P.lse_part[out_row] = -INFINITY;
+    if (qk_wave) {
+      const int64_t r = row_base + wave * kHeadsPerWave + hl;
+      for (int c = g; c < kDLatent; c += 2) store_elem<PART_DT>(P.u_part, r * kDLatent + c, 0.0f);
+      if (g == 0) P.lse_part[r] = -INFINITY;
     }
     return;
   }
 
-  // absorbed queries of this wave's 32 heads as the B operand:
-  // lane (hl, g) holds q_abs[h][16*kk + 8*g .. +7] for kk = 0..35
-  bf16x8_t qreg[kRowElems / 16];
-  if (active) {
-    const bf16x8_t* qrow = reinterpret_cast<const bf16x8_t*>(
-        static_cast<const uint16_t*>(P.q_abs) + (static_cast<int64_t>(b) * P.H + h) * kRowElems);
-#pragma unroll
-    for (int kk = 0; kk < kRowElems / 16; ++kk) qreg[kk] = qrow[2 * kk + g];
-  }
-
-  // transposing-read geometry: lane (G = lane/16, e, q4) reads rows
-  // 16*j + 4*(G/2) + e and +8, columns 32*cb + 16*(G%2) + 4*q4 .. +3
+  // transposing-read geometry of the PV A operand: lane (G = lane/16, e, q4)
+  // reads rows 16*j + 4*(G/2) + e and +8, columns 32*cb + 16*(G%2) + 4*q4 .. +3
   const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
   const int tr_row = 4 * (G >> 1) + e;
-  const int tr_key = tr_row & 7;
+  const int tr_key = swz(tr_row);
   const int tr_x = 2 * (G & 1) + (q4 >> 1);
   const int tr_byte = 8 * (q4 & 1);
   // column chunk 4*cb + tr_x: its low 3 bits are 4*(cb & 1) + tr_x
@@ -272,7 +291,7 @@ void decode_mfma_kernel(DecodeParams P) {
   // QK chunk 2*kk + g of token hl: its low 3 bits are 2*(kk & 3) + g
   int qk_off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) qk_off[i] = ((2 * i + g) ^ (hl & 7)) << 4;
+  for (int i = 0; i < 4; ++i) qk_off[i] = ((2 * i + g) ^ swz(hl)) << 4;
 
   const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
 
@@ -287,14 +306,22 @@ void decode_mfma_kernel(DecodeParams P) {
   float m_ref = -INFINITY;
   float m_seen = -INFINITY;  // true running max of head h
   float l_run = 0.0f;        // this lane's share of the sum of probabilities
-  f32x16_t acc[kDLatent / 32];
+  f32x16_t acc[kWaves * 4];  // Uᵀ blocks [head block][32-column block of this wave]
+
+  // absorbed queries of this wave's 32 heads as the B operand: lane (hl, g)
+  // holds q_abs[h][16*kk + 8*g .. +7] for kk = 0..35 (loaded after the first
+  // tile's loads are issued, so both are in flight together)
+  bf16x8_t qreg[kRowElems / 16];
+  const bf16x8_t* qrow = reinterpret_cast<const bf16x8_t*>(
+      static_cast<const uint16_t*>(P.q_abs) +
+      (static_cast<int64_t>(b) * P.H + (qk_wave ? h : hbase)) * kRowElems);
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int cb = 0; cb < kDLatent / 32; ++cb) {
+    for (int k = 0; k < kWaves * 4; ++k) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
-      asm volatile("" : "+a"(acc[cb]));
+      for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
+      asm volatile("" : "+a"(acc[k]));
     }
     // The PV MFMAs are inline asm, so the compiler cannot see the hazard
     // between these accumulator writes and their first matrix-core read.
@@ -304,30 +331,61 @@ void decode_mfma_kernel(DecodeParams P) {
 
     Fp8Regs R;
     if constexpr (FP8) {
-      tile_load_fp8(R, P, b, t_begin, min(kTileTokens, t_end - t_begin), tid);
+      tile_load_fp8(R, P, block_table, b, t_begin, min(kTileTokens, t_end - t_begin), tid);
       tile_store_fp8(R, smem, sscale[0], tid);
       if (ntiles > 1) {
         const int t1 = t_begin + kTileTokens;
-        tile_load_fp8(R, P, b, t1, min(kTileTokens, t_end - t1), tid);
+        tile_load_fp8(R, P, block_table, b, t1, min(kTileTokens, t_end - t1), tid);
       }
+      __syncthreads();
     } else {
-      tile_dma_bf16(P, smem, b, t_begin, min(kTileTokens, t_end - t_begin), wave, lane);
-      __builtin_amdgcn_s_waitcnt(0);
+      tile_dma_bf16(P, block_table, lds_addr(smem), b, t_begin, min(kTileTokens, t_end - t_begin),
+                    wave, lane);
     }
-    __syncthreads();
+    if (pass == 0 && qk_wave) {
+#pragma unroll
+      for (int kk = 0; kk < kRowElems / 16; ++kk) qreg[kk] = qrow[2 * kk + g];
+      // Consume the query loads here, once: otherwise the compiler keeps its
+      // waits for them inside the tile loop, where they would also drain the
+      // tile loads that are meant to stay in flight.  (Tile 0 was issued
+      // before the queries, so this also waits for it.)
+#pragma unroll
+      for (int kk = 0; kk < kRowElems / 16; ++kk) asm volatile("" : "+v"(qreg[kk]));
+    }
+    if constexpr (!FP8) {
+      // tiles 1 .. kNBuf-2 go out after that wait, so it does not cover them
+      for (int d = 1; d < kNBuf - 1 && d < ntiles; ++d) {
+        const int td = t_begin + d * kTileTokens;
+        tile_dma_bf16(P, block_table, lds_addr(smem) + d * kTileBytes, b, td,
+                      min(kTileTokens, t_end - td), wave, lane);
+      }
+    }
 
     for (int it = 0; it < ntiles; ++it) {
-      const int buf = it & 1;
+      const int buf = FP8 ? (it & 1) : (it & (kNBuf - 1));
       uint8_t* T = smem + buf * kTileBytes;
+      uint8_t* PB = pbuf + (it & 1) * kPBufBytes;
       const int t0 = t_begin + it * kTileTokens;
       if constexpr (!FP8) {
-        if (it + 1 < ntiles) {
-          const int t1 = t0 + kTileTokens;
-          tile_dma_bf16(P, smem + (buf ^ 1) * kTileBytes, b, t1, min(kTileTokens, t_end - t1),
-                        wave, lane);
+        // tile `it` has landed once at most 9 loads per later tile in flight
+        // remain outstanding; then every wave's share is visible after the
+        // barrier, and the buffer read in the previous iteration is free
+        const int later = min(ntiles, it + kNBuf - 1) - it - 1;
+        if (later >= 2)
+          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else if (later == 1)
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        if (it + kNBuf - 1 < ntiles) {
+          const int tn = t0 + (kNBuf - 1) * kTileTokens;
+          tile_dma_bf16(P, block_table, lds_addr(smem) + ((it + kNBuf - 1) & (kNBuf - 1)) * kTileBytes,
+                        b, tn, min(kTileTokens, t_end - tn), wave, lane);
         }
       }
-      if (active) {
+      bf16x8_t pk[2];
+      if (qk_wave) {
         // ---- QK: Sᵀ (32 tokens x 32 heads) over the 576-wide row.  Issued as
         //      inline asm so that Sᵀ lives in VGPRs: the 256 AGPRs hold Uᵀ.
         f32x16_t s;
@@ -335,22 +393,19 @@ void decode_mfma_kernel(DecodeParams P) {
         auto qk_read = [&](int kk) {
           return *reinterpret_cast<const bf16x8_t*>(arow + qk_off[kk & 3] + (kk >> 2) * 128);
         };
-        bf16x8_t a0 = qk_read(0), a1 = qk_read(1);
+        // operand ring: kQkAhead LDS reads stay in flight ahead of the MFMAs
+        bf16x8_t ring[kQkAhead];
 #pragma unroll
-        for (int kk = 0; kk < kRowElems / 16; kk += 2) {
-          bf16x8_t n0 = a0, n1 = a1;
-          if (kk + 2 < kRowElems / 16) {
-            n0 = qk_read(kk + 2);
-            n1 = qk_read(kk + 3);
-          }
+        for (int i = 0; i < kQkAhead; ++i) ring[i] = qk_read(i);
+#pragma unroll
+        for (int kk = 0; kk < kRowElems / 16; ++kk) {
+          const bf16x8_t a = ring[kk % kQkAhead];
+          if (kk + kQkAhead < kRowElems / 16) ring[kk % kQkAhead] = qk_read(kk + kQkAhead);
           if (kk == 0)
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a0), "v"(qreg[kk]));
+            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qreg[kk]));
           else
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a0), "v"(qreg[kk]));
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a1), "v"(qreg[kk + 1]));
-          __builtin_amdgcn_sched_barrier(0);
-          a0 = n0;
-          a1 = n1;
+            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qreg[kk]));
+          if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
         // the compiler does not see the asm results as MFMA writes: wait out
         // the matrix-core-write -> VALU-read hazard before Sᵀ is read
@@ -377,7 +432,6 @@ void decode_mfma_kernel(DecodeParams P) {
         if (pass == 0 && it == 0) m_ref = mx;
         m_seen = fmaxf(m_seen, mx);
         overflow |= (mx > m_ref + kRefSlack);
-        bf16x8_t pk[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = exp2f(s[r] - m_ref);
@@ -385,36 +439,42 @@ void decode_mfma_kernel(DecodeParams P) {
           if constexpr (FP8) pr *= sscale[buf][8 * (r >> 2) + 4 * g + (r & 3)];
           pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
         }
-        // ---- PV: Uᵀ[c][h] += Σ_t tile[t][c] P[t][h]: 16 column blocks x 2
-        //      token blocks of 16
+        // publish this head block's probabilities (B operands, lane order)
+        *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + lane * 16) = pk[0];
+        *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + 1024 + lane * 16) = pk[1];
+      }
+      asm volatile("s_barrier" ::: "memory");
+      // ---- PV: Uᵀ[c][h] += Σ_t tile[t][c] P[t][h] for this wave's 128
+      //      columns and every head block.  The transposed tile operands are
+      //      read once and reused for all head blocks.
+      {
         const uint8_t* r0 = T + tr_row * kRowBytes + tr_byte;
-        auto tr_read = [&](int j, int hi, int cb) {
-          const uint8_t* ptr =
-              r0 + tr_off[cb & 1] + (cb >> 1) * 128 + (16 * j + 8 * hi) * kRowBytes;
-          return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
-        };
-        // VALU-written probabilities -> matrix-core read
-        asm volatile("s_nop 4" : "+v"(pk[0]), "+v"(pk[1]));
-        bf16x4_t c00 = tr_read(0, 0, 0), c01 = tr_read(0, 1, 0);
-        bf16x4_t c10 = tr_read(1, 0, 0), c11 = tr_read(1, 1, 0);
+        bf16x8_t av[4][2];
 #pragma unroll
-        for (int cb = 0; cb < kDLatent / 32; ++cb) {
-          bf16x4_t n00 = c00, n01 = c01, n10 = c10, n11 = c11;
-          if (cb + 1 < kDLatent / 32) {
-            n00 = tr_read(0, 0, cb + 1);
-            n01 = tr_read(0, 1, cb + 1);
-            n10 = tr_read(1, 0, cb + 1);
-            n11 = tr_read(1, 1, cb + 1);
+        for (int cbl = 0; cbl < 4; ++cbl) {
+          const int cb = 4 * wave + cbl;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 128 + 16 * j * kRowBytes;
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
+            const bf16x4_t hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + 8 * kRowBytes));
+            av[cbl][j] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
-          const bf16x8_t A0 = {c00[0], c00[1], c00[2], c00[3], c01[0], c01[1], c01[2], c01[3]};
-          const bf16x8_t A1 = {c10[0], c10[1], c10[2], c10[3], c11[0], c11[1], c11[2], c11[3]};
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[cb]) : "v"(A0), "v"(pk[0]));
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[cb]) : "v"(A1), "v"(pk[1]));
-          __builtin_amdgcn_sched_barrier(0);
-          c00 = n00;
-          c01 = n01;
-          c10 = n10;
-          c11 = n11;
+        }
+#pragma unroll
+        for (int hb = 0; hb < kWaves; ++hb) {
+          if (hb < nhb) {
+            bf16x8_t pb0 = *reinterpret_cast<const bf16x8_t*>(PB + hb * 2048 + lane * 16);
+            bf16x8_t pb1 = *reinterpret_cast<const bf16x8_t*>(PB + hb * 2048 + 1024 + lane * 16);
+#pragma unroll
+            for (int cbl = 0; cbl < 4; ++cbl) {
+              asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                  : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl][0]), "v"(pb0));
+              asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                  : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl][1]), "v"(pb1));
+            }
+          }
         }
       }
       if constexpr (FP8) {
@@ -422,45 +482,88 @@ void decode_mfma_kernel(DecodeParams P) {
           tile_store_fp8(R, smem + (buf ^ 1) * kTileBytes, sscale[buf ^ 1], tid);
           if (it + 2 < ntiles) {
             const int t2 = t_begin + (it + 2) * kTileTokens;
-            tile_load_fp8(R, P, b, t2, min(kTileTokens, t_end - t2), tid);
+            tile_load_fp8(R, P, block_table, b, t2, min(kTileTokens, t_end - t2), tid);
           }
         }
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
       }
-      __syncthreads();
     }
-    // every wave takes the same number of passes (the tile loop has barriers)
-    if (!__syncthreads_or(overflow)) break;
+    // Every wave takes the same number of passes (the tile loop has
+    // barriers).  The votes go to the buffer that tile `ntiles` would use:
+    // nothing is loaded into it and no wave reads it any more.
+    int* votes = reinterpret_cast<int*>(smem + (ntiles & (kBufs - 1)) * kTileBytes);
+    const int any_wave = __any(overflow) ? 1 : 0;
+    if (lane == 0) votes[wave] = any_wave;
+    __syncthreads();
+    const int again = votes[0] | votes[1] | votes[2] | votes[3];
+    __syncthreads();
+    if (!again) break;
     m_ref = m_seen;
   }
 
-  if (active) {
-    // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.0f / l_tot;
-    // Uᵀ register r of block cb in lane (hl, g) is column 32*cb + 8*(r/4) + 4*g + r%4
-    const int64_t obase = out_row * kDLatent;
+  // ---- epilogue.  Normalisers of all head blocks via LDS (the tile buffers
+  //      are free now): linv[32*hb + hl] = 1 / Σ p of that head.
+  float* linv = reinterpret_cast<float*>(smem);
+  uint8_t* stage = smem + 1024;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qk_wave) {
+    if (g == 0) {
+      linv[wave * kHeadsPerWave + hl] = 1.0f / l_tot;
+      P.lse_part[row_base + wave * kHeadsPerWave + hl] = (m_ref + log2f(l_tot)) * kLn2;
+    }
+  }
+  __syncthreads();
+  // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  // Uᵀ register r of block (hb, cbl) in lane (hl, g) is column
+  // 128*wave + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
+  // wave stages one head block (32 rows x 128 columns) at a time in its own
+  // LDS region and writes 256 contiguous bytes per row.
+  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
+  constexpr int kColsRound = 256 / kEsz;                  // 128 bf16 / 64 fp32 columns
+  constexpr int kStageRow = kColsRound * kEsz + 16;       // padded: rows start 4 banks apart
+  uint8_t* W = stage + wave * kHeadsPerWave * kStageRow;
 #pragma unroll
-    for (int cb = 0; cb < kDLatent / 32; ++cb) {
+  for (int hb = 0; hb < kWaves; ++hb) {
+    if (hb < nhb) {
+      const float inv = linv[hb * kHeadsPerWave + hl];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int c = 32 * cb + 8 * r4 + 4 * g;
-        const float v0 = acc[cb][4 * r4 + 0] * inv, v1 = acc[cb][4 * r4 + 1] * inv;
-        const float v2 = acc[cb][4 * r4 + 2] * inv, v3 = acc[cb][4 * r4 + 3] * inv;
-        if constexpr (PART_DT == MLA_F32) {
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(P.u_part) + obase + c) =
-              f32x4_t{v0, v1, v2, v3};
-        } else {
-          const uint32_t w0 = f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-          const uint32_t w1 = f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
-          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(P.u_part) + obase + c) =
-              u32x2_t{w0, w1};
+      for (int half = 0; half < 128 / kColsRound; ++half) {
+#pragma unroll
+        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
+          const int cbl = half * (kColsRound / 32) + cbl2;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
+            const f32x16_t& A = acc[4 * hb + cbl];
+            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
+            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
+            uint8_t* wp = W + hl * kStageRow + c * kEsz;
+            if constexpr (PART_DT == MLA_F32) {
+              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
+            } else {
+              const uint32_t w0 = f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+              const uint32_t w1 = f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{w0, w1};
+            }
+          }
         }
+        // one wave's LDS operations complete in order: no barrier is needed
+        asm volatile("" ::: "memory");
+        // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
+        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
+                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * wave) * kEsz +
+                       half * (kColsRound * kEsz);
+#pragma unroll
+        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
+          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
+                                      (lane & 15) * 16) = v;
+        }
+        asm volatile("" ::: "memory");
       }
     }
-    if (g == 0) P.lse_part[out_row] = (m_ref + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -574,64 +677,94 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(DecodeF32Params
 
 // ================================================================ combine
 //
-// One workgroup of 128 threads per (b, head): log-sum-exp weights of the S
-// partials, then each thread sums four latent columns over the partials.
+// One wave per (b, head); lane l owns latent columns 8l .. 8l+7 (16 bytes of
+// each bf16 partial).  The first group of partial loads is issued before the
+// log-sum-exp weights are computed, so the two do not form a chain.
 
-constexpr int kCombThreads = 128;
+constexpr int kCombThreads = 64;
+
+template <int PART_DT>
+struct PartVec {  // 8 columns of one partial
+  static constexpr int kWords = PART_DT == MLA_F32 ? 8 : 4;
+  uint32_t w[kWords];
+};
+
+template <int PART_DT>
+__device__ inline PartVec<PART_DT> load_part(const void* u_part, int64_t elem) {
+  PartVec<PART_DT> v;
+  if constexpr (PART_DT == MLA_F32) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(u_part) + elem);
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(u_part) + elem + 4);
+    v.w[0] = a.x; v.w[1] = a.y; v.w[2] = a.z; v.w[3] = a.w;
+    v.w[4] = c.x; v.w[5] = c.y; v.w[6] = c.z; v.w[7] = c.w;
+  } else {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(u_part) + elem);
+    v.w[0] = a.x; v.w[1] = a.y; v.w[2] = a.z; v.w[3] = a.w;
+  }
+  return v;
+}
+
+template <int PART_DT>
+__device__ inline float part_elem(const PartVec<PART_DT>& v, int k) {
+  if constexpr (PART_DT == MLA_F32) return __uint_as_float(v.w[k]);
+  else return __uint_as_float((k & 1) ? (v.w[k >> 1] & 0xFFFF0000u) : (v.w[k >> 1] << 16));
+}
 
 template <int PART_DT, int U_DT>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* u_part,
                                                               const float* lse_part, void* u,
                                                               float* lse, int H, int S) {
-  extern __shared__ float wts[];  // [S]
-  __shared__ float red[2];
-  const int bh = blockIdx.x;
-  const int b = bh / H, h = bh % H;
-  const int tid = threadIdx.x;
+  constexpr int kG = PART_DT == MLA_F32 ? 8 : 16;  // partials in flight per lane
+  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int lane = threadIdx.x;
+  const int c0 = lane * 8;
+  auto part_at = [&](int p) {
+    return ((static_cast<int64_t>(b) * S + p) * H + h) * kDLatent + c0;
+  };
+  auto lse_at = [&](int p) { return lse_part[(static_cast<int64_t>(b) * S + p) * H + h]; };
+  PartVec<PART_DT> v[kG];
+#pragma unroll
+  for (int i = 0; i < kG; ++i)
+    if (i < S) v[i] = load_part<PART_DT>(u_part, part_at(i));
+  // log-sum-exp weights (parts with lse = -inf carry no weight)
   float mx = -INFINITY;
-  for (int p = tid; p < S; p += kCombThreads)
-    mx = fmaxf(mx, lse_part[(static_cast<int64_t>(b) * S + p) * H + h]);
+  for (int p = lane; p < S; p += 64) mx = fmaxf(mx, lse_at(p));
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(red[0], red[1]);
-  __syncthreads();
   float z = 0.0f;
-  for (int p = tid; p < S; p += kCombThreads) {
-    const float lp = lse_part[(static_cast<int64_t>(b) * S + p) * H + h];
-    const float w = (mx == -INFINITY) ? 0.0f : expf(lp - mx);
-    wts[p] = w;
-    z += w;
-  }
+  if (mx != -INFINITY)
+    for (int p = lane; p < S; p += 64) z += expf(lse_at(p) - mx);
   for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
-  if ((tid & 63) == 0) red[tid >> 6] = z;
-  __syncthreads();
-  z = red[0] + red[1];
   const float inv = (z > 0.0f) ? 1.0f / z : 0.0f;
-  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int c0 = tid * 4;
-  for (int p = 0; p < S; ++p) {
-    const float w = wts[p];
-    if (w == 0.0f) continue;
-    const int64_t base = ((static_cast<int64_t>(b) * S + p) * H + h) * kDLatent + c0;
-    if constexpr (PART_DT == MLA_F32) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(u_part) + base);
-      a[0] = fmaf(w, v[0], a[0]);
-      a[1] = fmaf(w, v[1], a[1]);
-      a[2] = fmaf(w, v[2], a[2]);
-      a[3] = fmaf(w, v[3], a[3]);
-    } else {
-      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(u_part) + base);
-      a[0] = fmaf(w, __uint_as_float(v.x << 16), a[0]);
-      a[1] = fmaf(w, __uint_as_float(v.x & 0xFFFF0000u), a[1]);
-      a[2] = fmaf(w, __uint_as_float(v.y << 16), a[2]);
-      a[3] = fmaf(w, __uint_as_float(v.y & 0xFFFF0000u), a[3]);
+  float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p0 = 0; p0 < S; p0 += kG) {
+    // weight of partial p0 + i sits in lane i; empty ranges hold u = 0
+    const int pl = p0 + (lane & (kG - 1));
+    const float wl = (pl < S && mx != -INFINITY) ? expf(lse_at(pl) - mx) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      const float w = __shfl(wl, i);
+      if (p0 + i < S) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = fmaf(w, part_elem<PART_DT>(v[i], k), a[k]);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < kG; ++i)
+      if (p0 + kG + i < S) v[i] = load_part<PART_DT>(u_part, part_at(p0 + kG + i));
   }
   const int64_t ob = (static_cast<int64_t>(b) * H + h) * kDLatent + c0;
+  if constexpr (U_DT == MLA_F32) {
+    float* dst = static_cast<float*>(u) + ob;
+    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv};
+    *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv};
+  } else {
+    u32x4_t w;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) store_elem<U_DT>(u, ob + i, a[i] * inv);
-  if (lse && tid == 0) lse[static_cast<int64_t>(b) * H + h] = (z > 0.0f) ? mx + logf(z) : -INFINITY;
+    for (int k = 0; k < 4; ++k)
+      w[k] = f32_to_bf16(a[2 * k] * inv) | (static_cast<uint32_t>(f32_to_bf16(a[2 * k + 1] * inv)) << 16);
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(u) + ob) = w;
+  }
+  if (lse && lane == 0) lse[static_cast<int64_t>(b) * H + h] = (z > 0.0f) ? mx + logf(z) : -INFINITY;
 }
 
 // ================================================================ absorb
@@ -738,6 +871,209 @@ __global__ __launch_bounds__(kMaxDHead) void up_proj_kernel(const void* u, const
     store_elem<O_DT>(o, (static_cast<int64_t>(b0 + bb) * H + h) * d_v + v, acc[bb]);
 }
 
+// ================================================================ absorb (MFMA)
+//
+// bf16 queries and W_UK: per head h, q̃ᵀ[c][b] = Σ_n W_UK[h][n][c] q_nope[b][h][n] on
+// v_mfma_f32_32x32x16_bf16 (M = 32 latent columns, N = 32 sequences, K = n).  The
+// contraction runs over W_UK's row axis, so a [d_nope x 128] column slab of W_UK[h]
+// is staged in LDS (rows padded to 288 B) and read with transposing LDS reads; the
+// query operand is 16 contiguous bytes of q_nope per lane.  Grid: (head, 4 slabs of
+// 128 columns); wave w owns columns 32w..32w+31 of its slab.
+
+constexpr int kProjThreads = 256;
+constexpr int kAbsRowBytes = 128 * 2 + 32;
+
+template <int OUT_DT>
+__global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_t* q_nope,
+                                                                  const void* q_rope,
+                                                                  const uint16_t* w_uk, void* q_abs,
+                                                                  int B, int H, int d_nope) {
+  __shared__ __attribute__((aligned(16))) uint8_t wt[kMaxDHead * kAbsRowBytes];
+  const int h = blockIdx.x;
+  const int c_slab = blockIdx.y * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, bl = lane & 31;
+  // Every independent load is issued before the first wait: the W_UK slab
+  // W_UK[h][0:d_nope][c_slab : c_slab+128] (16 chunks of 16 B per row), the
+  // query operands of the first tile of 32 sequences, and (slab 0) the RoPE
+  // rows that are copied through.
+  const uint16_t* wsrc = w_uk + static_cast<int64_t>(h) * d_nope * kDLatent + c_slab;
+  constexpr int kStage = kMaxDHead * 16 / kProjThreads;  // 16 chunks per thread at most
+  u32x4_t st[kStage];
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const int q = i * kProjThreads + tid;
+    if (q < d_nope * 16)
+      st[i] = *reinterpret_cast<const u32x4_t*>(wsrc + static_cast<int64_t>(q >> 4) * kDLatent +
+                                                 (q & 15) * 8);
+  }
+  auto load_q = [&](bf16x8_t (&bq)[kMaxDHead / 16], int b0) {
+    const int b = b0 + bl;
+    const uint16_t* qrow = q_nope + (static_cast<int64_t>(b < B ? b : 0) * H + h) * d_nope + 8 * g;
+#pragma unroll
+    for (int k = 0; k < kMaxDHead / 16; ++k)
+      bq[k] = (b < B && 16 * k < d_nope) ? *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k)
+                                         : bf16x8_t{};
+  };
+  bf16x8_t bq[kMaxDHead / 16];
+  load_q(bq, 0);
+  // RoPE rows: 8 chunks of 16 B per sequence
+  const bool rope_copy = blockIdx.y == 0 && tid < B * (kDRope / 8);
+  u32x4_t rv = u32x4_t{0u, 0u, 0u, 0u};
+  if (rope_copy)
+    rv = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q_rope) +
+                                           (static_cast<int64_t>(tid >> 3) * H + h) * kDRope +
+                                           8 * (tid & 7));
+#pragma unroll
+  for (int i = 0; i < kStage; ++i) {
+    const int q = i * kProjThreads + tid;
+    if (q < d_nope * 16) *reinterpret_cast<u32x4_t*>(wt + (q >> 4) * kAbsRowBytes + (q & 15) * 16) = st[i];
+  }
+  __syncthreads();
+  // A operand (M = c, K = n) by transposing reads: lane (G, e, q4) points at
+  // row n0 + 8*(G/2) + e (+4), columns 32*wave + 16*(G%2) + 4*q4
+  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
+  const uint8_t* abase = wt + (8 * (G >> 1) + e) * kAbsRowBytes + (32 * wave + 16 * (G & 1) + 4 * q4) * 2;
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    if (b0 > 0) load_q(bq, b0);
+    const int b = b0 + bl;
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxDHead / 16; ++k) {
+      if (16 * k < d_nope) {
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t*)(abase + 16 * k * kAbsRowBytes));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t*)(abase + (16 * k + 4) * kAbsRowBytes));
+        const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[k], acc, 0, 0, 0);
+      }
+    }
+    // accumulator: column b, rows c = 8*(r/4) + 4*g + r%4 of the wave's 32 columns
+    if (b < B) {
+      const int64_t ob = (static_cast<int64_t>(b) * H + h) * kRowElems + c_slab + 32 * wave;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int c = 8 * r4 + 4 * g;
+        if constexpr (OUT_DT == MLA_F32) {
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(q_abs) + ob + c) =
+              f32x4_t{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+        } else {
+          const uint32_t w0 = f32_to_bf16(acc[4 * r4]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 1])) << 16);
+          const uint32_t w1 = f32_to_bf16(acc[4 * r4 + 2]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 3])) << 16);
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(q_abs) + ob + c) = u32x2_t{w0, w1};
+        }
+      }
+    }
+  }
+  // the RoPE part is carried unchanged (slab 0 copies it; more rows than
+  // threads only when B > 32)
+  if (blockIdx.y == 0) {
+    for (int i = tid; i < B * (kDRope / 8); i += kProjThreads) {
+      const int b = i >> 3, j = 8 * (i & 7);
+      const u32x4_t v = (i == tid && rope_copy)
+                            ? rv
+                            : *reinterpret_cast<const u32x4_t*>(
+                                  static_cast<const uint16_t*>(q_rope) +
+                                  (static_cast<int64_t>(b) * H + h) * kDRope + j);
+      const int64_t ob = (static_cast<int64_t>(b) * H + h) * kRowElems + kDLatent + j;
+      if constexpr (OUT_DT == MLA_F32) {
+        float* dst = static_cast<float*>(q_abs) + ob;
+        *reinterpret_cast<f32x4_t*>(dst) =
+            f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                    __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+        *reinterpret_cast<f32x4_t*>(dst + 4) =
+            f32x4_t{__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                    __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u)};
+      } else {
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(q_abs) + ob) = v;
+      }
+    }
+  }
+}
+
+// ================================================================ up-projection (MFMA)
+//
+// bf16 u and W_UV: per head h, oᵀ[v][b] = Σ_c W_UV[h][v][c] u[b][h][c] on
+// v_mfma_f32_32x32x16_bf16 (M = 32 value rows, N = 32 sequences, K = c).  Both
+// operands are contiguous along c.  One workgroup (2 waves) per (head, 64
+// value rows): each wave keeps its 32 rows of W_UV (32 x 512) in VGPRs, loaded
+// straight from global memory, while the 32 x 512 tile of u rows is staged in
+// LDS (rows padded by 16 bytes) by both waves; all of these loads are issued
+// before the first wait.  Sequences are walked in tiles of 32.
+
+constexpr int kUpThreads = 128;
+constexpr int kUpRow = kDLatent * 2 + 16;  // padded LDS row of u
+
+template <int O_DT>
+__global__ __launch_bounds__(kUpThreads) void up_proj_mfma_kernel(const uint16_t* u,
+                                                                 const uint16_t* w_uv, void* o,
+                                                                 int B, int H, int d_v) {
+  __shared__ __attribute__((aligned(16))) uint8_t us[32 * kUpRow];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int v0 = blockIdx.y * 64 + wave * 32;
+  const int v = v0 + l32;
+  const bool vv = v < d_v;
+  bf16x8_t wa[kDLatent / 16];
+  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * d_v + (vv ? v : 0)) * kDLatent + 8 * g;
+#pragma unroll
+  for (int k = 0; k < kDLatent / 16; ++k)
+    wa[k] = vv ? *reinterpret_cast<const bf16x8_t*>(wrow + 16 * k) : bf16x8_t{};
+  for (int b0 = 0; b0 < B; b0 += 32) {
+    // stage u rows b0 .. b0+31 of head h: 32 x 64 chunks of 16 B, 16 per thread
+    u32x4_t st[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = i * kUpThreads + tid, r = q >> 6, cc = q & 63;
+      st[i] = (b0 + r < B) ? *reinterpret_cast<const u32x4_t*>(
+                                 u + (static_cast<int64_t>(b0 + r) * H + h) * kDLatent + cc * 8)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (b0 > 0) __syncthreads();  // previous tile fully read
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = i * kUpThreads + tid, r = q >> 6, cc = q & 63;
+      *reinterpret_cast<u32x4_t*>(us + r * kUpRow + cc * 16) = st[i];
+    }
+    __syncthreads();
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const uint8_t* urow = us + l32 * kUpRow + 16 * g;
+#pragma unroll
+    for (int k = 0; k < kDLatent / 16; ++k)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          wa[k], *reinterpret_cast<const bf16x8_t*>(urow + 32 * k), acc, 0, 0, 0);
+    // accumulator: column b = b0 + l32, rows v0 + 8*(r/4) + 4*g + r%4
+    const int b = b0 + l32;
+    if (b < B) {
+      const int64_t ob = (static_cast<int64_t>(b) * H + h) * d_v;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int vr = v0 + 8 * r4 + 4 * g;
+        if (vr + 3 < d_v && (d_v & 3) == 0) {
+          if constexpr (O_DT == MLA_F32) {
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + ob + vr) =
+                f32x4_t{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+          } else {
+            const uint32_t w0 = f32_to_bf16(acc[4 * r4]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 1])) << 16);
+            const uint32_t w1 = f32_to_bf16(acc[4 * r4 + 2]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 3])) << 16);
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + ob + vr) = u32x2_t{w0, w1};
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (vr + k < d_v) store_elem<O_DT>(o, ob + vr + k, acc[4 * r4 + k]);
+        }
+      }
+    }
+  }
+}
+
 mla_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
@@ -758,8 +1094,21 @@ extern "C" mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const vo
   if (st != MLA_OK || B == 0) return st;
   if (q_abs_dt == MLA_FP8_E4M3) return MLA_E_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(dims->heads, (B + kAbsBatch - 1) / kAbsBatch);
   const int H = dims->heads, dn = dims->d_nope;
+  if (q_dt == MLA_BF16 && w_dt == MLA_BF16 && dn % 16 == 0 &&
+      (q_abs_dt == MLA_BF16 || q_abs_dt == MLA_F32) &&
+      reinterpret_cast<uintptr_t>(q_nope) % 16 == 0 && reinterpret_cast<uintptr_t>(w_uk) % 16 == 0 &&
+      reinterpret_cast<uintptr_t>(q_rope) % 16 == 0) {
+    const dim3 g2(H, kDLatent / 128);
+    if (q_abs_dt == MLA_BF16)
+      absorb_mfma_kernel<MLA_BF16><<<g2, kProjThreads, 0, s>>>(
+          static_cast<const uint16_t*>(q_nope), q_rope, static_cast<const uint16_t*>(w_uk), q_abs, B, H, dn);
+    else
+      absorb_mfma_kernel<MLA_F32><<<g2, kProjThreads, 0, s>>>(
+          static_cast<const uint16_t*>(q_nope), q_rope, static_cast<const uint16_t*>(w_uk), q_abs, B, H, dn);
+    return launch_status();
+  }
+  const dim3 grid(dims->heads, (B + kAbsBatch - 1) / kAbsBatch);
 #define MLA_ABS(QD, WD, OD)                                                                     \
   if (q_dt == QD && w_dt == WD && q_abs_dt == OD) {                                             \
     absorb_kernel<QD, WD, OD><<<grid, kAbsThreads, 0, s>>>(q_nope, q_rope, w_uk, q_abs,         \
@@ -811,10 +1160,10 @@ extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid = static_cast<unsigned>(nblk);
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
-  if (!fp8 && part_dt == MLA_F32) decode_mfma_kernel<false, MLA_F32><<<grid, kThreads, 0, s>>>(P);
-  else if (!fp8) decode_mfma_kernel<false, MLA_BF16><<<grid, kThreads, 0, s>>>(P);
-  else if (part_dt == MLA_F32) decode_mfma_kernel<true, MLA_F32><<<grid, kThreads, 0, s>>>(P);
-  else decode_mfma_kernel<true, MLA_BF16><<<grid, kThreads, 0, s>>>(P);
+  if (!fp8 && part_dt == MLA_F32) decode_mfma_kernel<false, MLA_F32><<<grid, kThreads, 0, s>>>(P, cache->block_table);
+  else if (!fp8) decode_mfma_kernel<false, MLA_BF16><<<grid, kThreads, 0, s>>>(P, cache->block_table);
+  else if (part_dt == MLA_F32) decode_mfma_kernel<true, MLA_F32><<<grid, kThreads, 0, s>>>(P, cache->block_table);
+  else decode_mfma_kernel<true, MLA_BF16><<<grid, kThreads, 0, s>>>(P, cache->block_table);
   return launch_status();
 }
 
@@ -827,12 +1176,11 @@ extern "C" mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t n
   const int H = dims->heads;
   const int64_t nblk = static_cast<int64_t>(B) * H;
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
-  const size_t shm = sizeof(float) * num_splits;
   const unsigned grid = static_cast<unsigned>(nblk);
 #define MLA_COMB(PD, UD)                                                                       \
   if (part_dt == PD && u_dt == UD) {                                                           \
-    combine_kernel<PD, UD><<<grid, kCombThreads, shm, s>>>(u_part, lse_part, u, lse, H,        \
-                                                           num_splits);                        \
+    combine_kernel<PD, UD><<<grid, kCombThreads, 0, s>>>(u_part, lse_part, u, lse, H,          \
+                                                         num_splits);                          \
     return launch_status();                                                                    \
   }
   MLA_COMB(MLA_F32, MLA_F32)
@@ -850,6 +1198,17 @@ extern "C" mla_status_t mla_up_proj(const mla_dims_t* dims, int32_t B, const voi
   if (st != MLA_OK || B == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int H = dims->heads, dv = dims->d_v;
+  if (u_dt == MLA_BF16 && w_dt == MLA_BF16 && reinterpret_cast<uintptr_t>(u) % 16 == 0 &&
+      reinterpret_cast<uintptr_t>(w_uv) % 16 == 0) {
+    const dim3 g2(H, (dv + 63) / 64);
+    if (o_dt == MLA_BF16)
+      up_proj_mfma_kernel<MLA_BF16><<<g2, kUpThreads, 0, s>>>(
+          static_cast<const uint16_t*>(u), static_cast<const uint16_t*>(w_uv), o, B, H, dv);
+    else
+      up_proj_mfma_kernel<MLA_F32><<<g2, kUpThreads, 0, s>>>(
+          static_cast<const uint16_t*>(u), static_cast<const uint16_t*>(w_uv), o, B, H, dv);
+    return launch_status();
+  }
   const dim3 grid(H, (B + kUpBatch - 1) / kUpBatch);
 #define MLA_UP(UD, WD, OD)                                                                      \
   if (u_dt == UD && w_dt == WD && o_dt == OD) {                                                 \
