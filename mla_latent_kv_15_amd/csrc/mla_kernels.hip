@@ -175,16 +175,17 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // s of token t = s / 72 holds chunk (s % 72) ^ swz(t).  The loads are issued as
 // inline asm: the compiler then does not know they write LDS and does not wait
 // for them before every LDS read (it cannot prove the reads do not alias); the
-// kernel waits for them itself.  The per-lane source offsets are recomputed
-// for every tile from an opaque copy of the lane id, so the compiler does not
-// keep nine of them alive across the loop.
+// kernel waits for them itself.
 __device__ inline void tile_dma_bf16(const DecodeParams& P, const int32_t* __restrict__ block_table,
                                      uint32_t lds_tile, int b, int t0, int nvalid, int wave,
                                      int lane) {
   const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
   const uint8_t* base = P.rows + row0 * kRowBytes;
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
+  // the lane id is recomputed here (mbcnt) rather than kept live across the loop
+  (void)lane;
+  int ln;  // volatile: neither this nor the offsets below are hoisted out of the tile loop
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  wave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: slot bases stay scalar
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
     const int slot = (i * kWaves + wave) * 64 + ln;
@@ -492,6 +493,325 @@ void decode_mfma_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
     // barriers).  The votes go to the buffer that tile `ntiles` would use:
     // nothing is loaded into it and no wave reads it any more.
     int* votes = reinterpret_cast<int*>(smem + (ntiles & (kBufs - 1)) * kTileBytes);
+    const int any_wave = __any(overflow) ? 1 : 0;
+    if (lane == 0) votes[wave] = any_wave;
+    __syncthreads();
+    const int again = votes[0] | votes[1] | votes[2] | votes[3];
+    __syncthreads();
+    if (!again) break;
+    m_ref = m_seen;
+  }
+
+  // ---- epilogue.  Normalisers of all head blocks via LDS (the tile buffers
+  //      are free now): linv[32*hb + hl] = 1 / Σ p of that head.
+  float* linv = reinterpret_cast<float*>(smem);
+  uint8_t* stage = smem + 1024;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qk_wave) {
+    if (g == 0) {
+      linv[wave * kHeadsPerWave + hl] = 1.0f / l_tot;
+      P.lse_part[row_base + wave * kHeadsPerWave + hl] = (m_ref + log2f(l_tot)) * kLn2;
+    }
+  }
+  __syncthreads();
+  // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  // Uᵀ register r of block (hb, cbl) in lane (hl, g) is column
+  // 128*wave + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
+  // wave stages one head block (32 rows x 128 columns) at a time in its own
+  // LDS region and writes 256 contiguous bytes per row.
+  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
+  constexpr int kColsRound = 256 / kEsz;                  // 128 bf16 / 64 fp32 columns
+  constexpr int kStageRow = kColsRound * kEsz + 16;       // padded: rows start 4 banks apart
+  uint8_t* W = stage + wave * kHeadsPerWave * kStageRow;
+#pragma unroll
+  for (int hb = 0; hb < kWaves; ++hb) {
+    if (hb < nhb) {
+      const float inv = linv[hb * kHeadsPerWave + hl];
+#pragma unroll
+      for (int half = 0; half < 128 / kColsRound; ++half) {
+#pragma unroll
+        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
+          const int cbl = half * (kColsRound / 32) + cbl2;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
+            const f32x16_t& A = acc[4 * hb + cbl];
+            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
+            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
+            uint8_t* wp = W + hl * kStageRow + c * kEsz;
+            if constexpr (PART_DT == MLA_F32) {
+              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
+            } else {
+              const uint32_t w0 = f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
+              const uint32_t w1 = f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{w0, w1};
+            }
+          }
+        }
+        // one wave's LDS operations complete in order: no barrier is needed
+        asm volatile("" ::: "memory");
+        // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
+        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
+                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * wave) * kEsz +
+                       half * (kColsRound * kEsz);
+#pragma unroll
+        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
+          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
+                                      (lane & 15) * 16) = v;
+        }
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+}
+
+// ================================================================ decode (bf16, pipelined)
+//
+// The bf16 cache path of mla_decode, software-pipelined across tiles.  One
+// workgroup = one (sequence b, split range p, group of up to 128 heads); wave w
+// computes QK and softmax for head block w (32 heads) and PV for every head
+// block over latent columns [128 w, 128 w + 128).  Iteration i:
+//   1. wait until tile i+1 has landed; barrier.  The barrier also certifies
+//      that every wave has published the probabilities P(i) and finished
+//      iteration i-1, so tile i-1's buffer and P(i-1)'s buffer are free;
+//   2. issue the loads of tile i+3 into tile i-1's buffer;
+//   3. PV(i) and QK(i+1) alternate MFMA by MFMA: the 36 dependent QK steps
+//      hide behind PV's 16 independent accumulator chains, and the LDS reads
+//      of both stay in flight together;
+//   4. softmax of tile i+1, publish P(i+1).
+// Tiles (4 x 36 KiB) and two probability buffers (2 x 8 KiB) fill the 160 KiB
+// of LDS.  Softmax reference and the exact redo pass are as in the fp8 path.
+
+struct QkState {
+  f32x16_t s;
+};
+
+template <int PART_DT>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1)))
+void decode_bf16_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNBuf * kTileBytes + 2 * kPBufBytes];
+  uint8_t* pbuf = smem + kNBuf * kTileBytes;
+
+  const int nwork = P.B * P.S * P.HG;
+  const int wid = xcd_remap(blockIdx.x, nwork);
+  const int hg = wid % P.HG;
+  const int bp = wid / P.HG;
+  const int p = bp % P.S;
+  const int b = bp / P.S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane & 31;
+  const int g = lane >> 5;
+  const int hbase = hg * kHeadsPerBlock;
+  const int nhb = min(kWaves, (P.H - hbase) / kHeadsPerWave);  // workgroup-uniform
+  const bool qk_wave = wave < nhb;                              // wave-uniform
+  const int h = hbase + wave * kHeadsPerWave + hl;
+
+  const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
+  const int t_begin = p * P.chunk;
+  const int t_end = min(t_begin + P.chunk, L);
+  const int64_t row_base = (static_cast<int64_t>(b) * P.S + p) * P.H + hbase;
+
+  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
+    if (qk_wave) {
+      const int64_t r = row_base + wave * kHeadsPerWave + hl;
+      for (int c = g; c < kDLatent; c += 2) store_elem<PART_DT>(P.u_part, r * kDLatent + c, 0.0f);
+      if (g == 0) P.lse_part[r] = -INFINITY;
+    }
+    return;
+  }
+
+  // transposing-read geometry of the PV A operand (see decode_mfma_kernel)
+  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
+  const int tr_row = 4 * (G >> 1) + e;
+  const int tr_key = swz(tr_row);
+  const int tr_x = 2 * (G & 1) + (q4 >> 1);
+  const int tr_byte = 8 * (q4 & 1);
+  const int tr_off[2] = {((0 + tr_x) ^ tr_key) << 4, ((4 + tr_x) ^ tr_key) << 4};
+  int qk_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qk_off[i] = ((2 * i + g) ^ swz(hl)) << 4;
+
+  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
+  f32x16_t acc[kWaves * 4];
+  bf16x8_t qreg[kRowElems / 16];
+  const bf16x8_t* qrow = reinterpret_cast<const bf16x8_t*>(
+      static_cast<const uint16_t*>(P.q_abs) +
+      (static_cast<int64_t>(b) * P.H + (qk_wave ? h : hbase)) * kRowElems);
+
+  auto dma = [&](int tile) {
+    const int tt = t_begin + tile * kTileTokens;
+    tile_dma_bf16(P, block_table, lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes, b, tt,
+                  min(kTileTokens, t_end - tt), wave, lane);
+  };
+  // QK of tile `tile` restricted to k-steps [k0, k1): issued MFMA by MFMA by the
+  // callers below.  Operand reads run kRing steps ahead.
+  constexpr int kRing = 2;
+  auto qk_read = [&](const uint8_t* arow, int kk) {
+    return *reinterpret_cast<const bf16x8_t*>(arow + qk_off[kk & 3] + (kk >> 2) * 128);
+  };
+  // softmax of one tile's Sᵀ; publishes the probabilities into PB
+  auto softmax_publish = [&](f32x16_t& s, int tile, int pass, int& overflow, uint8_t* PB) {
+    const int nvalid = t_end - (t_begin + tile * kTileTokens);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] *= P.scale_log2;
+    if (nvalid < kTileTokens) {  // partial last tile: token 8*(r/4) + 4*g + r%4 present?
+      uint32_t present = ((1u << nvalid) - 1u) >> (4 * g);
+      asm volatile("" : "+v"(present));  // evaluated here, not hoisted as 16 lane masks
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[r] = ((present >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (pass == 0 && tile == 0) m_ref = mx;
+    m_seen = fmaxf(m_seen, mx);
+    overflow |= (mx > m_ref + kRefSlack);
+    bf16x8_t pk[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = exp2f(s[r] - m_ref);
+      l_run += pr;
+      pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
+    }
+    *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + lane * 16) = pk[0];
+    *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + 1024 + lane * 16) = pk[1];
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int k = 0; k < kWaves * 4; ++k) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
+      asm volatile("" : "+a"(acc[k]));
+    }
+    asm volatile("s_nop 4");  // accumulator writes -> first (inline-asm) MFMA read
+    l_run = 0.0f;
+    int overflow = 0;
+
+    // ---- prologue: tile 0, the queries, tiles 1 and 2
+    dma(0);
+    if (pass == 0 && qk_wave) {
+#pragma unroll
+      for (int kk = 0; kk < kRowElems / 16; ++kk) qreg[kk] = qrow[2 * kk + g];
+      // consume the query loads once, here (see decode_mfma_kernel)
+#pragma unroll
+      for (int kk = 0; kk < kRowElems / 16; ++kk) asm volatile("" : "+v"(qreg[kk]));
+    }
+    if (ntiles > 1) dma(1);
+    if (ntiles > 2) dma(2);
+    if (ntiles > 2)
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (ntiles > 1)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    if (qk_wave) {
+      const uint8_t* arow = smem + hl * kRowBytes;
+      f32x16_t s;
+      bf16x8_t ring[kRing];
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) ring[i] = qk_read(arow, i);
+#pragma unroll
+      for (int kk = 0; kk < kRowElems / 16; ++kk) {
+        const bf16x8_t a = ring[kk % kRing];
+        if (kk + kRing < kRowElems / 16) ring[kk % kRing] = qk_read(arow, kk + kRing);
+        if (kk == 0)
+          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qreg[kk]));
+        else
+          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qreg[kk]));
+      }
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+      softmax_publish(s, 0, pass, overflow, pbuf);
+    }
+
+    for (int i = 0; i < ntiles; ++i) {
+      // 1. tile i+1 landed (tile i+2 may stay in flight); barrier
+      if (i + 2 < ntiles)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
+      // 2. tile i+3 into tile i-1's buffer
+      if (i + 3 < ntiles) dma(i + 3);
+      // 3. PV(i) with QK(i+1)
+      const uint8_t* T = smem + (i & (kNBuf - 1)) * kTileBytes;
+      const uint8_t* PB = pbuf + (i & 1) * kPBufBytes;
+      const bool do_qk = qk_wave && (i + 1 < ntiles);  // wave-uniform
+      const uint8_t* arow = smem + ((i + 1) & (kNBuf - 1)) * kTileBytes + hl * kRowBytes;
+      // PV(i) in two halves of 64 columns: per half, the transposed tile
+      // operands of 2 column blocks (x 2 token halves) and, per head block, the
+      // published probabilities.  QK(i+1) steps are interleaved throughout.
+      const uint8_t* r0 = T + tr_row * kRowBytes + tr_byte;
+      auto load_av = [&](bf16x8_t (&av)[2][2], int half) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int cb = 4 * wave + 2 * half + c2;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 128 + 16 * j * kRowBytes;
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
+            const bf16x4_t hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + 8 * kRowBytes));
+            av[c2][j] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        }
+      };
+      // QK runs unconditionally (a branch per step would serialise the operand
+      // reads); when there is no tile i+1, or the wave has no heads, it reads
+      // stale LDS into a score block that is dropped.
+      f32x16_t s;
+      bf16x8_t ring[kRing];
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) ring[k] = qk_read(arow, k);
+      bf16x8_t av[2][2];
+      load_av(av, 0);
+      bf16x8_t pb0 = *reinterpret_cast<const bf16x8_t*>(PB + lane * 16);
+      bf16x8_t pb1 = *reinterpret_cast<const bf16x8_t*>(PB + 1024 + lane * 16);
+      // step st: QK k-step st (0..35) and PV step st (0..31): half st / 16,
+      // head block (st / 4) % 4, column block 2 * half + (st / 2) % 2, token half st % 2
+#pragma unroll
+      for (int st = 0; st < kRowElems / 16; ++st) {
+        {
+          const bf16x8_t a = ring[st % kRing];
+          if (st + kRing < kRowElems / 16) ring[st % kRing] = qk_read(arow, st + kRing);
+          if (st == 0)
+            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qreg[st]));
+          else
+            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qreg[st]));
+        }
+        if (st < 32) {
+          const int half = st >> 4, hb = (st >> 2) & 3, c2 = (st >> 1) & 1, j = st & 1;
+          // head blocks beyond nhb multiply stale probabilities into
+          // accumulators that are never stored: no branch in the MFMA stream
+          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+              : "+a"(acc[4 * hb + 2 * half + c2]) : "v"(av[c2][j]), "v"(j ? pb1 : pb0));
+          if ((st & 3) == 3 && st < 31) {  // next (half, head block): its probabilities
+            const int nhb2 = ((st + 1) >> 2) & 3;
+            pb0 = *reinterpret_cast<const bf16x8_t*>(PB + nhb2 * 2048 + lane * 16);
+            pb1 = *reinterpret_cast<const bf16x8_t*>(PB + nhb2 * 2048 + 1024 + lane * 16);
+          }
+          if (st == 15) load_av(av, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // 4. softmax of tile i+1, publish P(i+1)
+      if (do_qk) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+        softmax_publish(s, i + 1, pass, overflow, pbuf + ((i + 1) & 1) * kPBufBytes);
+      }
+    }
+    // same vote as decode_mfma_kernel: tile `ntiles` would use a buffer nobody reads
+    int* votes = reinterpret_cast<int*>(smem + (ntiles & (kNBuf - 1)) * kTileBytes);
     const int any_wave = __any(overflow) ? 1 : 0;
     if (lane == 0) votes[wave] = any_wave;
     __syncthreads();
@@ -1160,8 +1480,8 @@ extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid = static_cast<unsigned>(nblk);
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
-  if (!fp8 && part_dt == MLA_F32) decode_mfma_kernel<false, MLA_F32><<<grid, kThreads, 0, s>>>(P, cache->block_table);
-  else if (!fp8) decode_mfma_kernel<false, MLA_BF16><<<grid, kThreads, 0, s>>>(P, cache->block_table);
+  if (!fp8 && part_dt == MLA_F32) decode_bf16_kernel<MLA_F32><<<grid, kThreads, 0, s>>>(P, cache->block_table);
+  else if (!fp8) decode_bf16_kernel<MLA_BF16><<<grid, kThreads, 0, s>>>(P, cache->block_table);
   else if (part_dt == MLA_F32) decode_mfma_kernel<true, MLA_F32><<<grid, kThreads, 0, s>>>(P, cache->block_table);
   else decode_mfma_kernel<true, MLA_BF16><<<grid, kThreads, 0, s>>>(P, cache->block_table);
   return launch_status();
