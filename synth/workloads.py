@@ -69,7 +69,7 @@ WORKLOADS = {
         out_dtype="f32", seq_len=512, num_splits=1, seed=BASE_SEED + 1,
         description="tiny fp32 decode: B=1, h=16, L=512"),
     "dsv2_b32_l2k": Workload(
-        "dsv2_b32_l2k", batch=32, seq_len=2048, num_splits=8, seed=BASE_SEED + 2,
+        "dsv2_b32_l2k", batch=32, seq_len=2048, num_splits=4, seed=BASE_SEED + 2,
         description="DeepSeek-V2 geometry bf16 decode: B=32, h=128, L=2048"),
     "long_b4_l32k": Workload(
         "long_b4_l32k", batch=4, seq_len=32768, num_splits=64, seed=BASE_SEED + 3,
