@@ -1406,6 +1406,417 @@ void decode_h64_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
   }
 }
 
+// ================================================================ decode (bf16, warp-specialised)
+//
+// Same work unit as decode_h64_kernel (sequence b, split range p, 64 heads) with
+// 8 waves, two per SIMD, in two roles:
+//   * QK waves 0..3 (head block w & 1, token half w >> 1) hold their absorbed
+//     queries in AGPRs, compute the scores of tile i+1 with
+//     v_mfma_f32_16x16x32_bf16, run the softmax and publish the bf16
+//     probabilities;
+//   * PV waves 4..7 (latent columns 128(w-4)..+127 of all 64 heads) stream the
+//     tiles into LDS and accumulate U^T of tile i in AGPRs with
+//     v_mfma_f32_32x32x16_bf16.
+// Each SIMD runs one wave of each role, so the matrix core alternates between
+// the two while the other role waits on LDS or runs the softmax.  The roles
+// meet at one barrier per tile; their register footprints (queries vs
+// accumulators) share the same AGPRs because each role's code is a separate
+// region of the kernel.
+
+constexpr int kWsThreads = 512;
+
+template <int PART_DT>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads),
+                          amdgpu_waves_per_eu(2, 2)))
+void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kX64Off + 1024];
+  uint8_t* pbuf = smem + kNBuf * kTileBytes;
+  float* xch = reinterpret_cast<float*>(smem + kX64Off);  // [2][64] per-head exchange
+  int* votes = reinterpret_cast<int*>(smem + kX64Off + 512);
+  float* linv = reinterpret_cast<float*>(smem);  // epilogue: 1 / l per head (tile buffer 0)
+
+  const int nwork = P.B * P.S * P.HG;
+  const int wid = xcd_remap(blockIdx.x, nwork);
+  const int hg = wid % P.HG;
+  const int bp = wid / P.HG;
+  const int p = bp % P.S;
+  const int b = bp / P.S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+  const bool is_qk = wave < 4;                                // wave-uniform
+  const int rw = wave & 3;                                    // index within the role
+  const int hbase = hg * kH64;
+  const int nhb = min(kH64Blocks, (P.H - hbase) / kHeadsPerWave);  // 1 or 2
+
+  const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
+  const int t_begin = p * P.chunk;
+  const int t_end = min(t_begin + P.chunk, L);
+  const int64_t row_base = (static_cast<int64_t>(b) * P.S + p) * P.H + hbase;
+
+  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
+    if (!is_qk) {
+      const int pt = tid - 256;
+      for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
+        store_elem<PART_DT>(P.u_part, row_base * kDLatent + idx, 0.0f);
+      if (pt < nhb * kHeadsPerWave) P.lse_part[row_base + pt] = -INFINITY;
+    }
+    return;
+  }
+  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
+
+  // all s_barriers below are issued by both roles in the same order:
+  //   Q1 Q2 | per pass: T0 [AM AM] B_0..B_{n-1} V1 V2 [AM AM] | E1 E2
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  if (is_qk) {
+    // ------------------------------------------------------------ QK role
+    const int qhb = rw & 1, th = rw >> 1;
+    const bool active = qhb < nhb;  // wave-uniform
+    const int n16 = lane & 15, kg = lane >> 4;
+    const int qk_row = ((n16 >> 3) * kTokGroupBytes) + (n16 & 7) * 128;
+    const int qk_off[2] = {(kg ^ swz(n16 & 7)) << 4, ((4 + kg) ^ swz(n16 & 7)) << 4};
+    auto qk_addr = [&](int half, int ks) {
+      return 2 * half * kTokGroupBytes + qk_row + qk_off[ks & 1] + (ks >> 1) * 1024;
+    };
+    float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.0f, 0.0f};
+    // B operands: k-steps < kQkAgpr in AGPRs (the PV role's accumulators use
+    // the same 128 AGPRs), the rest in VGPRs
+    constexpr int kQkAgpr = 14;
+    bf16x8_t qa[kQkAgpr][2];
+    bf16x8_t qv[kQkSteps - kQkAgpr][2];
+
+    barrier();  // Q1: the queries are staged in tile buffers 2 and 3
+    if (active) {
+      const uint8_t* Q = smem + (2 + qhb) * kTileBytes;
+#pragma unroll
+      for (int ks = 0; ks < kQkSteps; ++ks)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (ks < kQkAgpr) {
+            qa[ks][hh] = *reinterpret_cast<const bf16x8_t*>(Q + qk_addr(hh, ks));
+            asm volatile("" : "+a"(qa[ks][hh]));
+          } else {
+            qv[ks - kQkAgpr][hh] = *reinterpret_cast<const bf16x8_t*>(Q + qk_addr(hh, ks));
+            asm volatile("" : "+v"(qv[ks - kQkAgpr][hh]));
+          }
+        }
+    }
+    barrier();  // Q2: staging buffers free
+
+    constexpr int kRing = 6;
+    auto qk_tile = [&](const uint8_t* T, f32x4_t (&s)[2]) {
+      bf16x8_t ring[kRing];
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) ring[k] = *reinterpret_cast<const bf16x8_t*>(T + qk_addr(th, k));
+#pragma unroll
+      for (int ks = 0; ks < kQkSteps; ++ks) {
+        const bf16x8_t a = ring[ks % kRing];
+        if (ks + kRing < kQkSteps)
+          ring[ks % kRing] = *reinterpret_cast<const bf16x8_t*>(T + qk_addr(th, ks + kRing));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (ks == 0)
+            asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(s[hh]) : "v"(a), "a"(qa[ks][hh]));
+          else if (ks < kQkAgpr)
+            asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(s[hh]) : "v"(a), "a"(qa[ks][hh]));
+          else
+            asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                : "+v"(s[hh]) : "v"(a), "v"(qv[ks - kQkAgpr][hh]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+    };
+    auto softmax_publish = [&](f32x4_t (&s)[2], int tile, int& overflow, uint8_t* PB) {
+      const int nvalid = t_end - (t_begin + tile * kTileTokens);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[hh][r] *= P.scale_log2;
+      if (nvalid < kTileTokens) {  // partial last tile: token 16 th + 4 kg + r present?
+        int first = 16 * th + 4 * kg;
+        asm volatile("" : "+v"(first));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[hh][r] = (first + r < nvalid) ? s[hh][r] : -INFINITY;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float mx = fmaxf(fmaxf(s[hh][0], s[hh][1]), fmaxf(s[hh][2], s[hh][3]));
+        m_seen[hh] = fmaxf(m_seen[hh], mx);
+        overflow |= (mx > m_ref[hh] + kRefSlack);
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(s[hh][r] - m_ref[hh]);  // v_exp_f32
+          l_run[hh] += pr[r];
+        }
+        // B-operand slot of token 16th + 4kg + r: k-step th, lane group kg & 1,
+        // slots 4 (kg >> 1) + r of head 32 qhb + 16 hh + n16
+        *reinterpret_cast<u32x2_t*>(PB + (((th * 2 + qhb) * 2 + (kg & 1)) * 32 + 16 * hh + n16) * 16 +
+                                    8 * (kg >> 1)) =
+            u32x2_t{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+      }
+    };
+    // per-head maximum over the lane groups and the two token halves
+    auto agree_max = [&](float (&m)[2]) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        m[hh] = fmaxf(m[hh], __shfl_xor(m[hh], 16));
+        m[hh] = fmaxf(m[hh], __shfl_xor(m[hh], 32));
+      }
+      if (active && kg == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) xch[th * 64 + qhb * 32 + 16 * hh + n16] = m[hh];
+      }
+      barrier();  // AM
+      if (active) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          m[hh] = fmaxf(m[hh], xch[(th ^ 1) * 64 + qhb * 32 + 16 * hh + n16]);
+      }
+      barrier();  // AM
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+      l_run[0] = l_run[1] = 0.0f;
+      int overflow = 0;
+      barrier();  // T0: tile 0 landed
+      f32x4_t s[2];
+      if (active) qk_tile(smem, s);
+      if (pass == 0) {  // reference: maximum of the first tile
+        float mx[2] = {-INFINITY, -INFINITY};
+        if (active) {
+          const int nvalid = t_end - t_begin;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * th + 4 * kg + r < nvalid) mx[hh] = fmaxf(mx[hh], s[hh][r] * P.scale_log2);
+        }
+        agree_max(mx);
+        m_ref[0] = mx[0];
+        m_ref[1] = mx[1];
+      }
+      if (active) softmax_publish(s, 0, overflow, pbuf);
+      for (int i = 0; i < ntiles; ++i) {
+        barrier();  // B_i: P(i) published, tile i+1 landed
+        if (active && i + 1 < ntiles) {
+          qk_tile(smem + ((i + 1) & (kNBuf - 1)) * kTileBytes, s);
+          softmax_publish(s, i + 1, overflow, pbuf + ((i + 1) & 1) * kP64Bytes);
+        }
+      }
+      if (lane == 0) votes[wave] = __any(overflow) ? 1 : 0;
+      barrier();  // V1
+      int again = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) again |= votes[w];
+      barrier();  // V2
+      if (!again) break;
+      agree_max(m_seen);  // redo the range with the range maximum as reference
+      m_ref[0] = m_seen[0];
+      m_ref[1] = m_seen[1];
+    }
+    // l per head: lane groups, then the two token halves
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      l_run[hh] += __shfl_xor(l_run[hh], 16);
+      l_run[hh] += __shfl_xor(l_run[hh], 32);
+    }
+    if (active && kg == 0) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) xch[th * 64 + qhb * 32 + 16 * hh + n16] = l_run[hh];
+    }
+    barrier();  // E1
+    if (active && th == 0 && kg == 0) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int hx = qhb * 32 + 16 * hh + n16;
+        const float l_tot = xch[hx] + xch[64 + hx];
+        linv[hx] = 1.0f / l_tot;
+        P.lse_part[row_base + hx] = (m_ref[hh] + log2f(l_tot)) * kLn2;
+      }
+    }
+    barrier();  // E2
+    return;
+  }
+
+  // -------------------------------------------------------------- PV role
+  const int hl = lane & 31, g = lane >> 5;
+  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
+  const int tr_row = 4 * (G >> 1) + e;
+  const int tr_key = swz(tr_row);
+  const int tr_x = 2 * (G & 1) + (q4 >> 1);
+  const int tr_byte = 8 * (q4 & 1);
+  const int tr_off[2] = {((0 + tr_x) ^ tr_key) << 4, ((4 + tr_x) ^ tr_key) << 4};
+  f32x16_t acc[kH64Blocks * 4];
+
+  auto dma_plan = [&](int tile) {
+    const int tt = t_begin + tile * kTileTokens;
+    const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
+    return rows_dma_plan(P.rows + row0 * kRowBytes, lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes,
+                         min(kTileTokens, t_end - tt), rw);
+  };
+  auto dma = [&](int tile) {
+    const RowsDma d = dma_plan(tile);
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
+  };
+
+  // the queries of both head blocks (32 rows each) into tile buffers 2 and 3,
+  // then tiles 0 and 1
+  const uint8_t* qsrc = static_cast<const uint8_t*>(P.q_abs) +
+                        (static_cast<int64_t>(b) * P.H + hbase) * kRowBytes;
+  for (int hb = 0; hb < nhb; ++hb)
+    rows_dma_g8(qsrc + hb * kHeadsPerWave * kRowBytes, lds_addr(smem) + (2 + hb) * kTileBytes,
+                kTileTokens, rw);
+  dma(0);
+  if (ntiles > 1) dma(1);
+  if (ntiles > 1)
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  barrier();  // Q1
+  barrier();  // Q2
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int k = 0; k < kH64Blocks * 4; ++k) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
+      asm volatile("" : "+a"(acc[k]));
+    }
+    asm volatile("s_nop 4");  // accumulator writes -> first (inline-asm) MFMA read
+    if (pass > 0) {
+      dma(0);
+      if (ntiles > 1) dma(1);
+    }
+    if (ntiles > 2) dma(2);
+    if (ntiles > 2)
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (ntiles > 1)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();  // T0
+    if (pass == 0) {
+      barrier();  // AM
+      barrier();  // AM
+    }
+    for (int i = 0; i < ntiles; ++i) {
+      if (i + 2 < ntiles)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      barrier();  // B_i
+      // tile i+3 into tile i-1's buffer, one wave instruction per MFMA below
+      const bool dnext = i + 3 < ntiles;  // workgroup-uniform
+      RowsDma dp{};
+      if (dnext) dp = dma_plan(i + 3);
+      const uint8_t* T = smem + (i & (kNBuf - 1)) * kTileBytes;
+      const uint8_t* PB = pbuf + (i & 1) * kP64Bytes;
+      const uint8_t* r0 = T + tr_row * 128 + tr_byte;
+      auto load_av = [&](int cbl, int j) {
+        const int cb = 4 * rw + cbl;
+        const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 1024 + 2 * j * kTokGroupBytes;
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
+        const bf16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + kTokGroupBytes));
+        return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      bf16x8_t pb[2][2];  // [token half j][head block]
+      bf16x8_t av[4][2];  // [column block][token half j]
+#pragma unroll
+      for (int cbl = 0; cbl < 4; ++cbl) {
+        av[cbl][0] = load_av(cbl, 0);
+        av[cbl][1] = load_av(cbl, 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          pb[j][hb] = *reinterpret_cast<const bf16x8_t*>(PB + ((j * 2 + hb) * 64 + lane) * 16);
+      // MFMA st: column block st / 4, token half (st / 2) % 2, head block st % 2.
+      // Head blocks beyond nhb multiply stale probabilities into accumulators
+      // that are never stored.
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const int cbl = st >> 2, j = (st >> 1) & 1, hb = st & 1;
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+            : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl][j]), "v"(pb[j][hb]));
+        if (dnext && st < kDmaPerWave) rows_dma_issue(dp, st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (lane == 0) votes[wave] = 0;
+    barrier();  // V1
+    int again = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) again |= votes[w];
+    barrier();  // V2
+    if (!again) break;
+    barrier();  // AM
+    barrier();  // AM
+  }
+
+  barrier();  // E1
+  barrier();  // E2: linv ready
+  // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  // U^T register r of block (hb, cbl) in lane (hl, g) is column
+  // 128*rw + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
+  // wave stages one head block (32 rows x 128 columns) at a time in its own
+  // LDS region (tile buffers 0-1, past linv) and writes 256 contiguous bytes
+  // per row.
+  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
+  constexpr int kColsRound = 256 / kEsz;             // 128 bf16 / 64 fp32 columns
+  constexpr int kStageRow = kColsRound * kEsz + 16;  // padded: rows start 4 banks apart
+  uint8_t* W = smem + 1024 + rw * kHeadsPerWave * kStageRow;
+#pragma unroll
+  for (int hb = 0; hb < kH64Blocks; ++hb) {
+    if (hb < nhb) {
+      const float inv = linv[hb * kHeadsPerWave + hl];
+#pragma unroll
+      for (int half = 0; half < 128 / kColsRound; ++half) {
+#pragma unroll
+        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
+          const int cbl = half * (kColsRound / 32) + cbl2;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
+            const f32x16_t& A = acc[4 * hb + cbl];
+            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
+            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
+            uint8_t* wp = W + hl * kStageRow + c * kEsz;
+            if constexpr (PART_DT == MLA_F32) {
+              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
+            } else {
+              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            }
+          }
+        }
+        // one wave's LDS operations complete in order: no barrier is needed
+        asm volatile("" ::: "memory");
+        // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
+        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
+                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * rw) * kEsz +
+                       half * (kColsRound * kEsz);
+#pragma unroll
+        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
+          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
+                                      (lane & 15) * 16) = v;
+        }
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+}
+
 // ================================================================ decode (fp32)
 //
 // Plain fp32 path for fp32 caches: one workgroup per (b, split, head), 256
@@ -2006,9 +2417,9 @@ extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void
     if (nblk64 > 0x7FFFFFFF) return MLA_E_SHAPE;
     P.HG = HG64;
     if (part_dt == MLA_F32)
-      decode_h64_kernel<MLA_F32><<<static_cast<unsigned>(nblk64), kThreads, 0, s>>>(P, cache->block_table);
+      decode_ws_kernel<MLA_F32><<<static_cast<unsigned>(nblk64), kWsThreads, 0, s>>>(P, cache->block_table);
     else
-      decode_h64_kernel<MLA_BF16><<<static_cast<unsigned>(nblk64), kThreads, 0, s>>>(P, cache->block_table);
+      decode_ws_kernel<MLA_BF16><<<static_cast<unsigned>(nblk64), kWsThreads, 0, s>>>(P, cache->block_table);
   } else if (part_dt == MLA_F32) decode_mfma_kernel<true, MLA_F32><<<grid, kThreads, 0, s>>>(P, cache->block_table);
   else decode_mfma_kernel<true, MLA_BF16><<<grid, kThreads, 0, s>>>(P, cache->block_table);
   return launch_status();
