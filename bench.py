@@ -3,7 +3,7 @@ one MI355X, synthetic inputs, printed as one JSON line.
 
 Timed workload (default): DeepSeek-V2 geometry, bf16 cache and weights with
 fp32 accumulation, batch 32, one query token per sequence, 128 heads,
-d_nope 128, d_rope 64, d_c 512, d_v 128, uniform cache length 2048, 8 split
+d_nope 128, d_rope 64, d_c 512, d_v 128, uniform cache length 2048, 4 split
 ranges per sequence.  A "step" is one decode step of one layer for the whole
 batch; tokens/s = batch / step time.
 
@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--replica-bytes", type=float, default=1.25 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-call-tail", action="store_true",
+                    help="merge and up-project with mla_combine + mla_up_proj")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -143,6 +145,10 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    # tail of the step: with several splits and bf16 W_UV the merge and the
+    # W_UV product run as one launch (mla_combine_up_proj; u is not stored)
+    fused = step.fused_tail(dev.w_uv) and not args.two_call_tail
+
     def one(i, ev=None):
         rp = reps[i % R]
         if ev is not None:
@@ -155,11 +161,18 @@ def main():
                        stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        if S > 1:
-            mla.mla_combine(step.geo, step.u_part, step.lse_part, step.u, step.lse, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
-        mla.mla_up_proj(step.geo, step.u, rp["w_uv"], step.o, stream=stream)
+        if fused:
+            mla.mla_combine_up_proj(step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o,
+                                    stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+        else:
+            if S > 1:
+                mla.mla_combine(step.geo, step.u_part, step.lse_part, step.u, step.lse,
+                                stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+            mla.mla_up_proj(step.geo, step.u, rp["w_uv"], step.o, stream=stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -187,6 +200,13 @@ def main():
     k_med = np.median(ker, axis=0)
     t_decode = float(k_mean[1]) * 1e-3
     t_dc = float(k_mean[1] + k_mean[2]) * 1e-3
+
+    def kernel_table(k):  # ms per launch -> us, keyed by entry point
+        if fused:
+            return {"mla_absorb_q": k[0] * 1e3, "mla_decode": k[1] * 1e3,
+                    "mla_combine_up_proj": k[2] * 1e3}
+        return {"mla_absorb_q": k[0] * 1e3, "mla_decode": k[1] * 1e3,
+                "mla_combine": k[2] * 1e3, "mla_up_proj": k[3] * 1e3}
 
     launch_bytes = cache_bytes  # algorithmic bytes of one mla_decode launch
     achieved = launch_bytes / t_decode / 1e9
@@ -218,10 +238,8 @@ def main():
                    "partials": args.part_dtype, "replicas": R, "parallelism": "none (1 GPU)"},
         "cache_GBps": cache_bytes / t_dc / 1e9,
         "cache_pct_hbm_peak": 100.0 * cache_bytes / t_dc / 1e9 / HBM_PEAK_GBPS,
-        "kernel_us_mean": {"absorb_q": k_mean[0] * 1e3, "decode": k_mean[1] * 1e3,
-                           "combine": k_mean[2] * 1e3, "up_proj": k_mean[3] * 1e3},
-        "kernel_us_median": {"absorb_q": k_med[0] * 1e3, "decode": k_med[1] * 1e3,
-                             "combine": k_med[2] * 1e3, "up_proj": k_med[3] * 1e3},
+        "kernel_us_mean": kernel_table(k_mean),
+        "kernel_us_median": kernel_table(k_med),
         "roofline": {"kernel": "mla_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes},

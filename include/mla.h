@@ -28,6 +28,7 @@
  *
  * The step is four calls, each only enqueued on the caller's HIP stream:
  *     mla_absorb_q  ->  mla_decode  ->  mla_combine  ->  mla_up_proj
+ * (mla_combine_up_proj does the last two in one launch for bf16 W_UV).
  * mla_decode splits every sequence into num_splits token ranges and writes one
  * normalised partial result per range; mla_combine merges them exactly with
  * log-sum-exp weights; with num_splits == 1 the partial already is the final
@@ -161,6 +162,22 @@ mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t num_splits,
 mla_status_t mla_up_proj(const mla_dims_t* dims, int32_t B, const void* u,
                          int32_t u_dt, const void* w_uv, int32_t w_dt, void* o,
                          int32_t o_dt, void* stream);
+
+/* mla_combine followed by mla_up_proj in one launch, without the round trip
+ * of u through memory:
+ *   u[b][i][:]  = merge of the split partials as in mla_combine, rounded to
+ *                 bf16 (the value mla_combine stores for u_dt = BF16)
+ *   o[b][i][v]  = sum_c W_UV[i][v][c] * u[b][i][c]      (fp32 accumulation)
+ * u_part/lse_part as written by mla_decode (part_dt F32 or BF16); w_uv
+ * [h][d_v][d_latent] BF16 only, d_v a multiple of 16; o [B][h][d_v] in o_dt
+ * (F32 or BF16).  u (BF16 [B][h][d_latent]) and lse (fp32 [B][h]) are
+ * optional copies of the merged values: NULL skips them.  Same conventions
+ * and errors as the two calls it replaces; MLA_E_DTYPE for other dtypes,
+ * MLA_E_SHAPE for d_v % 16 != 0. */
+mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_splits,
+                                 const void* u_part, int32_t part_dt, const float* lse_part,
+                                 const void* w_uv, int32_t w_dt, void* o, int32_t o_dt,
+                                 void* u, float* lse, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mla_status_str(mla_status_t status);

@@ -69,6 +69,9 @@ def lib():
         L.mla_combine.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, f32p, vp, i32, f32p, vp]
         L.mla_up_proj.restype = C.c_int
         L.mla_up_proj.argtypes = [C.POINTER(Dims), i32, vp, i32, vp, i32, vp, i32, vp]
+        L.mla_combine_up_proj.restype = C.c_int
+        L.mla_combine_up_proj.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, f32p, vp, i32, vp,
+                                          i32, vp, f32p, vp]
         L.mla_status_str.restype = C.c_char_p
         L.mla_status_str.argtypes = [C.c_int]
         L.mla_version.restype = C.c_int32
@@ -77,8 +80,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_up_proj", "mla_status_str",
-            "mla_version")
+EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
+            "mla_status_str", "mla_version")
 
 
 def status_str(status: int) -> str:
@@ -190,6 +193,19 @@ def mla_up_proj(geo: Geometry, u: torch.Tensor, w_uv: torch.Tensor, o: torch.Ten
     _check("mla_up_proj", st)
 
 
+def mla_combine_up_proj(geo: Geometry, u_part: torch.Tensor, lse_part: torch.Tensor,
+                        w_uv: torch.Tensor, o: torch.Tensor, u: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    B, S = int(u_part.shape[0]), int(u_part.shape[1])
+    if u is not None and u.dtype != torch.bfloat16:
+        raise TypeError("mla_combine_up_proj stores u as bfloat16 only")
+    d = geo.c()
+    st = lib().mla_combine_up_proj(C.byref(d), B, S, _ptr(u_part), dtype_code(u_part),
+                                   _ptr(lse_part), _ptr(w_uv), dtype_code(w_uv), _ptr(o),
+                                   dtype_code(o), _ptr(u), _ptr(lse), _stream(stream))
+    _check("mla_combine_up_proj", st)
+
+
 def split_chunk(max_seq_len: int, num_splits: int) -> int:
     """Tokens per split range (mirrors the rule stated in include/mla.h)."""
     if max_seq_len <= 0:
@@ -222,9 +238,20 @@ class DecodeStep:
                     else torch.empty(batch, h, dtype=torch.float32, device=device))
         self.o = torch.empty(batch, h, geo.d_v, dtype=out_dtype, device=device)
 
-    def run(self, q_nope, q_rope, w_uk, w_uv, cache: Cache, stream=None) -> torch.Tensor:
+    def fused_tail(self, w_uv: torch.Tensor) -> bool:
+        """Whether run() merges the splits and applies W_UV in one launch
+        (mla_combine_up_proj): several splits, bf16 W_UV and u."""
+        return (self.S > 1 and w_uv.dtype == torch.bfloat16 and self.u.dtype == torch.bfloat16
+                and self.geo.d_v % 16 == 0)
+
+    def run(self, q_nope, q_rope, w_uk, w_uv, cache: Cache, stream=None,
+            fused: bool = True) -> torch.Tensor:
         mla_absorb_q(self.geo, q_nope, q_rope, w_uk, self.q_abs, stream=stream)
         mla_decode(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part, stream=stream)
+        if fused and self.fused_tail(w_uv):
+            mla_combine_up_proj(self.geo, self.u_part, self.lse_part, w_uv, self.o, self.u,
+                                self.lse, stream=stream)
+            return self.o
         if self.S > 1:
             mla_combine(self.geo, self.u_part, self.lse_part, self.u, self.lse, stream=stream)
         mla_up_proj(self.geo, self.u, w_uv, self.o, stream=stream)

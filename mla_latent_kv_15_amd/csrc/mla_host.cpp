@@ -132,6 +132,23 @@ mla_status_t check_up_proj(const mla_dims_t* dims, int32_t B, const void* u,
   return MLA_OK;
 }
 
+mla_status_t check_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_splits,
+                                   const void* u_part, int32_t part_dt, const float* lse_part,
+                                   const void* w_uv, int32_t w_dt, const void* o, int32_t o_dt,
+                                   const void* u) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (B < 0 || num_splits < 1 || num_splits > kMaxSplits) return MLA_E_ARG;
+  if (!valid_dtype(part_dt) || !valid_dtype(w_dt) || !valid_dtype(o_dt)) return MLA_E_ARG;
+  if (B == 0) return MLA_OK;
+  if (!u_part || !lse_part || !w_uv || !o) return MLA_E_ARG;
+  if (part_dt == MLA_FP8_E4M3 || o_dt == MLA_FP8_E4M3) return MLA_E_DTYPE;
+  if (w_dt != MLA_BF16) return MLA_E_DTYPE;
+  if (dims->d_v % 16 != 0) return MLA_E_SHAPE;
+  if (!aligned(u_part, 16) || !aligned(w_uv, 16) || (u && !aligned(u, 16))) return MLA_E_ALIGN;
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 extern "C" const char* mla_status_str(mla_status_t status) {

@@ -49,4 +49,9 @@ mla_status_t check_up_proj(const mla_dims_t* dims, int32_t B, const void* u,
                            int32_t u_dt, const void* w_uv, int32_t w_dt, const void* o,
                            int32_t o_dt);
 
+mla_status_t check_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_splits,
+                                   const void* u_part, int32_t part_dt, const float* lse_part,
+                                   const void* w_uv, int32_t w_dt, const void* o, int32_t o_dt,
+                                   const void* u);
+
 }  // namespace mla

@@ -33,18 +33,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// binary32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
-// OCP E4M3 code -> value.  Placing the 7 magnitude bits at binary32 bit 20
-// gives exponent field e and mantissa m/8 (or, for e = 0, the binary32
-// subnormal m*2^-129); multiplying by 2^120 rebases the exponent from bias 127
-// to bias 7, which is exact for normal and subnormal codes alike.
 // two floats -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), low half first
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -55,6 +43,13 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return r;
 }
 
+// binary32 -> bf16 bits, round to nearest even (NaN stays NaN)
+__device__ inline uint16_t f32_to_bf16(float f) { return static_cast<uint16_t>(pack_bf16x2(f, 0.0f)); }
+
+// OCP E4M3 code -> value.  Placing the 7 magnitude bits at binary32 bit 20
+// gives exponent field e and mantissa m/8 (or, for e = 0, the binary32
+// subnormal m*2^-129); multiplying by 2^120 rebases the exponent from bias 127
+// to bias 7, which is exact for normal and subnormal codes alike.
 __device__ inline float e4m3_to_f32(uint32_t code) {
   float f = __uint_as_float((code & 0x7Fu) << 20) * 0x1p120f;
   f = (code & 0x80u) ? -f : f;
@@ -578,8 +573,8 @@ void decode_mfma_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
             if constexpr (PART_DT == MLA_F32) {
               *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
             } else {
-              const uint32_t w0 = f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-              const uint32_t w1 = f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+              const uint32_t w0 = pack_bf16x2(v0, v1);
+              const uint32_t w1 = pack_bf16x2(v2, v3);
               *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{w0, w1};
             }
           }
@@ -927,8 +922,8 @@ void decode_bf16_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
             if constexpr (PART_DT == MLA_F32) {
               *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
             } else {
-              const uint32_t w0 = f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-              const uint32_t w1 = f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+              const uint32_t w0 = pack_bf16x2(v0, v1);
+              const uint32_t w1 = pack_bf16x2(v2, v3);
               *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{w0, w1};
             }
           }
@@ -2011,7 +2006,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* u_par
     u32x4_t w;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      w[k] = f32_to_bf16(a[2 * k] * inv) | (static_cast<uint32_t>(f32_to_bf16(a[2 * k + 1] * inv)) << 16);
+      w[k] = pack_bf16x2(a[2 * k] * inv, a[2 * k + 1] * inv);
     *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(u) + ob) = w;
   }
   if (lse && lane == 0) lse[static_cast<int64_t>(b) * H + h] = (z > 0.0f) ? mx + logf(z) : -INFINITY;
@@ -2211,8 +2206,8 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
           *reinterpret_cast<f32x4_t*>(static_cast<float*>(q_abs) + ob + c) =
               f32x4_t{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
         } else {
-          const uint32_t w0 = f32_to_bf16(acc[4 * r4]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 1])) << 16);
-          const uint32_t w1 = f32_to_bf16(acc[4 * r4 + 2]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 3])) << 16);
+          const uint32_t w0 = pack_bf16x2(acc[4 * r4], acc[4 * r4 + 1]);
+          const uint32_t w1 = pack_bf16x2(acc[4 * r4 + 2], acc[4 * r4 + 3]);
           *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(q_abs) + ob + c) = u32x2_t{w0, w1};
         }
       }
@@ -2310,8 +2305,8 @@ __global__ __launch_bounds__(kUpThreads) void up_proj_mfma_kernel(const uint16_t
             *reinterpret_cast<f32x4_t*>(static_cast<float*>(o) + ob + vr) =
                 f32x4_t{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
           } else {
-            const uint32_t w0 = f32_to_bf16(acc[4 * r4]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 1])) << 16);
-            const uint32_t w1 = f32_to_bf16(acc[4 * r4 + 2]) | (static_cast<uint32_t>(f32_to_bf16(acc[4 * r4 + 3])) << 16);
+            const uint32_t w0 = pack_bf16x2(acc[4 * r4], acc[4 * r4 + 1]);
+            const uint32_t w1 = pack_bf16x2(acc[4 * r4 + 2], acc[4 * r4 + 3]);
             *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + ob + vr) = u32x2_t{w0, w1};
           }
         } else {
@@ -2320,6 +2315,162 @@ __global__ __launch_bounds__(kUpThreads) void up_proj_mfma_kernel(const uint16_t
             if (vr + k < d_v) store_elem<O_DT>(o, ob + vr + k, acc[4 * r4 + k]);
         }
       }
+    }
+  }
+}
+
+// ================================================================ combine + up-projection
+//
+// mla_combine followed by mla_up_proj in one kernel, for bf16 W_UV: one
+// workgroup of 8 waves per (head h, 16 consecutive sequences).
+//   1. the u rows of the 16 sequences are merged from the split partials with
+//      log-sum-exp weights (32 lanes per row, 16 latent columns per lane) and
+//      rounded to bf16 into LDS — the same values mla_combine stores;
+//   2. o[b][h][:] = W_UV[h] u[b] on v_mfma_f32_16x16x32_bf16 (M = 16
+//      sequences, N = 16 value rows per wave, K = 32 latent columns): A = u
+//      from LDS, B = rows of W_UV, 16 contiguous bytes per lane from global
+//      memory.
+// Every independent load is issued first: the wave's W_UV rows, then the
+// first splits' partial rows, then the log-sum-exp inputs; later splits are
+// requested one batch ahead of their use.
+
+constexpr int kCuThreads = 512;
+constexpr int kCuRows = 16;                // sequences per workgroup
+constexpr int kCuRow = kDLatent * 2 + 16;  // padded LDS row of u (bf16)
+constexpr int kCuBatch = 4;                // splits per batch of partial loads
+
+template <int PART_DT, int O_DT>
+__global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
+    const void* u_part, const float* lse_part, const uint16_t* w_uv, void* o, uint16_t* u_out,
+    float* lse_out, int B, int H, int S, int d_v) {
+  __shared__ __attribute__((aligned(16))) uint8_t us[kCuRows * kCuRow];
+  const int nbt = (B + kCuRows - 1) / kCuRows;
+  const int wid = xcd_remap(blockIdx.x, H * nbt);
+  const int h = wid / nbt;  // the sequence tiles of one head share W_UV[h] in L2
+  const int b0 = (wid % nbt) * kCuRows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, kg = lane >> 4;
+  const int nnb = d_v / 16;  // value blocks of 16 rows
+  constexpr int kWaves = kCuThreads / 64;
+  constexpr int kKs = kDLatent / 32;  // k-steps
+
+  // W_UV operands of the wave's first value block
+  auto wrow = [&](int nb) {
+    return w_uv + (static_cast<int64_t>(h) * d_v + 16 * nb + n16) * kDLatent + 8 * kg;
+  };
+  bf16x8_t wk[kKs];
+  if (wave < nnb) {
+    const uint16_t* wr = wrow(wave);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
+  }
+
+  // ---- 1. merge: thread -> row r = tid / 32, columns 16 cg .. 16 cg + 15
+  const int r = tid >> 5, cg = tid & 31;
+  const int b = b0 + r;
+  const bool valid = b < B;
+  const int64_t prow = (static_cast<int64_t>(valid ? b : 0) * S) * H + h;  // (b, p = 0, h)
+  constexpr int kEl = PART_DT == MLA_F32 ? 4 : 8;  // elements per 16-byte load
+  constexpr int kLd = 16 / kEl;                     // loads per split
+  auto load_batch = [&](u32x4_t (&v)[kCuBatch][kLd], int p0) {
+#pragma unroll
+    for (int q = 0; q < kCuBatch; ++q) {
+      const int p = p0 + q;
+      const int64_t e = (prow + static_cast<int64_t>(p < S ? p : 0) * H) * kDLatent + 16 * cg;
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) {
+        if constexpr (PART_DT == MLA_F32)
+          v[q][i] = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(u_part) + e + 4 * i);
+        else
+          v[q][i] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(u_part) + e + 8 * i);
+      }
+    }
+  };
+  u32x4_t va[kCuBatch][kLd], vb[kCuBatch][kLd];
+  load_batch(va, 0);
+  // log-sum-exp weights: the 32 lanes of a row share the split list
+  float mx = -INFINITY;
+  for (int p = cg; p < S; p += 32) mx = fmaxf(mx, lse_part[prow + static_cast<int64_t>(p) * H]);
+#pragma unroll
+  for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+  float z = 0.0f;
+  if (mx != -INFINITY)
+    for (int p = cg; p < S; p += 32) z += expf(lse_part[prow + static_cast<int64_t>(p) * H] - mx);
+#pragma unroll
+  for (int o2 = 1; o2 < 32; o2 <<= 1) z += __shfl_xor(z, o2);
+  const float inv = (z > 0.0f) ? 1.0f / z : 0.0f;
+  float acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+  float wl = 0.0f;  // weight of split 32 * (p / 32) + (lane % 32) in that lane
+  auto accumulate = [&](const u32x4_t (&v)[kCuBatch][kLd], int p0) {
+    if ((p0 & 31) == 0) {
+      const int pl = p0 + cg;
+      wl = (pl < S && mx != -INFINITY) ? expf(lse_part[prow + static_cast<int64_t>(pl) * H] - mx) : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kCuBatch; ++q) {
+      const float w = __shfl(wl, (lane & ~31) | ((p0 + q) & 31));
+      if (p0 + q < S) {
+#pragma unroll
+        for (int i = 0; i < kLd; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if constexpr (PART_DT == MLA_F32) {
+              acc[4 * i + k] = fmaf(w, __uint_as_float(v[q][i][k]), acc[4 * i + k]);
+            } else {
+              acc[8 * i + 2 * k] = fmaf(w, __uint_as_float(v[q][i][k] << 16), acc[8 * i + 2 * k]);
+              acc[8 * i + 2 * k + 1] = fmaf(w, __uint_as_float(v[q][i][k] & 0xFFFF0000u), acc[8 * i + 2 * k + 1]);
+            }
+          }
+      }
+    }
+  };
+  // batches of kCuBatch splits, the next batch in flight while one is summed
+  for (int p0 = 0; p0 < S; p0 += 2 * kCuBatch) {
+    if (p0 + kCuBatch < S) load_batch(vb, p0 + kCuBatch);
+    accumulate(va, p0);
+    if (p0 + kCuBatch < S) {
+      if (p0 + 2 * kCuBatch < S) load_batch(va, p0 + 2 * kCuBatch);
+      accumulate(vb, p0 + kCuBatch);
+    }
+  }
+  const u32x4_t u0 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  const u32x4_t u1 = {pack_bf16x2(acc[8] * inv, acc[9] * inv), pack_bf16x2(acc[10] * inv, acc[11] * inv),
+                      pack_bf16x2(acc[12] * inv, acc[13] * inv), pack_bf16x2(acc[14] * inv, acc[15] * inv)};
+  *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32) = u0;
+  *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32 + 16) = u1;
+  if (valid) {
+    if (u_out) {
+      uint16_t* dst = u_out + (static_cast<int64_t>(b) * H + h) * kDLatent + 16 * cg;
+      *reinterpret_cast<u32x4_t*>(dst) = u0;
+      *reinterpret_cast<u32x4_t*>(dst + 8) = u1;
+    }
+    if (lse_out && cg == 0) lse_out[static_cast<int64_t>(b) * H + h] = (z > 0.0f) ? mx + logf(z) : -INFINITY;
+  }
+  __syncthreads();
+
+  // ---- 2. o = u W_UV^T on the matrix cores
+  const uint8_t* arow = us + n16 * kCuRow + 16 * kg;  // A: row n16 (sequence), k group kg
+  for (int nb = wave; nb < nnb; nb += kWaves) {
+    if (nb != wave) {
+      const uint16_t* wr = wrow(nb);
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
+    }
+    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 64 * ks);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wk[ks], d, 0, 0, 0);
+    }
+    // D: column n16 = value row 16 nb + n16, rows 4 kg + i = sequences
+    const int v = 16 * nb + n16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bb = b0 + 4 * kg + i;
+      if (bb < B) store_elem<O_DT>(o, (static_cast<int64_t>(bb) * H + h) * d_v + v, d[i]);
     }
   }
 }
@@ -2480,5 +2631,34 @@ extern "C" mla_status_t mla_up_proj(const mla_dims_t* dims, int32_t B, const voi
   MLA_UP(MLA_BF16, MLA_BF16, MLA_F32)
   MLA_UP(MLA_F32, MLA_F32, MLA_BF16)
 #undef MLA_UP
+  return MLA_E_DTYPE;
+}
+
+extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_splits,
+                                            const void* u_part, int32_t part_dt,
+                                            const float* lse_part, const void* w_uv, int32_t w_dt,
+                                            void* o, int32_t o_dt, void* u, float* lse,
+                                            void* stream) {
+  mla_status_t st = check_combine_up_proj(dims, B, num_splits, u_part, part_dt, lse_part, w_uv,
+                                          w_dt, o, o_dt, u);
+  if (st != MLA_OK || B == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = dims->heads;
+  const int64_t nblk = static_cast<int64_t>(H) * ((B + kCuRows - 1) / kCuRows);
+  if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
+  const unsigned grid = static_cast<unsigned>(nblk);
+  uint16_t* ub = static_cast<uint16_t*>(u);
+  const uint16_t* w = static_cast<const uint16_t*>(w_uv);
+#define MLA_CU(PD, OD)                                                                          \
+  if (part_dt == PD && o_dt == OD) {                                                            \
+    combine_up_kernel<PD, OD><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, B, H, \
+                                                          num_splits, dims->d_v);               \
+    return launch_status();                                                                     \
+  }
+  MLA_CU(MLA_BF16, MLA_BF16)
+  MLA_CU(MLA_BF16, MLA_F32)
+  MLA_CU(MLA_F32, MLA_BF16)
+  MLA_CU(MLA_F32, MLA_F32)
+#undef MLA_CU
   return MLA_E_DTYPE;
 }

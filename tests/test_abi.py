@@ -131,6 +131,30 @@ def test_combine_and_up_proj_validation():
     assert L.mla_up_proj(C.byref(dims(dv=512)), 2, P, F32, P, F32, P, F32, None) == E_SHAPE
 
 
+def test_combine_up_proj_validation():
+    L = mla.lib()
+    d = dims()
+
+    def cu(B=2, S=4, up=P, p_dt=BF16, lse=P, w=P, w_dt=BF16, o=P, o_dt=BF16, u=None, l=None, dd=d):
+        return L.mla_combine_up_proj(C.byref(dd), B, S, up, p_dt, lse, w, w_dt, o, o_dt, u, l, None)
+
+    assert cu(B=0, up=None, lse=None, w=None, o=None) == OK
+    assert cu(S=0) == E_ARG
+    assert cu(S=1025) == E_ARG
+    assert cu(up=None) == E_ARG
+    assert cu(lse=None) == E_ARG
+    assert cu(w=None) == E_ARG
+    assert cu(o=None) == E_ARG
+    assert cu(p_dt=9) == E_ARG
+    assert cu(p_dt=FP8) == E_DTYPE
+    assert cu(o_dt=FP8) == E_DTYPE
+    assert cu(w_dt=F32) == E_DTYPE  # bf16 W_UV only
+    assert cu(dd=dims(dv=120)) == E_SHAPE  # d_v % 16
+    assert cu(up=P + 4) == E_ALIGN
+    assert cu(w=P + 2) == E_ALIGN
+    assert cu(u=P + 2) == E_ALIGN
+
+
 @pytest.mark.parametrize("L,S,expect", [(0, 4, 0), (1, 1, 32), (2048, 8, 256), (32768, 64, 512),
                                          (131072, 256, 512), (16384, 32, 512), (100, 3, 64),
                                          (33, 1, 64)])
