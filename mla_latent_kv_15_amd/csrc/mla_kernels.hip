@@ -203,31 +203,6 @@ __device__ inline void tile_dma_bf16(const DecodeParams& P, const int32_t* __res
   }
 }
 
-// Tile layout of the pipelined bf16 kernel: tokens in groups of 8 and 16-byte
-// chunks in groups of 8, token t / chunk c at
-//   (t / 8) * 9216 + (c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swz(t % 8)) * 16.
-// One 1 KB LDS-DMA wave instruction then moves 8 tokens x 8 chunks, i.e. 8
-// whole 128-byte lines of the cache, and a lane's source offset is the same
-// for all 9 instructions of a wave (only the scalar base and M0 advance).
-constexpr int kTokGroupBytes = 8 * kRowBytes;  // 9216
-
-__device__ inline void tile_dma_g8(const DecodeParams& P, const int32_t* __restrict__ block_table,
-                                   uint32_t lds_tile, int b, int t0, int nvalid, int wave) {
-  const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
-  const uint8_t* base = P.rows + row0 * kRowBytes;
-  int ln;  // volatile: recomputed per tile rather than kept live across the loop
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  const int k = ln >> 3, j = ln & 7;
-  const int t = 8 * wave + k;  // wave w fills token group w
-  const uint32_t off = static_cast<uint32_t>(((t < nvalid) ? t : 0) * kRowBytes + ((j ^ swz(k)) << 4));
-  const uint32_t m0 = lds_tile + wave * kTokGroupBytes;
-#pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base + 128 * i),
-                 "{m0}"(m0 + 1024 * i) : "memory");
-  }
-}
-
 struct Fp8Regs {
   u32x4_t r[kFp8PerThread];
   float scale;
@@ -598,380 +573,33 @@ void decode_mfma_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
   }
 }
 
-// ================================================================ decode (bf16, pipelined)
+// ================================================================ decode (bf16)
 //
-// The bf16 cache path of mla_decode, software-pipelined across tiles.  One
-// workgroup = one (sequence b, split range p, group of up to 128 heads); wave w
-// computes QK and softmax for head block w (32 heads) and PV for every head
-// block over latent columns [128 w, 128 w + 128).  Iteration i:
-//   1. wait until tile i+1 has landed; barrier.  The barrier also certifies
-//      that every wave has published the probabilities P(i) and finished
-//      iteration i-1, so tile i-1's buffer and P(i-1)'s buffer are free;
-//   2. issue the loads of tile i+3 into tile i-1's buffer;
-//   3. PV(i) and QK(i+1) alternate MFMA by MFMA: the 36 dependent QK steps
-//      hide behind PV's 16 independent accumulator chains, and the LDS reads
-//      of both stay in flight together;
-//   4. softmax of tile i+1, publish P(i+1).
-// Tiles (4 x 36 KiB) and two probability buffers (2 x 8 KiB) fill the 160 KiB
-// of LDS.  Softmax reference and the exact redo pass are as in the fp8 path.
-
-struct QkState {
-  f32x16_t s;
-};
-
-template <int PART_DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1)))
-void decode_bf16_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNBuf * kTileBytes + 2 * kPBufBytes];
-  uint8_t* pbuf = smem + kNBuf * kTileBytes;
-
-  const int nwork = P.B * P.S * P.HG;
-  const int wid = xcd_remap(blockIdx.x, nwork);
-  const int hg = wid % P.HG;
-  const int bp = wid / P.HG;
-  const int p = bp % P.S;
-  const int b = bp / P.S;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane & 31;
-  const int g = lane >> 5;
-  const int hbase = hg * kHeadsPerBlock;
-  const int nhb = min(kWaves, (P.H - hbase) / kHeadsPerWave);  // workgroup-uniform
-  const bool qk_wave = wave < nhb;                              // wave-uniform
-
-  const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
-  const int t_begin = p * P.chunk;
-  const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(b) * P.S + p) * P.H + hbase;
-
-  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
-    if (qk_wave) {
-      const int64_t r = row_base + wave * kHeadsPerWave + hl;
-      for (int c = g; c < kDLatent; c += 2) store_elem<PART_DT>(P.u_part, r * kDLatent + c, 0.0f);
-      if (g == 0) P.lse_part[r] = -INFINITY;
-    }
-    return;
-  }
-
-  // transposing-read geometry of the PV A operand (see decode_mfma_kernel)
-  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
-  const int tr_row = 4 * (G >> 1) + e;
-  const int tr_key = swz(tr_row);
-  const int tr_x = 2 * (G & 1) + (q4 >> 1);
-  const int tr_byte = 8 * (q4 & 1);
-  const int tr_off[2] = {((0 + tr_x) ^ tr_key) << 4, ((4 + tr_x) ^ tr_key) << 4};
-  int qk_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) qk_off[i] = ((2 * i + g) ^ swz(hl)) << 4;
-
-  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
-  f32x16_t acc[kWaves * 4];
-  bf16x8_t qreg[kRowElems / 16];
-
-  auto dma = [&](int tile) {
-    const int tt = t_begin + tile * kTileTokens;
-    tile_dma_g8(P, block_table, lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes, b, tt,
-                min(kTileTokens, t_end - tt), wave);
-  };
-  // QK operand row of this lane (token hl of a tile, or head hl of the query
-  // staging area) in the token-group layout
-  const int arow_off = (hl >> 3) * kTokGroupBytes + (hl & 7) * 128;
-  // QK of tile `tile` restricted to k-steps [k0, k1): issued MFMA by MFMA by the
-  // callers below.  Operand reads run kRing steps ahead.
-  constexpr int kRing = 2;
-  auto qk_read = [&](const uint8_t* arow, int kk) {
-    return *reinterpret_cast<const bf16x8_t*>(arow + qk_off[kk & 3] + (kk >> 2) * 1024);
-  };
-  // softmax of one tile's Sᵀ; publishes the probabilities into PB
-  auto softmax_publish = [&](f32x16_t& s, int tile, int pass, int& overflow, uint8_t* PB) {
-    const int nvalid = t_end - (t_begin + tile * kTileTokens);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] *= P.scale_log2;
-    if (nvalid < kTileTokens) {  // partial last tile: token 8*(r/4) + 4*g + r%4 present?
-      uint32_t present = ((1u << nvalid) - 1u) >> (4 * g);
-      asm volatile("" : "+v"(present));  // evaluated here, not hoisted as 16 lane masks
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[r] = ((present >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (pass == 0 && tile == 0) m_ref = mx;
-    m_seen = fmaxf(m_seen, mx);
-    overflow |= (mx > m_ref + kRefSlack);
-    bf16x8_t pk[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pr = exp2f(s[r] - m_ref);
-      l_run += pr;
-      pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
-    }
-    *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + lane * 16) = pk[0];
-    *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + 1024 + lane * 16) = pk[1];
-  };
-
-  // ---- the queries and tile 0 of the first pass.
-  // The wave's 32 query rows are read with whole-line loads (8 heads x 128
-  // bytes per instruction) and turned into the MFMA operand layout through a
-  // 4 KB LDS staging area per wave in tile buffer 3 (free until tile 3 is
-  // requested, after the barrier below), 8 chunks of every head at a time.
-  // The raw lines are loaded into the operand registers themselves (qreg[4r +
-  // i] = heads 8i..8i+7, chunks 8r..8r+7) and rewritten in place, round by
-  // round: qreg also carries the queries into the second pass, so a
-  // separate staging array would double the live registers.
-  if (qk_wave) {
-    // wave-uniform base (scalar registers) + one per-lane 32-bit offset
-    const uint8_t* qw = static_cast<const uint8_t*>(P.q_abs) +
-                        ((static_cast<int64_t>(b) * P.H + hbase + wave * kHeadsPerWave) * kRowElems) * 2;
-    const uint32_t qlane = (lane >> 3) * kRowBytes + (lane & 7) * 16;
-#pragma unroll
-    for (int r = 0; r < kRowChunks / 8; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qreg[4 * r + i] = *reinterpret_cast<const bf16x8_t*>((qw + i * kTokGroupBytes + r * 128) + qlane);
-  }
-  dma(0);
-  if (qk_wave) {
-    uint8_t* stg = smem + 3 * kTileBytes + wave * 4096;
-    const int wr = (lane >> 3) * 128 + (((lane & 7) ^ swz(lane >> 3)) << 4);
-    const int rd = (hl >> 3) * 1024 + (hl & 7) * 128;
-#pragma unroll
-    for (int r = 0; r < kRowChunks / 8; ++r) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8_t*>(stg + i * 1024 + wr) = qreg[4 * r + i];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        qreg[4 * r + q] = *reinterpret_cast<const bf16x8_t*>(stg + rd + qk_off[q]);
-    }
-    // consume the staged queries once, here, so no wait for them is left
-    // inside the tile loop
-#pragma unroll
-    for (int kk = 0; kk < kRowElems / 16; ++kk) asm volatile("" : "+v"(qreg[kk]));
-  }
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int k = 0; k < kWaves * 4; ++k) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
-      asm volatile("" : "+a"(acc[k]));
-    }
-    asm volatile("s_nop 4");  // accumulator writes -> first (inline-asm) MFMA read
-    l_run = 0.0f;
-    int overflow = 0;
-
-    if (pass > 0) dma(0);  // pass 0 requested tile 0 before staging the queries
-    if (ntiles > 1) dma(1);
-    if (ntiles > 2) dma(2);
-    if (ntiles > 2)
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if (ntiles > 1)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_barrier" ::: "memory");
-    if (qk_wave) {
-      const uint8_t* arow = smem + arow_off;
-      f32x16_t s;
-      bf16x8_t ring[kRing];
-#pragma unroll
-      for (int i = 0; i < kRing; ++i) ring[i] = qk_read(arow, i);
-#pragma unroll
-      for (int kk = 0; kk < kRowElems / 16; ++kk) {
-        const bf16x8_t a = ring[kk % kRing];
-        if (kk + kRing < kRowElems / 16) ring[kk % kRing] = qk_read(arow, kk + kRing);
-        if (kk == 0)
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qreg[kk]));
-        else
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qreg[kk]));
-      }
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-      softmax_publish(s, 0, pass, overflow, pbuf);
-    }
-
-    for (int i = 0; i < ntiles; ++i) {
-      // 1. tile i+1 landed (tile i+2 may stay in flight); barrier
-      if (i + 2 < ntiles)
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      asm volatile("s_barrier" ::: "memory");
-      // 2. tile i+3 into tile i-1's buffer
-      if (i + 3 < ntiles) dma(i + 3);
-      // 3. PV(i) with QK(i+1)
-      const uint8_t* T = smem + (i & (kNBuf - 1)) * kTileBytes;
-      const uint8_t* PB = pbuf + (i & 1) * kPBufBytes;
-      const bool do_qk = qk_wave && (i + 1 < ntiles);  // wave-uniform
-      const uint8_t* arow = smem + ((i + 1) & (kNBuf - 1)) * kTileBytes + arow_off;
-      // PV(i) in two halves of 64 columns: per half, the transposed tile
-      // operands of 2 column blocks (x 2 token halves) and, per head block, the
-      // published probabilities.  QK(i+1) steps are interleaved throughout.
-      const uint8_t* r0 = T + tr_row * 128 + tr_byte;
-      auto load_av = [&](bf16x8_t (&av)[2][2], int half) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int cb = 4 * wave + 2 * half + c2;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            // tokens 16j + tr_row (lo) and 16j + 8 + tr_row (hi): token groups 2j, 2j + 1
-            const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 1024 + 2 * j * kTokGroupBytes;
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
-            const bf16x4_t hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + kTokGroupBytes));
-            av[c2][j] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-        }
-      };
-      // QK runs unconditionally (a branch per step would serialise the operand
-      // reads); when there is no tile i+1, or the wave has no heads, it reads
-      // stale LDS into a score block that is dropped.
-      f32x16_t s;
-      bf16x8_t ring[kRing];
-#pragma unroll
-      for (int k = 0; k < kRing; ++k) ring[k] = qk_read(arow, k);
-      bf16x8_t av[2][2];
-      load_av(av, 0);
-      bf16x8_t pb0 = *reinterpret_cast<const bf16x8_t*>(PB + lane * 16);
-      bf16x8_t pb1 = *reinterpret_cast<const bf16x8_t*>(PB + 1024 + lane * 16);
-      // step st: QK k-step st (0..35) and PV step st (0..31): half st / 16,
-      // head block (st / 4) % 4, column block 2 * half + (st / 2) % 2, token half st % 2
-#pragma unroll
-      for (int st = 0; st < kRowElems / 16; ++st) {
-        {
-          const bf16x8_t a = ring[st % kRing];
-          if (st + kRing < kRowElems / 16) ring[st % kRing] = qk_read(arow, st + kRing);
-          if (st == 0)
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qreg[st]));
-          else
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qreg[st]));
-        }
-        if (st < 32) {
-          const int half = st >> 4, hb = (st >> 2) & 3, c2 = (st >> 1) & 1, j = st & 1;
-          // head blocks beyond nhb multiply stale probabilities into
-          // accumulators that are never stored: no branch in the MFMA stream
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-              : "+a"(acc[4 * hb + 2 * half + c2]) : "v"(av[c2][j]), "v"(j ? pb1 : pb0));
-          if ((st & 3) == 3 && st < 31) {  // next (half, head block): its probabilities
-            const int nhb2 = ((st + 1) >> 2) & 3;
-            pb0 = *reinterpret_cast<const bf16x8_t*>(PB + nhb2 * 2048 + lane * 16);
-            pb1 = *reinterpret_cast<const bf16x8_t*>(PB + nhb2 * 2048 + 1024 + lane * 16);
-          }
-          if (st == 15) load_av(av, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // 4. softmax of tile i+1, publish P(i+1)
-      if (do_qk) {
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-        softmax_publish(s, i + 1, pass, overflow, pbuf + ((i + 1) & 1) * kPBufBytes);
-      }
-    }
-    // same vote as decode_mfma_kernel: tile `ntiles` would use a buffer nobody reads
-    int* votes = reinterpret_cast<int*>(smem + (ntiles & (kNBuf - 1)) * kTileBytes);
-    const int any_wave = __any(overflow) ? 1 : 0;
-    if (lane == 0) votes[wave] = any_wave;
-    __syncthreads();
-    const int again = votes[0] | votes[1] | votes[2] | votes[3];
-    __syncthreads();
-    if (!again) break;
-    m_ref = m_seen;
-  }
-
-  // ---- epilogue.  Normalisers of all head blocks via LDS (the tile buffers
-  //      are free now): linv[32*hb + hl] = 1 / Σ p of that head.
-  float* linv = reinterpret_cast<float*>(smem);
-  uint8_t* stage = smem + 1024;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qk_wave) {
-    if (g == 0) {
-      linv[wave * kHeadsPerWave + hl] = 1.0f / l_tot;
-      P.lse_part[row_base + wave * kHeadsPerWave + hl] = (m_ref + log2f(l_tot)) * kLn2;
-    }
-  }
-  __syncthreads();
-  // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-  // Uᵀ register r of block (hb, cbl) in lane (hl, g) is column
-  // 128*wave + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
-  // wave stages one head block (32 rows x 128 columns) at a time in its own
-  // LDS region and writes 256 contiguous bytes per row.
-  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
-  constexpr int kColsRound = 256 / kEsz;                  // 128 bf16 / 64 fp32 columns
-  constexpr int kStageRow = kColsRound * kEsz + 16;       // padded: rows start 4 banks apart
-  uint8_t* W = stage + wave * kHeadsPerWave * kStageRow;
-#pragma unroll
-  for (int hb = 0; hb < kWaves; ++hb) {
-    if (hb < nhb) {
-      const float inv = linv[hb * kHeadsPerWave + hl];
-#pragma unroll
-      for (int half = 0; half < 128 / kColsRound; ++half) {
-#pragma unroll
-        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
-          const int cbl = half * (kColsRound / 32) + cbl2;
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
-            const f32x16_t& A = acc[4 * hb + cbl];
-            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
-            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
-            uint8_t* wp = W + hl * kStageRow + c * kEsz;
-            if constexpr (PART_DT == MLA_F32) {
-              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
-            } else {
-              const uint32_t w0 = pack_bf16x2(v0, v1);
-              const uint32_t w1 = pack_bf16x2(v2, v3);
-              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{w0, w1};
-            }
-          }
-        }
-        // one wave's LDS operations complete in order: no barrier is needed
-        asm volatile("" ::: "memory");
-        // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
-        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
-                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * wave) * kEsz +
-                       half * (kColsRound * kEsz);
-#pragma unroll
-        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
-          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
-                                      (lane & 15) * 16) = v;
-        }
-        asm volatile("" ::: "memory");
-      }
-    }
-  }
-}
-
-// ================================================================ decode (bf16, 64 heads)
-//
-// One workgroup = one (sequence b, split range p, group of up to 64 heads),
-// 4 waves.  Per 32-token tile held in LDS (token-group layout above):
-//   * QK: wave w = (head block w & 1, token half w >> 1) computes the scores
-//     of its 32 heads x 16 tokens with v_mfma_f32_16x16x32_bf16: the tile is
-//     the A operand (one 16-byte LDS read per k-step of 32, shared by the two
-//     16-head halves), the absorbed queries the B operand, kept in VGPRs;
-//   * softmax in the base-2 domain against a fixed per-head reference (the
-//     maximum over the first tile, agreed between the two token halves); a
-//     score more than 2^kRefSlack above it makes the workgroup redo the range
-//     with the range maximum as reference, so no accumulator is ever rescaled;
-//   * the bf16 probabilities of the tile (64 heads x 32 tokens) are published
-//     in LDS in the B-operand layout of the next product;
-//   * PV: wave w accumulates U^T for latent columns 128w..128w+127 of all 64
-//     heads (8 blocks of 32x32 in AGPRs) with v_mfma_f32_32x32x16_bf16, the
-//     tile read with transposing ds_read_b64_tr_b16 as the A operand.
-// The loop is software-pipelined: PV of tile i is interleaved with QK of tile
-// i+1, and up to three tiles are in flight from HBM (four LDS buffers).
+// Shared pieces of the bf16 cache path: the work unit is (sequence b, split
+// range p, group of up to 64 heads); tiles of 32 tokens sit in LDS in the
+// token-group layout below.
 
 constexpr int kH64 = 64;                 // heads per workgroup
 constexpr int kH64Blocks = 2;            // head blocks of 32
 constexpr int kQkSteps = kRowElems / 32;  // 18 k-steps of 32
 constexpr int kP64Bytes = 4096;           // bf16 probabilities, 64 heads x 32 tokens
 constexpr int kX64Off = kNBuf * kTileBytes + 2 * kP64Bytes;  // exchange area (float[2][64] + votes)
+
+// Token-group tile layout: tokens in groups of 8 and 16-byte chunks in groups
+// of 8, token t / chunk c at
+//   (t / 8) * 9216 + (c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swzg(t)) * 16,
+//   swzg(t) = 5 (t % 8) mod 8.
+// One 1 KB LDS-DMA wave instruction moves 8 tokens x 8 chunks, i.e. 8 whole
+// 128-byte lines of the cache, and a lane's source offset is the same for all
+// 9 instructions of a wave (only the scalar base and M0 advance).  The XOR key
+// was chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950) among the
+// permutations of the 8 rows of a group: with it neither operand read pattern
+// has bank conflicts -- the QK read (16 lanes = one chunk of 8 rows in each of
+// two groups) nor the transposing PV read (4 rows x 2 chunks x 2 halves);
+// the pattern of the fp8 path, swz, costs the QK read one extra pass.
+constexpr int kTokGroupBytes = 8 * kRowBytes;  // 9216
+
+__device__ inline int swzg(int t) { return (5 * (t & 7)) & 7; }
 
 // DMA of 32 rows of 1152 bytes starting at `base` (rows consecutive in
 // memory) into an LDS tile in the token-group layout; wave w moves rows
@@ -992,7 +620,7 @@ __device__ inline RowsDma rows_dma_plan(const uint8_t* base, uint32_t lds_tile, 
   const int t = 8 * wave + k;
   RowsDma d;
   d.base = base;
-  d.off = static_cast<uint32_t>(((t < nvalid) ? t : 0) * kRowBytes + ((j ^ swz(k)) << 4));
+  d.off = static_cast<uint32_t>(((t < nvalid) ? t : 0) * kRowBytes + ((j ^ swzg(t)) << 4));
   d.m0 = lds_tile + wave * kTokGroupBytes;
   return d;
 }
@@ -1008,403 +636,10 @@ __device__ inline void rows_dma_g8(const uint8_t* base, uint32_t lds_tile, int n
   for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
 }
 
-template <int PART_DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1)))
-void decode_h64_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kX64Off + 1024];
-  uint8_t* pbuf = smem + kNBuf * kTileBytes;
-  float* xch = reinterpret_cast<float*>(smem + kX64Off);  // [2][64] per-head exchange
-  int* votes = reinterpret_cast<int*>(smem + kX64Off + 512);
-
-  const int nwork = P.B * P.S * P.HG;
-  const int wid = xcd_remap(blockIdx.x, nwork);
-  const int hg = wid % P.HG;
-  const int bp = wid / P.HG;
-  const int p = bp % P.S;
-  const int b = bp / P.S;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hbase = hg * kH64;
-  const int nhb = min(kH64Blocks, (P.H - hbase) / kHeadsPerWave);  // 1 or 2, workgroup-uniform
-  const int qhb = wave & 1;                                         // QK head block
-  const int th = wave >> 1;                                         // QK token half
-  const bool qk_wave = qhb < nhb;                                   // wave-uniform
-  // QK lane roles (16x16 blocks): token / head n = lane % 16, k group kg = lane / 16
-  const int n16 = lane & 15, kg = lane >> 4;
-  // PV lane roles (32x32 blocks): head hl = lane % 32, token group g = lane / 32
-  const int hl = lane & 31, g = lane >> 5;
-
-  const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
-  const int t_begin = p * P.chunk;
-  const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(b) * P.S + p) * P.H + hbase;
-
-  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
-    if (qk_wave && th == 0) {
-      const int64_t r = row_base + qhb * kHeadsPerWave + hl;
-      for (int c = g; c < kDLatent; c += 2) store_elem<PART_DT>(P.u_part, r * kDLatent + c, 0.0f);
-      if (g == 0) P.lse_part[r] = -INFINITY;
-    }
-    return;
-  }
-
-  // transposing-read geometry of the PV A operand
-  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
-  const int tr_row = 4 * (G >> 1) + e;
-  const int tr_key = swz(tr_row);
-  const int tr_x = 2 * (G & 1) + (q4 >> 1);
-  const int tr_byte = 8 * (q4 & 1);
-  const int tr_off[2] = {((0 + tr_x) ^ tr_key) << 4, ((4 + tr_x) ^ tr_key) << 4};
-  // QK A/B operand reads: row 16*half + n16 of a 32-row tile, chunk 4ks + kg
-  const int qk_row = ((n16 >> 3) * kTokGroupBytes) + (n16 & 7) * 128;
-  const int qk_off[2] = {(kg ^ swz(n16 & 7)) << 4, ((4 + kg) ^ swz(n16 & 7)) << 4};
-  auto qk_addr = [&](int half, int ks) {
-    return 2 * half * kTokGroupBytes + qk_row + qk_off[ks & 1] + (ks >> 1) * 1024;
-  };
-
-  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-  // per-lane softmax state for heads 16*hh + n16 of head block qhb
-  float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.0f, 0.0f};
-  f32x16_t acc[kH64Blocks * 4];
-  bf16x8_t qreg[kQkSteps][2];
-
-  auto dma_plan = [&](int tile) {
-    const int tt = t_begin + tile * kTileTokens;
-    const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
-    return rows_dma_plan(P.rows + row0 * kRowBytes, lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes,
-                         min(kTileTokens, t_end - tt), wave);
-  };
-  auto dma = [&](int tile) {
-    const RowsDma d = dma_plan(tile);
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
-  };
-  // QK of one tile: 18 k-steps x 2 head halves
-  constexpr int kRing = 3;
-  auto qk_read = [&](const uint8_t* T, int ks) {
-    return *reinterpret_cast<const bf16x8_t*>(T + qk_addr(th, ks));
-  };
-  // softmax of one tile's scores (s[hh] = 4 tokens of head 16hh + n16), publish P
-  auto softmax_publish = [&](f32x4_t (&s)[2], int tile, int pass, int& overflow, uint8_t* PB) {
-    const int nvalid = t_end - (t_begin + tile * kTileTokens);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[hh][r] *= P.scale_log2;
-    if (nvalid < kTileTokens) {  // partial last tile: token 16 th + 4 kg + r present?
-      int first = 16 * th + 4 * kg;
-      asm volatile("" : "+v"(first));  // evaluated here, not hoisted as lane masks
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[hh][r] = (first + r < nvalid) ? s[hh][r] : -INFINITY;
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const float mx = fmaxf(fmaxf(s[hh][0], s[hh][1]), fmaxf(s[hh][2], s[hh][3]));
-      m_seen[hh] = fmaxf(m_seen[hh], mx);
-      overflow |= (mx > m_ref[hh] + kRefSlack);
-      float pr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(s[hh][r] - m_ref[hh]);  // v_exp_f32
-        l_run[hh] += pr[r];
-      }
-      const uint32_t w0 = pack_bf16x2(pr[0], pr[1]);
-      const uint32_t w1 = pack_bf16x2(pr[2], pr[3]);
-      // B-operand slot of token 16th + 4kg + r: k-step th, lane group kg & 1,
-      // slots 4 (kg >> 1) + r of head 32 qhb + 16 hh + n16
-      *reinterpret_cast<u32x2_t*>(PB + (((th * 2 + qhb) * 2 + (kg & 1)) * 32 + 16 * hh + n16) * 16 +
-                                  8 * (kg >> 1)) = u32x2_t{w0, w1};
-    }
-  };
-  // per-head maximum over the two token halves (and the lane groups): used for
-  // the first tile's reference and for the redo pass
-  auto agree_max = [&](float (&m)[2]) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      m[hh] = fmaxf(m[hh], __shfl_xor(m[hh], 16));
-      m[hh] = fmaxf(m[hh], __shfl_xor(m[hh], 32));
-    }
-    if (qk_wave && kg == 0) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) xch[th * 64 + qhb * 32 + 16 * hh + n16] = m[hh];
-    }
-    __syncthreads();
-    if (qk_wave) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) m[hh] = fmaxf(m[hh], xch[(th ^ 1) * 64 + qhb * 32 + 16 * hh + n16]);
-    }
-    __syncthreads();
-  };
-
-  // ---- the queries: both head blocks (32 rows of 1152 bytes each) are moved
-  // into tile buffers 2 and 3 in the tile layout, then every QK wave reads its
-  // B operands from there.  Tiles 0 and 1 are requested right behind them.
-  const uint8_t* qsrc = static_cast<const uint8_t*>(P.q_abs) +
-                        (static_cast<int64_t>(b) * P.H + hbase) * kRowBytes;
-  for (int hb = 0; hb < nhb; ++hb)
-    rows_dma_g8(qsrc + hb * kHeadsPerWave * kRowBytes, lds_addr(smem) + (2 + hb) * kTileBytes,
-                kTileTokens, wave);
-  dma(0);
-  if (ntiles > 1) dma(1);
-  if (ntiles > 1)
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  asm volatile("s_barrier" ::: "memory");
-  if (qk_wave) {
-    const uint8_t* Q = smem + (2 + qhb) * kTileBytes;
-#pragma unroll
-    for (int ks = 0; ks < kQkSteps; ++ks)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        qreg[ks][hh] = *reinterpret_cast<const bf16x8_t*>(Q + qk_addr(hh, ks));
-    // consume the query reads once, here, so no wait for them is left inside
-    // the tile loop
-#pragma unroll
-    for (int ks = 0; ks < kQkSteps; ++ks) {
-      asm volatile("" : "+v"(qreg[ks][0]));
-      asm volatile("" : "+v"(qreg[ks][1]));
-    }
-  }
-  __syncthreads();  // buffers 2 and 3 are free again
-
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int k = 0; k < kH64Blocks * 4; ++k) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
-      asm volatile("" : "+a"(acc[k]));
-    }
-    asm volatile("s_nop 4");  // accumulator writes -> first (inline-asm) MFMA read
-    l_run[0] = l_run[1] = 0.0f;
-    int overflow = 0;
-
-    // ---- prologue: tiles 0..2 (pass 0 requested 0 and 1 with the queries)
-    if (pass > 0) {
-      dma(0);
-      if (ntiles > 1) dma(1);
-    }
-    if (ntiles > 2) dma(2);
-    if (ntiles > 2)
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if (ntiles > 1)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_barrier" ::: "memory");
-    {
-      f32x4_t s[2];
-      if (qk_wave) {
-        bf16x8_t ring[kRing];
-#pragma unroll
-        for (int k = 0; k < kRing; ++k) ring[k] = qk_read(smem, k);
-#pragma unroll
-        for (int ks = 0; ks < kQkSteps; ++ks) {
-          const bf16x8_t a = ring[ks % kRing];
-          if (ks + kRing < kQkSteps) ring[ks % kRing] = qk_read(smem, ks + kRing);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            if (ks == 0)
-              asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(s[hh]) : "v"(a), "v"(qreg[ks][hh]));
-            else
-              asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(s[hh]) : "v"(a), "v"(qreg[ks][hh]));
-          }
-        }
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
-      }
-      if (pass == 0) {  // reference: maximum of the first tile (its tokens are all valid
-                        // unless the range is shorter than a tile)
-        float mx[2] = {-INFINITY, -INFINITY};
-        if (qk_wave) {
-          const int nvalid = t_end - t_begin;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (16 * th + 4 * kg + r < nvalid) mx[hh] = fmaxf(mx[hh], s[hh][r] * P.scale_log2);
-        }
-        agree_max(mx);
-        m_ref[0] = mx[0];
-        m_ref[1] = mx[1];
-      }
-      if (qk_wave) softmax_publish(s, 0, pass, overflow, pbuf);
-    }
-
-    for (int i = 0; i < ntiles; ++i) {
-      // 1. tile i+1 landed (tile i+2 may stay in flight); P(i) published; barrier
-      if (i + 2 < ntiles)
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      asm volatile("s_barrier" ::: "memory");
-      // 2. tile i+3 into tile i-1's buffer, one wave instruction per step below
-      const bool dnext = i + 3 < ntiles;  // workgroup-uniform
-      RowsDma dp{};
-      if (dnext) dp = dma_plan(i + 3);
-      // 3. PV(i) interleaved with QK(i+1).  QK runs unconditionally (a branch
-      //    per step would serialise the operand reads); without a tile i+1, or
-      //    for a wave without heads, it reads stale LDS into dropped scores.
-      const uint8_t* T = smem + (i & (kNBuf - 1)) * kTileBytes;
-      const uint8_t* Tn = smem + ((i + 1) & (kNBuf - 1)) * kTileBytes;
-      const uint8_t* PB = pbuf + (i & 1) * kP64Bytes;
-      const uint8_t* r0 = T + tr_row * 128 + tr_byte;
-      // A operand of PV for column block cbl (0..3) of this wave, token half j
-      auto load_av = [&](int cbl, int j) {
-        const int cb = 4 * wave + cbl;
-        const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 1024 + 2 * j * kTokGroupBytes;
-        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
-        const bf16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + kTokGroupBytes));
-        return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      bf16x8_t pb[2][2];  // [token half j][head block]
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          pb[j][hb] = *reinterpret_cast<const bf16x8_t*>(PB + ((j * 2 + hb) * 64 + lane) * 16);
-      bf16x8_t av[2][2];  // [column block parity][token half]
-      av[0][0] = load_av(0, 0);
-      av[0][1] = load_av(0, 1);
-      f32x4_t s[2];
-      bf16x8_t ring[kRing];
-#pragma unroll
-      for (int k = 0; k < kRing; ++k) ring[k] = qk_read(Tn, k);
-      // step st (0..17): QK k-step st (two MFMAs); PV MFMA st for st < 16:
-      // column block st / 4, token half (st / 2) % 2, head block st % 2
-#pragma unroll
-      for (int st = 0; st < kQkSteps; ++st) {
-        if (st >= 1 && st <= kDmaPerWave && dnext) rows_dma_issue(dp, st - 1);
-        {
-          const bf16x8_t a = ring[st % kRing];
-          if (st + kRing < kQkSteps) ring[st % kRing] = qk_read(Tn, st + kRing);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            if (st == 0)
-              asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(s[hh]) : "v"(a), "v"(qreg[st][hh]));
-            else
-              asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(s[hh]) : "v"(a), "v"(qreg[st][hh]));
-          }
-        }
-        if (st < 16) {
-          const int cbl = st >> 2, j = (st >> 1) & 1, hb = st & 1;
-          // head blocks beyond nhb multiply stale probabilities into
-          // accumulators that are never stored: no branch in the MFMA stream
-          asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-              : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl & 1][j]), "v"(pb[j][hb]));
-          if ((st & 3) == 1 && cbl < 3) {  // next column block's operands
-            av[(cbl + 1) & 1][0] = load_av(cbl + 1, 0);
-            av[(cbl + 1) & 1][1] = load_av(cbl + 1, 1);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // 4. softmax of tile i+1, publish P(i+1)
-      if (qk_wave && i + 1 < ntiles) {
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
-        softmax_publish(s, i + 1, pass, overflow, pbuf + ((i + 1) & 1) * kP64Bytes);
-      }
-    }
-    // any wave saw a score far above its reference: redo the range with the
-    // range maximum (agreed per head) as reference
-    const int any_wave = __any(overflow) ? 1 : 0;
-    if (lane == 0) votes[wave] = any_wave;
-    __syncthreads();
-    const int again = votes[0] | votes[1] | votes[2] | votes[3];
-    __syncthreads();
-    if (!again) break;
-    agree_max(m_seen);
-    m_ref[0] = m_seen[0];
-    m_ref[1] = m_seen[1];
-  }
-
-  // ---- epilogue.  l per head: lane groups, then the two token halves via LDS;
-  //      linv[32*hb + hl] = 1 / l of that head.
-  float* linv = reinterpret_cast<float*>(smem);
-  uint8_t* stage = smem + 1024;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    l_run[hh] += __shfl_xor(l_run[hh], 16);
-    l_run[hh] += __shfl_xor(l_run[hh], 32);
-  }
-  if (qk_wave && kg == 0) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) xch[th * 64 + qhb * 32 + 16 * hh + n16] = l_run[hh];
-  }
-  __syncthreads();
-  if (qk_wave && th == 0 && kg == 0) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int hx = qhb * 32 + 16 * hh + n16;
-      const float l_tot = xch[hx] + xch[64 + hx];
-      linv[hx] = 1.0f / l_tot;
-      P.lse_part[row_base + hx] = (m_ref[hh] + log2f(l_tot)) * kLn2;
-    }
-  }
-  __syncthreads();
-  // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-  // U^T register r of block (hb, cbl) in lane (hl, g) is column
-  // 128*wave + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
-  // wave stages one head block (32 rows x 128 columns) at a time in its own
-  // LDS region and writes 256 contiguous bytes per row.
-  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
-  constexpr int kColsRound = 256 / kEsz;             // 128 bf16 / 64 fp32 columns
-  constexpr int kStageRow = kColsRound * kEsz + 16;  // padded: rows start 4 banks apart
-  uint8_t* W = stage + wave * kHeadsPerWave * kStageRow;
-#pragma unroll
-  for (int hb = 0; hb < kH64Blocks; ++hb) {
-    if (hb < nhb) {
-      const float inv = linv[hb * kHeadsPerWave + hl];
-#pragma unroll
-      for (int half = 0; half < 128 / kColsRound; ++half) {
-#pragma unroll
-        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
-          const int cbl = half * (kColsRound / 32) + cbl2;
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
-            const f32x16_t& A = acc[4 * hb + cbl];
-            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
-            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
-            uint8_t* wp = W + hl * kStageRow + c * kEsz;
-            if constexpr (PART_DT == MLA_F32) {
-              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
-            } else {
-              const uint32_t w0 = pack_bf16x2(v0, v1);
-              const uint32_t w1 = pack_bf16x2(v2, v3);
-              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{w0, w1};
-            }
-          }
-        }
-        // one wave's LDS operations complete in order: no barrier is needed
-        asm volatile("" ::: "memory");
-        // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
-        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
-                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * wave) * kEsz +
-                       half * (kColsRound * kEsz);
-#pragma unroll
-        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
-          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
-                                      (lane & 15) * 16) = v;
-        }
-        asm volatile("" ::: "memory");
-      }
-    }
-  }
-}
-
 // ================================================================ decode (bf16, warp-specialised)
 //
-// Same work unit as decode_h64_kernel (sequence b, split range p, 64 heads) with
-// 8 waves, two per SIMD, in two roles:
+// One workgroup per (sequence b, split range p, 64 heads), 8 waves, two per
+// SIMD, in two roles:
 //   * QK waves 0..3 (head block w & 1, token half w >> 1) hold their absorbed
 //     queries in AGPRs, compute the scores of tile i+1 with
 //     v_mfma_f32_16x16x32_bf16, run the softmax and publish the bf16
@@ -1470,7 +705,8 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     const bool active = qhb < nhb;  // wave-uniform
     const int n16 = lane & 15, kg = lane >> 4;
     const int qk_row = ((n16 >> 3) * kTokGroupBytes) + (n16 & 7) * 128;
-    const int qk_off[2] = {(kg ^ swz(n16 & 7)) << 4, ((4 + kg) ^ swz(n16 & 7)) << 4};
+    const int qk_key = swzg(n16);  // row n16 % 8 of group n16 / 8 of a 16-row half
+    const int qk_off[2] = {(kg ^ qk_key) << 4, ((4 + kg) ^ qk_key) << 4};
     auto qk_addr = [&](int half, int ks) {
       return 2 * half * kTokGroupBytes + qk_row + qk_off[ks & 1] + (ks >> 1) * 1024;
     };
@@ -1643,7 +879,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   const int hl = lane & 31, g = lane >> 5;
   const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
   const int tr_row = 4 * (G >> 1) + e;
-  const int tr_key = swz(tr_row);
+  const int tr_key = swzg(tr_row);
   const int tr_x = 2 * (G & 1) + (q4 >> 1);
   const int tr_byte = 8 * (q4 & 1);
   const int tr_off[2] = {((0 + tr_x) ^ tr_key) << 4, ((4 + tr_x) ^ tr_key) << 4};
