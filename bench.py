@@ -45,6 +45,10 @@ def parse():
                     help="merge and up-project with mla_combine + mla_up_proj")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (counter calibration)")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="no GPU work: read the rocprofv3 --pmc CSVs under DIR/{fetch,write,"
+                         "cfetch,cwrite} and store the decode kernel's HBM bytes per launch in "
+                         "profiles/decode_traffic.json")
     return ap.parse_args()
 
 
@@ -67,6 +71,42 @@ def stored_traffic(launch_cache_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_means(path, counter):
+    """mean value of `counter` per kernel name in a rocprofv3 counter CSV"""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        v = acc.setdefault(name, [0.0, 0])
+        v[0] += float(r["Counter_Value"])
+        v[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
+def record_traffic(d):
+    """HBM bytes per mla_decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the factor that maps the same counter onto the
+    known bytes of a 1 GiB device copy."""
+    f = _counter_means(os.path.join(d, "fetch", "run_counter_collection.csv"), "FETCH_SIZE")
+    w = _counter_means(os.path.join(d, "write", "run_counter_collection.csv"), "WRITE_SIZE")
+    cf = _counter_means(os.path.join(d, "cfetch", "run_counter_collection.csv"), "FETCH_SIZE")
+    cw = _counter_means(os.path.join(d, "cwrite", "run_counter_collection.csv"), "WRITE_SIZE")
+    copy_kib = (1 << 30) / 1024.0
+    kf = copy_kib / max(v for k, v in cf.items() if "copyBuffer" in k)
+    kw = copy_kib / max(v for k, v in cw.items() if "copyBuffer" in k)
+    name = next(k for k in f if "decode_" in k and "kernel" in k)
+    short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+    rec = {"kernel": short, "kernel_source_sha256_16": source_hash(),
+           "fetch_kib_per_launch": f[name], "write_kib_per_launch": w[name],
+           "fetch_scale": kf, "write_scale": kw,
+           "hbm_bytes_per_launch": (f[name] * kf + w[name] * kw) * 1024.0,
+           "counters_from": d}
+    json.dump(rec, open(PROFILE_TRAFFIC, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def calibrate_copy():
     import torch
     n = 1 << 30
@@ -81,14 +121,19 @@ def calibrate_copy():
                       "launches": 5}), flush=True)
 
 
-def cpu_baseline(inp, n_seq: int):
-    """The oracle timed on the host cores on n_seq whole sequences (all heads,
-    all cached tokens) of the same workload; tokens/s = n_seq / seconds."""
+def cpu_baseline(inp, target_s: float = 15.0):
+    """The oracle timed on the host cores on whole sequences (all heads, all
+    cached tokens) of the same workload, as many as fit in about target_s
+    seconds (at least one); tokens/s = sequences / seconds."""
     import oracle
     wl = inp.wl
-    pairs = [(b, h) for b in range(n_seq) for h in range(wl.heads)]
     t = time.perf_counter()
-    oracle.decode_inputs(inp, sel=pairs)
+    oracle.decode_inputs(inp, sel=[(0, h) for h in range(wl.heads)])
+    first = time.perf_counter() - t
+    n_seq = int(max(1, min(wl.batch, round(target_s / max(first, 1e-3)))))
+    if n_seq > 1:
+        pairs = [(b, h) for b in range(1, n_seq) for h in range(wl.heads)]
+        oracle.decode_inputs(inp, sel=pairs)
     dt = time.perf_counter() - t
     return {"value": n_seq / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
@@ -99,6 +144,9 @@ def cpu_baseline(inp, n_seq: int):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(run with --gpus 1)", file=sys.stderr)
@@ -149,32 +197,20 @@ def main():
     # W_UV product run as one launch (mla_combine_up_proj; u is not stored)
     fused = step.fused_tail(dev.w_uv) and not args.two_call_tail
 
-    def one(i, ev=None):
+    def one(i):
         rp = reps[i % R]
-        if ev is not None:
-            ev[0].record(stream)
         mla.mla_absorb_q(step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs,
                          stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         mla.mla_decode(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
                        stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
         if fused:
             mla.mla_combine_up_proj(step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o,
                                     stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
         else:
             if S > 1:
                 mla.mla_combine(step.geo, step.u_part, step.lse_part, step.u, step.lse,
                                 stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
             mla.mla_up_proj(step.geo, step.u, rp["w_uv"], step.o, stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
 
     print(f"[bench] warmup {args.warmup}, R={R} replicas", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -189,24 +225,34 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # per-kernel timing with HIP events on the launch stream (a separate pass)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        one(i, evs[i])
-    torch.cuda.synchronize()
-    ker = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(4)]
-                    for i in range(args.steps)])  # ms
-    k_mean = ker.mean(axis=0)
-    k_med = np.median(ker, axis=0)
-    t_decode = float(k_mean[1]) * 1e-3
-    t_dc = float(k_mean[1] + k_mean[2]) * 1e-3
+    # per-kernel timing: each entry point launched `steps` times back to back
+    # (rotating over the replicas) between two HIP events recorded on the
+    # launch stream; mean time per launch
+    def loop_ms(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(reps[i % R])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
 
-    def kernel_table(k):  # ms per launch -> us, keyed by entry point
-        if fused:
-            return {"mla_absorb_q": k[0] * 1e3, "mla_decode": k[1] * 1e3,
-                    "mla_combine_up_proj": k[2] * 1e3}
-        return {"mla_absorb_q": k[0] * 1e3, "mla_decode": k[1] * 1e3,
-                "mla_combine": k[2] * 1e3, "mla_up_proj": k[3] * 1e3}
+    stages = [("mla_absorb_q", lambda rp: mla.mla_absorb_q(
+                  step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs, stream=stream)),
+              ("mla_decode", lambda rp: mla.mla_decode(
+                  step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part, stream=stream))]
+    if fused:
+        stages.append(("mla_combine_up_proj", lambda rp: mla.mla_combine_up_proj(
+            step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o, stream=stream)))
+    else:
+        if S > 1:
+            stages.append(("mla_combine", lambda rp: mla.mla_combine(
+                step.geo, step.u_part, step.lse_part, step.u, step.lse, stream=stream)))
+        stages.append(("mla_up_proj", lambda rp: mla.mla_up_proj(
+            step.geo, step.u, rp["w_uv"], step.o, stream=stream)))
+    kernel_us = {name: loop_ms(fn) * 1e3 for name, fn in stages}
+    t_decode = kernel_us["mla_decode"] * 1e-6
 
     launch_bytes = cache_bytes  # algorithmic bytes of one mla_decode launch
     achieved = launch_bytes / t_decode / 1e9
@@ -216,7 +262,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp, 2 if wl.batch >= 2 else 1)
+        cpu = cpu_baseline(inp)
 
     rec = {
         "metric": "MLA decode tokens/s + latent-KV HBM GB/s (% of MI355X peak), 1 GPU",
@@ -236,10 +282,9 @@ def main():
                    "d_v": wl.d_v, "seq_len": int(inp.max_seq_len), "splits": S,
                    "cache": f"{wl.cache_dtype} {'paged' if wl.page_size else 'contiguous'}",
                    "partials": args.part_dtype, "replicas": R, "parallelism": "none (1 GPU)"},
-        "cache_GBps": cache_bytes / t_dc / 1e9,
-        "cache_pct_hbm_peak": 100.0 * cache_bytes / t_dc / 1e9 / HBM_PEAK_GBPS,
-        "kernel_us_mean": kernel_table(k_mean),
-        "kernel_us_median": kernel_table(k_med),
+        "cache_GBps": cache_bytes / t_decode / 1e9,
+        "cache_pct_hbm_peak": 100.0 * cache_bytes / t_decode / 1e9 / HBM_PEAK_GBPS,
+        "kernel_us_mean": kernel_us,
         "roofline": {"kernel": "mla_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes},
