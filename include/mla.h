@@ -117,10 +117,10 @@ typedef struct {
  *   q_abs[b][i][d_latent:+d_rope]  = q_rope[b][i][:]
  * q_nope [B][h][d_nope], q_rope [B][h][d_rope] (dtype q_dt, F32 or BF16);
  * w_uk [h][d_nope][d_latent] (w_dt, F32 or BF16); fp32 accumulation.
- * q_abs [B][h][d_latent+d_rope] in q_abs_dt: F32, BF16 (round to nearest
- * even) or FP8_E4M3, in which case q_abs_scale [B][h] receives one fp32
- * factor per (b, i) (amax/448) and q_abs holds RNE(x / factor); otherwise
- * q_abs_scale must be NULL. */
+ * q_abs [B][h][d_latent+d_rope] in q_abs_dt: F32 or BF16 (round to nearest
+ * even).  q_abs_scale is reserved for an FP8 query and must be NULL: q_abs_dt
+ * FP8_E4M3 returns MLA_E_UNSUPPORTED (an fp8 cache is read with a bf16
+ * query). */
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* q_nope,
                           const void* q_rope, int32_t q_dt, const void* w_uk,
                           int32_t w_dt, void* q_abs, int32_t q_abs_dt,
@@ -134,11 +134,14 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* q_nope,
  *   s_t  = scale * (q_abs[b][i][0:d_latent]·c_t + q_abs[b][i][d_latent:]·k_R,t)
  *   u_part[b][p][i][:] = sum_{t in R} e^{s_t} c_t / sum_{t in R} e^{s_t}
  *   lse_part[b][p][i]  = ln sum_{t in R} e^{s_t}      (natural log)
- * q_abs [B][h][d_latent+d_rope] (q_abs_dt); q_abs_scale [B][h] when q_abs is
- * FP8, else NULL.  u_part [B][num_splits][h][d_latent] in part_dt (F32 or
- * BF16); lse_part [B][num_splits][h] fp32.  1 <= num_splits <= 1024.
- * Provided dtype pairs (cache / q_abs): F32/F32, BF16/BF16, FP8/BF16,
- * FP8/FP8.  The BF16 and FP8 paths need h to be a multiple of 32. */
+ * q_abs [B][h][d_latent+d_rope] (q_abs_dt); q_abs_scale is reserved and must
+ * be NULL.  u_part [B][num_splits][h][d_latent] in part_dt (F32 or BF16);
+ * lse_part [B][num_splits][h] fp32.  1 <= num_splits <= 1024.
+ * Provided dtype pairs (cache / q_abs): F32/F32, BF16/BF16 and FP8/BF16;
+ * other pairs return MLA_E_DTYPE.  An FP8 cache is read as code * row_scale
+ * with every code widened exactly to bf16; the row scale multiplies the
+ * score, and the bf16-rounded probability in the PV product.  The BF16 and
+ * FP8 paths need h to be a multiple of 32. */
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
                         int32_t q_abs_dt, const float* q_abs_scale,
                         const mla_cache_t* cache, int32_t num_splits, void* u_part,

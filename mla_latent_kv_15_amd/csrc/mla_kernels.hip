@@ -46,27 +46,17 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 // binary32 -> bf16 bits, round to nearest even (NaN stays NaN)
 __device__ inline uint16_t f32_to_bf16(float f) { return static_cast<uint16_t>(pack_bf16x2(f, 0.0f)); }
 
-// OCP E4M3 code -> value.  Placing the 7 magnitude bits at binary32 bit 20
-// gives exponent field e and mantissa m/8 (or, for e = 0, the binary32
-// subnormal m*2^-129); multiplying by 2^120 rebases the exponent from bias 127
-// to bias 7, which is exact for normal and subnormal codes alike.
-__device__ inline float e4m3_to_f32(uint32_t code) {
-  float f = __uint_as_float((code & 0x7Fu) << 20) * 0x1p120f;
-  f = (code & 0x80u) ? -f : f;
-  return ((code & 0x7Fu) == 0x7Fu) ? __uint_as_float(0x7FC00000u) : f;
-}
-
-// 4 codes (one 32-bit word) -> 4 bf16 (two 32-bit words).  E4M3 values have at
-// most 4 significant bits, so the bf16 truncation of the binary32 is exact.
+// 4 OCP E4M3 codes (one 32-bit word, first code in the low byte) -> 4 bf16
+// (two words, same order) with v_cvt_scalef32_pk_bf16_fp8 at unit scale.
+// Exact: every E4M3 value, subnormals included, is a bf16 value; the two NaN
+// codes give NaN.
 __device__ inline u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
-  u32x2_t r;
-  const uint32_t b0 = __float_as_uint(e4m3_to_f32(w & 0xFFu)) >> 16;
-  const uint32_t b1 = __float_as_uint(e4m3_to_f32((w >> 8) & 0xFFu)) >> 16;
-  const uint32_t b2 = __float_as_uint(e4m3_to_f32((w >> 16) & 0xFFu)) >> 16;
-  const uint32_t b3 = __float_as_uint(e4m3_to_f32(w >> 24)) >> 16;
-  r.x = b0 | (b1 << 16);
-  r.y = b2 | (b3 << 16);
-  return r;
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  uint32_t x, y;
+  __builtin_memcpy(&x, &lo, 4);
+  __builtin_memcpy(&y, &hi, 4);
+  return u32x2_t{x, y};
 }
 
 template <int DT>
@@ -104,45 +94,34 @@ __device__ inline int64_t tile_row0(const int32_t* block_table, int32_t max_page
 
 // ================================================================ decode (MFMA)
 //
-// One workgroup = one (sequence b, split range p, group of up to 128 heads);
-// 4 waves, wave w owns 32 heads.  Per 32-token tile:
+// The bf16 and fp8 cache paths share one kernel design: one workgroup per
+// (sequence b, split range p, group of up to 64 heads).  Per 32-token tile:
 //   * the 32 cached rows are staged once in LDS as bf16 and shared by all
-//     waves.  bf16 rows travel HBM -> LDS directly (global_load_lds_dwordx4,
-//     16 bytes per lane, no VGPR staging); fp8 rows are loaded into VGPRs and
-//     widened exactly to bf16 on the way.  Rows are stored unpadded with the
-//     16-byte chunks of token t permuted by XOR (t & 7), which spreads both
-//     read patterns below over the LDS banks;
-//   * QK:  Sᵀ[t][h] = Σ_k tile[t][k] · q_abs[h][k]  — v_mfma_f32_32x32x16_bf16
-//     with the tile as A (k-contiguous 16-byte LDS reads) and the wave's
-//     absorbed queries as B, held in VGPRs for the whole range;
-//   * online softmax in the base-2 domain.  In the Sᵀ accumulator layout each
-//     lane owns one head (column = lane % 32), so the running max and sum need
-//     one cross-half exchange only.  The accumulator is rescaled only when a
-//     head's maximum grows by more than 2^8 (exact: numerator and denominator
-//     always share the same reference maximum);
-//   * PV:  Uᵀ[c][h] += Σ_t tile[t][c] · P[t][h] — the probabilities stay in the
-//     registers they were computed in (B operand); the latent, contracted over
-//     tokens here, is read from the same LDS tile with ds_read_b64_tr_b16
-//     transposing reads (A operand).
-// Tiles are double-buffered: the next tile's loads are in flight while the
-// current one is computed.  Tokens past the end of the range are loaded from
-// the range's first row instead (finite data; their probability is zero).
+//     heads of the workgroup.  bf16 rows travel HBM -> LDS directly
+//     (global_load_lds_dwordx4, no VGPR staging); fp8 rows pass through
+//     registers and are widened exactly to bf16 on their way in;
+//   * QK:  S[t][h] = sum_k tile[t][k] q_abs[h][k] on the matrix cores, the
+//     absorbed queries held in registers for the whole range;
+//   * a softmax with one reference maximum per head and range (below), in
+//     the base-2 domain;
+//   * PV:  Uᵀ[c][h] += sum_t tile[t][c] P[t][h] on the matrix cores, the
+//     latent read from the same LDS tile with transposing reads.
+// Tokens past the end of the range are loaded from the tile's first row
+// (finite data; their probability is zero).
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kHeadsPerBlock = kWaves * kHeadsPerWave;  // 128
-constexpr int kRowBytes = kRowElems * 2;                // 1152: bf16 row in LDS
-constexpr int kRowChunks = kRowBytes / 16;              // 72
-constexpr int kTileBytes = kTileTokens * kRowBytes;     // 36864
-constexpr int kBf16Chunks = kTileTokens * kRowChunks;   // 2304 x 16 B
-constexpr int kDmaPerWave = kBf16Chunks / 64 / kWaves;  // 9 wave-loads of 1 KB
-constexpr int kFp8RowChunks = kRowElems / 16;           // 36 x 16 B per fp8 row
-constexpr int kFp8Chunks = kTileTokens * kFp8RowChunks;               // 1152
-constexpr int kFp8PerThread = (kFp8Chunks + kThreads - 1) / kThreads;  // 5
-constexpr int kNBuf = 4;  // bf16 LDS tile buffers: up to 3 tiles in flight
-constexpr int kPBufBytes = 4 * 2048;
-constexpr int kQkAhead = 8;  // QK operand reads in flight  // bf16 probabilities of 4 head blocks x 32 tokens
-constexpr float kRefSlack = 64.0f;  // log2 units, see the softmax reference note
+constexpr int kRowBytes = kRowElems * 2;             // 1152: bf16 row in LDS
+constexpr int kTileBytes = kTileTokens * kRowBytes;  // 36864
+constexpr int kDmaPerWave = kTileBytes / 1024 / 4;   // 9 wave-loads of 1 KB per wave of 4
+constexpr int kNBuf = 4;                             // LDS tile buffers
+// Softmax reference.  The probabilities are taken relative to a reference
+// maximum m_ref (log2 domain) fixed at the first tile of the range instead of
+// the running maximum, so the accumulators are never rescaled.  A later score
+// may exceed m_ref by up to kRefSlack: probabilities then stay below
+// 2^kRefSlack, far from the bf16/fp32 range limits.  If any score exceeds it
+// (no realistic logit spread does), the range is computed again with m_ref set
+// to the true maximum found by the first pass.  Either way numerator and
+// denominator share one reference, so the result is exact.
+constexpr float kRefSlack = 64.0f;  // log2 units
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -162,422 +141,14 @@ struct DecodeParams {
   float* lse_part;
 };
 
-// 16-byte chunk c of token t sits at chunk position c ^ swz(t) of the token's
-// row (the XOR stays inside the aligned group of 8 chunks).  swz maps
-// t = 0..7 to 0,2,4,6,1,3,5,7: the QK operand reads (8 consecutive tokens, one
-// chunk) and the transposing reads (4 consecutive tokens, two neighbouring
-// chunks) both touch 8 different chunk positions, i.e. all 32 banks once.
-__device__ inline int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
-
-// byte offset in an LDS tile of 16-byte chunk c of token t
-__device__ inline int lds_chunk(int t, int c) { return t * kRowBytes + ((c ^ swz(t)) << 4); }
-
 __device__ inline uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
 }
 
-// bf16 tile: wave w fills LDS chunk slots [(4i + w)*64, +64) for i = 0..8; slot
-// s of token t = s / 72 holds chunk (s % 72) ^ swz(t).  The loads are issued as
-// inline asm: the compiler then does not know they write LDS and does not wait
-// for them before every LDS read (it cannot prove the reads do not alias); the
-// kernel waits for them itself.
-__device__ inline void tile_dma_bf16(const DecodeParams& P, const int32_t* __restrict__ block_table,
-                                     uint32_t lds_tile, int b, int t0, int nvalid, int wave,
-                                     int lane) {
-  const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
-  const uint8_t* base = P.rows + row0 * kRowBytes;
-  // the lane id is recomputed here (mbcnt) rather than kept live across the loop
-  (void)lane;
-  int ln;  // volatile: neither this nor the offsets below are hoisted out of the tile loop
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  wave = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: slot bases stay scalar
-#pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int slot = (i * kWaves + wave) * 64 + ln;
-    const int t = slot / kRowChunks;
-    const int c = (slot - t * kRowChunks) ^ swz(t);
-    const uint32_t off = static_cast<uint32_t>(((t < nvalid) ? t : 0) * kRowBytes + c * 16);
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_tile + (i * kWaves + wave) * 1024);
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0)
-                 : "memory");
-  }
-}
-
-struct Fp8Regs {
-  u32x4_t r[kFp8PerThread];
-  float scale;
-};
-
-__device__ inline void tile_load_fp8(Fp8Regs& R, const DecodeParams& P,
-                                     const int32_t* __restrict__ block_table, int b, int t0,
-                                     int nvalid, int tid) {
-  const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, t0);
-  const uint8_t* base = P.rows + row0 * kRowElems;
-#pragma unroll
-  for (int i = 0; i < kFp8PerThread; ++i) {
-    const int q = i * kThreads + tid;
-    const int t = q / kFp8RowChunks;
-    if (q < kFp8Chunks && t < nvalid)
-      R.r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base) + q);
-    else
-      R.r[i] = u32x4_t{0u, 0u, 0u, 0u};
-  }
-  R.scale = (tid < nvalid) ? P.row_scale[row0 + tid] : 0.0f;
-}
-
-__device__ inline void tile_store_fp8(const Fp8Regs& R, uint8_t* T, float* tscale, int tid) {
-#pragma unroll
-  for (int i = 0; i < kFp8PerThread; ++i) {
-    const int q = i * kThreads + tid;
-    if (q < kFp8Chunks) {
-      const int t = q / kFp8RowChunks, cc = q % kFp8RowChunks;
-      const u32x2_t a = e4m3x4_to_bf16x4(R.r[i].x), bb = e4m3x4_to_bf16x4(R.r[i].y);
-      const u32x2_t c = e4m3x4_to_bf16x4(R.r[i].z), d = e4m3x4_to_bf16x4(R.r[i].w);
-      *reinterpret_cast<u32x4_t*>(T + lds_chunk(t, 2 * cc)) = u32x4_t{a.x, a.y, bb.x, bb.y};
-      *reinterpret_cast<u32x4_t*>(T + lds_chunk(t, 2 * cc + 1)) = u32x4_t{c.x, c.y, d.x, d.y};
-    }
-  }
-  if (tid < kTileTokens) tscale[tid] = R.scale;
-}
-
-template <bool FP8, int PART_DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1)))
-void decode_mfma_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
-  constexpr int kBufs = FP8 ? 2 : kNBuf;
-  // tiles, then two probability buffers of 4 head blocks x 2 KiB
-  // (fp8: then the two tiles' row scales).  The bf16 layout uses all 160 KiB.
-  __shared__ __attribute__((aligned(1024)))
-  uint8_t smem[kBufs * kTileBytes + 2 * kPBufBytes + (FP8 ? 2 * kTileTokens * 4 : 0)];
-  uint8_t* pbuf = smem + kBufs * kTileBytes;
-  float (*sscale)[kTileTokens] = reinterpret_cast<float (*)[kTileTokens]>(pbuf + 2 * kPBufBytes);
-
-  const int nwork = P.B * P.S * P.HG;
-  const int wid = xcd_remap(blockIdx.x, nwork);
-  const int hg = wid % P.HG;
-  const int bp = wid / P.HG;
-  const int p = bp % P.S;
-  const int b = bp / P.S;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hl = lane & 31;  // head within a 32-head block (column of Sᵀ and Uᵀ)
-  const int g = lane >> 5;   // k-slot half
-  const int hbase = hg * kHeadsPerBlock;
-  // head blocks of this group: wave w computes QK/softmax for block w, and PV
-  // for every block over latent columns [128 w, 128 w + 128)
-  const int nhb = min(kWaves, (P.H - hbase) / kHeadsPerWave);  // workgroup-uniform
-  const bool qk_wave = wave < nhb;                              // wave-uniform
-  const int h = hbase + wave * kHeadsPerWave + hl;              // this lane's QK head
-
-  // lengths are clamped to [0, max_seq_len]: the cache is never read past it
-  const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
-  const int t_begin = p * P.chunk;
-  const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(b) * P.S + p) * P.H + hbase;  // u_part row of head hbase
-
-  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
-    if (qk_wave) {
-      const int64_t r = row_base + wave * kHeadsPerWave + hl;
-      for (int c = g; c < kDLatent; c += 2) store_elem<PART_DT>(P.u_part, r * kDLatent + c, 0.0f);
-      if (g == 0) P.lse_part[r] = -INFINITY;
-    }
-    return;
-  }
-
-  // transposing-read geometry of the PV A operand: lane (G = lane/16, e, q4)
-  // reads rows 16*j + 4*(G/2) + e and +8, columns 32*cb + 16*(G%2) + 4*q4 .. +3
-  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
-  const int tr_row = 4 * (G >> 1) + e;
-  const int tr_key = swz(tr_row);
-  const int tr_x = 2 * (G & 1) + (q4 >> 1);
-  const int tr_byte = 8 * (q4 & 1);
-  // column chunk 4*cb + tr_x: its low 3 bits are 4*(cb & 1) + tr_x
-  const int tr_off[2] = {((0 + tr_x) ^ tr_key) << 4, ((4 + tr_x) ^ tr_key) << 4};
-  // QK chunk 2*kk + g of token hl: its low 3 bits are 2*(kk & 3) + g
-  int qk_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) qk_off[i] = ((2 * i + g) ^ swz(hl)) << 4;
-
-  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-
-  // Softmax reference.  The probabilities are taken relative to a reference
-  // maximum m_ref (log2 domain) fixed at the first tile instead of the running
-  // maximum, so the accumulators are never rescaled.  A later score may exceed
-  // m_ref by up to kRefSlack: probabilities then stay below 2^kRefSlack, far
-  // from the bf16/fp32 range limits.  If any score exceeds it (no realistic
-  // logit spread does), the range is recomputed once with m_ref set to the
-  // true maximum found by the first pass.  Either way numerator and
-  // denominator share one reference, so the result is exact.
-  float m_ref = -INFINITY;
-  float m_seen = -INFINITY;  // true running max of head h
-  float l_run = 0.0f;        // this lane's share of the sum of probabilities
-  f32x16_t acc[kWaves * 4];  // Uᵀ blocks [head block][32-column block of this wave]
-
-  // absorbed queries of this wave's 32 heads as the B operand: lane (hl, g)
-  // holds q_abs[h][16*kk + 8*g .. +7] for kk = 0..35 (loaded after the first
-  // tile's loads are issued, so both are in flight together)
-  bf16x8_t qreg[kRowElems / 16];
-  const bf16x8_t* qrow = reinterpret_cast<const bf16x8_t*>(
-      static_cast<const uint16_t*>(P.q_abs) +
-      (static_cast<int64_t>(b) * P.H + (qk_wave ? h : hbase)) * kRowElems);
-
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int k = 0; k < kWaves * 4; ++k) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
-      asm volatile("" : "+a"(acc[k]));
-    }
-    // The PV MFMAs are inline asm, so the compiler cannot see the hazard
-    // between these accumulator writes and their first matrix-core read.
-    asm volatile("s_nop 4");
-    l_run = 0.0f;
-    int overflow = 0;
-
-    Fp8Regs R;
-    if constexpr (FP8) {
-      tile_load_fp8(R, P, block_table, b, t_begin, min(kTileTokens, t_end - t_begin), tid);
-      tile_store_fp8(R, smem, sscale[0], tid);
-      if (ntiles > 1) {
-        const int t1 = t_begin + kTileTokens;
-        tile_load_fp8(R, P, block_table, b, t1, min(kTileTokens, t_end - t1), tid);
-      }
-      __syncthreads();
-    } else {
-      tile_dma_bf16(P, block_table, lds_addr(smem), b, t_begin, min(kTileTokens, t_end - t_begin),
-                    wave, lane);
-    }
-    if (pass == 0 && qk_wave) {
-#pragma unroll
-      for (int kk = 0; kk < kRowElems / 16; ++kk) qreg[kk] = qrow[2 * kk + g];
-      // Consume the query loads here, once: otherwise the compiler keeps its
-      // waits for them inside the tile loop, where they would also drain the
-      // tile loads that are meant to stay in flight.  (Tile 0 was issued
-      // before the queries, so this also waits for it.)
-#pragma unroll
-      for (int kk = 0; kk < kRowElems / 16; ++kk) asm volatile("" : "+v"(qreg[kk]));
-    }
-    if constexpr (!FP8) {
-      // tiles 1 .. kNBuf-2 go out after that wait, so it does not cover them
-      for (int d = 1; d < kNBuf - 1 && d < ntiles; ++d) {
-        const int td = t_begin + d * kTileTokens;
-        tile_dma_bf16(P, block_table, lds_addr(smem) + d * kTileBytes, b, td,
-                      min(kTileTokens, t_end - td), wave, lane);
-      }
-    }
-
-    for (int it = 0; it < ntiles; ++it) {
-      const int buf = FP8 ? (it & 1) : (it & (kNBuf - 1));
-      uint8_t* T = smem + buf * kTileBytes;
-      uint8_t* PB = pbuf + (it & 1) * kPBufBytes;
-      const int t0 = t_begin + it * kTileTokens;
-      if constexpr (!FP8) {
-        // tile `it` has landed once at most 9 loads per later tile in flight
-        // remain outstanding; then every wave's share is visible after the
-        // barrier, and the buffer read in the previous iteration is free
-        const int later = min(ntiles, it + kNBuf - 1) - it - 1;
-        if (later >= 2)
-          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else if (later == 1)
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        asm volatile("s_barrier" ::: "memory");
-        if (it + kNBuf - 1 < ntiles) {
-          const int tn = t0 + (kNBuf - 1) * kTileTokens;
-          tile_dma_bf16(P, block_table, lds_addr(smem) + ((it + kNBuf - 1) & (kNBuf - 1)) * kTileBytes,
-                        b, tn, min(kTileTokens, t_end - tn), wave, lane);
-        }
-      }
-      bf16x8_t pk[2];
-      if (qk_wave) {
-        // ---- QK: Sᵀ (32 tokens x 32 heads) over the 576-wide row.  Issued as
-        //      inline asm so that Sᵀ lives in VGPRs: the 256 AGPRs hold Uᵀ.
-        f32x16_t s;
-        const uint8_t* arow = T + hl * kRowBytes;
-        auto qk_read = [&](int kk) {
-          return *reinterpret_cast<const bf16x8_t*>(arow + qk_off[kk & 3] + (kk >> 2) * 128);
-        };
-        // operand ring: kQkAhead LDS reads stay in flight ahead of the MFMAs
-        bf16x8_t ring[kQkAhead];
-#pragma unroll
-        for (int i = 0; i < kQkAhead; ++i) ring[i] = qk_read(i);
-#pragma unroll
-        for (int kk = 0; kk < kRowElems / 16; ++kk) {
-          const bf16x8_t a = ring[kk % kQkAhead];
-          if (kk + kQkAhead < kRowElems / 16) ring[kk % kQkAhead] = qk_read(kk + kQkAhead);
-          if (kk == 0)
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(qreg[kk]));
-          else
-            asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(qreg[kk]));
-          if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-        }
-        // the compiler does not see the asm results as MFMA writes: wait out
-        // the matrix-core-write -> VALU-read hazard before Sᵀ is read
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-        // ---- softmax.  Register r of lane (hl, g) holds token
-        //      8*(r/4) + 4*g + r%4 of the tile, head h.
-        const int nvalid = t_end - t0;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[r] * P.scale_log2;
-          if constexpr (FP8) v *= sscale[buf][8 * (r >> 2) + 4 * g + (r & 3)];
-          s[r] = v;
-        }
-        if (nvalid < kTileTokens) {  // partial last tile: drop absent tokens
-          const int nv = nvalid - 4 * g;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[r] = (8 * (r >> 2) + (r & 3) < nv) ? s[r] : -INFINITY;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (pass == 0 && it == 0) m_ref = mx;
-        m_seen = fmaxf(m_seen, mx);
-        overflow |= (mx > m_ref + kRefSlack);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = exp2f(s[r] - m_ref);
-          l_run += pr;
-          if constexpr (FP8) pr *= sscale[buf][8 * (r >> 2) + 4 * g + (r & 3)];
-          pk[r >> 3][r & 7] = static_cast<__bf16>(pr);
-        }
-        // publish this head block's probabilities (B operands, lane order)
-        *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + lane * 16) = pk[0];
-        *reinterpret_cast<bf16x8_t*>(PB + wave * 2048 + 1024 + lane * 16) = pk[1];
-      }
-      asm volatile("s_barrier" ::: "memory");
-      // ---- PV: Uᵀ[c][h] += Σ_t tile[t][c] P[t][h] for this wave's 128
-      //      columns and every head block.  The transposed tile operands are
-      //      read once and reused for all head blocks.
-      {
-        const uint8_t* r0 = T + tr_row * kRowBytes + tr_byte;
-        bf16x8_t av[4][2];
-#pragma unroll
-        for (int cbl = 0; cbl < 4; ++cbl) {
-          const int cb = 4 * wave + cbl;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 128 + 16 * j * kRowBytes;
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
-            const bf16x4_t hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + 8 * kRowBytes));
-            av[cbl][j] = bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-        }
-#pragma unroll
-        for (int hb = 0; hb < kWaves; ++hb) {
-          if (hb < nhb) {
-            bf16x8_t pb0 = *reinterpret_cast<const bf16x8_t*>(PB + hb * 2048 + lane * 16);
-            bf16x8_t pb1 = *reinterpret_cast<const bf16x8_t*>(PB + hb * 2048 + 1024 + lane * 16);
-#pragma unroll
-            for (int cbl = 0; cbl < 4; ++cbl) {
-              asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                  : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl][0]), "v"(pb0));
-              asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                  : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl][1]), "v"(pb1));
-            }
-          }
-        }
-      }
-      if constexpr (FP8) {
-        if (it + 1 < ntiles) {
-          tile_store_fp8(R, smem + (buf ^ 1) * kTileBytes, sscale[buf ^ 1], tid);
-          if (it + 2 < ntiles) {
-            const int t2 = t_begin + (it + 2) * kTileTokens;
-            tile_load_fp8(R, P, block_table, b, t2, min(kTileTokens, t_end - t2), tid);
-          }
-        }
-        __syncthreads();
-      }
-    }
-    // Every wave takes the same number of passes (the tile loop has
-    // barriers).  The votes go to the buffer that tile `ntiles` would use:
-    // nothing is loaded into it and no wave reads it any more.
-    int* votes = reinterpret_cast<int*>(smem + (ntiles & (kBufs - 1)) * kTileBytes);
-    const int any_wave = __any(overflow) ? 1 : 0;
-    if (lane == 0) votes[wave] = any_wave;
-    __syncthreads();
-    const int again = votes[0] | votes[1] | votes[2] | votes[3];
-    __syncthreads();
-    if (!again) break;
-    m_ref = m_seen;
-  }
-
-  // ---- epilogue.  Normalisers of all head blocks via LDS (the tile buffers
-  //      are free now): linv[32*hb + hl] = 1 / Σ p of that head.
-  float* linv = reinterpret_cast<float*>(smem);
-  uint8_t* stage = smem + 1024;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qk_wave) {
-    if (g == 0) {
-      linv[wave * kHeadsPerWave + hl] = 1.0f / l_tot;
-      P.lse_part[row_base + wave * kHeadsPerWave + hl] = (m_ref + log2f(l_tot)) * kLn2;
-    }
-  }
-  __syncthreads();
-  // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-  // Uᵀ register r of block (hb, cbl) in lane (hl, g) is column
-  // 128*wave + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
-  // wave stages one head block (32 rows x 128 columns) at a time in its own
-  // LDS region and writes 256 contiguous bytes per row.
-  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
-  constexpr int kColsRound = 256 / kEsz;                  // 128 bf16 / 64 fp32 columns
-  constexpr int kStageRow = kColsRound * kEsz + 16;       // padded: rows start 4 banks apart
-  uint8_t* W = stage + wave * kHeadsPerWave * kStageRow;
-#pragma unroll
-  for (int hb = 0; hb < kWaves; ++hb) {
-    if (hb < nhb) {
-      const float inv = linv[hb * kHeadsPerWave + hl];
-#pragma unroll
-      for (int half = 0; half < 128 / kColsRound; ++half) {
-#pragma unroll
-        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
-          const int cbl = half * (kColsRound / 32) + cbl2;
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
-            const f32x16_t& A = acc[4 * hb + cbl];
-            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
-            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
-            uint8_t* wp = W + hl * kStageRow + c * kEsz;
-            if constexpr (PART_DT == MLA_F32) {
-              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
-            } else {
-              const uint32_t w0 = pack_bf16x2(v0, v1);
-              const uint32_t w1 = pack_bf16x2(v2, v3);
-              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{w0, w1};
-            }
-          }
-        }
-        // one wave's LDS operations complete in order: no barrier is needed
-        asm volatile("" ::: "memory");
-        // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
-        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
-                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * wave) * kEsz +
-                       half * (kColsRound * kEsz);
-#pragma unroll
-        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
-          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
-                                      (lane & 15) * 16) = v;
-        }
-        asm volatile("" ::: "memory");
-      }
-    }
-  }
-}
-
-// ================================================================ decode (bf16)
+// ================================================================ decode: tile layout
 //
-// Shared pieces of the bf16 cache path: the work unit is (sequence b, split
-// range p, group of up to 64 heads); tiles of 32 tokens sit in LDS in the
-// token-group layout below.
+// The work unit is (sequence b, split range p, group of up to 64 heads);
+// tiles of 32 tokens sit in LDS as bf16 in the token-group layout below.
 
 constexpr int kH64 = 64;                 // heads per workgroup
 constexpr int kH64Blocks = 2;            // head blocks of 32
@@ -595,8 +166,7 @@ constexpr int kX64Off = kNBuf * kTileBytes + 2 * kP64Bytes;  // exchange area (f
 // was chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950) among the
 // permutations of the 8 rows of a group: with it neither operand read pattern
 // has bank conflicts -- the QK read (16 lanes = one chunk of 8 rows in each of
-// two groups) nor the transposing PV read (4 rows x 2 chunks x 2 halves);
-// the pattern of the fp8 path, swz, costs the QK read one extra pass.
+// two groups) nor the transposing PV read (4 rows x 2 chunks x 2 halves).
 constexpr int kTokGroupBytes = 8 * kRowBytes;  // 9216
 
 __device__ inline int swzg(int t) { return (5 * (t & 7)) & 7; }
@@ -636,7 +206,7 @@ __device__ inline void rows_dma_g8(const uint8_t* base, uint32_t lds_tile, int n
   for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
 }
 
-// ================================================================ decode (bf16, warp-specialised)
+// ================================================================ decode (warp-specialised)
 //
 // One workgroup per (sequence b, split range p, 64 heads), 8 waves, two per
 // SIMD, in two roles:
@@ -652,18 +222,34 @@ __device__ inline void rows_dma_g8(const uint8_t* base, uint32_t lds_tile, int n
 // meet at one barrier per tile; their register footprints (queries vs
 // accumulators) share the same AGPRs because each role's code is a separate
 // region of the kernel.
+//
+// fp8 caches (FP8 = true): the PV waves load the codes of tile i+4 into
+// registers while the MFMAs of tile i run, and widen tile i+2 (loaded two
+// tiles earlier) into the same bf16 layout; the row scales go to a small LDS
+// array.  The scores are multiplied by the row scales after the QK product,
+// and the published probabilities carry them into the PV product.
 
 constexpr int kWsThreads = 512;
 
-template <int PART_DT>
+// fp8 rows in flight in a PV wave's registers: lane (k = lane / 8, j = lane % 8)
+// of PV wave w holds, for i = 0..8, the 8 codes of bf16 chunk 8 i + (j ^ swzg(t))
+// of row t = 8 w + k (the chunk that the token-group layout puts at slot j of
+// line (i, t)), and that row's scale
+struct Fp8Rows {
+  u32x2_t w[kDmaPerWave];
+  float sc;
+};
+
+template <bool FP8, int PART_DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kX64Off + 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kX64Off + (FP8 ? 1536 : 1024)];
   uint8_t* pbuf = smem + kNBuf * kTileBytes;
   float* xch = reinterpret_cast<float*>(smem + kX64Off);  // [2][64] per-head exchange
   int* votes = reinterpret_cast<int*>(smem + kX64Off + 512);
   float* linv = reinterpret_cast<float*>(smem);  // epilogue: 1 / l per head (tile buffer 0)
+  float* tscale = reinterpret_cast<float*>(smem + kX64Off + 1024);  // fp8: [kNBuf][32] row scales
 
   const int nwork = P.B * P.S * P.HG;
   const int wid = xcd_remap(blockIdx.x, nwork);
@@ -694,6 +280,10 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     return;
   }
   const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
+  // fp8: the PV loop runs in pairs of tiles (one register set each), so an odd
+  // range gets one more tile: it is loaded from the range's first rows and all
+  // of its tokens are masked, which adds exact zeros
+  const int ntp = FP8 ? ((ntiles + 1) & ~1) : ntiles;
 
   // all s_barriers below are issued by both roles in the same order:
   //   Q1 Q2 | per pass: T0 [AM AM] B_0..B_{n-1} V1 V2 [AM AM] | E1 E2
@@ -760,7 +350,18 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
       }
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
     };
-    auto softmax_publish = [&](f32x4_t (&s)[2], int tile, int& overflow, uint8_t* PB) {
+    // fp8: scores of the raw codes times the row scales of tokens
+    // 16 th + 4 kg + r; returns the scales for the probabilities
+    auto row_scale = [&](f32x4_t (&s)[2], int buf) {
+      const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(tscale + buf * kTileTokens + 16 * th + 4 * kg);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[hh][r] *= sc[r];
+      return sc;
+    };
+    auto softmax_publish = [&](f32x4_t (&s)[2], const f32x4_t& sc, int tile, int& overflow,
+                               uint8_t* PB) {
       const int nvalid = t_end - (t_begin + tile * kTileTokens);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -784,6 +385,12 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
         for (int r = 0; r < 4; ++r) {
           pr[r] = __builtin_amdgcn_exp2f(s[hh][r] - m_ref[hh]);  // v_exp_f32
           l_run[hh] += pr[r];
+        }
+        // fp8: the PV product takes the raw codes, so the probability carries
+        // the row scale (the sum l does not)
+        if constexpr (FP8) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pr[r] *= sc[r];
         }
         // B-operand slot of token 16th + 4kg + r: k-step th, lane group kg & 1,
         // slots 4 (kg >> 1) + r of head 32 qhb + 16 hh + n16
@@ -817,7 +424,11 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
       int overflow = 0;
       barrier();  // T0: tile 0 landed
       f32x4_t s[2];
-      if (active) qk_tile(smem, s);
+      f32x4_t sc = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (active) {
+        qk_tile(smem, s);
+        if constexpr (FP8) sc = row_scale(s, 0);
+      }
       if (pass == 0) {  // reference: maximum of the first tile
         float mx[2] = {-INFINITY, -INFINITY};
         if (active) {
@@ -832,12 +443,14 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
         m_ref[0] = mx[0];
         m_ref[1] = mx[1];
       }
-      if (active) softmax_publish(s, 0, overflow, pbuf);
-      for (int i = 0; i < ntiles; ++i) {
+      if (active) softmax_publish(s, sc, 0, overflow, pbuf);
+      for (int i = 0; i < ntp; ++i) {
         barrier();  // B_i: P(i) published, tile i+1 landed
-        if (active && i + 1 < ntiles) {
-          qk_tile(smem + ((i + 1) & (kNBuf - 1)) * kTileBytes, s);
-          softmax_publish(s, i + 1, overflow, pbuf + ((i + 1) & 1) * kP64Bytes);
+        if (active && i + 1 < ntp) {
+          const int buf = (i + 1) & (kNBuf - 1);
+          qk_tile(smem + buf * kTileBytes, s);
+          if constexpr (FP8) sc = row_scale(s, buf);
+          softmax_publish(s, sc, i + 1, overflow, pbuf + ((i + 1) & 1) * kP64Bytes);
         }
       }
       if (lane == 0) votes[wave] = __any(overflow) ? 1 : 0;
@@ -885,35 +498,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   const int tr_off[2] = {((0 + tr_x) ^ tr_key) << 4, ((4 + tr_x) ^ tr_key) << 4};
   f32x16_t acc[kH64Blocks * 4];
 
-  auto dma_plan = [&](int tile) {
-    const int tt = t_begin + tile * kTileTokens;
-    const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
-    return rows_dma_plan(P.rows + row0 * kRowBytes, lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes,
-                         min(kTileTokens, t_end - tt), rw);
-  };
-  auto dma = [&](int tile) {
-    const RowsDma d = dma_plan(tile);
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
-  };
-
-  // the queries of both head blocks (32 rows each) into tile buffers 2 and 3,
-  // then tiles 0 and 1
-  const uint8_t* qsrc = static_cast<const uint8_t*>(P.q_abs) +
-                        (static_cast<int64_t>(b) * P.H + hbase) * kRowBytes;
-  for (int hb = 0; hb < nhb; ++hb)
-    rows_dma_g8(qsrc + hb * kHeadsPerWave * kRowBytes, lds_addr(smem) + (2 + hb) * kTileBytes,
-                kTileTokens, rw);
-  dma(0);
-  if (ntiles > 1) dma(1);
-  if (ntiles > 1)
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  barrier();  // Q1
-  barrier();  // Q2
-
-  for (int pass = 0; pass < 2; ++pass) {
+  auto zero_acc = [&] {
 #pragma unroll
     for (int k = 0; k < kH64Blocks * 4; ++k) {
 #pragma unroll
@@ -921,76 +506,210 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
       asm volatile("" : "+a"(acc[k]));
     }
     asm volatile("s_nop 4");  // accumulator writes -> first (inline-asm) MFMA read
-    if (pass > 0) {
-      dma(0);
-      if (ntiles > 1) dma(1);
+  };
+  // Uᵀ += tile i ⋅ P(i): 16 MFMAs; after_mfma(st) runs after MFMA st (the
+  // staging of a later tile is spread between them)
+  auto pv_tile = [&](int i, auto&& after_mfma) {
+    const uint8_t* T = smem + (i & (kNBuf - 1)) * kTileBytes;
+    const uint8_t* PB = pbuf + (i & 1) * kP64Bytes;
+    const uint8_t* r0 = T + tr_row * 128 + tr_byte;
+    auto load_av = [&](int cbl, int j) {
+      const int cb = 4 * rw + cbl;
+      const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 1024 + 2 * j * kTokGroupBytes;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
+      const bf16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + kTokGroupBytes));
+      return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8_t pb[2][2];  // [token half j][head block]
+    bf16x8_t av[4][2];  // [column block][token half j]
+#pragma unroll
+    for (int cbl = 0; cbl < 4; ++cbl) {
+      av[cbl][0] = load_av(cbl, 0);
+      av[cbl][1] = load_av(cbl, 1);
     }
-    if (ntiles > 2) dma(2);
-    if (ntiles > 2)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        pb[j][hb] = *reinterpret_cast<const bf16x8_t*>(PB + ((j * 2 + hb) * 64 + lane) * 16);
+    // MFMA st: column block st / 4, token half (st / 2) % 2, head block st % 2.
+    // Head blocks beyond nhb multiply stale probabilities into accumulators
+    // that are never stored.
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int cbl = st >> 2, j = (st >> 1) & 1, hb = st & 1;
+      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+          : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl][j]), "v"(pb[j][hb]));
+      after_mfma(st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // the queries of both head blocks (32 rows each) go into tile buffers 2 and 3
+  const uint8_t* qsrc = static_cast<const uint8_t*>(P.q_abs) +
+                        (static_cast<int64_t>(b) * P.H + hbase) * kRowBytes;
+  auto stage_q = [&] {
+    for (int hb = 0; hb < nhb; ++hb)
+      rows_dma_g8(qsrc + hb * kHeadsPerWave * kRowBytes, lds_addr(smem) + (2 + hb) * kTileBytes,
+                  kTileTokens, rw);
+  };
+
+  if constexpr (!FP8) {
+    auto dma_plan = [&](int tile) {
+      const int tt = t_begin + tile * kTileTokens;
+      const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
+      return rows_dma_plan(P.rows + row0 * kRowBytes, lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes,
+                           min(kTileTokens, t_end - tt), rw);
+    };
+    auto dma = [&](int tile) {
+      const RowsDma d = dma_plan(tile);
+#pragma unroll
+      for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
+    };
+
+    // queries, then tiles 0 and 1
+    stage_q();
+    dma(0);
+    if (ntiles > 1) dma(1);
+    if (ntiles > 1)
       asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if (ntiles > 1)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    barrier();  // T0
-    if (pass == 0) {
-      barrier();  // AM
-      barrier();  // AM
-    }
-    for (int i = 0; i < ntiles; ++i) {
-      if (i + 2 < ntiles)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    barrier();  // Q1
+    barrier();  // Q2
+
+    for (int pass = 0; pass < 2; ++pass) {
+      zero_acc();
+      if (pass > 0) {
+        dma(0);
+        if (ntiles > 1) dma(1);
+      }
+      if (ntiles > 2) dma(2);
+      if (ntiles > 2)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      else if (ntiles > 1)
         asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      barrier();  // B_i
-      // tile i+3 into tile i-1's buffer, one wave instruction per MFMA below
-      const bool dnext = i + 3 < ntiles;  // workgroup-uniform
-      RowsDma dp{};
-      if (dnext) dp = dma_plan(i + 3);
-      const uint8_t* T = smem + (i & (kNBuf - 1)) * kTileBytes;
-      const uint8_t* PB = pbuf + (i & 1) * kP64Bytes;
-      const uint8_t* r0 = T + tr_row * 128 + tr_byte;
-      auto load_av = [&](int cbl, int j) {
-        const int cb = 4 * rw + cbl;
-        const uint8_t* ptr = r0 + tr_off[cb & 1] + (cb >> 1) * 1024 + 2 * j * kTokGroupBytes;
-        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ptr);
-        const bf16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + kTokGroupBytes));
-        return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      };
-      bf16x8_t pb[2][2];  // [token half j][head block]
-      bf16x8_t av[4][2];  // [column block][token half j]
-#pragma unroll
-      for (int cbl = 0; cbl < 4; ++cbl) {
-        av[cbl][0] = load_av(cbl, 0);
-        av[cbl][1] = load_av(cbl, 1);
+      barrier();  // T0
+      if (pass == 0) {
+        barrier();  // AM
+        barrier();  // AM
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          pb[j][hb] = *reinterpret_cast<const bf16x8_t*>(PB + ((j * 2 + hb) * 64 + lane) * 16);
-      // MFMA st: column block st / 4, token half (st / 2) % 2, head block st % 2.
-      // Head blocks beyond nhb multiply stale probabilities into accumulators
-      // that are never stored.
-#pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        const int cbl = st >> 2, j = (st >> 1) & 1, hb = st & 1;
-        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-            : "+a"(acc[4 * hb + cbl]) : "v"(av[cbl][j]), "v"(pb[j][hb]));
-        if (dnext && st < kDmaPerWave) rows_dma_issue(dp, st);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < ntiles; ++i) {
+        if (i + 2 < ntiles)
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();  // B_i
+        // tile i+3 into tile i-1's buffer, one wave instruction per MFMA
+        const bool dnext = i + 3 < ntiles;  // workgroup-uniform
+        RowsDma dp{};
+        if (dnext) dp = dma_plan(i + 3);
+        pv_tile(i, [&](int st) {
+          if (dnext && st < kDmaPerWave) rows_dma_issue(dp, st);
+        });
       }
+      if (lane == 0) votes[wave] = 0;
+      barrier();  // V1
+      int again = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) again |= votes[w];
+      barrier();  // V2
+      if (!again) break;
+      barrier();  // AM
+      barrier();  // AM
     }
-    if (lane == 0) votes[wave] = 0;
-    barrier();  // V1
-    int again = 0;
+  } else {
+    // fp8 rows travel through registers: tile k is loaded two tiles ahead of
+    // its conversion, into register set k % 2, and widened to bf16 on its way
+    // into the same token-group layout as the bf16 path
+    auto f8_load = [&](Fp8Rows& S, int tile) {
+      // tiles past the range (the padding tile, and the loads issued ahead of
+      // the last iterations, whose registers are never read) read the last
+      // tile again: every wave then issues the same loads in every iteration,
+      // which keeps the compiler's wait counts exact
+      const int tc = min(tile, ntiles - 1);
+      const int tt = t_begin + tc * kTileTokens;
+      const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
+      const int nvalid = min(kTileTokens, t_end - tt);
+      int ln;  // volatile: recomputed per call rather than kept live across the loop
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int t = 8 * rw + (ln >> 3);
+      const int tr = t < nvalid ? t : 0;  // rows past the end: the tile's first row
+      const uint8_t* base = P.rows + row0 * kRowElems;  // wave-uniform
+      const uint32_t off = static_cast<uint32_t>(tr * kRowElems + ((ln & 7) ^ swzg(t)) * 8);
+      S.sc = (P.row_scale + row0)[tr];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) again |= votes[w];
-    barrier();  // V2
-    if (!again) break;
-    barrier();  // AM
-    barrier();  // AM
+      for (int i = 0; i < kDmaPerWave; ++i)
+        S.w[i] = *reinterpret_cast<const u32x2_t*>(base + off + 64 * i);
+    };
+    auto f8_store_chunk = [&](const Fp8Rows& S, int buf, int i) {
+      uint8_t* T = smem + buf * kTileBytes + rw * kTokGroupBytes + 1024 * i + lane * 16;
+      const u32x2_t lo = e4m3x4_to_bf16x4(S.w[i].x), hi = e4m3x4_to_bf16x4(S.w[i].y);
+      *reinterpret_cast<u32x4_t*>(T) = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    };
+    auto f8_store_scale = [&](const Fp8Rows& S, int buf) {
+      if ((lane & 7) == 0) tscale[buf * kTileTokens + 8 * rw + (lane >> 3)] = S.sc;
+    };
+    auto f8_store = [&](const Fp8Rows& S, int buf) {
+#pragma unroll
+      for (int i = 0; i < kDmaPerWave; ++i) f8_store_chunk(S, buf, i);
+      f8_store_scale(S, buf);
+    };
+    // iteration i: Uᵀ of tile i, tile i+2 from set S into LDS, then tile i+4
+    // into S.  With a set in flight for each of the next two tiles, the
+    // compiler's waits before each conversion leave the other set's loads
+    // outstanding.
+    auto f8_iter = [&](int i, Fp8Rows& S) {
+      barrier();  // B_i
+      const bool conv = i + 2 < ntp;  // workgroup-uniform
+      const int cb = (i + 2) & (kNBuf - 1);
+      pv_tile(i, [&](int st) {
+        if (conv && st == 0) f8_store_scale(S, cb);
+        if (conv && st < kDmaPerWave) f8_store_chunk(S, cb, st);
+        if (st == kDmaPerWave + 1) f8_load(S, i + 4);
+      });
+    };
+
+    Fp8Rows A, B;
+    stage_q();
+    f8_load(A, 0);
+    f8_load(B, 1);
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");  // queries (and tile 0) landed
+    barrier();  // Q1
+    barrier();  // Q2
+
+    for (int pass = 0; pass < 2; ++pass) {
+      zero_acc();
+      if (pass > 0) {
+        f8_load(A, 0);
+        f8_load(B, 1);
+      }
+      f8_store(A, 0);
+      f8_load(A, 2);
+      barrier();  // T0
+      if (pass == 0) {
+        barrier();  // AM
+        barrier();  // AM
+      }
+      f8_store(B, 1);
+      f8_load(B, 3);
+      for (int i = 0; i < ntp; i += 2) {
+        f8_iter(i, A);
+        f8_iter(i + 1, B);
+      }
+      if (lane == 0) votes[wave] = 0;
+      barrier();  // V1
+      int again = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) again |= votes[w];
+      barrier();  // V2
+      if (!again) break;
+      barrier();  // AM
+      barrier();  // AM
+    }
   }
 
   barrier();  // E1
@@ -1788,27 +1507,24 @@ extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void
       decode_f32_kernel<MLA_BF16><<<static_cast<unsigned>(nblk), kF32Threads, 0, s>>>(P);
     return launch_status();
   }
-  const int32_t HG = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  // workgroups of 64 heads
+  const int32_t HG64 = (H + kH64 - 1) / kH64;
+  const int64_t nblk64 = static_cast<int64_t>(B) * num_splits * HG64;
+  if (nblk64 > 0x7FFFFFFF) return MLA_E_SHAPE;
+  const unsigned grid64 = static_cast<unsigned>(nblk64);
   DecodeParams P{q_abs, static_cast<const uint8_t*>(cache->rows), cache->row_scale,
                  cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
-                 cache->page_size != 0, B, H, num_splits, HG, chunk, cache->max_seq_len,
+                 cache->page_size != 0, B, H, num_splits, HG64, chunk, cache->max_seq_len,
                  scale * kLog2e, u_part, lse_part};
-  const int64_t nblk = static_cast<int64_t>(B) * num_splits * HG;
-  if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
-  const unsigned grid = static_cast<unsigned>(nblk);
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
-  if (!fp8) {
-    // bf16 cache: workgroups of 64 heads
-    const int32_t HG64 = (H + kH64 - 1) / kH64;
-    const int64_t nblk64 = static_cast<int64_t>(B) * num_splits * HG64;
-    if (nblk64 > 0x7FFFFFFF) return MLA_E_SHAPE;
-    P.HG = HG64;
-    if (part_dt == MLA_F32)
-      decode_ws_kernel<MLA_F32><<<static_cast<unsigned>(nblk64), kWsThreads, 0, s>>>(P, cache->block_table);
-    else
-      decode_ws_kernel<MLA_BF16><<<static_cast<unsigned>(nblk64), kWsThreads, 0, s>>>(P, cache->block_table);
-  } else if (part_dt == MLA_F32) decode_mfma_kernel<true, MLA_F32><<<grid, kThreads, 0, s>>>(P, cache->block_table);
-  else decode_mfma_kernel<true, MLA_BF16><<<grid, kThreads, 0, s>>>(P, cache->block_table);
+  if (fp8 && part_dt == MLA_F32)
+    decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
+  else if (fp8)
+    decode_ws_kernel<true, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
+  else if (part_dt == MLA_F32)
+    decode_ws_kernel<false, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
+  else
+    decode_ws_kernel<false, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
   return launch_status();
 }
 

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from tests.mla_cases import (TOL, DeviceInputs, check_against_oracle, run_step, sample_pairs)
 
@@ -80,6 +81,36 @@ def test_fp8_small():
     pairs = [(b, h) for b in range(4) for h in (0, 31, 64, 127)]
     e = check_against_oracle(dev, step, pairs, TOL["fp8"])
     _log(f"fp8 small: err o/u/lse = {e}")
+
+
+def test_fp8_codes_exact():
+    """Every finite E4M3 code reaches the PV product unchanged.  With a zero
+    query every probability is 1; each sequence holds one row of codes 32
+    times (every position of a tile) with a power-of-two scale, so u is that
+    row times its scale with no rounding at all, and is compared for equality
+    with the oracle's own E4M3 decoder."""
+    wl = synth.workload("fp8_b1_l128k").with_(batch=8, seq_len=32, num_splits=1,
+                                             seed=synth.workloads.BASE_SEED + 108)
+    inp = synth.make_inputs(wl)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    width = inp.rows.shape[1]
+    want = []
+    for b in range(wl.batch):
+        codes = np.roll(np.resize(finite, width), 37 * b)
+        scale = np.float32(2.0 ** -(b % 4 + 1))
+        for t in range(wl.seq_len):
+            r = inp.row_index(b, t)
+            inp.rows[r] = codes
+            inp.row_scale[r] = scale
+        want.append(oracle.decode_array(codes[:wl.d_latent], "fp8") * float(scale))
+    dev = DeviceInputs(inp)
+    dev.q_nope.zero_()
+    dev.q_rope.zero_()
+    step = run_step(dev, 1, part_dtype=torch.float32, out_dtype=torch.float32)
+    u = step.u_part.float().cpu().numpy()  # [B, 1, H, d_latent]
+    for b in range(wl.batch):
+        got = u[b, 0].astype(np.float64)
+        assert np.array_equal(got, np.broadcast_to(want[b], got.shape)), b
 
 
 def test_paged_matches_contiguous_bitwise():
