@@ -1279,8 +1279,9 @@ __global__ __launch_bounds__(kUpThreads) void up_proj_mfma_kernel(const uint16_t
 // mla_combine followed by mla_up_proj in one kernel, for bf16 W_UV: one
 // workgroup of 8 waves per (head h, 16 consecutive sequences).
 //   1. the u rows of the 16 sequences are merged from the split partials with
-//      log-sum-exp weights (32 lanes per row, 16 latent columns per lane) and
-//      rounded to bf16 into LDS — the same values mla_combine stores;
+//      log-sum-exp weights (32 lanes per row and split phase, 16 latent
+//      columns per lane; fewer sequences get more phases) and rounded to bf16
+//      into LDS — the values mla_combine stores, up to summation order;
 //   2. o[b][h][:] = W_UV[h] u[b] on v_mfma_f32_16x16x32_bf16 (M = 16
 //      sequences, N = 16 value rows per wave, K = 32 latent columns): A = u
 //      from LDS, B = rows of W_UV, 16 contiguous bytes per lane from global
@@ -1298,7 +1299,8 @@ template <int PART_DT, int O_DT>
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     const void* u_part, const float* lse_part, const uint16_t* w_uv, void* o, uint16_t* u_out,
     float* lse_out, int B, int H, int S, int d_v) {
-  __shared__ __attribute__((aligned(16))) uint8_t us[kCuRows * kCuRow];
+  // u rows (bf16), then the per-group fp32 sums of the phase reduction
+  __shared__ __attribute__((aligned(16))) uint8_t us[kCuRows * kCuRow + kCuRows * 32 * 64];
   const int nbt = (B + kCuRows - 1) / kCuRows;
   const int wid = xcd_remap(blockIdx.x, H * nbt);
   const int h = wid / nbt;  // the sequence tiles of one head share W_UV[h] in L2
@@ -1320,18 +1322,26 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
   }
 
-  // ---- 1. merge: thread -> row r = tid / 32, columns 16 cg .. 16 cg + 15
-  const int r = tid >> 5, cg = tid & 31;
+  // ---- 1. merge: 16 groups of 32 lanes, 16 latent columns per lane.  With
+  // nrows sequences in the workgroup, group g takes sequence r = g % nrows
+  // and every nph-th split from ph = g / nrows, so small batches still keep
+  // all 512 threads' loads in flight; the groups of a sequence are summed in
+  // LDS afterwards, in phase order.
+  const int nrows = min(kCuRows, B - b0);  // >= 1
+  const int nph = kCuRows / nrows;         // split phases per sequence
+  const int grp = tid >> 5, cg = tid & 31;
+  const int r = grp % nrows, ph = grp / nrows;
+  const int ns = (ph < nph && ph < S) ? (S - ph + nph - 1) / nph : 0;  // this group's splits
   const int b = b0 + r;
-  const bool valid = b < B;
-  const int64_t prow = (static_cast<int64_t>(valid ? b : 0) * S) * H + h;  // (b, p = 0, h)
+  const int64_t prow = (static_cast<int64_t>(b) * S) * H + h;  // (b, p = 0, h)
+  auto split = [&](int kk) { return ph + nph * kk; };
   constexpr int kEl = PART_DT == MLA_F32 ? 4 : 8;  // elements per 16-byte load
   constexpr int kLd = 16 / kEl;                     // loads per split
-  auto load_batch = [&](u32x4_t (&v)[kCuBatch][kLd], int p0) {
+  auto load_batch = [&](u32x4_t (&v)[kCuBatch][kLd], int k0) {  // requires k0 < ns
 #pragma unroll
     for (int q = 0; q < kCuBatch; ++q) {
-      const int p = p0 + q;
-      const int64_t e = (prow + static_cast<int64_t>(p < S ? p : 0) * H) * kDLatent + 16 * cg;
+      const int p = split(k0 + q < ns ? k0 + q : k0);
+      const int64_t e = (prow + static_cast<int64_t>(p) * H) * kDLatent + 16 * cg;
 #pragma unroll
       for (int i = 0; i < kLd; ++i) {
         if constexpr (PART_DT == MLA_F32)
@@ -1342,8 +1352,9 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     }
   };
   u32x4_t va[kCuBatch][kLd], vb[kCuBatch][kLd];
-  load_batch(va, 0);
-  // log-sum-exp weights: the 32 lanes of a row share the split list
+  if (ns > 0) load_batch(va, 0);
+  // log-sum-exp weights over all splits of the sequence (every group of the
+  // sequence computes the same values)
   float mx = -INFINITY;
   for (int p = cg; p < S; p += 32) mx = fmaxf(mx, lse_part[prow + static_cast<int64_t>(p) * H]);
 #pragma unroll
@@ -1357,16 +1368,18 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   float acc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-  float wl = 0.0f;  // weight of split 32 * (p / 32) + (lane % 32) in that lane
-  auto accumulate = [&](const u32x4_t (&v)[kCuBatch][kLd], int p0) {
-    if ((p0 & 31) == 0) {
-      const int pl = p0 + cg;
-      wl = (pl < S && mx != -INFINITY) ? expf(lse_part[prow + static_cast<int64_t>(pl) * H] - mx) : 0.0f;
+  float wl = 0.0f;  // weight of the group's split 32 * (k / 32) + (lane % 32)
+  auto accumulate = [&](const u32x4_t (&v)[kCuBatch][kLd], int k0) {
+    if ((k0 & 31) == 0) {
+      const int kl = k0 + cg;
+      wl = (kl < ns && mx != -INFINITY)
+               ? expf(lse_part[prow + static_cast<int64_t>(split(kl)) * H] - mx)
+               : 0.0f;
     }
 #pragma unroll
     for (int q = 0; q < kCuBatch; ++q) {
-      const float w = __shfl(wl, (lane & ~31) | ((p0 + q) & 31));
-      if (p0 + q < S) {
+      const float w = __shfl(wl, (lane & ~31) | ((k0 + q) & 31));
+      if (k0 + q < ns) {
 #pragma unroll
         for (int i = 0; i < kLd; ++i)
 #pragma unroll
@@ -1382,21 +1395,39 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     }
   };
   // batches of kCuBatch splits, the next batch in flight while one is summed
-  for (int p0 = 0; p0 < S; p0 += 2 * kCuBatch) {
-    if (p0 + kCuBatch < S) load_batch(vb, p0 + kCuBatch);
-    accumulate(va, p0);
-    if (p0 + kCuBatch < S) {
-      if (p0 + 2 * kCuBatch < S) load_batch(va, p0 + 2 * kCuBatch);
-      accumulate(vb, p0 + kCuBatch);
+  for (int k0 = 0; k0 < ns; k0 += 2 * kCuBatch) {
+    if (k0 + kCuBatch < ns) load_batch(vb, k0 + kCuBatch);
+    accumulate(va, k0);
+    if (k0 + kCuBatch < ns) {
+      if (k0 + 2 * kCuBatch < ns) load_batch(va, k0 + 2 * kCuBatch);
+      accumulate(vb, k0 + kCuBatch);
     }
   }
-  const u32x4_t u0 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                      pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-  const u32x4_t u1 = {pack_bf16x2(acc[8] * inv, acc[9] * inv), pack_bf16x2(acc[10] * inv, acc[11] * inv),
-                      pack_bf16x2(acc[12] * inv, acc[13] * inv), pack_bf16x2(acc[14] * inv, acc[15] * inv)};
-  *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32) = u0;
-  *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32 + 16) = u1;
-  if (valid) {
+  if (nph > 1) {  // workgroup-uniform: sum the phases of each sequence
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(us + kCuRows * kCuRow);  // [group][4][lane]
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+      red[(grp * 4 + k4) * 32 + cg] = f32x4_t{acc[4 * k4], acc[4 * k4 + 1], acc[4 * k4 + 2], acc[4 * k4 + 3]};
+    __syncthreads();
+    if (ph == 0) {
+      for (int j = 1; j < nph; ++j) {
+        const int g2 = j * nrows + r;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const f32x4_t x = red[(g2 * 4 + k4) * 32 + cg];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[4 * k4 + k] += x[k];
+        }
+      }
+    }
+  }
+  if (ph == 0) {
+    const u32x4_t u0 = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                        pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    const u32x4_t u1 = {pack_bf16x2(acc[8] * inv, acc[9] * inv), pack_bf16x2(acc[10] * inv, acc[11] * inv),
+                        pack_bf16x2(acc[12] * inv, acc[13] * inv), pack_bf16x2(acc[14] * inv, acc[15] * inv)};
+    *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32) = u0;
+    *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32 + 16) = u1;
     if (u_out) {
       uint16_t* dst = u_out + (static_cast<int64_t>(b) * H + h) * kDLatent + 16 * cg;
       *reinterpret_cast<u32x4_t*>(dst) = u0;
@@ -1407,7 +1438,9 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   __syncthreads();
 
   // ---- 2. o = u W_UV^T on the matrix cores
-  const uint8_t* arow = us + n16 * kCuRow + 16 * kg;  // A: row n16 (sequence), k group kg
+  // A: row n16 (sequence), k group kg.  Rows past the batch are never written;
+  // they only reach D rows that are not stored.
+  const uint8_t* arow = us + n16 * kCuRow + 16 * kg;
   for (int nb = wave; nb < nnb; nb += kWaves) {
     if (nb != wave) {
       const uint16_t* wr = wrow(nb);

@@ -64,9 +64,15 @@ def test_fused_tail_matches_two_calls_and_oracle(B, lens, S, part, out):
     o_only = torch.empty_like(o2)
     mla.mla_combine_up_proj(step.geo, step.u_part, step.lse_part, dev.w_uv, o_only)
     torch.cuda.synchronize()
-    # u within one bf16 place of mla_combine's, lse equal up to fp32 rounding
+    # u within one bf16 place of mla_combine's: the two sum the splits in
+    # different orders, so a rounding may flip (across a power of two that
+    # place is the one of the larger value), plus the fp32 reordering error,
+    # which is absolute on the scale of the summands (an element near zero
+    # after cancellation has no relative bound); lse equal up to fp32 rounding
     du = (u.float() - u2.float()).abs()
-    assert torch.all(du <= 2.0 ** -7 * u2.float().abs() + 1e-30), du.max().item()
+    row = u2.float().abs().amax(dim=-1, keepdim=True)
+    bound = 2.0 ** -7 * torch.maximum(u.float().abs(), u2.float().abs()) + 2.0 ** -14 * row
+    assert torch.all(du <= bound + 1e-30), du.max().item()
     fin = torch.isfinite(lse2)
     assert torch.equal(fin, torch.isfinite(lse))
     assert torch.allclose(lse[fin], lse2[fin], rtol=0, atol=1e-5)
