@@ -1107,13 +1107,15 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
       st[i] = *reinterpret_cast<const u32x4_t*>(wsrc + static_cast<int64_t>(q >> 4) * kDLatent +
                                                  (q & 15) * 8);
   }
+  // Lanes of sequences past B read sequence 0 (their output columns are not
+  // stored) and k-steps past d_nope are never multiplied, so every load is
+  // unconditional: no zero fill that would have to wait for a load in flight.
   auto load_q = [&](bf16x8_t (&bq)[kMaxDHead / 16], int b0) {
     const int b = b0 + bl;
     const uint16_t* qrow = q_nope + (static_cast<int64_t>(b < B ? b : 0) * H + h) * d_nope + 8 * g;
 #pragma unroll
     for (int k = 0; k < kMaxDHead / 16; ++k)
-      bq[k] = (b < B && 16 * k < d_nope) ? *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k)
-                                         : bf16x8_t{};
+      if (16 * k < d_nope) bq[k] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k);
   };
   bf16x8_t bq[kMaxDHead / 16];
   load_q(bq, 0);
@@ -1311,17 +1313,6 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   constexpr int kWaves = kCuThreads / 64;
   constexpr int kKs = kDLatent / 32;  // k-steps
 
-  // W_UV operands of the wave's first value block
-  auto wrow = [&](int nb) {
-    return w_uv + (static_cast<int64_t>(h) * d_v + 16 * nb + n16) * kDLatent + 8 * kg;
-  };
-  bf16x8_t wk[kKs];
-  if (wave < nnb) {
-    const uint16_t* wr = wrow(wave);
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
-  }
-
   // ---- 1. merge: 16 groups of 32 lanes, 16 latent columns per lane.  With
   // nrows sequences in the workgroup, group g takes sequence r = g % nrows
   // and every nph-th split from ph = g / nrows, so small batches still keep
@@ -1335,12 +1326,28 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   const int b = b0 + r;
   const int64_t prow = (static_cast<int64_t>(b) * S) * H + h;  // (b, p = 0, h)
   auto split = [&](int kk) { return ph + nph * kk; };
+
+  // Every independent load is issued before the first wait, and all of them
+  // unconditionally (clamped to valid addresses) so that the compiler's wait
+  // counts stay exact: the log-sum-exp input of split cg (the only one a lane
+  // needs when S <= 32), the wave's W_UV rows, the first batch of partials.
+  const bool lse_reg = S <= 32;  // workgroup-uniform
+  float lse_l = lse_part[prow + static_cast<int64_t>(min(cg, S - 1)) * H];
+  auto wrow = [&](int nb) {
+    return w_uv + (static_cast<int64_t>(h) * d_v + 16 * nb + n16) * kDLatent + 8 * kg;
+  };
+  bf16x8_t wk[kKs];
+  {
+    const uint16_t* wr = wrow(min(wave, nnb - 1));
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
+  }
   constexpr int kEl = PART_DT == MLA_F32 ? 4 : 8;  // elements per 16-byte load
   constexpr int kLd = 16 / kEl;                     // loads per split
-  auto load_batch = [&](u32x4_t (&v)[kCuBatch][kLd], int k0) {  // requires k0 < ns
+  auto load_batch = [&](u32x4_t (&v)[kCuBatch][kLd], int k0) {
 #pragma unroll
     for (int q = 0; q < kCuBatch; ++q) {
-      const int p = split(k0 + q < ns ? k0 + q : k0);
+      const int p = ns > 0 ? split(min(k0 + q, ns - 1)) : 0;
       const int64_t e = (prow + static_cast<int64_t>(p) * H) * kDLatent + 16 * cg;
 #pragma unroll
       for (int i = 0; i < kLd; ++i) {
@@ -1352,25 +1359,34 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     }
   };
   u32x4_t va[kCuBatch][kLd], vb[kCuBatch][kLd];
-  if (ns > 0) load_batch(va, 0);
+  load_batch(va, 0);
   // log-sum-exp weights over all splits of the sequence (every group of the
   // sequence computes the same values)
-  float mx = -INFINITY;
-  for (int p = cg; p < S; p += 32) mx = fmaxf(mx, lse_part[prow + static_cast<int64_t>(p) * H]);
+  float mx = -INFINITY, z = 0.0f;
+  float e_l = 0.0f;  // S <= 32: weight of split cg
+  if (lse_reg) {
+    lse_l = cg < S ? lse_l : -INFINITY;
+    mx = lse_l;
 #pragma unroll
-  for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
-  float z = 0.0f;
-  if (mx != -INFINITY)
-    for (int p = cg; p < S; p += 32) z += expf(lse_part[prow + static_cast<int64_t>(p) * H] - mx);
+    for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+    e_l = (mx != -INFINITY) ? expf(lse_l - mx) : 0.0f;
+    z = e_l;
+  } else {
+    for (int p = cg; p < S; p += 32) mx = fmaxf(mx, lse_part[prow + static_cast<int64_t>(p) * H]);
+#pragma unroll
+    for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+    if (mx != -INFINITY)
+      for (int p = cg; p < S; p += 32) z += expf(lse_part[prow + static_cast<int64_t>(p) * H] - mx);
+  }
 #pragma unroll
   for (int o2 = 1; o2 < 32; o2 <<= 1) z += __shfl_xor(z, o2);
   const float inv = (z > 0.0f) ? 1.0f / z : 0.0f;
   float acc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-  float wl = 0.0f;  // weight of the group's split 32 * (k / 32) + (lane % 32)
+  float wl = 0.0f;  // S > 32: weight of the group's split 32 * (k / 32) + (lane % 32)
   auto accumulate = [&](const u32x4_t (&v)[kCuBatch][kLd], int k0) {
-    if ((k0 & 31) == 0) {
+    if (!lse_reg && (k0 & 31) == 0) {
       const int kl = k0 + cg;
       wl = (kl < ns && mx != -INFINITY)
                ? expf(lse_part[prow + static_cast<int64_t>(split(kl)) * H] - mx)
@@ -1378,7 +1394,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     }
 #pragma unroll
     for (int q = 0; q < kCuBatch; ++q) {
-      const float w = __shfl(wl, (lane & ~31) | ((k0 + q) & 31));
+      const float w = lse_reg ? __shfl(e_l, (lane & ~31) | (split(k0 + q) & 31))
+                              : __shfl(wl, (lane & ~31) | ((k0 + q) & 31));
       if (k0 + q < ns) {
 #pragma unroll
         for (int i = 0; i < kLd; ++i)
