@@ -1322,7 +1322,9 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   const int nph = kCuRows / nrows;         // split phases per sequence
   const int grp = tid >> 5, cg = tid & 31;
   const int r = grp % nrows, ph = grp / nrows;
-  const int ns = (ph < nph && ph < S) ? (S - ph + nph - 1) / nph : 0;  // this group's splits
+  // this group's splits: all of its phase at first; once the log-sum-exp
+  // inputs are in, only those below the last non-empty split
+  int ns = (ph < nph && ph < S) ? (S - ph + nph - 1) / nph : 0;
   const int b = b0 + r;
   const int64_t prow = (static_cast<int64_t>(b) * S) * H + h;  // (b, p = 0, h)
   auto split = [&](int kk) { return ph + nph * kk; };
@@ -1364,23 +1366,35 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   // sequence computes the same values)
   float mx = -INFINITY, z = 0.0f;
   float e_l = 0.0f;  // S <= 32: weight of split cg
+  int last = -1;     // last split with a finite log-sum-exp
   if (lse_reg) {
     lse_l = cg < S ? lse_l : -INFINITY;
     mx = lse_l;
+    last = lse_l != -INFINITY ? cg : -1;
 #pragma unroll
     for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
     e_l = (mx != -INFINITY) ? expf(lse_l - mx) : 0.0f;
     z = e_l;
   } else {
-    for (int p = cg; p < S; p += 32) mx = fmaxf(mx, lse_part[prow + static_cast<int64_t>(p) * H]);
+    for (int p = cg; p < S; p += 32) {
+      const float x = lse_part[prow + static_cast<int64_t>(p) * H];
+      mx = fmaxf(mx, x);
+      last = x != -INFINITY ? p : last;
+    }
 #pragma unroll
     for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
     if (mx != -INFINITY)
       for (int p = cg; p < S; p += 32) z += expf(lse_part[prow + static_cast<int64_t>(p) * H] - mx);
   }
 #pragma unroll
-  for (int o2 = 1; o2 < 32; o2 <<= 1) z += __shfl_xor(z, o2);
+  for (int o2 = 1; o2 < 32; o2 <<= 1) {
+    z += __shfl_xor(z, o2);
+    last = max(last, __shfl_xor(last, o2));
+  }
   const float inv = (z > 0.0f) ? 1.0f / z : 0.0f;
+  // Splits past the last finite log-sum-exp are empty ranges (the trailing
+  // ranges of a short sequence): weight 0, so their partials are not read.
+  ns = min(ns, ph <= last ? (last - ph) / nph + 1 : 0);
   float acc[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) acc[k] = 0.0f;

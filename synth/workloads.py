@@ -76,7 +76,7 @@ WORKLOADS = {
         description="long-context bf16 decode: B=4, L=32768, 64 splits"),
     "paged_b64_ragged": Workload(
         "paged_b64_ragged", batch=64, seq_len=None, len_range=(512, 16384),
-        page_size=64, num_splits=32, seed=BASE_SEED + 4,
+        page_size=64, num_splits=8, seed=BASE_SEED + 4,
         description="paged ragged bf16 decode: B=64, L~U[512,16384], 64-token pages"),
     "fp8_b1_l128k": Workload(
         "fp8_b1_l128k", batch=1, seq_len=131072, cache_dtype="fp8", num_splits=256,
