@@ -102,7 +102,7 @@ def record_traffic(d):
            "fetch_kib_per_launch": f[name], "write_kib_per_launch": w[name],
            "fetch_scale": kf, "write_scale": kw,
            "hbm_bytes_per_launch": (f[name] * kf + w[name] * kw) * 1024.0,
-           "counters_from": d}
+           "counters_from": os.path.relpath(os.path.abspath(d), ROOT)}
     json.dump(rec, open(PROFILE_TRAFFIC, "w"), indent=1)
     print(json.dumps(rec))
 
