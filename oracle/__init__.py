@@ -62,6 +62,13 @@ def lib():
         L.oracle_mla_cache_bytes_per_token.argtypes = [C.c_int32] * 4
         L.oracle_mha_cache_bytes.restype = C.c_int64
         L.oracle_mha_cache_bytes.argtypes = [C.c_int64] * 5
+        L.oracle_cache_append.restype = C.c_int
+        L.oracle_cache_append.argtypes = [C.c_int32] * 3 + [C.c_void_p, C.c_void_p, C.c_int32,
+                                                            C.c_void_p, C.c_void_p, C.c_int32,
+                                                            C.c_void_p, C.c_int32, C.c_int64,
+                                                            C.c_void_p, C.c_int32]
+        L.oracle_encode_e4m3.restype = C.c_uint8
+        L.oracle_encode_e4m3.argtypes = [C.c_float]
         L.oracle_num_threads.restype = C.c_int
         L.oracle_num_threads.argtypes = []
         _lib = L
@@ -163,6 +170,36 @@ def combine(u_part, lse_part):
     if rc != 0:
         raise ValueError(f"oracle_combine failed: {rc}")
     return u, lse
+
+
+def cache_append(c_kv, k_r, src_dtype, positions, rows, cache_dtype, row_scale=None,
+                 page_size=0, seq_stride=0, block_table=None):
+    """Write one token per sequence into the cache arrays (modified in place).
+
+    c_kv [B, d_latent], k_r [B, d_rope] stored bits in src_dtype ("f32" or
+    "bf16"); rows [n_rows, d_latent + d_rope] stored bits in cache_dtype;
+    row_scale [n_rows] float32 for "fp8"; positions [B] int32 (negative or
+    past the capacity: skipped)."""
+    sd, cd = _dt(src_dtype), _dt(cache_dtype)
+    c_kv, k_r = _arr(c_kv, sd), _arr(k_r, sd)
+    B, dl = c_kv.shape
+    dr = k_r.shape[1]
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    assert rows.flags.c_contiguous and rows.dtype == _NP[cd]
+    if row_scale is not None:
+        assert row_scale.flags.c_contiguous and row_scale.dtype == np.float32
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    max_pages = 0 if bt is None else bt.shape[1]
+    rc = lib().oracle_cache_append(B, dl, dr, _ptr(c_kv), _ptr(k_r), sd, _ptr(pos), _ptr(rows),
+                                   cd, _ptr(row_scale), int(page_size), int(seq_stride), _ptr(bt),
+                                   max_pages)
+    if rc != 0:
+        raise ValueError(f"oracle_cache_append failed: {rc}")
+
+
+def encode_e4m3(y: float) -> int:
+    """The E4M3 code nearest to the binary32 value y (|y| <= 448)."""
+    return int(lib().oracle_encode_e4m3(float(y)))
 
 
 def up_proj(u, w_uv, w_dtype):

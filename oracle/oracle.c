@@ -297,6 +297,98 @@ int oracle_up_proj(int32_t B, int32_t H, int32_t d_v, int32_t d_latent,
   return 0;
 }
 
+/* ------------------------------------------------------ cache append */
+
+/* OCP E4M3: value = 2^(e-7) * (1 + m/8) for exponent field e in 1..15 (field
+ * 15 with mantissa 7 is NaN, so the largest value is 448), and m * 2^-9 for
+ * e = 0.  The representable values are spaced 2^(k-3) in the binade
+ * [2^k, 2^(k+1)) for k >= -6 and 2^-9 below 2^-6, so the nearest one is
+ * found by scaling |y| to units of that spacing (exact: a power of two) and
+ * rounding to the nearest integer, ties to even (rint in the default
+ * rounding mode).  A binade's count of 16 spacings is the next binade's
+ * first value. */
+uint8_t oracle_encode_e4m3(float y) {
+  const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  double a = fabs((double)y);
+  if (a > 448.0) a = 448.0;
+  if (a < ldexp(1.0, -6)) {                 /* subnormal spacing 2^-9 */
+    const double q = rint(ldexp(a, 9));     /* 0 .. 8; 8 is the code of 2^-6 */
+    return (uint8_t)(sign | (uint8_t)q);
+  }
+  int k;
+  (void)frexp(a, &k);                       /* a = f * 2^k, f in [0.5, 1) */
+  k -= 1;                                   /* a in [2^k, 2^(k+1)) */
+  double q = rint(ldexp(a, 3 - k));         /* 8 .. 16 spacings of 2^(k-3) */
+  if (q == 16.0) {
+    q = 8.0;
+    k += 1;
+  }
+  return (uint8_t)(sign | (uint8_t)(((k + 7) << 3) | ((int)q - 8)));
+}
+
+static void round_bf16(float x, uint16_t* out) {
+  /* nearest bf16 (the binary32 values whose low 16 bits are zero), ties to
+   * the even one: compare with the two neighbours in double */
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  const uint32_t lo = u & 0xFFFF0000u, hi = lo + 0x10000u;
+  float flo, fhi;
+  memcpy(&flo, &lo, sizeof flo);
+  memcpy(&fhi, &hi, sizeof fhi);
+  const double dlo = fabs((double)x - (double)flo), dhi = fabs((double)fhi - (double)x);
+  uint32_t r = lo;
+  if (dhi < dlo || (dhi == dlo && ((lo >> 16) & 1u))) r = hi;
+  *out = (uint16_t)(r >> 16);
+}
+
+int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void* c_kv,
+                        const void* k_r, int32_t src_dtype, const int32_t* positions,
+                        void* rows, int32_t cache_dtype, float* row_scale, int32_t page_size,
+                        int64_t seq_stride, const int32_t* block_table, int32_t max_pages) {
+  if (B < 0 || d_latent <= 0 || d_rope < 0 || !positions || !rows) return -1;
+  if (B > 0 && (!c_kv || (d_rope > 0 && !k_r))) return -1;
+  if (src_dtype != ORACLE_F32 && src_dtype != ORACLE_BF16) return -3;
+  if (cache_dtype != ORACLE_F32 && cache_dtype != ORACLE_BF16 && cache_dtype != ORACLE_E4M3)
+    return -3;
+  if (cache_dtype == ORACLE_E4M3 && !row_scale) return -4;
+  if (page_size < 0 || (page_size > 0 && (!block_table || max_pages < 1))) return -2;
+  if (page_size == 0 && seq_stride < 1) return -2;
+  const int32_t w = d_latent + d_rope;
+  const int64_t capacity = page_size ? (int64_t)max_pages * page_size : seq_stride;
+  float* x = (float*)malloc(sizeof(float) * (size_t)w);
+  if (!x) return -5;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t t = positions[b];
+    if (t < 0 || t >= capacity) continue;
+    const int64_t row = page_size
+        ? (int64_t)block_table[(int64_t)b * max_pages + t / page_size] * page_size + t % page_size
+        : (int64_t)b * seq_stride + t;
+    /* the new row as binary32 values (both input formats convert exactly) */
+    for (int32_t j = 0; j < d_latent; ++j)
+      x[j] = (float)load_elem(c_kv, src_dtype, (int64_t)b * d_latent + j);
+    for (int32_t j = 0; j < d_rope; ++j)
+      x[d_latent + j] = (float)load_elem(k_r, src_dtype, (int64_t)b * d_rope + j);
+    if (cache_dtype == ORACLE_F32) {
+      memcpy((float*)rows + row * w, x, sizeof(float) * (size_t)w);
+    } else if (cache_dtype == ORACLE_BF16) {
+      for (int32_t j = 0; j < w; ++j) round_bf16(x[j], (uint16_t*)rows + row * w + j);
+    } else {
+      float amax = 0.0f;
+      for (int32_t j = 0; j < w; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      const float s = fmaxf(amax, 0x1p-126f) / 448.0f;
+      row_scale[row] = s;
+      for (int32_t j = 0; j < w; ++j) {
+        float y = x[j] / s;
+        if (y > 448.0f) y = 448.0f;
+        if (y < -448.0f) y = -448.0f;
+        ((uint8_t*)rows)[row * w + j] = oracle_encode_e4m3(y);
+      }
+    }
+  }
+  free(x);
+  return 0;
+}
+
 /* ------------------------------------------------------ size arithmetic */
 
 /* [V2] §2.3: per token and layer only KV_comp (d_latent) and k_R (d_rope)

@@ -72,6 +72,30 @@ int oracle_combine(int32_t B, int32_t S, int32_t H, int32_t D,
 int oracle_up_proj(int32_t B, int32_t H, int32_t d_v, int32_t d_latent,
                    const double* u, const void* w_uv, int32_t w_dtype, double* o);
 
+/* Append one token per sequence to the cache ([V2] §2.3: per token only the
+ * latent c_KV and the shared RoPE key k_R are cached; [DSA]: the 128K cache is
+ * kept in FP8).  For every b with 0 <= positions[b] < capacity (contiguous:
+ * seq_stride rows per sequence; paged: max_pages * page_size), the row of
+ * token positions[b] (same row map as oracle_mla_problem) becomes
+ * [c_kv[b][0:d_latent] | k_r[b][0:d_rope]] in the cache dtype:
+ *   F32   the input value (exact from F32 or BF16 input);
+ *   BF16  the input rounded to nearest even (a copy for BF16 input);
+ *   E4M3  one fp32 factor per row, s = fl32(max(amax, 2^-126) / 448) with amax
+ *         the largest |value| of the row, stored in row_scale[row]; each code is
+ *         the E4M3 value nearest to fl32(x / s) (ties to even mantissa), with
+ *         |fl32(x / s)| first clamped to 448.
+ * Other positions are skipped; no other row is touched.  Inputs [B][d] in
+ * src_dtype (F32 or BF16), finite.  Returns 0, or a negative value on a bad
+ * argument. */
+int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void* c_kv,
+                        const void* k_r, int32_t src_dtype, const int32_t* positions,
+                        void* rows, int32_t cache_dtype, float* row_scale, int32_t page_size,
+                        int64_t seq_stride, const int32_t* block_table, int32_t max_pages);
+
+/* The E4M3 code nearest to the binary32 value y (|y| <= 448, finite), ties to
+ * the even mantissa. */
+uint8_t oracle_encode_e4m3(float y);
+
 /* element decoders (exact) */
 double oracle_decode_bf16(uint16_t bits);
 double oracle_decode_e4m3(uint8_t code);

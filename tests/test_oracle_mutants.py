@@ -12,6 +12,7 @@ import pytest
 import oracle
 from oracle.build import CFLAGS
 
+from . import test_oracle_append as append
 from . import test_oracle_codecs as codecs
 from . import test_oracle_pins as pins
 
@@ -34,6 +35,15 @@ MUTANTS = {
     "lse_base2": ("lse[idx] = m + log(l);", "lse[idx] = m + log2(l);"),
     "combine_ignores_weights": ("out[d] += wgt * up[d];", "out[d] += up[d] / S;"),
     "row_scale_ignored": ("if (P->cache_dtype == ORACLE_E4M3) f = (double)P->row_scale[r];", ""),
+    # cache append
+    "e4m3_encode_truncates": ("double q = rint(ldexp(a, 3 - k));", "double q = floor(ldexp(a, 3 - k));"),
+    "e4m3_encode_subnormal_spacing": ("const double q = rint(ldexp(a, 9));",
+                                      "const double q = rint(ldexp(a, 8));"),
+    "append_scale_to_240": ("const float s = fmaxf(amax, 0x1p-126f) / 448.0f;",
+                            "const float s = fmaxf(amax, 0x1p-126f) / 240.0f;"),
+    "append_bf16_truncates": ("if (dhi < dlo || (dhi == dlo && ((lo >> 16) & 1u))) r = hi;", ""),
+    "append_row_off_by_one": (": (int64_t)b * seq_stride + t;", ": (int64_t)b * seq_stride + t + 1;"),
+    "append_ignores_capacity": ("if (t < 0 || t >= capacity) continue;", "if (t < 0) continue;"),
 }
 
 PIN_CHECKS = [
@@ -50,6 +60,11 @@ PIN_CHECKS = [
     pins.test_paged_equals_contiguous_and_poison_is_unread,
     pins.test_fp8_rows_are_decoded_codes_times_row_scale,
     codecs.test_e4m3_decode_all_codes,
+    append.test_e4m3_encode_returns_every_code_of_its_value,
+    append.test_e4m3_encode_ties_go_to_the_even_mantissa,
+    lambda: append.test_fp8_append_matches_the_input_quantiser(3.0),
+    append.test_bf16_append_rounds_to_nearest_even,
+    append.test_append_places_rows_like_the_decode_row_map,
 ]
 
 
@@ -76,7 +91,7 @@ def test_pins_catch_planted_mistake(tmp_path, name, monkeypatch):
     for fn in ("oracle_mla_decode", "oracle_absorb_q", "oracle_combine", "oracle_up_proj",
                "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_array",
                "oracle_mla_cache_bytes_per_token", "oracle_mha_cache_bytes",
-               "oracle_num_threads"):
+               "oracle_num_threads", "oracle_cache_append", "oracle_encode_e4m3"):
         getattr(mut, fn).restype = getattr(good, fn).restype
         getattr(mut, fn).argtypes = getattr(good, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mut)
