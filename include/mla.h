@@ -29,6 +29,8 @@
  * The step is four calls, each only enqueued on the caller's HIP stream:
  *     mla_absorb_q  ->  mla_decode  ->  mla_combine  ->  mla_up_proj
  * (mla_combine_up_proj does the last two in one launch for bf16 W_UV).
+ * mla_cache_append writes each sequence's new token into the cache before the
+ * step.
  * mla_decode splits every sequence into num_splits token ranges and writes one
  * normalised partial result per range; mla_combine merges them exactly with
  * log-sum-exp weights; with num_splits == 1 the partial already is the final
@@ -181,6 +183,32 @@ mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_
                                  const void* u_part, int32_t part_dt, const float* lse_part,
                                  const void* w_uv, int32_t w_dt, void* o, int32_t o_dt,
                                  void* u, float* lse, void* stream);
+
+/* Append the new token of every sequence to the cache: the step before
+ * mla_decode ([V2] §2.3: per token and layer only the latent c_KV and the
+ * RoPE key k_R shared by all heads are cached; [DSA]: a 128K-token cache is
+ * kept in FP8).  For each b with 0 <= positions[b] < capacity (contiguous:
+ * seq_stride rows per sequence; paged: max_pages * 64 tokens) the row of
+ * token positions[b] (the row mla_decode reads for it) becomes
+ *   [c_kv[b][0:d_latent] | k_r[b][0:d_rope]]
+ * in the cache dtype: F32 the input value; BF16 the input rounded to nearest
+ * even; FP8_E4M3 the codes of x / s with s = fp32(max(amax, 2^-126) / 448),
+ * amax the row's largest |x|, each quotient (binary32, correctly rounded)
+ * clamped to +-448 and rounded to the nearest E4M3 value, ties to the even
+ * mantissa; s is stored in row_scale[row].  The same bits as the input
+ * quantiser of the fp8 workloads.
+ * c_kv [B][d_latent] and k_r [B][d_rope] in src_dt (F32 or BF16), finite;
+ * positions: device int32 [B].  A position < 0 or past the capacity, or a
+ * negative page id in block_table, skips the sequence; no other row is
+ * written.  cache->rows (and row_scale for FP8) are written through: they must
+ * be writable; seq_lens and max_seq_len are neither read nor changed (the
+ * caller advances its lengths).  The cache must satisfy mla_decode's layout
+ * rules (16-byte aligned rows, page_size 0 or 64).  Errors: MLA_E_ARG for
+ * missing pointers or a bad layout, MLA_E_SHAPE for another page size,
+ * MLA_E_DTYPE for an FP8 input, MLA_E_ALIGN for misaligned rows. */
+mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, const void* c_kv,
+                              const void* k_r, int32_t src_dt, const int32_t* positions,
+                              const mla_cache_t* cache, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mla_status_str(mla_status_t status);

@@ -72,6 +72,9 @@ def lib():
         L.mla_combine_up_proj.restype = C.c_int
         L.mla_combine_up_proj.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, f32p, vp, i32, vp,
                                           i32, vp, f32p, vp]
+        L.mla_cache_append.restype = C.c_int
+        L.mla_cache_append.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp,
+                                       C.POINTER(CacheDesc), vp]
         L.mla_status_str.restype = C.c_char_p
         L.mla_status_str.argtypes = [C.c_int]
         L.mla_version.restype = C.c_int32
@@ -81,7 +84,7 @@ def lib():
 
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
-            "mla_status_str", "mla_version")
+            "mla_cache_append", "mla_status_str", "mla_version")
 
 
 def status_str(status: int) -> str:
@@ -150,6 +153,21 @@ class Cache:
         return CacheDesc(dtype_code(self.rows), _ptr(self.rows), _ptr(self.row_scale),
                          int(self.page_size), int(self.seq_stride), _ptr(self.block_table), mp,
                          _ptr(self.seq_lens), int(self.max_seq_len))
+
+
+def mla_cache_append(geo: Geometry, c_kv: torch.Tensor, k_r: torch.Tensor,
+                     positions: torch.Tensor, cache: Cache, stream=None) -> None:
+    """Write token positions[b] of every sequence b: c_kv [B, d_latent] and
+    k_r [B, d_rope] (float32 or bfloat16) into cache.rows (and row_scale for
+    an e4m3 cache).  positions: int32 [B] on the device."""
+    B = int(c_kv.shape[0])
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    d = geo.c()
+    cd = cache.c()
+    st = lib().mla_cache_append(C.byref(d), B, _ptr(c_kv), _ptr(k_r), dtype_code(c_kv),
+                                _ptr(positions), C.byref(cd), _stream(stream))
+    _check("mla_cache_append", st)
 
 
 def mla_absorb_q(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor,

@@ -149,6 +149,31 @@ mla_status_t check_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t nu
   return MLA_OK;
 }
 
+mla_status_t check_cache_append(const mla_dims_t* dims, int32_t B, const void* c_kv,
+                                const void* k_r, int32_t src_dt, const int32_t* positions,
+                                const mla_cache_t* cache) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!cache || B < 0) return MLA_E_ARG;
+  if (!valid_dtype(src_dt) || !valid_dtype(cache->dtype)) return MLA_E_ARG;
+  if (cache->page_size != 0 && cache->page_size != kPageSize) return MLA_E_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!c_kv || !k_r || !positions || !cache->rows) return MLA_E_ARG;
+  if (src_dt == MLA_FP8_E4M3) return MLA_E_DTYPE;
+  if (cache->dtype == MLA_FP8_E4M3) {
+    if (!cache->row_scale) return MLA_E_ARG;
+  } else if (cache->row_scale) {
+    return MLA_E_ARG;
+  }
+  if (cache->page_size == 0) {
+    if (cache->seq_stride < 1) return MLA_E_ARG;
+  } else {
+    if (!cache->block_table || cache->max_pages < 1) return MLA_E_ARG;
+  }
+  if (!aligned(cache->rows, 16)) return MLA_E_ALIGN;
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 extern "C" const char* mla_status_str(mla_status_t status) {

@@ -54,4 +54,8 @@ mla_status_t check_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t nu
                                    const void* w_uv, int32_t w_dt, const void* o, int32_t o_dt,
                                    const void* u);
 
+mla_status_t check_cache_append(const mla_dims_t* dims, int32_t B, const void* c_kv,
+                                const void* k_r, int32_t src_dt, const int32_t* positions,
+                                const mla_cache_t* cache);
+
 }  // namespace mla

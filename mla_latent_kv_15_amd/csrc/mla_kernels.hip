@@ -1494,6 +1494,82 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   }
 }
 
+// ================================================================ cache append
+//
+// One wave per sequence writes the new token's row (576 elements: lane l
+// takes elements l + 64 j, so every store instruction covers 64 consecutive
+// elements).  For an E4M3 cache the row maximum is reduced across the wave,
+// the factor s = max(amax, 2^-126) / 448 and the quotients x / s are
+// correctly rounded binary32 divisions (the library is built without fast
+// math), and each quotient is rounded to E4M3 by e4m3_encode.
+
+constexpr int kAppendThreads = 256;  // 4 sequences per workgroup
+
+// Nearest E4M3 code to y (|y| <= 448 after clamping), ties to the even
+// mantissa, from the format's spacing: 2^-9 below 2^-6, and 2^(k-3) in the
+// binade [2^k, 2^(k+1)).  Scaling |y| by that spacing is exact, so
+// v_rndne_f32 makes the decision; a count of 16 is the next binade's first
+// value.  The sign is kept (-0 gives 0x80).
+__device__ inline uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.0f);
+  if (a < 0x1p-6f) return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  int k = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+  int q = static_cast<int>(__builtin_rintf(__builtin_ldexpf(a, 3 - k)));
+  if (q == 16) {
+    q = 8;
+    ++k;
+  }
+  return sign | static_cast<uint32_t>(((k + 7) << 3) | (q - 8));
+}
+
+template <int SRC_DT, int CACHE_DT>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(
+    const void* c_kv, const void* k_r, const int32_t* positions, void* rows, float* row_scale,
+    const int32_t* block_table, int32_t max_pages, int32_t paged, int64_t seq_stride, int B) {
+  const int b = blockIdx.x * (kAppendThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= B) return;
+  const int64_t t = positions[b];
+  const int64_t capacity = paged ? static_cast<int64_t>(max_pages) * kPageSize : seq_stride;
+  if (t < 0 || t >= capacity) return;
+  int64_t row;
+  if (paged) {
+    const int64_t page = block_table[static_cast<int64_t>(b) * max_pages + (t >> 6)];
+    if (page < 0) return;
+    row = page * kPageSize + (t & 63);
+  } else {
+    row = static_cast<int64_t>(b) * seq_stride + t;
+  }
+  constexpr int kPer = kRowElems / 64;  // 9
+  float x[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + 64 * j;
+    x[j] = e < kDLatent ? load_elem<SRC_DT>(c_kv, static_cast<int64_t>(b) * kDLatent + e)
+                        : load_elem<SRC_DT>(k_r, static_cast<int64_t>(b) * kDRope + (e - kDLatent));
+  }
+  const int64_t base = row * kRowElems;
+  if constexpr (CACHE_DT == MLA_FP8_E4M3) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) amax = fmaxf(amax, fabsf(x[j]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float sc = fmaxf(amax, 0x1p-126f) / 448.0f;
+    uint8_t* dst = static_cast<uint8_t*>(rows) + base;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float y = fminf(fmaxf(x[j] / sc, -448.0f), 448.0f);
+      dst[lane + 64 * j] = static_cast<uint8_t>(e4m3_encode(y));
+    }
+    if (lane == 0) row_scale[row] = sc;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) store_elem<CACHE_DT>(rows, base + lane + 64 * j, x[j]);
+  }
+}
+
 mla_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
@@ -1676,5 +1752,34 @@ extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, i
   MLA_CU(MLA_F32, MLA_BF16)
   MLA_CU(MLA_F32, MLA_F32)
 #undef MLA_CU
+  return MLA_E_DTYPE;
+}
+
+extern "C" mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, const void* c_kv,
+                                         const void* k_r, int32_t src_dt,
+                                         const int32_t* positions, const mla_cache_t* cache,
+                                         void* stream) {
+  mla_status_t st = check_cache_append(dims, B, c_kv, k_r, src_dt, positions, cache);
+  if (st != MLA_OK || B == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned grid = static_cast<unsigned>((B + kAppendThreads / 64 - 1) / (kAppendThreads / 64));
+  // the cache is written through: the caller passes writable buffers
+  void* rows = const_cast<void*>(cache->rows);
+  float* scale = const_cast<float*>(cache->row_scale);
+  const int32_t paged = cache->page_size != 0;
+#define MLA_AP(SD, CD)                                                                          \
+  if (src_dt == SD && cache->dtype == CD) {                                                    \
+    append_kernel<SD, CD><<<grid, kAppendThreads, 0, s>>>(c_kv, k_r, positions, rows, scale,   \
+                                                          cache->block_table, cache->max_pages, \
+                                                          paged, cache->seq_stride, B);         \
+    return launch_status();                                                                   \
+  }
+  MLA_AP(MLA_F32, MLA_F32)
+  MLA_AP(MLA_F32, MLA_BF16)
+  MLA_AP(MLA_F32, MLA_FP8_E4M3)
+  MLA_AP(MLA_BF16, MLA_F32)
+  MLA_AP(MLA_BF16, MLA_BF16)
+  MLA_AP(MLA_BF16, MLA_FP8_E4M3)
+#undef MLA_AP
   return MLA_E_DTYPE;
 }

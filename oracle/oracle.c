@@ -360,9 +360,9 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
   for (int32_t b = 0; b < B; ++b) {
     const int64_t t = positions[b];
     if (t < 0 || t >= capacity) continue;
-    const int64_t row = page_size
-        ? (int64_t)block_table[(int64_t)b * max_pages + t / page_size] * page_size + t % page_size
-        : (int64_t)b * seq_stride + t;
+    const int64_t page = page_size ? block_table[(int64_t)b * max_pages + t / page_size] : 0;
+    if (page < 0) continue; /* no page mapped */
+    const int64_t row = page_size ? page * page_size + t % page_size : (int64_t)b * seq_stride + t;
     /* the new row as binary32 values (both input formats convert exactly) */
     for (int32_t j = 0; j < d_latent; ++j)
       x[j] = (float)load_elem(c_kv, src_dtype, (int64_t)b * d_latent + j);

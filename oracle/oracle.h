@@ -84,7 +84,8 @@ int oracle_up_proj(int32_t B, int32_t H, int32_t d_v, int32_t d_latent,
  *         the largest |value| of the row, stored in row_scale[row]; each code is
  *         the E4M3 value nearest to fl32(x / s) (ties to even mantissa), with
  *         |fl32(x / s)| first clamped to 448.
- * Other positions are skipped; no other row is touched.  Inputs [B][d] in
+ * Other positions, and positions whose page id is negative, are skipped; no
+ * other row is touched.  Inputs [B][d] in
  * src_dtype (F32 or BF16), finite.  Returns 0, or a negative value on a bad
  * argument. */
 int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void* c_kv,

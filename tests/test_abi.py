@@ -162,3 +162,28 @@ def test_split_chunk_rule(L, S, expect):
     assert mla.split_chunk(L, S) == expect
     if L:
         assert expect % mla.TILE_TOKENS == 0 and expect * S >= L
+
+
+def test_cache_append_validation():
+    L = mla.lib()
+
+    def ap(B=2, ckv=P, kr=P, src=BF16, pos=P, c=None, d=None):
+        c = c if c is not None else cache()
+        return L.mla_cache_append(C.byref(d or dims()), B, ckv, kr, src, pos, C.byref(c), None)
+
+    assert ap(B=0, ckv=None, kr=None, pos=None) == OK
+    assert ap(B=-1) == E_ARG
+    assert ap(ckv=None) == E_ARG
+    assert ap(kr=None) == E_ARG
+    assert ap(pos=None) == E_ARG
+    assert ap(c=cache(rows=None)) == E_ARG
+    assert ap(src=9) == E_ARG
+    assert ap(src=FP8) == E_DTYPE
+    assert ap(c=cache(dtype=FP8)) == E_ARG                 # fp8 needs row_scale
+    assert ap(c=cache(dtype=BF16, row_scale=P)) == E_ARG   # only fp8 has one
+    assert ap(c=cache(seq_stride=0)) == E_ARG
+    assert ap(c=cache(page_size=32, block_table=P, max_pages=4)) == E_SHAPE
+    assert ap(c=cache(page_size=64, block_table=None, max_pages=4)) == E_ARG
+    assert ap(c=cache(page_size=64, block_table=P, max_pages=0)) == E_ARG
+    assert ap(c=cache(rows=P + 8)) == E_ALIGN
+    assert ap(d=dims(dl=256)) == E_SHAPE
