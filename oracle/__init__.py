@@ -67,6 +67,11 @@ def lib():
                                                             C.c_void_p, C.c_void_p, C.c_int32,
                                                             C.c_void_p, C.c_int32, C.c_int64,
                                                             C.c_void_p, C.c_int32]
+        L.oracle_rope.restype = C.c_int
+        L.oracle_rope.argtypes = [C.c_int32] * 3 + [C.c_void_p, C.c_int32, C.c_void_p,
+                                                    C.c_double, C.c_void_p]
+        L.oracle_rope_inv_freq.restype = None
+        L.oracle_rope_inv_freq.argtypes = [C.c_int32, C.c_double, C.c_void_p]
         L.oracle_encode_e4m3.restype = C.c_uint8
         L.oracle_encode_e4m3.argtypes = [C.c_float]
         L.oracle_num_threads.restype = C.c_int
@@ -195,6 +200,26 @@ def cache_append(c_kv, k_r, src_dtype, positions, rows, cache_dtype, row_scale=N
                                    max_pages)
     if rc != 0:
         raise ValueError(f"oracle_cache_append failed: {rc}")
+
+
+def rope(x, dtype, positions, base=10000.0):
+    """Decoupled RoPE of x [B, H, d_r] (stored bits in dtype) at positions [B]
+    (int32) -> float64 [B, H, d_r]."""
+    d = _dt(dtype)
+    x = _arr(x, d)
+    B, H, dr = x.shape
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    out = np.zeros((B, H, dr), dtype=np.float64)
+    rc = lib().oracle_rope(B, H, dr, _ptr(x), d, _ptr(pos), float(base), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_rope failed: {rc}")
+    return out
+
+
+def rope_inv_freq(d_r=64, base=10000.0) -> np.ndarray:
+    f = np.zeros(d_r // 2, dtype=np.float32)
+    lib().oracle_rope_inv_freq(d_r, float(base), _ptr(f))
+    return f
 
 
 def encode_e4m3(y: float) -> int:

@@ -389,6 +389,37 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
   return 0;
 }
 
+/* ------------------------------------------------------ decoupled RoPE */
+
+void oracle_rope_inv_freq(int32_t d_r, double base, float* inv_freq) {
+  for (int32_t i = 0; i < d_r / 2; ++i)
+    inv_freq[i] = (float)pow(base, -(2.0 * (double)i) / (double)d_r);
+}
+
+int oracle_rope(int32_t B, int32_t H, int32_t d_r, const void* x, int32_t dtype,
+                const int32_t* positions, double base, double* out) {
+  if (B < 0 || H <= 0 || d_r <= 0 || (d_r & 1) || !x || !positions || !out) return -1;
+  if (!valid_dtype(dtype)) return -3;
+  if (!(base > 1.0)) return -2;
+  const int32_t half = d_r / 2;
+  float* inv_freq = (float*)malloc(sizeof(float) * (size_t)half);
+  if (!inv_freq) return -5;
+  oracle_rope_inv_freq(d_r, base, inv_freq);
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    const float pos = (float)positions[bh / H];
+    for (int32_t i = 0; i < half; ++i) {
+      const float theta = pos * inv_freq[i]; /* binary32 product */
+      const double c = cos((double)theta), s = sin((double)theta);
+      const double a = load_elem(x, dtype, bh * d_r + i);
+      const double b = load_elem(x, dtype, bh * d_r + i + half);
+      out[bh * d_r + i] = a * c - b * s;
+      out[bh * d_r + i + half] = b * c + a * s;
+    }
+  }
+  free(inv_freq);
+  return 0;
+}
+
 /* ------------------------------------------------------ size arithmetic */
 
 /* [V2] §2.3: per token and layer only KV_comp (d_latent) and k_R (d_rope)

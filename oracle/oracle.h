@@ -93,6 +93,24 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
                         void* rows, int32_t cache_dtype, float* row_scale, int32_t page_size,
                         int64_t seq_stride, const int32_t* block_table, int32_t max_pages);
 
+/* Decoupled RoPE of the positional query ([V2] §2.2: only q_R and k_R are
+ * rotated, q_C is left as it is; frequencies 1/10000^(2i/d) as in the
+ * listings of [V2] and [LAT]; the [LAT] listing repeats the d/2 frequencies
+ * over both halves, so element i pairs with element i + d/2, rotate-half):
+ *   inv_freq[i] = binary32 nearest to base^(-2i/d_r), i < d_r/2,
+ *   theta_i     = binary32 product position * inv_freq[i] (the listings work
+ *                 in float32),
+ *   out[i]          = x[i] cos theta_i - x[i + d_r/2] sin theta_i,
+ *   out[i + d_r/2]  = x[i + d_r/2] cos theta_i + x[i] sin theta_i,
+ * cos and sin in float64.  x [B][H][d_r] in dtype, positions [B] (one per
+ * sequence: every head of a token shares its position); out float64.
+ * Returns 0, or a negative value on a bad argument. */
+int oracle_rope(int32_t B, int32_t H, int32_t d_r, const void* x, int32_t dtype,
+                const int32_t* positions, double base, double* out);
+
+/* inv_freq[i] of oracle_rope for i < d_r/2 */
+void oracle_rope_inv_freq(int32_t d_r, double base, float* inv_freq);
+
 /* The E4M3 code nearest to the binary32 value y (|y| <= 448, finite), ties to
  * the even mantissa. */
 uint8_t oracle_encode_e4m3(float y);

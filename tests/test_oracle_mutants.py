@@ -15,6 +15,7 @@ from oracle.build import CFLAGS
 from . import test_oracle_append as append
 from . import test_oracle_codecs as codecs
 from . import test_oracle_pins as pins
+from . import test_oracle_rope as rope
 
 HERE = os.path.dirname(os.path.abspath(oracle.__file__))
 
@@ -44,6 +45,12 @@ MUTANTS = {
     "append_bf16_truncates": ("if (dhi < dlo || (dhi == dlo && ((lo >> 16) & 1u))) r = hi;", ""),
     "append_row_off_by_one": (": (int64_t)b * seq_stride + t;", ": (int64_t)b * seq_stride + t + 1;"),
     "append_ignores_capacity": ("if (t < 0 || t >= capacity) continue;", "if (t < 0) continue;"),
+    # decoupled RoPE
+    "rope_sign": ("out[bh * d_r + i] = a * c - b * s;", "out[bh * d_r + i] = a * c + b * s;"),
+    "rope_frequency_exponent": ("inv_freq[i] = (float)pow(base, -(2.0 * (double)i) / (double)d_r);",
+                                "inv_freq[i] = (float)pow(base, -(1.0 * (double)i) / (double)d_r);"),
+    "rope_angle_in_double": ("const float theta = pos * inv_freq[i]; /* binary32 product */",
+                             "const double theta = (double)pos * (double)inv_freq[i];"),
 }
 
 PIN_CHECKS = [
@@ -65,6 +72,10 @@ PIN_CHECKS = [
     lambda: append.test_fp8_append_matches_the_input_quantiser(3.0),
     append.test_bf16_append_rounds_to_nearest_even,
     append.test_append_places_rows_like_the_decode_row_map,
+    rope.test_inverse_frequencies,
+    rope.test_position_zero_is_the_identity,
+    lambda: rope.test_pairs_keep_their_length(2048),
+    rope.test_matches_the_listing_form,
 ]
 
 
@@ -91,7 +102,8 @@ def test_pins_catch_planted_mistake(tmp_path, name, monkeypatch):
     for fn in ("oracle_mla_decode", "oracle_absorb_q", "oracle_combine", "oracle_up_proj",
                "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_array",
                "oracle_mla_cache_bytes_per_token", "oracle_mha_cache_bytes",
-               "oracle_num_threads", "oracle_cache_append", "oracle_encode_e4m3"):
+               "oracle_num_threads", "oracle_cache_append", "oracle_encode_e4m3",
+               "oracle_rope", "oracle_rope_inv_freq"):
         getattr(mut, fn).restype = getattr(good, fn).restype
         getattr(mut, fn).argtypes = getattr(good, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mut)
