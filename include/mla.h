@@ -128,6 +128,25 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* q_nope,
                           int32_t w_dt, void* q_abs, int32_t q_abs_dt,
                           float* q_abs_scale, void* stream);
 
+/* mla_absorb_q with the decoupled RoPE of the positional query ([V2] §2.2:
+ * q_R and k_R carry the position, q_C does not; frequencies 1/base^(2i/d_r)
+ * as in the rotary listings of [V2] and [LAT], whose cat(freqs, freqs) form
+ * pairs element i with element i + d_r/2):
+ *   q_abs[b][i][d_latent + j] = rotation of q_rope[b][i][:] by positions[b]:
+ *     x[j] cos t_j - x[j + d_r/2] sin t_j          (j < d_r/2)
+ *     x[j] cos t_j + x[j - d_r/2] sin t_(j-d_r/2)  (j >= d_r/2)
+ *   t_j = positions[b] * inv_freq[j] in binary32, inv_freq[j] = base^(-2j/d_r)
+ *   rounded once to binary32; every head of a sequence shares its position.
+ * The latent part is mla_absorb_q's.  positions: device int32 [B] (any value);
+ * rope_base > 1 and finite (10000 in the listings), else MLA_E_ARG.  k_R in
+ * the cache is expected already rotated by its own token's position.  Other
+ * arguments and errors as mla_absorb_q; q_abs_dt FP8_E4M3 (which would need a
+ * scale) returns MLA_E_ARG. */
+mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t B, const void* q_nope,
+                               const void* q_rope, int32_t q_dt, const void* w_uk,
+                               int32_t w_dt, const int32_t* positions, float rope_base,
+                               void* q_abs, int32_t q_abs_dt, void* stream);
+
 /* Attention of every head over the latent cache, split into num_splits token
  * ranges per sequence.  Split p of sequence b covers tokens
  *   [p*C, min((p+1)*C, L_b)),  C = 32 * ceil(max_seq_len / (32*num_splits)),

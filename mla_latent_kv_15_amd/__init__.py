@@ -72,6 +72,9 @@ def lib():
         L.mla_combine_up_proj.restype = C.c_int
         L.mla_combine_up_proj.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, f32p, vp, i32, vp,
                                           i32, vp, f32p, vp]
+        L.mla_absorb_q_rope.restype = C.c_int
+        L.mla_absorb_q_rope.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp, i32, vp,
+                                        C.c_float, vp, i32, vp]
         L.mla_cache_append.restype = C.c_int
         L.mla_cache_append.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp,
                                        C.POINTER(CacheDesc), vp]
@@ -84,7 +87,7 @@ def lib():
 
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
-            "mla_cache_append", "mla_status_str", "mla_version")
+            "mla_absorb_q_rope", "mla_cache_append", "mla_status_str", "mla_version")
 
 
 def status_str(status: int) -> str:
@@ -153,6 +156,20 @@ class Cache:
         return CacheDesc(dtype_code(self.rows), _ptr(self.rows), _ptr(self.row_scale),
                          int(self.page_size), int(self.seq_stride), _ptr(self.block_table), mp,
                          _ptr(self.seq_lens), int(self.max_seq_len))
+
+
+def mla_absorb_q_rope(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor,
+                      w_uk: torch.Tensor, positions: torch.Tensor, q_abs: torch.Tensor,
+                      rope_base: float = 10000.0, stream=None) -> None:
+    """mla_absorb_q with q_R rotated by positions (int32 [B] on the device)."""
+    B = int(q_nope.shape[0])
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    d = geo.c()
+    st = lib().mla_absorb_q_rope(C.byref(d), B, _ptr(q_nope), _ptr(q_rope), dtype_code(q_nope),
+                                 _ptr(w_uk), dtype_code(w_uk), _ptr(positions), float(rope_base),
+                                 _ptr(q_abs), dtype_code(q_abs), _stream(stream))
+    _check("mla_absorb_q_rope", st)
 
 
 def mla_cache_append(geo: Geometry, c_kv: torch.Tensor, k_r: torch.Tensor,

@@ -8,6 +8,7 @@
 // (mla_up_proj).  Full per-head keys and values are never formed.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <cmath>
 #include <stdint.h>
 
 #include <mutex>
@@ -967,6 +968,28 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* u_par
   if (lse && lane == 0) lse[static_cast<int64_t>(b) * H + h] = (z > 0.0f) ? mx + logf(z) : -INFINITY;
 }
 
+// ================================================================ decoupled RoPE
+//
+// Rotation of the positional query q_R by the sequence's position (the
+// content part q_C is not rotated): element i pairs with element i + d_r/2,
+//   out[i]         = x[i] cos t_i - x[i + d_r/2] sin t_i,
+//   out[i + d_r/2] = x[i + d_r/2] cos t_i + x[i] sin t_i,
+// t_i = position * inv_freq[i] in binary32, inv_freq[i] = base^(-2i/d_r)
+// rounded once to binary32 on the host.
+
+struct RopeArgs {
+  const int32_t* positions;  // [B]; nullptr: q_R is carried unchanged
+  float inv_freq[kDRope / 2];
+};
+
+// element j of the rotated row whose element j is xj and element j ^ 32 is xp
+__device__ inline float rope_elem(const RopeArgs& R, int pos, int j, float xj, float xp) {
+  const float t = static_cast<float>(pos) * R.inv_freq[j & (kDRope / 2 - 1)];
+  float sn, cs;
+  sincosf(t, &sn, &cs);
+  return j < kDRope / 2 ? xj * cs - xp * sn : xj * cs + xp * sn;
+}
+
 // ================================================================ absorb
 //
 // q_abs[b][h][c] = Σ_n q_nope[b][h][n] W_UK[h][n][c] for a block of up to 8
@@ -980,7 +1003,7 @@ template <int Q_DT, int W_DT, int OUT_DT>
 __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(const void* q_nope, const void* q_rope,
                                                             const void* w_uk, void* q_abs,
                                                             float* q_abs_scale, int B, int H,
-                                                            int d_nope) {
+                                                            int d_nope, RopeArgs R) {
   __shared__ float qs[kAbsBatch][kMaxDHead];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kAbsBatch;
@@ -1007,8 +1030,12 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_kernel(const void* q_nope,
   for (int bb = 0; bb < nb; ++bb) {
     const int64_t ob = (static_cast<int64_t>(b0 + bb) * H + h) * kRowElems;
     float r0 = 0.0f;  // RoPE element handled by this thread (tid < 64)
-    if (tid < kDRope)
-      r0 = load_elem<Q_DT>(q_rope, (static_cast<int64_t>(b0 + bb) * H + h) * kDRope + tid);
+    if (tid < kDRope) {
+      const int64_t rb = (static_cast<int64_t>(b0 + bb) * H + h) * kDRope;
+      r0 = load_elem<Q_DT>(q_rope, rb + tid);
+      if (R.positions)
+        r0 = rope_elem(R, R.positions[b0 + bb], tid, r0, load_elem<Q_DT>(q_rope, rb + (tid ^ 32)));
+    }
     if constexpr (OUT_DT == MLA_FP8_E4M3) {
       // the fp8 absorbed query is not provided yet
       (void)q_abs_scale;
@@ -1087,7 +1114,8 @@ template <int OUT_DT>
 __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_t* q_nope,
                                                                   const void* q_rope,
                                                                   const uint16_t* w_uk, void* q_abs,
-                                                                  int B, int H, int d_nope) {
+                                                                  int B, int H, int d_nope,
+                                                                  RopeArgs R) {
   __shared__ __attribute__((aligned(16))) uint8_t wt[kMaxDHead * kAbsRowBytes];
   const int h = blockIdx.x;
   const int c_slab = blockIdx.y * 128;
@@ -1170,16 +1198,36 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
       }
     }
   }
-  // the RoPE part is carried unchanged (slab 0 copies it; more rows than
-  // threads only when B > 32)
+  // the RoPE part: slab 0 carries it (more rows than threads only when
+  // B > 32), rotated by the sequence's position when positions are given
   if (blockIdx.y == 0) {
     for (int i = tid; i < B * (kDRope / 8); i += kProjThreads) {
       const int b = i >> 3, j = 8 * (i & 7);
-      const u32x4_t v = (i == tid && rope_copy)
-                            ? rv
-                            : *reinterpret_cast<const u32x4_t*>(
-                                  static_cast<const uint16_t*>(q_rope) +
-                                  (static_cast<int64_t>(b) * H + h) * kDRope + j);
+      const uint16_t* rrow = static_cast<const uint16_t*>(q_rope) + (static_cast<int64_t>(b) * H + h) * kDRope;
+      u32x4_t v = (i == tid && rope_copy) ? rv : *reinterpret_cast<const u32x4_t*>(rrow + j);
+      if (R.positions) {  // pair with the chunk 32 elements away
+        const u32x4_t vp = *reinterpret_cast<const u32x4_t*>(rrow + (j ^ 32));
+        const int pos = R.positions[b];
+        float y[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t wv = v[k >> 1], wp = vp[k >> 1];
+          const float xj = __uint_as_float((k & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+          const float xq = __uint_as_float((k & 1) ? (wp & 0xFFFF0000u) : (wp << 16));
+          y[k] = rope_elem(R, pos, j + k, xj, xq);
+        }
+        const int64_t ob = (static_cast<int64_t>(b) * H + h) * kRowElems + kDLatent + j;
+        if constexpr (OUT_DT == MLA_F32) {
+          float* dst = static_cast<float*>(q_abs) + ob;
+          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{y[0], y[1], y[2], y[3]};
+          *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{y[4], y[5], y[6], y[7]};
+        } else {
+          *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(q_abs) + ob) =
+              u32x4_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                      pack_bf16x2(y[6], y[7])};
+        }
+        continue;
+      }
       const int64_t ob = (static_cast<int64_t>(b) * H + h) * kRowElems + kDLatent + j;
       if constexpr (OUT_DT == MLA_F32) {
         float* dst = static_cast<float*>(q_abs) + ob;
@@ -1581,15 +1629,10 @@ using namespace mla;
 
 // ================================================================ entry points
 
-extern "C" mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* q_nope,
-                                     const void* q_rope, int32_t q_dt, const void* w_uk,
-                                     int32_t w_dt, void* q_abs, int32_t q_abs_dt,
-                                     float* q_abs_scale, void* stream) {
-  mla_status_t st = check_absorb(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt,
-                                 q_abs_scale);
-  if (st != MLA_OK || B == 0) return st;
-  if (q_abs_dt == MLA_FP8_E4M3) return MLA_E_UNSUPPORTED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+static mla_status_t absorb_launch(const mla_dims_t* dims, int32_t B, const void* q_nope,
+                                  const void* q_rope, int32_t q_dt, const void* w_uk, int32_t w_dt,
+                                  void* q_abs, int32_t q_abs_dt, const RopeArgs& R,
+                                  hipStream_t s) {
   const int H = dims->heads, dn = dims->d_nope;
   if (q_dt == MLA_BF16 && w_dt == MLA_BF16 && dn % 16 == 0 &&
       (q_abs_dt == MLA_BF16 || q_abs_dt == MLA_F32) &&
@@ -1598,17 +1641,17 @@ extern "C" mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const vo
     const dim3 g2(H, kDLatent / 128);
     if (q_abs_dt == MLA_BF16)
       absorb_mfma_kernel<MLA_BF16><<<g2, kProjThreads, 0, s>>>(
-          static_cast<const uint16_t*>(q_nope), q_rope, static_cast<const uint16_t*>(w_uk), q_abs, B, H, dn);
+          static_cast<const uint16_t*>(q_nope), q_rope, static_cast<const uint16_t*>(w_uk), q_abs, B, H, dn, R);
     else
       absorb_mfma_kernel<MLA_F32><<<g2, kProjThreads, 0, s>>>(
-          static_cast<const uint16_t*>(q_nope), q_rope, static_cast<const uint16_t*>(w_uk), q_abs, B, H, dn);
+          static_cast<const uint16_t*>(q_nope), q_rope, static_cast<const uint16_t*>(w_uk), q_abs, B, H, dn, R);
     return launch_status();
   }
   const dim3 grid(dims->heads, (B + kAbsBatch - 1) / kAbsBatch);
 #define MLA_ABS(QD, WD, OD)                                                                     \
   if (q_dt == QD && w_dt == WD && q_abs_dt == OD) {                                             \
     absorb_kernel<QD, WD, OD><<<grid, kAbsThreads, 0, s>>>(q_nope, q_rope, w_uk, q_abs,         \
-                                                           q_abs_scale, B, H, dn);              \
+                                                           nullptr, B, H, dn, R);               \
     return launch_status();                                                                     \
   }
   MLA_ABS(MLA_F32, MLA_F32, MLA_F32)
@@ -1619,6 +1662,40 @@ extern "C" mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const vo
   MLA_ABS(MLA_BF16, MLA_F32, MLA_BF16)
 #undef MLA_ABS
   return MLA_E_DTYPE;
+}
+
+extern "C" mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* q_nope,
+                                     const void* q_rope, int32_t q_dt, const void* w_uk,
+                                     int32_t w_dt, void* q_abs, int32_t q_abs_dt,
+                                     float* q_abs_scale, void* stream) {
+  mla_status_t st = check_absorb(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt,
+                                 q_abs_scale);
+  if (st != MLA_OK || B == 0) return st;
+  if (q_abs_dt == MLA_FP8_E4M3) return MLA_E_UNSUPPORTED;
+  RopeArgs R{};
+  R.positions = nullptr;
+  return absorb_launch(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt, R,
+                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t B, const void* q_nope,
+                                          const void* q_rope, int32_t q_dt, const void* w_uk,
+                                          int32_t w_dt, const int32_t* positions, float rope_base,
+                                          void* q_abs, int32_t q_abs_dt, void* stream) {
+  mla_status_t st = check_absorb(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt,
+                                 nullptr);
+  if (st != MLA_OK) return st;
+  if (!(rope_base > 1.0f) || !(rope_base < INFINITY)) return MLA_E_ARG;
+  if (B == 0) return MLA_OK;
+  if (!positions) return MLA_E_ARG;
+  if (q_abs_dt == MLA_FP8_E4M3) return MLA_E_UNSUPPORTED;
+  RopeArgs R{};
+  R.positions = positions;
+  for (int i = 0; i < kDRope / 2; ++i)
+    R.inv_freq[i] = static_cast<float>(std::pow(static_cast<double>(rope_base),
+                                                -2.0 * static_cast<double>(i) / kDRope));
+  return absorb_launch(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt, R,
+                       static_cast<hipStream_t>(stream));
 }
 
 extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,

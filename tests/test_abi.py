@@ -187,3 +187,22 @@ def test_cache_append_validation():
     assert ap(c=cache(page_size=64, block_table=P, max_pages=0)) == E_ARG
     assert ap(c=cache(rows=P + 8)) == E_ALIGN
     assert ap(d=dims(dl=256)) == E_SHAPE
+
+
+def test_absorb_q_rope_validation():
+    L = mla.lib()
+
+    def ar(B=2, qn=P, qr=P, q_dt=BF16, w=P, w_dt=BF16, pos=P, base=10000.0, qa=P, qa_dt=BF16):
+        return L.mla_absorb_q_rope(C.byref(dims()), B, qn, qr, q_dt, w, w_dt, pos, base, qa, qa_dt,
+                                   None)
+
+    assert ar(B=0, qn=None, qr=None, w=None, pos=None, qa=None) == OK
+    assert ar(pos=None) == E_ARG
+    assert ar(base=1.0) == E_ARG
+    assert ar(base=float("inf")) == E_ARG
+    assert ar(base=float("nan")) == E_ARG
+    assert ar(B=0, base=0.5) == E_ARG
+    assert ar(qn=None) == E_ARG
+    assert ar(q_dt=FP8) == E_DTYPE
+    assert ar(qa_dt=FP8) == E_ARG  # an fp8 q_abs needs a scale this call does not take
+    assert ar(qa=P + 8) == E_ALIGN
