@@ -276,6 +276,11 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     outside_us = {"mla_cache_append": e0.elapsed_time(e1) / args.steps * 1e3}
+    # and the absorb with the decoupled RoPE of q_R (the step's absorb variant
+    # for callers whose q_R is not rotated yet)
+    outside_us["mla_absorb_q_rope"] = loop_ms(lambda rp: mla.mla_absorb_q_rope(
+        step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], last, step.q_abs,
+        stream=stream)) * 1e3
 
     launch_bytes = cache_bytes  # algorithmic bytes of one mla_decode launch
     achieved = launch_bytes / t_decode / 1e9
