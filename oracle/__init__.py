@@ -67,6 +67,9 @@ def lib():
                                                             C.c_void_p, C.c_void_p, C.c_int32,
                                                             C.c_void_p, C.c_int32, C.c_int64,
                                                             C.c_void_p, C.c_int32]
+        L.oracle_mha_decode.restype = C.c_int
+        L.oracle_mha_decode.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 3 + [
+            C.c_int32, C.c_void_p, C.c_int64, C.c_double, C.c_void_p, C.c_void_p]
         L.oracle_rope.restype = C.c_int
         L.oracle_rope.argtypes = [C.c_int32] * 3 + [C.c_void_p, C.c_int32, C.c_void_p,
                                                     C.c_double, C.c_void_p]
@@ -200,6 +203,25 @@ def cache_append(c_kv, k_r, src_dtype, positions, rows, cache_dtype, row_scale=N
                                    max_pages)
     if rc != 0:
         raise ValueError(f"oracle_cache_append failed: {rc}")
+
+
+def mha_decode(q, k, v, dtype, seq_lens, scale=0.0):
+    """Textbook multi-head attention decode over a per-head cache.
+    q [B, H, d_qk], k [B, H, stride, d_qk], v [B, H, stride, d_v] (stored bits
+    in dtype), seq_lens [B] -> (o [B, H, d_v], lse [B, H]) float64."""
+    d = _dt(dtype)
+    q, k, v = _arr(q, d), _arr(k, d), _arr(v, d)
+    B, H, dq = q.shape
+    stride, dv = k.shape[2], v.shape[3]
+    assert k.shape == (B, H, stride, dq) and v.shape[:3] == (B, H, stride)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    o = np.zeros((B, H, dv), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    rc = lib().oracle_mha_decode(B, H, dq, dv, _ptr(q), _ptr(k), _ptr(v), d, _ptr(lens), stride,
+                                 float(scale), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_mha_decode failed: {rc}")
+    return o, lse
 
 
 def rope(x, dtype, positions, base=10000.0):

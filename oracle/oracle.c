@@ -389,6 +389,59 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
   return 0;
 }
 
+/* ------------------------------------------------------ MHA baseline */
+
+int oracle_mha_decode(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, const void* q,
+                      const void* k, const void* v, int32_t dtype, const int32_t* seq_lens,
+                      int64_t seq_stride, double scale, double* o, double* lse) {
+  if (B < 0 || H <= 0 || d_qk <= 0 || d_v <= 0 || !q || !k || !v || !seq_lens || !o || !lse)
+    return -1;
+  if (!valid_dtype(dtype)) return -3;
+  if (seq_stride < 0) return -2;
+  const double sc = scale > 0.0 ? scale : 1.0 / sqrt((double)d_qk);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+    const int64_t b = bh / H;
+    const int64_t L = seq_lens[b];
+    double* out = o + bh * d_v;
+    for (int32_t j = 0; j < d_v; ++j) out[j] = 0.0;
+    if (L < 0 || L > seq_stride) {
+      bad = 1;
+      continue;
+    }
+    if (L == 0) {
+      lse[bh] = -INFINITY;
+      continue;
+    }
+    double* s = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!s) {
+      bad = 1;
+      continue;
+    }
+    /* scores */
+    double m = -INFINITY;
+    for (int64_t t = 0; t < L; ++t) {
+      double dot = 0.0;
+      for (int32_t j = 0; j < d_qk; ++j)
+        dot += load_elem(q, dtype, bh * d_qk + j) * load_elem(k, dtype, (bh * seq_stride + t) * d_qk + j);
+      s[t] = sc * dot;
+      if (s[t] > m) m = s[t];
+    }
+    /* softmax weights and the weighted sum of the values */
+    double l = 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      const double p = exp(s[t] - m);
+      l += p;
+      for (int32_t j = 0; j < d_v; ++j) out[j] += p * load_elem(v, dtype, (bh * seq_stride + t) * d_v + j);
+    }
+    for (int32_t j = 0; j < d_v; ++j) out[j] /= l;
+    lse[bh] = m + log(l);
+    free(s);
+  }
+  return bad ? -2 : 0;
+}
+
 /* ------------------------------------------------------ decoupled RoPE */
 
 void oracle_rope_inv_freq(int32_t d_r, double base, float* inv_freq) {

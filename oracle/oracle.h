@@ -93,6 +93,20 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
                         void* rows, int32_t cache_dtype, float* row_scale, int32_t page_size,
                         int64_t seq_stride, const int32_t* block_table, int32_t max_pages);
 
+/* Multi-head attention decode over a full per-head K/V cache, the baseline
+ * the latent cache replaces ([LAT] §2.1 textbook attention
+ * softmax(q k^T / sqrt(d_k)) v; [V2] §1.1 the MHA cache holds K and V of
+ * every head):
+ *   o[b][i] = sum_t p_t v[b][i][t] / sum_t p_t,  p_t = exp(s_t - max s),
+ *   s_t = scale * q[b][i] . k[b][i][t],  t < seq_lens[b],
+ * scale <= 0 means 1/sqrt(d_qk).  q [B][H][d_qk]; k [B][H][seq_stride][d_qk]
+ * and v [B][H][seq_stride][d_v] (head-major) in dtype; o [B][H][d_v] and
+ * lse [B][H] (natural log, -inf for an empty sequence) in float64.  Returns 0,
+ * or a negative value on a bad argument. */
+int oracle_mha_decode(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, const void* q,
+                      const void* k, const void* v, int32_t dtype, const int32_t* seq_lens,
+                      int64_t seq_stride, double scale, double* o, double* lse);
+
 /* Decoupled RoPE of the positional query ([V2] §2.2: only q_R and k_R are
  * rotated, q_C is left as it is; frequencies 1/10000^(2i/d) as in the
  * listings of [V2] and [LAT]; the [LAT] listing repeats the d/2 frequencies

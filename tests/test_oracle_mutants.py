@@ -14,6 +14,7 @@ from oracle.build import CFLAGS
 
 from . import test_oracle_append as append
 from . import test_oracle_codecs as codecs
+from . import test_oracle_mha as mha
 from . import test_oracle_pins as pins
 from . import test_oracle_rope as rope
 
@@ -49,6 +50,12 @@ MUTANTS = {
     "rope_sign": ("out[bh * d_r + i] = a * c - b * s;", "out[bh * d_r + i] = a * c + b * s;"),
     "rope_frequency_exponent": ("inv_freq[i] = (float)pow(base, -(2.0 * (double)i) / (double)d_r);",
                                 "inv_freq[i] = (float)pow(base, -(1.0 * (double)i) / (double)d_r);"),
+    # MHA baseline
+    "mha_scale_over_dv": ("const double sc = scale > 0.0 ? scale : 1.0 / sqrt((double)d_qk);",
+                          "const double sc = scale > 0.0 ? scale : 1.0 / sqrt((double)d_v);"),
+    "mha_missing_normalisation": ("for (int32_t j = 0; j < d_v; ++j) out[j] /= l;", ""),
+    "mha_key_stride": ("load_elem(k, dtype, (bh * seq_stride + t) * d_qk + j)",
+                       "load_elem(k, dtype, (bh * seq_stride + t) * d_v + j)"),
     "rope_angle_in_double": ("const float theta = pos * inv_freq[i]; /* binary32 product */",
                              "const double theta = (double)pos * (double)inv_freq[i];"),
 }
@@ -76,6 +83,9 @@ PIN_CHECKS = [
     rope.test_position_zero_is_the_identity,
     lambda: rope.test_pairs_keep_their_length(2048),
     rope.test_matches_the_listing_form,
+    lambda: mha.test_matches_library_attention(192, 128),
+    mha.test_mla_is_mha_on_rebuilt_keys_and_values,
+    mha.test_closed_forms,
 ]
 
 
@@ -103,7 +113,7 @@ def test_pins_catch_planted_mistake(tmp_path, name, monkeypatch):
                "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_array",
                "oracle_mla_cache_bytes_per_token", "oracle_mha_cache_bytes",
                "oracle_num_threads", "oracle_cache_append", "oracle_encode_e4m3",
-               "oracle_rope", "oracle_rope_inv_freq"):
+               "oracle_rope", "oracle_rope_inv_freq", "oracle_mha_decode"):
         getattr(mut, fn).restype = getattr(good, fn).restype
         getattr(mut, fn).argtypes = getattr(good, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mut)
