@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-call-tail", action="store_true",
                     help="merge and up-project with mla_combine + mla_up_proj")
+    ap.add_argument("--mha", action="store_true",
+                    help="the MHA baseline instead: per-head bf16 K/V cache at the geometry of "
+                         "--workload (batch, heads, lengths; head dim 128), mla_mha_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -107,6 +110,72 @@ def record_traffic(d):
     print(json.dumps(rec))
 
 
+def mha_baseline(args):
+    """Multi-head attention decode over a per-head K/V cache (what MLA's latent
+    cache replaces) at the batch, heads and lengths of --workload: one launch
+    of mla_mha_decode per step.  The cache (2 x h x 128 bf16 per token) is far
+    larger than the 256 MB Infinity Cache, so one copy is streamed from HBM."""
+    import torch
+
+    import mla_latent_kv_15_amd as mla
+    import synth
+
+    wl = synth.workload(args.workload)
+    lens = synth.workloads.sequence_lengths(wl)
+    B, H, D = wl.batch, wl.heads, 128
+    L = int(lens.max())
+    print(f"[bench] MHA baseline at {wl.name}: B={B} h={H} L<={L}", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    q = torch.randn(B, H, D, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.empty(B, H, L, D, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    for b in range(B):  # per sequence, to bound the fp32 temporaries
+        k[b] = torch.randn(H, L, D, device="cuda", generator=g).to(torch.bfloat16)
+        v[b] = torch.randn(H, L, D, device="cuda", generator=g).to(torch.bfloat16)
+    seq = torch.from_numpy(lens.astype("int32")).cuda()
+    o = torch.empty(B, H, D, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one():
+        mla.mla_mha_decode(q, k, v, seq, L, o, stream=stream)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        one()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_k = e0.elapsed_time(e1) / args.steps * 1e-3
+    kv_bytes = int(lens.astype("int64").sum()) * H * D * 2 * 2
+    mla_bytes = synth.cache_bytes(wl, lens)
+    achieved = kv_bytes / t_k / 1e9
+    rec = {
+        "metric": "MHA baseline decode tokens/s + K/V HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) q, K, V)",
+        "config": {"workload": f"mha_baseline_{wl.name}", "batch": B, "heads": H, "d_head": D,
+                   "seq_len": L, "cache": "bf16 per-head K and V, head-major",
+                   "parallelism": "none (1 GPU)"},
+        "kv_cache_bytes": kv_bytes, "mla_cache_bytes_same_tokens": mla_bytes,
+        "cache_ratio": kv_bytes / mla_bytes,
+        "kernel_us_mean": {"mla_mha_decode": t_k * 1e6},
+        "roofline": {"kernel": "mla_mha_decode", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": kv_bytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def calibrate_copy():
     import torch
     n = 1 << 30
@@ -162,6 +231,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.mha:
+        mha_baseline(args)
         return
 
     wl = synth.workload(args.workload)

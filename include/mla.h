@@ -229,6 +229,25 @@ mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, const void* c_k
                               const void* k_r, int32_t src_dt, const int32_t* positions,
                               const mla_cache_t* cache, void* stream);
 
+/* Multi-head attention decode over a full per-head K/V cache: the baseline
+ * the latent cache replaces ([LAT] §2.1 softmax(q k^T / sqrt(d_k)) v; [V2]
+ * §1.1 the MHA cache holds K and V of every head, 2 x h x d elements per
+ * token and layer against MLA's d_c + d_r).  For every sequence b and head i:
+ *   s_t = scale * q[b][i] . k[b][i][t],  t < L_b = min(seq_lens[b], max_seq_len)
+ *   o[b][i][:] = sum_t e^{s_t} v[b][i][t][:] / sum_t e^{s_t}
+ *   lse[b][i]  = ln sum_t e^{s_t}  (-inf and o = 0 for an empty sequence)
+ * scale = softmax_scale, or 1/sqrt(d_head) when softmax_scale <= 0.
+ * q [B][heads][d_head]; k_cache, v_cache [B][heads][seq_stride][d_head]
+ * (head-major), all BF16 and 16-byte aligned; d_head = 128; seq_stride >=
+ * max_seq_len; o [B][heads][d_head] in o_dt (F32 or BF16); lse fp32 [B][heads]
+ * or NULL.  Errors: MLA_E_ARG (pointers, lengths, NaN scale), MLA_E_SHAPE
+ * (d_head), MLA_E_DTYPE (dtypes), MLA_E_ALIGN. */
+mla_status_t mla_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void* q,
+                            const void* k_cache, const void* v_cache, int32_t dt,
+                            const int32_t* seq_lens, int64_t seq_stride, int32_t max_seq_len,
+                            float softmax_scale, void* o, int32_t o_dt, float* lse,
+                            void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mla_status_str(mla_status_t status);
 

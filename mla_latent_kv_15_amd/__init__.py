@@ -75,6 +75,9 @@ def lib():
         L.mla_absorb_q_rope.restype = C.c_int
         L.mla_absorb_q_rope.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp, i32, vp,
                                         C.c_float, vp, i32, vp]
+        L.mla_mha_decode.restype = C.c_int
+        L.mla_mha_decode.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, C.c_int64, i32,
+                                     C.c_float, vp, i32, f32p, vp]
         L.mla_cache_append.restype = C.c_int
         L.mla_cache_append.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp,
                                        C.POINTER(CacheDesc), vp]
@@ -87,7 +90,8 @@ def lib():
 
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
-            "mla_absorb_q_rope", "mla_cache_append", "mla_status_str", "mla_version")
+            "mla_absorb_q_rope", "mla_cache_append", "mla_mha_decode", "mla_status_str",
+            "mla_version")
 
 
 def status_str(status: int) -> str:
@@ -170,6 +174,20 @@ def mla_absorb_q_rope(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor,
                                  _ptr(w_uk), dtype_code(w_uk), _ptr(positions), float(rope_base),
                                  _ptr(q_abs), dtype_code(q_abs), _stream(stream))
     _check("mla_absorb_q_rope", st)
+
+
+def mla_mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seq_lens: torch.Tensor, max_seq_len: int, o: torch.Tensor,
+                   lse: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                   stream=None) -> None:
+    """MHA baseline decode: q [B, h, 128], k_cache / v_cache [B, h, stride, 128]
+    (bfloat16), seq_lens int32 [B] on the device; o [B, h, 128]."""
+    B, H, D = (int(x) for x in q.shape)
+    st = lib().mla_mha_decode(B, H, D, _ptr(q), _ptr(k_cache), _ptr(v_cache), dtype_code(q),
+                              _ptr(seq_lens), int(k_cache.shape[2]), int(max_seq_len),
+                              float(softmax_scale), _ptr(o), dtype_code(o), _ptr(lse),
+                              _stream(stream))
+    _check("mla_mha_decode", st)
 
 
 def mla_cache_append(geo: Geometry, c_kv: torch.Tensor, k_r: torch.Tensor,

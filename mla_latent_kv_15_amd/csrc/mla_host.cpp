@@ -174,6 +174,22 @@ mla_status_t check_cache_append(const mla_dims_t* dims, int32_t B, const void* c
   return MLA_OK;
 }
 
+mla_status_t check_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void* q,
+                              const void* k_cache, const void* v_cache, int32_t dt,
+                              const int32_t* seq_lens, int64_t seq_stride, int32_t max_seq_len,
+                              float softmax_scale, const void* o, int32_t o_dt) {
+  if (B < 0 || heads < 1 || d_head < 1 || max_seq_len < 0) return MLA_E_ARG;
+  if (!(softmax_scale == softmax_scale)) return MLA_E_ARG;  // NaN
+  if (!valid_dtype(dt) || !valid_dtype(o_dt)) return MLA_E_ARG;
+  if (d_head != kMhaHeadDim) return MLA_E_SHAPE;
+  if (seq_stride < max_seq_len || seq_stride < 1) return MLA_E_ARG;
+  if (B == 0) return MLA_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !o) return MLA_E_ARG;
+  if (dt != MLA_BF16 || o_dt == MLA_FP8_E4M3) return MLA_E_DTYPE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return MLA_E_ALIGN;
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 extern "C" const char* mla_status_str(mla_status_t status) {

@@ -17,6 +17,7 @@ constexpr int32_t kPageSize = 64;
 constexpr int32_t kMaxSplits = 1024;
 constexpr int32_t kMaxDHead = 256;  // d_nope / d_v bound of absorb and up-projection
 constexpr int32_t kHeadsPerWave = 32;
+constexpr int32_t kMhaHeadDim = 128;  // head dimension of the MHA baseline kernel
 
 inline int32_t dtype_bytes(int32_t dt) {
   return dt == MLA_F32 ? 4 : dt == MLA_BF16 ? 2 : dt == MLA_FP8_E4M3 ? 1 : 0;
@@ -57,5 +58,10 @@ mla_status_t check_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t nu
 mla_status_t check_cache_append(const mla_dims_t* dims, int32_t B, const void* c_kv,
                                 const void* k_r, int32_t src_dt, const int32_t* positions,
                                 const mla_cache_t* cache);
+
+mla_status_t check_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void* q,
+                              const void* k_cache, const void* v_cache, int32_t dt,
+                              const int32_t* seq_lens, int64_t seq_stride, int32_t max_seq_len,
+                              float softmax_scale, const void* o, int32_t o_dt);
 
 }  // namespace mla

@@ -1542,6 +1542,148 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   }
 }
 
+// ================================================================ MHA baseline decode
+//
+// Multi-head attention decode over a full per-head bf16 K/V cache (head-major
+// [B][h][seq_stride][128]), the baseline the latent cache replaces.  One
+// workgroup of 4 waves per (b, head); wave w streams a contiguous quarter of
+// the tokens with its own online softmax.  Per step a wave takes 16 tokens:
+// lane group g (16 lanes) owns tokens 4u + g, lane k of a group holds
+// elements 8k..8k+7 of a key and a value row (16-byte loads, 256 contiguous
+// bytes per token), the dot products reduce over the 16 lanes, one maximum
+// per step rescales the accumulators.  The next step's 8 loads per lane are
+// in flight while a step is summed.  The four waves merge in LDS.  No matrix
+// cores: one query row per head has nothing to reuse, the kernel is a stream.
+
+constexpr int kMhaThreads = 256;
+constexpr int kMhaD = 128;
+
+template <int O_DT>
+__global__ __launch_bounds__(kMhaThreads) void mha_decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ seq_lens, int64_t seq_stride, int32_t max_seq_len, int H,
+    float scale_log2, void* o, float* lse) {
+  __shared__ float red_m[4], red_l[4];
+  __shared__ __attribute__((aligned(16))) float red_acc[4][kMhaD];
+  const int bh = blockIdx.x;
+  const int b = bh / H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, k = lane & 15;
+  const int L = min(max(seq_lens[b], 0), max_seq_len);
+  const int chunk = ((L + 3) / 4 + 15) & ~15;  // tokens per wave, a multiple of 16
+  const int t0 = min(wave * chunk, L), t1 = min(t0 + chunk, L);
+  const int64_t rowbase = static_cast<int64_t>(bh) * seq_stride;
+
+  float qv[8];
+  {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(q + static_cast<int64_t>(bh) * kMhaD + 8 * k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[2 * i] = __uint_as_float(w[i] << 16) * scale_log2;
+      qv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * scale_log2;
+    }
+  }
+  float m = -INFINITY, l = 0.0f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+
+  // rows of tokens past the wave's range are replaced by its first row
+  // (finite data, weight zero); a wave with no tokens loads nothing
+  auto load = [&](u32x4_t (&kr)[4], u32x4_t (&vr)[4], int ts) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = ts + 4 * u + g;
+      const int64_t r = (rowbase + (t < t1 ? t : t0)) * kMhaD + 8 * k;
+      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc + r));
+      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc + r));
+    }
+  };
+  auto step = [&](const u32x4_t (&kr)[4], const u32x4_t (&vr)[4], int ts) {
+    float sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d = fmaf(qv[2 * i], __uint_as_float(kr[u][i] << 16), d);
+        d = fmaf(qv[2 * i + 1], __uint_as_float(kr[u][i] & 0xFFFF0000u), d);
+      }
+#pragma unroll
+      for (int o2 = 8; o2 >= 1; o2 >>= 1) d += __shfl_xor(d, o2);
+      sc[u] = (ts + 4 * u + g < t1) ? d : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);  // finite: every step holds at least one token
+    const float r = __builtin_amdgcn_exp2f(m - mn);
+    l *= r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float p = __builtin_amdgcn_exp2f(sc[u] - mn);
+      l += p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(p, __uint_as_float(vr[u][i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(p, __uint_as_float(vr[u][i] & 0xFFFF0000u), acc[2 * i + 1]);
+      }
+    }
+    m = mn;
+  };
+  if (t0 < t1) {
+    u32x4_t ka[4], va[4], kb[4], vb[4];
+    load(ka, va, t0);
+    for (int ts = t0; ts < t1; ts += 32) {
+      if (ts + 16 < t1) load(kb, vb, ts + 16);
+      step(ka, va, ts);
+      if (ts + 16 < t1) {
+        if (ts + 32 < t1) load(ka, va, ts + 32);
+        step(kb, vb, ts + 16);
+      }
+    }
+  }
+  // the four lane groups: the sums of their own tokens (m is common)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i] += __shfl_xor(acc[i], 16);
+    acc[i] += __shfl_xor(acc[i], 32);
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (lane < 16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red_acc[wave][8 * lane + i] = acc[i];
+  }
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_l[wave] = l;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w]);
+    float lt = 0.0f, ot[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ot[i] = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = __builtin_amdgcn_exp2f(red_m[w] - M);  // 0 for a wave without tokens
+        lt += f * red_l[w];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ot[i] += f * red_acc[w][8 * lane + i];
+      }
+    }
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) store_elem<O_DT>(o, static_cast<int64_t>(bh) * kMhaD + 8 * lane + i, ot[i] * inv);
+    if (lse && lane == 0) lse[bh] = lt > 0.0f ? (M + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 // ================================================================ cache append
 //
 // One wave per sequence writes the new token's row (576 elements: lane l
@@ -1859,4 +2001,28 @@ extern "C" mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, cons
   MLA_AP(MLA_BF16, MLA_FP8_E4M3)
 #undef MLA_AP
   return MLA_E_DTYPE;
+}
+
+extern "C" mla_status_t mla_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void* q,
+                                       const void* k_cache, const void* v_cache, int32_t dt,
+                                       const int32_t* seq_lens, int64_t seq_stride,
+                                       int32_t max_seq_len, float softmax_scale, void* o,
+                                       int32_t o_dt, float* lse, void* stream) {
+  mla_status_t st = check_mha_decode(B, heads, d_head, q, k_cache, v_cache, dt, seq_lens,
+                                     seq_stride, max_seq_len, softmax_scale, o, o_dt);
+  if (st != MLA_OK || B == 0) return st;
+  const int64_t nblk = static_cast<int64_t>(B) * heads;
+  if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(d_head));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* qp = static_cast<const uint16_t*>(q);
+  const auto* kp = static_cast<const uint16_t*>(k_cache);
+  const auto* vp = static_cast<const uint16_t*>(v_cache);
+  if (o_dt == MLA_F32)
+    mha_decode_kernel<MLA_F32><<<static_cast<unsigned>(nblk), kMhaThreads, 0, s>>>(
+        qp, kp, vp, seq_lens, seq_stride, max_seq_len, heads, scale * kLog2e, o, lse);
+  else
+    mha_decode_kernel<MLA_BF16><<<static_cast<unsigned>(nblk), kMhaThreads, 0, s>>>(
+        qp, kp, vp, seq_lens, seq_stride, max_seq_len, heads, scale * kLog2e, o, lse);
+  return launch_status();
 }

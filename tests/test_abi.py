@@ -206,3 +206,27 @@ def test_absorb_q_rope_validation():
     assert ar(q_dt=FP8) == E_DTYPE
     assert ar(qa_dt=FP8) == E_ARG  # an fp8 q_abs needs a scale this call does not take
     assert ar(qa=P + 8) == E_ALIGN
+
+
+def test_mha_decode_validation():
+    L = mla.lib()
+
+    def mh(B=2, H=128, D=128, q=P, k=P, v=P, dt=BF16, lens=P, stride=4096, maxl=4096, sc=0.0,
+           o=P, o_dt=BF16, lse=None):
+        return L.mla_mha_decode(B, H, D, q, k, v, dt, lens, stride, maxl, sc, o, o_dt, lse, None)
+
+    assert mh(B=0, q=None, k=None, v=None, lens=None, o=None) == OK
+    assert mh(B=-1) == E_ARG
+    assert mh(H=0) == E_ARG
+    assert mh(D=64) == E_SHAPE
+    assert mh(q=None) == E_ARG
+    assert mh(k=None) == E_ARG
+    assert mh(lens=None) == E_ARG
+    assert mh(o=None) == E_ARG
+    assert mh(stride=100, maxl=200) == E_ARG
+    assert mh(maxl=-1) == E_ARG
+    assert mh(sc=float("nan")) == E_ARG
+    assert mh(dt=F32) == E_DTYPE
+    assert mh(o_dt=FP8) == E_DTYPE
+    assert mh(dt=7) == E_ARG
+    assert mh(k=P + 2) == E_ALIGN
