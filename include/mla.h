@@ -168,6 +168,25 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
                         const mla_cache_t* cache, int32_t num_splits, void* u_part,
                         int32_t part_dt, float* lse_part, void* stream);
 
+/* mla_decode for q_len query tokens per sequence (a multi-token step, e.g. a
+ * speculative draft): the last q_len cached rows of sequence b are its new
+ * tokens, and query token j (0-based) attends causally ([LAT]'s varlen
+ * attention call with causal=True) to the cached rows
+ *   t < L_b - (q_len - 1 - j),   L_b = min(seq_lens[b], max_seq_len),
+ * i.e. its own row and the rows before it (none if that bound is <= 0: u = 0,
+ * lse = -inf).  q_abs [B][q_len][h][576] (mla_absorb_q over B*q_len
+ * sequences); u_part [B][q_len][num_splits][h][d_latent] and lse_part
+ * [B][q_len][num_splits][h] are laid out as mla_decode's for B*q_len
+ * sequences, so mla_combine / mla_combine_up_proj over B*q_len finish the
+ * step.  Split ranges as mla_decode's (from max_seq_len).  1 <= q_len <= 16
+ * (else MLA_E_ARG); BF16 and FP8 caches (an F32 cache with q_len > 1 returns
+ * MLA_E_UNSUPPORTED).  Other arguments and errors as mla_decode (no
+ * q_abs_scale). */
+mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
+                              const void* q_abs, int32_t q_abs_dt, const mla_cache_t* cache,
+                              int32_t num_splits, void* u_part, int32_t part_dt,
+                              float* lse_part, void* stream);
+
 /* Merge the split partials of mla_decode with log-sum-exp weights:
  *   lse[b][i] = ln sum_p e^{lse_part[b][p][i]}
  *   u[b][i][:] = sum_p e^{lse_part[b][p][i] - lse[b][i]} * u_part[b][p][i][:]

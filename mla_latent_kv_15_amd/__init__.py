@@ -65,6 +65,9 @@ def lib():
         L.mla_decode.restype = C.c_int
         L.mla_decode.argtypes = [C.POINTER(Dims), i32, vp, i32, f32p, C.POINTER(CacheDesc), i32,
                                  vp, i32, f32p, vp]
+        L.mla_decode_multi.restype = C.c_int
+        L.mla_decode_multi.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, C.POINTER(CacheDesc),
+                                       i32, vp, i32, f32p, vp]
         L.mla_combine.restype = C.c_int
         L.mla_combine.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, f32p, vp, i32, f32p, vp]
         L.mla_up_proj.restype = C.c_int
@@ -89,7 +92,7 @@ def lib():
     return _lib
 
 
-EXPORTED = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
+EXPORTED = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
             "mla_absorb_q_rope", "mla_cache_append", "mla_mha_decode", "mla_status_str",
             "mla_version")
 
@@ -226,6 +229,20 @@ def mla_decode(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int
                           C.byref(cd), int(num_splits), _ptr(u_part), dtype_code(u_part),
                           _ptr(lse_part), _stream(stream))
     _check("mla_decode", st)
+
+
+def mla_decode_multi(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int,
+                     u_part: torch.Tensor, lse_part: torch.Tensor, stream=None) -> None:
+    """Multi-token decode: q_abs [B, q_len, h, 576]; u_part [B, q_len, S, h,
+    512]; lse_part [B, q_len, S, h] (the last q_len cached rows are the new
+    tokens, attended causally)."""
+    B, QL = int(q_abs.shape[0]), int(q_abs.shape[1])
+    d = geo.c()
+    cd = cache.c()
+    st = lib().mla_decode_multi(C.byref(d), B, QL, _ptr(q_abs), dtype_code(q_abs), C.byref(cd),
+                                int(num_splits), _ptr(u_part), dtype_code(u_part), _ptr(lse_part),
+                                _stream(stream))
+    _check("mla_decode_multi", st)
 
 
 def mla_combine(geo: Geometry, u_part: torch.Tensor, lse_part: torch.Tensor, u: torch.Tensor,

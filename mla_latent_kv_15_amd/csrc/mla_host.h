@@ -18,6 +18,7 @@ constexpr int32_t kMaxSplits = 1024;
 constexpr int32_t kMaxDHead = 256;  // d_nope / d_v bound of absorb and up-projection
 constexpr int32_t kHeadsPerWave = 32;
 constexpr int32_t kMhaHeadDim = 128;  // head dimension of the MHA baseline kernel
+constexpr int32_t kMaxQueryTokens = 16;  // query tokens per sequence in mla_decode_multi
 
 inline int32_t dtype_bytes(int32_t dt) {
   return dt == MLA_F32 ? 4 : dt == MLA_BF16 ? 2 : dt == MLA_FP8_E4M3 ? 1 : 0;

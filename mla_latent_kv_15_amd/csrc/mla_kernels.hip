@@ -137,6 +137,7 @@ struct DecodeParams {
   int32_t paged;
   int32_t B, H, S, HG, chunk;
   int32_t max_seq_len;
+  int32_t QL;  // query tokens per sequence (1: plain decode)
   float scale_log2;
   void* u_part;
   float* lse_part;
@@ -252,12 +253,18 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   float* linv = reinterpret_cast<float*>(smem);  // epilogue: 1 / l per head (tile buffer 0)
   float* tscale = reinterpret_cast<float*>(smem + kX64Off + 1024);  // fp8: [kNBuf][32] row scales
 
-  const int nwork = P.B * P.S * P.HG;
+  // work id -> (head group, query token j, split p, sequence b), the head
+  // groups and query tokens of one split range adjacent (same XCD, so they
+  // share each tile through L2)
+  const int nwork = P.B * P.QL * P.S * P.HG;
   const int wid = xcd_remap(blockIdx.x, nwork);
   const int hg = wid % P.HG;
-  const int bp = wid / P.HG;
-  const int p = bp % P.S;
-  const int b = bp / P.S;
+  const int r1 = wid / P.HG;
+  const int qj = r1 % P.QL;
+  const int r2 = r1 / P.QL;
+  const int p = r2 % P.S;
+  const int b = r2 / P.S;
+  const int bj = b * P.QL + qj;  // row of (b, qj) in q_abs, u_part and lse_part
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
@@ -266,10 +273,12 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   const int hbase = hg * kH64;
   const int nhb = min(kH64Blocks, (P.H - hbase) / kHeadsPerWave);  // 1 or 2
 
-  const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
+  // query token qj of QL new tokens (the last QL cached rows) sees the cached
+  // rows up to and including its own: the first L - (QL - 1 - qj)
+  const int L = max(min(max(P.seq_lens[b], 0), P.max_seq_len) - (P.QL - 1 - qj), 0);
   const int t_begin = p * P.chunk;
   const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(b) * P.S + p) * P.H + hbase;
+  const int64_t row_base = (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase;
 
   if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
     if (!is_qk) {
@@ -549,7 +558,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
 
   // the queries of both head blocks (32 rows each) go into tile buffers 2 and 3
   const uint8_t* qsrc = static_cast<const uint8_t*>(P.q_abs) +
-                        (static_cast<int64_t>(b) * P.H + hbase) * kRowBytes;
+                        (static_cast<int64_t>(bj) * P.H + hbase) * kRowBytes;
   auto stage_q = [&] {
     for (int hb = 0; hb < nhb; ++hb)
       rows_dma_g8(qsrc + hb * kHeadsPerWave * kRowBytes, lds_addr(smem) + (2 + hb) * kTileBytes,
@@ -1840,20 +1849,16 @@ extern "C" mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t B, con
                        static_cast<hipStream_t>(stream));
 }
 
-extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
-                                   int32_t q_abs_dt, const float* q_abs_scale,
-                                   const mla_cache_t* cache, int32_t num_splits, void* u_part,
-                                   int32_t part_dt, float* lse_part, void* stream) {
-  mla_status_t st = check_decode(dims, B, q_abs, q_abs_dt, q_abs_scale, cache, num_splits,
-                                 u_part, part_dt, lse_part);
-  if (st != MLA_OK || B == 0) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_len,
+                                  const void* q_abs, const mla_cache_t* cache, int32_t num_splits,
+                                  void* u_part, int32_t part_dt, float* lse_part, hipStream_t s) {
   const int32_t H = dims->heads;
   // with max_seq_len == 0 every range is empty; a chunk of 32 keeps the
   // kernels' range arithmetic well defined
   const int32_t chunk = max(split_chunk(cache->max_seq_len, num_splits), kTileTokens);
   const float scale = effective_scale(dims);
   if (cache->dtype == MLA_F32) {
+    if (q_len != 1) return MLA_E_UNSUPPORTED;
     DecodeF32Params P{static_cast<const float*>(q_abs), static_cast<const float*>(cache->rows),
                       cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                       cache->page_size != 0, B, H, num_splits, chunk, cache->max_seq_len, scale,
@@ -1866,15 +1871,15 @@ extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void
       decode_f32_kernel<MLA_BF16><<<static_cast<unsigned>(nblk), kF32Threads, 0, s>>>(P);
     return launch_status();
   }
-  // workgroups of 64 heads
+  // workgroups of 64 heads of one query token
   const int32_t HG64 = (H + kH64 - 1) / kH64;
-  const int64_t nblk64 = static_cast<int64_t>(B) * num_splits * HG64;
+  const int64_t nblk64 = static_cast<int64_t>(B) * q_len * num_splits * HG64;
   if (nblk64 > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid64 = static_cast<unsigned>(nblk64);
   DecodeParams P{q_abs, static_cast<const uint8_t*>(cache->rows), cache->row_scale,
                  cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                  cache->page_size != 0, B, H, num_splits, HG64, chunk, cache->max_seq_len,
-                 scale * kLog2e, u_part, lse_part};
+                 q_len, scale * kLog2e, u_part, lse_part};
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
   if (fp8 && part_dt == MLA_F32)
     decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
@@ -1885,6 +1890,31 @@ extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void
   else
     decode_ws_kernel<false, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
   return launch_status();
+}
+
+extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
+                                   int32_t q_abs_dt, const float* q_abs_scale,
+                                   const mla_cache_t* cache, int32_t num_splits, void* u_part,
+                                   int32_t part_dt, float* lse_part, void* stream) {
+  mla_status_t st = check_decode(dims, B, q_abs, q_abs_dt, q_abs_scale, cache, num_splits,
+                                 u_part, part_dt, lse_part);
+  if (st != MLA_OK || B == 0) return st;
+  return decode_launch(dims, B, 1, q_abs, cache, num_splits, u_part, part_dt, lse_part,
+                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
+                                         const void* q_abs, int32_t q_abs_dt,
+                                         const mla_cache_t* cache, int32_t num_splits,
+                                         void* u_part, int32_t part_dt, float* lse_part,
+                                         void* stream) {
+  if (q_len < 1 || q_len > kMaxQueryTokens) return MLA_E_ARG;
+  mla_status_t st = check_decode(dims, B, q_abs, q_abs_dt, nullptr, cache, num_splits, u_part,
+                                 part_dt, lse_part);
+  if (st != MLA_OK || B == 0) return st;
+  if (static_cast<int64_t>(B) * q_len > 0x7FFFFFFF) return MLA_E_SHAPE;
+  return decode_launch(dims, B, q_len, q_abs, cache, num_splits, u_part, part_dt, lse_part,
+                       static_cast<hipStream_t>(stream));
 }
 
 extern "C" mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t num_splits,

@@ -230,3 +230,22 @@ def test_mha_decode_validation():
     assert mh(o_dt=FP8) == E_DTYPE
     assert mh(dt=7) == E_ARG
     assert mh(k=P + 2) == E_ALIGN
+
+
+def test_decode_multi_validation():
+    L = mla.lib()
+
+    def dm(B=2, ql=4, q=P, q_dt=BF16, c=None, S=4, u=P, u_dt=BF16, lse=P):
+        c = c if c is not None else cache()
+        return L.mla_decode_multi(C.byref(dims()), B, ql, q, q_dt, C.byref(c), S, u, u_dt, lse,
+                                  None)
+
+    assert dm(B=0, q=None, u=None, lse=None) == OK
+    assert dm(ql=0) == E_ARG
+    assert dm(ql=17) == E_ARG
+    assert dm(q=None) == E_ARG
+    assert dm(S=0) == E_ARG
+    assert dm(q_dt=F32) == E_DTYPE          # bf16 cache, fp32 queries
+    assert dm(u_dt=FP8) == E_DTYPE
+    assert dm(c=cache(dtype=FP8)) == E_ARG  # fp8 cache without row scales
+    assert dm(u=P + 4) == E_ALIGN
