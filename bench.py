@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-call-tail", action="store_true",
                     help="merge and up-project with mla_combine + mla_up_proj")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence (> 1: multi-token decode with "
+                         "mla_decode_multi; tokens/s counts every query token)")
     ap.add_argument("--mha", action="store_true",
                     help="the MHA baseline instead: per-head bf16 K/V cache at the geometry of "
                          "--workload (batch, heads, lengths; head dim 128), mla_mha_decode")
@@ -108,6 +111,77 @@ def record_traffic(d):
            "counters_from": os.path.relpath(os.path.abspath(d), ROOT)}
     json.dump(rec, open(PROFILE_TRAFFIC, "w"), indent=1)
     print(json.dumps(rec))
+
+
+def multi_token_bench(args, wl, dev, reps, R, S, act, part, out, cache_bytes):
+    """Multi-token decode step: mla_absorb_q over B*q_len query tokens ->
+    mla_decode_multi -> mla_combine_up_proj over B*q_len rows.  Synthetic
+    queries (seeded); the cache replicas of the plain bench."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_15_amd as mla
+
+    B, QL, H = wl.batch, args.q_len, wl.heads
+    g = torch.Generator(device="cuda").manual_seed(wl.seed + QL)
+    qn = torch.randn(B * QL, H, wl.d_nope, device="cuda", generator=g).to(act)
+    qr = torch.randn(B * QL, H, wl.d_rope, device="cuda", generator=g).to(act)
+    q_abs = torch.empty(B, QL, H, 576, dtype=act, device="cuda")
+    u_part = torch.empty(B, QL, S, H, wl.d_latent, dtype=part, device="cuda")
+    lse_part = torch.empty(B, QL, S, H, dtype=torch.float32, device="cuda")
+    o = torch.empty(B * QL, H, wl.d_v, dtype=out, device="cuda")
+    stream = torch.cuda.current_stream()
+    geo = dev.geo
+
+    stages = [
+        ("mla_absorb_q", lambda rp: mla.mla_absorb_q(geo, qn, qr, rp["w_uk"], q_abs.view(B * QL, H, 576),
+                                                     stream=stream)),
+        ("mla_decode_multi", lambda rp: mla.mla_decode_multi(geo, q_abs, rp["cache"], S, u_part,
+                                                             lse_part, stream=stream)),
+        ("mla_combine_up_proj", lambda rp: mla.mla_combine_up_proj(
+            geo, u_part.view(B * QL, S, H, wl.d_latent), lse_part.view(B * QL, S, H), rp["w_uv"], o,
+            stream=stream)),
+    ]
+
+    def one(i):
+        for _, fn in stages:
+            fn(reps[i % R])
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kernel_us = {}
+    for name, fn in stages:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(reps[i % R])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kernel_us[name] = e0.elapsed_time(e1) / args.steps * 1e3
+    t_dec = kernel_us["mla_decode_multi"] * 1e-6
+    flops = float(np.sum(np.asarray(dev.inp.seq_lens, np.float64))) * QL * 2 * H * 1088
+    rec = {
+        "metric": "MLA multi-token decode query tokens/s (q_len per sequence), 1 GPU",
+        "value": B * QL / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if wl.cache_dtype == "bf16" else wl.cache_dtype,
+        "data": "synthetic (seeded N(0,1) activations/cache, N(0,1/512) weights)",
+        "config": {"workload": wl.name, "batch": B, "q_len": QL, "heads": H, "splits": S,
+                   "seq_len": int(dev.inp.max_seq_len), "parallelism": "none (1 GPU)"},
+        "cache_GBps": cache_bytes / t_dec / 1e9,
+        "kernel_us_mean": kernel_us,
+        "roofline": {"kernel": "mla_decode_multi", "bound": "mfma", "achieved": flops / t_dec / 1e12,
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": flops / t_dec / 1e12 / 2500.0,
+                     "traffic": None, "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def mha_baseline(args):
@@ -261,6 +335,9 @@ def main():
     act = torch.float32 if wl.cache_dtype == "f32" else torch.bfloat16
     part = torch.float32 if args.part_dtype == "f32" else act
     out = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    QL = args.q_len
+    if QL > 1:
+        return multi_token_bench(args, wl, dev, reps, R, S, act, part, out, cache_bytes)
     step = mla.DecodeStep(dev.geo, wl.batch, S, act_dtype=act, part_dtype=part, out_dtype=out)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
