@@ -29,8 +29,11 @@
  * The step is four calls, each only enqueued on the caller's HIP stream:
  *     mla_absorb_q  ->  mla_decode  ->  mla_combine  ->  mla_up_proj
  * (mla_combine_up_proj does the last two in one launch for bf16 W_UV).
- * mla_cache_append writes each sequence's new token into the cache before the
- * step.
+ * Around the step: mla_cache_append writes each sequence's new token into the
+ * cache before it; mla_absorb_q_rope is mla_absorb_q with the decoupled RoPE
+ * of q_R applied; mla_decode_multi takes several query tokens per sequence
+ * (causal among them); mla_mha_decode is the multi-head attention baseline
+ * over a full per-head K/V cache, the cache MLA replaces.
  * mla_decode splits every sequence into num_splits token ranges and writes one
  * normalised partial result per range; mla_combine merges them exactly with
  * log-sum-exp weights; with num_splits == 1 the partial already is the final
