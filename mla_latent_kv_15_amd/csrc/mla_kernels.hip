@@ -1357,13 +1357,16 @@ constexpr int kCuBatch = 4;                // splits per batch of partial loads
 template <int PART_DT, int O_DT>
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     const void* u_part, const float* lse_part, const uint16_t* w_uv, void* o, uint16_t* u_out,
-    float* lse_out, int B, int H, int S, int d_v) {
+    float* lse_out, int B, int H, int S, int d_v, int rows) {
   // u rows (bf16), then the per-group fp32 sums of the phase reduction
   __shared__ __attribute__((aligned(16))) uint8_t us[kCuRows * kCuRow + kCuRows * 32 * 64];
-  const int nbt = (B + kCuRows - 1) / kCuRows;
+  // `rows` (a power of two <= 16) consecutive sequences of one head per
+  // workgroup: fewer than 16 when the batch is small, so the grid still
+  // covers the CUs
+  const int nbt = (B + rows - 1) / rows;
   const int wid = xcd_remap(blockIdx.x, H * nbt);
   const int h = wid / nbt;  // the sequence tiles of one head share W_UV[h] in L2
-  const int b0 = (wid % nbt) * kCuRows;
+  const int b0 = (wid % nbt) * rows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
   const int nnb = d_v / 16;  // value blocks of 16 rows
@@ -1375,7 +1378,7 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   // and every nph-th split from ph = g / nrows, so small batches still keep
   // all 512 threads' loads in flight; the groups of a sequence are summed in
   // LDS afterwards, in phase order.
-  const int nrows = min(kCuRows, B - b0);  // >= 1
+  const int nrows = min(rows, B - b0);  // >= 1
   const int nph = kCuRows / nrows;         // split phases per sequence
   const int grp = tid >> 5, cg = tid & 31;
   const int r = grp % nrows, ph = grp / nrows;
@@ -1541,12 +1544,14 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 64 * ks);
       d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wk[ks], d, 0, 0, 0);
     }
-    // D: column n16 = value row 16 nb + n16, rows 4 kg + i = sequences
+    // D: column n16 = value row 16 nb + n16, rows 4 kg + i = sequences (only
+    // the workgroup's own nrows are stored)
     const int v = 16 * nb + n16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int bb = b0 + 4 * kg + i;
-      if (bb < B) store_elem<O_DT>(o, (static_cast<int64_t>(bb) * H + h) * d_v + v, d[i]);
+      const int rr = 4 * kg + i;
+      if (rr < nrows)
+        store_elem<O_DT>(o, (static_cast<int64_t>(b0 + rr) * H + h) * d_v + v, d[i]);
     }
   }
 }
@@ -1985,7 +1990,11 @@ extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, i
   if (st != MLA_OK || B == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int H = dims->heads;
-  const int64_t nblk = static_cast<int64_t>(H) * ((B + kCuRows - 1) / kCuRows);
+  // sequences per workgroup: 16, halved while the grid would not cover the
+  // 256 CUs (small batches)
+  int rows = kCuRows;
+  while (rows > 1 && static_cast<int64_t>(H) * ((B + rows - 1) / rows) < 256) rows >>= 1;
+  const int64_t nblk = static_cast<int64_t>(H) * ((B + rows - 1) / rows);
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid = static_cast<unsigned>(nblk);
   uint16_t* ub = static_cast<uint16_t*>(u);
@@ -1993,7 +2002,7 @@ extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, i
 #define MLA_CU(PD, OD)                                                                          \
   if (part_dt == PD && o_dt == OD) {                                                            \
     combine_up_kernel<PD, OD><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, B, H, \
-                                                          num_splits, dims->d_v);               \
+                                                          num_splits, dims->d_v, rows);         \
     return launch_status();                                                                     \
   }
   MLA_CU(MLA_BF16, MLA_BF16)
