@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default="dsv2_b32_l2k")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--decode-kernel", default="auto", choices=["auto", "h64", "h128"],
+                    help="decode work decomposition (mla_decode_ex); auto = mla_decode's choice")
     ap.add_argument("--replica-bytes", type=float, default=1.25 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-call-tail", action="store_true",
@@ -346,12 +348,17 @@ def main():
     # W_UV product run as one launch (mla_combine_up_proj; u is not stored)
     fused = step.fused_tail(dev.w_uv) and not args.two_call_tail
 
+    kernel = {"auto": mla.KERNEL_AUTO, "h64": mla.KERNEL_H64, "h128": mla.KERNEL_H128}[args.decode_kernel]
+
+    def decode(rp):
+        mla.mla_decode_ex(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
+                          kernel=kernel, stream=stream)
+
     def one(i):
         rp = reps[i % R]
         mla.mla_absorb_q(step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs,
                          stream=stream)
-        mla.mla_decode(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
-                       stream=stream)
+        decode(rp)
         if fused:
             mla.mla_combine_up_proj(step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o,
                                     stream=stream)
@@ -389,8 +396,7 @@ def main():
 
     stages = [("mla_absorb_q", lambda rp: mla.mla_absorb_q(
                   step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs, stream=stream)),
-              ("mla_decode", lambda rp: mla.mla_decode(
-                  step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part, stream=stream))]
+              ("mla_decode", decode)]
     if fused:
         stages.append(("mla_combine_up_proj", lambda rp: mla.mla_combine_up_proj(
             step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o, stream=stream)))
@@ -458,7 +464,8 @@ def main():
                    "d_nope": wl.d_nope, "d_rope": wl.d_rope, "d_latent": wl.d_latent,
                    "d_v": wl.d_v, "seq_len": int(inp.max_seq_len), "splits": S,
                    "cache": f"{wl.cache_dtype} {'paged' if wl.page_size else 'contiguous'}",
-                   "partials": args.part_dtype, "replicas": R, "parallelism": "none (1 GPU)"},
+                   "partials": args.part_dtype, "decode_kernel": args.decode_kernel,
+                   "replicas": R, "parallelism": "none (1 GPU)"},
         "cache_GBps": cache_bytes / t_decode / 1e9,
         "cache_pct_hbm_peak": 100.0 * cache_bytes / t_decode / 1e9 / HBM_PEAK_GBPS,
         "kernel_us_mean": kernel_us,

@@ -190,6 +190,30 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
                               int32_t num_splits, void* u_part, int32_t part_dt,
                               float* lse_part, void* stream);
 
+/* Decode kernels (the work decomposition of the BF16-cache decode; the result
+ * is the same up to rounding order):
+ *   MLA_KERNEL_H64  -- one workgroup per (sequence, split range, 64 heads);
+ *                      two workgroups share each cached tile through L2.
+ *                      Every cache dtype.
+ *   MLA_KERNEL_H128 -- one workgroup per (sequence, split range, 128 heads):
+ *                      each tile enters one CU once for all of its heads.
+ *                      BF16 cache, h a multiple of 128.
+ *   MLA_KERNEL_AUTO -- what mla_decode and mla_decode_multi use: H64, which
+ *                      measured as fast or faster than H128 on every bf16
+ *                      workload and split count tried (H128 runs one wave per
+ *                      SIMD, which leaves the matrix cores idle while a wave
+ *                      waits on LDS, the tile DMA or its softmax). */
+typedef enum { MLA_KERNEL_AUTO = 0, MLA_KERNEL_H64 = 1, MLA_KERNEL_H128 = 2 } mla_decode_kernel_t;
+
+/* mla_decode_multi with the decode kernel chosen by the caller (`kernel`, an
+ * mla_decode_kernel_t).  q_len = 1 is mla_decode.  MLA_KERNEL_H128 for a cache
+ * or head count it does not cover returns MLA_E_UNSUPPORTED; an unknown
+ * value MLA_E_ARG.  Other arguments, layouts and errors as mla_decode_multi. */
+mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t B, int32_t q_len, const void* q_abs,
+                           int32_t q_abs_dt, const mla_cache_t* cache, int32_t num_splits,
+                           void* u_part, int32_t part_dt, float* lse_part, int32_t kernel,
+                           void* stream);
+
 /* Merge the split partials of mla_decode with log-sum-exp weights:
  *   lse[b][i] = ln sum_p e^{lse_part[b][p][i]}
  *   u[b][i][:] = sum_p e^{lse_part[b][p][i] - lse[b][i]} * u_part[b][p][i][:]

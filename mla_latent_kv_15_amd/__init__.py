@@ -65,6 +65,9 @@ def lib():
         L.mla_decode.restype = C.c_int
         L.mla_decode.argtypes = [C.POINTER(Dims), i32, vp, i32, f32p, C.POINTER(CacheDesc), i32,
                                  vp, i32, f32p, vp]
+        L.mla_decode_ex.restype = C.c_int
+        L.mla_decode_ex.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, C.POINTER(CacheDesc), i32,
+                                    vp, i32, f32p, i32, vp]
         L.mla_decode_multi.restype = C.c_int
         L.mla_decode_multi.argtypes = [C.POINTER(Dims), i32, i32, vp, i32, C.POINTER(CacheDesc),
                                        i32, vp, i32, f32p, vp]
@@ -92,7 +95,7 @@ def lib():
     return _lib
 
 
-EXPORTED = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
+EXPORTED = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_decode_ex", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
             "mla_absorb_q_rope", "mla_cache_append", "mla_mha_decode", "mla_status_str",
             "mla_version")
 
@@ -245,6 +248,24 @@ def mla_decode_multi(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_split
     _check("mla_decode_multi", st)
 
 
+KERNEL_AUTO, KERNEL_H64, KERNEL_H128 = 0, 1, 2  # mla_decode_kernel_t
+
+
+def mla_decode_ex(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int,
+                  u_part: torch.Tensor, lse_part: torch.Tensor, kernel: int = KERNEL_AUTO,
+                  stream=None) -> None:
+    """mla_decode (q_abs [B, h, 576]) or mla_decode_multi (q_abs [B, q_len, h,
+    576]) with the decode kernel chosen by the caller (KERNEL_*)."""
+    B = int(q_abs.shape[0])
+    QL = int(q_abs.shape[1]) if q_abs.dim() == 4 else 1
+    d = geo.c()
+    cd = cache.c()
+    st = lib().mla_decode_ex(C.byref(d), B, QL, _ptr(q_abs), dtype_code(q_abs), C.byref(cd),
+                             int(num_splits), _ptr(u_part), dtype_code(u_part), _ptr(lse_part),
+                             int(kernel), _stream(stream))
+    _check("mla_decode_ex", st)
+
+
 def mla_combine(geo: Geometry, u_part: torch.Tensor, lse_part: torch.Tensor, u: torch.Tensor,
                 lse: Optional[torch.Tensor] = None, stream=None) -> None:
     B, S = int(u_part.shape[0]), int(u_part.shape[1])
@@ -293,8 +314,10 @@ class DecodeStep:
     act_dtype is the dtype of q_abs / u; part_dtype of the split partials."""
 
     def __init__(self, geo: Geometry, batch: int, num_splits: int, device="cuda",
-                 act_dtype=torch.bfloat16, part_dtype=torch.bfloat16, out_dtype=torch.bfloat16):
+                 act_dtype=torch.bfloat16, part_dtype=torch.bfloat16, out_dtype=torch.bfloat16,
+                 kernel: int = KERNEL_AUTO):
         self.geo = geo
+        self.kernel = int(kernel)
         self.B = batch
         self.S = int(num_splits)
         h = geo.heads
@@ -317,7 +340,11 @@ class DecodeStep:
     def run(self, q_nope, q_rope, w_uk, w_uv, cache: Cache, stream=None,
             fused: bool = True) -> torch.Tensor:
         mla_absorb_q(self.geo, q_nope, q_rope, w_uk, self.q_abs, stream=stream)
-        mla_decode(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part, stream=stream)
+        if self.kernel == KERNEL_AUTO:
+            mla_decode(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part, stream=stream)
+        else:
+            mla_decode_ex(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part,
+                          kernel=self.kernel, stream=stream)
         if fused and self.fused_tail(w_uv):
             mla_combine_up_proj(self.geo, self.u_part, self.lse_part, w_uv, self.o, self.u,
                                 self.lse, stream=stream)

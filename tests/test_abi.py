@@ -249,3 +249,23 @@ def test_decode_multi_validation():
     assert dm(u_dt=FP8) == E_DTYPE
     assert dm(c=cache(dtype=FP8)) == E_ARG  # fp8 cache without row scales
     assert dm(u=P + 4) == E_ALIGN
+
+
+def test_decode_ex_kernel_choice_validation():
+    """mla_decode_ex: the kernel argument is checked on the host before any
+    launch; the 128-head kernel covers bf16 caches with h a multiple of 128."""
+    L = mla.lib()
+
+    def dx(kernel, h=128, c=None, B=2, ql=1):
+        c = c if c is not None else cache()
+        return L.mla_decode_ex(C.byref(dims(h=h)), B, ql, P, BF16, C.byref(c), 4, P, BF16, P,
+                               kernel, None)
+
+    assert dx(mla.KERNEL_H128, B=0) == OK
+    assert dx(3) == E_ARG
+    assert dx(-1) == E_ARG
+    assert dx(mla.KERNEL_H128, h=64) == E_UNSUP
+    assert dx(mla.KERNEL_H128, h=160) == E_UNSUP
+    assert dx(mla.KERNEL_H128, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP
+    assert dx(mla.KERNEL_H64, ql=0) == E_ARG
+    assert dx(mla.KERNEL_H64, ql=17) == E_ARG

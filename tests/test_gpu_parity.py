@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import mla_latent_kv_15_amd as mla
 import oracle
 import synth
 from tests.mla_cases import (TOL, DeviceInputs, check_against_oracle, run_step, sample_pairs)
@@ -46,27 +47,35 @@ def test_tiny_f32_every_output(splits):
 RAGGED = [0, 1, 31, 32, 45, 300, 257]
 
 
-@pytest.mark.parametrize("heads", [32, 128, 160])
+H64, H128 = mla.KERNEL_H64, mla.KERNEL_H128
+
+
+@pytest.mark.parametrize("heads,kernel", [(32, H64), (128, H64), (128, H128), (160, H64),
+                                          (256, H64), (256, H128)])
 @pytest.mark.parametrize("splits", [1, 3, 7])
-def test_ragged_bf16(heads, splits):
-    """bf16, several tiles plus ragged tails, empty and 1-token sequences, a
-    partial head group (160 = 128 + 32) and waves without heads (32)."""
+def test_ragged_bf16(heads, kernel, splits):
+    """bf16, several tiles plus ragged tails, empty and 1-token sequences, on
+    both decode kernels: a partial head group (160 = 128 + 32), waves without
+    heads (32), two head groups of either kernel (256)."""
     wl = synth.workload("dsv2_b32_l2k").with_(batch=len(RAGGED), heads=heads, seq_len=None,
                                              seed=synth.workloads.BASE_SEED + 101)
     dev = DeviceInputs(synth.make_inputs(wl, lengths=RAGGED))
-    step = run_step(dev, splits)
+    _log(f"ragged h={heads} kernel={kernel} S={splits}")
+    step = run_step(dev, splits, kernel=kernel)
     pairs = [(b, h) for b in range(wl.batch) for h in sorted({0, 1, heads // 2, heads - 1})]
     e = check_against_oracle(dev, step, pairs, TOL["bf16"])
-    _log(f"ragged h={heads} S={splits}: err o/u/lse = {e}")
+    _log(f"  err o/u/lse = {e}")
 
 
+@pytest.mark.parametrize("kernel", [H64, H128])
 @pytest.mark.parametrize("part", ["f32", "bf16"])
-def test_ragged_fp32_partials(part):
+def test_ragged_fp32_partials(part, kernel):
     """The same bf16 problem with fp32 or bf16 split partials."""
     wl = synth.workload("dsv2_b32_l2k").with_(batch=len(RAGGED), seq_len=None,
                                              seed=synth.workloads.BASE_SEED + 102)
     dev = DeviceInputs(synth.make_inputs(wl, lengths=RAGGED))
-    step = run_step(dev, 5, part_dtype=torch.float32 if part == "f32" else torch.bfloat16)
+    step = run_step(dev, 5, part_dtype=torch.float32 if part == "f32" else torch.bfloat16,
+                    kernel=kernel)
     pairs = [(b, h) for b in range(wl.batch) for h in (0, 77, 127)]
     check_against_oracle(dev, step, pairs, TOL["bf16"])
 
@@ -129,7 +138,8 @@ def test_paged_matches_contiguous_bitwise():
     check_against_oracle(paged, a, pairs, TOL["bf16"])
 
 
-def test_split_count_invariance():
+@pytest.mark.parametrize("kernel", [H64, H128])
+def test_split_count_invariance(kernel):
     """Different split counts give the same result.  With a zero query every
     score is 0, so every probability is exactly 1 in bf16 and u is the plain
     mean of the cached latents: split ranges may only change the fp32
@@ -141,7 +151,7 @@ def test_split_count_invariance():
     dev.q_nope.zero_()
     dev.q_rope.zero_()
     f32 = torch.float32
-    ref = run_step(dev, 1, part_dtype=f32, out_dtype=f32)
+    ref = run_step(dev, 1, part_dtype=f32, out_dtype=f32, kernel=kernel)
     ref_u = ref.u.clone()
     # u equals the column mean of the cached latents
     rows = dev.cache.rows.float()
@@ -149,9 +159,9 @@ def test_split_count_invariance():
         mean = rows[b * dev.cache.seq_stride: b * dev.cache.seq_stride + L, :512].mean(0)
         assert (ref_u[b] - mean).abs().max().item() < 1e-5
     for s in (2, 3, 7, 32):
-        got = run_step(dev, s, part_dtype=f32, out_dtype=f32).u
+        got = run_step(dev, s, part_dtype=f32, out_dtype=f32, kernel=kernel).u
         err = (got - ref_u).abs().max().item()
-        _log(f"split invariance S={s}: {err:.2e}")
+        _log(f"split invariance kernel={kernel} S={s}: {err:.2e}")
         assert err < 1e-5, (s, err)
 
 
@@ -181,24 +191,27 @@ def test_repeat_is_deterministic():
 
 # ---------------------------------------------------------------- full sizes
 
+AUTO = mla.KERNEL_AUTO
 FULL = [
-    ("dsv2_b32_l2k", "bf16", 4, 4),
-    ("long_b4_l32k", "bf16", 4, 3),
-    ("paged_b64_ragged", "bf16", 4, 3),
-    ("fp8_b1_l128k", "fp8", 1, 4),
-    ("fp8_b8_l128k", "fp8", 2, 2),
+    ("dsv2_b32_l2k", "bf16", 4, 4, AUTO),
+    ("dsv2_b32_l2k", "bf16", 4, 4, H128),
+    ("long_b4_l32k", "bf16", 4, 3, AUTO),
+    ("long_b4_l32k", "bf16", 4, 3, H64),
+    ("paged_b64_ragged", "bf16", 4, 3, AUTO),
+    ("fp8_b1_l128k", "fp8", 1, 4, AUTO),
+    ("fp8_b8_l128k", "fp8", 2, 2, AUTO),
 ]
 
 
-@pytest.mark.parametrize("name,kind,nb,nh", FULL)
-def test_full_size_sampled(name, kind, nb, nh):
+@pytest.mark.parametrize("name,kind,nb,nh,kernel", FULL)
+def test_full_size_sampled(name, kind, nb, nh, kernel):
     """Each workload at its full size with its stated split count, checked on a
     spread of (b, h) pairs that the oracle computes one by one."""
     wl = synth.workload(name)
     _log(f"{name}: generating inputs")
     dev = DeviceInputs(synth.make_inputs(wl))
-    _log(f"{name}: running S={wl.num_splits}")
-    step = run_step(dev, wl.num_splits)
+    _log(f"{name}: running S={wl.num_splits} kernel={kernel}")
+    step = run_step(dev, wl.num_splits, kernel=kernel)
     pairs = sample_pairs(wl.batch, wl.heads, nb, nh)
     e = check_against_oracle(dev, step, pairs, TOL[kind])
     _log(f"{name}: err o/u/lse = {e}")
