@@ -301,7 +301,7 @@ def main():
 
     import mla_latent_kv_15_amd as mla
     import synth
-    from tests.mla_cases import DeviceInputs
+    from tests.device_inputs import DeviceInputs
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
