@@ -30,12 +30,13 @@ def _bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-CASES = [("dsv2_b32_l2k", 2, 3), ("dsv2_b32_l2k", 4, 1), ("paged_b64_ragged", 3, 4),
-         ("fp8_b1_l128k", 4, 3)]
+AUTO, H128 = mla.KERNEL_AUTO, mla.KERNEL_H128
+CASES = [("dsv2_b32_l2k", 2, 3, AUTO), ("dsv2_b32_l2k", 4, 1, AUTO), ("paged_b64_ragged", 3, 4, AUTO),
+         ("fp8_b1_l128k", 4, 3, AUTO), ("dsv2_b32_l2k", 2, 3, H128), ("paged_b64_ragged", 3, 4, H128)]
 
 
-@pytest.mark.parametrize("name,ql,S", CASES)
-def test_multi_token_decode_matches_oracle(name, ql, S):
+@pytest.mark.parametrize("name,ql,S,kernel", CASES)
+def test_multi_token_decode_matches_oracle(name, ql, S, kernel):
     lens = np.array([300, 2, 64, 97, 1], np.int32)  # lengths below q_len: early queries see nothing
     B = len(lens)
     wl = synth.workload(name).with_(batch=B, seq_len=None, num_splits=S,
@@ -51,8 +52,11 @@ def test_multi_token_decode_matches_oracle(name, ql, S):
                      dev.w_uk, q_abs.view(B * ql, H, 576))
     u_part = torch.empty(B, ql, S, H, 512, dtype=torch.bfloat16, device="cuda")
     lse_part = torch.empty(B, ql, S, H, dtype=torch.float32, device="cuda")
-    _log(f"multi-token {name} q_len={ql} S={S}")
-    mla.mla_decode_multi(dev.geo, q_abs, dev.cache, S, u_part, lse_part)
+    _log(f"multi-token {name} q_len={ql} S={S} kernel={kernel}")
+    if kernel == AUTO:
+        mla.mla_decode_multi(dev.geo, q_abs, dev.cache, S, u_part, lse_part)
+    else:
+        mla.mla_decode_ex(dev.geo, q_abs, dev.cache, S, u_part, lse_part, kernel=kernel)
     o = torch.empty(B * ql, H, wl.d_v, dtype=torch.bfloat16, device="cuda")
     u = torch.empty(B * ql, H, 512, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B * ql, H, dtype=torch.float32, device="cuda")

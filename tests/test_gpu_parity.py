@@ -122,15 +122,16 @@ def test_fp8_codes_exact():
         assert np.array_equal(got, np.broadcast_to(want[b], got.shape)), b
 
 
-def test_paged_matches_contiguous_bitwise():
+@pytest.mark.parametrize("kernel", [H64, H128])
+def test_paged_matches_contiguous_bitwise(kernel):
     """The same tokens in a shuffled paged pool and in contiguous rows give
     bit-identical partials (the tiles see the same rows in the same order)."""
     base = synth.workload("paged_b64_ragged").with_(batch=6, seed=synth.workloads.BASE_SEED + 104)
     lens = [1, 64, 65, 700, 129, 0]
     paged = DeviceInputs(synth.make_inputs(base, lengths=lens))
     contig = DeviceInputs(synth.make_inputs(base.with_(page_size=0), lengths=lens))
-    a = run_step(paged, 3)
-    b = run_step(contig, 3)
+    a = run_step(paged, 3, kernel=kernel)
+    b = run_step(contig, 3, kernel=kernel)
     assert torch.equal(a.u_part.view(torch.int16), b.u_part.view(torch.int16))
     assert torch.equal(a.lse_part, b.lse_part)
     assert torch.equal(a.o.view(torch.int16), b.o.view(torch.int16))
