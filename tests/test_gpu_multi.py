@@ -32,7 +32,8 @@ def _bf16_dev(bits):
 
 AUTO, H128 = mla.KERNEL_AUTO, mla.KERNEL_H128
 CASES = [("dsv2_b32_l2k", 2, 3, AUTO), ("dsv2_b32_l2k", 4, 1, AUTO), ("paged_b64_ragged", 3, 4, AUTO),
-         ("fp8_b1_l128k", 4, 3, AUTO), ("dsv2_b32_l2k", 2, 3, H128), ("paged_b64_ragged", 3, 4, H128)]
+         ("fp8_b1_l128k", 4, 3, AUTO), ("dsv2_b32_l2k", 2, 3, H128), ("paged_b64_ragged", 3, 4, H128),
+         ("dsv2_b32_l2k", 16, 2, AUTO)]  # the largest q_len the ABI takes
 
 
 @pytest.mark.parametrize("name,ql,S,kernel", CASES)

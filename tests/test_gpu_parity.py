@@ -181,6 +181,22 @@ def test_split_count_random_inputs():
         assert err < 1e-2, (s, err)
 
 
+@pytest.mark.parametrize("kernel", [H64, H128])
+def test_max_splits(kernel):
+    """The largest split count the ABI takes (1024): 64-token ranges over a
+    40,000-token sequence, most ranges of the short and the empty sequence
+    empty, and the merge's path for more than 32 splits per sequence."""
+    lens = [40000, 33, 0]
+    wl = synth.workload("dsv2_b32_l2k").with_(batch=len(lens), seq_len=None,
+                                             seed=synth.workloads.BASE_SEED + 108)
+    dev = DeviceInputs(synth.make_inputs(wl, lengths=lens))
+    _log(f"max splits kernel={kernel}")
+    step = run_step(dev, 1024, kernel=kernel)
+    pairs = [(b, h) for b in range(len(lens)) for h in (0, 127)]
+    e = check_against_oracle(dev, step, pairs, TOL["bf16"])
+    _log(f"  err o/u/lse = {e}")
+
+
 def test_repeat_is_deterministic():
     wl = synth.workload("dsv2_b32_l2k").with_(batch=2, seq_len=333,
                                              seed=synth.workloads.BASE_SEED + 106)
