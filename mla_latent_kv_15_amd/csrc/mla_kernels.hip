@@ -1593,8 +1593,32 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
     for (int k = 0; k < kMaxDHead / 16; ++k)
       if (16 * k < d_nope) bq[k] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * k);
   };
+  // With d_nope <= 128 the W_UK rows fill half of the LDS buffer, and the
+  // query rows of a tile of 32 sequences (which all 4 waves multiply) are
+  // staged once in the other half instead of being loaded by every wave:
+  // thread tid moves 16-byte chunks tid and tid + 256 of the tile.
+  const bool q_lds = d_nope <= kMaxDHead / 2;  // workgroup-uniform
+  const int qcpr = d_nope / 8;                 // 16-byte chunks per query row
+  const int q_stride = 2 * d_nope + 16;        // padded LDS row
+  uint8_t* qs = wt + d_nope * kAbsRowBytes;
+  auto q_chunk = [&](int i, int b0) {  // i-th chunk of this thread: (row, column) of the tile
+    const int c = tid + i * kProjThreads;
+    const int row = c / qcpr, col = 8 * (c % qcpr);
+    const int b = b0 + row;
+    return *reinterpret_cast<const u32x4_t*>(q_nope + (static_cast<int64_t>(b < B ? b : 0) * H + h) * d_nope + col);
+  };
+  auto q_store = [&](int i, const u32x4_t& v) {
+    const int c = tid + i * kProjThreads;
+    if (c < 32 * qcpr) *reinterpret_cast<u32x4_t*>(qs + (c / qcpr) * q_stride + 16 * (c % qcpr)) = v;
+  };
   bf16x8_t bq[kMaxDHead / 16];
-  load_q(bq, 0);
+  u32x4_t qv[2];
+  if (q_lds) {
+    qv[0] = q_chunk(0, 0);
+    qv[1] = q_chunk(1, 0);
+  } else {
+    load_q(bq, 0);
+  }
   // RoPE rows: 8 chunks of 16 B per sequence
   const bool rope_copy = blockIdx.y == 0 && tid < B * (kDRope / 8);
   u32x4_t rv = u32x4_t{0u, 0u, 0u, 0u};
@@ -1607,13 +1631,33 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
     const int q = i * kProjThreads + tid;
     if (q < d_nope * 16) *reinterpret_cast<u32x4_t*>(wt + (q >> 4) * kAbsRowBytes + (q & 15) * 16) = st[i];
   }
+  if (q_lds) {
+    q_store(0, qv[0]);
+    q_store(1, qv[1]);
+  }
   __syncthreads();
   // A operand (M = c, K = n) by transposing reads: lane (G, e, q4) points at
   // row n0 + 8*(G/2) + e (+4), columns 32*wave + 16*(G%2) + 4*q4
   const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
   const uint8_t* abase = wt + (8 * (G >> 1) + e) * kAbsRowBytes + (32 * wave + 16 * (G & 1) + 4 * q4) * 2;
   for (int b0 = 0; b0 < B; b0 += 32) {
-    if (b0 > 0) load_q(bq, b0);
+    if (q_lds) {
+      if (b0 > 0) {  // the next tile of sequences replaces the staged rows
+        qv[0] = q_chunk(0, b0);
+        qv[1] = q_chunk(1, b0);
+        __syncthreads();
+        q_store(0, qv[0]);
+        q_store(1, qv[1]);
+        __syncthreads();
+      }
+      // B operand: lane (sequence bl, half g) reads elements 16k + 8g .. +7
+#pragma unroll
+      for (int k = 0; k < kMaxDHead / 16; ++k)
+        if (16 * k < d_nope)
+          bq[k] = *reinterpret_cast<const bf16x8_t*>(qs + bl * q_stride + 32 * k + 16 * g);
+    } else if (b0 > 0) {
+      load_q(bq, b0);
+    }
     const int b = b0 + bl;
     f32x16_t acc;
 #pragma unroll
