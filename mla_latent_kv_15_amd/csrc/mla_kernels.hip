@@ -466,7 +466,10 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
           softmax_publish(s, sc, i + 1, overflow, pbuf + ((i + 1) & 1) * kP64Bytes);
         }
       }
-      if (lane == 0) votes[wave] = __any(overflow) ? 1 : 0;
+      // the vote over all lanes, taken before the branch that stores it
+      // (inside `lane == 0` it would see lane 0's flag only)
+      const int vote = __any(overflow) ? 1 : 0;
+      if (lane == 0) votes[wave] = vote;
       barrier();  // V1
       int again = 0;
 #pragma unroll
@@ -1157,7 +1160,8 @@ void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier();  // every wave is done with the tile buffers
     int* votes = reinterpret_cast<int*>(smem);
-    if (lane == 0) votes[wave] = __any(overflow) ? 1 : 0;
+    const int vote = __any(overflow) ? 1 : 0;  // all lanes, outside the store's branch
+    if (lane == 0) votes[wave] = vote;
     barrier();
     int again = 0;
 #pragma unroll

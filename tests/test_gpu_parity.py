@@ -197,6 +197,45 @@ def test_max_splits(kernel):
     _log(f"  err o/u/lse = {e}")
 
 
+SPIKE_CASES = [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("fp8_b1_l128k", H64)]
+
+
+@pytest.mark.parametrize("name,kernel", SPIKE_CASES)
+def test_score_spike_recomputes_range(name, kernel):
+    """One late token whose RoPE key is 20 q_R of head 0: its score exceeds the
+    first tile's reference maximum by far more than the 2^64 slack, so the
+    range is computed a second time against its true maximum.  Head 0's output
+    is then (nearly) W_UV times that token's latent; every output against the
+    oracle."""
+    from synth.encode import bf16_bits_to_f32, f32_to_bf16_bits, quantize_rows_e4m3
+    lens = [700, 333]
+    # past the first tile of the range that holds them, in lanes other than
+    # lane 0 of the score layouts of both kernels
+    spike = [655, 205]
+    wl = synth.workload(name).with_(batch=len(lens), seq_len=None,
+                                    seed=synth.workloads.BASE_SEED + 109)
+    inp = synth.make_inputs(wl, lengths=lens)
+    qr0 = bf16_bits_to_f32(inp.q_rope[:, 0, :])  # [B, 64] query RoPE part of head 0
+    for b, t in enumerate(spike):
+        r = b * inp.seq_stride + t
+        if wl.cache_dtype == "fp8":
+            tbl = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+            row = tbl[inp.rows[r]] * inp.row_scale[r]
+            row[512:] = 20.0 * qr0[b]
+            codes, sc = quantize_rows_e4m3(row[None, :].astype(np.float32))
+            inp.rows[r], inp.row_scale[r] = codes[0], sc[0]
+        else:
+            inp.rows[r, 512:] = f32_to_bf16_bits(20.0 * qr0[b])
+    dev = DeviceInputs(inp)
+    _log(f"score spike {name} kernel={kernel}")
+    kind = "fp8" if wl.cache_dtype == "fp8" else "bf16"
+    for splits in (1, 3):
+        step = run_step(dev, splits, kernel=kernel)
+        pairs = [(b, h) for b in range(len(lens)) for h in (0, 1, 77, 127)]
+        e = check_against_oracle(dev, step, pairs, TOL[kind])
+        _log(f"  S={splits}: err o/u/lse = {e}")
+
+
 def test_repeat_is_deterministic():
     wl = synth.workload("dsv2_b32_l2k").with_(batch=2, seq_len=333,
                                              seed=synth.workloads.BASE_SEED + 106)
