@@ -83,6 +83,10 @@ __device__ inline int xcd_remap(int bid, int n) {
   return x * per + (x < rem ? x : rem) + k;
 }
 
+// maximum that keeps a NaN (fmaxf drops it): a NaN split log-sum-exp must make
+// the merged result NaN, not be skipped
+__device__ inline float max_nan(float a, float b) { return (a != a) ? a : ((b != b) ? b : fmaxf(a, b)); }
+
 // Physical row of the first token of a 32-token tile (tiles never straddle a
 // 64-row page because every split range starts at a multiple of 32).
 __device__ inline int64_t tile_row0(const int32_t* block_table, int32_t max_pages,
@@ -1381,13 +1385,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* u_par
     if (i < S) v[i] = load_part<PART_DT>(u_part, part_at(i));
   // log-sum-exp weights (parts with lse = -inf carry no weight)
   float mx = -INFINITY;
-  for (int p = lane; p < S; p += 64) mx = fmaxf(mx, lse_at(p));
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  for (int p = lane; p < S; p += 64) mx = max_nan(mx, lse_at(p));
+  for (int o = 32; o > 0; o >>= 1) mx = max_nan(mx, __shfl_xor(mx, o));
   float z = 0.0f;
   if (mx != -INFINITY)
     for (int p = lane; p < S; p += 64) z += expf(lse_at(p) - mx);
   for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
-  const float inv = (z > 0.0f) ? 1.0f / z : 0.0f;
+  const bool live = z > 0.0f || z != z;  // not every range empty (a NaN sum stays NaN)
+  const float inv = live ? 1.0f / z : 0.0f;
   float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   for (int p0 = 0; p0 < S; p0 += kG) {
     // weight of partial p0 + i sits in lane i; empty ranges hold u = 0
@@ -1417,7 +1422,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* u_par
       w[k] = pack_bf16x2(a[2 * k] * inv, a[2 * k + 1] * inv);
     *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(u) + ob) = w;
   }
-  if (lse && lane == 0) lse[static_cast<int64_t>(b) * H + h] = (z > 0.0f) ? mx + logf(z) : -INFINITY;
+  if (lse && lane == 0) lse[static_cast<int64_t>(b) * H + h] = live ? mx + logf(z) : -INFINITY;
 }
 
 // ================================================================ decoupled RoPE
@@ -1919,17 +1924,17 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     mx = lse_l;
     last = lse_l != -INFINITY ? cg : -1;
 #pragma unroll
-    for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+    for (int o2 = 1; o2 < 32; o2 <<= 1) mx = max_nan(mx, __shfl_xor(mx, o2));
     e_l = (mx != -INFINITY) ? expf(lse_l - mx) : 0.0f;
     z = e_l;
   } else {
     for (int p = cg; p < S; p += 32) {
       const float x = lse_part[prow + static_cast<int64_t>(p) * H];
-      mx = fmaxf(mx, x);
+      mx = max_nan(mx, x);
       last = x != -INFINITY ? p : last;
     }
 #pragma unroll
-    for (int o2 = 1; o2 < 32; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+    for (int o2 = 1; o2 < 32; o2 <<= 1) mx = max_nan(mx, __shfl_xor(mx, o2));
     if (mx != -INFINITY)
       for (int p = cg; p < S; p += 32) z += expf(lse_part[prow + static_cast<int64_t>(p) * H] - mx);
   }
@@ -1938,7 +1943,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     z += __shfl_xor(z, o2);
     last = max(last, __shfl_xor(last, o2));
   }
-  const float inv = (z > 0.0f) ? 1.0f / z : 0.0f;
+  const bool live = z > 0.0f || z != z;  // not every range empty (a NaN sum stays NaN)
+  const float inv = live ? 1.0f / z : 0.0f;
   // Splits past the last finite log-sum-exp are empty ranges (the trailing
   // ranges of a short sequence): weight 0, so their partials are not read.
   ns = min(ns, ph <= last ? (last - ph) / nph + 1 : 0);
@@ -2011,7 +2017,7 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
       *reinterpret_cast<u32x4_t*>(dst) = u0;
       *reinterpret_cast<u32x4_t*>(dst + 8) = u1;
     }
-    if (lse_out && cg == 0) lse_out[static_cast<int64_t>(b) * H + h] = (z > 0.0f) ? mx + logf(z) : -INFINITY;
+    if (lse_out && cg == 0) lse_out[static_cast<int64_t>(b) * H + h] = live ? mx + logf(z) : -INFINITY;
   }
   __syncthreads();
 

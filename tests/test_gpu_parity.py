@@ -236,6 +236,54 @@ def test_score_spike_recomputes_range(name, kernel):
         _log(f"  S={splits}: err o/u/lse = {e}")
 
 
+@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128),
+                                         ("tiny_f32", H64)])
+def test_custom_softmax_scale(name, kernel):
+    """A caller-given softmax scale (0.05) replaces 1/sqrt(d_nope + d_rope)."""
+    wl = synth.workload(name).with_(batch=3, seq_len=None, seed=synth.workloads.BASE_SEED + 110)
+    dev = DeviceInputs(synth.make_inputs(wl, lengths=[300, 1, 97]))
+    dev.geo.softmax_scale = 0.05
+    step = run_step(dev, 3, kernel=kernel)
+    pairs = [(b, h) for b in range(3) for h in (0, wl.heads - 1)]
+    o_ref, lse_ref, u_ref = oracle.decode_inputs(dev.inp, sel=pairs, want_u=True, scale=0.05)
+    kind = "f32" if wl.cache_dtype == "f32" else "bf16"
+    o = step.o.float().cpu().numpy()
+    lse = step.lse.float().cpu().numpy()
+    got = np.stack([o[b, h] for b, h in pairs])
+    assert np.abs(got - o_ref).max() <= TOL[kind] * np.abs(o_ref).max()
+    assert np.abs(np.array([lse[b, h] for b, h in pairs]) - lse_ref).max() <= TOL[kind]
+
+
+@pytest.mark.parametrize("kernel", [H64, H128])
+def test_nan_in_a_read_row_propagates(kernel):
+    """A NaN in a cached row that is attended makes every output of that
+    sequence NaN (o, u, lse), with one range or several; the other sequence is
+    unaffected."""
+    lens = [300, 97]
+    wl = synth.workload("dsv2_b32_l2k").with_(batch=2, seq_len=None,
+                                             seed=synth.workloads.BASE_SEED + 111)
+    inp = synth.make_inputs(wl, lengths=lens)
+    inp.rows[150, 3] = 0x7FC0  # sequence 0, token 150, latent element 3
+    dev = DeviceInputs(inp)
+    for splits in (1, 3):
+        step = run_step(dev, splits, kernel=kernel)
+        o = step.o.float().cpu().numpy()
+        u = step.u.float().cpu().numpy()
+        lse = step.lse.float().cpu().numpy()
+        _log(f"nan row kernel={kernel} S={splits}: nan o/u/lse in seq 0: "
+             f"{np.isnan(o[0]).mean():.2f} {np.isnan(u[0]).mean():.2f} {np.isnan(lse[0]).mean():.2f}")
+        assert np.isnan(o[0]).all() and np.isnan(u[0]).all() and np.isnan(lse[0]).all()
+        if splits > 1:  # the two-call tail (mla_combine, then mla_up_proj) as well
+            step.run(dev.q_nope, dev.q_rope, dev.w_uk, dev.w_uv, dev.cache, fused=False)
+            torch.cuda.synchronize()
+            assert torch.isnan(step.o[0]).all() and torch.isnan(step.u[0].float()).all()
+            assert torch.isnan(step.lse[0]).all()
+        pairs = [(1, h) for h in (0, 77, 127)]
+        o_ref, _, _ = oracle.decode_inputs(dev.inp, sel=pairs)
+        got = np.stack([o[b, h] for b, h in pairs])
+        assert np.abs(got - o_ref).max() <= TOL["bf16"] * np.abs(o_ref).max()
+
+
 def test_repeat_is_deterministic():
     wl = synth.workload("dsv2_b32_l2k").with_(batch=2, seq_len=333,
                                              seed=synth.workloads.BASE_SEED + 106)
