@@ -284,6 +284,23 @@ def test_nan_in_a_read_row_propagates(kernel):
         assert np.abs(got - o_ref).max() <= TOL["bf16"] * np.abs(o_ref).max()
 
 
+@pytest.mark.parametrize("kernel", [H64, H128])
+def test_large_batch_of_short_sequences(kernel):
+    """300 sequences of 0-120 tokens: many 32-sequence tiles in the absorb (the
+    staged query rows are replaced tile after tile), many merge workgroups,
+    empty and one-token sequences among them."""
+    r = np.random.default_rng(112)
+    lens = r.integers(0, 121, 300).tolist()
+    lens[7], lens[8] = 0, 1
+    wl = synth.workload("dsv2_b32_l2k").with_(batch=len(lens), seq_len=None,
+                                             seed=synth.workloads.BASE_SEED + 112)
+    dev = DeviceInputs(synth.make_inputs(wl, lengths=lens))
+    step = run_step(dev, 2, kernel=kernel)
+    pairs = [(b, h) for b in (0, 7, 8, 31, 32, 33, 150, 255, 256, 299) for h in (0, 127)]
+    e = check_against_oracle(dev, step, pairs, TOL["bf16"])
+    _log(f"large batch kernel={kernel}: err o/u/lse = {e}")
+
+
 def test_repeat_is_deterministic():
     wl = synth.workload("dsv2_b32_l2k").with_(batch=2, seq_len=333,
                                              seed=synth.workloads.BASE_SEED + 106)
