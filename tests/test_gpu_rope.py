@@ -93,3 +93,45 @@ def test_decode_with_rotated_query(name):
     e = rel_err(np.stack([o[b, h] for b, h in pairs]), o_ref)
     _log(f"  o err {e:.2e}")
     assert e <= TOL["fp8" if wl.cache_dtype == "fp8" else "bf16"]
+
+
+F32, BF16 = "f32", "bf16"
+ABSORB_DTYPES = [(F32, F32, F32), (F32, F32, BF16), (BF16, BF16, BF16), (BF16, BF16, F32),
+                 (F32, BF16, BF16), (BF16, F32, BF16)]
+
+
+@pytest.mark.parametrize("q_dt,w_dt,out_dt", ABSORB_DTYPES)
+def test_absorb_dtypes_match_oracle(q_dt, w_dt, out_dt):
+    """mla_absorb_q for every provided (query, weight, output) dtype triple
+    against the oracle's absorbed query (float64 over the same stored bits):
+    the matrix-core kernel for bf16/bf16 and the VALU kernel for the rest, 37
+    sequences (more than one tile of 32)."""
+    from synth.encode import f32_to_bf16_bits
+    B, H, dn = 37, 128, 128
+    r = np.random.default_rng(140)
+    qn = r.standard_normal((B, H, dn)).astype(np.float32)
+    qr = r.standard_normal((B, H, 64)).astype(np.float32)
+    wk = (r.standard_normal((H, dn, 512)) / np.sqrt(512)).astype(np.float32)
+
+    def stored(x, dt):  # the bits both sides read
+        return f32_to_bf16_bits(x) if dt == BF16 else x
+
+    def dev(x, dt):
+        if dt == BF16:
+            return torch.from_numpy(stored(x, dt).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    geo = mla.Geometry(heads=H)
+    q_abs = torch.empty(B, H, 576, dtype=torch.float32 if out_dt == F32 else torch.bfloat16,
+                        device="cuda")
+    _log(f"absorb q={q_dt} w={w_dt} out={out_dt}")
+    mla.mla_absorb_q(geo, dev(qn, q_dt), dev(qr, q_dt), dev(wk, w_dt), q_abs)
+    torch.cuda.synchronize()
+    want = oracle.absorb_q(stored(qn, q_dt), stored(qr, q_dt), q_dt, stored(wk, w_dt), w_dt)
+    got = q_abs.float().cpu().numpy().astype(np.float64)
+    scale = np.abs(want).max(axis=-1, keepdims=True)
+    # bf16 output: one rounding; fp32 output: fp32 accumulation over d_nope products
+    tol = 2.0 ** -8 if out_dt == BF16 else 1e-5
+    err = (np.abs(got - want) / scale).max()
+    _log(f"  max rel err {err:.2e}")
+    assert err <= tol
