@@ -804,10 +804,11 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
 //     probabilities never leave the wave;
 //   * PV: U^T[c][h] (512 columns x 32 heads, all 256 AGPRs) += 32 MFMAs with
 //     the tile read by ds_read_b64_tr_b16 as A.
-// The QK product of tile i+1 is interleaved with the PV product of tile i.
-// The waves meet once per tile, at the barrier that releases a tile buffer to
-// the DMA: 4 buffers, 3 tiles in flight.  LDS: 4 x 36 KB tiles + 16 KB of
-// RoPE queries = 160 KB.
+// The QK product of tile i+1 is interleaved with the PV product of tile i,
+// which runs 10 steps behind, so that the softmax of tile i+1 fits between the
+// last PV MFMAs.  The waves meet once per tile, at the barrier that releases a
+// tile buffer to the DMA: 4 buffers, 3 tiles in flight.  LDS: 4 x 36 KB tiles
+// + 16 KB of RoPE queries = 160 KB.
 
 // The 16 accumulator blocks U^T[32cb..32cb+31][32 heads] (16 fp32 each) live in
 // fixed AGPRs a[16cb..16cb+15], named in the instructions below rather than
@@ -1041,17 +1042,11 @@ void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
   };
   constexpr int kRing = 2;   // PV operand reads in flight
   constexpr int kRingQ = 2;  // QK operand reads in flight
-  // QK of the tile in Tq, interleaved (if PV) with PV of the tile in Tp and
-  // the DMA of a later tile slot (one wave instruction per step)
-  auto qk_pass = [&](const uint8_t* Tq, const uint8_t* Tp, auto PV, const RowsDma& dp) {
-    constexpr bool kPv = decltype(PV)::value;
-    bf16x8_t rq[kRingQ], rp[kRing], rr[kRingQ];
+  // QK of the tile in Tq alone (the first tile of a pass)
+  auto qk_only = [&](const uint8_t* Tq) {
+    bf16x8_t rq[kRingQ], rr[kRingQ];
 #pragma unroll
     for (int k = 0; k < kRingQ; ++k) rq[k] = ld_qk(Tq, k);
-    if constexpr (kPv) {
-#pragma unroll
-      for (int k = 0; k < kRing; ++k) rp[k] = ld_pv(Tp, k);
-    }
     static_for<kH128Steps>([&](auto ST) {
       constexpr int st = decltype(ST)::value;
       const bf16x8_t a = rq[st % kRingQ];
@@ -1060,14 +1055,6 @@ void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
       if constexpr (st + kRingQ >= kH128LatSteps && st + kRingQ < kH128Steps)
         rr[(st + kRingQ) % kRingQ] = ld_qr(st + kRingQ);
       qk_mfma(st, a, qb);
-      if constexpr (kPv) {
-        if constexpr (st < 32) {
-          const bf16x8_t v = rp[st % kRing];
-          if constexpr (st + kRing < 32) rp[st % kRing] = ld_pv(Tp, st + kRing);
-          pv_mfma(ST, v);
-        }
-        if constexpr (st < kDmaPerWave) rows_dma_issue(dp, st);
-      }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -1122,6 +1109,80 @@ void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
     __builtin_memcpy(&pb[1], &w1, 16);
   };
 
+  // The softmax of the tile whose QK pass just ended, in steps that can sit
+  // between MFMAs: step 0 scales and masks the scores and takes their maximum,
+  // steps 1..4 turn 4 scores each into probabilities (2 packed words each).
+  auto softmax_step = [&](int c, int tile, int& overflow, uint32_t (&w)[8]) {
+    if (c == 0) {
+      const int nvalid = t_end - (t_begin + tile * kTileTokens);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] *= P.scale_log2;
+      if (nvalid < kTileTokens) {
+        const int t0 = tok0();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] = (t0 + 8 * (r >> 2) + (r & 3) < nvalid) ? S[r] : -INFINITY;
+      }
+      float mx = S[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+      m_seen = fmaxf(m_seen, mx);
+      overflow |= (mx > m_ref + kRefSlack);
+      return;
+    }
+#pragma unroll
+    for (int r2 = 2 * (c - 1); r2 < 2 * c; ++r2) {
+      const float p0 = __builtin_amdgcn_exp2f(S[2 * r2] - m_ref);
+      const float p1 = __builtin_amdgcn_exp2f(S[2 * r2 + 1] - m_ref);
+      l_run += p0;
+      l_run += p1;
+      w[r2] = pack_bf16x2(p0, p1);
+    }
+  };
+  // QK of tile `tnext` (in Tq) with the PV of the tile in Tp running kLag
+  // steps behind it, so that the QK product ends first and the softmax of
+  // tnext runs between the last PV MFMAs; its probabilities go to pbn (pb is
+  // still being read).  The DMA of a later tile slot is issued one wave
+  // instruction per step.
+  constexpr int kLag = 10;
+  bf16x8_t pbn[2];
+  auto qk_pv_softmax = [&](const uint8_t* Tq, const uint8_t* Tp, const RowsDma& dp, int tnext,
+                           int& overflow) {
+    bf16x8_t rq[kRingQ], rp[kRing], rr[kRingQ];
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < kRingQ; ++k) rq[k] = ld_qk(Tq, k);
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) rp[k] = ld_pv(Tp, k);
+    static_for<32 + kLag>([&](auto SL) {
+      constexpr int st = decltype(SL)::value;
+      if constexpr (st < kH128Steps) {
+        const bf16x8_t a = rq[st % kRingQ];
+        const bf16x8_t qb = st < kH128LatSteps ? q[st < kH128LatSteps ? st : 0] : rr[st % kRingQ];
+        if constexpr (st + kRingQ < kH128Steps) rq[st % kRingQ] = ld_qk(Tq, st + kRingQ);
+        if constexpr (st + kRingQ >= kH128LatSteps && st + kRingQ < kH128Steps)
+          rr[(st + kRingQ) % kRingQ] = ld_qr(st + kRingQ);
+        qk_mfma(st, a, qb);
+      }
+      if constexpr (st >= kLag) {
+        constexpr int k = st - kLag;
+        const bf16x8_t v = rp[k % kRing];
+        if constexpr (k + kRing < 32) rp[k % kRing] = ld_pv(Tp, k + kRing);
+        pv_mfma(std::integral_constant<int, k>{}, v);
+      }
+      if constexpr (st < kDmaPerWave) rows_dma_issue(dp, st);
+      if constexpr (st == kH128Steps) {
+        // the last QK MFMA's scores -> VALU reads
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        softmax_step(0, tnext, overflow, w);
+      }
+      if constexpr (st > kH128Steps && st <= kH128Steps + 4) softmax_step(st - kH128Steps, tnext, overflow, w);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    const u32x4_t w0{w[0], w[1], w[2], w[3]}, w1{w[4], w[5], w[6], w[7]};
+    __builtin_memcpy(&pbn[0], &w0, 16);
+    __builtin_memcpy(&pbn[1], &w1, 16);
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
     static_for<16>([&](auto CB) { AccBlock<decltype(CB)::value>::zero(zero8); });
     if (pass > 0) {
@@ -1133,7 +1194,7 @@ void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
     // issued before tiles 1 and 2) landed
     asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
     barrier();
-    qk_pass(smem, smem, std::false_type{}, RowsDma{});
+    qk_only(smem);
     mfma_drain();
     if (pass == 0) {  // reference: maximum of the first tile, both lane halves
       const int nvalid = t_end - t_begin;
@@ -1146,16 +1207,18 @@ void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
     }
     l_run = 0.0f;
     int overflow = 0;
+    softmax(0, overflow);
     for (int i = 0; i < ntiles; ++i) {
-      softmax(i, overflow);
       asm volatile("s_nop 4" ::: "memory");  // VALU writes of pb -> MFMA reads
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
       barrier();  // tile i+1 landed; tile i-1's buffer released
       const RowsDma dp = dma_plan(i + 3);
       const uint8_t* Tp = smem + (i & (kNBuf - 1)) * kTileBytes;
       if (i + 1 < ntiles) {
-        qk_pass(smem + ((i + 1) & (kNBuf - 1)) * kTileBytes, Tp, std::true_type{}, dp);
-        mfma_drain();
+        qk_pv_softmax(smem + ((i + 1) & (kNBuf - 1)) * kTileBytes, Tp, dp, i + 1, overflow);
+        mfma_drain();  // the PV MFMAs still reading pb -> its replacement
+        pb[0] = pbn[0];
+        pb[1] = pbn[1];
       } else {
         pv_only(Tp, dp);
       }
