@@ -11,7 +11,6 @@
 #include <cmath>
 #include <stdint.h>
 
-#include <mutex>
 #include <type_traits>
 
 #include "../../include/mla.h"
@@ -1629,6 +1628,10 @@ __global__ __launch_bounds__(kMaxDHead) void up_proj_kernel(const void* u, const
 
 constexpr int kProjThreads = 256;
 constexpr int kAbsRowBytes = 128 * 2 + 32;
+// output stage of the staged-query case (d_nope <= 128): past a 128-row W_UK
+// slab and 32 query rows of 128 elements; 32 rows x (512 + 16) bytes at most
+constexpr int kAbsOutOff = 128 * kAbsRowBytes + 32 * (2 * 128 + 16);
+static_assert(kAbsOutOff + 32 * (128 * 4 + 16) <= kMaxDHead * kAbsRowBytes, "absorb LDS stage");
 
 template <int OUT_DT>
 __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_t* q_nope,
@@ -1746,7 +1749,39 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
       }
     }
     // accumulator: column b, rows c = 8*(r/4) + 4*g + r%4 of the wave's 32 columns
-    if (b < B) {
+    if (q_lds) {
+      // the 32 x 128 output tile goes through LDS (past the W_UK slab and the
+      // query rows), so that each store writes 16 bytes per lane along whole
+      // 256-byte (bf16) or 512-byte (fp32) row segments instead of 8 or 16
+      // bytes at a 1152-byte stride
+      constexpr int kEsz = OUT_DT == MLA_F32 ? 4 : 2;
+      constexpr int kOStride = 128 * kEsz + 16;
+      constexpr int kOChunks = 128 * kEsz / 16;  // 16-byte chunks per row
+      uint8_t* os = wt + kAbsOutOff;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint8_t* wp = os + bl * kOStride + (32 * wave + 8 * r4 + 4 * g) * kEsz;
+        if constexpr (OUT_DT == MLA_F32) {
+          *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+        } else {
+          *reinterpret_cast<u32x2_t*>(wp) =
+              u32x2_t{pack_bf16x2(acc[4 * r4], acc[4 * r4 + 1]), pack_bf16x2(acc[4 * r4 + 2], acc[4 * r4 + 3])};
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 32 * kOChunks / kProjThreads; ++i) {
+        const int q = i * kProjThreads + tid, row = q / kOChunks, ch = q % kOChunks;
+        if (b0 + row < B) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(os + row * kOStride + 16 * ch);
+          uint8_t* dst = static_cast<uint8_t*>(q_abs) +
+                         ((static_cast<int64_t>(b0 + row) * H + h) * kRowElems + c_slab) * kEsz;
+          *reinterpret_cast<u32x4_t*>(dst + 16 * ch) = v;
+        }
+      }
+      // the next tile's first barrier (before its query rows are staged)
+      // orders these reads before the next tile's writes to the stage
+    } else if (b < B) {
       const int64_t ob = (static_cast<int64_t>(b) * H + h) * kRowElems + c_slab + 32 * wave;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
