@@ -135,3 +135,36 @@ def test_absorb_dtypes_match_oracle(q_dt, w_dt, out_dt):
     err = (np.abs(got - want) / scale).max()
     _log(f"  max rel err {err:.2e}")
     assert err <= tol
+
+
+@pytest.mark.parametrize("dn", [64, 192, 256])
+@pytest.mark.parametrize("out_dt", [BF16, F32])
+def test_absorb_other_head_dims_match_oracle(dn, out_dt):
+    """The matrix-core absorb at d_nope other than 128: 64 takes the path that
+    stages query rows and the output tile in LDS, 192 and 256 the path that
+    keeps the query operands in registers and stores from the accumulators
+    (37 sequences: a full tile of 32 and a ragged one)."""
+    from synth.encode import f32_to_bf16_bits, bf16_bits_to_f32
+    B, H = 37, 16
+    r = np.random.default_rng(143 + dn)
+    qn = f32_to_bf16_bits(r.standard_normal((B, H, dn)).astype(np.float32))
+    qr = f32_to_bf16_bits(r.standard_normal((B, H, 64)).astype(np.float32))
+    wk = f32_to_bf16_bits((r.standard_normal((H, dn, 512)) / np.sqrt(512)).astype(np.float32))
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+    geo = mla.Geometry(heads=H, d_nope=dn)
+    q_abs = torch.empty(B, H, 576, dtype=torch.float32 if out_dt == F32 else torch.bfloat16,
+                        device="cuda")
+    _log(f"absorb d_nope={dn} out={out_dt}")
+    mla.mla_absorb_q(geo, dev(qn), dev(qr), dev(wk), q_abs)
+    torch.cuda.synchronize()
+    want = oracle.absorb_q(qn, qr, BF16, wk, BF16)
+    got = q_abs.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[..., 512:], bf16_bits_to_f32(qr).astype(np.float64))
+    scale = np.abs(want).max(axis=-1, keepdims=True)
+    tol = 2.0 ** -8 if out_dt == BF16 else 1e-5
+    err = (np.abs(got - want) / scale).max()
+    _log(f"  max rel err {err:.2e}")
+    assert err <= tol
