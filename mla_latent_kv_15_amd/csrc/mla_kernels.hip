@@ -1944,7 +1944,7 @@ constexpr int kCuRows = 16;                // sequences per workgroup
 constexpr int kCuRow = kDLatent * 2 + 16;  // padded LDS row of u (bf16)
 constexpr int kCuBatch = 4;                // splits per batch of partial loads
 
-template <int PART_DT, int O_DT>
+template <int PART_DT, int O_DT, int VS>
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     const void* u_part, const float* lse_part, const uint16_t* w_uv, void* o, uint16_t* u_out,
     float* lse_out, int B, int H, int S, int d_v, int rows) {
@@ -1952,14 +1952,20 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t us[kCuRows * kCuRow + kCuRows * 32 * 64];
   // `rows` (a power of two <= 16) consecutive sequences of one head per
   // workgroup: fewer than 16 when the batch is small, so the grid still
-  // covers the CUs
+  // covers the CUs.  With one sequence per workgroup and still too few
+  // workgroups, VS = 2 workgroups share a (head, sequence): each merges all
+  // of its partials and multiplies by its half of the value rows.
+  static_assert(VS == 1 || VS == 2, "value split");
   const int nbt = (B + rows - 1) / rows;
-  const int wid = xcd_remap(blockIdx.x, H * nbt);
-  const int h = wid / nbt;  // the sequence tiles of one head share W_UV[h] in L2
-  const int b0 = (wid % nbt) * rows;
+  const int wid = xcd_remap(blockIdx.x, H * nbt * VS);
+  const int vs = wid % VS;  // adjacent: the halves read the partials through one L2
+  const int h = wid / VS / nbt;  // the sequence tiles of one head share W_UV[h] in L2
+  const int b0 = (wid / VS % nbt) * rows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
   const int nnb = d_v / 16;  // value blocks of 16 rows
+  const int nbper = (nnb + VS - 1) / VS;
+  const int nb0 = vs * nbper, nb1 = min(nnb, nb0 + nbper);  // this workgroup's value blocks
   constexpr int kWaves = kCuThreads / 64;
   constexpr int kKs = kDLatent / 32;  // k-steps
 
@@ -1989,8 +1995,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     return w_uv + (static_cast<int64_t>(h) * d_v + 16 * nb + n16) * kDLatent + 8 * kg;
   };
   bf16x8_t wk[kKs];
-  {
-    const uint16_t* wr = wrow(min(wave, nnb - 1));
+  if (VS == 1 || nb0 + wave < nb1) {  // wave-uniform
+    const uint16_t* wr = wrow(min(nb0 + wave, nb1 - 1));
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
   }
@@ -2110,12 +2116,12 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
                         pack_bf16x2(acc[12] * inv, acc[13] * inv), pack_bf16x2(acc[14] * inv, acc[15] * inv)};
     *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32) = u0;
     *reinterpret_cast<u32x4_t*>(us + r * kCuRow + cg * 32 + 16) = u1;
-    if (u_out) {
+    if (u_out && vs == 0) {
       uint16_t* dst = u_out + (static_cast<int64_t>(b) * H + h) * kDLatent + 16 * cg;
       *reinterpret_cast<u32x4_t*>(dst) = u0;
       *reinterpret_cast<u32x4_t*>(dst + 8) = u1;
     }
-    if (lse_out && cg == 0) lse_out[static_cast<int64_t>(b) * H + h] = live ? mx + logf(z) : -INFINITY;
+    if (lse_out && cg == 0 && vs == 0) lse_out[static_cast<int64_t>(b) * H + h] = live ? mx + logf(z) : -INFINITY;
   }
   __syncthreads();
 
@@ -2123,8 +2129,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   // A: row n16 (sequence), k group kg.  Rows past the batch are never written;
   // they only reach D rows that are not stored.
   const uint8_t* arow = us + n16 * kCuRow + 16 * kg;
-  for (int nb = wave; nb < nnb; nb += kWaves) {
-    if (nb != wave) {
+  for (int nb = nb0 + wave; nb < nb1; nb += kWaves) {
+    if (nb != nb0 + wave) {
       const uint16_t* wr = wrow(nb);
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
@@ -2617,16 +2623,23 @@ extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, i
   // 256 CUs (small batches)
   int rows = kCuRows;
   while (rows > 1 && static_cast<int64_t>(H) * ((B + rows - 1) / rows) < 256) rows >>= 1;
-  const int64_t nblk = static_cast<int64_t>(H) * ((B + rows - 1) / rows);
+  // one sequence per workgroup and still fewer workgroups than CUs (B = 1 at
+  // 128 heads): two workgroups per (head, sequence), each with half the value rows
+  const int vsplit = (static_cast<int64_t>(H) * B < 256 && dims->d_v >= 32) ? 2 : 1;  // VS
+  const int64_t nblk = static_cast<int64_t>(H) * ((B + rows - 1) / rows) * vsplit;
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid = static_cast<unsigned>(nblk);
   uint16_t* ub = static_cast<uint16_t*>(u);
   const uint16_t* w = static_cast<const uint16_t*>(w_uv);
-#define MLA_CU(PD, OD)                                                                          \
-  if (part_dt == PD && o_dt == OD) {                                                            \
-    combine_up_kernel<PD, OD><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, B, H, \
-                                                          num_splits, dims->d_v, rows);         \
-    return launch_status();                                                                     \
+#define MLA_CU(PD, OD)                                                                             \
+  if (part_dt == PD && o_dt == OD) {                                                               \
+    if (vsplit == 2)                                                                               \
+      combine_up_kernel<PD, OD, 2><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, B, \
+                                                               H, num_splits, dims->d_v, rows);    \
+    else                                                                                           \
+      combine_up_kernel<PD, OD, 1><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, B, \
+                                                               H, num_splits, dims->d_v, rows);    \
+    return launch_status();                                                                        \
   }
   MLA_CU(MLA_BF16, MLA_BF16)
   MLA_CU(MLA_BF16, MLA_F32)

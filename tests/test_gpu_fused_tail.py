@@ -46,6 +46,10 @@ CASES = [  # (batch, lengths or uniform L, splits, partial dtype, output dtype)
     (16, 1500, 1, torch.bfloat16, torch.bfloat16),
     (5, 4096, 64, torch.float32, torch.bfloat16),
     (20, 2000, 17, torch.float32, torch.float32),
+    # one sequence: two workgroups per head, each with half of the value rows
+    (1, 5000, 37, torch.bfloat16, torch.bfloat16),
+    (1, 3000, 256, torch.bfloat16, torch.float32),
+    (1, 700, 5, torch.float32, torch.bfloat16),
 ]
 
 
