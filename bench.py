@@ -67,14 +67,21 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(launch_cache_bytes):
+def traffic_key(workload, splits, partials, decode_kernel):
+    """the launch configuration a traffic record belongs to"""
+    return {"workload": workload, "splits": splits, "partials": partials,
+            "decode_kernel": decode_kernel}
+
+
+def stored_traffic(key):
     """HBM bytes per decode launch measured by rocprofv3 counters, if they were
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and on the launch configuration `key`;
+    else None."""
     try:
         rec = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != source_hash():
+    if rec.get("kernel_source_sha256_16") != source_hash() or rec.get("config") != key:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -93,10 +100,14 @@ def _counter_means(path, counter):
     return {k: v[0] / v[1] for k, v in acc.items()}
 
 
-def record_traffic(d):
+def record_traffic(d, args):
     """HBM bytes per mla_decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by the factor that maps the same counter onto the
-    known bytes of a 1 GiB device copy."""
+    known bytes of a 1 GiB device copy.  The counter runs used the launch
+    configuration given by the other options (the defaults unless stated)."""
+    import synth
+    key = traffic_key(args.workload, args.splits or synth.workload(args.workload).num_splits,
+                      args.part_dtype, args.decode_kernel)
     f = _counter_means(os.path.join(d, "fetch", "run_counter_collection.csv"), "FETCH_SIZE")
     w = _counter_means(os.path.join(d, "write", "run_counter_collection.csv"), "WRITE_SIZE")
     cf = _counter_means(os.path.join(d, "cfetch", "run_counter_collection.csv"), "FETCH_SIZE")
@@ -106,7 +117,7 @@ def record_traffic(d):
     kw = copy_kib / max(v for k, v in cw.items() if "copyBuffer" in k)
     name = next(k for k in f if "decode_" in k and "kernel" in k)
     short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-    rec = {"kernel": short, "kernel_source_sha256_16": source_hash(),
+    rec = {"kernel": short, "kernel_source_sha256_16": source_hash(), "config": key,
            "fetch_kib_per_launch": f[name], "write_kib_per_launch": w[name],
            "fetch_scale": kf, "write_scale": kw,
            "hbm_bytes_per_launch": (f[name] * kf + w[name] * kw) * 1024.0,
@@ -290,7 +301,7 @@ def cpu_baseline(inp, target_s: float = 15.0):
 def main():
     args = parse()
     if args.record_traffic:
-        record_traffic(args.record_traffic)
+        record_traffic(args.record_traffic, args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -439,7 +450,7 @@ def main():
 
     launch_bytes = cache_bytes  # algorithmic bytes of one mla_decode launch
     achieved = launch_bytes / t_decode / 1e9
-    traffic = stored_traffic(launch_bytes)
+    traffic = stored_traffic(traffic_key(wl.name, S, args.part_dtype, args.decode_kernel))
     tokens_per_s = wl.batch / (ms_per_step * 1e-3)
 
     cpu = None
