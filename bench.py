@@ -1,15 +1,18 @@
 """Benchmark: MLA decode step (absorb -> decode -> combine -> up-projection) on
 one MI355X, synthetic inputs, printed as one JSON line.
 
-Timed workload (default): DeepSeek-V2 geometry, bf16 cache and weights with
-fp32 accumulation, batch 32, one query token per sequence, 128 heads,
-d_nope 128, d_rope 64, d_c 512, d_v 128, uniform cache length 2048, 4 split
-ranges per sequence.  A "step" is one decode step of one layer for the whole
-batch; tokens/s = batch / step time.
+Timed workload (default): the paged ragged batch, the largest configuration
+that fits one GPU -- DeepSeek-V2 geometry (128 heads, d_nope 128, d_rope 64,
+d_c 512, d_v 128), bf16 cache and weights with fp32 accumulation, 64
+sequences with lengths drawn uniformly in [512, 16384], the cache in 64-token
+pages in a shuffled block table, 8 split ranges per sequence.  A "step" is one
+decode step of one layer for the whole batch; tokens/s = batch / step time.
 
-The inputs of R independent replicas (cache rows, queries, weights; >= 1 GiB
-in total) are resident in HBM before timing starts and the steps rotate over
-them, so the 256 MB Infinity Cache cannot serve the cache stream.
+The inputs of R independent replicas (cache rows, queries, weights; >= 1.25
+GiB in total) are resident in HBM before timing starts and the steps rotate
+over them, so the 256 MB Infinity Cache cannot serve the cache stream.  HIP
+events recorded between the step's launches, on the launch stream, give each
+kernel's per-launch duration over the timed steps (median, p10, p90, mean).
 """
 
 from __future__ import annotations
@@ -28,6 +31,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense matrix-core peaks at 2.4 GHz
+CLOCK_HZ = 2.4e9  # rated engine clock (the matrix-core peaks are quoted at it)
+N_SIMD = 256 * 4
 KERNEL_SOURCE = os.path.join(ROOT, "mla_latent_kv_15_amd", "csrc", "mla_kernels.hip")
 
 
@@ -36,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dsv2_b32_l2k")
+    ap.add_argument("--workload", default="paged_b64_ragged")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--decode-kernel", default="auto", choices=["auto", "h64", "h128"],
@@ -73,17 +79,22 @@ def traffic_key(workload, splits, partials, decode_kernel):
             "decode_kernel": decode_kernel}
 
 
-def stored_traffic(key):
-    """HBM bytes per decode launch measured by rocprofv3 counters, if they were
-    taken on the current kernel source and on the launch configuration `key`;
-    else None."""
+def _records():
     try:
         rec = json.load(open(PROFILE_TRAFFIC))
     except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256_16") != source_hash() or rec.get("config") != key:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return []
+    return rec.get("records", []) if isinstance(rec, dict) else []
+
+
+def stored_counters(key):
+    """The counter record of the decode kernel (HBM bytes per launch from
+    FETCH_SIZE / WRITE_SIZE, matrix-core busy cycles), if it was taken on the
+    current kernel source and on the launch configuration `key`; else None."""
+    for rec in _records():
+        if rec.get("kernel_source_sha256_16") == source_hash() and rec.get("config") == key:
+            return rec
+    return None
 
 
 def _counter_means(path, counter):
@@ -103,8 +114,10 @@ def _counter_means(path, counter):
 def record_traffic(d, args):
     """HBM bytes per mla_decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by the factor that maps the same counter onto the
-    known bytes of a 1 GiB device copy.  The counter runs used the launch
-    configuration given by the other options (the defaults unless stated)."""
+    known bytes of a 1 GiB device copy, and (if DIR/sq exists) the decode's
+    SQ_VALU_MFMA_BUSY_CYCLES per launch.  The counter runs used the launch
+    configuration given by the other options (the defaults unless stated);
+    the record replaces any earlier one for the same configuration."""
     import synth
     key = traffic_key(args.workload, args.splits or synth.workload(args.workload).num_splits,
                       args.part_dtype, args.decode_kernel)
@@ -122,8 +135,27 @@ def record_traffic(d, args):
            "fetch_scale": kf, "write_scale": kw,
            "hbm_bytes_per_launch": (f[name] * kf + w[name] * kw) * 1024.0,
            "counters_from": os.path.relpath(os.path.abspath(d), ROOT)}
-    json.dump(rec, open(PROFILE_TRAFFIC, "w"), indent=1)
+    sq = os.path.join(d, "sq", "run_counter_collection.csv")
+    if os.path.exists(sq):
+        busy = _counter_means(sq, "SQ_VALU_MFMA_BUSY_CYCLES")
+        if name in busy:
+            rec["mfma_busy_cycles_per_launch"] = busy[name]
+    recs = [r for r in _records() if r.get("config") != key]
+    recs.append(rec)
+    json.dump({"records": recs}, open(PROFILE_TRAFFIC, "w"), indent=1)
     print(json.dumps(rec))
+
+
+def pct(xs, q):
+    """q-th percentile (0..100) of the samples xs, linear between order statistics"""
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, np.float64), q))
+
+
+def launch_stats(us):
+    """per-launch durations (us) -> {median, p10, p90, mean, n}"""
+    return {"median": pct(us, 50), "p10": pct(us, 10), "p90": pct(us, 90),
+            "mean": float(sum(us) / len(us)), "n": len(us)}
 
 
 def multi_token_bench(args, wl, dev, reps, R, S, act, part, out, cache_bytes):
@@ -361,40 +393,59 @@ def main():
 
     kernel = {"auto": mla.KERNEL_AUTO, "h64": mla.KERNEL_H64, "h128": mla.KERNEL_H128}[args.decode_kernel]
 
-    def decode(rp):
-        mla.mla_decode_ex(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
-                          kernel=kernel, stream=stream)
+    def decode(rp, prepare=False):
+        return mla.mla_decode_ex(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
+                                 kernel=kernel, stream=stream, prepare=prepare)
 
-    def one(i):
-        rp = reps[i % R]
-        mla.mla_absorb_q(step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs,
-                         stream=stream)
-        decode(rp)
-        if fused:
-            mla.mla_combine_up_proj(step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o,
-                                    stream=stream)
-        else:
-            if S > 1:
-                mla.mla_combine(step.geo, step.u_part, step.lse_part, step.u, step.lse,
-                                stream=stream)
-            mla.mla_up_proj(step.geo, step.u, rp["w_uv"], step.o, stream=stream)
+    # the step's launches in order: (name, fn(replica, prepare))
+    stages = [("mla_absorb_q", lambda rp, prepare=False: mla.mla_absorb_q(
+                  step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs, stream=stream,
+                  prepare=prepare)),
+              ("mla_decode", decode)]
+    if fused:
+        stages.append(("mla_combine_up_proj", lambda rp, prepare=False: mla.mla_combine_up_proj(
+            step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o, stream=stream,
+            prepare=prepare)))
+    else:
+        if S > 1:
+            stages.append(("mla_combine", lambda rp, prepare=False: mla.mla_combine(
+                step.geo, step.u_part, step.lse_part, step.u, step.lse, stream=stream,
+                prepare=prepare)))
+        stages.append(("mla_up_proj", lambda rp, prepare=False: mla.mla_up_proj(
+            step.geo, step.u, rp["w_uv"], step.o, stream=stream, prepare=prepare)))
+    # every launch validated and marshalled once per replica (mla.Call), so the
+    # timed loop issues launches without the binding's per-call checks
+    prepared = [[fn(rp, prepare=True) for _, fn in stages] for rp in reps]
 
     print(f"[bench] warmup {args.warmup}, R={R} replicas", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        one(i)
+        for call in prepared[i % R]:
+            call()
     torch.cuda.synchronize()
 
-    # whole-step timing: K steps between two synchronisations
+    # the timed region: K steps between two synchronisations; an event on
+    # the launch stream before the first launch of each step and after each
+    # launch gives every kernel's per-launch duration
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one(i)
+        ev[i][0].record(stream)
+        for j, call in enumerate(prepared[i % R]):
+            call()
+            ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    per_launch = {name: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(args.steps)]
+                  for j, (name, _) in enumerate(stages)}
+    kernel_stats = {name: launch_stats(us) for name, us in per_launch.items()}
+    kernel_us = {name: st["mean"] for name, st in kernel_stats.items()}
+    t_decode = kernel_us["mla_decode"] * 1e-6
+    t_tail = sum(v for k, v in kernel_us.items() if k not in ("mla_absorb_q", "mla_decode")) * 1e-6
 
-    # per-kernel timing: each entry point launched `steps` times back to back
-    # (rotating over the replicas) between two HIP events recorded on the
-    # launch stream; mean time per launch
+    # outside the step: the cache append that precedes it (each sequence's
+    # last row is rewritten with a fresh bf16 row), timed the same way
     def loop_ms(fn):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -405,23 +456,6 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    stages = [("mla_absorb_q", lambda rp: mla.mla_absorb_q(
-                  step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs, stream=stream)),
-              ("mla_decode", decode)]
-    if fused:
-        stages.append(("mla_combine_up_proj", lambda rp: mla.mla_combine_up_proj(
-            step.geo, step.u_part, step.lse_part, rp["w_uv"], step.o, stream=stream)))
-    else:
-        if S > 1:
-            stages.append(("mla_combine", lambda rp: mla.mla_combine(
-                step.geo, step.u_part, step.lse_part, step.u, step.lse, stream=stream)))
-        stages.append(("mla_up_proj", lambda rp: mla.mla_up_proj(
-            step.geo, step.u, rp["w_uv"], step.o, stream=stream)))
-    kernel_us = {name: loop_ms(fn) * 1e3 for name, fn in stages}
-    t_decode = kernel_us["mla_decode"] * 1e-6
-
-    # outside the step: the cache append that precedes it (each sequence's
-    # last row is rewritten with a fresh bf16 row), timed the same way
     g = torch.Generator(device="cuda").manual_seed(7)
     new_c = torch.randn(wl.batch, wl.d_latent, device="cuda", generator=g).to(act)
     new_r = torch.randn(wl.batch, wl.d_rope, device="cuda", generator=g).to(act)
@@ -448,9 +482,25 @@ def main():
         step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], last, step.q_abs,
         stream=stream)) * 1e3
 
-    launch_bytes = cache_bytes  # algorithmic bytes of one mla_decode launch
+    # roofline of the decode: algorithmic bytes of one launch (the cache rows
+    # it attends) over its mean launch duration
+    launch_bytes = cache_bytes
     achieved = launch_bytes / t_decode / 1e9
-    traffic = stored_traffic(traffic_key(wl.name, S, args.part_dtype, args.decode_kernel))
+    key = traffic_key(wl.name, S, args.part_dtype, args.decode_kernel)
+    counters = stored_counters(key)
+    traffic = None if counters is None else counters.get("hbm_bytes_per_launch")
+    # matrix-core work of the decode: 2 h (576 + 512) FLOP per attended token
+    n_tok = float(np.sum(np.asarray(inp.seq_lens, np.float64)))
+    dec_flops = n_tok * 2 * wl.heads * (576 + wl.d_latent)
+    mfma_dt = "fp8" if step.q_abs.dtype == torch.uint8 else "bf16"  # the QK operand type
+    mfma = {"algorithmic_flops_per_launch": dec_flops,
+            "achieved_tflops": dec_flops / t_decode / 1e12,
+            "peak_tflops": MFMA_PEAK_TFLOPS[mfma_dt],
+            "frac_of_peak": dec_flops / t_decode / 1e12 / MFMA_PEAK_TFLOPS[mfma_dt],
+            "busy_frac_from_counters": None}
+    if counters is not None and "mfma_busy_cycles_per_launch" in counters:
+        mfma["busy_frac_from_counters"] = (counters["mfma_busy_cycles_per_launch"] / N_SIMD
+                                           / (t_decode * CLOCK_HZ))
     tokens_per_s = wl.batch / (ms_per_step * 1e-3)
 
     cpu = None
@@ -473,14 +523,21 @@ def main():
         "data": "synthetic (seeded N(0,1) activations/cache, N(0,1/512) weights)",
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads,
                    "d_nope": wl.d_nope, "d_rope": wl.d_rope, "d_latent": wl.d_latent,
-                   "d_v": wl.d_v, "seq_len": int(inp.max_seq_len), "splits": S,
+                   "d_v": wl.d_v, "seq_len": int(inp.max_seq_len),
+                   "tokens_attended": int(n_tok), "splits": S,
                    "cache": f"{wl.cache_dtype} {'paged' if wl.page_size else 'contiguous'}",
                    "partials": args.part_dtype, "decode_kernel": args.decode_kernel,
                    "replicas": R, "parallelism": "none (1 GPU)"},
-        "cache_GBps": cache_bytes / t_decode / 1e9,
-        "cache_pct_hbm_peak": 100.0 * cache_bytes / t_decode / 1e9 / HBM_PEAK_GBPS,
-        "kernel_us_mean": kernel_us,
+        # cache bytes over the time of the launches that handle the cache
+        # stream: the decode and the merge of its partials (the fused tail
+        # also applies W_UV)
+        "cache_bytes": cache_bytes,
+        "cache_GBps": cache_bytes / (t_decode + t_tail) / 1e9,
+        "cache_pct_hbm_peak": 100.0 * cache_bytes / (t_decode + t_tail) / 1e9 / HBM_PEAK_GBPS,
+        "cache_GBps_decode_only": achieved,
+        "kernel_us": kernel_stats,
         "outside_step_us_mean": outside_us,
+        "mfma": mfma,
         "roofline": {"kernel": "mla_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes},

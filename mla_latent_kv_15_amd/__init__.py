@@ -1,7 +1,9 @@
 """Python binding of libmla.so, the MI355X (gfx950) MLA decode library.
 
 Argument marshalling only: every function here takes torch tensors that live
-on the GPU, checks their dtype/shape/contiguity, and passes raw device
+on the GPU, checks their device, dtype, exact shape (from the batch, split
+count, heads and widths the call implies) and contiguity before anything
+reaches the library, and passes raw device
 pointers plus the current HIP stream to the C entry point of the same name
 declared in include/mla.h.  All arithmetic runs in the library's kernels.
 There is no CPU fallback: importing this module without the built library
@@ -124,7 +126,77 @@ def _ptr(t: Optional[torch.Tensor]):
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to the MLA library must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"tensors passed to the MLA library must be on the GPU, got {t.device}")
     return t.data_ptr()
+
+
+def _need(name: str, t: Optional[torch.Tensor], shape, dtypes=None, optional=False) -> None:
+    """Checks, before anything reaches the C library, that `t` is a tensor of
+    exactly `shape` (and of one of `dtypes`) and contiguous: the
+    kernels index every buffer by the sizes the call implies, so a smaller
+    buffer would be read or written out of bounds."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    shape = tuple(int(x) for x in shape)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, the call needs {shape}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, the call needs one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(*ts) -> None:
+    """every given buffer (None: absent) lives on the GPU; checked after the
+    shapes, so a shape error is reported as such whatever the device"""
+    for x in ts:
+        if x is not None and x.device.type != "cuda":
+            raise ValueError(f"tensors passed to the MLA library must be on the GPU, got {x.device}")
+
+
+def _cache_tensors(cache: "Cache"):
+    return (cache.rows, cache.seq_lens, cache.row_scale, cache.block_table)
+
+
+_FLOAT = (torch.float32, torch.bfloat16)
+_CACHE_DT = (torch.float32, torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
+
+
+def _need_cache(cache: "Cache", B: int, geo: "Geometry") -> None:
+    """The cache descriptor's buffers against the batch: rows [n, 576],
+    seq_lens int32 [B], block_table int32 [B, max_pages] (paged), row_scale
+    float32 [n] (e4m3); a contiguous cache must hold B * seq_stride rows (the
+    last sequence at least max_seq_len).  Page ids inside block_table live on
+    the device and are the caller's contract."""
+    w = geo.d_latent + geo.d_rope
+    r = cache.rows
+    if not isinstance(r, torch.Tensor) or r.dim() != 2 or int(r.shape[1]) != w:
+        raise ValueError(f"cache.rows must be [n_rows, {w}]")
+    _need("cache.rows", r, tuple(r.shape), _CACHE_DT)
+    n = int(r.shape[0])
+    _need("cache.seq_lens", cache.seq_lens, (B,), (torch.int32,))
+    if int(cache.max_seq_len) < 0:
+        raise ValueError("cache.max_seq_len must be >= 0")
+    if dtype_code(r) == MLA_FP8_E4M3:
+        _need("cache.row_scale", cache.row_scale, (n,), (torch.float32,))
+    if cache.page_size:
+        bt = cache.block_table
+        if not isinstance(bt, torch.Tensor) or bt.dim() != 2:
+            raise ValueError("a paged cache needs block_table [B, max_pages]")
+        _need("cache.block_table", bt, (B, int(bt.shape[1])), (torch.int32,))
+        if int(bt.shape[1]) * int(cache.page_size) < int(cache.max_seq_len):
+            raise ValueError("block_table has fewer pages than max_seq_len needs")
+    elif B > 0 and cache.max_seq_len > 0:
+        if int(cache.seq_stride) < int(cache.max_seq_len):
+            raise ValueError("cache.seq_stride must be >= max_seq_len")
+        if (B - 1) * int(cache.seq_stride) + int(cache.max_seq_len) > n:
+            raise ValueError(f"cache.rows holds {n} rows, B={B} sequences of stride "
+                             f"{cache.seq_stride} need {(B - 1) * cache.seq_stride + cache.max_seq_len}")
 
 
 def _stream(stream) -> int:
@@ -168,84 +240,155 @@ class Cache:
                          _ptr(self.seq_lens), int(self.max_seq_len))
 
 
+class Call:
+    """One library call whose arguments were validated and marshalled once:
+    calling it enqueues the same launch again (the buffers' contents may have
+    changed since, not their addresses or shapes).  The ctypes structures the
+    arguments point to are kept alive with it."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.name = name
+        self.fn = getattr(lib(), name)
+        self.args = args
+        self._keep = keep
+
+    def __call__(self) -> None:
+        _check(self.name, self.fn(*self.args))
+
+
+def _launch(name: str, args: tuple, keep: tuple, prepare: bool):
+    if prepare:
+        return Call(name, args, keep)
+    _check(name, getattr(lib(), name)(*args))
+    return None
+
+
+def _dims(geo: Geometry):
+    return geo.heads, geo.d_latent + geo.d_rope
+
+
 def mla_absorb_q_rope(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor,
                       w_uk: torch.Tensor, positions: torch.Tensor, q_abs: torch.Tensor,
-                      rope_base: float = 10000.0, stream=None) -> None:
+                      rope_base: float = 10000.0, stream=None, prepare: bool = False):
     """mla_absorb_q with q_R rotated by positions (int32 [B] on the device)."""
     B = int(q_nope.shape[0])
-    if positions.dtype != torch.int32:
-        raise TypeError("positions must be int32")
+    H, W = _dims(geo)
+    _need("q_nope", q_nope, (B, H, geo.d_nope), _FLOAT)
+    _need("q_rope", q_rope, (B, H, geo.d_rope), _FLOAT)
+    _need("w_uk", w_uk, (H, geo.d_nope, geo.d_latent), _FLOAT)
+    _need("positions", positions, (B,), (torch.int32,))
+    _need("q_abs", q_abs, (B, H, W), _FLOAT)
+    _on_gpu(q_nope, q_rope, w_uk, positions, q_abs)
     d = geo.c()
-    st = lib().mla_absorb_q_rope(C.byref(d), B, _ptr(q_nope), _ptr(q_rope), dtype_code(q_nope),
+    return _launch("mla_absorb_q_rope", (C.byref(d), B, _ptr(q_nope), _ptr(q_rope), dtype_code(q_nope),
                                  _ptr(w_uk), dtype_code(w_uk), _ptr(positions), float(rope_base),
-                                 _ptr(q_abs), dtype_code(q_abs), _stream(stream))
-    _check("mla_absorb_q_rope", st)
+                                 _ptr(q_abs), dtype_code(q_abs), _stream(stream),), (d,), prepare)
 
 
 def mla_mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    seq_lens: torch.Tensor, max_seq_len: int, o: torch.Tensor,
                    lse: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
-                   stream=None) -> None:
+                   stream=None, prepare: bool = False):
     """MHA baseline decode: q [B, h, 128], k_cache / v_cache [B, h, stride, 128]
     (bfloat16), seq_lens int32 [B] on the device; o [B, h, 128]."""
     B, H, D = (int(x) for x in q.shape)
-    st = lib().mla_mha_decode(B, H, D, _ptr(q), _ptr(k_cache), _ptr(v_cache), dtype_code(q),
-                              _ptr(seq_lens), int(k_cache.shape[2]), int(max_seq_len),
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, h, stride, d_head]")
+    stride = int(k_cache.shape[2])
+    _need("q", q, (B, H, D), _FLOAT)
+    _need("k_cache", k_cache, (B, H, stride, D), (q.dtype,))
+    _need("v_cache", v_cache, (B, H, stride, D), (q.dtype,))
+    _need("seq_lens", seq_lens, (B,), (torch.int32,))
+    _need("o", o, (B, H, D), _FLOAT)
+    _need("lse", lse, (B, H), (torch.float32,), optional=True)
+    if not 0 <= int(max_seq_len) <= stride:
+        raise ValueError("max_seq_len must lie in [0, stride]")
+    _on_gpu(q, k_cache, v_cache, seq_lens, o, lse)
+    return _launch("mla_mha_decode", (B, H, D, _ptr(q), _ptr(k_cache), _ptr(v_cache), dtype_code(q),
+                              _ptr(seq_lens), stride, int(max_seq_len),
                               float(softmax_scale), _ptr(o), dtype_code(o), _ptr(lse),
-                              _stream(stream))
-    _check("mla_mha_decode", st)
+                              _stream(stream),), (), prepare)
 
 
 def mla_cache_append(geo: Geometry, c_kv: torch.Tensor, k_r: torch.Tensor,
-                     positions: torch.Tensor, cache: Cache, stream=None) -> None:
+                     positions: torch.Tensor, cache: Cache, stream=None, prepare: bool = False):
     """Write token positions[b] of every sequence b: c_kv [B, d_latent] and
     k_r [B, d_rope] (float32 or bfloat16) into cache.rows (and row_scale for
     an e4m3 cache).  positions: int32 [B] on the device."""
     B = int(c_kv.shape[0])
-    if positions.dtype != torch.int32:
-        raise TypeError("positions must be int32")
+    _need("c_kv", c_kv, (B, geo.d_latent), _FLOAT)
+    _need("k_r", k_r, (B, geo.d_rope), (c_kv.dtype,))
+    _need("positions", positions, (B,), (torch.int32,))
+    _need_cache(cache, B, geo)
+    _on_gpu(c_kv, k_r, positions, *_cache_tensors(cache))
     d = geo.c()
     cd = cache.c()
-    st = lib().mla_cache_append(C.byref(d), B, _ptr(c_kv), _ptr(k_r), dtype_code(c_kv),
-                                _ptr(positions), C.byref(cd), _stream(stream))
-    _check("mla_cache_append", st)
+    return _launch("mla_cache_append", (C.byref(d), B, _ptr(c_kv), _ptr(k_r), dtype_code(c_kv),
+                                _ptr(positions), C.byref(cd), _stream(stream),), (d, cd), prepare)
 
 
 def mla_absorb_q(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor,
                  q_abs: torch.Tensor, q_abs_scale: Optional[torch.Tensor] = None,
-                 stream=None) -> None:
+                 stream=None, prepare: bool = False):
+    """q_nope [B, h, d_nope], q_rope [B, h, d_rope], w_uk [h, d_nope, 512] ->
+    q_abs [B, h, 576] (float32, bfloat16, or e4m3 codes as uint8 /
+    float8_e4m3fn with q_abs_scale float32 [B, h])."""
     B = int(q_nope.shape[0])
+    H, W = _dims(geo)
+    _need("q_nope", q_nope, (B, H, geo.d_nope), _FLOAT)
+    _need("q_rope", q_rope, (B, H, geo.d_rope), _FLOAT)
+    _need("w_uk", w_uk, (H, geo.d_nope, geo.d_latent), _FLOAT)
+    _need("q_abs", q_abs, (B, H, W), _CACHE_DT)
+    _need("q_abs_scale", q_abs_scale, (B, H), (torch.float32,), optional=True)
+    _on_gpu(q_nope, q_rope, w_uk, q_abs, q_abs_scale)
     d = geo.c()
-    st = lib().mla_absorb_q(C.byref(d), B, _ptr(q_nope), _ptr(q_rope), dtype_code(q_nope),
+    return _launch("mla_absorb_q", (C.byref(d), B, _ptr(q_nope), _ptr(q_rope), dtype_code(q_nope),
                             _ptr(w_uk), dtype_code(w_uk), _ptr(q_abs), dtype_code(q_abs),
-                            _ptr(q_abs_scale), _stream(stream))
-    _check("mla_absorb_q", st)
+                            _ptr(q_abs_scale), _stream(stream),), (d,), prepare)
+
+
+def _need_parts(geo: Geometry, lead: tuple, S: int, u_part, lse_part) -> None:
+    H = geo.heads
+    _need("u_part", u_part, (*lead, S, H, geo.d_latent), _FLOAT)
+    _need("lse_part", lse_part, (*lead, S, H), (torch.float32,))
 
 
 def mla_decode(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int,
                u_part: torch.Tensor, lse_part: torch.Tensor,
-               q_abs_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+               q_abs_scale: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """q_abs [B, h, 576]; u_part [B, S, h, 512]; lse_part [B, S, h]."""
     B = int(q_abs.shape[0])
+    H, W = _dims(geo)
+    _need("q_abs", q_abs, (B, H, W), _CACHE_DT)
+    _need("q_abs_scale", q_abs_scale, (B, H), (torch.float32,), optional=True)
+    _need_parts(geo, (B,), int(num_splits), u_part, lse_part)
+    _need_cache(cache, B, geo)
+    _on_gpu(q_abs, q_abs_scale, u_part, lse_part, *_cache_tensors(cache))
     d = geo.c()
     cd = cache.c()
-    st = lib().mla_decode(C.byref(d), B, _ptr(q_abs), dtype_code(q_abs), _ptr(q_abs_scale),
+    return _launch("mla_decode", (C.byref(d), B, _ptr(q_abs), dtype_code(q_abs), _ptr(q_abs_scale),
                           C.byref(cd), int(num_splits), _ptr(u_part), dtype_code(u_part),
-                          _ptr(lse_part), _stream(stream))
-    _check("mla_decode", st)
+                          _ptr(lse_part), _stream(stream),), (d, cd), prepare)
 
 
 def mla_decode_multi(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int,
-                     u_part: torch.Tensor, lse_part: torch.Tensor, stream=None) -> None:
+                     u_part: torch.Tensor, lse_part: torch.Tensor, stream=None, prepare: bool = False):
     """Multi-token decode: q_abs [B, q_len, h, 576]; u_part [B, q_len, S, h,
     512]; lse_part [B, q_len, S, h] (the last q_len cached rows are the new
     tokens, attended causally)."""
+    if q_abs.dim() != 4:
+        raise ValueError("q_abs must be [B, q_len, h, 576]")
     B, QL = int(q_abs.shape[0]), int(q_abs.shape[1])
+    H, W = _dims(geo)
+    _need("q_abs", q_abs, (B, QL, H, W), _FLOAT)
+    _need_parts(geo, (B, QL), int(num_splits), u_part, lse_part)
+    _need_cache(cache, B, geo)
+    _on_gpu(q_abs, u_part, lse_part, *_cache_tensors(cache))
     d = geo.c()
     cd = cache.c()
-    st = lib().mla_decode_multi(C.byref(d), B, QL, _ptr(q_abs), dtype_code(q_abs), C.byref(cd),
+    return _launch("mla_decode_multi", (C.byref(d), B, QL, _ptr(q_abs), dtype_code(q_abs), C.byref(cd),
                                 int(num_splits), _ptr(u_part), dtype_code(u_part), _ptr(lse_part),
-                                _stream(stream))
-    _check("mla_decode_multi", st)
+                                _stream(stream),), (d, cd), prepare)
 
 
 KERNEL_AUTO, KERNEL_H64, KERNEL_H128 = 0, 1, 2  # mla_decode_kernel_t
@@ -253,48 +396,71 @@ KERNEL_AUTO, KERNEL_H64, KERNEL_H128 = 0, 1, 2  # mla_decode_kernel_t
 
 def mla_decode_ex(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int,
                   u_part: torch.Tensor, lse_part: torch.Tensor, kernel: int = KERNEL_AUTO,
-                  stream=None) -> None:
+                  stream=None, prepare: bool = False):
     """mla_decode (q_abs [B, h, 576]) or mla_decode_multi (q_abs [B, q_len, h,
     576]) with the decode kernel chosen by the caller (KERNEL_*)."""
     B = int(q_abs.shape[0])
     QL = int(q_abs.shape[1]) if q_abs.dim() == 4 else 1
+    H, W = _dims(geo)
+    lead = (B, QL) if q_abs.dim() == 4 else (B,)
+    _need("q_abs", q_abs, (*lead, H, W), _FLOAT)
+    _need_parts(geo, lead, int(num_splits), u_part, lse_part)
+    _need_cache(cache, B, geo)
+    _on_gpu(q_abs, u_part, lse_part, *_cache_tensors(cache))
     d = geo.c()
     cd = cache.c()
-    st = lib().mla_decode_ex(C.byref(d), B, QL, _ptr(q_abs), dtype_code(q_abs), C.byref(cd),
+    return _launch("mla_decode_ex", (C.byref(d), B, QL, _ptr(q_abs), dtype_code(q_abs), C.byref(cd),
                              int(num_splits), _ptr(u_part), dtype_code(u_part), _ptr(lse_part),
-                             int(kernel), _stream(stream))
-    _check("mla_decode_ex", st)
+                             int(kernel), _stream(stream),), (d, cd), prepare)
 
 
 def mla_combine(geo: Geometry, u_part: torch.Tensor, lse_part: torch.Tensor, u: torch.Tensor,
-                lse: Optional[torch.Tensor] = None, stream=None) -> None:
+                lse: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """u_part [B, S, h, 512], lse_part [B, S, h] -> u [B, h, 512], lse [B, h]."""
     B, S = int(u_part.shape[0]), int(u_part.shape[1])
+    H = geo.heads
+    _need_parts(geo, (B,), S, u_part, lse_part)
+    _need("u", u, (B, H, geo.d_latent), _FLOAT)
+    _need("lse", lse, (B, H), (torch.float32,), optional=True)
+    _on_gpu(u_part, lse_part, u, lse)
     d = geo.c()
-    st = lib().mla_combine(C.byref(d), B, S, _ptr(u_part), dtype_code(u_part), _ptr(lse_part),
-                           _ptr(u), dtype_code(u), _ptr(lse), _stream(stream))
-    _check("mla_combine", st)
+    return _launch("mla_combine", (C.byref(d), B, S, _ptr(u_part), dtype_code(u_part), _ptr(lse_part),
+                           _ptr(u), dtype_code(u), _ptr(lse), _stream(stream),), (d,), prepare)
 
 
 def mla_up_proj(geo: Geometry, u: torch.Tensor, w_uv: torch.Tensor, o: torch.Tensor,
-                stream=None) -> None:
+                stream=None, prepare: bool = False):
+    """u [B, h, 512], w_uv [h, d_v, 512] -> o [B, h, d_v]."""
     B = int(u.shape[0])
+    H = geo.heads
+    _need("u", u, (B, H, geo.d_latent), _FLOAT)
+    _need("w_uv", w_uv, (H, geo.d_v, geo.d_latent), _FLOAT)
+    _need("o", o, (B, H, geo.d_v), _FLOAT)
+    _on_gpu(u, w_uv, o)
     d = geo.c()
-    st = lib().mla_up_proj(C.byref(d), B, _ptr(u), dtype_code(u), _ptr(w_uv), dtype_code(w_uv),
-                           _ptr(o), dtype_code(o), _stream(stream))
-    _check("mla_up_proj", st)
+    return _launch("mla_up_proj", (C.byref(d), B, _ptr(u), dtype_code(u), _ptr(w_uv), dtype_code(w_uv),
+                           _ptr(o), dtype_code(o), _stream(stream),), (d,), prepare)
 
 
 def mla_combine_up_proj(geo: Geometry, u_part: torch.Tensor, lse_part: torch.Tensor,
                         w_uv: torch.Tensor, o: torch.Tensor, u: Optional[torch.Tensor] = None,
-                        lse: Optional[torch.Tensor] = None, stream=None) -> None:
+                        lse: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """u_part [B, S, h, 512], lse_part [B, S, h], w_uv [h, d_v, 512] ->
+    o [B, h, d_v]; optionally u [B, h, 512] (bfloat16) and lse [B, h]."""
     B, S = int(u_part.shape[0]), int(u_part.shape[1])
+    H = geo.heads
     if u is not None and u.dtype != torch.bfloat16:
         raise TypeError("mla_combine_up_proj stores u as bfloat16 only")
+    _need_parts(geo, (B,), S, u_part, lse_part)
+    _need("w_uv", w_uv, (H, geo.d_v, geo.d_latent), _FLOAT)
+    _need("o", o, (B, H, geo.d_v), _FLOAT)
+    _need("u", u, (B, H, geo.d_latent), (torch.bfloat16,), optional=True)
+    _need("lse", lse, (B, H), (torch.float32,), optional=True)
+    _on_gpu(u_part, lse_part, w_uv, o, u, lse)
     d = geo.c()
-    st = lib().mla_combine_up_proj(C.byref(d), B, S, _ptr(u_part), dtype_code(u_part),
+    return _launch("mla_combine_up_proj", (C.byref(d), B, S, _ptr(u_part), dtype_code(u_part),
                                    _ptr(lse_part), _ptr(w_uv), dtype_code(w_uv), _ptr(o),
-                                   dtype_code(o), _ptr(u), _ptr(lse), _stream(stream))
-    _check("mla_combine_up_proj", st)
+                                   dtype_code(o), _ptr(u), _ptr(lse), _stream(stream),), (d,), prepare)
 
 
 def split_chunk(max_seq_len: int, num_splits: int) -> int:

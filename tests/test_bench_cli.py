@@ -18,19 +18,34 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.stdout == ""
 
 
-def test_traffic_record_applies_only_to_its_source_and_launch(monkeypatch):
-    """The stored counter bytes are reported for the kernel source and the
-    launch configuration they were measured on, and for nothing else."""
+def test_counter_record_applies_only_to_its_source_and_launch(monkeypatch, tmp_path):
+    """A stored counter record is reported for the kernel source and the launch
+    configuration it was measured on, and for nothing else; records of several
+    configurations live side by side."""
     sys.path.insert(0, ROOT)
     import bench
     with open(os.path.join(ROOT, "profiles", "decode_traffic.json")) as f:
-        rec = json.load(f)
-    key = rec["config"]
-    monkeypatch.setattr(bench, "source_hash", lambda: rec["kernel_source_sha256_16"])
-    t = bench.stored_traffic(key)
-    assert t is not None and t > 75497472  # at least the default workload's cache stream
-    other = dict(key, workload="long_b4_l32k", splits=64)
-    assert bench.stored_traffic(other) is None
-    assert bench.stored_traffic(dict(key, decode_kernel="h128")) is None
+        recs = json.load(f)["records"]
+    assert recs and all("config" in r and "hbm_bytes_per_launch" in r for r in recs)
+    a = bench.traffic_key("paged_b64_ragged", 8, "bf16", "auto")
+    b = bench.traffic_key("long_b4_l32k", 64, "bf16", "auto")
+    store = tmp_path / "t.json"
+    json.dump({"records": [dict(config=a, kernel_source_sha256_16="1" * 16, hbm_bytes_per_launch=7.0),
+                           dict(config=b, kernel_source_sha256_16="1" * 16, hbm_bytes_per_launch=9.0)]},
+              open(store, "w"))
+    monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(store))
+    monkeypatch.setattr(bench, "source_hash", lambda: "1" * 16)
+    assert bench.stored_counters(a)["hbm_bytes_per_launch"] == 7.0
+    assert bench.stored_counters(b)["hbm_bytes_per_launch"] == 9.0
+    assert bench.stored_counters(dict(a, decode_kernel="h128")) is None
+    assert bench.stored_counters(dict(a, splits=16)) is None
     monkeypatch.setattr(bench, "source_hash", lambda: "0" * 16)
-    assert bench.stored_traffic(key) is None
+    assert bench.stored_counters(a) is None
+
+
+def test_launch_stats():
+    sys.path.insert(0, ROOT)
+    import bench
+    st = bench.launch_stats([float(x) for x in range(1, 102)])
+    assert st["median"] == 51.0 and st["p10"] == 11.0 and st["p90"] == 91.0
+    assert st["mean"] == 51.0 and st["n"] == 101

@@ -315,28 +315,67 @@ def test_repeat_is_deterministic():
 # ---------------------------------------------------------------- full sizes
 
 AUTO = mla.KERNEL_AUTO
+# (workload, tolerance kind, sequences x heads sampled, kernel, parts): the
+# sampled sequences are spread from the first to the last (both ends of the
+# XCD-aware work order) and the heads over both 64-head groups; a sample whose
+# oracle run is long is checked in parts, one test each, on the same run
 FULL = [
-    ("dsv2_b32_l2k", "bf16", 4, 4, AUTO),
-    ("dsv2_b32_l2k", "bf16", 4, 4, H128),
-    ("long_b4_l32k", "bf16", 4, 3, AUTO),
-    ("long_b4_l32k", "bf16", 4, 3, H64),
-    ("paged_b64_ragged", "bf16", 4, 3, AUTO),
-    ("fp8_b1_l128k", "fp8", 1, 4, AUTO),
-    ("fp8_b8_l128k", "fp8", 2, 2, AUTO),
+    ("dsv2_b32_l2k", "bf16", 8, 8, AUTO, 1),
+    ("dsv2_b32_l2k", "bf16", 4, 4, H128, 1),
+    ("long_b4_l32k", "bf16", 4, 8, AUTO, 1),
+    ("long_b4_l32k", "bf16", 4, 3, H64, 1),
+    ("paged_b64_ragged", "bf16", 8, 8, AUTO, 2),
+    ("fp8_b1_l128k", "fp8", 1, 8, AUTO, 1),
+    ("fp8_b8_l128k", "fp8", 8, 8, AUTO, 4),
 ]
+FULL_CASES = [(n, k, nb, nh, ker, part, parts) for n, k, nb, nh, ker, parts in FULL
+              for part in range(parts)]
+
+_full_cache = {}
 
 
-@pytest.mark.parametrize("name,kind,nb,nh,kernel", FULL)
-def test_full_size_sampled(name, kind, nb, nh, kernel):
+def _full_run(name, kernel):
+    """inputs and step outputs of one full-size workload, kept for the parts
+    of its sample (one workload at a time)"""
+    key = (name, kernel)
+    if key not in _full_cache:
+        _full_cache.clear()
+        torch.cuda.empty_cache()
+        wl = synth.workload(name)
+        _log(f"{name}: generating inputs")
+        dev = DeviceInputs(synth.make_inputs(wl))
+        _log(f"{name}: running S={wl.num_splits} kernel={kernel}")
+        step = run_step(dev, wl.num_splits, kernel=kernel)
+        _full_cache[key] = (dev, step)
+    return _full_cache[key]
+
+
+@pytest.mark.parametrize("name,kind,nb,nh,kernel,part,parts", FULL_CASES)
+def test_full_size_sampled(name, kind, nb, nh, kernel, part, parts):
     """Each workload at its full size with its stated split count, checked on a
     spread of (b, h) pairs that the oracle computes one by one."""
     wl = synth.workload(name)
-    _log(f"{name}: generating inputs")
-    dev = DeviceInputs(synth.make_inputs(wl))
-    _log(f"{name}: running S={wl.num_splits} kernel={kernel}")
-    step = run_step(dev, wl.num_splits, kernel=kernel)
+    dev, step = _full_run(name, kernel)
     pairs = sample_pairs(wl.batch, wl.heads, nb, nh)
+    pairs = pairs[part * len(pairs) // parts:(part + 1) * len(pairs) // parts]
+    _log(f"{name}: part {part + 1}/{parts}, {len(pairs)} pairs")
     e = check_against_oracle(dev, step, pairs, TOL[kind])
     _log(f"{name}: err o/u/lse = {e}")
     o = step.o.float()
     assert torch.isfinite(o).all()
+
+
+def test_full_size_paged_kernels_agree_on_every_output():
+    """The paged ragged workload at full size: the 64-head and the 128-head
+    decode kernels (separate code, separate work decompositions) give the same
+    o, u and lse for all 64 x 128 (b, h) pairs within the bf16 tolerance."""
+    wl = synth.workload("paged_b64_ragged")
+    dev, a = _full_run("paged_b64_ragged", AUTO)
+    o_a, u_a, l_a = a.o.float().clone(), a.u.float().clone(), a.lse.clone()
+    b = run_step(dev, wl.num_splits, kernel=H128)
+    for x, y, what in ((o_a, b.o.float(), "o"), (u_a, b.u.float(), "u")):
+        err = ((x - y).abs().max() / y.abs().max()).item()
+        _log(f"  {what}: max rel diff {err:.2e}")
+        assert err <= TOL["bf16"], what
+    assert (l_a - b.lse).abs().max().item() <= TOL["bf16"]
+    _full_cache.clear()

@@ -158,3 +158,21 @@ def test_append_places_rows_like_the_decode_row_map():
         others = [i for i in range(n_rows) if i not in written]
         assert np.all(rows[others] == -7.0)
         assert len(written) == (4 if paged else 3)
+
+
+def test_unmapped_page_is_skipped():
+    """A negative block-table entry names no page (the convention the library
+    and the oracle share: a caller that has not mapped a page yet marks it -1):
+    the append of that sequence writes nothing, and the sequences after it are
+    still written."""
+    ps = 64
+    bt = np.array([[0, 1], [-1, 2], [3, -1], [4, 5]], np.int32)
+    pos = np.array([5, 3, 70, 64], np.int32)  # sequences 1 and 2 land on unmapped pages
+    x = np.random.default_rng(10).standard_normal((4, W)).astype(np.float32)
+    rows = np.full((6 * ps, W), -7.0, dtype=np.float32)
+    oracle.cache_append(x[:, :DL], x[:, DL:], "f32", pos, rows, "f32", page_size=ps,
+                        block_table=bt)
+    assert np.array_equal(rows[0 * ps + 5], x[0])
+    assert np.array_equal(rows[5 * ps + 0], x[3])
+    others = [i for i in range(6 * ps) if i not in (5, 5 * ps)]
+    assert np.all(rows[others] == -7.0)

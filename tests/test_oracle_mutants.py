@@ -46,6 +46,19 @@ MUTANTS = {
     "append_bf16_truncates": ("if (dhi < dlo || (dhi == dlo && ((lo >> 16) & 1u))) r = hi;", ""),
     "append_row_off_by_one": (": (int64_t)b * seq_stride + t;", ": (int64_t)b * seq_stride + t + 1;"),
     "append_ignores_capacity": ("if (t < 0 || t >= capacity) continue;", "if (t < 0) continue;"),
+    # absorb and up-projection
+    "absorb_transposed_w_uk": ("out[j] += q * load_elem(w_uk, w_dtype, (h * d_nope + n) * d_latent + j);",
+                               "out[j] += q * load_elem(w_uk, w_dtype, (h * d_latent + j) * d_nope + n);"),
+    "absorb_drops_rope_copy": ("out[d_latent + j] = load_elem(q_rope, q_dtype, bh * d_rope + j);",
+                               "out[d_latent + j] = 0.0;"),
+    "absorb_wrong_query_row": ("const double q = load_elem(q_nope, q_dtype, bh * d_nope + n);",
+                               "const double q = load_elem(q_nope, q_dtype, h * d_nope + n);"),
+    "up_proj_transposed_w_uv": ("acc += load_elem(w_uv, w_dtype, (h * d_v + v) * d_latent + c) * u[bh * d_latent + c];",
+                                "acc += load_elem(w_uv, w_dtype, (h * d_latent + c) * d_v + v) * u[bh * d_latent + c];"),
+    "up_proj_drops_last_latent": ("for (int32_t c = 0; c < d_latent; ++c)\n        acc += load_elem(w_uv",
+                                  "for (int32_t c = 0; c < d_latent - 1; ++c)\n        acc += load_elem(w_uv"),
+    "append_unmapped_page_stops": ("if (page < 0) continue; /* no page mapped */",
+                                   "if (page < 0) break; /* no page mapped */"),
     # decoupled RoPE
     "rope_sign": ("out[bh * d_r + i] = a * c - b * s;", "out[bh * d_r + i] = a * c + b * s;"),
     "rope_frequency_exponent": ("inv_freq[i] = (float)pow(base, -(2.0 * (double)i) / (double)d_r);",
@@ -82,7 +95,11 @@ PIN_CHECKS = [
     rope.test_inverse_frequencies,
     rope.test_position_zero_is_the_identity,
     lambda: rope.test_pairs_keep_their_length(2048),
-    rope.test_matches_the_listing_form,
+    lambda: rope.test_rotation_angle_is_the_binary32_product(131071),
+    rope.test_quarter_turns_of_the_unit_frequency_pair,
+    lambda: rope.test_angles_add(100, 28),
+    pins.test_absorb_q_and_up_proj_outputs_reproduce_the_naive_decode,
+    append.test_unmapped_page_is_skipped,
     lambda: mha.test_matches_library_attention(192, 128),
     mha.test_mla_is_mha_on_rebuilt_keys_and_values,
     mha.test_closed_forms,

@@ -258,6 +258,35 @@ def test_absorb_and_up_proj_calls():
     assert_close(o, np.einsum("hvc,bhc->bhv", p["w_uv"], u))
 
 
+def test_absorb_q_and_up_proj_outputs_reproduce_the_naive_decode():
+    """oracle.absorb_q's output, taken as the query of attention straight over
+    the 576-wide cached rows [c_KV | k_R], and oracle.up_proj applied to the
+    weighted latent sum, give the naive decode that rebuilds each head's keys
+    and values (itself pinned to library SDPA above): absorbing W_UK into the
+    query and applying W_UV after the sum is exact algebra ([V2] §2.3, §4.1),
+    so they agree to rounding.  Widths differ (d_nope != d_latent != d_v) so
+    a transposed weight index reads other elements."""
+    rng = np.random.default_rng(23)
+    B, H, L = 2, 5, 37
+    p = rand_problem(rng, B=B, H=H, L=L, dn=24, dr=8, dl=40, dv=12)
+    o_ref, lse_ref, u_ref = run(p, want_u=True)
+    qa = oracle.absorb_q(p["q_nope"], p["q_rope"], "f64", p["w_uk"], "f64")
+    dn, dr, dl, dv = p["dims"]
+    assert qa.shape == (B, H, dl + dr)
+    u = np.zeros((B, H, dl))
+    lse = np.zeros((B, H))
+    for b in range(B):
+        rows = p["rows"][b * L:(b + 1) * L]
+        s = (rows @ qa[b].T) / math.sqrt(dn + dr)  # [L, H]
+        m = s.max(axis=0)
+        w = np.exp(s - m)
+        u[b] = (w.T @ rows[:, :dl]) / w.sum(axis=0)[:, None]
+        lse[b] = m + np.log(w.sum(axis=0))
+    assert_close(u.reshape(-1, dl), u_ref)
+    assert_close(lse.reshape(-1), lse_ref)
+    assert_close(oracle.up_proj(u, p["w_uv"], "f64").reshape(-1, dv), o_ref)
+
+
 def test_default_scale_is_one_over_sqrt_nope_plus_rope():
     rng = np.random.default_rng(22)
     p = rand_problem(rng)
