@@ -76,7 +76,8 @@ typedef enum {
   MLA_E_SHAPE = 3,       /* dimension outside the compiled geometry */
   MLA_E_ALIGN = 4,       /* a pointer or stride violates the stated alignment */
   MLA_E_HIP = 5,         /* the HIP runtime reported an error at launch */
-  MLA_E_UNSUPPORTED = 6  /* valid request the library does not provide */
+  MLA_E_UNSUPPORTED = 6, /* valid request the library does not provide */
+  MLA_E_SCRATCH = 7      /* request larger than the library's static scratch */
 } mla_status_t;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype_t;
@@ -293,6 +294,33 @@ mla_status_t mla_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void
                             const int32_t* seq_lens, int64_t seq_stride, int32_t max_seq_len,
                             float softmax_scale, void* o, int32_t o_dt, float* lse,
                             void* stream);
+
+/* For callers that cannot allocate: code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc.  mla_decode followed by
+ * mla_combine_up_proj, with the split partials (bf16) and their log-sum-exps
+ * in a device buffer the library owns instead of caller-given u_part /
+ * lse_part.  No call here allocates or frees memory: the buffer is a static
+ * device array of 64 MiB + 256 KiB, one per GPU the library runs on, held
+ * until the process ends; its address on a device is looked up on the first
+ * call made with that device current.
+ *   Limit: B * num_splits * heads <= 65536 rows (e.g. 64 sequences x 8 splits
+ *   x 128 heads); larger requests return MLA_E_SCRATCH before any launch.
+ * Every call on one GPU uses that GPU's single buffer: calls that overlap on
+ * one GPU (other streams, other host threads) race and must be serialised by
+ * the caller; consecutive calls on one stream are ordered.  The decode writes
+ * every partial row it is asked for (u = 0, lse = -inf for an empty range),
+ * so nothing is cleared between calls.
+ * Arguments as mla_decode (q_abs BF16 for BF16 / FP8 caches, F32 for F32;
+ * no q_abs_scale) and mla_combine_up_proj (w_uv BF16, d_v % 16 == 0; o in
+ * o_dt F32 or BF16; u BF16 [B][h][d_latent] and lse fp32 [B][h] optional,
+ * NULL skips them); the same errors, plus MLA_E_SCRATCH, and MLA_E_HIP if
+ * the buffer's address cannot be found. */
+mla_status_t mla_decode_combine_up_proj_noalloc(const mla_dims_t* dims, int32_t B,
+                                                const void* q_abs, int32_t q_abs_dt,
+                                                const mla_cache_t* cache, int32_t num_splits,
+                                                const void* w_uv, int32_t w_dt, void* o,
+                                                int32_t o_dt, void* u, float* lse,
+                                                void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mla_status_str(mla_status_t status);

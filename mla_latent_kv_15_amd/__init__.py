@@ -89,6 +89,10 @@ def lib():
         L.mla_cache_append.restype = C.c_int
         L.mla_cache_append.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp,
                                        C.POINTER(CacheDesc), vp]
+        L.mla_decode_combine_up_proj_noalloc.restype = C.c_int
+        L.mla_decode_combine_up_proj_noalloc.argtypes = [C.POINTER(Dims), i32, vp, i32,
+                                                         C.POINTER(CacheDesc), i32, vp, i32, vp,
+                                                         i32, vp, f32p, vp]
         L.mla_status_str.restype = C.c_char_p
         L.mla_status_str.argtypes = [C.c_int]
         L.mla_version.restype = C.c_int32
@@ -99,7 +103,7 @@ def lib():
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_decode_ex", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
             "mla_absorb_q_rope", "mla_cache_append", "mla_mha_decode", "mla_status_str",
-            "mla_version")
+            "mla_version", "mla_decode_combine_up_proj_noalloc")
 
 
 def status_str(status: int) -> str:
@@ -461,6 +465,34 @@ def mla_combine_up_proj(geo: Geometry, u_part: torch.Tensor, lse_part: torch.Ten
     return _launch("mla_combine_up_proj", (C.byref(d), B, S, _ptr(u_part), dtype_code(u_part),
                                    _ptr(lse_part), _ptr(w_uv), dtype_code(w_uv), _ptr(o),
                                    dtype_code(o), _ptr(u), _ptr(lse), _stream(stream),), (d,), prepare)
+
+
+def mla_decode_combine_up_proj_noalloc(geo: Geometry, q_abs: torch.Tensor, cache: Cache,
+                                       num_splits: int, w_uv: torch.Tensor, o: torch.Tensor,
+                                       u: Optional[torch.Tensor] = None,
+                                       lse: Optional[torch.Tensor] = None, stream=None,
+                                       prepare: bool = False):
+    """mla_decode + mla_combine_up_proj with the split partials in the
+    library's static device scratch (no allocation by anyone): q_abs [B, h,
+    576], w_uv [h, d_v, 512] -> o [B, h, d_v]; optionally u [B, h, 512]
+    (bfloat16) and lse [B, h].  B * num_splits * h <= 65536."""
+    B = int(q_abs.shape[0])
+    H, W = _dims(geo)
+    if u is not None and u.dtype != torch.bfloat16:
+        raise TypeError("the merged u is stored as bfloat16 only")
+    _need("q_abs", q_abs, (B, H, W), _FLOAT)
+    _need("w_uv", w_uv, (H, geo.d_v, geo.d_latent), _FLOAT)
+    _need("o", o, (B, H, geo.d_v), _FLOAT)
+    _need("u", u, (B, H, geo.d_latent), (torch.bfloat16,), optional=True)
+    _need("lse", lse, (B, H), (torch.float32,), optional=True)
+    _need_cache(cache, B, geo)
+    _on_gpu(q_abs, w_uv, o, u, lse, *_cache_tensors(cache))
+    d = geo.c()
+    cd = cache.c()
+    return _launch("mla_decode_combine_up_proj_noalloc",
+                   (C.byref(d), B, _ptr(q_abs), dtype_code(q_abs), C.byref(cd), int(num_splits),
+                    _ptr(w_uv), dtype_code(w_uv), _ptr(o), dtype_code(o), _ptr(u), _ptr(lse),
+                    _stream(stream)), (d, cd), prepare)
 
 
 def split_chunk(max_seq_len: int, num_splits: int) -> int:

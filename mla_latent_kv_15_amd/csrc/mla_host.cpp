@@ -201,6 +201,7 @@ extern "C" const char* mla_status_str(mla_status_t status) {
     case MLA_E_ALIGN: return "pointer or stride misaligned";
     case MLA_E_HIP: return "HIP runtime error at launch";
     case MLA_E_UNSUPPORTED: return "request not provided by this library";
+    case MLA_E_SCRATCH: return "request larger than the library's static scratch";
   }
   return "unknown status";
 }

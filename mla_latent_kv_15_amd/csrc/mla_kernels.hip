@@ -11,6 +11,7 @@
 #include <cmath>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/mla.h"
@@ -2609,15 +2610,10 @@ extern "C" mla_status_t mla_up_proj(const mla_dims_t* dims, int32_t B, const voi
   return MLA_E_DTYPE;
 }
 
-extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_splits,
-                                            const void* u_part, int32_t part_dt,
-                                            const float* lse_part, const void* w_uv, int32_t w_dt,
-                                            void* o, int32_t o_dt, void* u, float* lse,
-                                            void* stream) {
-  mla_status_t st = check_combine_up_proj(dims, B, num_splits, u_part, part_dt, lse_part, w_uv,
-                                          w_dt, o, o_dt, u);
-  if (st != MLA_OK || B == 0) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+static mla_status_t combine_up_launch(const mla_dims_t* dims, int32_t B, int32_t num_splits,
+                                      const void* u_part, int32_t part_dt, const float* lse_part,
+                                      const void* w_uv, void* o, int32_t o_dt, void* u, float* lse,
+                                      hipStream_t s) {
   const int H = dims->heads;
   // sequences per workgroup: 16, halved while the grid would not cover the
   // 256 CUs (small batches)
@@ -2647,6 +2643,86 @@ extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, i
   MLA_CU(MLA_F32, MLA_F32)
 #undef MLA_CU
   return MLA_E_DTYPE;
+}
+
+extern "C" mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_splits,
+                                            const void* u_part, int32_t part_dt,
+                                            const float* lse_part, const void* w_uv, int32_t w_dt,
+                                            void* o, int32_t o_dt, void* u, float* lse,
+                                            void* stream) {
+  mla_status_t st = check_combine_up_proj(dims, B, num_splits, u_part, part_dt, lse_part, w_uv,
+                                          w_dt, o, o_dt, u);
+  if (st != MLA_OK || B == 0) return st;
+  return combine_up_launch(dims, B, num_splits, u_part, part_dt, lse_part, w_uv, o, o_dt, u, lse,
+                           static_cast<hipStream_t>(stream));
+}
+
+// ================================================================ no-allocation decode + tail
+//
+// Callers that cannot allocate (code under HIP graph capture, serving loops
+// that forbid hipMalloc) get the split partials in a buffer the library owns:
+// a file-scope device array, one copy per GPU, held until the process ends.
+// In host code `scratch` only names the symbol; its device address on the
+// current GPU is looked up once per device (hipGetSymbolAddress) and only that
+// address is passed to kernels.  Layout: bf16 partials [rows][512], then the
+// fp32 log-sum-exps [rows], rows = B * num_splits * heads <= kScratchRows.
+
+constexpr int64_t kScratchRows = 65536;
+constexpr int64_t kScratchPartBytes = kScratchRows * kDLatent * 2;  // 64 MiB
+constexpr int64_t kScratchBytes = kScratchPartBytes + kScratchRows * 4;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// device address of this GPU's scratch array, looked up on the first call on
+// the device (with that device current); nullptr if the lookup failed
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&sl] {
+    void* p = nullptr;
+    sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (sl.err == hipSuccess) sl.ptr = p;
+  });
+  return sl.err == hipSuccess ? sl.ptr : nullptr;
+}
+}  // namespace
+
+extern "C" mla_status_t mla_decode_combine_up_proj_noalloc(
+    const mla_dims_t* dims, int32_t B, const void* q_abs, int32_t q_abs_dt,
+    const mla_cache_t* cache, int32_t num_splits, const void* w_uv, int32_t w_dt, void* o,
+    int32_t o_dt, void* u, float* lse, void* stream) {
+  // the partial buffers are the library's: validate with a stand-in address
+  // (any 256-byte aligned non-null value) and substitute the real one after
+  const void* stand_in = reinterpret_cast<const void*>(static_cast<uintptr_t>(256));
+  mla_status_t st = check_decode(dims, B, q_abs, q_abs_dt, nullptr, cache, num_splits, stand_in,
+                                 MLA_BF16, static_cast<const float*>(stand_in));
+  if (st != MLA_OK) return st;
+  st = check_combine_up_proj(dims, B, num_splits, stand_in, MLA_BF16,
+                             static_cast<const float*>(stand_in), w_uv, w_dt, o, o_dt, u);
+  if (st != MLA_OK || B == 0) return st;
+  if (static_cast<int64_t>(B) * num_splits * dims->heads > kScratchRows) return MLA_E_SCRATCH;
+  uint8_t* base = static_cast<uint8_t*>(scratch_on_current_device());
+  if (!base) return MLA_E_HIP;
+  void* u_part = base;
+  float* lse_part = reinterpret_cast<float*>(base + kScratchPartBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the decode writes every (sequence, split, head) row it is asked for (an
+  // empty range writes u = 0 and lse = -inf), so nothing needs clearing
+  st = decode_launch(dims, B, 1, q_abs, cache, num_splits, u_part, MLA_BF16, lse_part,
+                     MLA_KERNEL_AUTO, s);
+  if (st != MLA_OK) return st;
+  return combine_up_launch(dims, B, num_splits, u_part, MLA_BF16, lse_part, w_uv, o, o_dt, u, lse,
+                           s);
 }
 
 extern "C" mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, const void* c_kv,

@@ -14,7 +14,7 @@ import mla_latent_kv_15_amd as mla
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla.h")
 
-OK, E_ARG, E_DTYPE, E_SHAPE, E_ALIGN, E_HIP, E_UNSUP = range(7)
+OK, E_ARG, E_DTYPE, E_SHAPE, E_ALIGN, E_HIP, E_UNSUP, E_SCRATCH = range(8)
 F32, BF16, FP8 = mla.MLA_F32, mla.MLA_BF16, mla.MLA_FP8_E4M3
 P = 0x10000  # a fake, 64 KiB-aligned "device" address: never dereferenced
 
@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert mla.status_str(s) and mla.status_str(s) != "unknown status"
     assert mla.status_str(99) == "unknown status"
     assert mla.lib().mla_version() >= 100
@@ -269,3 +269,30 @@ def test_decode_ex_kernel_choice_validation():
     assert dx(mla.KERNEL_H128, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP
     assert dx(mla.KERNEL_H64, ql=0) == E_ARG
     assert dx(mla.KERNEL_H64, ql=17) == E_ARG
+
+
+def noalloc(d=None, B=2, q=P, q_dt=BF16, c=None, S=4, w=P, w_dt=BF16, o=P, o_dt=BF16, u=None,
+            lse=None):
+    d = d or dims()
+    c = c or cache()
+    return mla.lib().mla_decode_combine_up_proj_noalloc(C.byref(d), B, q, q_dt, C.byref(c), S, w,
+                                                        w_dt, o, o_dt, u, lse, None)
+
+
+def test_noalloc_validation_before_any_launch():
+    """The no-allocation decode + tail checks its arguments like mla_decode and
+    mla_combine_up_proj, and refuses a request beyond its static scratch (B *
+    num_splits * heads > 65536 rows) before touching the device."""
+    assert noalloc(B=0) == OK
+    assert noalloc(q=None) == E_ARG
+    assert noalloc(w=None) == E_ARG
+    assert noalloc(o=None) == E_ARG
+    assert noalloc(S=0) == E_ARG
+    assert noalloc(S=1025) == E_ARG
+    assert noalloc(w_dt=F32) == E_DTYPE
+    assert noalloc(o_dt=FP8) == E_DTYPE
+    assert noalloc(d=dims(dv=120)) == E_SHAPE
+    assert noalloc(w=P + 8) == E_ALIGN
+    assert noalloc(B=65, S=8) == E_SCRATCH          # 66,560 rows
+    assert noalloc(B=1, S=1024, d=dims(h=128)) == E_SCRATCH  # 131,072 rows
+    assert noalloc(B=513, S=1) == E_SCRATCH
