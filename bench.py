@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--mha", action="store_true",
                     help="the MHA baseline instead: per-head bf16 K/V cache at the geometry of "
                          "--workload (batch, heads, lengths; head dim 128), mla_mha_decode")
+    ap.add_argument("--gqa", type=int, default=0, metavar="KV_HEADS",
+                    help="with --mha: grouped-query attention with this many key/value heads "
+                         "(mla_gqa_decode); 0 = one per query head")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -230,10 +233,12 @@ def multi_token_bench(args, wl, dev, reps, R, S, act, part, out, cache_bytes):
 
 
 def mha_baseline(args):
-    """Multi-head attention decode over a per-head K/V cache (what MLA's latent
-    cache replaces) at the batch, heads and lengths of --workload: one launch
-    of mla_mha_decode per step.  The cache (2 x h x 128 bf16 per token) is far
-    larger than the 256 MB Infinity Cache, so one copy is streamed from HBM."""
+    """Multi-head (or, with --gqa N, grouped-query with N key/value heads)
+    attention decode over a per-head K/V cache -- what MLA's latent cache
+    replaces -- at the batch, heads and lengths of --workload: one launch of
+    mla_mha_decode / mla_gqa_decode per step.  The cache (2 x h_kv x 128 bf16
+    per token) is streamed from HBM (replicas rotated when one copy would fit
+    the 256 MB Infinity Cache)."""
     import torch
 
     import mla_latent_kv_15_amd as mla
@@ -242,52 +247,59 @@ def mha_baseline(args):
     wl = synth.workload(args.workload)
     lens = synth.workloads.sequence_lengths(wl)
     B, H, D = wl.batch, wl.heads, 128
+    Hkv = args.gqa or H
+    if H % Hkv:
+        sys.exit(f"--gqa {Hkv} does not divide {H} heads")
     L = int(lens.max())
-    print(f"[bench] MHA baseline at {wl.name}: B={B} h={H} L<={L}", file=sys.stderr, flush=True)
+    kind = "MHA" if Hkv == H else f"GQA ({Hkv} key/value heads)"
+    print(f"[bench] {kind} baseline at {wl.name}: B={B} h={H} L<={L}", file=sys.stderr, flush=True)
     g = torch.Generator(device="cuda").manual_seed(wl.seed)
     q = torch.randn(B, H, D, device="cuda", generator=g).to(torch.bfloat16)
-    k = torch.empty(B, H, L, D, dtype=torch.bfloat16, device="cuda")
-    v = torch.empty_like(k)
-    for b in range(B):  # per sequence, to bound the fp32 temporaries
-        k[b] = torch.randn(H, L, D, device="cuda", generator=g).to(torch.bfloat16)
-        v[b] = torch.randn(H, L, D, device="cuda", generator=g).to(torch.bfloat16)
+    kv_bytes = int(lens.astype("int64").sum()) * Hkv * D * 2 * 2
+    R = max(1, math.ceil(args.replica_bytes / (B * Hkv * L * D * 2 * 2)))
+    reps = []
+    for _ in range(R):
+        k = torch.empty(B, Hkv, L, D, dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        for b in range(B):  # per sequence, to bound the fp32 temporaries
+            k[b] = torch.randn(Hkv, L, D, device="cuda", generator=g).to(torch.bfloat16)
+            v[b] = torch.randn(Hkv, L, D, device="cuda", generator=g).to(torch.bfloat16)
+        reps.append((k, v))
     seq = torch.from_numpy(lens.astype("int32")).cuda()
     o = torch.empty(B, H, D, dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    calls = [mla.mla_gqa_decode(q, k, v, seq, L, o, stream=stream, prepare=True)
+             for k, v in reps]
 
-    def one():
-        mla.mla_mha_decode(q, k, v, seq, L, o, stream=stream)
-
-    for _ in range(args.warmup):
-        one()
+    for i in range(args.warmup):
+        calls[i % R]()
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one()
+    for i in range(args.steps):
+        ev[i].record(stream)
+        calls[i % R]()
+    ev[args.steps].record(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        one()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_k = e0.elapsed_time(e1) / args.steps * 1e-3
-    kv_bytes = int(lens.astype("int64").sum()) * H * D * 2 * 2
+    us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)]
+    st = launch_stats(us)
+    t_k = st["mean"] * 1e-6
     mla_bytes = synth.cache_bytes(wl, lens)
     achieved = kv_bytes / t_k / 1e9
+    name = "MHA" if Hkv == H else "GQA"
     rec = {
-        "metric": "MHA baseline decode tokens/s + K/V HBM GB/s (% of MI355X peak), 1 GPU",
+        "metric": f"{name} baseline decode tokens/s + K/V HBM GB/s (% of MI355X peak), 1 GPU",
         "value": B / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) q, K, V)",
-        "config": {"workload": f"mha_baseline_{wl.name}", "batch": B, "heads": H, "d_head": D,
-                   "seq_len": L, "cache": "bf16 per-head K and V, head-major",
-                   "parallelism": "none (1 GPU)"},
+        "config": {"workload": f"{name.lower()}_baseline_{wl.name}", "batch": B, "heads": H,
+                   "kv_heads": Hkv, "d_head": D, "seq_len": L, "replicas": R,
+                   "cache": "bf16 per-head K and V, head-major", "parallelism": "none (1 GPU)"},
         "kv_cache_bytes": kv_bytes, "mla_cache_bytes_same_tokens": mla_bytes,
         "cache_ratio": kv_bytes / mla_bytes,
-        "kernel_us_mean": {"mla_mha_decode": t_k * 1e6},
-        "roofline": {"kernel": "mla_mha_decode", "bound": "hbm", "achieved": achieved,
+        "kernel_us": {"mla_gqa_decode": st},
+        "roofline": {"kernel": "mla_gqa_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None, "algorithmic_bytes_per_launch": kv_bytes},
         "cpu_baseline": None,

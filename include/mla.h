@@ -104,6 +104,15 @@ typedef struct {
  *   block_table[b*max_pages + t/64]*64 + t%64  (pages of 64 rows; the DeepSeek
  * V2 page §1.2 / §3.3 lists paged KV memory as the companion optimisation).
  *
+ * Ring (ring == 1, contiguous only; [V2] §4.1 keeps the KV cache in a ring
+ * buffer so that it can grow): the seq_stride rows of sequence b are a ring of
+ * capacity C = seq_stride and token t sits in row b*seq_stride + t % C, so
+ * the ring holds the last min(L_b, C) tokens; those are the ones attended
+ * (a window of the last C tokens once L_b > C; seq_lens and max_seq_len may
+ * then exceed seq_stride).  Attention does not depend on the order of the
+ * tokens, so the decode reads the ring's first min(L_b, C) rows.
+ * mla_cache_ring_grow moves a ring into a larger one.
+ *
  * rows must be 16-byte aligned.  An FP8_E4M3 cache carries one fp32 factor per
  * row in row_scale (same row index): value = decode(code) * row_scale[row]. */
 typedef struct {
@@ -116,6 +125,7 @@ typedef struct {
   int32_t max_pages;
   const int32_t* seq_lens;     /* device, [B], each in [0, max_seq_len] */
   int32_t max_seq_len;         /* host-side bound on every seq_lens[b] */
+  int32_t ring;                /* 0, or 1: contiguous rows used as a ring (above) */
 } mla_cache_t;
 
 /* Absorb W_UK into the query (DeepSeek V2 page §2.3 and §4.1):
@@ -184,7 +194,8 @@ mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
  * sequences, so mla_combine / mla_combine_up_proj over B*q_len finish the
  * step.  Split ranges as mla_decode's (from max_seq_len).  1 <= q_len <= 16
  * (else MLA_E_ARG); BF16 and FP8 caches (an F32 cache with q_len > 1 returns
- * MLA_E_UNSUPPORTED).  Other arguments and errors as mla_decode (no
+ * MLA_E_UNSUPPORTED, and so does a ring cache with q_len > 1: the windows of
+ * the earlier query tokens reach tokens the ring has overwritten).  Other arguments and errors as mla_decode (no
  * q_abs_scale). */
 mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
                               const void* q_abs, int32_t q_abs_dt, const mla_cache_t* cache,
@@ -266,7 +277,8 @@ mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_
  * c_kv [B][d_latent] and k_r [B][d_rope] in src_dt (F32 or BF16), finite;
  * positions: device int32 [B].  A position < 0 or past the capacity, or a
  * negative page id in block_table, skips the sequence; no other row is
- * written.  cache->rows (and row_scale for FP8) are written through: they must
+ * written.  A ring cache (ring == 1) has no capacity limit: token t goes to
+ * row b*seq_stride + t % seq_stride, over the token C positions back.  cache->rows (and row_scale for FP8) are written through: they must
  * be writable; seq_lens and max_seq_len are neither read nor changed (the
  * caller advances its lengths).  The cache must satisfy mla_decode's layout
  * rules (16-byte aligned rows, page_size 0 or 64).  Errors: MLA_E_ARG for
@@ -275,6 +287,20 @@ mla_status_t mla_combine_up_proj(const mla_dims_t* dims, int32_t B, int32_t num_
 mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, const void* c_kv,
                               const void* k_r, int32_t src_dt, const int32_t* positions,
                               const mla_cache_t* cache, void* stream);
+
+/* Grow (or shrink) ring caches ([V2] §4.1: the ring buffer allows the cache
+ * to grow): for every sequence b, the tokens its ring in `src` holds, the last
+ * k = min(L_b, src.seq_stride, dst.seq_stride) of them (L_b = min(seq_lens[b],
+ * max_seq_len) of src), are copied with their row factors into the ring of
+ * `dst`, token t to row b*dst.seq_stride + t % dst.seq_stride.  Nothing else
+ * in dst is written.  A ring grown before it wrapped (L_b <= src.seq_stride)
+ * keeps every token; the caller then sets dst's lengths (the same L_b) and
+ * appends into dst.  Both caches: ring == 1, contiguous, the same dtype
+ * (FP8: both carry row_scale), 16-byte aligned rows, and must not overlap.
+ * Errors: MLA_E_ARG (pointers, not rings, a paged cache), MLA_E_DTYPE
+ * (dtypes differ), MLA_E_ALIGN. */
+mla_status_t mla_cache_ring_grow(int32_t B, const mla_cache_t* src, const mla_cache_t* dst,
+                                 void* stream);
 
 /* Multi-head attention decode over a full per-head K/V cache: the baseline
  * the latent cache replaces ([LAT] §2.1 softmax(q k^T / sqrt(d_k)) v; [V2]
@@ -321,6 +347,20 @@ mla_status_t mla_decode_combine_up_proj_noalloc(const mla_dims_t* dims, int32_t 
                                                 const void* w_uv, int32_t w_dt, void* o,
                                                 int32_t o_dt, void* u, float* lse,
                                                 void* stream);
+
+/* Grouped-query attention decode, the other baseline ([LAT] §2.2: the query
+ * heads are split into groups and each group shares one key/value head; [V2]
+ * §1.2 lists MQA/GQA next to MLA).  The heads query heads form kv_heads
+ * contiguous groups of G = heads / kv_heads: query head i reads key/value head
+ * i / G.  As mla_mha_decode otherwise, with k_cache and v_cache
+ * [B][kv_heads][seq_stride][d_head]; kv_heads == heads is mla_mha_decode and
+ * kv_heads == 1 multi-query attention.  kv_heads < 1 or not dividing heads:
+ * MLA_E_ARG. */
+mla_status_t mla_gqa_decode(int32_t B, int32_t heads, int32_t kv_heads, int32_t d_head,
+                            const void* q, const void* k_cache, const void* v_cache, int32_t dt,
+                            const int32_t* seq_lens, int64_t seq_stride, int32_t max_seq_len,
+                            float softmax_scale, void* o, int32_t o_dt, float* lse,
+                            void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mla_status_str(mla_status_t status);

@@ -47,7 +47,7 @@ class CacheDesc(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("rows", C.c_void_p), ("row_scale", C.c_void_p),
                 ("page_size", C.c_int32), ("seq_stride", C.c_int64),
                 ("block_table", C.c_void_p), ("max_pages", C.c_int32),
-                ("seq_lens", C.c_void_p), ("max_seq_len", C.c_int32)]
+                ("seq_lens", C.c_void_p), ("max_seq_len", C.c_int32), ("ring", C.c_int32)]
 
 
 _lib = None
@@ -86,6 +86,9 @@ def lib():
         L.mla_mha_decode.restype = C.c_int
         L.mla_mha_decode.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, C.c_int64, i32,
                                      C.c_float, vp, i32, f32p, vp]
+        L.mla_gqa_decode.restype = C.c_int
+        L.mla_gqa_decode.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp, C.c_int64, i32,
+                                     C.c_float, vp, i32, f32p, vp]
         L.mla_cache_append.restype = C.c_int
         L.mla_cache_append.argtypes = [C.POINTER(Dims), i32, vp, vp, i32, vp,
                                        C.POINTER(CacheDesc), vp]
@@ -93,6 +96,8 @@ def lib():
         L.mla_decode_combine_up_proj_noalloc.argtypes = [C.POINTER(Dims), i32, vp, i32,
                                                          C.POINTER(CacheDesc), i32, vp, i32, vp,
                                                          i32, vp, f32p, vp]
+        L.mla_cache_ring_grow.restype = C.c_int
+        L.mla_cache_ring_grow.argtypes = [i32, C.POINTER(CacheDesc), C.POINTER(CacheDesc), vp]
         L.mla_status_str.restype = C.c_char_p
         L.mla_status_str.argtypes = [C.c_int]
         L.mla_version.restype = C.c_int32
@@ -103,7 +108,8 @@ def lib():
 
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_decode_ex", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
             "mla_absorb_q_rope", "mla_cache_append", "mla_mha_decode", "mla_status_str",
-            "mla_version", "mla_decode_combine_up_proj_noalloc")
+            "mla_version", "mla_decode_combine_up_proj_noalloc", "mla_cache_ring_grow",
+            "mla_gqa_decode")
 
 
 def status_str(status: int) -> str:
@@ -188,7 +194,13 @@ def _need_cache(cache: "Cache", B: int, geo: "Geometry") -> None:
         raise ValueError("cache.max_seq_len must be >= 0")
     if dtype_code(r) == MLA_FP8_E4M3:
         _need("cache.row_scale", cache.row_scale, (n,), (torch.float32,))
-    if cache.page_size:
+    if cache.ring:
+        if cache.page_size:
+            raise ValueError("a ring cache is contiguous (page_size 0)")
+        if int(cache.seq_stride) < 1 or B * int(cache.seq_stride) > n:
+            raise ValueError(f"cache.rows holds {n} rows, B={B} rings of {cache.seq_stride} "
+                             f"need {B * cache.seq_stride}")
+    elif cache.page_size:
         bt = cache.block_table
         if not isinstance(bt, torch.Tensor) or bt.dim() != 2:
             raise ValueError("a paged cache needs block_table [B, max_pages]")
@@ -236,12 +248,13 @@ class Cache:
     block_table: Optional[torch.Tensor] = None
     seq_stride: int = 0
     page_size: int = 0
+    ring: bool = False  # contiguous rows used as rings of seq_stride slots
 
     def c(self) -> CacheDesc:
         mp = 0 if self.block_table is None else int(self.block_table.shape[1])
         return CacheDesc(dtype_code(self.rows), _ptr(self.rows), _ptr(self.row_scale),
                          int(self.page_size), int(self.seq_stride), _ptr(self.block_table), mp,
-                         _ptr(self.seq_lens), int(self.max_seq_len))
+                         _ptr(self.seq_lens), int(self.max_seq_len), int(bool(self.ring)))
 
 
 class Call:
@@ -289,6 +302,34 @@ def mla_absorb_q_rope(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor,
                                  _ptr(q_abs), dtype_code(q_abs), _stream(stream),), (d,), prepare)
 
 
+def mla_gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   seq_lens: torch.Tensor, max_seq_len: int, o: torch.Tensor,
+                   lse: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
+                   stream=None, prepare: bool = False):
+    """Grouped-query baseline decode: q [B, h, 128], k_cache / v_cache [B, h_kv,
+    stride, 128] (bfloat16, h a multiple of h_kv; query head i reads key/value
+    head i // (h / h_kv)), seq_lens int32 [B] on the device; o [B, h, 128]."""
+    B, H, D = (int(x) for x in q.shape)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, h_kv, stride, d_head]")
+    Hkv, stride = int(k_cache.shape[1]), int(k_cache.shape[2])
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{Hkv} key/value heads do not divide {H} query heads")
+    _need("q", q, (B, H, D), _FLOAT)
+    _need("k_cache", k_cache, (B, Hkv, stride, D), (q.dtype,))
+    _need("v_cache", v_cache, (B, Hkv, stride, D), (q.dtype,))
+    _need("seq_lens", seq_lens, (B,), (torch.int32,))
+    _need("o", o, (B, H, D), _FLOAT)
+    _need("lse", lse, (B, H), (torch.float32,), optional=True)
+    if not 0 <= int(max_seq_len) <= stride:
+        raise ValueError("max_seq_len must lie in [0, stride]")
+    _on_gpu(q, k_cache, v_cache, seq_lens, o, lse)
+    return _launch("mla_gqa_decode", (B, H, Hkv, D, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      dtype_code(q), _ptr(seq_lens), stride, int(max_seq_len),
+                                      float(softmax_scale), _ptr(o), dtype_code(o), _ptr(lse),
+                                      _stream(stream)), (), prepare)
+
+
 def mla_mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    seq_lens: torch.Tensor, max_seq_len: int, o: torch.Tensor,
                    lse: Optional[torch.Tensor] = None, softmax_scale: float = 0.0,
@@ -296,7 +337,7 @@ def mla_mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     """MHA baseline decode: q [B, h, 128], k_cache / v_cache [B, h, stride, 128]
     (bfloat16), seq_lens int32 [B] on the device; o [B, h, 128]."""
     B, H, D = (int(x) for x in q.shape)
-    if k_cache.dim() != 4:
+    if k_cache.dim() != 4 or int(k_cache.shape[1]) != H:
         raise ValueError("k_cache must be [B, h, stride, d_head]")
     stride = int(k_cache.shape[2])
     _need("q", q, (B, H, D), _FLOAT)
@@ -308,10 +349,10 @@ def mla_mha_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     if not 0 <= int(max_seq_len) <= stride:
         raise ValueError("max_seq_len must lie in [0, stride]")
     _on_gpu(q, k_cache, v_cache, seq_lens, o, lse)
-    return _launch("mla_mha_decode", (B, H, D, _ptr(q), _ptr(k_cache), _ptr(v_cache), dtype_code(q),
-                              _ptr(seq_lens), stride, int(max_seq_len),
-                              float(softmax_scale), _ptr(o), dtype_code(o), _ptr(lse),
-                              _stream(stream),), (), prepare)
+    return _launch("mla_mha_decode", (B, H, D, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      dtype_code(q), _ptr(seq_lens), stride, int(max_seq_len),
+                                      float(softmax_scale), _ptr(o), dtype_code(o), _ptr(lse),
+                                      _stream(stream)), (), prepare)
 
 
 def mla_cache_append(geo: Geometry, c_kv: torch.Tensor, k_r: torch.Tensor,
@@ -329,6 +370,25 @@ def mla_cache_append(geo: Geometry, c_kv: torch.Tensor, k_r: torch.Tensor,
     cd = cache.c()
     return _launch("mla_cache_append", (C.byref(d), B, _ptr(c_kv), _ptr(k_r), dtype_code(c_kv),
                                 _ptr(positions), C.byref(cd), _stream(stream),), (d, cd), prepare)
+
+
+def mla_cache_ring_grow(geo: Geometry, src: Cache, dst: Cache, stream=None,
+                        prepare: bool = False):
+    """Move every sequence's live window from the ring cache `src` into the
+    ring cache `dst` (token t to row t % dst.seq_stride); lengths from src."""
+    B = int(src.seq_lens.shape[0])
+    for name, c in (("src", src), ("dst", dst)):
+        if not c.ring:
+            raise ValueError(f"{name} must be a ring cache")
+        _need_cache(c, B, geo) if c is src else _need_cache(
+            Cache(rows=c.rows, seq_lens=src.seq_lens, max_seq_len=0, row_scale=c.row_scale,
+                  seq_stride=c.seq_stride, ring=True), B, geo)
+    if src.rows.dtype != dst.rows.dtype:
+        raise TypeError("src and dst rings must have the same dtype")
+    _on_gpu(*_cache_tensors(src), *_cache_tensors(dst))
+    cs, cd = src.c(), dst.c()
+    return _launch("mla_cache_ring_grow", (B, C.byref(cs), C.byref(cd), _stream(stream)),
+                   (cs, cd), prepare)
 
 
 def mla_absorb_q(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor,

@@ -70,6 +70,8 @@ mla_status_t check_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
     return MLA_E_ARG;
   if (cache->max_seq_len < 0) return MLA_E_ARG;
   if (cache->page_size != 0 && cache->page_size != kPageSize) return MLA_E_SHAPE;
+  if (cache->ring != 0 && cache->ring != 1) return MLA_E_ARG;
+  if (cache->ring && cache->page_size != 0) return MLA_E_ARG;
   if (B == 0) return MLA_OK;
   if (!q_abs || !u_part || !lse_part || !cache->rows || !cache->seq_lens) return MLA_E_ARG;
   if (part_dt == MLA_FP8_E4M3) return MLA_E_DTYPE;
@@ -90,7 +92,8 @@ mla_status_t check_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
     return MLA_E_ARG;
   }
   if (cache->page_size == 0) {
-    if (cache->seq_stride < cache->max_seq_len) return MLA_E_ARG;
+    // a ring holds the last seq_stride tokens: lengths may exceed it
+    if (cache->seq_stride < (cache->ring ? 1 : cache->max_seq_len)) return MLA_E_ARG;
   } else {
     if (!cache->block_table || cache->max_pages < 1) return MLA_E_ARG;
     const int64_t need = (static_cast<int64_t>(cache->max_seq_len) + kPageSize - 1) / kPageSize;
@@ -157,6 +160,8 @@ mla_status_t check_cache_append(const mla_dims_t* dims, int32_t B, const void* c
   if (!cache || B < 0) return MLA_E_ARG;
   if (!valid_dtype(src_dt) || !valid_dtype(cache->dtype)) return MLA_E_ARG;
   if (cache->page_size != 0 && cache->page_size != kPageSize) return MLA_E_SHAPE;
+  if (cache->ring != 0 && cache->ring != 1) return MLA_E_ARG;
+  if (cache->ring && cache->page_size != 0) return MLA_E_ARG;
   if (B == 0) return MLA_OK;
   if (!c_kv || !k_r || !positions || !cache->rows) return MLA_E_ARG;
   if (src_dt == MLA_FP8_E4M3) return MLA_E_DTYPE;
@@ -171,6 +176,21 @@ mla_status_t check_cache_append(const mla_dims_t* dims, int32_t B, const void* c
     if (!cache->block_table || cache->max_pages < 1) return MLA_E_ARG;
   }
   if (!aligned(cache->rows, 16)) return MLA_E_ALIGN;
+  return MLA_OK;
+}
+
+mla_status_t check_ring_grow(int32_t B, const mla_cache_t* src, const mla_cache_t* dst) {
+  if (!src || !dst || B < 0) return MLA_E_ARG;
+  if (src->ring != 1 || dst->ring != 1 || src->page_size != 0 || dst->page_size != 0)
+    return MLA_E_ARG;
+  if (src->seq_stride < 1 || dst->seq_stride < 1 || src->max_seq_len < 0) return MLA_E_ARG;
+  if (!valid_dtype(src->dtype) || !valid_dtype(dst->dtype)) return MLA_E_ARG;
+  if (src->dtype != dst->dtype) return MLA_E_DTYPE;
+  if (B == 0) return MLA_OK;
+  if (!src->rows || !dst->rows || !src->seq_lens) return MLA_E_ARG;
+  const bool fp8 = src->dtype == MLA_FP8_E4M3;
+  if (fp8 != (src->row_scale != nullptr) || fp8 != (dst->row_scale != nullptr)) return MLA_E_ARG;
+  if (!aligned(src->rows, 16) || !aligned(dst->rows, 16)) return MLA_E_ALIGN;
   return MLA_OK;
 }
 

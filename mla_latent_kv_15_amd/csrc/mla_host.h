@@ -60,6 +60,8 @@ mla_status_t check_cache_append(const mla_dims_t* dims, int32_t B, const void* c
                                 const void* k_r, int32_t src_dt, const int32_t* positions,
                                 const mla_cache_t* cache);
 
+mla_status_t check_ring_grow(int32_t B, const mla_cache_t* src, const mla_cache_t* dst);
+
 mla_status_t check_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void* q,
                               const void* k_cache, const void* v_cache, int32_t dt,
                               const int32_t* seq_lens, int64_t seq_stride, int32_t max_seq_len,

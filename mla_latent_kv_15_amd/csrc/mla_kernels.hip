@@ -146,7 +146,18 @@ struct DecodeParams {
   float scale_log2;
   void* u_part;
   float* lse_part;
+  int32_t ring;  // contiguous rows used as a ring of seq_stride slots
 };
+
+// Tokens of sequence b that the decode attends: its length, clamped to the
+// host bound; a ring of C slots holds (and attends) only the last C, which
+// sit in its first min(L, C) rows -- attention does not depend on their order.
+__device__ inline int attended_len(const int32_t* seq_lens, int b, int max_seq_len,
+                                   int ring, int64_t seq_stride) {
+  int L = min(max(seq_lens[b], 0), max_seq_len);
+  if (ring) L = static_cast<int>(min(static_cast<int64_t>(L), seq_stride));
+  return L;
+}
 
 __device__ inline uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
@@ -282,7 +293,8 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
 
   // query token qj of QL new tokens (the last QL cached rows) sees the cached
   // rows up to and including its own: the first L - (QL - 1 - qj)
-  const int L = max(min(max(P.seq_lens[b], 0), P.max_seq_len) - (P.QL - 1 - qj), 0);
+  const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
+                        (P.QL - 1 - qj), 0);
   const int t_begin = p * P.chunk;
   const int t_end = min(t_begin + P.chunk, L);
   const int64_t row_base = (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase;
@@ -933,7 +945,8 @@ void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table)
   const int hl = lane & 31, g = lane >> 5;
   const int hw = hg * kH128 + wave * kHeadsPerWave;  // first head of this wave
 
-  const int L = max(min(max(P.seq_lens[b], 0), P.max_seq_len) - (P.QL - 1 - qj), 0);
+  const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
+                        (P.QL - 1 - qj), 0);
   const int t_begin = p * P.chunk;
   const int t_end = min(t_begin + P.chunk, L);
   const int64_t row_base = (static_cast<int64_t>(bj) * P.S + p) * P.H + hw;
@@ -1309,6 +1322,7 @@ struct DecodeF32Params {
   float scale;
   void* u_part;
   float* lse_part;
+  int32_t ring;
 };
 
 __device__ inline int64_t token_row(const DecodeF32Params& P, int b, int t) {
@@ -1350,7 +1364,7 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(DecodeF32Params
   const int p = (blockIdx.x / P.H) % P.S;
   const int b = blockIdx.x / (P.H * P.S);
   const int tid = threadIdx.x;
-  const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
+  const int L = attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride);
   const int t_begin = p * P.chunk;
   const int t_end = min(t_begin + P.chunk, L);
   const int64_t out_row = (static_cast<int64_t>(b) * P.S + p) * P.H + h;
@@ -2154,11 +2168,14 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   }
 }
 
-// ================================================================ MHA baseline decode
+// ================================================================ MHA / GQA baseline decode
 //
-// Multi-head attention decode over a full per-head bf16 K/V cache (head-major
-// [B][h][seq_stride][128]), the baseline the latent cache replaces.  One
-// workgroup of 4 waves per (b, head); wave w streams a contiguous quarter of
+// Multi-head (and grouped-query) attention decode over a full bf16 K/V cache
+// (head-major [B][h_kv][seq_stride][128]), the baselines the latent cache
+// replaces.  Query head h reads key/value head h / G (G = h / h_kv query heads
+// per group); the G workgroups of a group are adjacent in the work order and
+// so run on one XCD, where its L2 serves the K/V rows to all of them after one
+// HBM read.  One workgroup of 4 waves per (b, query head); wave w streams a contiguous quarter of
 // the tokens with its own online softmax.  Per step a wave takes 16 tokens:
 // lane group g (16 lanes) owns tokens 4u + g, lane k of a group holds
 // elements 8k..8k+7 of a key and a value row (16-byte loads, 256 contiguous
@@ -2174,17 +2191,19 @@ template <int O_DT>
 __global__ __launch_bounds__(kMhaThreads) void mha_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, int64_t seq_stride, int32_t max_seq_len, int H,
-    float scale_log2, void* o, float* lse) {
+    int G, float scale_log2, void* o, float* lse) {
   __shared__ float red_m[4], red_l[4];
   __shared__ __attribute__((aligned(16))) float red_acc[4][kMhaD];
-  const int bh = blockIdx.x;
+  // work id (b, query head): consecutive ids, one group's heads, on one XCD
+  const int bh = G > 1 ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
   const int b = bh / H;
+  const int kv = b * (H / G) + (bh % H) / G;  // (b, key/value head) row block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, k = lane & 15;
   const int L = min(max(seq_lens[b], 0), max_seq_len);
   const int chunk = ((L + 3) / 4 + 15) & ~15;  // tokens per wave, a multiple of 16
   const int t0 = min(wave * chunk, L), t1 = min(t0 + chunk, L);
-  const int64_t rowbase = static_cast<int64_t>(bh) * seq_stride;
+  const int64_t rowbase = static_cast<int64_t>(kv) * seq_stride;
 
   float qv[8];
   {
@@ -2328,20 +2347,21 @@ __device__ inline uint32_t e4m3_encode(float y) {
 template <int SRC_DT, int CACHE_DT>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const void* c_kv, const void* k_r, const int32_t* positions, void* rows, float* row_scale,
-    const int32_t* block_table, int32_t max_pages, int32_t paged, int64_t seq_stride, int B) {
+    const int32_t* block_table, int32_t max_pages, int32_t paged, int64_t seq_stride, int ring,
+    int B) {
   const int b = blockIdx.x * (kAppendThreads / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (b >= B) return;
   const int64_t t = positions[b];
   const int64_t capacity = paged ? static_cast<int64_t>(max_pages) * kPageSize : seq_stride;
-  if (t < 0 || t >= capacity) return;
+  if (t < 0 || (!ring && t >= capacity)) return;  // a ring overwrites, it has no end
   int64_t row;
   if (paged) {
     const int64_t page = block_table[static_cast<int64_t>(b) * max_pages + (t >> 6)];
     if (page < 0) return;
     row = page * kPageSize + (t & 63);
   } else {
-    row = static_cast<int64_t>(b) * seq_stride + t;
+    row = static_cast<int64_t>(b) * seq_stride + (ring ? t % seq_stride : t);
   }
   constexpr int kPer = kRowElems / 64;  // 9
   float x[kPer];
@@ -2369,6 +2389,33 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
   } else {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) store_elem<CACHE_DT>(rows, base + lane + 64 * j, x[j]);
+  }
+}
+
+// Ring grow: workgroup (b, y) copies rows k = 16y .. 16y+15 of sequence b's
+// live window, the last `keep` tokens, token t = L - keep + k from row t % Cs
+// of the source ring to row t % Cd of the destination, as 16-byte chunks
+// (and the row factor of an fp8 cache).
+constexpr int kGrowThreads = 256;
+constexpr int kGrowRows = 16;
+
+__global__ __launch_bounds__(kGrowThreads) void ring_grow_kernel(
+    const uint8_t* src, const float* src_scale, int64_t src_cap, uint8_t* dst, float* dst_scale,
+    int64_t dst_cap, const int32_t* seq_lens, int max_seq_len, int row_chunks) {
+  const int b = blockIdx.x;
+  const int64_t L = min(max(seq_lens[b], 0), max_seq_len);
+  const int64_t keep = min(L, min(src_cap, dst_cap));
+  const int64_t row_bytes = static_cast<int64_t>(row_chunks) * 16;
+  for (int idx = threadIdx.x; idx < kGrowRows * row_chunks; idx += kGrowThreads) {
+    const int64_t k = static_cast<int64_t>(blockIdx.y) * kGrowRows + idx / row_chunks;
+    const int c = idx % row_chunks;
+    if (k >= keep) continue;
+    const int64_t t = L - keep + k;
+    const int64_t rs = static_cast<int64_t>(b) * src_cap + t % src_cap;
+    const int64_t rd = static_cast<int64_t>(b) * dst_cap + t % dst_cap;
+    *reinterpret_cast<u32x4_t*>(dst + rd * row_bytes + 16 * c) =
+        *reinterpret_cast<const u32x4_t*>(src + rs * row_bytes + 16 * c);
+    if (c == 0 && dst_scale) dst_scale[rd] = src_scale[rs];
   }
 }
 
@@ -2459,8 +2506,13 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   const int32_t H = dims->heads;
   // with max_seq_len == 0 every range is empty; a chunk of 32 keeps the
   // kernels' range arithmetic well defined
-  const int32_t chunk = max(split_chunk(cache->max_seq_len, num_splits), kTileTokens);
+  // a ring attends at most seq_stride tokens per sequence
+  const int32_t span = cache->ring ? static_cast<int32_t>(min(static_cast<int64_t>(cache->max_seq_len),
+                                                              cache->seq_stride))
+                                   : cache->max_seq_len;
+  const int32_t chunk = max(split_chunk(span, num_splits), kTileTokens);
   const float scale = effective_scale(dims);
+  if (cache->ring && q_len != 1) return MLA_E_UNSUPPORTED;
   if (kernel != MLA_KERNEL_AUTO && kernel != MLA_KERNEL_H64 && kernel != MLA_KERNEL_H128)
     return MLA_E_ARG;
   if (cache->dtype == MLA_F32) {
@@ -2468,7 +2520,7 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
     DecodeF32Params P{static_cast<const float*>(q_abs), static_cast<const float*>(cache->rows),
                       cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                       cache->page_size != 0, B, H, num_splits, chunk, cache->max_seq_len, scale,
-                      u_part, lse_part};
+                      u_part, lse_part, cache->ring};
     const int64_t nblk = static_cast<int64_t>(B) * num_splits * H;
     if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
     if (part_dt == MLA_F32)
@@ -2485,7 +2537,7 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   DecodeParams P{q_abs, static_cast<const uint8_t*>(cache->rows), cache->row_scale,
                  cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                  cache->page_size != 0, B, H, num_splits, HG64, chunk, cache->max_seq_len,
-                 q_len, scale * kLog2e, u_part, lse_part};
+                 q_len, scale * kLog2e, u_part, lse_part, cache->ring};
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
   const bool h128_ok = !fp8 && H % kH128 == 0;
   const int64_t nblk = static_cast<int64_t>(B) * q_len * num_splits * (H / kH128);
@@ -2741,7 +2793,7 @@ extern "C" mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, cons
   if (src_dt == SD && cache->dtype == CD) {                                                    \
     append_kernel<SD, CD><<<grid, kAppendThreads, 0, s>>>(c_kv, k_r, positions, rows, scale,   \
                                                           cache->block_table, cache->max_pages, \
-                                                          paged, cache->seq_stride, B);         \
+                                                          paged, cache->seq_stride, cache->ring, B); \
     return launch_status();                                                                   \
   }
   MLA_AP(MLA_F32, MLA_F32)
@@ -2754,16 +2806,38 @@ extern "C" mla_status_t mla_cache_append(const mla_dims_t* dims, int32_t B, cons
   return MLA_E_DTYPE;
 }
 
-extern "C" mla_status_t mla_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void* q,
-                                       const void* k_cache, const void* v_cache, int32_t dt,
-                                       const int32_t* seq_lens, int64_t seq_stride,
-                                       int32_t max_seq_len, float softmax_scale, void* o,
-                                       int32_t o_dt, float* lse, void* stream) {
+extern "C" mla_status_t mla_cache_ring_grow(int32_t B, const mla_cache_t* src,
+                                            const mla_cache_t* dst, void* stream) {
+  mla_status_t st = check_ring_grow(B, src, dst);
+  if (st != MLA_OK || B == 0) return st;
+  const int64_t keep = min(static_cast<int64_t>(src->max_seq_len),
+                           min(src->seq_stride, dst->seq_stride));
+  if (keep == 0) return MLA_OK;
+  const int64_t ys = (keep + kGrowRows - 1) / kGrowRows;
+  if (ys > 65535) return MLA_E_SHAPE;
+  const int row_chunks = kRowElems * dtype_bytes(src->dtype) / 16;
+  const dim3 grid(static_cast<unsigned>(B), static_cast<unsigned>(ys));
+  ring_grow_kernel<<<grid, kGrowThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(src->rows), src->row_scale, src->seq_stride,
+      static_cast<uint8_t*>(const_cast<void*>(dst->rows)), const_cast<float*>(dst->row_scale),
+      dst->seq_stride, src->seq_lens, src->max_seq_len, row_chunks);
+  return launch_status();
+}
+
+extern "C" mla_status_t mla_gqa_decode(int32_t B, int32_t heads, int32_t kv_heads,
+                                       int32_t d_head, const void* q, const void* k_cache,
+                                       const void* v_cache, int32_t dt, const int32_t* seq_lens,
+                                       int64_t seq_stride, int32_t max_seq_len,
+                                       float softmax_scale, void* o, int32_t o_dt, float* lse,
+                                       void* stream) {
   mla_status_t st = check_mha_decode(B, heads, d_head, q, k_cache, v_cache, dt, seq_lens,
                                      seq_stride, max_seq_len, softmax_scale, o, o_dt);
-  if (st != MLA_OK || B == 0) return st;
+  if (st != MLA_OK) return st;
+  if (kv_heads < 1 || heads % kv_heads != 0) return MLA_E_ARG;
+  if (B == 0) return MLA_OK;
   const int64_t nblk = static_cast<int64_t>(B) * heads;
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
+  const int G = heads / kv_heads;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(d_head));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* qp = static_cast<const uint16_t*>(q);
@@ -2771,9 +2845,18 @@ extern "C" mla_status_t mla_mha_decode(int32_t B, int32_t heads, int32_t d_head,
   const auto* vp = static_cast<const uint16_t*>(v_cache);
   if (o_dt == MLA_F32)
     mha_decode_kernel<MLA_F32><<<static_cast<unsigned>(nblk), kMhaThreads, 0, s>>>(
-        qp, kp, vp, seq_lens, seq_stride, max_seq_len, heads, scale * kLog2e, o, lse);
+        qp, kp, vp, seq_lens, seq_stride, max_seq_len, heads, G, scale * kLog2e, o, lse);
   else
     mha_decode_kernel<MLA_BF16><<<static_cast<unsigned>(nblk), kMhaThreads, 0, s>>>(
-        qp, kp, vp, seq_lens, seq_stride, max_seq_len, heads, scale * kLog2e, o, lse);
+        qp, kp, vp, seq_lens, seq_stride, max_seq_len, heads, G, scale * kLog2e, o, lse);
   return launch_status();
+}
+
+extern "C" mla_status_t mla_mha_decode(int32_t B, int32_t heads, int32_t d_head, const void* q,
+                                       const void* k_cache, const void* v_cache, int32_t dt,
+                                       const int32_t* seq_lens, int64_t seq_stride,
+                                       int32_t max_seq_len, float softmax_scale, void* o,
+                                       int32_t o_dt, float* lse, void* stream) {
+  return mla_gqa_decode(B, heads, heads, d_head, q, k_cache, v_cache, dt, seq_lens, seq_stride,
+                        max_seq_len, softmax_scale, o, o_dt, lse, stream);
 }

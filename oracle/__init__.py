@@ -30,7 +30,7 @@ class _Problem(C.Structure):
         ("w_uk", C.c_void_p), ("w_uv", C.c_void_p), ("w_dtype", C.c_int32),
         ("rows", C.c_void_p), ("row_scale", C.c_void_p), ("cache_dtype", C.c_int32),
         ("page_size", C.c_int32), ("seq_stride", C.c_int64), ("block_table", C.c_void_p),
-        ("max_pages", C.c_int32), ("seq_lens", C.c_void_p),
+        ("max_pages", C.c_int32), ("seq_lens", C.c_void_p), ("ring", C.c_int32),
     ]
 
 
@@ -66,9 +66,15 @@ def lib():
         L.oracle_cache_append.argtypes = [C.c_int32] * 3 + [C.c_void_p, C.c_void_p, C.c_int32,
                                                             C.c_void_p, C.c_void_p, C.c_int32,
                                                             C.c_void_p, C.c_int32, C.c_int64,
-                                                            C.c_void_p, C.c_int32]
+                                                            C.c_void_p, C.c_int32, C.c_int32]
+        L.oracle_ring_grow.restype = C.c_int
+        L.oracle_ring_grow.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                       C.c_int64, C.c_void_p, C.c_void_p, C.c_int64]
         L.oracle_mha_decode.restype = C.c_int
         L.oracle_mha_decode.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 3 + [
+            C.c_int32, C.c_void_p, C.c_int64, C.c_double, C.c_void_p, C.c_void_p]
+        L.oracle_gqa_decode.restype = C.c_int
+        L.oracle_gqa_decode.argtypes = [C.c_int32] * 5 + [C.c_void_p] * 3 + [
             C.c_int32, C.c_void_p, C.c_int64, C.c_double, C.c_void_p, C.c_void_p]
         L.oracle_rope.restype = C.c_int
         L.oracle_rope.argtypes = [C.c_int32] * 3 + [C.c_void_p, C.c_int32, C.c_void_p,
@@ -99,7 +105,7 @@ def decode(q_nope, q_rope, q_dtype, w_uk, w_uv, w_dtype, rows, cache_dtype, seq_
            row_scale=None, page_size: int = 0, seq_stride: Optional[int] = None,
            block_table=None, scale: Optional[float] = None,
            sel: Optional[Sequence[tuple]] = None, t_begin=None, t_end=None,
-           want_u: bool = False):
+           want_u: bool = False, ring: bool = False):
     """Naive MLA decode.  Arrays hold stored bits (float32 / uint16 bf16 /
     uint8 e4m3 / float64).  Returns (o [n, d_v], lse [n], u [n, d_latent] or
     None) as float64, for the selected (b, h) pairs or all B*H in order."""
@@ -122,7 +128,7 @@ def decode(q_nope, q_rope, q_dtype, w_uk, w_uv, w_dtype, rows, cache_dtype, seq_
     P = _Problem(B, H, dn, dr, dl, dv, float(scale) if scale else 0.0,
                  _ptr(q_nope), _ptr(q_rope), qd, _ptr(w_uk), _ptr(w_uv), wd,
                  _ptr(rows), _ptr(rs), cd, int(page_size), int(seq_stride), _ptr(bt),
-                 0 if bt is None else int(bt.shape[1]), _ptr(seq_lens))
+                 0 if bt is None else int(bt.shape[1]), _ptr(seq_lens), int(bool(ring)))
     if sel is None:
         n = B * H
         sb = sh = None
@@ -143,14 +149,15 @@ def decode(q_nope, q_rope, q_dtype, w_uk, w_uv, w_dtype, rows, cache_dtype, seq_
     return o, lse, u
 
 
-def decode_inputs(inp, sel=None, want_u=False, t_begin=None, t_end=None, scale=None):
+def decode_inputs(inp, sel=None, want_u=False, t_begin=None, t_end=None, scale=None,
+                  ring=False):
     """decode() on a synth.MLAInputs-like object (duck-typed)."""
     wl = inp.wl
     return decode(inp.q_nope, inp.q_rope, wl.act_dtype, inp.w_uk, inp.w_uv, wl.act_dtype,
                   inp.rows, wl.cache_dtype, inp.seq_lens, row_scale=inp.row_scale,
                   page_size=wl.page_size, seq_stride=inp.seq_stride,
                   block_table=inp.block_table, scale=scale, sel=sel, t_begin=t_begin,
-                  t_end=t_end, want_u=want_u)
+                  t_end=t_end, want_u=want_u, ring=ring)
 
 
 def absorb_q(q_nope, q_rope, q_dtype, w_uk, w_dtype):
@@ -181,13 +188,14 @@ def combine(u_part, lse_part):
 
 
 def cache_append(c_kv, k_r, src_dtype, positions, rows, cache_dtype, row_scale=None,
-                 page_size=0, seq_stride=0, block_table=None):
+                 page_size=0, seq_stride=0, block_table=None, ring=False):
     """Write one token per sequence into the cache arrays (modified in place).
 
     c_kv [B, d_latent], k_r [B, d_rope] stored bits in src_dtype ("f32" or
     "bf16"); rows [n_rows, d_latent + d_rope] stored bits in cache_dtype;
     row_scale [n_rows] float32 for "fp8"; positions [B] int32 (negative or
-    past the capacity: skipped)."""
+    past the capacity: skipped; a ring (contiguous, ring=True) writes token t
+    into row t mod seq_stride of its sequence)."""
     sd, cd = _dt(src_dtype), _dt(cache_dtype)
     c_kv, k_r = _arr(c_kv, sd), _arr(k_r, sd)
     B, dl = c_kv.shape
@@ -200,9 +208,48 @@ def cache_append(c_kv, k_r, src_dtype, positions, rows, cache_dtype, row_scale=N
     max_pages = 0 if bt is None else bt.shape[1]
     rc = lib().oracle_cache_append(B, dl, dr, _ptr(c_kv), _ptr(k_r), sd, _ptr(pos), _ptr(rows),
                                    cd, _ptr(row_scale), int(page_size), int(seq_stride), _ptr(bt),
-                                   max_pages)
+                                   max_pages, int(bool(ring)))
     if rc != 0:
         raise ValueError(f"oracle_cache_append failed: {rc}")
+
+
+def gqa_decode(q, k, v, dtype, seq_lens, scale=0.0):
+    """Grouped-query attention decode.  q [B, H, d_qk]; k [B, H_kv, stride,
+    d_qk], v [B, H_kv, stride, d_v] (stored bits in dtype), H a multiple of
+    H_kv, query head h reading key/value head h // (H / H_kv); seq_lens [B]
+    -> (o [B, H, d_v], lse [B, H]) float64."""
+    d = _dt(dtype)
+    q, k, v = _arr(q, d), _arr(k, d), _arr(v, d)
+    B, H, dq = q.shape
+    Hkv, stride, dv = k.shape[1], k.shape[2], v.shape[3]
+    assert k.shape == (B, Hkv, stride, dq) and v.shape[:3] == (B, Hkv, stride)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    o = np.zeros((B, H, dv), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    rc = lib().oracle_gqa_decode(B, H, Hkv, dq, dv, _ptr(q), _ptr(k), _ptr(v), d, _ptr(lens),
+                                 stride, float(scale), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_gqa_decode failed: {rc}")
+    return o, lse
+
+
+def ring_grow(seq_lens, src, src_cap, dst_cap, src_scale=None):
+    """Move each sequence's live window from a ring of src_cap rows per
+    sequence (src [B*src_cap, W], any dtype) into a new ring of dst_cap rows
+    (token t to row t mod dst_cap).  Returns (dst, dst_scale or None); rows
+    the window does not reach are zero."""
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = lens.shape[0]
+    src = np.ascontiguousarray(src)
+    W = src.shape[1]
+    dst = np.zeros((B * dst_cap, W), dtype=src.dtype)
+    ss = None if src_scale is None else np.ascontiguousarray(src_scale, dtype=np.float32)
+    ds = None if ss is None else np.zeros(B * dst_cap, dtype=np.float32)
+    rc = lib().oracle_ring_grow(B, W * src.dtype.itemsize, _ptr(lens), _ptr(src), _ptr(ss),
+                                int(src_cap), _ptr(dst), _ptr(ds), int(dst_cap))
+    if rc != 0:
+        raise ValueError(f"oracle_ring_grow failed: {rc}")
+    return dst, ds
 
 
 def mha_decode(q, k, v, dtype, seq_lens, scale=0.0):

@@ -29,6 +29,11 @@
  * [h][d_v][d_latent], the nn.Linear layout of the [DSA] listing; one 576-wide
  * row per token holds [c_KV | k_R]; e4m3 rows carry one fp32 factor; every
  * cached token is attended, no mask) are listed with the tests that pin them.
+ * Ring cache ([V2] §4.1 keeps the KV cache in a ring buffer so that it can
+ * grow): a sequence's seq_stride rows are a ring of that capacity C, token t
+ * sits in row t mod C, so the ring holds the last min(L, C) tokens and those
+ * are the ones attended (a window of C tokens once L > C); growing moves that
+ * window into a larger ring, token t to row t mod C'.
  *
  * Pins (tests/test_oracle_*.py): library SDPA over explicitly rebuilt K/V,
  * the absorbed-form identity, closed forms (one token, zero query, dominant
@@ -91,6 +96,7 @@ static int valid_dtype(int32_t d) { return d >= ORACLE_F32 && d <= ORACLE_F64; }
 /* physical row of token t of sequence b: contiguous [b][seq_stride] rows, or a
  * page of page_size rows named by the block table ([V2] §1.2/§3.3 paging) */
 static int64_t row_of(const oracle_mla_problem* P, int32_t b, int64_t t) {
+  if (P->ring) return (int64_t)b * P->seq_stride + t % P->seq_stride;
   if (P->page_size > 0) {
     int64_t page = P->block_table[(int64_t)b * P->max_pages + t / P->page_size];
     return page * P->page_size + t % P->page_size;
@@ -120,6 +126,7 @@ int oracle_mla_decode(const oracle_mla_problem* P, const int32_t* sel_b,
     return -3;
   if (P->cache_dtype == ORACLE_E4M3 && !P->row_scale) return -4;
   if (P->page_size > 0 && !P->block_table) return -5;
+  if (P->ring && (P->page_size > 0 || P->seq_stride < 1)) return -7;
   const int32_t all = (sel_b == NULL);
   const int64_t n = all ? (int64_t)P->B * P->H : n_sel;
   const double scale =
@@ -140,6 +147,8 @@ int oracle_mla_decode(const oracle_mla_problem* P, const int32_t* sel_b,
     int64_t t1 = t_end ? t_end[b] : L;
     if (t0 < 0) t0 = 0;
     if (t1 > L) t1 = L;
+    /* a ring of C rows keeps only the last C tokens */
+    if (P->ring && t0 < L - P->seq_stride) t0 = L - P->seq_stride;
     double* out_o = o + idx * dv;
     double* out_u = u ? u + idx * dl : NULL;
     for (int32_t v = 0; v < dv; ++v) out_o[v] = 0.0;
@@ -344,7 +353,8 @@ static void round_bf16(float x, uint16_t* out) {
 int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void* c_kv,
                         const void* k_r, int32_t src_dtype, const int32_t* positions,
                         void* rows, int32_t cache_dtype, float* row_scale, int32_t page_size,
-                        int64_t seq_stride, const int32_t* block_table, int32_t max_pages) {
+                        int64_t seq_stride, const int32_t* block_table, int32_t max_pages,
+                        int32_t ring) {
   if (B < 0 || d_latent <= 0 || d_rope < 0 || !positions || !rows) return -1;
   if (B > 0 && (!c_kv || (d_rope > 0 && !k_r))) return -1;
   if (src_dtype != ORACLE_F32 && src_dtype != ORACLE_BF16) return -3;
@@ -353,16 +363,19 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
   if (cache_dtype == ORACLE_E4M3 && !row_scale) return -4;
   if (page_size < 0 || (page_size > 0 && (!block_table || max_pages < 1))) return -2;
   if (page_size == 0 && seq_stride < 1) return -2;
+  if (ring && page_size != 0) return -2;
   const int32_t w = d_latent + d_rope;
   const int64_t capacity = page_size ? (int64_t)max_pages * page_size : seq_stride;
   float* x = (float*)malloc(sizeof(float) * (size_t)w);
   if (!x) return -5;
   for (int32_t b = 0; b < B; ++b) {
     const int64_t t = positions[b];
-    if (t < 0 || t >= capacity) continue;
+    if (t < 0 || (!ring && t >= capacity)) continue;
     const int64_t page = page_size ? block_table[(int64_t)b * max_pages + t / page_size] : 0;
     if (page < 0) continue; /* no page mapped */
-    const int64_t row = page_size ? page * page_size + t % page_size : (int64_t)b * seq_stride + t;
+    /* a ring overwrites the token C positions back */
+    const int64_t slot = ring ? t % seq_stride : t;
+    const int64_t row = page_size ? page * page_size + t % page_size : (int64_t)b * seq_stride + slot;
     /* the new row as binary32 values (both input formats convert exactly) */
     for (int32_t j = 0; j < d_latent; ++j)
       x[j] = (float)load_elem(c_kv, src_dtype, (int64_t)b * d_latent + j);
@@ -389,20 +402,57 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
   return 0;
 }
 
+/* Growing a ring ([V2] §4.1): the tokens a sequence's ring of src_cap rows
+ * holds, the last min(L, src_cap), move to a ring of dst_cap rows, token t to
+ * row t mod dst_cap; a smaller ring keeps the last dst_cap of them.  Rows are
+ * moved as bytes (any cache dtype), with their fp32 factor when given. */
+int oracle_ring_grow(int32_t B, int32_t row_bytes, const int32_t* seq_lens, const void* src,
+                     const float* src_scale, int64_t src_cap, void* dst, float* dst_scale,
+                     int64_t dst_cap) {
+  if (B < 0 || row_bytes < 1 || src_cap < 1 || dst_cap < 1) return -1;
+  if (B > 0 && (!seq_lens || !src || !dst)) return -1;
+  if ((src_scale == NULL) != (dst_scale == NULL)) return -1;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = seq_lens[b];
+    if (L < 0) return -2;
+    int64_t keep = L < src_cap ? L : src_cap;
+    if (keep > dst_cap) keep = dst_cap;
+    for (int64_t t = L - keep; t < L; ++t) {
+      const int64_t rs = (int64_t)b * src_cap + t % src_cap;
+      const int64_t rd = (int64_t)b * dst_cap + t % dst_cap;
+      memcpy((uint8_t*)dst + rd * row_bytes, (const uint8_t*)src + rs * row_bytes,
+             (size_t)row_bytes);
+      if (dst_scale) dst_scale[rd] = src_scale[rs];
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------ MHA baseline */
 
-int oracle_mha_decode(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, const void* q,
-                      const void* k, const void* v, int32_t dtype, const int32_t* seq_lens,
-                      int64_t seq_stride, double scale, double* o, double* lse) {
-  if (B < 0 || H <= 0 || d_qk <= 0 || d_v <= 0 || !q || !k || !v || !seq_lens || !o || !lse)
+/* Grouped-query attention decode ([LAT] §2.2: query heads in groups, each
+ * group sharing one key/value head; [V2] §1.2 lists MQA/GQA as the cache
+ * reductions MLA is compared with).  The H query heads form H_kv contiguous
+ * groups of G = H / H_kv: query head h reads key/value head h / G.  H_kv = H
+ * is multi-head attention, H_kv = 1 multi-query attention. */
+int oracle_gqa_decode(int32_t B, int32_t H, int32_t H_kv, int32_t d_qk, int32_t d_v,
+                      const void* q, const void* k, const void* v, int32_t dtype,
+                      const int32_t* seq_lens, int64_t seq_stride, double scale, double* o,
+                      double* lse) {
+  if (B < 0 || H <= 0 || H_kv <= 0 || d_qk <= 0 || d_v <= 0 || !q || !k || !v || !seq_lens ||
+      !o || !lse)
     return -1;
+  if (H % H_kv != 0) return -2;
   if (!valid_dtype(dtype)) return -3;
   if (seq_stride < 0) return -2;
+  const int64_t G = H / H_kv;
   const double sc = scale > 0.0 ? scale : 1.0 / sqrt((double)d_qk);
   int bad = 0;
 #pragma omp parallel for schedule(dynamic) reduction(| : bad)
   for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
-    const int64_t b = bh / H;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t kvh = h / G;                  /* the group's key/value head */
+    const int64_t kv = b * H_kv + kvh;          /* its rows: [b][kvh][seq_stride] */
     const int64_t L = seq_lens[b];
     double* out = o + bh * d_v;
     for (int32_t j = 0; j < d_v; ++j) out[j] = 0.0;
@@ -424,7 +474,7 @@ int oracle_mha_decode(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, const voi
     for (int64_t t = 0; t < L; ++t) {
       double dot = 0.0;
       for (int32_t j = 0; j < d_qk; ++j)
-        dot += load_elem(q, dtype, bh * d_qk + j) * load_elem(k, dtype, (bh * seq_stride + t) * d_qk + j);
+        dot += load_elem(q, dtype, bh * d_qk + j) * load_elem(k, dtype, (kv * seq_stride + t) * d_qk + j);
       s[t] = sc * dot;
       if (s[t] > m) m = s[t];
     }
@@ -433,13 +483,20 @@ int oracle_mha_decode(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, const voi
     for (int64_t t = 0; t < L; ++t) {
       const double p = exp(s[t] - m);
       l += p;
-      for (int32_t j = 0; j < d_v; ++j) out[j] += p * load_elem(v, dtype, (bh * seq_stride + t) * d_v + j);
+      for (int32_t j = 0; j < d_v; ++j) out[j] += p * load_elem(v, dtype, (kv * seq_stride + t) * d_v + j);
     }
     for (int32_t j = 0; j < d_v; ++j) out[j] /= l;
     lse[bh] = m + log(l);
     free(s);
   }
   return bad ? -2 : 0;
+}
+
+/* Multi-head attention decode: every query head has its own key/value head. */
+int oracle_mha_decode(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, const void* q,
+                      const void* k, const void* v, int32_t dtype, const int32_t* seq_lens,
+                      int64_t seq_stride, double scale, double* o, double* lse) {
+  return oracle_gqa_decode(B, H, H, d_qk, d_v, q, k, v, dtype, seq_lens, seq_stride, scale, o, lse);
 }
 
 /* ------------------------------------------------------ decoupled RoPE */

@@ -42,6 +42,7 @@ typedef struct {
   const int32_t* block_table; /* paged: row = block_table[b*max_pages + t/ps]*ps + t%ps */
   int32_t max_pages;
   const int32_t* seq_lens; /* [B] */
+  int32_t ring; /* contiguous only: 1 = each sequence's seq_stride rows are a ring */
 } oracle_mla_problem;
 
 /* Naive decode: rebuild K and V per cached token, then textbook attention.
@@ -91,7 +92,12 @@ int oracle_up_proj(int32_t B, int32_t H, int32_t d_v, int32_t d_latent,
 int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void* c_kv,
                         const void* k_r, int32_t src_dtype, const int32_t* positions,
                         void* rows, int32_t cache_dtype, float* row_scale, int32_t page_size,
-                        int64_t seq_stride, const int32_t* block_table, int32_t max_pages);
+                        int64_t seq_stride, const int32_t* block_table, int32_t max_pages,
+                        int32_t ring);
+
+int oracle_ring_grow(int32_t B, int32_t row_bytes, const int32_t* seq_lens, const void* src,
+                     const float* src_scale, int64_t src_cap, void* dst, float* dst_scale,
+                     int64_t dst_cap);
 
 /* Multi-head attention decode over a full per-head K/V cache, the baseline
  * the latent cache replaces ([LAT] §2.1 textbook attention
@@ -119,6 +125,11 @@ int oracle_mha_decode(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, const voi
  * cos and sin in float64.  x [B][H][d_r] in dtype, positions [B] (one per
  * sequence: every head of a token shares its position); out float64.
  * Returns 0, or a negative value on a bad argument. */
+int oracle_gqa_decode(int32_t B, int32_t H, int32_t H_kv, int32_t d_qk, int32_t d_v,
+                      const void* q, const void* k, const void* v, int32_t dtype,
+                      const int32_t* seq_lens, int64_t seq_stride, double scale, double* o,
+                      double* lse);
+
 int oracle_rope(int32_t B, int32_t H, int32_t d_r, const void* x, int32_t dtype,
                 const int32_t* positions, double base, double* out);
 

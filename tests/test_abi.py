@@ -50,9 +50,9 @@ def dims(h=128, dn=128, dr=64, dl=512, dv=128, scale=0.0):
 
 
 def cache(dtype=BF16, rows=P, row_scale=None, page_size=0, seq_stride=4096, block_table=None,
-          max_pages=0, seq_lens=P, max_seq_len=4096):
+          max_pages=0, seq_lens=P, max_seq_len=4096, ring=0):
     return mla.CacheDesc(dtype, rows, row_scale, page_size, seq_stride, block_table, max_pages,
-                         seq_lens, max_seq_len)
+                         seq_lens, max_seq_len, ring)
 
 
 def decode(d=None, B=2, q=P, q_dt=BF16, q_scale=None, c=None, S=4, u=P, u_dt=F32, lse=P):
@@ -296,3 +296,27 @@ def test_noalloc_validation_before_any_launch():
     assert noalloc(B=65, S=8) == E_SCRATCH          # 66,560 rows
     assert noalloc(B=1, S=1024, d=dims(h=128)) == E_SCRATCH  # 131,072 rows
     assert noalloc(B=513, S=1) == E_SCRATCH
+
+
+def test_ring_cache_validation():
+    """A ring is contiguous; its lengths may exceed its capacity; a multi-token
+    decode over a ring is refused (earlier query tokens would need rows the
+    ring overwrote) before any launch."""
+    assert decode(c=cache(ring=2)) == E_ARG
+    assert decode(c=cache(ring=1, page_size=64, block_table=P, max_pages=64)) == E_ARG
+    assert decode(c=cache(ring=1, seq_stride=0)) == E_ARG
+    assert decode(c=cache(ring=0, seq_stride=1024, max_seq_len=4096)) == E_ARG
+    d = dims()
+    multi = mla.lib().mla_decode_multi(C.byref(d), 2, 2, P, BF16,
+                                       C.byref(cache(ring=1, seq_stride=1024, max_seq_len=4096)),
+                                       4, P, F32, P, None)
+    assert multi == E_UNSUP
+    src, dst = cache(ring=1, seq_stride=256), cache(ring=1, seq_stride=512)
+    L = mla.lib()
+    assert L.mla_cache_ring_grow(0, C.byref(src), C.byref(dst), None) == OK
+    assert L.mla_cache_ring_grow(2, C.byref(src), C.byref(cache(ring=0)), None) == E_ARG
+    assert L.mla_cache_ring_grow(2, None, C.byref(dst), None) == E_ARG
+    assert L.mla_cache_ring_grow(2, C.byref(src), C.byref(cache(ring=1, dtype=F32)), None) == E_DTYPE
+    assert L.mla_cache_ring_grow(2, C.byref(src), C.byref(cache(ring=1, rows=P + 8)), None) == E_ALIGN
+    fp8 = cache(ring=1, dtype=FP8, row_scale=P)
+    assert L.mla_cache_ring_grow(2, C.byref(fp8), C.byref(cache(ring=1, dtype=FP8)), None) == E_ARG

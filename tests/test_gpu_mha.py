@@ -73,3 +73,31 @@ def test_mha_dsv2_heads_sampled():
         o_ref, _ = oracle.mha_decode(_bits(q[b:b + 1, h:h + 1]), _bits(k[b:b + 1, h:h + 1]),
                                      _bits(v[b:b + 1, h:h + 1]), "bf16", np.array([L], np.int32))
         assert rel_err(got[b, h], o_ref[0, 0]) <= 2e-2, (b, h)
+
+
+@pytest.mark.parametrize("Hkv", [1, 8, 16, 128])
+def test_gqa_every_output(Hkv):
+    """Grouped-query decode at 128 query heads and 1 / 8 / 16 / 128 key/value
+    heads (multi-query ... multi-head), ragged and empty sequences, every
+    output against the oracle."""
+    lens = [0, 1, 33, 700, 2048]
+    B, H, stride = len(lens), 128, 2048
+    g = torch.Generator(device="cuda").manual_seed(40 + Hkv)
+    q = torch.randn(B, H, 128, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, stride, 128, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, stride, 128, device="cuda", generator=g).to(torch.bfloat16)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o = torch.empty(B, H, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, H, dtype=torch.float32, device="cuda")
+    _log(f"gqa kv_heads={Hkv}")
+    mla.mla_gqa_decode(q, k, v, seq, max(lens), o, lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.gqa_decode(_bits(q), _bits(k), _bits(v), "bf16",
+                                       np.array(lens, np.int32))
+    got = o.cpu().numpy()
+    e = rel_err(got.reshape(-1, 128), o_ref.reshape(-1, 128))
+    fin = np.isfinite(lse_ref)
+    el = np.abs(lse.cpu().numpy()[fin] - lse_ref[fin]).max()
+    _log(f"  err o {e:.2e} lse {el:.2e}")
+    assert e <= 1e-4 and el <= 1e-4
+    assert np.all(got[0] == 0) and np.all(np.isneginf(lse.cpu().numpy()[0]))

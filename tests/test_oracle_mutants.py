@@ -16,6 +16,7 @@ from . import test_oracle_append as append
 from . import test_oracle_codecs as codecs
 from . import test_oracle_mha as mha
 from . import test_oracle_pins as pins
+from . import test_oracle_ring as ring
 from . import test_oracle_rope as rope
 
 HERE = os.path.dirname(os.path.abspath(oracle.__file__))
@@ -44,8 +45,17 @@ MUTANTS = {
     "append_scale_to_240": ("const float s = fmaxf(amax, 0x1p-126f) / 448.0f;",
                             "const float s = fmaxf(amax, 0x1p-126f) / 240.0f;"),
     "append_bf16_truncates": ("if (dhi < dlo || (dhi == dlo && ((lo >> 16) & 1u))) r = hi;", ""),
-    "append_row_off_by_one": (": (int64_t)b * seq_stride + t;", ": (int64_t)b * seq_stride + t + 1;"),
-    "append_ignores_capacity": ("if (t < 0 || t >= capacity) continue;", "if (t < 0) continue;"),
+    "append_row_off_by_one": (": (int64_t)b * seq_stride + slot;", ": (int64_t)b * seq_stride + slot + 1;"),
+    "append_ignores_capacity": ("if (t < 0 || (!ring && t >= capacity)) continue;", "if (t < 0) continue;"),
+    # ring cache
+    "ring_slot_off_by_one": ("const int64_t slot = ring ? t % seq_stride : t;",
+                             "const int64_t slot = ring ? (t + 1) % seq_stride : t;"),
+    "ring_window_one_short": ("if (P->ring && t0 < L - P->seq_stride) t0 = L - P->seq_stride;",
+                              "if (P->ring && t0 < L - P->seq_stride) t0 = L - P->seq_stride + 1;"),
+    "ring_decode_row_map": ("if (P->ring) return (int64_t)b * P->seq_stride + t % P->seq_stride;",
+                            "if (P->ring) return (int64_t)b * P->seq_stride + (t + 1) % P->seq_stride;"),
+    "ring_grow_destination": ("const int64_t rd = (int64_t)b * dst_cap + t % dst_cap;",
+                              "const int64_t rd = (int64_t)b * dst_cap + (t + 1) % dst_cap;"),
     # absorb and up-projection
     "absorb_transposed_w_uk": ("out[j] += q * load_elem(w_uk, w_dtype, (h * d_nope + n) * d_latent + j);",
                                "out[j] += q * load_elem(w_uk, w_dtype, (h * d_latent + j) * d_nope + n);"),
@@ -67,8 +77,10 @@ MUTANTS = {
     "mha_scale_over_dv": ("const double sc = scale > 0.0 ? scale : 1.0 / sqrt((double)d_qk);",
                           "const double sc = scale > 0.0 ? scale : 1.0 / sqrt((double)d_v);"),
     "mha_missing_normalisation": ("for (int32_t j = 0; j < d_v; ++j) out[j] /= l;", ""),
-    "mha_key_stride": ("load_elem(k, dtype, (bh * seq_stride + t) * d_qk + j)",
-                       "load_elem(k, dtype, (bh * seq_stride + t) * d_v + j)"),
+    "mha_key_stride": ("load_elem(k, dtype, (kv * seq_stride + t) * d_qk + j)",
+                       "load_elem(k, dtype, (kv * seq_stride + t) * d_v + j)"),
+    "gqa_strided_groups": ("const int64_t kvh = h / G;", "const int64_t kvh = h % H_kv;"),
+    "gqa_values_of_head_zero": ("const int64_t kv = b * H_kv + kvh;", "const int64_t kv = b * H_kv;"),
     "rope_angle_in_double": ("const float theta = pos * inv_freq[i]; /* binary32 product */",
                              "const double theta = (double)pos * (double)inv_freq[i];"),
 }
@@ -100,9 +112,15 @@ PIN_CHECKS = [
     lambda: rope.test_angles_add(100, 28),
     pins.test_absorb_q_and_up_proj_outputs_reproduce_the_naive_decode,
     append.test_unmapped_page_is_skipped,
+    lambda: ring.test_ring_decode_is_the_linear_decode_over_the_last_c_tokens(45, 32),
+    ring.test_ring_within_capacity_equals_the_linear_cache_bit_for_bit,
+    lambda: ring.test_grown_ring_decodes_like_the_window_it_keeps(16, 48, [12, 16, 0]),
+    lambda: ring.test_grown_ring_decodes_like_the_window_it_keeps(32, 8, [50, 9, 0]),
     lambda: mha.test_matches_library_attention(192, 128),
     mha.test_mla_is_mha_on_rebuilt_keys_and_values,
     mha.test_closed_forms,
+    lambda: mha.test_gqa_matches_library_grouped_attention(8, 2),
+    mha.test_mqa_is_mla_with_identity_up_projections,
 ]
 
 
@@ -130,7 +148,7 @@ def test_pins_catch_planted_mistake(tmp_path, name, monkeypatch):
                "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_array",
                "oracle_mla_cache_bytes_per_token", "oracle_mha_cache_bytes",
                "oracle_num_threads", "oracle_cache_append", "oracle_encode_e4m3",
-               "oracle_rope", "oracle_rope_inv_freq", "oracle_mha_decode"):
+               "oracle_rope", "oracle_rope_inv_freq", "oracle_mha_decode", "oracle_ring_grow", "oracle_gqa_decode"):
         getattr(mut, fn).restype = getattr(good, fn).restype
         getattr(mut, fn).argtypes = getattr(good, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mut)
