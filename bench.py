@@ -57,6 +57,11 @@ def parse():
     ap.add_argument("--mha", action="store_true",
                     help="the MHA baseline instead: per-head bf16 K/V cache at the geometry of "
                          "--workload (batch, heads, lengths; head dim 128), mla_mha_decode")
+    ap.add_argument("--prefill", type=int, default=0, metavar="CHUNK",
+                    help="chunked prefill in the naive form instead: the last CHUNK cached "
+                         "tokens of every sequence of --workload are the queries; keys and values "
+                         "rebuilt for the whole context (mla_prefill_rebuild_kv), then causal "
+                         "attention (mla_prefill_attn); query tokens/s, matrix-core roofline")
     ap.add_argument("--gqa", type=int, default=0, metavar="KV_HEADS",
                     help="with --mha: grouped-query attention with this many key/value heads "
                          "(mla_gqa_decode); 0 = one per query head")
@@ -307,6 +312,83 @@ def mha_baseline(args):
     print(json.dumps(rec), flush=True)
 
 
+def prefill_bench(args):
+    """Chunked prefill, naive (rebuild) form: each step rebuilds every head's
+    keys and values for each sequence's whole context and runs the causal
+    attention of its last CHUNK tokens.  Inputs of the workload (one copy: the
+    rebuilt keys and values alone are larger than the Infinity Cache)."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_15_amd as mla
+    import synth
+    from tests.device_inputs import DeviceInputs
+
+    wl = synth.workload(args.workload)
+    inp = synth.make_inputs(wl)
+    dev = DeviceInputs(inp)
+    lens = np.asarray(inp.seq_lens, np.int64)
+    B, H, QL = wl.batch, wl.heads, args.prefill
+    S = int(-(-int(lens.max()) // 32) * 32)
+    nq = np.minimum(lens, QL)
+    print(f"[bench] prefill {wl.name}: B={B} h={H} chunk={QL} context<={int(lens.max())}",
+          file=sys.stderr, flush=True)
+    g = torch.Generator(device="cuda").manual_seed(wl.seed + 9)
+    q = torch.randn(B, QL, H, wl.d_nope + wl.d_rope, device="cuda", generator=g).to(torch.bfloat16)
+    q_lens = torch.from_numpy(nq.astype(np.int32)).cuda()
+    k = torch.empty(B, H, S, wl.d_nope + wl.d_rope, dtype=torch.bfloat16, device="cuda")
+    vt = torch.empty(B, H, wl.d_v, S, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty(B, QL, H, wl.d_v, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    stages = [("mla_prefill_rebuild_kv", mla.mla_prefill_rebuild_kv(
+                  dev.geo, dev.cache, dev.w_uk, dev.w_uv, k, vt, stream=stream, prepare=True)),
+              ("mla_prefill_attn", mla.mla_prefill_attn(
+                  dev.geo, q, q_lens, k, vt, dev.cache.seq_lens, int(lens.max()), o,
+                  stream=stream, prepare=True))]
+    for _ in range(args.warmup):
+        for _, c in stages:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for jj, (_, c) in enumerate(stages):
+            c()
+            ev[i][jj + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    st = {name: launch_stats([ev[i][jj].elapsed_time(ev[i][jj + 1]) * 1e3
+                              for i in range(args.steps)])
+          for jj, (name, _) in enumerate(stages)}
+    # matrix-core work: rebuild 2 * 512 * (d_nope + d_v) per head and cached
+    # token; attention 2 * (192 + 128) per head, query and attended key
+    f_rebuild = float(lens.sum()) * H * 2 * wl.d_latent * (wl.d_nope + wl.d_v)
+    att_keys = float(sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2
+                         for L, n in zip(lens, nq)))
+    f_attn = att_keys * H * 2 * (wl.d_nope + wl.d_rope + wl.d_v)
+    t_r, t_a = st["mla_prefill_rebuild_kv"]["mean"] * 1e-6, st["mla_prefill_attn"]["mean"] * 1e-6
+    rec = {
+        "metric": "MLA chunked prefill (naive rebuild form) query tokens/s, 1 GPU",
+        "value": float(nq.sum()) / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) queries/cache, N(0,1/512) weights)",
+        "config": {"workload": f"prefill_{wl.name}_chunk{QL}", "batch": B, "heads": H,
+                   "chunk": QL, "context_max": int(lens.max()), "query_tokens": int(nq.sum()),
+                   "parallelism": "none (1 GPU)"},
+        "kernel_us": st,
+        "tflops": {"mla_prefill_rebuild_kv": f_rebuild / t_r / 1e12,
+                   "mla_prefill_attn": f_attn / t_a / 1e12},
+        "roofline": {"kernel": "mla_prefill_attn", "bound": "mfma",
+                     "achieved": f_attn / t_a / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": f_attn / t_a / 1e12 / 2500.0, "traffic": None,
+                     "algorithmic_flops_per_launch": f_attn},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def calibrate_copy():
     import torch
     n = 1 << 30
@@ -365,6 +447,9 @@ def main():
         return
     if args.mha:
         mha_baseline(args)
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
 
     wl = synth.workload(args.workload)

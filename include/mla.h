@@ -362,6 +362,47 @@ mla_status_t mla_gqa_decode(int32_t B, int32_t heads, int32_t kv_heads, int32_t 
                             float softmax_scale, void* o, int32_t o_dt, float* lse,
                             void* stream);
 
+/* Chunked prefill in the naive (rebuild) form, step 1 of 2 ([V2] §2.1: keys
+ * and values rebuilt from the latent; [LAT] §4.2-4.3: prefill of long inputs
+ * with a causal varlen attention; [REV] "2. 分块并行计算": the prompt in
+ * chunks).  For every sequence b and cached token t in [from_b, L_b)
+ * (from_b = rebuild_from[b], or 0 when rebuild_from is NULL; L_b =
+ * min(seq_lens[b], max_seq_len)) and every head i:
+ *   k[b][i][t][0:d_nope]        = W_UK[i] c_t     (fp32 accumulation, bf16 RNE)
+ *   k[b][i][t][d_nope:+d_rope]  = k_R,t           (copied)
+ *   vt[b][i][v][t]              = (W_UV[i] c_t)[v]
+ * k [B][h][kv_stride][d_nope + d_rope], vt [B][h][d_v][kv_stride] (values
+ * stored transposed: the layout the attention step reads), BF16, 16-byte
+ * aligned; kv_stride >= max_seq_len and a multiple of 32.  Rows outside
+ * [from_b, L_b) are not written: with rebuild_from the caller keeps the keys
+ * and values of earlier chunks and rebuilds only the new rows.  Cache: BF16,
+ * contiguous or paged (not a ring); w_uk, w_uv BF16; d_nope = d_v = 128.
+ * Errors: MLA_E_ARG, MLA_E_SHAPE (geometry), MLA_E_DTYPE, MLA_E_ALIGN,
+ * MLA_E_UNSUPPORTED (ring cache). */
+mla_status_t mla_prefill_rebuild_kv(const mla_dims_t* dims, int32_t B, const mla_cache_t* cache,
+                                    const int32_t* rebuild_from, const void* w_uk,
+                                    const void* w_uv, int32_t w_dt, void* k, void* vt,
+                                    int64_t kv_stride, void* stream);
+
+/* Chunked prefill, step 2 of 2: causal attention of a chunk of new tokens
+ * over the rebuilt keys and values.  Sequence b has n_b = min(q_lens[b], q_len)
+ * new tokens, the last n_b of its L_b = min(seq_lens[b], max_seq_len) cached
+ * tokens; query token j < n_b sits at position p = L_b - n_b + j and attends
+ * the tokens t <= p ([LAT] §4.2: causal=True):
+ *   s_t = scale * q[b][j][i] . k[b][i][t]                 (192 wide)
+ *   o[b][j][i][:] = sum_t e^{s_t} V[b][i][t][:] / sum_t e^{s_t}
+ *   lse[b][j][i]  = ln sum_t e^{s_t}
+ * (no token: o = 0, lse = -inf).  q [B][q_len][h][d_nope + d_rope] BF16, the
+ * un-absorbed query [q_C | q_R]; q_lens device int32 [B]; k, vt as written by
+ * mla_prefill_rebuild_kv; o [B][q_len][h][d_v] in o_dt (F32 or BF16); lse fp32
+ * [B][q_len][h] or NULL.  Rows j >= n_b are not written.  Errors as
+ * mla_prefill_rebuild_kv. */
+mla_status_t mla_prefill_attn(const mla_dims_t* dims, int32_t B, int32_t q_len,
+                              const int32_t* q_lens, const void* q, int32_t q_dt, const void* k,
+                              const void* vt, int64_t kv_stride, const int32_t* seq_lens,
+                              int32_t max_seq_len, void* o, int32_t o_dt, float* lse,
+                              void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mla_status_str(mla_status_t status);
 

@@ -98,6 +98,12 @@ def lib():
                                                          i32, vp, f32p, vp]
         L.mla_cache_ring_grow.restype = C.c_int
         L.mla_cache_ring_grow.argtypes = [i32, C.POINTER(CacheDesc), C.POINTER(CacheDesc), vp]
+        L.mla_prefill_rebuild_kv.restype = C.c_int
+        L.mla_prefill_rebuild_kv.argtypes = [C.POINTER(Dims), i32, C.POINTER(CacheDesc), vp, vp, vp,
+                                             i32, vp, vp, C.c_int64, vp]
+        L.mla_prefill_attn.restype = C.c_int
+        L.mla_prefill_attn.argtypes = [C.POINTER(Dims), i32, i32, vp, vp, i32, vp, vp, C.c_int64,
+                                       vp, i32, vp, i32, f32p, vp]
         L.mla_status_str.restype = C.c_char_p
         L.mla_status_str.argtypes = [C.c_int]
         L.mla_version.restype = C.c_int32
@@ -109,7 +115,7 @@ def lib():
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_decode_ex", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
             "mla_absorb_q_rope", "mla_cache_append", "mla_mha_decode", "mla_status_str",
             "mla_version", "mla_decode_combine_up_proj_noalloc", "mla_cache_ring_grow",
-            "mla_gqa_decode")
+            "mla_gqa_decode", "mla_prefill_rebuild_kv", "mla_prefill_attn")
 
 
 def status_str(status: int) -> str:
@@ -553,6 +559,60 @@ def mla_decode_combine_up_proj_noalloc(geo: Geometry, q_abs: torch.Tensor, cache
                    (C.byref(d), B, _ptr(q_abs), dtype_code(q_abs), C.byref(cd), int(num_splits),
                     _ptr(w_uv), dtype_code(w_uv), _ptr(o), dtype_code(o), _ptr(u), _ptr(lse),
                     _stream(stream)), (d, cd), prepare)
+
+
+def mla_prefill_rebuild_kv(geo: Geometry, cache: Cache, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                           k: torch.Tensor, vt: torch.Tensor,
+                           rebuild_from: Optional[torch.Tensor] = None, stream=None,
+                           prepare: bool = False):
+    """Naive-form keys k [B, h, kv_stride, 192] and transposed values vt [B, h,
+    128, kv_stride] (bfloat16) of the cached tokens [rebuild_from[b], L_b)."""
+    B = int(cache.seq_lens.shape[0])
+    H = geo.heads
+    if k.dim() != 4:
+        raise ValueError("k must be [B, h, kv_stride, d_nope + d_rope]")
+    S = int(k.shape[2])
+    _need("k", k, (B, H, S, geo.d_nope + geo.d_rope), (torch.bfloat16,))
+    _need("vt", vt, (B, H, geo.d_v, S), (torch.bfloat16,))
+    _need("w_uk", w_uk, (H, geo.d_nope, geo.d_latent), (torch.bfloat16,))
+    _need("w_uv", w_uv, (H, geo.d_v, geo.d_latent), (torch.bfloat16,))
+    _need("rebuild_from", rebuild_from, (B,), (torch.int32,), optional=True)
+    _need_cache(cache, B, geo)
+    _on_gpu(k, vt, w_uk, w_uv, rebuild_from, *_cache_tensors(cache))
+    d = geo.c()
+    cd = cache.c()
+    return _launch("mla_prefill_rebuild_kv",
+                   (C.byref(d), B, C.byref(cd), _ptr(rebuild_from), _ptr(w_uk), _ptr(w_uv),
+                    dtype_code(w_uk), _ptr(k), _ptr(vt), S, _stream(stream)), (d, cd), prepare)
+
+
+def mla_prefill_attn(geo: Geometry, q: torch.Tensor, q_lens: torch.Tensor, k: torch.Tensor,
+                     vt: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, o: torch.Tensor,
+                     lse: Optional[torch.Tensor] = None, stream=None, prepare: bool = False):
+    """Causal attention of each sequence's last q_lens[b] cached tokens (queries
+    q [B, q_len, h, 192] = [q_C | q_R], bfloat16) over k / vt from
+    mla_prefill_rebuild_kv -> o [B, q_len, h, 128], lse [B, q_len, h]."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, q_len, h, 192] and k [B, h, kv_stride, 192]")
+    B, QL = int(q.shape[0]), int(q.shape[1])
+    H = geo.heads
+    S = int(k.shape[2])
+    W = geo.d_nope + geo.d_rope
+    _need("q", q, (B, QL, H, W), (torch.bfloat16,))
+    _need("q_lens", q_lens, (B,), (torch.int32,))
+    _need("k", k, (B, H, S, W), (torch.bfloat16,))
+    _need("vt", vt, (B, H, geo.d_v, S), (torch.bfloat16,))
+    _need("seq_lens", seq_lens, (B,), (torch.int32,))
+    _need("o", o, (B, QL, H, geo.d_v), _FLOAT)
+    _need("lse", lse, (B, QL, H), (torch.float32,), optional=True)
+    if not 0 <= int(max_seq_len) <= S:
+        raise ValueError("max_seq_len must lie in [0, kv_stride]")
+    _on_gpu(q, q_lens, k, vt, seq_lens, o, lse)
+    d = geo.c()
+    return _launch("mla_prefill_attn",
+                   (C.byref(d), B, QL, _ptr(q_lens), _ptr(q), dtype_code(q), _ptr(k), _ptr(vt), S,
+                    _ptr(seq_lens), int(max_seq_len), _ptr(o), dtype_code(o), _ptr(lse),
+                    _stream(stream)), (d,), prepare)
 
 
 def split_chunk(max_seq_len: int, num_splits: int) -> int:

@@ -44,6 +44,9 @@ def lib():
         L.oracle_mla_decode.argtypes = [C.POINTER(_Problem), C.c_void_p, C.c_void_p, C.c_int32,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p]
+        L.oracle_rebuild_kv.restype = C.c_int
+        L.oracle_rebuild_kv.argtypes = [C.POINTER(_Problem), C.c_int32, C.c_int32, C.c_int32,
+                                        C.c_void_p, C.c_void_p]
         L.oracle_absorb_q.restype = C.c_int
         L.oracle_absorb_q.argtypes = [C.c_int32] * 5 + [C.c_void_p, C.c_void_p, C.c_int32,
                                                         C.c_void_p, C.c_int32, C.c_void_p]
@@ -147,6 +150,42 @@ def decode(q_nope, q_rope, q_dtype, w_uk, w_uv, w_dtype, rows, cache_dtype, seq_
     if rc != 0:
         raise ValueError(f"oracle_mla_decode failed: {rc}")
     return o, lse, u
+
+
+def rebuild_kv(q_nope, q_rope, q_dtype, w_uk, w_uv, w_dtype, rows, cache_dtype, seq_lens, b,
+               t_begin, t_end, *, row_scale=None, page_size: int = 0,
+               seq_stride: Optional[int] = None, block_table=None):
+    """The naive form's keys and values of sequence b, tokens [t_begin, t_end):
+    (k [H, n, d_nope + d_rope], v [H, n, d_v]) float64 (arguments as decode)."""
+    qd, wd, cd = _dt(q_dtype), _dt(w_dtype), _dt(cache_dtype)
+    q_nope, q_rope = _arr(q_nope, qd), _arr(q_rope, qd)
+    w_uk, w_uv, rows = _arr(w_uk, wd), _arr(w_uv, wd), _arr(rows, cd)
+    B, H, dn = q_nope.shape
+    dr, dl, dv = q_rope.shape[2], w_uk.shape[2], w_uv.shape[1]
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    rs = None if row_scale is None else np.ascontiguousarray(row_scale, dtype=np.float32)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    if seq_stride is None:
+        seq_stride = int(seq_lens.max()) if B else 0
+    P = _Problem(B, H, dn, dr, dl, dv, 0.0, _ptr(q_nope), _ptr(q_rope), qd, _ptr(w_uk),
+                 _ptr(w_uv), wd, _ptr(rows), _ptr(rs), cd, int(page_size), int(seq_stride),
+                 _ptr(bt), 0 if bt is None else int(bt.shape[1]), _ptr(seq_lens), 0)
+    n = int(t_end) - int(t_begin)
+    k = np.zeros((H, n, dn + dr), dtype=np.float64)
+    v = np.zeros((H, n, dv), dtype=np.float64)
+    rc = lib().oracle_rebuild_kv(C.byref(P), int(b), int(t_begin), int(t_end), _ptr(k), _ptr(v))
+    if rc != 0:
+        raise ValueError(f"oracle_rebuild_kv failed: {rc}")
+    return k, v
+
+
+def rebuild_kv_inputs(inp, b, t_begin, t_end):
+    """rebuild_kv() on a synth.MLAInputs-like object."""
+    wl = inp.wl
+    return rebuild_kv(inp.q_nope, inp.q_rope, wl.act_dtype, inp.w_uk, inp.w_uv, wl.act_dtype,
+                      inp.rows, wl.cache_dtype, inp.seq_lens, b, t_begin, t_end,
+                      row_scale=inp.row_scale, page_size=wl.page_size,
+                      seq_stride=inp.seq_stride, block_table=inp.block_table)
 
 
 def decode_inputs(inp, sel=None, want_u=False, t_begin=None, t_end=None, scale=None,

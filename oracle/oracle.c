@@ -224,6 +224,42 @@ int oracle_mla_decode(const oracle_mla_problem* P, const int32_t* sel_b,
   return err;
 }
 
+/* The naive form's rebuild ([V2] §2.1, [DSA]'s MLA listing): for sequence b
+ * and every cached token t in [t_begin, t_end), each head's key is the
+ * concatenation of the rebuilt content key W_UK[h]·c_t and the shared k_R,t
+ * ([V2] §2.2), and its value W_UV[h]·c_t.  k [H][n_t][d_nope + d_rope],
+ * v [H][n_t][d_v], n_t = t_end - t_begin, float64. */
+int oracle_rebuild_kv(const oracle_mla_problem* P, int32_t b, int32_t t_begin, int32_t t_end,
+                      double* k, double* v) {
+  if (!P || !k || !v || b < 0 || b >= P->B || t_begin < 0 || t_end < t_begin) return -1;
+  const int32_t dn = P->d_nope, dr = P->d_rope, dl = P->d_latent, dv = P->d_v;
+  const int64_t nt = t_end - t_begin;
+  double* c = malloc(sizeof(double) * (dl + dr));
+  if (!c) return -5;
+  for (int64_t t = 0; t < nt; ++t) {
+    load_row(P, row_of(P, b, t_begin + t), c);
+    for (int32_t h = 0; h < P->H; ++h) {
+      double* kr = k + ((int64_t)h * nt + t) * (dn + dr);
+      double* vr = v + ((int64_t)h * nt + t) * dv;
+      for (int32_t i = 0; i < dn; ++i) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < dl; ++j)
+          acc += load_elem(P->w_uk, P->w_dtype, ((int64_t)h * dn + i) * dl + j) * c[j];
+        kr[i] = acc;
+      }
+      for (int32_t i = 0; i < dr; ++i) kr[dn + i] = c[dl + i];
+      for (int32_t i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < dl; ++j)
+          acc += load_elem(P->w_uv, P->w_dtype, ((int64_t)h * dv + i) * dl + j) * c[j];
+        vr[i] = acc;
+      }
+    }
+  }
+  free(c);
+  return 0;
+}
+
 /* ------------------------------------------------------- the other calls */
 
 /* Absorbing W_UK into the query ([V2] §2.3, §4.1): the content score

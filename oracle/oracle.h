@@ -58,6 +58,9 @@ int oracle_mla_decode(const oracle_mla_problem* P, const int32_t* sel_b,
 
 /* q_abs[b][h][:d_latent] = sum_n q_nope[b][h][n] * W_UK[h][n][:] ;
  * q_abs[b][h][d_latent:] = q_rope[b][h][:]  (float64 out) */
+int oracle_rebuild_kv(const oracle_mla_problem* P, int32_t b, int32_t t_begin, int32_t t_end,
+                      double* k, double* v);
+
 int oracle_absorb_q(int32_t B, int32_t H, int32_t d_nope, int32_t d_rope,
                     int32_t d_latent, const void* q_nope, const void* q_rope,
                     int32_t q_dtype, const void* w_uk, int32_t w_dtype,

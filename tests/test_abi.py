@@ -320,3 +320,28 @@ def test_ring_cache_validation():
     assert L.mla_cache_ring_grow(2, C.byref(src), C.byref(cache(ring=1, rows=P + 8)), None) == E_ALIGN
     fp8 = cache(ring=1, dtype=FP8, row_scale=P)
     assert L.mla_cache_ring_grow(2, C.byref(fp8), C.byref(cache(ring=1, dtype=FP8)), None) == E_ARG
+
+
+def test_prefill_validation():
+    L = mla.lib()
+    d = dims()
+    c = cache(seq_stride=4096, max_seq_len=4096)
+
+    def rb(d=d, B=2, c=c, frm=None, wk=P, wv=P, w_dt=BF16, k=P, vt=P, S=4096):
+        return L.mla_prefill_rebuild_kv(C.byref(d), B, C.byref(c), frm, wk, wv, w_dt, k, vt, S, None)
+
+    def at(d=d, B=2, QL=64, ql=P, q=P, q_dt=BF16, k=P, vt=P, S=4096, sl=P, msl=4096, o=P,
+           o_dt=BF16):
+        return L.mla_prefill_attn(C.byref(d), B, QL, ql, q, q_dt, k, vt, S, sl, msl, o, o_dt,
+                                  None, None)
+
+    assert rb(B=0) == OK and at(B=0) == OK and at(QL=0) == OK
+    assert rb(wk=None) == E_ARG and rb(k=None) == E_ARG and rb(c=cache(rows=None)) == E_ARG
+    assert rb(S=4064) == E_ARG and rb(S=4100) == E_ARG          # < max_seq_len, not x32
+    assert rb(d=dims(dn=64)) == E_SHAPE and rb(d=dims(dv=64)) == E_SHAPE
+    assert rb(w_dt=F32) == E_DTYPE and rb(c=cache(dtype=F32)) == E_DTYPE
+    assert rb(c=cache(ring=1, seq_stride=4096)) == E_UNSUP
+    assert rb(k=P + 8) == E_ALIGN
+    assert at(q=None) == E_ARG and at(ql=None) == E_ARG and at(S=4000) == E_ARG
+    assert at(q_dt=F32) == E_DTYPE and at(o_dt=FP8) == E_DTYPE
+    assert at(d=dims(dn=192)) == E_SHAPE and at(o=P + 4) == E_ALIGN

@@ -16,6 +16,7 @@ from . import test_oracle_append as append
 from . import test_oracle_codecs as codecs
 from . import test_oracle_mha as mha
 from . import test_oracle_pins as pins
+from . import test_oracle_prefill as prefill
 from . import test_oracle_ring as ring
 from . import test_oracle_rope as rope
 
@@ -79,6 +80,9 @@ MUTANTS = {
     "mha_missing_normalisation": ("for (int32_t j = 0; j < d_v; ++j) out[j] /= l;", ""),
     "mha_key_stride": ("load_elem(k, dtype, (kv * seq_stride + t) * d_qk + j)",
                        "load_elem(k, dtype, (kv * seq_stride + t) * d_v + j)"),
+    "rebuild_key_drops_rope": ("for (int32_t i = 0; i < dr; ++i) kr[dn + i] = c[dl + i];", ""),
+    "rebuild_value_uses_w_uk": ("acc += load_elem(P->w_uv, P->w_dtype, ((int64_t)h * dv + i) * dl + j) * c[j];",
+                                "acc += load_elem(P->w_uk, P->w_dtype, ((int64_t)h * dv + i) * dl + j) * c[j];"),
     "gqa_strided_groups": ("const int64_t kvh = h / G;", "const int64_t kvh = h % H_kv;"),
     "gqa_values_of_head_zero": ("const int64_t kv = b * H_kv + kvh;", "const int64_t kv = b * H_kv;"),
     "rope_angle_in_double": ("const float theta = pos * inv_freq[i]; /* binary32 product */",
@@ -121,6 +125,8 @@ PIN_CHECKS = [
     mha.test_closed_forms,
     lambda: mha.test_gqa_matches_library_grouped_attention(8, 2),
     mha.test_mqa_is_mla_with_identity_up_projections,
+    prefill.test_rebuilt_keys_and_values_reproduce_the_decode,
+    prefill.test_sub_range_is_a_slice_and_paged_equals_contiguous,
 ]
 
 
@@ -148,7 +154,7 @@ def test_pins_catch_planted_mistake(tmp_path, name, monkeypatch):
                "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_array",
                "oracle_mla_cache_bytes_per_token", "oracle_mha_cache_bytes",
                "oracle_num_threads", "oracle_cache_append", "oracle_encode_e4m3",
-               "oracle_rope", "oracle_rope_inv_freq", "oracle_mha_decode", "oracle_ring_grow", "oracle_gqa_decode"):
+               "oracle_rope", "oracle_rope_inv_freq", "oracle_mha_decode", "oracle_ring_grow", "oracle_gqa_decode", "oracle_rebuild_kv"):
         getattr(mut, fn).restype = getattr(good, fn).restype
         getattr(mut, fn).argtypes = getattr(good, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mut)
