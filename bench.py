@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--workload", default="paged_b64_ragged")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--decode-kernel", default="auto", choices=["auto", "h64", "h128"],
+    ap.add_argument("--decode-kernel", default="auto", choices=["auto", "h64", "h128", "h128ws"],
                     help="decode work decomposition (mla_decode_ex); auto = mla_decode's choice")
     ap.add_argument("--replica-bytes", type=float, default=1.25 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -488,7 +488,8 @@ def main():
     # W_UV product run as one launch (mla_combine_up_proj; u is not stored)
     fused = step.fused_tail(dev.w_uv) and not args.two_call_tail
 
-    kernel = {"auto": mla.KERNEL_AUTO, "h64": mla.KERNEL_H64, "h128": mla.KERNEL_H128}[args.decode_kernel]
+    kernel = {"auto": mla.KERNEL_AUTO, "h64": mla.KERNEL_H64, "h128": mla.KERNEL_H128,
+              "h128ws": mla.KERNEL_H128_WS}[args.decode_kernel]
 
     def decode(rp, prepare=False):
         return mla.mla_decode_ex(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,

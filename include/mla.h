@@ -210,12 +210,22 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
  *   MLA_KERNEL_H128 -- one workgroup per (sequence, split range, 128 heads):
  *                      each tile enters one CU once for all of its heads.
  *                      BF16 cache, h a multiple of 128.
+ *   MLA_KERNEL_H128_WS -- one workgroup per (sequence, split range, 128
+ *                      heads) of 12 waves: 4 compute the scores and the
+ *                      softmax of 32 heads each, 8 the value product of 64
+ *                      heads x 128 latent columns each, three waves per SIMD.
+ *                      BF16 cache, h a multiple of 128.
  *   MLA_KERNEL_AUTO -- what mla_decode and mla_decode_multi use: H64, which
  *                      measured as fast or faster than H128 on every bf16
  *                      workload and split count tried (H128 runs one wave per
  *                      SIMD, which leaves the matrix cores idle while a wave
  *                      waits on LDS, the tile DMA or its softmax). */
-typedef enum { MLA_KERNEL_AUTO = 0, MLA_KERNEL_H64 = 1, MLA_KERNEL_H128 = 2 } mla_decode_kernel_t;
+typedef enum {
+  MLA_KERNEL_AUTO = 0,
+  MLA_KERNEL_H64 = 1,
+  MLA_KERNEL_H128 = 2,
+  MLA_KERNEL_H128_WS = 3
+} mla_decode_kernel_t;
 
 /* mla_decode_multi with the decode kernel chosen by the caller (`kernel`, an
  * mla_decode_kernel_t).  q_len = 1 is mla_decode.  MLA_KERNEL_H128 for a cache

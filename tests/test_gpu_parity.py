@@ -47,11 +47,11 @@ def test_tiny_f32_every_output(splits):
 RAGGED = [0, 1, 31, 32, 45, 300, 257]
 
 
-H64, H128 = mla.KERNEL_H64, mla.KERNEL_H128
+H64, H128, W12 = mla.KERNEL_H64, mla.KERNEL_H128, mla.KERNEL_H128_WS
 
 
 @pytest.mark.parametrize("heads,kernel", [(32, H64), (128, H64), (128, H128), (160, H64),
-                                          (256, H64), (256, H128)])
+                                          (256, H64), (256, H128), (128, W12), (256, W12)])
 @pytest.mark.parametrize("splits", [1, 3, 7])
 def test_ragged_bf16(heads, kernel, splits):
     """bf16, several tiles plus ragged tails, empty and 1-token sequences, on
@@ -67,7 +67,7 @@ def test_ragged_bf16(heads, kernel, splits):
     _log(f"  err o/u/lse = {e}")
 
 
-@pytest.mark.parametrize("kernel", [H64, H128])
+@pytest.mark.parametrize("kernel", [H64, H128, W12])
 @pytest.mark.parametrize("part", ["f32", "bf16"])
 def test_ragged_fp32_partials(part, kernel):
     """The same bf16 problem with fp32 or bf16 split partials."""
@@ -122,7 +122,7 @@ def test_fp8_codes_exact():
         assert np.array_equal(got, np.broadcast_to(want[b], got.shape)), b
 
 
-@pytest.mark.parametrize("kernel", [H64, H128])
+@pytest.mark.parametrize("kernel", [H64, H128, W12])
 def test_paged_matches_contiguous_bitwise(kernel):
     """The same tokens in a shuffled paged pool and in contiguous rows give
     bit-identical partials (the tiles see the same rows in the same order)."""
@@ -139,7 +139,7 @@ def test_paged_matches_contiguous_bitwise(kernel):
     check_against_oracle(paged, a, pairs, TOL["bf16"])
 
 
-@pytest.mark.parametrize("kernel", [H64, H128])
+@pytest.mark.parametrize("kernel", [H64, H128, W12])
 def test_split_count_invariance(kernel):
     """Different split counts give the same result.  With a zero query every
     score is 0, so every probability is exactly 1 in bf16 and u is the plain
@@ -181,7 +181,7 @@ def test_split_count_random_inputs():
         assert err < 1e-2, (s, err)
 
 
-@pytest.mark.parametrize("kernel", [H64, H128])
+@pytest.mark.parametrize("kernel", [H64, H128, W12])
 def test_max_splits(kernel):
     """The largest split count the ABI takes (1024): 64-token ranges over a
     40,000-token sequence, most ranges of the short and the empty sequence
@@ -197,7 +197,8 @@ def test_max_splits(kernel):
     _log(f"  err o/u/lse = {e}")
 
 
-SPIKE_CASES = [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("fp8_b1_l128k", H64)]
+SPIKE_CASES = [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("dsv2_b32_l2k", W12),
+               ("fp8_b1_l128k", H64)]
 
 
 @pytest.mark.parametrize("name,kernel", SPIKE_CASES)
@@ -236,7 +237,7 @@ def test_score_spike_recomputes_range(name, kernel):
         _log(f"  S={splits}: err o/u/lse = {e}")
 
 
-@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128),
+@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("dsv2_b32_l2k", W12),
                                          ("tiny_f32", H64)])
 def test_custom_softmax_scale(name, kernel):
     """A caller-given softmax scale (0.05) replaces 1/sqrt(d_nope + d_rope)."""
@@ -254,7 +255,7 @@ def test_custom_softmax_scale(name, kernel):
     assert np.abs(np.array([lse[b, h] for b, h in pairs]) - lse_ref).max() <= TOL[kind]
 
 
-@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128),
+@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("dsv2_b32_l2k", W12),
                                          ("fp8_b1_l128k", H64)])
 def test_nan_in_a_read_row_propagates(name, kernel):
     """A NaN in a cached row that is attended (a bf16 NaN, or the E4M3 NaN
@@ -286,7 +287,7 @@ def test_nan_in_a_read_row_propagates(name, kernel):
         assert np.abs(got - o_ref).max() <= tol * np.abs(o_ref).max()
 
 
-@pytest.mark.parametrize("kernel", [H64, H128])
+@pytest.mark.parametrize("kernel", [H64, H128, W12])
 def test_large_batch_of_short_sequences(kernel):
     """300 sequences of 0-120 tokens: many 32-sequence tiles in the absorb (the
     staged query rows are replaced tile after tile), many merge workgroups,
@@ -322,6 +323,9 @@ AUTO = mla.KERNEL_AUTO
 FULL = [
     ("dsv2_b32_l2k", "bf16", 8, 8, AUTO, 1),
     ("dsv2_b32_l2k", "bf16", 4, 4, H128, 1),
+    ("dsv2_b32_l2k", "bf16", 8, 8, W12, 1),
+    ("long_b4_l32k", "bf16", 4, 8, W12, 1),
+    ("paged_b64_ragged", "bf16", 8, 8, W12, 2),
     ("long_b4_l32k", "bf16", 4, 8, AUTO, 1),
     ("long_b4_l32k", "bf16", 4, 3, H64, 1),
     ("paged_b64_ragged", "bf16", 8, 8, AUTO, 2),
