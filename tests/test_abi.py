@@ -262,8 +262,10 @@ def test_decode_ex_kernel_choice_validation():
                                kernel, None)
 
     assert dx(mla.KERNEL_H128, B=0) == OK
-    assert dx(3) == E_ARG
+    assert dx(4) == E_ARG
     assert dx(-1) == E_ARG
+    assert dx(mla.KERNEL_H128_WS, h=64) == E_UNSUP
+    assert dx(mla.KERNEL_H128_WS, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP
     assert dx(mla.KERNEL_H128, h=64) == E_UNSUP
     assert dx(mla.KERNEL_H128, h=160) == E_UNSUP
     assert dx(mla.KERNEL_H128, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP
