@@ -47,6 +47,14 @@ def lib():
         L.oracle_rebuild_kv.restype = C.c_int
         L.oracle_rebuild_kv.argtypes = [C.POINTER(_Problem), C.c_int32, C.c_int32, C.c_int32,
                                         C.c_void_p, C.c_void_p]
+        L.oracle_absorbed_decode.restype = C.c_int
+        L.oracle_absorbed_decode.argtypes = [C.POINTER(_Problem), C.c_void_p, C.c_int32,
+                                             C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                             C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                             C.c_void_p]
+        L.oracle_quantize_e4m3_rows.restype = C.c_int
+        L.oracle_quantize_e4m3_rows.argtypes = [C.c_int64, C.c_int32, C.c_void_p, C.c_void_p,
+                                                C.c_void_p]
         L.oracle_absorb_q.restype = C.c_int
         L.oracle_absorb_q.argtypes = [C.c_int32] * 5 + [C.c_void_p, C.c_void_p, C.c_int32,
                                                         C.c_void_p, C.c_int32, C.c_void_p]
@@ -197,6 +205,75 @@ def decode_inputs(inp, sel=None, want_u=False, t_begin=None, t_end=None, scale=N
                   page_size=wl.page_size, seq_stride=inp.seq_stride,
                   block_table=inp.block_table, scale=scale, sel=sel, t_begin=t_begin,
                   t_end=t_end, want_u=want_u, ring=ring)
+
+
+def absorbed_decode(q_abs, q_dtype, rows, cache_dtype, seq_lens, *, q_scale=None,
+                    row_scale=None, page_size: int = 0, seq_stride: Optional[int] = None,
+                    block_table=None, scale: Optional[float] = None, d_nope: int = 128,
+                    w_uv=None, w_dtype="bf16", sel: Optional[Sequence[tuple]] = None,
+                    t_begin=None, t_end=None, ring: bool = False):
+    """Absorbed-form attention for a given q_abs [B, H, d_latent + d_rope]
+    (stored bits in q_dtype; E4M3 with q_scale [B, H]).  Returns (u [n,
+    d_latent], lse [n], o [n, d_v] or None) float64 for the selected (b, h)
+    pairs or all B*H in order; o needs w_uv [H, d_v, d_latent]."""
+    qd, cd, wd = _dt(q_dtype), _dt(cache_dtype), _dt(w_dtype)
+    q_abs = _arr(q_abs, qd)
+    rows = _arr(rows, cd)
+    B, H, w = q_abs.shape
+    dr = 64 if w > 64 else 0
+    dl = w - dr
+    assert rows.shape[-1] == w
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qs = None if q_scale is None else np.ascontiguousarray(q_scale, dtype=np.float32)
+    rs = None if row_scale is None else np.ascontiguousarray(row_scale, dtype=np.float32)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    wv = None if w_uv is None else _arr(w_uv, wd)
+    dv = 0 if wv is None else int(wv.shape[1])
+    if seq_stride is None:
+        seq_stride = int(seq_lens.max()) if B else 0
+    P = _Problem(B, H, int(d_nope), dr, dl, dv, float(scale) if scale else 0.0, None, None, 0,
+                 None, _ptr(wv), wd, _ptr(rows), _ptr(rs), cd, int(page_size), int(seq_stride),
+                 _ptr(bt), 0 if bt is None else int(bt.shape[1]), _ptr(seq_lens), int(bool(ring)))
+    if sel is None:
+        n = B * H
+        sb = sh = None
+    else:
+        sel = list(sel)
+        n = len(sel)
+        sb = np.ascontiguousarray([x[0] for x in sel], dtype=np.int32)
+        sh = np.ascontiguousarray([x[1] for x in sel], dtype=np.int32)
+    tb = None if t_begin is None else np.ascontiguousarray(t_begin, dtype=np.int32)
+    te = None if t_end is None else np.ascontiguousarray(t_end, dtype=np.int32)
+    u = np.zeros((n, dl), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    o = None if wv is None else np.zeros((n, dv), dtype=np.float64)
+    rc = lib().oracle_absorbed_decode(C.byref(P), _ptr(q_abs), qd, _ptr(qs), _ptr(sb), _ptr(sh),
+                                      n, _ptr(tb), _ptr(te), _ptr(u), _ptr(lse), _ptr(o))
+    if rc != 0:
+        raise ValueError(f"oracle_absorbed_decode failed: {rc}")
+    return u, lse, o
+
+
+def quantize_e4m3_rows(x):
+    """E4M3 codes and one fp32 factor per row of the binary32 array x [..., w]
+    (the E4M3 cache rule).  Returns (codes uint8 like x, scale float32 x.shape[:-1])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = x.shape[-1]
+    n = x.size // w
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scale = np.zeros(x.shape[:-1], dtype=np.float32)
+    rc = lib().oracle_quantize_e4m3_rows(n, w, _ptr(x), _ptr(codes), _ptr(scale))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_e4m3_rows failed: {rc}")
+    return codes, scale
+
+
+def absorb_q_fp8(q_nope, q_rope, q_dtype, w_uk, w_dtype):
+    """The absorbed query in E4M3 with one factor per (b, h): the float64
+    absorbed rows rounded to binary32, then quantize_e4m3_rows.  Returns
+    (codes [B, H, d_latent + d_rope] uint8, scale [B, H] float32)."""
+    qa = absorb_q(q_nope, q_rope, q_dtype, w_uk, w_dtype)
+    return quantize_e4m3_rows(qa.astype(np.float32))
 
 
 def absorb_q(q_nope, q_rope, q_dtype, w_uk, w_dtype):

@@ -260,6 +260,98 @@ int oracle_rebuild_kv(const oracle_mla_problem* P, int32_t b, int32_t t_begin, i
   return 0;
 }
 
+/* Attention of an absorbed query over the cached latent rows ([V2] §2.3:
+ * with W_UK folded into the query the score of token t is the dot product of
+ * the query row [q~ | q_R] with the cached row [c_KV | k_R], times the softmax
+ * scale; the weights multiply c_KV itself, and W_UV is applied to the weighted
+ * mean afterwards).  q_abs [B][H][d_latent + d_rope] in q_dtype; an E4M3
+ * query carries one factor per (b, h) in q_scale (value = code x factor, the
+ * rows' own convention).  Cache, selection and token ranges as in
+ * oracle_mla_decode.  Outputs per selected pair: u [d_latent], lse, and
+ * o [d_v] = W_UV[h] u when o is not NULL (P->w_uv, P->w_dtype). */
+int oracle_absorbed_decode(const oracle_mla_problem* P, const void* q_abs, int32_t q_dtype,
+                           const float* q_scale, const int32_t* sel_b, const int32_t* sel_h,
+                           int32_t n_sel, const int32_t* t_begin, const int32_t* t_end,
+                           double* u, double* lse, double* o) {
+  if (!P || !q_abs || !u || !lse) return -1;
+  if (P->B < 0 || P->H <= 0 || P->d_rope < 0 || P->d_latent <= 0 || (o && P->d_v <= 0)) return -2;
+  if (!valid_dtype(q_dtype) || !valid_dtype(P->cache_dtype) || (o && !valid_dtype(P->w_dtype)))
+    return -3;
+  if ((q_dtype == ORACLE_E4M3 && !q_scale) || (P->cache_dtype == ORACLE_E4M3 && !P->row_scale))
+    return -4;
+  if (P->page_size > 0 && !P->block_table) return -5;
+  if (P->ring && (P->page_size > 0 || P->seq_stride < 1)) return -7;
+  if (o && !P->w_uv) return -1;
+  const int32_t all = (sel_b == NULL);
+  const int64_t n = all ? (int64_t)P->B * P->H : n_sel;
+  const double scale =
+      P->scale > 0 ? P->scale : 1.0 / sqrt((double)P->d_nope + (double)P->d_rope);
+  const int32_t dl = P->d_latent, w = P->d_latent + P->d_rope;
+  int err = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t idx = 0; idx < n; ++idx) {
+    const int32_t b = all ? (int32_t)(idx / P->H) : sel_b[idx];
+    const int32_t h = all ? (int32_t)(idx % P->H) : sel_h[idx];
+    if (b < 0 || b >= P->B || h < 0 || h >= P->H) {
+      err = -6;
+      continue;
+    }
+    int64_t L = P->seq_lens[b];
+    int64_t t0 = t_begin ? t_begin[b] : 0;
+    int64_t t1 = t_end ? t_end[b] : L;
+    if (t0 < 0) t0 = 0;
+    if (t1 > L) t1 = L;
+    if (P->ring && L - t0 > P->seq_stride) t0 = L - P->seq_stride; /* ring window */
+    double* out_u = u + idx * dl;
+    for (int32_t j = 0; j < dl; ++j) out_u[j] = 0.0;
+    if (o)
+      for (int32_t v = 0; v < P->d_v; ++v) o[idx * P->d_v + v] = 0.0;
+    if (t1 <= t0) {
+      lse[idx] = -INFINITY;
+      continue;
+    }
+    const int64_t nt = t1 - t0;
+    double* q = malloc(sizeof(double) * w);
+    double* c = malloc(sizeof(double) * w);
+    double* s = malloc(sizeof(double) * nt);
+    const int64_t qrow = (int64_t)b * P->H + h;
+    const double qf = q_dtype == ORACLE_E4M3 ? (double)q_scale[qrow] : 1.0;
+    for (int32_t j = 0; j < w; ++j) q[j] = load_elem(q_abs, q_dtype, qrow * w + j) * qf;
+    /* scores over the whole 576-wide rows */
+    for (int64_t t = 0; t < nt; ++t) {
+      load_row(P, row_of(P, b, t0 + t), c);
+      double dot = 0.0;
+      for (int32_t j = 0; j < w; ++j) dot += q[j] * c[j];
+      s[t] = scale * dot;
+    }
+    double m = -INFINITY;
+    for (int64_t t = 0; t < nt; ++t)
+      if (s[t] > m) m = s[t];
+    double l = 0.0;
+    for (int64_t t = 0; t < nt; ++t) {
+      s[t] = exp(s[t] - m);
+      l += s[t];
+    }
+    /* weighted mean of the latents c_KV */
+    for (int64_t t = 0; t < nt; ++t) {
+      load_row(P, row_of(P, b, t0 + t), c);
+      for (int32_t j = 0; j < dl; ++j) out_u[j] += s[t] * c[j];
+    }
+    for (int32_t j = 0; j < dl; ++j) out_u[j] /= l;
+    lse[idx] = log(l) + m;
+    if (o)
+      for (int32_t v = 0; v < P->d_v; ++v) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < dl; ++j)
+          acc += load_elem(P->w_uv, P->w_dtype, ((int64_t)h * P->d_v + v) * dl + j) * out_u[j];
+        o[idx * P->d_v + v] = acc;
+      }
+    free(q); free(c); free(s);
+  }
+  return err;
+}
+
 /* ------------------------------------------------------- the other calls */
 
 /* Absorbing W_UK into the query ([V2] §2.3, §4.1): the content score
@@ -371,6 +463,23 @@ uint8_t oracle_encode_e4m3(float y) {
   return (uint8_t)(sign | (uint8_t)(((k + 7) << 3) | ((int)q - 8)));
 }
 
+/* One row of w binary32 values in E4M3 with one fp32 factor ([DSA]'s FP8
+ * cache; the factor maps the row's largest magnitude onto E4M3's largest
+ * finite value 448): s = fl32(max(amax, 2^-126) / 448), each code the E4M3
+ * value nearest to fl32(x / s) after clamping to +-448. */
+static void quantize_row_e4m3(const float* x, int32_t w, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int32_t j = 0; j < w; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  const float s = fmaxf(amax, 0x1p-126f) / 448.0f;
+  *scale = s;
+  for (int32_t j = 0; j < w; ++j) {
+    float y = x[j] / s;
+    if (y > 448.0f) y = 448.0f;
+    if (y < -448.0f) y = -448.0f;
+    codes[j] = oracle_encode_e4m3(y);
+  }
+}
+
 static void round_bf16(float x, uint16_t* out) {
   /* nearest bf16 (the binary32 values whose low 16 bits are zero), ties to
    * the even one: compare with the two neighbours in double */
@@ -422,19 +531,17 @@ int oracle_cache_append(int32_t B, int32_t d_latent, int32_t d_rope, const void*
     } else if (cache_dtype == ORACLE_BF16) {
       for (int32_t j = 0; j < w; ++j) round_bf16(x[j], (uint16_t*)rows + row * w + j);
     } else {
-      float amax = 0.0f;
-      for (int32_t j = 0; j < w; ++j) amax = fmaxf(amax, fabsf(x[j]));
-      const float s = fmaxf(amax, 0x1p-126f) / 448.0f;
-      row_scale[row] = s;
-      for (int32_t j = 0; j < w; ++j) {
-        float y = x[j] / s;
-        if (y > 448.0f) y = 448.0f;
-        if (y < -448.0f) y = -448.0f;
-        ((uint8_t*)rows)[row * w + j] = oracle_encode_e4m3(y);
-      }
+      quantize_row_e4m3(x, w, (uint8_t*)rows + row * w, row_scale + row);
     }
   }
   free(x);
+  return 0;
+}
+
+int oracle_quantize_e4m3_rows(int64_t n, int32_t w, const float* x, uint8_t* codes,
+                              float* scale) {
+  if (n < 0 || w <= 0 || (n > 0 && (!x || !codes || !scale))) return -1;
+  for (int64_t r = 0; r < n; ++r) quantize_row_e4m3(x + r * w, w, codes + r * w, scale + r);
   return 0;
 }
 

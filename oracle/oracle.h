@@ -56,11 +56,31 @@ int oracle_mla_decode(const oracle_mla_problem* P, const int32_t* sel_b,
                       const int32_t* sel_h, int32_t n_sel, const int32_t* t_begin,
                       const int32_t* t_end, double* o, double* lse, double* u);
 
-/* q_abs[b][h][:d_latent] = sum_n q_nope[b][h][n] * W_UK[h][n][:] ;
- * q_abs[b][h][d_latent:] = q_rope[b][h][:]  (float64 out) */
+/* The naive form's per-head keys and values of sequence b's tokens
+ * [t_begin, t_end): k [H][n_t][d_nope + d_rope] = [W_UK[h] c_t ; k_R,t],
+ * v [H][n_t][d_v] = W_UV[h] c_t, float64. */
 int oracle_rebuild_kv(const oracle_mla_problem* P, int32_t b, int32_t t_begin, int32_t t_end,
                       double* k, double* v);
 
+/* Absorbed-form attention for a given absorbed query q_abs
+ * [B][H][d_latent + d_rope] (q_dtype; E4M3 with one factor per (b, h) in
+ * q_scale): s_t = scale * q_abs . row_t over the whole cached row, softmax,
+ * u = sum_t p_t c_KV,t / sum_t p_t, lse = log sum_t e^{s_t}, and optionally
+ * o = W_UV[h] u.  P gives the cache, d_latent, d_rope, d_v, the scale (d_nope
+ * only for the default 1/sqrt(d_nope + d_rope)) and W_UV; its query fields are
+ * not read.  Selection and token ranges as in oracle_mla_decode. */
+int oracle_absorbed_decode(const oracle_mla_problem* P, const void* q_abs, int32_t q_dtype,
+                           const float* q_scale, const int32_t* sel_b, const int32_t* sel_h,
+                           int32_t n_sel, const int32_t* t_begin, const int32_t* t_end,
+                           double* u, double* lse, double* o);
+
+/* E4M3 rows with one fp32 factor each, the rule of oracle_cache_append's E4M3
+ * cache: x [n][w] binary32 -> codes [n][w], scale [n]. */
+int oracle_quantize_e4m3_rows(int64_t n, int32_t w, const float* x, uint8_t* codes,
+                              float* scale);
+
+/* q_abs[b][h][:d_latent] = sum_n q_nope[b][h][n] * W_UK[h][n][:] ;
+ * q_abs[b][h][d_latent:] = q_rope[b][h][:]  (float64 out) */
 int oracle_absorb_q(int32_t B, int32_t H, int32_t d_nope, int32_t d_rope,
                     int32_t d_latent, const void* q_nope, const void* q_rope,
                     int32_t q_dtype, const void* w_uk, int32_t w_dtype,

@@ -12,6 +12,7 @@ import pytest
 import oracle
 from oracle.build import CFLAGS
 
+from . import test_oracle_absorbed as absorbed
 from . import test_oracle_append as append
 from . import test_oracle_codecs as codecs
 from . import test_oracle_mha as mha
@@ -87,6 +88,19 @@ MUTANTS = {
     "gqa_values_of_head_zero": ("const int64_t kv = b * H_kv + kvh;", "const int64_t kv = b * H_kv;"),
     "rope_angle_in_double": ("const float theta = pos * inv_freq[i]; /* binary32 product */",
                              "const double theta = (double)pos * (double)inv_freq[i];"),
+    # absorbed-form attention and the E4M3 query
+    "absorbed_drops_rope": ("for (int32_t j = 0; j < w; ++j) dot += q[j] * c[j];",
+                            "for (int32_t j = 0; j < dl; ++j) dot += q[j] * c[j];"),
+    "absorbed_query_factor_ignored": ("const double qf = q_dtype == ORACLE_E4M3 ? (double)q_scale[qrow] : 1.0;",
+                                      "const double qf = 1.0;"),
+    "absorbed_query_factor_transposed": ("const double qf = q_dtype == ORACLE_E4M3 ? (double)q_scale[qrow] : 1.0;",
+                                         "const double qf = q_dtype == ORACLE_E4M3 ? (double)q_scale[(int64_t)h * P->B + b] : 1.0;"),
+    "absorbed_missing_normalisation": ("    for (int32_t j = 0; j < dl; ++j) out_u[j] /= l;\n    lse[idx] = log(l) + m;\n    if (o)",
+                                       "    lse[idx] = log(l) + m;\n    if (o)"),
+    "absorbed_transposed_w_uv": ("acc += load_elem(P->w_uv, P->w_dtype, ((int64_t)h * P->d_v + v) * dl + j) * out_u[j];",
+                                 "acc += load_elem(P->w_uv, P->w_dtype, ((int64_t)h * dl + j) * P->d_v + v) * out_u[j];"),
+    "quantiser_amax_skips_last": ("for (int32_t j = 0; j < w; ++j) amax = fmaxf(amax, fabsf(x[j]));",
+                                  "for (int32_t j = 0; j < w - 1; ++j) amax = fmaxf(amax, fabsf(x[j]));"),
 }
 
 PIN_CHECKS = [
@@ -127,6 +141,12 @@ PIN_CHECKS = [
     mha.test_mqa_is_mla_with_identity_up_projections,
     prefill.test_rebuilt_keys_and_values_reproduce_the_decode,
     prefill.test_sub_range_is_a_slice_and_paged_equals_contiguous,
+    lambda: absorbed.test_absorbed_form_reproduces_the_naive_decode("dsv2_b32_l2k", {}),
+    absorbed.test_sub_ranges_and_ring_follow_the_naive_decode,
+    absorbed.test_closed_forms,
+    absorbed.test_e4m3_query_is_codes_times_its_factor,
+    absorbed.test_quantiser_equals_an_independent_one_and_the_cache_rows,
+    absorbed.test_absorb_q_fp8_is_the_quantised_absorbed_query,
 ]
 
 
@@ -154,7 +174,8 @@ def test_pins_catch_planted_mistake(tmp_path, name, monkeypatch):
                "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_array",
                "oracle_mla_cache_bytes_per_token", "oracle_mha_cache_bytes",
                "oracle_num_threads", "oracle_cache_append", "oracle_encode_e4m3",
-               "oracle_rope", "oracle_rope_inv_freq", "oracle_mha_decode", "oracle_ring_grow", "oracle_gqa_decode", "oracle_rebuild_kv"):
+               "oracle_rope", "oracle_rope_inv_freq", "oracle_mha_decode", "oracle_ring_grow", "oracle_gqa_decode", "oracle_rebuild_kv",
+               "oracle_absorbed_decode", "oracle_quantize_e4m3_rows"):
         getattr(mut, fn).restype = getattr(good, fn).restype
         getattr(mut, fn).argtypes = getattr(good, fn).argtypes
     monkeypatch.setattr(oracle, "_lib", mut)
