@@ -34,7 +34,10 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_traffic.json")
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}  # dense matrix-core peaks at 2.4 GHz
 CLOCK_HZ = 2.4e9  # rated engine clock (the matrix-core peaks are quoted at it)
 N_SIMD = 256 * 4
-KERNEL_SOURCE = os.path.join(ROOT, "mla_latent_kv_15_amd", "csrc", "mla_kernels.hip")
+# the sources of the decode kernels (a traffic record is valid for these bytes only)
+KERNEL_SOURCES = [os.path.join(ROOT, "mla_latent_kv_15_amd", "csrc", f)
+                  for f in ("mla_kernels.hip", "mla_decode_fp8.hip", "mla_decode_tile.h",
+                            "mla_device.h")]
 
 
 def parse():
@@ -47,6 +50,10 @@ def parse():
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--decode-kernel", default="auto", choices=["auto", "h64", "h128", "h128ws"],
                     help="decode work decomposition (mla_decode_ex); auto = mla_decode's choice")
+    ap.add_argument("--query-dtype", default="auto", choices=["auto", "bf16", "fp8"],
+                    help="absorbed-query format: fp8 (E4M3 + one factor per sequence and head; "
+                         "the decode then runs on the fp8 matrix cores) needs an fp8 cache; "
+                         "auto = fp8 for an fp8 cache, else the activation dtype")
     ap.add_argument("--replica-bytes", type=float, default=1.25 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-call-tail", action="store_true",
@@ -76,15 +83,28 @@ def parse():
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE,):
+    for f in KERNEL_SOURCES:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_key(workload, splits, partials, decode_kernel):
-    """the launch configuration a traffic record belongs to"""
-    return {"workload": workload, "splits": splits, "partials": partials,
-            "decode_kernel": decode_kernel}
+def query_dtype(args, wl) -> str:
+    """the absorbed query's format for this run"""
+    if args.query_dtype == "auto":
+        return "fp8" if wl.cache_dtype == "fp8" else ("f32" if wl.cache_dtype == "f32" else "bf16")
+    if args.query_dtype == "fp8" and wl.cache_dtype != "fp8":
+        raise SystemExit("an fp8 query needs an fp8 cache")
+    return args.query_dtype
+
+
+def traffic_key(workload, splits, partials, decode_kernel, query="bf16"):
+    """the launch configuration a traffic record belongs to (an fp8 query,
+    which runs another kernel, is part of it)"""
+    key = {"workload": workload, "splits": splits, "partials": partials,
+           "decode_kernel": decode_kernel}
+    if query == "fp8":
+        key["query"] = "fp8"
+    return key
 
 
 def _records():
@@ -127,8 +147,9 @@ def record_traffic(d, args):
     configuration given by the other options (the defaults unless stated);
     the record replaces any earlier one for the same configuration."""
     import synth
-    key = traffic_key(args.workload, args.splits or synth.workload(args.workload).num_splits,
-                      args.part_dtype, args.decode_kernel)
+    wl = synth.workload(args.workload)
+    key = traffic_key(args.workload, args.splits or wl.num_splits, args.part_dtype,
+                      args.decode_kernel, query_dtype(args, wl))
     f = _counter_means(os.path.join(d, "fetch", "run_counter_collection.csv"), "FETCH_SIZE")
     w = _counter_means(os.path.join(d, "write", "run_counter_collection.csv"), "WRITE_SIZE")
     cf = _counter_means(os.path.join(d, "cfetch", "run_counter_collection.csv"), "FETCH_SIZE")
@@ -480,7 +501,11 @@ def main():
     QL = args.q_len
     if QL > 1:
         return multi_token_bench(args, wl, dev, reps, R, S, act, part, out, cache_bytes)
-    step = mla.DecodeStep(dev.geo, wl.batch, S, act_dtype=act, part_dtype=part, out_dtype=out)
+    fp8q = query_dtype(args, wl) == "fp8"
+    if fp8q and args.decode_kernel != "auto":
+        raise SystemExit("an fp8 query runs its own decode kernel: use --decode-kernel auto")
+    step = mla.DecodeStep(dev.geo, wl.batch, S, act_dtype=act, part_dtype=part, out_dtype=out,
+                          fp8_query=fp8q)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -492,13 +517,16 @@ def main():
               "h128ws": mla.KERNEL_H128_WS}[args.decode_kernel]
 
     def decode(rp, prepare=False):
+        if fp8q:
+            return mla.mla_decode(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
+                                  q_abs_scale=step.q_abs_scale, stream=stream, prepare=prepare)
         return mla.mla_decode_ex(step.geo, step.q_abs, rp["cache"], S, step.u_part, step.lse_part,
                                  kernel=kernel, stream=stream, prepare=prepare)
 
     # the step's launches in order: (name, fn(replica, prepare))
     stages = [("mla_absorb_q", lambda rp, prepare=False: mla.mla_absorb_q(
-                  step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs, stream=stream,
-                  prepare=prepare)),
+                  step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], step.q_abs, step.q_abs_scale,
+                  stream=stream, prepare=prepare)),
               ("mla_decode", decode)]
     if fused:
         stages.append(("mla_combine_up_proj", lambda rp, prepare=False: mla.mla_combine_up_proj(
@@ -576,15 +604,17 @@ def main():
     outside_us = {"mla_cache_append": e0.elapsed_time(e1) / args.steps * 1e3}
     # and the absorb with the decoupled RoPE of q_R (the step's absorb variant
     # for callers whose q_R is not rotated yet)
+    q_rope_out = (torch.empty(wl.batch, wl.heads, 576, dtype=act, device="cuda") if fp8q
+                  else step.q_abs)  # the RoPE variant writes a bf16 / fp32 query
     outside_us["mla_absorb_q_rope"] = loop_ms(lambda rp: mla.mla_absorb_q_rope(
-        step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], last, step.q_abs,
+        step.geo, rp["q_nope"], rp["q_rope"], rp["w_uk"], last, q_rope_out,
         stream=stream)) * 1e3
 
     # roofline of the decode: algorithmic bytes of one launch (the cache rows
     # it attends) over its mean launch duration
     launch_bytes = cache_bytes
     achieved = launch_bytes / t_decode / 1e9
-    key = traffic_key(wl.name, S, args.part_dtype, args.decode_kernel)
+    key = traffic_key(wl.name, S, args.part_dtype, args.decode_kernel, "fp8" if fp8q else "bf16")
     counters = stored_counters(key)
     traffic = None if counters is None else counters.get("hbm_bytes_per_launch")
     # matrix-core work of the decode: 2 h (576 + 512) FLOP per attended token
@@ -625,6 +655,7 @@ def main():
                    "tokens_attended": int(n_tok), "splits": S,
                    "cache": f"{wl.cache_dtype} {'paged' if wl.page_size else 'contiguous'}",
                    "partials": args.part_dtype, "decode_kernel": args.decode_kernel,
+                   "query": "fp8" if fp8q else str(act).replace("torch.", ""),
                    "replicas": R, "parallelism": "none (1 GPU)"},
         # cache bytes over the time of the launches that handle the cache
         # stream: the decode and the merge of its partials (the fused tail

@@ -134,9 +134,16 @@ typedef struct {
  * q_nope [B][h][d_nope], q_rope [B][h][d_rope] (dtype q_dt, F32 or BF16);
  * w_uk [h][d_nope][d_latent] (w_dt, F32 or BF16); fp32 accumulation.
  * q_abs [B][h][d_latent+d_rope] in q_abs_dt: F32 or BF16 (round to nearest
- * even).  q_abs_scale is reserved for an FP8 query and must be NULL: q_abs_dt
- * FP8_E4M3 returns MLA_E_UNSUPPORTED (an fp8 cache is read with a bf16
- * query). */
+ * even), or FP8_E4M3 for the fp8-cache decode (the FP8 KV cache of the
+ * "engineering DeepSeek sparse attention long context inference" page, with
+ * the query in the same format): then q_abs_scale is device fp32 [B][h] and
+ * each row, the 576 values of one (b, i) computed in fp32, is stored by the
+ * fp8 cache rows' rule: q_abs_scale[b][i] = max(amax, 2^-126) / 448 with amax
+ * the row's largest magnitude, code = the E4M3 value nearest to the binary32
+ * quotient value / q_abs_scale[b][i] (ties to even, clamped to +-448).  The
+ * FP8 output needs BF16 inputs, d_nope a multiple of 16 and at most 128, and
+ * 16-byte aligned q_nope, q_rope and w_uk (else MLA_E_UNSUPPORTED).
+ * q_abs_scale must be NULL for the other output dtypes (MLA_E_ARG). */
 mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const void* q_nope,
                           const void* q_rope, int32_t q_dt, const void* w_uk,
                           int32_t w_dt, void* q_abs, int32_t q_abs_dt,
@@ -169,14 +176,21 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t B, const void* q_
  *   s_t  = scale * (q_abs[b][i][0:d_latent]·c_t + q_abs[b][i][d_latent:]·k_R,t)
  *   u_part[b][p][i][:] = sum_{t in R} e^{s_t} c_t / sum_{t in R} e^{s_t}
  *   lse_part[b][p][i]  = ln sum_{t in R} e^{s_t}      (natural log)
- * q_abs [B][h][d_latent+d_rope] (q_abs_dt); q_abs_scale is reserved and must
- * be NULL.  u_part [B][num_splits][h][d_latent] in part_dt (F32 or BF16);
- * lse_part [B][num_splits][h] fp32.  1 <= num_splits <= 1024.
- * Provided dtype pairs (cache / q_abs): F32/F32, BF16/BF16 and FP8/BF16;
- * other pairs return MLA_E_DTYPE.  An FP8 cache is read as code * row_scale
- * with every code widened exactly to bf16; the row scale multiplies the
- * score, and the bf16-rounded probability in the PV product.  The BF16 and
- * FP8 paths need h to be a multiple of 32. */
+ * q_abs [B][h][d_latent+d_rope] (q_abs_dt); q_abs_scale: device fp32 [B][h]
+ * for an FP8 query (value = code * q_abs_scale[b][i]), else NULL.  u_part
+ * [B][num_splits][h][d_latent] in part_dt (F32 or BF16); lse_part
+ * [B][num_splits][h] fp32.  1 <= num_splits <= 1024.
+ * Provided dtype pairs (cache / q_abs): F32/F32, BF16/BF16, FP8/BF16 and
+ * FP8/FP8; other pairs return MLA_E_DTYPE.  An FP8 cache is read as
+ * code * row_scale.  With a BF16 query every code is widened exactly to bf16,
+ * the row scale multiplies the score and the bf16-rounded probability in the
+ * PV product.  With an FP8 query both products run on the fp8 matrix cores
+ * over the raw codes, in ranges of whole 64-token tiles
+ * (C = 64 * ceil(max_seq_len / (64*num_splits))): the scores are the exact
+ * code products times both factors, and the PV product takes p * row_scale
+ * rounded to E4M3 with one power-of-two factor per (head, 32 tokens) that
+ * puts the largest of them in [128, 256); l sums the unrounded p.  The BF16
+ * and FP8 paths need h to be a multiple of 32. */
 mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
                         int32_t q_abs_dt, const float* q_abs_scale,
                         const mla_cache_t* cache, int32_t num_splits, void* u_part,
@@ -215,6 +229,7 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
  *                      softmax of 32 heads each, 8 the value product of 64
  *                      heads x 128 latent columns each, three waves per SIMD.
  *                      BF16 cache, h a multiple of 128.
+ *   (an FP8 query always runs its own 64-head kernel: AUTO or H64.)
  *   MLA_KERNEL_AUTO -- what mla_decode and mla_decode_multi use: H64, which
  *                      measured as fast or faster than H128 on every bf16
  *                      workload and split count tried (H128 runs one wave per

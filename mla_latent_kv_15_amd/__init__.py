@@ -629,18 +629,25 @@ class DecodeStep:
 
     q_nope [B, h, d_nope], q_rope [B, h, d_rope], w_uk [h, d_nope, 512],
     w_uv [h, d_v, 512] (float32 or bfloat16); the cache as `Cache`.
-    act_dtype is the dtype of q_abs / u; part_dtype of the split partials."""
+    act_dtype is the dtype of q_abs / u; part_dtype of the split partials.
+    fp8_query: q_abs in E4M3 with one factor per (sequence, head) (an fp8
+    cache only; the decode then runs on the fp8 matrix cores)."""
 
     def __init__(self, geo: Geometry, batch: int, num_splits: int, device="cuda",
                  act_dtype=torch.bfloat16, part_dtype=torch.bfloat16, out_dtype=torch.bfloat16,
-                 kernel: int = KERNEL_AUTO):
+                 kernel: int = KERNEL_AUTO, fp8_query: bool = False):
         self.geo = geo
         self.kernel = int(kernel)
         self.B = batch
         self.S = int(num_splits)
         h = geo.heads
         w = geo.d_latent + geo.d_rope
-        self.q_abs = torch.empty(batch, h, w, dtype=act_dtype, device=device)
+        if fp8_query and self.kernel != KERNEL_AUTO:
+            raise ValueError("an fp8 query runs its own kernel (KERNEL_AUTO)")
+        self.q_abs = torch.empty(batch, h, w, dtype=torch.uint8 if fp8_query else act_dtype,
+                                 device=device)
+        self.q_abs_scale = (torch.empty(batch, h, dtype=torch.float32, device=device)
+                            if fp8_query else None)
         self.u_part = torch.empty(batch, self.S, h, geo.d_latent, dtype=part_dtype, device=device)
         self.lse_part = torch.empty(batch, self.S, h, dtype=torch.float32, device=device)
         self.u = (self.u_part.view(batch, h, geo.d_latent) if self.S == 1
@@ -657,9 +664,10 @@ class DecodeStep:
 
     def run(self, q_nope, q_rope, w_uk, w_uv, cache: Cache, stream=None,
             fused: bool = True) -> torch.Tensor:
-        mla_absorb_q(self.geo, q_nope, q_rope, w_uk, self.q_abs, stream=stream)
+        mla_absorb_q(self.geo, q_nope, q_rope, w_uk, self.q_abs, self.q_abs_scale, stream=stream)
         if self.kernel == KERNEL_AUTO:
-            mla_decode(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part, stream=stream)
+            mla_decode(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part,
+                       q_abs_scale=self.q_abs_scale, stream=stream)
         else:
             mla_decode_ex(self.geo, self.q_abs, cache, self.S, self.u_part, self.lse_part,
                           kernel=self.kernel, stream=stream)

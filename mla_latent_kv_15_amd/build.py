@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["mla_host.cpp", "mla_kernels.hip", "mla_prefill.hip"]
+SOURCES = ["mla_host.cpp", "mla_kernels.hip", "mla_decode_fp8.hip", "mla_prefill.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 HIPFLAGS = [

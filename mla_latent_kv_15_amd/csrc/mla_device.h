@@ -50,6 +50,24 @@ __device__ inline u32x2_t e4m3x4_to_bf16x4(uint32_t w) {
   return u32x2_t{x, y};
 }
 
+// Nearest E4M3 code to y (|y| <= 448 after clamping), ties to the even
+// mantissa, from the format's spacing: 2^-9 below 2^-6, and 2^(k-3) in the
+// binade [2^k, 2^(k+1)).  Scaling |y| by that spacing is exact, so
+// v_rndne_f32 makes the decision; a count of 16 is the next binade's first
+// value.  The sign is kept (-0 gives 0x80).
+__device__ inline uint32_t e4m3_encode(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.0f);
+  if (a < 0x1p-6f) return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  int k = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+  int q = static_cast<int>(__builtin_rintf(__builtin_ldexpf(a, 3 - k)));
+  if (q == 16) {
+    q = 8;
+    ++k;
+  }
+  return sign | static_cast<uint32_t>(((k + 7) << 3) | (q - 8));
+}
+
 template <int DT>
 __device__ inline float load_elem(const void* p, int64_t i) {
   if constexpr (DT == MLA_F32) return static_cast<const float*>(p)[i];

@@ -79,7 +79,7 @@ mla_status_t check_decode(const mla_dims_t* dims, int32_t B, const void* q_abs,
   const int32_t cd = cache->dtype;
   const bool pair_ok = (cd == MLA_F32 && q_abs_dt == MLA_F32) ||
                        (cd == MLA_BF16 && q_abs_dt == MLA_BF16) ||
-                       (cd == MLA_FP8_E4M3 && q_abs_dt == MLA_BF16);
+                       (cd == MLA_FP8_E4M3 && (q_abs_dt == MLA_BF16 || q_abs_dt == MLA_FP8_E4M3));
   if (!pair_ok) return MLA_E_DTYPE;
   if (q_abs_dt == MLA_FP8_E4M3) {
     if (!q_abs_scale) return MLA_E_ARG;

@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "../../include/mla.h"
+#include "mla_decode_tile.h"
 #include "mla_device.h"
 #include "mla_host.h"
 
@@ -37,117 +38,6 @@ namespace {
 //     latent read from the same LDS tile with transposing reads.
 // Tokens past the end of the range are loaded from the tile's first row
 // (finite data; their probability is zero).
-
-constexpr int kRowBytes = kRowElems * 2;             // 1152: bf16 row in LDS
-constexpr int kTileBytes = kTileTokens * kRowBytes;  // 36864
-constexpr int kDmaPerWave = kTileBytes / 1024 / 4;   // 9 wave-loads of 1 KB per wave of 4
-constexpr int kNBuf = 4;                             // LDS tile buffers
-// Softmax reference.  The probabilities are taken relative to a reference
-// maximum m_ref (log2 domain) fixed at the first tile of the range instead of
-// the running maximum, so the accumulators are never rescaled.  A later score
-// may exceed m_ref by up to kRefSlack: probabilities then stay below
-// 2^kRefSlack, far from the bf16/fp32 range limits.  If any score exceeds it
-// (no realistic logit spread does), the range is computed again with m_ref set
-// to the true maximum found by the first pass.  Either way numerator and
-// denominator share one reference, so the result is exact.
-constexpr float kRefSlack = 64.0f;  // log2 units
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-struct DecodeParams {
-  const void* q_abs;        // [B][H][576] bf16
-  const uint8_t* rows;      // cache rows
-  const float* row_scale;   // fp8 only
-  const int32_t* block_table;
-  const int32_t* seq_lens;
-  int64_t seq_stride;
-  int32_t max_pages;
-  int32_t paged;
-  int32_t B, H, S, HG, chunk;
-  int32_t max_seq_len;
-  int32_t QL;  // query tokens per sequence (1: plain decode)
-  float scale_log2;
-  void* u_part;
-  float* lse_part;
-  int32_t ring;  // contiguous rows used as a ring of seq_stride slots
-};
-
-// Tokens of sequence b that the decode attends: its length, clamped to the
-// host bound; a ring of C slots holds (and attends) only the last C, which
-// sit in its first min(L, C) rows -- attention does not depend on their order.
-__device__ inline int attended_len(const int32_t* seq_lens, int b, int max_seq_len,
-                                   int ring, int64_t seq_stride) {
-  int L = min(max(seq_lens[b], 0), max_seq_len);
-  if (ring) L = static_cast<int>(min(static_cast<int64_t>(L), seq_stride));
-  return L;
-}
-
-__device__ inline uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
-}
-
-// ================================================================ decode: tile layout
-//
-// The work unit is (sequence b, split range p, group of up to 64 heads);
-// tiles of 32 tokens sit in LDS as bf16 in the token-group layout below.
-
-constexpr int kH64 = 64;                 // heads per workgroup
-constexpr int kH64Blocks = 2;            // head blocks of 32
-constexpr int kQkSteps = kRowElems / 32;  // 18 k-steps of 32
-constexpr int kP64Bytes = 4096;           // bf16 probabilities, 64 heads x 32 tokens
-constexpr int kX64Off = kNBuf * kTileBytes + 2 * kP64Bytes;  // exchange area (float[2][64] + votes)
-
-// Token-group tile layout: tokens in groups of 8 and 16-byte chunks in groups
-// of 8, token t / chunk c at
-//   (t / 8) * 9216 + (c / 8) * 1024 + (t % 8) * 128 + ((c % 8) ^ swzg(t)) * 16,
-//   swzg(t) = (5 (t % 8) mod 8) xor (2 (t & 2)).
-// One 1 KB LDS-DMA wave instruction moves 8 tokens x 8 chunks, i.e. 8 whole
-// 128-byte lines of the cache, and a lane's source offset is the same for all
-// 9 instructions of a wave (only the scalar base and M0 advance).  The XOR key
-// was chosen by measurement (SQ_LDS_BANK_CONFLICT on gfx950, one read pattern
-// per kernel): with it neither operand read has bank conflicts -- the 16x16x32
-// QK read (16 lanes = one chunk of 8 rows in each of two groups) nor the
-// transposing PV read (per half-wave 4 rows x 4 chunks: rows t and t + 2 need
-// keys that differ in bit 2, which 5t mod 8 alone does not give; it cost two
-// extra LDS cycles per ds_read_b64_tr_b16).
-constexpr int kTokGroupBytes = 8 * kRowBytes;  // 9216
-
-__device__ inline int swzg(int t) { return ((5 * t) & 7) ^ ((t & 2) << 1); }
-
-// DMA of 32 rows of 1152 bytes starting at `base` (rows consecutive in
-// memory) into an LDS tile in the token-group layout; wave w moves rows
-// 8w..8w+7, rows >= nvalid are replaced by row 0.
-// The 9 wave instructions can be issued one at a time (rows_dma_issue), spread
-// between other work: the vector memory unit of a CU accepts about 64 bytes
-// per clock, so the 36 instructions of a tile occupy it for ~600 clocks.
-struct RowsDma {
-  const uint8_t* base;  // wave-uniform
-  uint32_t off;         // per lane
-  uint32_t m0;          // wave-uniform
-};
-
-__device__ inline RowsDma rows_dma_plan(const uint8_t* base, uint32_t lds_tile, int nvalid, int wave) {
-  int ln;  // volatile: recomputed per call rather than kept live across the loop
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  const int k = ln >> 3, j = ln & 7;
-  const int t = 8 * wave + k;
-  RowsDma d;
-  d.base = base;
-  d.off = static_cast<uint32_t>(((t < nvalid) ? t : 0) * kRowBytes + ((j ^ swzg(t)) << 4));
-  d.m0 = lds_tile + wave * kTokGroupBytes;
-  return d;
-}
-
-__device__ inline void rows_dma_issue(const RowsDma& d, int i) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(d.off), "s"(d.base + 128 * i),
-               "{m0}"(d.m0 + 1024 * i) : "memory");
-}
-
-__device__ inline void rows_dma_g8(const uint8_t* base, uint32_t lds_tile, int nvalid, int wave) {
-  const RowsDma d = rows_dma_plan(base, lds_tile, nvalid, wave);
-#pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
-}
 
 // ================================================================ decode (warp-specialised)
 //
@@ -2140,6 +2030,171 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
   }
 }
 
+// ================================================================ absorb with an E4M3 output
+//
+// The fp8 decode takes the absorbed query in E4M3 with one fp32 factor per
+// (sequence, head), by the rule of the fp8 cache rows: the factor maps the
+// row's largest magnitude over all 576 elements onto 448, each code is the
+// correctly rounded quotient x / factor rounded to the nearest E4M3 value
+// (ties to even).  The factor needs the whole row in one workgroup: one
+// workgroup per (head, 32 sequences), 8 waves.  W_UK[h] (d_nope x 512 bf16,
+// d_nope <= 128) is staged whole in LDS; wave w computes latent columns
+// 64w..64w+63 of the 32 sequences on v_mfma_f32_32x32x16_bf16 (A = W_UK^T by
+// transposing reads, B = the query rows, as in absorb_mfma_kernel); the first
+// 256 threads carry the RoPE part (rotated when positions are given); the row
+// maxima meet in LDS; the codes are staged in LDS over the W_UK slab, which
+// is no longer read, and leave as whole 576-byte rows.
+constexpr int kAf8Threads = 512;
+constexpr int kAf8Row = kDLatent * 2 + 16;               // padded LDS row of W_UK[h]
+constexpr int kAf8QStride = 2 * 128 + 16;                // padded query row (d_nope <= 128)
+constexpr int kAf8QOff = 128 * kAf8Row;
+constexpr int kAf8RedOff = kAf8QOff + 32 * kAf8QStride;  // float [32][16]: row maxima
+constexpr int kAf8ScOff = kAf8RedOff + 32 * 16 * 4;      // float [32]: factors
+constexpr int kAf8Lds = kAf8ScOff + 32 * 4;
+constexpr int kAf8Out = kRowElems + 16;                  // staged code row
+static_assert(32 * kAf8Out <= kAf8QOff, "absorb fp8 output stage");
+static_assert(kAf8Lds <= 160 * 1024, "absorb fp8 LDS");
+
+__global__ __launch_bounds__(kAf8Threads) void absorb_f8_kernel(const uint16_t* q_nope,
+                                                               const uint16_t* q_rope,
+                                                               const uint16_t* w_uk, uint8_t* q_abs,
+                                                               float* q_scale, int B, int H,
+                                                               int d_nope, RopeArgs R) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kAf8Lds];
+  float* red = reinterpret_cast<float*>(sm + kAf8RedOff);
+  float* fac = reinterpret_cast<float*>(sm + kAf8ScOff);
+  const int h = blockIdx.x, b0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, bl = lane & 31;
+  // every load before the first wait: W_UK[h] (d_nope rows of 64 chunks of
+  // 16 B, 16 per thread), the 32 query rows (one chunk per thread), the RoPE
+  // rows (threads < 256: 8 elements of sequence b0 + tid / 8)
+  const uint16_t* wsrc = w_uk + static_cast<int64_t>(h) * d_nope * kDLatent;
+  u32x4_t st[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int q = i * kAf8Threads + tid;
+    if (q < d_nope * 64) st[i] = *reinterpret_cast<const u32x4_t*>(wsrc + (q >> 6) * kDLatent + (q & 63) * 8);
+  }
+  const int qcpr = d_nope / 8;
+  const int qrow = tid / qcpr, qcol = tid % qcpr;
+  const bool q_thread = tid < 32 * qcpr;
+  u32x4_t qv = u32x4_t{0u, 0u, 0u, 0u};
+  if (q_thread) {
+    const int b = b0 + qrow;
+    qv = *reinterpret_cast<const u32x4_t*>(q_nope + (static_cast<int64_t>(b < B ? b : 0) * H + h) * d_nope + 8 * qcol);
+  }
+  const bool rope_thread = tid < 256;
+  const int rb = b0 + (tid >> 3), rj = 8 * (tid & 7);
+  float y[8];
+  if (rope_thread) {
+    const uint16_t* rrow = q_rope + (static_cast<int64_t>(rb < B ? rb : 0) * H + h) * kDRope;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rrow + rj);
+    if (R.positions) {  // pair with the chunk 32 elements away
+      const u32x4_t vp = *reinterpret_cast<const u32x4_t*>(rrow + (rj ^ 32));
+      const int pos = R.positions[rb < B ? rb : 0];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t wv = v[k >> 1], wp = vp[k >> 1];
+        const float xj = __uint_as_float((k & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+        const float xq = __uint_as_float((k & 1) ? (wp & 0xFFFF0000u) : (wp << 16));
+        y[k] = rope_elem(R, pos, rj + k, xj, xq);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t wv = v[k >> 1];
+        y[k] = __uint_as_float((k & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int q = i * kAf8Threads + tid;
+    if (q < d_nope * 64) *reinterpret_cast<u32x4_t*>(sm + (q >> 6) * kAf8Row + (q & 63) * 16) = st[i];
+  }
+  uint8_t* qs = sm + kAf8QOff;
+  if (q_thread) *reinterpret_cast<u32x4_t*>(qs + qrow * kAf8QStride + 16 * qcol) = qv;
+  __syncthreads();
+
+  // columns 32 cb .. 32 cb + 31, cb = 2 wave + c2; accumulator: column
+  // 32 cb + 8 (r / 4) + 4 g + r % 4 of sequence b0 + bl
+  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
+  f32x16_t acc[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c2][r] = 0.0f;
+  for (int k = 0; k < d_nope / 16; ++k) {
+    const bf16x8_t bq = *reinterpret_cast<const bf16x8_t*>(qs + bl * kAf8QStride + 32 * k + 16 * g);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const uint8_t* ab = sm + (16 * k + 8 * (G >> 1) + e) * kAf8Row +
+                          (32 * (2 * wave + c2) + 16 * (G & 1) + 4 * q4) * 2;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ab);
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ab + 4 * kAf8Row));
+      const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[c2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[c2], 0, 0, 0);
+    }
+  }
+  // row maxima: 8 waves x 2 column halves, and 8 RoPE chunks, per sequence
+  float m = 0.0f;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[c2][r]));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (g == 0) red[bl * 16 + wave] = m;
+  if (rope_thread) {
+    float mr = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mr = fmaxf(mr, fabsf(y[k]));
+    red[(tid >> 3) * 16 + 8 + (tid & 7)] = mr;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, red[tid * 16 + i]);
+    const float f = fmaxf(amax, 0x1p-126f) / 448.0f;
+    fac[tid] = f;
+    if (b0 + tid < B) q_scale[static_cast<int64_t>(b0 + tid) * H + h] = f;
+  }
+  __syncthreads();
+  // codes, staged over the W_UK slab (every wave is past its last read)
+  {
+    const float f = fac[bl];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x = fminf(fmaxf(acc[c2][4 * r4 + q] / f, -448.0f), 448.0f);
+          w |= e4m3_encode(x) << (8 * q);
+        }
+        *reinterpret_cast<uint32_t*>(sm + bl * kAf8Out + 32 * (2 * wave + c2) + 8 * r4 + 4 * g) = w;
+      }
+  }
+  if (rope_thread) {
+    const float f = fac[tid >> 3];
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k >> 2] |= e4m3_encode(fminf(fmaxf(y[k] / f, -448.0f), 448.0f)) << (8 * (k & 3));
+    *reinterpret_cast<u32x2_t*>(sm + (tid >> 3) * kAf8Out + kDLatent + rj) = u32x2_t{w[0], w[1]};
+  }
+  __syncthreads();
+  // 32 rows x 36 chunks of 16 B
+  for (int i = tid; i < 32 * (kRowElems / 16); i += kAf8Threads) {
+    const int row = i / (kRowElems / 16), ch = i % (kRowElems / 16);
+    if (b0 + row < B)
+      *reinterpret_cast<u32x4_t*>(q_abs + (static_cast<int64_t>(b0 + row) * H + h) * kRowElems + 16 * ch) =
+          *reinterpret_cast<const u32x4_t*>(sm + row * kAf8Out + 16 * ch);
+  }
+}
+
 // ================================================================ up-projection (MFMA)
 //
 // bf16 u and W_UV: per head h, oᵀ[v][b] = Σ_c W_UV[h][v][c] u[b][h][c] on
@@ -2608,24 +2663,6 @@ __global__ __launch_bounds__(kMhaThreads) void mha_decode_kernel(
 
 constexpr int kAppendThreads = 256;  // 4 sequences per workgroup
 
-// Nearest E4M3 code to y (|y| <= 448 after clamping), ties to the even
-// mantissa, from the format's spacing: 2^-9 below 2^-6, and 2^(k-3) in the
-// binade [2^k, 2^(k+1)).  Scaling |y| by that spacing is exact, so
-// v_rndne_f32 makes the decision; a count of 16 is the next binade's first
-// value.  The sign is kept (-0 gives 0x80).
-__device__ inline uint32_t e4m3_encode(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.0f);
-  if (a < 0x1p-6f) return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  int k = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;
-  int q = static_cast<int>(__builtin_rintf(__builtin_ldexpf(a, 3 - k)));
-  if (q == 16) {
-    q = 8;
-    ++k;
-  }
-  return sign | static_cast<uint32_t>(((k + 7) << 3) | (q - 8));
-}
-
 template <int SRC_DT, int CACHE_DT>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const void* c_kv, const void* k_r, const int32_t* positions, void* rows, float* row_scale,
@@ -2714,9 +2751,20 @@ using namespace mla;
 
 static mla_status_t absorb_launch(const mla_dims_t* dims, int32_t B, const void* q_nope,
                                   const void* q_rope, int32_t q_dt, const void* w_uk, int32_t w_dt,
-                                  void* q_abs, int32_t q_abs_dt, const RopeArgs& R,
-                                  hipStream_t s) {
+                                  void* q_abs, int32_t q_abs_dt, float* q_abs_scale,
+                                  const RopeArgs& R, hipStream_t s) {
   const int H = dims->heads, dn = dims->d_nope;
+  if (q_abs_dt == MLA_FP8_E4M3) {  // bf16 inputs only, whole W_UK[h] in LDS
+    if (q_dt != MLA_BF16 || w_dt != MLA_BF16 || dn % 16 != 0 || dn > 128 || !q_abs_scale ||
+        reinterpret_cast<uintptr_t>(q_nope) % 16 != 0 || reinterpret_cast<uintptr_t>(w_uk) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(q_rope) % 16 != 0)
+      return MLA_E_UNSUPPORTED;
+    const dim3 grid(H, (B + 31) / 32);
+    absorb_f8_kernel<<<grid, kAf8Threads, 0, s>>>(
+        static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
+        static_cast<const uint16_t*>(w_uk), static_cast<uint8_t*>(q_abs), q_abs_scale, B, H, dn, R);
+    return launch_status();
+  }
   if (q_dt == MLA_BF16 && w_dt == MLA_BF16 && dn % 16 == 0 &&
       (q_abs_dt == MLA_BF16 || q_abs_dt == MLA_F32) &&
       reinterpret_cast<uintptr_t>(q_nope) % 16 == 0 && reinterpret_cast<uintptr_t>(w_uk) % 16 == 0 &&
@@ -2754,10 +2802,9 @@ extern "C" mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t B, const vo
   mla_status_t st = check_absorb(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt,
                                  q_abs_scale);
   if (st != MLA_OK || B == 0) return st;
-  if (q_abs_dt == MLA_FP8_E4M3) return MLA_E_UNSUPPORTED;
   RopeArgs R{};
   R.positions = nullptr;
-  return absorb_launch(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt, R,
+  return absorb_launch(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt, q_abs_scale, R,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -2777,14 +2824,14 @@ extern "C" mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t B, con
   for (int i = 0; i < kDRope / 2; ++i)
     R.inv_freq[i] = static_cast<float>(std::pow(static_cast<double>(rope_base),
                                                 -2.0 * static_cast<double>(i) / kDRope));
-  return absorb_launch(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt, R,
+  return absorb_launch(dims, B, q_nope, q_rope, q_dt, w_uk, w_dt, q_abs, q_abs_dt, nullptr, R,
                        static_cast<hipStream_t>(stream));
 }
 
 static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_len,
-                                  const void* q_abs, const mla_cache_t* cache, int32_t num_splits,
-                                  void* u_part, int32_t part_dt, float* lse_part, int32_t kernel,
-                                  hipStream_t s) {
+                                  const void* q_abs, int32_t q_abs_dt, const float* q_abs_scale,
+                                  const mla_cache_t* cache, int32_t num_splits, void* u_part,
+                                  int32_t part_dt, float* lse_part, int32_t kernel, hipStream_t s) {
   const int32_t H = dims->heads;
   // with max_seq_len == 0 every range is empty; a chunk of 32 keeps the
   // kernels' range arithmetic well defined
@@ -2814,6 +2861,18 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   }
   // workgroups of 64 heads of one query token
   const int32_t HG64 = (H + kH64 - 1) / kH64;
+  if (q_abs_dt == MLA_FP8_E4M3) {  // fp8 cache and query: 64-token tiles on the fp8 matrix cores
+    if (kernel != MLA_KERNEL_AUTO && kernel != MLA_KERNEL_H64) return MLA_E_UNSUPPORTED;
+    const int64_t nblk = static_cast<int64_t>(B) * q_len * num_splits * HG64;
+    if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
+    const int32_t per = 2 * kTileTokens * num_splits;
+    const int32_t chunk64 = max((span + per - 1) / per, 1) * (2 * kTileTokens);
+    DecodeParams Q{q_abs, static_cast<const uint8_t*>(cache->rows), cache->row_scale,
+                   cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
+                   cache->page_size != 0, B, H, num_splits, HG64, chunk64, cache->max_seq_len,
+                   q_len, scale * kLog2e, u_part, lse_part, cache->ring, q_abs_scale};
+    return decode_fp8q_launch(Q, part_dt, static_cast<unsigned>(nblk), s);
+  }
   const int64_t nblk64 = static_cast<int64_t>(B) * q_len * num_splits * HG64;
   if (nblk64 > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid64 = static_cast<unsigned>(nblk64);
@@ -2864,8 +2923,8 @@ extern "C" mla_status_t mla_decode(const mla_dims_t* dims, int32_t B, const void
   mla_status_t st = check_decode(dims, B, q_abs, q_abs_dt, q_abs_scale, cache, num_splits,
                                  u_part, part_dt, lse_part);
   if (st != MLA_OK || B == 0) return st;
-  return decode_launch(dims, B, 1, q_abs, cache, num_splits, u_part, part_dt, lse_part,
-                       MLA_KERNEL_AUTO, static_cast<hipStream_t>(stream));
+  return decode_launch(dims, B, 1, q_abs, q_abs_dt, q_abs_scale, cache, num_splits, u_part,
+                       part_dt, lse_part, MLA_KERNEL_AUTO, static_cast<hipStream_t>(stream));
 }
 
 extern "C" mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
@@ -2878,8 +2937,8 @@ extern "C" mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int3
                                  part_dt, lse_part);
   if (st != MLA_OK || B == 0) return st;
   if (static_cast<int64_t>(B) * q_len > 0x7FFFFFFF) return MLA_E_SHAPE;
-  return decode_launch(dims, B, q_len, q_abs, cache, num_splits, u_part, part_dt, lse_part,
-                       MLA_KERNEL_AUTO, static_cast<hipStream_t>(stream));
+  return decode_launch(dims, B, q_len, q_abs, q_abs_dt, nullptr, cache, num_splits, u_part,
+                       part_dt, lse_part, MLA_KERNEL_AUTO, static_cast<hipStream_t>(stream));
 }
 
 extern "C" mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t B, int32_t q_len,
@@ -2892,8 +2951,8 @@ extern "C" mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t B, int32_t
                                  part_dt, lse_part);
   if (st != MLA_OK || B == 0) return st;
   if (static_cast<int64_t>(B) * q_len > 0x7FFFFFFF) return MLA_E_SHAPE;
-  return decode_launch(dims, B, q_len, q_abs, cache, num_splits, u_part, part_dt, lse_part,
-                       kernel, static_cast<hipStream_t>(stream));
+  return decode_launch(dims, B, q_len, q_abs, q_abs_dt, nullptr, cache, num_splits, u_part,
+                       part_dt, lse_part, kernel, static_cast<hipStream_t>(stream));
 }
 
 extern "C" mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t num_splits,
@@ -3062,8 +3121,8 @@ extern "C" mla_status_t mla_decode_combine_up_proj_noalloc(
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the decode writes every (sequence, split, head) row it is asked for (an
   // empty range writes u = 0 and lse = -inf), so nothing needs clearing
-  st = decode_launch(dims, B, 1, q_abs, cache, num_splits, u_part, MLA_BF16, lse_part,
-                     MLA_KERNEL_AUTO, s);
+  st = decode_launch(dims, B, 1, q_abs, q_abs_dt, nullptr, cache, num_splits, u_part, MLA_BF16,
+                     lse_part, MLA_KERNEL_AUTO, s);
   if (st != MLA_OK) return st;
   return combine_up_launch(dims, B, num_splits, u_part, MLA_BF16, lse_part, w_uv, o, o_dt, u, lse,
                            s);

@@ -16,14 +16,15 @@ TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
 
 
 def run_step(dev: DeviceInputs, num_splits: int, part_dtype=None, out_dtype=None,
-             kernel: int = mla.KERNEL_AUTO):
+             kernel: int = mla.KERNEL_AUTO, fp8_query: bool = False):
     """absorb -> decode -> combine -> up_proj.  Returns the DecodeStep (its
     buffers hold q_abs, u_part, lse_part, u, lse, o)."""
     wl = dev.wl
     act = act_torch_dtype(wl)
     step = mla.DecodeStep(dev.geo, wl.batch, num_splits, act_dtype=act,
                           part_dtype=part_dtype or act,
-                          out_dtype=out_dtype or TORCH_DT[wl.out_dtype], kernel=kernel)
+                          out_dtype=out_dtype or TORCH_DT[wl.out_dtype], kernel=kernel,
+                          fp8_query=fp8_query)
     step.run(dev.q_nope, dev.q_rope, dev.w_uk, dev.w_uv, dev.cache)
     torch.cuda.synchronize()
     return step

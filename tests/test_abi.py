@@ -94,6 +94,11 @@ def test_decode_validation():
     assert decode(c=cache(dtype=FP8)) == E_ARG  # fp8 cache without row scales
     assert decode(c=cache(dtype=BF16, row_scale=P)) == E_ARG  # scales on a bf16 cache
     assert decode(q_scale=P) == E_ARG  # q scales with a bf16 query
+    # an E4M3 query: an E4M3 cache only, with its factors
+    f8 = cache(dtype=FP8, row_scale=P)
+    assert decode(q_dt=FP8, q_scale=None, c=f8) == E_ARG
+    assert decode(q_dt=FP8, q_scale=P) == E_DTYPE  # bf16 cache
+    assert decode(q_dt=FP8, q_scale=P, c=cache(dtype=F32)) == E_DTYPE
     # alignment
     assert decode(c=cache(rows=P + 8)) == E_ALIGN
     assert decode(q=P + 2) == E_ALIGN
@@ -113,6 +118,11 @@ def test_absorb_validation():
     assert absorb(q_dt=FP8) == E_DTYPE
     assert absorb(out_dt=FP8, scale=None) == E_ARG
     assert absorb(out_dt=BF16, scale=P) == E_ARG
+    # the E4M3 output needs bf16 inputs and d_nope <= 128 (host checks, nothing launched)
+    assert absorb(out_dt=FP8, scale=P, q_dt=F32) == E_UNSUP
+    assert absorb(out_dt=FP8, scale=P, w_dt=F32) == E_UNSUP
+    assert absorb(out_dt=FP8, scale=P, dd=dims(dn=192)) == E_UNSUP
+    assert absorb(out_dt=FP8, scale=P, qn=P + 2) == E_UNSUP
     assert absorb(dd=dims(dn=300)) == E_SHAPE
     assert absorb(out=P + 2) == E_ALIGN
 

@@ -316,6 +316,7 @@ def test_repeat_is_deterministic():
 # ---------------------------------------------------------------- full sizes
 
 AUTO = mla.KERNEL_AUTO
+F8Q = "fp8 query"  # mla.KERNEL_AUTO with the E4M3 absorbed query
 # (workload, tolerance kind, sequences x heads sampled, kernel, parts): the
 # sampled sequences are spread from the first to the last (both ends of the
 # XCD-aware work order) and the heads over both 64-head groups; a sample whose
@@ -331,6 +332,9 @@ FULL = [
     ("paged_b64_ragged", "bf16", 8, 8, AUTO, 2),
     ("fp8_b1_l128k", "fp8", 1, 8, AUTO, 1),
     ("fp8_b8_l128k", "fp8", 8, 8, AUTO, 4),
+    # the fp8 absorbed query on the fp8 matrix cores
+    ("fp8_b1_l128k", "fp8", 1, 8, F8Q, 1),
+    ("fp8_b8_l128k", "fp8", 8, 8, F8Q, 4),
 ]
 FULL_CASES = [(n, k, nb, nh, ker, part, parts) for n, k, nb, nh, ker, parts in FULL
               for part in range(parts)]
@@ -349,7 +353,10 @@ def _full_run(name, kernel):
         _log(f"{name}: generating inputs")
         dev = DeviceInputs(synth.make_inputs(wl))
         _log(f"{name}: running S={wl.num_splits} kernel={kernel}")
-        step = run_step(dev, wl.num_splits, kernel=kernel)
+        if kernel == F8Q:
+            step = run_step(dev, wl.num_splits, fp8_query=True)
+        else:
+            step = run_step(dev, wl.num_splits, kernel=kernel)
         _full_cache[key] = (dev, step)
     return _full_cache[key]
 
