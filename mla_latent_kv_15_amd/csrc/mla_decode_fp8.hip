@@ -57,8 +57,8 @@ constexpr int kF8PBytes = kH64 * kF8Tok;    // P' codes of one tile: 64 heads x 
 constexpr int kF8POff = kNBuf * kTileBytes;             // P' [2 tiles][hb][half][lane][16 B]
 constexpr int kF8SOff = kF8POff + 2 * kF8PBytes;        // P' factors [2 tiles][hb][half][32] (E8M0)
 constexpr int kF8ROff = kF8SOff + 2 * 128;              // row factors [kNBuf][64] fp32
-constexpr int kF8XOff = kF8ROff + kNBuf * kF8Tok * 4;   // exchange float[2][2][64], votes int[8]
-constexpr int kF8Lds = kF8XOff + 1024 + 32;
+constexpr int kF8XOff = kF8ROff + kNBuf * kF8Tok * 4;   // exchange float[2][2][64], linv float[64], votes int[8]
+constexpr int kF8Lds = kF8XOff + 1024 + 256 + 32;
 static_assert(kF8Lds <= 160 * 1024, "fp8 decode LDS");
 // vector-memory instructions per tile and PV wave: 9 row lines + 1 factor load
 // (the s_waitcnt vmcnt counts below are multiples of it)
@@ -132,21 +132,25 @@ __device__ inline void f8_factor_issue(const float* tile_scale, uint32_t lds_fac
 template <int PART_DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kF8Threads, kF8Threads),
                           amdgpu_waves_per_eu(2, 2)))
-void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
+void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table, int R) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kF8Lds];
   float* rfac = reinterpret_cast<float*>(smem + kF8ROff);  // [kNBuf][64] row factors
   float* xch = reinterpret_cast<float*>(smem + kF8XOff);   // [2][2][64] per-head exchange
-  int* votes = reinterpret_cast<int*>(smem + kF8XOff + 1024);
-  float* linv = reinterpret_cast<float*>(smem);  // epilogue: 1 / l per head (tile buffer 0)
+  float* linv = xch + 256;                                 // [64] 1 / normaliser per head
+  int* votes = reinterpret_cast<int*>(smem + kF8XOff + 1280);
 
-  const int nwork = P.B * P.QL * P.S * P.HG;
+  // work id -> (head group, query token j, group of R split ranges, sequence
+  // b), the head groups and query tokens of one range group adjacent (same
+  // XCD: they share each tile through L2)
+  const int NG = (P.S + R - 1) / R;
+  const int nwork = P.B * P.QL * NG * P.HG;
   const int wid = xcd_remap(blockIdx.x, nwork);
   const int hg = wid % P.HG;
   const int r1 = wid / P.HG;
   const int qj = r1 % P.QL;
   const int r2 = r1 / P.QL;
-  const int p = r2 % P.S;
-  const int b = r2 / P.S;
+  const int grp = r2 % NG;
+  const int b = r2 / NG;
   const int bj = b * P.QL + qj;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,23 +162,34 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
 
   const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
                         (P.QL - 1 - qj), 0);
-  const int t_begin = p * P.chunk;
-  const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase;
+  // the workgroup's ranges p_first .. p_end - 1 cover tokens [T0, T1): K
+  // consecutive 64-token tiles (every range is a whole number ntf of tiles),
+  // one pipeline through all of them; ranges from p_live on hold no token
+  const int p_first = grp * R, p_end = min(p_first + R, P.S);
+  const int T0 = p_first * P.chunk;
+  const int T1 = min(p_end * P.chunk, L);
+  const int K = T1 > T0 ? (T1 - T0 + kF8Tok - 1) / kF8Tok : 0;
+  const int ntf = P.chunk / kF8Tok;
+  const int p_live = K > 0 ? p_first + (K - 1) / ntf + 1 : p_first;
+  auto row_base = [&](int p) { return (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase; };
 
-  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
-    if (!is_qk) {
-      const int pt = tid - 256;
-      for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
-        store_elem<PART_DT>(P.u_part, row_base * kDLatent + idx, 0.0f);
-      if (pt < nhb * kHeadsPerWave) P.lse_part[row_base + pt] = -INFINITY;
-    }
+  // ranges without tokens: u = 0, lse = -inf (PV waves)
+  auto write_empty = [&](int p) {
+    const int pt = tid - 256;
+    for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
+      store_elem<PART_DT>(P.u_part, row_base(p) * kDLatent + idx, 0.0f);
+    if (pt < nhb * kHeadsPerWave) P.lse_part[row_base(p) + pt] = -INFINITY;
+  };
+  if (K == 0) {
+    if (!is_qk)
+      for (int p = p_first; p < p_end; ++p) write_empty(p);
     return;
   }
-  const int ntiles = (t_end - t_begin + kF8Tok - 1) / kF8Tok;
 
   // s_barriers, issued by both roles in the same order:
-  //   Q1 Q2 | per pass: T0 [AM AM] B_0..B_{n-1} V1 V2 [AM AM] | E1 E2
+  //   Q1 Q2 T0 | per range: [pass 0: AM AM] B_k0 .. B_k1-1 V1 V2
+  //   [redo: AM AM T0 B_k0 .. B_k1-1 V1 V2] E1 E2
+  // E2 of a range also certifies that the next range's first tile landed.
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   if (is_qk) {
@@ -237,10 +252,8 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
       // matrix-core result -> VALU reads (16-pass MFMA)
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
     };
-    // scores in the log2 domain: raw x row factor x query factor x scale;
-    // tokens past the range end -> -inf.  rs receives the row factors, ri
-    // their reciprocals.
-    auto scale_scores = [&](f32x16_t& s, float (&rs)[16], float (&ri)[16], int buf, int tile) {
+    // row factors of the lane's 16 tokens of tile buffer buf
+    auto load_factors = [&](float (&rs)[16], int buf) {
       const float* rp = rfac + buf * kF8Tok + 32 * th + 4 * gq;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
@@ -248,12 +261,14 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
 #pragma unroll
         for (int q = 0; q < 4; ++q) rs[4 * s4 + q] = v[q];
       }
+    };
+    // scores in the log2 domain: raw x row factor x query factor x scale;
+    // tokens past the range end (nvalid tokens in the tile) -> -inf
+    auto scale_scores = [&](f32x16_t& s, int buf, int nvalid) {
+      float rs[16];
+      load_factors(rs, buf);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] *= qf * rs[r];
-        ri[r] = __builtin_amdgcn_rcpf(rs[r]);
-      }
-      const int nvalid = t_end - (t_begin + tile * kF8Tok);
+      for (int r = 0; r < 16; ++r) s[r] *= qf * rs[r];
       if (nvalid < kF8Tok) {
         int first = 32 * th + 4 * gq;
         asm volatile("" : "+v"(first));
@@ -262,8 +277,11 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
           s[r] = (first + 8 * (r >> 2) + (r & 3) < nvalid) ? s[r] : -INFINITY;
       }
     };
-    auto softmax_publish = [&](const f32x16_t& s, const float (&rs)[16], const float (&ri)[16],
-                               int& overflow, uint8_t* PB, uint8_t* SB) {
+    auto softmax_publish = [&](const f32x16_t& s, int& overflow, int k) {
+      float rs[16];  // reloaded: not held across the MFMAs
+      load_factors(rs, k & (kNBuf - 1));
+      uint8_t* PB = smem + kF8POff + (k & 1) * kF8PBytes;
+      uint8_t* SB = smem + kF8SOff + (k & 1) * 128;
       float mx = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -289,8 +307,8 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
         // the weights as the value product sees them: code / f / row factor
         const f32x2_t c01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
         const f32x2_t c23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-        lu += c01[0] * ri[4 * s4] + c01[1] * ri[4 * s4 + 1] + c23[0] * ri[4 * s4 + 2] +
-              c23[1] * ri[4 * s4 + 3];
+        lu += c01[0] * __builtin_amdgcn_rcpf(rs[4 * s4]) + c01[1] * __builtin_amdgcn_rcpf(rs[4 * s4 + 1]) +
+              c23[0] * __builtin_amdgcn_rcpf(rs[4 * s4 + 2]) + c23[1] * __builtin_amdgcn_rcpf(rs[4 * s4 + 3]);
         // tokens 8 s4 + 4 gq .. +3 of the half: lane n + 32 (s4 / 2) of the
         // B operand, bytes 8 (s4 % 2) + 4 gq
         *reinterpret_cast<int*>(PB + ((qhb * 2 + th) * 64 + n + 32 * (s4 >> 1)) * 16 + 8 * (s4 & 1) +
@@ -308,62 +326,68 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
       barrier();  // AM
     };
 
-    for (int pass = 0; pass < 2; ++pass) {
-      l_run = 0.0f;
-      l_used = 0.0f;
-      int overflow = 0;
-      barrier();  // T0: tile 0 landed
-      f32x16_t s;
-      float rs[16], ri[16];
-      if (active) {
-        qk_tile(smem, s);
-        scale_scores(s, rs, ri, 0, 0);
-      }
-      if (pass == 0) {  // reference: maximum of the first tile
-        float mx = -INFINITY;
+    barrier();  // T0: the first tile landed
+    for (int p = p_first; p < p_live; ++p) {
+      const int k0 = (p - p_first) * ntf, k1 = min(k0 + ntf, K);
+      const int te = min((p + 1) * P.chunk, L);  // the range's end
+      auto nvalid = [&](int k) { return te - (T0 + k * kF8Tok); };
+      m_ref = -INFINITY;
+      m_seen = -INFINITY;
+      for (int pass = 0; pass < 2; ++pass) {
+        l_run = 0.0f;
+        l_used = 0.0f;
+        int overflow = 0;
+        if (pass > 0) barrier();  // T0: the range's first tile loaded again
+        f32x16_t s;
         if (active) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+          qk_tile(smem + (k0 & (kNBuf - 1)) * kTileBytes, s);
+          scale_scores(s, k0 & (kNBuf - 1), nvalid(k0));
         }
-        agree_max(mx);
-        m_ref = mx;
-      }
-      if (active) softmax_publish(s, rs, ri, overflow, smem + kF8POff, smem + kF8SOff);
-      for (int i = 0; i < ntiles; ++i) {
-        barrier();  // B_i: P'(i) published, tile i+1 landed
-        if (active && i + 1 < ntiles) {
-          const int buf = (i + 1) & (kNBuf - 1);
-          qk_tile(smem + buf * kTileBytes, s);
-          scale_scores(s, rs, ri, buf, i + 1);
-          softmax_publish(s, rs, ri, overflow, smem + kF8POff + ((i + 1) & 1) * kF8PBytes,
-                          smem + kF8SOff + ((i + 1) & 1) * 128);
-        }
-      }
-      const int vote = __any(overflow) ? 1 : 0;
-      if (lane == 0) votes[wave] = vote;
-      barrier();  // V1
-      int again = 0;
+        if (pass == 0) {  // reference: maximum of the range's first tile
+          float mx = -INFINITY;
+          if (active) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) again |= votes[w];
-      barrier();  // V2
-      if (!again) break;
-      agree_max(m_seen);  // redo the range with the range maximum as reference
-      m_ref = m_seen;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+          }
+          agree_max(mx);
+          m_ref = mx;
+        }
+        if (active) softmax_publish(s, overflow, k0);
+        for (int k = k0; k < k1; ++k) {
+          barrier();  // B_k: P'(k) published, tile k+1 landed
+          if (active && k + 1 < k1) {
+            const int buf = (k + 1) & (kNBuf - 1);
+            qk_tile(smem + buf * kTileBytes, s);
+            scale_scores(s, buf, nvalid(k + 1));
+            softmax_publish(s, overflow, k + 1);
+          }
+        }
+        const int vote = __any(overflow) ? 1 : 0;
+        if (lane == 0) votes[wave] = vote;
+        barrier();  // V1
+        int again = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) again |= votes[w];
+        barrier();  // V2
+        if (!again) break;
+        agree_max(m_seen);  // redo the range with the range maximum as reference
+        m_ref = m_seen;
+      }
+      l_run += __shfl_xor(l_run, 32);
+      l_used += __shfl_xor(l_used, 32);
+      if (active && gq == 0) {
+        xch[th * 64 + qhb * 32 + n] = l_run;
+        xch[128 + th * 64 + qhb * 32 + n] = l_used;
+      }
+      barrier();  // E1
+      if (active && th == 0 && gq == 0) {
+        const int hx = qhb * 32 + n;
+        const float l_tot = xch[hx] + xch[64 + hx];
+        linv[hx] = 1.0f / (xch[128 + hx] + xch[192 + hx]);
+        P.lse_part[row_base(p) + hx] = (m_ref + log2f(l_tot)) * kLn2;
+      }
+      barrier();  // E2
     }
-    l_run += __shfl_xor(l_run, 32);
-    l_used += __shfl_xor(l_used, 32);
-    if (active && gq == 0) {
-      xch[th * 64 + qhb * 32 + n] = l_run;
-      xch[128 + th * 64 + qhb * 32 + n] = l_used;
-    }
-    barrier();  // E1
-    if (active && th == 0 && gq == 0) {
-      const int hx = qhb * 32 + n;
-      const float l_tot = xch[hx] + xch[64 + hx];
-      linv[hx] = 1.0f / (xch[128 + hx] + xch[192 + hx]);
-      P.lse_part[row_base + hx] = (m_ref + log2f(l_tot)) * kLn2;
-    }
-    barrier();  // E2
     return;
   }
 
@@ -399,11 +423,11 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
     }
     asm volatile("s_nop 4");  // accumulator writes -> first (inline-asm) MFMA read
   };
-  // U^T += V(i)^T P'(i): 8 block-scaled MFMAs; after_mfma(st) runs after MFMA st
-  auto pv_tile = [&](int i, auto&& after_mfma) {
-    const uint8_t* T = smem + (i & (kNBuf - 1)) * kTileBytes;
-    const uint8_t* PB = smem + kF8POff + (i & 1) * kF8PBytes;
-    const uint8_t* SB = smem + kF8SOff + (i & 1) * 128;
+  // U^T += V(k)^T P'(k): 8 block-scaled MFMAs; after_mfma(st) runs after MFMA st
+  auto pv_tile = [&](int k, auto&& after_mfma) {
+    const uint8_t* T = smem + (k & (kNBuf - 1)) * kTileBytes;
+    const uint8_t* PB = smem + kF8POff + (k & 1) * kF8PBytes;
+    const uint8_t* SB = smem + kF8SOff + (k & 1) * 128;
     i32x8_t av[4];
 #pragma unroll
     for (int cbl = 0; cbl < 4; ++cbl)
@@ -443,153 +467,177 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
     const float* scale;
     int nvalid;
   };
-  auto dma_plan = [&](int tile) {
-    const int tt = t_begin + tile * kF8Tok;
+  // tile k of the workgroup: tokens T0 + 64 k .., all attended (T1 <= L)
+  auto dma_plan = [&](int k) {
+    const int tt = T0 + k * kF8Tok;
     const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
-    const int nvalid = min(kF8Tok, t_end - tt);
+    const int nvalid = min(kF8Tok, T1 - tt);
     TileDma d;
     d.rows = f8_dma_plan(P.rows + row0 * kRowElems,
-                         lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes, nvalid, rw);
+                         lds_addr(smem) + (k & (kNBuf - 1)) * kTileBytes, nvalid, rw);
     d.scale = P.row_scale + row0;
     d.nvalid = nvalid;
     return d;
   };
-  auto dma_factors = [&](const TileDma& d, int tile) {
-    f8_factor_issue(d.scale, lds_addr(rfac) + (tile & (kNBuf - 1)) * kF8Tok * 4, d.nvalid, rw, lane);
+  auto dma_factors = [&](const TileDma& d, int k) {
+    f8_factor_issue(d.scale, lds_addr(rfac) + (k & (kNBuf - 1)) * kF8Tok * 4, d.nvalid, rw, lane);
   };
-  auto dma = [&](int tile) {
-    const TileDma d = dma_plan(tile);
+  auto dma = [&](int k) {
+    const TileDma d = dma_plan(k);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) f8_dma_issue(d.rows, i);
-    dma_factors(d, tile);
+    dma_factors(d, k);
+  };
+  // wait until tile k has landed, when tiles up to min(k + 2, K - 1) were
+  // issued (and nothing after them)
+  auto wait_tile = [&](int k) {
+    const int later = min(K - 1, k + 2) - k;  // 0, 1 or 2 tiles issued after k
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
-  // queries (one tile buffer: 64 heads x 576 codes), then tiles 0 and 1
+  // queries (one tile buffer: 64 heads x 576 codes), then tiles 0-2
   {
     const F8Dma dq = f8_dma_plan(qsrc, lds_addr(smem) + 3 * kTileBytes, nhb * kHeadsPerWave, rw);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) f8_dma_issue(dq, i);
   }
   dma(0);
-  if (ntiles > 1) dma(1);
-  if (ntiles > 1)
-    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (K > 1) dma(1);
+  wait_tile(0);  // at least the queries (issued first) have landed
   barrier();  // Q1
-  barrier();  // Q2
+  barrier();  // Q2: buffer 3 free
+  if (K > 2) dma(2);
+  wait_tile(0);
+  barrier();  // T0
 
-  for (int pass = 0; pass < 2; ++pass) {
-    zero_acc();
-    if (pass > 0) {
-      dma(0);
-      if (ntiles > 1) dma(1);
-    }
-    if (ntiles > 2) dma(2);
-    if (ntiles > 2)
-      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-    else if (ntiles > 1)
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    barrier();  // T0
-    if (pass == 0) {
-      barrier();  // AM
-      barrier();  // AM
-    }
-    for (int i = 0; i < ntiles; ++i) {
-      if (i + 2 < ntiles)
-        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else
+  for (int p = p_first; p < p_live; ++p) {
+    const int k0 = (p - p_first) * ntf, k1 = min(k0 + ntf, K);
+    for (int pass = 0; pass < 2; ++pass) {
+      zero_acc();
+      if (pass > 0) {  // the range again: its first tiles back into the buffers
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      barrier();  // B_i
-      // tile i+3 into tile i-1's buffer: one row line after each MFMA, the
-      // last line and the row factors after the last
-      const bool dnext = i + 3 < ntiles;  // workgroup-uniform
-      TileDma dp{};
-      if (dnext) dp = dma_plan(i + 3);
-      pv_tile(i, [&](int st) {
-        if (dnext) {
-          f8_dma_issue(dp.rows, st);
-          if (st == 7) {
-            f8_dma_issue(dp.rows, 8);
-            dma_factors(dp, i + 3);
-          }
-        }
-      });
-    }
-    if (lane == 0) votes[wave] = 0;
-    barrier();  // V1
-    int again = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) again |= votes[w];
-    barrier();  // V2
-    if (!again) break;
-    barrier();  // AM
-    barrier();  // AM
-  }
-
-  barrier();  // E1
-  barrier();  // E2: linv ready
-  // matrix-core accumulator writes -> VALU reads
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-  // U^T register r of block (hb, cbl) in lane (hl, g) is column
-  // 128 rw + 32 cbl + 8 (r / 4) + 4 g + r % 4 of head hbase + 32 hb + hl; each
-  // wave stages one head block (32 rows x 128 columns) at a time in its own
-  // LDS region (tile buffer 0, past linv) and writes 256 contiguous bytes per
-  // row.
-  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
-  constexpr int kColsRound = 256 / kEsz;
-  constexpr int kStageRow = kColsRound * kEsz + 16;
-  uint8_t* W = smem + 1024 + rw * kHeadsPerWave * kStageRow;
-#pragma unroll
-  for (int hb = 0; hb < kH64Blocks; ++hb) {
-    if (hb < nhb) {
-      const float inv = linv[hb * kHeadsPerWave + hl];
-#pragma unroll
-      for (int half = 0; half < 128 / kColsRound; ++half) {
-#pragma unroll
-        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
-          const int cbl = half * (kColsRound / 32) + cbl2;
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
-            const f32x16_t& A = acc[4 * hb + cbl];
-            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
-            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
-            uint8_t* wp = W + hl * kStageRow + c * kEsz;
-            if constexpr (PART_DT == MLA_F32) {
-              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
-            } else {
-              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        dma(k0);
+        if (k0 + 1 < K) dma(k0 + 1);
+        if (k0 + 2 < K) dma(k0 + 2);
+        wait_tile(k0);
+        barrier();  // T0
+      } else {
+        barrier();  // AM
+        barrier();  // AM
+      }
+      for (int k = k0; k < k1; ++k) {
+        // tiles up to min(k + 2, K - 1) are issued: tile k + 1 lands
+        if (k + 2 < K)
+          asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        barrier();  // B_k
+        // tile k+3 into tile k-1's buffer: one row line after each MFMA, the
+        // last line and the row factors after the last
+        const bool dnext = k + 3 < K;  // workgroup-uniform
+        TileDma dp{};
+        if (dnext) dp = dma_plan(k + 3);
+        pv_tile(k, [&](int st) {
+          if (dnext) {
+            f8_dma_issue(dp.rows, st);
+            if (st == 7) {
+              f8_dma_issue(dp.rows, 8);
+              dma_factors(dp, k + 3);
             }
           }
-        }
-        asm volatile("" ::: "memory");
-        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
-                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * rw) * kEsz +
-                       half * (kColsRound * kEsz);
+        });
+      }
+      if (lane == 0) votes[wave] = 0;
+      barrier();  // V1
+      int again = 0;
 #pragma unroll
-        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
-          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
-                                      (lane & 15) * 16) = v;
+      for (int w = 0; w < 4; ++w) again |= votes[w];
+      barrier();  // V2
+      if (!again) break;
+      barrier();  // AM
+      barrier();  // AM
+    }
+    if (k1 < K) wait_tile(k1);  // E2 certifies the next range's first tile
+    barrier();  // E1
+    barrier();  // E2: linv ready
+    // matrix-core accumulator writes -> VALU reads
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    // U^T register r of block (hb, cbl) in lane (hl, g) is column
+    // 128 rw + 32 cbl + 8 (r / 4) + 4 g + r % 4 of head hbase + 32 hb + hl;
+    // each wave stages one head block (32 rows x 128 columns) at a time in its
+    // own region of the range's last tile buffer (free: its next tile is
+    // loaded only after B_k1) and writes 256 contiguous bytes per row.
+    constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
+    constexpr int kColsRound = 256 / kEsz;
+    constexpr int kStageRow = kColsRound * kEsz + 16;
+    // the lane index recomputed here (volatile), so that the epilogue's
+    // addresses are formed in place rather than held across the range loop
+    int eln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(eln));
+    const int hl = eln & 31, g = eln >> 5;
+    uint8_t* W = smem + ((k1 - 1) & (kNBuf - 1)) * kTileBytes + rw * kHeadsPerWave * kStageRow;
+#pragma unroll
+    for (int hb = 0; hb < kH64Blocks; ++hb) {
+      if (hb < nhb) {
+        const float inv = linv[hb * kHeadsPerWave + hl];
+#pragma unroll
+        for (int half = 0; half < 128 / kColsRound; ++half) {
+#pragma unroll
+          for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
+            const int cbl = half * (kColsRound / 32) + cbl2;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int c = 32 * cbl2 + 8 * r4 + 4 * g;
+              const f32x16_t& A = acc[4 * hb + cbl];
+              const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
+              const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
+              uint8_t* wp = W + hl * kStageRow + c * kEsz;
+              if constexpr (PART_DT == MLA_F32) {
+                *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
+              } else {
+                *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+              }
+            }
+          }
+          asm volatile("" ::: "memory");
+          uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
+                         ((row_base(p) + hb * kHeadsPerWave) * kDLatent + 128 * rw) * kEsz +
+                         half * (kColsRound * kEsz);
+#pragma unroll
+          for (int i = 0; i < kHeadsPerWave / 4; ++i) {
+            const int row = 4 * i + (eln >> 4);
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (eln & 15) * 16);
+            *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
+                                        (eln & 15) * 16) = v;
+          }
+          asm volatile("" ::: "memory");
         }
-        asm volatile("" ::: "memory");
       }
     }
   }
+  for (int p = p_live; p < p_end; ++p) write_empty(p);
 }
 
 }  // namespace
 
-mla_status_t decode_fp8q_launch(const DecodeParams& P, int32_t part_dt, unsigned grid,
-                                hipStream_t s) {
+mla_status_t decode_fp8q_launch(const DecodeParams& P, int32_t part_dt, hipStream_t s) {
+  // split ranges per workgroup: enough workgroups to fill the 256 CUs once,
+  // each walking consecutive ranges of one sequence with one pipeline
+  const int64_t units = static_cast<int64_t>(P.B) * P.QL * P.S * P.HG;
+  const int64_t per_cu = units / 256;
+  const int R = static_cast<int>(per_cu < 1 ? 1 : (per_cu > P.S ? P.S : per_cu));
+  const int64_t nblk = static_cast<int64_t>(P.B) * P.QL * ((P.S + R - 1) / R) * P.HG;
+  if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
+  const unsigned grid = static_cast<unsigned>(nblk);
   if (part_dt == MLA_F32)
-    decode_f8q_kernel<MLA_F32><<<grid, kF8Threads, 0, s>>>(P, P.block_table);
+    decode_f8q_kernel<MLA_F32><<<grid, kF8Threads, 0, s>>>(P, P.block_table, R);
   else
-    decode_f8q_kernel<MLA_BF16><<<grid, kF8Threads, 0, s>>>(P, P.block_table);
+    decode_f8q_kernel<MLA_BF16><<<grid, kF8Threads, 0, s>>>(P, P.block_table, R);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 

@@ -32,10 +32,9 @@ struct DecodeParams {
   const float* q_scale;  // E4M3 query: one factor per (b, query token, head)
 };
 
-// fp8 cache and fp8 absorbed query, on the fp8 matrix cores (grid: one
-// workgroup per (sequence, query token, split range, 64 heads))
-mla_status_t decode_fp8q_launch(const DecodeParams& P, int32_t part_dt, unsigned grid,
-                                hipStream_t s);
+// fp8 cache and fp8 absorbed query, on the fp8 matrix cores (one workgroup
+// per (sequence, query token, group of consecutive split ranges, 64 heads))
+mla_status_t decode_fp8q_launch(const DecodeParams& P, int32_t part_dt, hipStream_t s);
 
 namespace {
 

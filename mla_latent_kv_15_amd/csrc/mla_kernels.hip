@@ -2863,15 +2863,13 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   const int32_t HG64 = (H + kH64 - 1) / kH64;
   if (q_abs_dt == MLA_FP8_E4M3) {  // fp8 cache and query: 64-token tiles on the fp8 matrix cores
     if (kernel != MLA_KERNEL_AUTO && kernel != MLA_KERNEL_H64) return MLA_E_UNSUPPORTED;
-    const int64_t nblk = static_cast<int64_t>(B) * q_len * num_splits * HG64;
-    if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
     const int32_t per = 2 * kTileTokens * num_splits;
     const int32_t chunk64 = max((span + per - 1) / per, 1) * (2 * kTileTokens);
     DecodeParams Q{q_abs, static_cast<const uint8_t*>(cache->rows), cache->row_scale,
                    cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                    cache->page_size != 0, B, H, num_splits, HG64, chunk64, cache->max_seq_len,
                    q_len, scale * kLog2e, u_part, lse_part, cache->ring, q_abs_scale};
-    return decode_fp8q_launch(Q, part_dt, static_cast<unsigned>(nblk), s);
+    return decode_fp8q_launch(Q, part_dt, s);
   }
   const int64_t nblk64 = static_cast<int64_t>(B) * q_len * num_splits * HG64;
   if (nblk64 > 0x7FFFFFFF) return MLA_E_SHAPE;

@@ -11,6 +11,11 @@ ABI, against the oracle.
   odd lengths (a pair of rows whose second row is past the end), a one-token
   sequence, empty sequences, 32 and 128 heads, several splits;
 * the score-spike redo on this path.
+* workgroups that walk several consecutive split ranges with one pipeline
+  (many splits and few sequences: 256 splits at 2 x 128 heads gives 4 ranges
+  per workgroup), including ranges past the end of a sequence, a range group
+  that straddles it, and a score-spike redo of a range in the middle of a
+  group.
 The end-to-end step (absorb -> decode -> tail) at the full 128K sizes is in
 test_gpu_parity.py (the "fp8 query" cases)."""
 
@@ -205,4 +210,71 @@ def test_fp8_query_score_spike_recomputes_range():
     e_u = _rel(np.stack([u[b, h] for b, h in pairs]), u_ref)
     e_l = float(np.abs(np.array([lse[b, h] for b, h in pairs]) - l_ref).max())
     _log(f"spike: err u {e_u:.2e} lse {e_l:.2e}")
+    assert e_u <= TOL_FP8 and e_l <= TOL_FP8
+
+
+def test_fp8_query_multi_range_workgroups():
+    """256 splits x 2 sequences x 2 head groups: each workgroup walks 4
+    consecutive ranges of 64 tokens; sequences of 3000 and 700 tokens leave
+    most range groups partly or wholly past the end.  Every split's partial
+    against the oracle over its range."""
+    lens = [3000, 700]
+    S = 256
+    wl = synth.workload("fp8_b1_l128k").with_(batch=2, heads=128, seq_len=None,
+                                              seed=synth.workloads.BASE_SEED + 418)
+    inp = synth.make_inputs(wl, lengths=lens)
+    dev = DeviceInputs(inp)
+    codes, scale = _query(2, 128, 419)
+    _log("fp8 query multi-range")
+    u, lse, u_part, lse_part = _decode(dev, codes, scale, S, part=torch.float32)
+    pairs = [(b, h) for b in range(2) for h in (0, 64, 127)]
+    e_u, e_l = _check(inp, codes, scale, u, lse, pairs)
+    _log(f"  merged: err u {e_u:.2e} lse {e_l:.2e}")
+    assert e_u <= TOL_FP8 and e_l <= TOL_FP8
+    up, lp = u_part.cpu().numpy(), lse_part.cpu().numpy()
+    chunk = 64
+    for p in (0, 1, 3, 4, 10, 11, 12, 46, 47, 48, 255):
+        tb = [min(p * chunk, L) for L in lens]
+        te = [min((p + 1) * chunk, L) for L in lens]
+        u_ref, l_ref, _ = oracle.absorbed_decode(
+            codes, "fp8", inp.rows, "fp8", inp.seq_lens, q_scale=scale, row_scale=inp.row_scale,
+            seq_stride=inp.seq_stride, sel=pairs, t_begin=tb, t_end=te)
+        for k, (b, h) in enumerate(pairs):
+            if not np.isfinite(l_ref[k]):
+                assert np.all(up[b, p, h] == 0) and np.isneginf(lp[b, p, h]), (p, b, h)
+                continue
+            assert abs(lp[b, p, h] - l_ref[k]) <= TOL_FP8, (p, b, h)
+            assert _rel(up[b, p, h], u_ref[k]) <= TOL_FP8, (p, b, h)
+
+
+def test_fp8_query_spike_inside_a_range_group():
+    """A score spike in range 13 of 256 (ranges 12-15 share a workgroup): that
+    range alone is computed again, its neighbours are not disturbed."""
+    lens = [4000, 4000]
+    S = 256
+    wl = synth.workload("fp8_b1_l128k").with_(batch=2, heads=128, seq_len=None,
+                                              seed=synth.workloads.BASE_SEED + 420)
+    inp = synth.make_inputs(wl, lengths=lens)
+    codes, scale = _query(2, 128, 421)
+    q = oracle.decode_array(codes, "fp8")[0] * scale[0].astype(np.float64)[:, None]
+    spike = np.sign(q.mean(axis=0)) * 40.0
+    r = inp.row_index(0, 64 * 13 + 10)
+    c8, s8 = quantize_rows_e4m3(spike[None, :].astype(np.float32))
+    rows, rsc = inp.rows.copy(), inp.row_scale.copy()
+    rows[r], rsc[r] = c8[0], s8[0]
+    inp = dataclasses.replace(inp, rows=rows, row_scale=rsc)
+    dev = DeviceInputs(inp)
+    u, lse, u_part, lse_part = _decode(dev, codes, scale, S, part=torch.float32)
+    pairs = [(b, h) for b in range(2) for h in (0, 77, 127)]
+    up, lp = u_part.cpu().numpy(), lse_part.cpu().numpy()
+    for p in (11, 12, 13, 14, 15, 16):
+        tb, te = [p * 64] * 2, [(p + 1) * 64] * 2
+        u_ref, l_ref, _ = oracle.absorbed_decode(
+            codes, "fp8", inp.rows, "fp8", inp.seq_lens, q_scale=scale, row_scale=inp.row_scale,
+            seq_stride=inp.seq_stride, sel=pairs, t_begin=tb, t_end=te)
+        for k, (b, h) in enumerate(pairs):
+            assert abs(lp[b, p, h] - l_ref[k]) <= TOL_FP8, (p, b, h)
+            assert _rel(up[b, p, h], u_ref[k]) <= TOL_FP8, (p, b, h)
+    e_u, e_l = _check(inp, codes, scale, u, lse, pairs)
+    _log(f"spike in a range group: err u {e_u:.2e} lse {e_l:.2e}")
     assert e_u <= TOL_FP8 and e_l <= TOL_FP8

@@ -50,6 +50,9 @@ CASES = [  # (batch, lengths or uniform L, splits, partial dtype, output dtype)
     (1, 5000, 37, torch.bfloat16, torch.bfloat16),
     (1, 3000, 256, torch.bfloat16, torch.float32),
     (1, 700, 5, torch.float32, torch.bfloat16),
+    # many splits: fewer sequences per workgroup than the grid alone would need
+    (8, 9000, 256, torch.bfloat16, torch.bfloat16),
+    (33, 500, 64, torch.bfloat16, torch.float32),
 ]
 
 
