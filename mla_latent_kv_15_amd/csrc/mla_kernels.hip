@@ -2036,20 +2036,21 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
 // (sequence, head), by the rule of the fp8 cache rows: the factor maps the
 // row's largest magnitude over all 576 elements onto 448, each code is the
 // correctly rounded quotient x / factor rounded to the nearest E4M3 value
-// (ties to even).  The factor needs the whole row in one workgroup: one
-// workgroup per (head, 32 sequences), 8 waves.  W_UK[h] (d_nope x 512 bf16,
-// d_nope <= 128) is staged whole in LDS; wave w computes latent columns
-// 64w..64w+63 of the 32 sequences on v_mfma_f32_32x32x16_bf16 (A = W_UK^T by
-// transposing reads, B = the query rows, as in absorb_mfma_kernel); the first
-// 256 threads carry the RoPE part (rotated when positions are given); the row
-// maxima meet in LDS; the codes are staged in LDS over the W_UK slab, which
-// is no longer read, and leave as whole 576-byte rows.
-constexpr int kAf8Threads = 512;
+// (ties to even, by the hardware conversion).  The factor needs the whole row
+// in one workgroup: one workgroup per (head, 32 sequences), 16 waves.
+// W_UK[h] (d_nope x 512 bf16, d_nope <= 128) is staged whole in LDS; wave w
+// computes latent columns 32w..32w+31 of the 32 sequences on
+// v_mfma_f32_32x32x16_bf16 (A = W_UK^T by transposing reads, B = the query
+// rows, as in absorb_mfma_kernel); the first 256 threads carry the RoPE part
+// (rotated when positions are given); the row maxima meet in LDS; the codes
+// are staged in LDS over the W_UK slab, which is no longer read, and leave as
+// whole 576-byte rows.
+constexpr int kAf8Threads = 1024;
 constexpr int kAf8Row = kDLatent * 2 + 16;               // padded LDS row of W_UK[h]
 constexpr int kAf8QStride = 2 * 128 + 16;                // padded query row (d_nope <= 128)
 constexpr int kAf8QOff = 128 * kAf8Row;
-constexpr int kAf8RedOff = kAf8QOff + 32 * kAf8QStride;  // float [32][16]: row maxima
-constexpr int kAf8ScOff = kAf8RedOff + 32 * 16 * 4;      // float [32]: factors
+constexpr int kAf8RedOff = kAf8QOff + 32 * kAf8QStride;  // float [32][24]: row maxima
+constexpr int kAf8ScOff = kAf8RedOff + 32 * 24 * 4;      // float [32]: factors
 constexpr int kAf8Lds = kAf8ScOff + 32 * 4;
 constexpr int kAf8Out = kRowElems + 16;                  // staged code row
 static_assert(32 * kAf8Out <= kAf8QOff, "absorb fp8 output stage");
@@ -2067,12 +2068,13 @@ __global__ __launch_bounds__(kAf8Threads) void absorb_f8_kernel(const uint16_t* 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, bl = lane & 31;
   // every load before the first wait: W_UK[h] (d_nope rows of 64 chunks of
-  // 16 B, 16 per thread), the 32 query rows (one chunk per thread), the RoPE
+  // 16 B, 8 per thread), the 32 query rows (one chunk per thread), the RoPE
   // rows (threads < 256: 8 elements of sequence b0 + tid / 8)
   const uint16_t* wsrc = w_uk + static_cast<int64_t>(h) * d_nope * kDLatent;
-  u32x4_t st[16];
+  constexpr int kSt = 128 * 64 / kAf8Threads;
+  u32x4_t st[kSt];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < kSt; ++i) {
     const int q = i * kAf8Threads + tid;
     if (q < d_nope * 64) st[i] = *reinterpret_cast<const u32x4_t*>(wsrc + (q >> 6) * kDLatent + (q & 63) * 8);
   }
@@ -2109,7 +2111,7 @@ __global__ __launch_bounds__(kAf8Threads) void absorb_f8_kernel(const uint16_t* 
     }
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < kSt; ++i) {
     const int q = i * kAf8Threads + tid;
     if (q < d_nope * 64) *reinterpret_cast<u32x4_t*>(sm + (q >> 6) * kAf8Row + (q & 63) * 16) = st[i];
   }
@@ -2117,45 +2119,38 @@ __global__ __launch_bounds__(kAf8Threads) void absorb_f8_kernel(const uint16_t* 
   if (q_thread) *reinterpret_cast<u32x4_t*>(qs + qrow * kAf8QStride + 16 * qcol) = qv;
   __syncthreads();
 
-  // columns 32 cb .. 32 cb + 31, cb = 2 wave + c2; accumulator: column
-  // 32 cb + 8 (r / 4) + 4 g + r % 4 of sequence b0 + bl
+  // columns 32 wave .. 32 wave + 31; accumulator: column
+  // 32 wave + 8 (r / 4) + 4 g + r % 4 of sequence b0 + bl
   const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
-  f32x16_t acc[2];
+  f32x16_t acc;
 #pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[c2][r] = 0.0f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
   for (int k = 0; k < d_nope / 16; ++k) {
     const bf16x8_t bq = *reinterpret_cast<const bf16x8_t*>(qs + bl * kAf8QStride + 32 * k + 16 * g);
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const uint8_t* ab = sm + (16 * k + 8 * (G >> 1) + e) * kAf8Row +
-                          (32 * (2 * wave + c2) + 16 * (G & 1) + 4 * q4) * 2;
-      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ab);
-      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ab + 4 * kAf8Row));
-      const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[c2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[c2], 0, 0, 0);
-    }
+    const uint8_t* ab = sm + (16 * k + 8 * (G >> 1) + e) * kAf8Row +
+                        (32 * wave + 16 * (G & 1) + 4 * q4) * 2;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)ab);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ab + 4 * kAf8Row));
+    const bf16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
   }
-  // row maxima: 8 waves x 2 column halves, and 8 RoPE chunks, per sequence
+  // row maxima: 16 waves, and 8 RoPE chunks, per sequence
   float m = 0.0f;
 #pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[c2][r]));
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[r]));
   m = fmaxf(m, __shfl_xor(m, 32));
-  if (g == 0) red[bl * 16 + wave] = m;
+  if (g == 0) red[bl * 24 + wave] = m;
   if (rope_thread) {
     float mr = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) mr = fmaxf(mr, fabsf(y[k]));
-    red[(tid >> 3) * 16 + 8 + (tid & 7)] = mr;
+    red[(tid >> 3) * 24 + 16 + (tid & 7)] = mr;
   }
   __syncthreads();
   if (tid < 32) {
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, red[tid * 16 + i]);
+    for (int i = 0; i < 24; ++i) amax = fmaxf(amax, red[tid * 24 + i]);
     const float f = fmaxf(amax, 0x1p-126f) / 448.0f;
     fac[tid] = f;
     if (b0 + tid < B) q_scale[static_cast<int64_t>(b0 + tid) * H + h] = f;
@@ -2165,25 +2160,28 @@ __global__ __launch_bounds__(kAf8Threads) void absorb_f8_kernel(const uint16_t* 
   {
     const float f = fac[bl];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float x[4];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float x = fminf(fmaxf(acc[c2][4 * r4 + q] / f, -448.0f), 448.0f);
-          w |= e4m3_encode(x) << (8 * q);
-        }
-        *reinterpret_cast<uint32_t*>(sm + bl * kAf8Out + 32 * (2 * wave + c2) + 8 * r4 + 4 * g) = w;
-      }
+      for (int q = 0; q < 4; ++q) x[q] = fminf(fmaxf(acc[4 * r4 + q] / f, -448.0f), 448.0f);
+      // v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even (the same codes as
+      // e4m3_encode for |x| <= 448)
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+      *reinterpret_cast<int*>(sm + bl * kAf8Out + 32 * wave + 8 * r4 + 4 * g) = w;
+    }
   }
   if (rope_thread) {
     const float f = fac[tid >> 3];
-    uint32_t w[2] = {0u, 0u};
+    float x[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      w[k >> 2] |= e4m3_encode(fminf(fmaxf(y[k] / f, -448.0f), 448.0f)) << (8 * (k & 3));
-    *reinterpret_cast<u32x2_t*>(sm + (tid >> 3) * kAf8Out + kDLatent + rj) = u32x2_t{w[0], w[1]};
+    for (int k = 0; k < 8; ++k) x[k] = fminf(fmaxf(y[k] / f, -448.0f), 448.0f);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], w1, true);
+    *reinterpret_cast<u32x2_t*>(sm + (tid >> 3) * kAf8Out + kDLatent + rj) =
+        u32x2_t{static_cast<uint32_t>(w0), static_cast<uint32_t>(w1)};
   }
   __syncthreads();
   // 32 rows x 36 chunks of 16 B
@@ -2296,7 +2294,7 @@ constexpr int kCuRows = 16;                // sequences per workgroup
 constexpr int kCuRow = kDLatent * 2 + 16;  // padded LDS row of u (bf16)
 constexpr int kCuBatch = 4;                // splits per batch of partial loads
 
-template <int PART_DT, int O_DT, int VS>
+template <int PART_DT, int O_DT, int VS, int LSE_BLK>
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     const void* u_part, const float* lse_part, const uint16_t* w_uv, void* o, uint16_t* u_out,
     float* lse_out, int B, int H, int S, int d_v, int rows) {
@@ -2339,10 +2337,15 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
 
   // Every independent load is issued before the first wait, and all of them
   // unconditionally (clamped to valid addresses) so that the compiler's wait
-  // counts stay exact: the log-sum-exp input of split cg (the only one a lane
-  // needs when S <= 32), the wave's W_UV rows, the first batch of partials.
-  const bool lse_reg = S <= 32;  // workgroup-uniform
-  float lse_l = lse_part[prow + static_cast<int64_t>(min(cg, S - 1)) * H];
+  // counts stay exact: the log-sum-exp inputs of splits cg + 32 j (all a lane
+  // needs when S <= 32 kCuLse), the wave's W_UV rows, the first batch of
+  // partials.  LSE_BLK = 1 (S <= 32) or 8 (S <= 256) registers of them.
+  constexpr int kCuLse = LSE_BLK;
+  const bool lse_reg = S <= 32 * kCuLse;  // workgroup-uniform
+  float lse_l[kCuLse];
+#pragma unroll
+  for (int j = 0; j < kCuLse; ++j)
+    lse_l[j] = lse_part[prow + static_cast<int64_t>(min(cg + 32 * j, S - 1)) * H];
   auto wrow = [&](int nb) {
     return w_uv + (static_cast<int64_t>(h) * d_v + 16 * nb + n16) * kDLatent + 8 * kg;
   };
@@ -2373,16 +2376,22 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   // log-sum-exp weights over all splits of the sequence (every group of the
   // sequence computes the same values)
   float mx = -INFINITY, z = 0.0f;
-  float e_l = 0.0f;  // S <= 32: weight of split cg
-  int last = -1;     // last split with a finite log-sum-exp
+  float e_l[kCuLse];  // S <= 32 kCuLse: weights of splits cg + 32 j
+  int last = -1;       // last split with a finite log-sum-exp
   if (lse_reg) {
-    lse_l = cg < S ? lse_l : -INFINITY;
-    mx = lse_l;
-    last = lse_l != -INFINITY ? cg : -1;
+#pragma unroll
+    for (int j = 0; j < kCuLse; ++j) {
+      lse_l[j] = cg + 32 * j < S ? lse_l[j] : -INFINITY;
+      mx = max_nan(mx, lse_l[j]);
+      last = lse_l[j] != -INFINITY ? cg + 32 * j : last;
+    }
 #pragma unroll
     for (int o2 = 1; o2 < 32; o2 <<= 1) mx = max_nan(mx, __shfl_xor(mx, o2));
-    e_l = (mx != -INFINITY) ? expf(lse_l - mx) : 0.0f;
-    z = e_l;
+#pragma unroll
+    for (int j = 0; j < kCuLse; ++j) {
+      e_l[j] = (mx != -INFINITY) ? expf(lse_l[j] - mx) : 0.0f;
+      z += e_l[j];
+    }
   } else {
     for (int p = cg; p < S; p += 32) {
       const float x = lse_part[prow + static_cast<int64_t>(p) * H];
@@ -2417,8 +2426,16 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     }
 #pragma unroll
     for (int q = 0; q < kCuBatch; ++q) {
-      const float w = lse_reg ? __shfl(e_l, (lane & ~31) | (split(k0 + q) & 31))
-                              : __shfl(wl, (lane & ~31) | ((k0 + q) & 31));
+      float w;
+      if (lse_reg) {  // split p's weight: lane p % 32, register p / 32
+        const int sp = split(k0 + q);
+        float ev = e_l[0];
+#pragma unroll
+        for (int j = 1; j < kCuLse; ++j) ev = (sp >> 5) == j ? e_l[j] : ev;
+        w = __shfl(ev, (lane & ~31) | (sp & 31));
+      } else {
+        w = __shfl(wl, (lane & ~31) | ((k0 + q) & 31));
+      }
       if (k0 + q < ns) {
 #pragma unroll
         for (int i = 0; i < kLd; ++i)
@@ -3030,12 +3047,18 @@ static mla_status_t combine_up_launch(const mla_dims_t* dims, int32_t B, int32_t
   const uint16_t* w = static_cast<const uint16_t*>(w_uv);
 #define MLA_CU(PD, OD)                                                                             \
   if (part_dt == PD && o_dt == OD) {                                                               \
-    if (vsplit == 2)                                                                               \
-      combine_up_kernel<PD, OD, 2><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, B, \
-                                                               H, num_splits, dims->d_v, rows);    \
+    if (vsplit == 2 && num_splits <= 32)                                                           \
+      combine_up_kernel<PD, OD, 2, 1><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
+                                                                  B, H, num_splits, dims->d_v, rows); \
+    else if (vsplit == 2)                                                                          \
+      combine_up_kernel<PD, OD, 2, 8><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
+                                                                  B, H, num_splits, dims->d_v, rows); \
+    else if (num_splits <= 32)                                                                     \
+      combine_up_kernel<PD, OD, 1, 1><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
+                                                                  B, H, num_splits, dims->d_v, rows); \
     else                                                                                           \
-      combine_up_kernel<PD, OD, 1><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, B, \
-                                                               H, num_splits, dims->d_v, rows);    \
+      combine_up_kernel<PD, OD, 1, 8><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
+                                                                  B, H, num_splits, dims->d_v, rows); \
     return launch_status();                                                                        \
   }
   MLA_CU(MLA_BF16, MLA_BF16)
