@@ -221,20 +221,20 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
  *   MLA_KERNEL_H64  -- one workgroup per (sequence, split range, 64 heads);
  *                      two workgroups share each cached tile through L2.
  *                      Every cache dtype.
- *   MLA_KERNEL_H128 -- one workgroup per (sequence, split range, 128 heads):
- *                      each tile enters one CU once for all of its heads.
- *                      BF16 cache, h a multiple of 128.
  *   MLA_KERNEL_H128_WS -- one workgroup per (sequence, split range, 128
  *                      heads) of 12 waves: 4 compute the scores and the
  *                      softmax of 32 heads each, 8 the value product of 64
- *                      heads x 128 latent columns each, three waves per SIMD.
+ *                      heads x 128 latent columns each, three waves per SIMD;
+ *                      each tile enters one CU once for all of its heads.
  *                      BF16 cache, h a multiple of 128.
+ *   MLA_KERNEL_H128 -- the same 128-head decomposition (the name of an
+ *                      earlier 4-wave kernel that measured no faster).
  *   (an FP8 query always runs its own 64-head kernel: AUTO or H64.)
  *   MLA_KERNEL_AUTO -- what mla_decode and mla_decode_multi use: H64, which
- *                      measured as fast or faster than H128 on every bf16
- *                      workload and split count tried (H128 runs one wave per
- *                      SIMD, which leaves the matrix cores idle while a wave
- *                      waits on LDS, the tile DMA or its softmax). */
+ *                      measured as fast or faster than the 128-head
+ *                      decomposition on the full-size bf16 workloads (with one
+ *                      36 KB tile in flight per CU the 128-head stream is
+ *                      latency-bound under full load). */
 typedef enum {
   MLA_KERNEL_AUTO = 0,
   MLA_KERNEL_H64 = 1,

@@ -22,12 +22,14 @@ HIPFLAGS = [
 ]
 
 
-# Kernels whose matrix accumulators are named as fixed AGPRs in inline asm
-# (the compiler does not see them as values): the build fails unless the
-# compiler keeps its own registers out of the AGPR file, i.e. no spills, no
-# scratch, fewer than 256 VGPRs (a full VGPR file is where it would start
-# parking values in AGPRs), and all 256 AGPRs allocated.
-FIXED_AGPR_KERNELS = ("decode_h128_kernel",)
+# The two decode kernels of the automatic choice wait on their own tile loads
+# with hand-counted s_waitcnt vmcnt(N).  A register spill adds scratch loads
+# and stores to that counter: the counted waits stay correct (ops issued after
+# a tile's loads only make vmcnt(N) wait for more) but then stall on scratch
+# traffic inside the tile loop.  The build fails unless the compiler reports
+# no VGPR spill and no scratch for them.  (The 12-wave 128-head kernel, an
+# option of mla_decode_ex, has a few spills and is not checked.)
+COUNTED_WAIT_KERNELS = ("decode_ws_kernel", "decode_f8q_kernel")
 
 
 def resource_usage(remarks: str) -> dict:
@@ -44,16 +46,15 @@ def resource_usage(remarks: str) -> dict:
     return out
 
 
-def check_fixed_agpr_kernels(usage: dict) -> None:
-    found = [k for k in usage if any(f in k for f in FIXED_AGPR_KERNELS)]
-    if not found:
-        raise RuntimeError("no resource usage reported for the fixed-AGPR kernels")
-    for k in found:
-        u = usage[k]
-        ok = (u.get("VGPRs Spill") == "0" and u.get("ScratchSize [bytes/lane]") == "0"
-              and int(u.get("VGPRs", 256)) < 256 and u.get("AGPRs") == "256")
-        if not ok:
-            raise RuntimeError(f"{k}: the compiler's registers reach the fixed accumulators: {u}")
+def check_counted_wait_kernels(usage: dict) -> None:
+    for name in COUNTED_WAIT_KERNELS:
+        found = [k for k in usage if name in k]
+        if not found:
+            raise RuntimeError(f"no resource usage reported for {name}")
+        for k in found:
+            u = usage[k]
+            if u.get("VGPRs Spill") != "0" or u.get("ScratchSize [bytes/lane]") != "0":
+                raise RuntimeError(f"{k}: spills or scratch in a decode kernel with counted waits: {u}")
 
 
 def build(verbose: bool = False, extra: list | None = None) -> str:
@@ -67,7 +68,7 @@ def build(verbose: bool = False, extra: list | None = None) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise subprocess.CalledProcessError(r.returncode, cmd)
-    check_fixed_agpr_kernels(resource_usage(r.stderr))
+    check_counted_wait_kernels(resource_usage(r.stderr))
     os.replace(tmp, LIB)
     return LIB
 

@@ -612,91 +612,11 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   }
 }
 
-// ================================================================ decode (128 heads per workgroup)
+// ================================================================ decode: 128-head tile layout
 //
-// bf16 caches with a multiple of 128 heads: one workgroup per (sequence b,
-// split range p, 128 heads), so each cached tile enters one CU once for all
-// 128 heads.  4 waves, one per SIMD; wave w owns heads 32w..32w+31 for both
-// products:
-//   * QK: S[t][h] (32 tokens x 32 heads) = 36 v_mfma_f32_32x32x16_bf16 with
-//     the tile rows as A (LDS) and the wave's absorbed queries as B: the 512
-//     latent elements in 128 VGPRs held for the whole range, the 64 RoPE
-//     elements read from LDS;
-//   * the softmax (fixed reference maximum, base 2, as above) in registers:
-//     the accumulator layout of S -- lane = head, register r = token
-//     8(r/4) + 4(lane/32) + r%4 -- is exactly the B operand layout that the
-//     PV product needs with the transposing tile reads below, so the
-//     probabilities never leave the wave;
-//   * PV: U^T[c][h] (512 columns x 32 heads, all 256 AGPRs) += 32 MFMAs with
-//     the tile read by ds_read_b64_tr_b16 as A.
-// The QK product of tile i+1 is interleaved with the PV product of tile i,
-// which runs 10 steps behind, so that the softmax of tile i+1 fits between the
-// last PV MFMAs.  The waves meet once per tile, at the barrier that releases a
-// tile buffer to the DMA: 4 buffers, 3 tiles in flight.  LDS: 4 x 36 KB tiles
-// + 16 KB of RoPE queries = 160 KB.
-
-// The 16 accumulator blocks U^T[32cb..32cb+31][32 heads] (16 fp32 each) live in
-// fixed AGPRs a[16cb..16cb+15], named in the instructions below rather than
-// held as compiler values: with 128 query VGPRs also live, the register
-// allocator would otherwise keep the accumulators in VGPRs and copy them into
-// AGPRs around every MFMA.  The kernel's own code uses no AGPRs (its VGPR
-// demand stays below 256, checked in the ISA: no spills, no accvgpr moves).
-template <int CB> struct AccBlock;
-#define MLA_A16(n0, n1, n2, n3, n4, n5, n6, n7, n8, n9, n10, n11, n12, n13, n14, n15)           \
-  "a" #n0, "a" #n1, "a" #n2, "a" #n3, "a" #n4, "a" #n5, "a" #n6, "a" #n7, "a" #n8, "a" #n9,    \
-      "a" #n10, "a" #n11, "a" #n12, "a" #n13, "a" #n14, "a" #n15
-#define MLA_ACC_BLOCK(CB, LO, HI, n0, n1, n2, n3, n4, n5, n6, n7, n8, n9, n10, n11, n12, n13,  \
-                      n14, n15)                                                                 \
-  template <> struct AccBlock<CB> {                                                             \
-    /* a[LO:HI] = 0 (the product of zeros plus an inline zero) */                               \
-    __device__ static void zero(const bf16x8_t& z) {                                            \
-      asm volatile("v_mfma_f32_32x32x16_bf16 a[" #LO ":" #HI "], %0, %0, 0" ::"v"(z)           \
-                   : MLA_A16(n0, n1, n2, n3, n4, n5, n6, n7, n8, n9, n10, n11, n12, n13, n14,   \
-                             n15));                                                             \
-    }                                                                                           \
-    /* a[LO:HI] += A B */                                                                       \
-    __device__ static void mfma(const bf16x8_t& a, const bf16x8_t& b) {                         \
-      asm volatile("v_mfma_f32_32x32x16_bf16 a[" #LO ":" #HI "], %0, %1, a[" #LO ":" #HI "]"     \
-                   ::"v"(a), "v"(b)                                                             \
-                   : MLA_A16(n0, n1, n2, n3, n4, n5, n6, n7, n8, n9, n10, n11, n12, n13, n14,   \
-                             n15));                                                             \
-    }                                                                                           \
-    /* the block in VGPRs; read only after the caller's matrix-core drain */                    \
-    __device__ static f32x16_t read() {                                                         \
-      float r[16];                                                                              \
-      asm volatile("v_accvgpr_read_b32 %0, a" #n0 "\n\tv_accvgpr_read_b32 %1, a" #n1            \
-                   "\n\tv_accvgpr_read_b32 %2, a" #n2 "\n\tv_accvgpr_read_b32 %3, a" #n3        \
-                   "\n\tv_accvgpr_read_b32 %4, a" #n4 "\n\tv_accvgpr_read_b32 %5, a" #n5        \
-                   "\n\tv_accvgpr_read_b32 %6, a" #n6 "\n\tv_accvgpr_read_b32 %7, a" #n7        \
-                   "\n\tv_accvgpr_read_b32 %8, a" #n8 "\n\tv_accvgpr_read_b32 %9, a" #n9        \
-                   "\n\tv_accvgpr_read_b32 %10, a" #n10 "\n\tv_accvgpr_read_b32 %11, a" #n11   \
-                   "\n\tv_accvgpr_read_b32 %12, a" #n12 "\n\tv_accvgpr_read_b32 %13, a" #n13   \
-                   "\n\tv_accvgpr_read_b32 %14, a" #n14 "\n\tv_accvgpr_read_b32 %15, a" #n15   \
-                   : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]),    \
-                     "=v"(r[6]), "=v"(r[7]), "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]),  \
-                     "=v"(r[12]), "=v"(r[13]), "=v"(r[14]), "=v"(r[15]));                       \
-      return f32x16_t{r[0], r[1], r[2],  r[3],  r[4],  r[5],  r[6],  r[7],                     \
-                      r[8], r[9], r[10], r[11], r[12], r[13], r[14], r[15]};                    \
-    }                                                                                           \
-  };
-MLA_ACC_BLOCK(0, 0, 15, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15)
-MLA_ACC_BLOCK(1, 16, 31, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31)
-MLA_ACC_BLOCK(2, 32, 47, 32, 33, 34, 35, 36, 37, 38, 39, 40, 41, 42, 43, 44, 45, 46, 47)
-MLA_ACC_BLOCK(3, 48, 63, 48, 49, 50, 51, 52, 53, 54, 55, 56, 57, 58, 59, 60, 61, 62, 63)
-MLA_ACC_BLOCK(4, 64, 79, 64, 65, 66, 67, 68, 69, 70, 71, 72, 73, 74, 75, 76, 77, 78, 79)
-MLA_ACC_BLOCK(5, 80, 95, 80, 81, 82, 83, 84, 85, 86, 87, 88, 89, 90, 91, 92, 93, 94, 95)
-MLA_ACC_BLOCK(6, 96, 111, 96, 97, 98, 99, 100, 101, 102, 103, 104, 105, 106, 107, 108, 109, 110, 111)
-MLA_ACC_BLOCK(7, 112, 127, 112, 113, 114, 115, 116, 117, 118, 119, 120, 121, 122, 123, 124, 125, 126, 127)
-MLA_ACC_BLOCK(8, 128, 143, 128, 129, 130, 131, 132, 133, 134, 135, 136, 137, 138, 139, 140, 141, 142, 143)
-MLA_ACC_BLOCK(9, 144, 159, 144, 145, 146, 147, 148, 149, 150, 151, 152, 153, 154, 155, 156, 157, 158, 159)
-MLA_ACC_BLOCK(10, 160, 175, 160, 161, 162, 163, 164, 165, 166, 167, 168, 169, 170, 171, 172, 173, 174, 175)
-MLA_ACC_BLOCK(11, 176, 191, 176, 177, 178, 179, 180, 181, 182, 183, 184, 185, 186, 187, 188, 189, 190, 191)
-MLA_ACC_BLOCK(12, 192, 207, 192, 193, 194, 195, 196, 197, 198, 199, 200, 201, 202, 203, 204, 205, 206, 207)
-MLA_ACC_BLOCK(13, 208, 223, 208, 209, 210, 211, 212, 213, 214, 215, 216, 217, 218, 219, 220, 221, 222, 223)
-MLA_ACC_BLOCK(14, 224, 239, 224, 225, 226, 227, 228, 229, 230, 231, 232, 233, 234, 235, 236, 237, 238, 239)
-MLA_ACC_BLOCK(15, 240, 255, 240, 241, 242, 243, 244, 245, 246, 247, 248, 249, 250, 251, 252, 253, 254, 255)
-#undef MLA_ACC_BLOCK
-#undef MLA_A16
+// The 12-wave decode below (one workgroup per 128 heads) reads each tile with
+// 32x32x16 QK operands, which take 32 rows of one chunk; its tile layout and
+// DMA plan follow.
 
 // calls f(std::integral_constant<int, I>) for I = 0..N-1
 template <int N, int I = 0, class F>
@@ -730,388 +650,8 @@ __device__ inline RowsDma rows_dma_plan_h128(const uint8_t* base, uint32_t lds_t
   return d;
 }
 
-constexpr int kH128Threads = 256;
 constexpr int kH128 = 128;
-constexpr int kH128Steps = kRowElems / 16;    // 36 QK k-steps of 16
-constexpr int kH128LatSteps = kDLatent / 16;  // 32 of them over the latent
-constexpr int kQropeOff = kNBuf * kTileBytes;  // [128 heads][64] bf16, 128 B per head
-
-template <int PART_DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kH128Threads, kH128Threads),
-                          amdgpu_waves_per_eu(1, 1)))
-void decode_h128_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kQropeOff + kH128 * 128];
-
-  // work id -> (head group, query token j, split p, sequence b); the work of
-  // one sequence is adjacent (same XCD: its queries are shared through L2)
-  const int nwork = P.B * P.QL * P.S * P.HG;
-  const int wid = xcd_remap(blockIdx.x, nwork);
-  const int hg = wid % P.HG;
-  const int r1 = wid / P.HG;
-  const int qj = r1 % P.QL;
-  const int r2 = r1 / P.QL;
-  const int p = r2 % P.S;
-  const int b = r2 / P.S;
-  const int bj = b * P.QL + qj;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..3
-  const int hl = lane & 31, g = lane >> 5;
-  const int hw = hg * kH128 + wave * kHeadsPerWave;  // first head of this wave
-
-  const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
-                        (P.QL - 1 - qj), 0);
-  const int t_begin = p * P.chunk;
-  const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(bj) * P.S + p) * P.H + hw;
-
-  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf (no barrier is reached)
-    for (int idx = lane; idx < kHeadsPerWave * kDLatent; idx += 64)
-      store_elem<PART_DT>(P.u_part, row_base * kDLatent + idx, 0.0f);
-    if (lane < kHeadsPerWave) P.lse_part[row_base + lane] = -INFINITY;
-    return;
-  }
-  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  // inline-asm MFMA results are not tracked by the compiler's hazard checks:
-  // matrix-core writes -> VALU reads of the same registers
-  auto mfma_drain = [] { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
-
-  // DMA of tile k into buffer k % 4.  Every wave issues the same 9
-  // instructions per tile slot; a slot past the range reloads the last tile's
-  // rows into buffer k % 4, which no later tile of the range uses, so the
-  // wait counts below are the same in every iteration.
-  auto dma_plan = [&](int k) {
-    const int kc = min(k, ntiles - 1);
-    const int tt = t_begin + kc * kTileTokens;
-    const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
-    return rows_dma_plan_h128(P.rows + row0 * kRowBytes, lds_addr(smem) + (k & (kNBuf - 1)) * kTileBytes,
-                              min(kTileTokens, t_end - tt), wave);
-  };
-  auto dma = [&](int k) {
-    const RowsDma d = dma_plan(k);
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
-  };
-
-  // QK A operand: lane (token hl, half g) reads the 16-byte chunk 2ks + g of
-  // row hl, i.e. latent elements 16ks + 8g .. +7
-  const uint32_t qk_base = (hl >> 3) * kTokGroupBytes + ((hl & 7) ^ ((hl >> 3) & 1)) * 128;
-  const int qk_key = swzg(hl & 7);
-  auto ld_qk = [&](const uint8_t* T, int ks) {
-    return *reinterpret_cast<const bf16x8_t*>(T + qk_base + (ks >> 2) * 1024 +
-                                              (((2 * (ks & 3) + g) ^ qk_key) << 4));
-  };
-  // RoPE part of the QK B operand, from LDS, in the tile layout with heads for
-  // tokens: head h's 16-byte chunk c (elements 8c..8c+7 of q_R) sits at
-  // (h ^ (h / 8 % 2)) * 128 + (c ^ swzg(h % 8)) * 16
-  const int hq = wave * kHeadsPerWave + hl;  // head within the workgroup
-  const uint32_t qr_base = kQropeOff + (hq ^ ((hq >> 3) & 1)) * 128;
-  const int qr_key = swzg(hq & 7);
-  auto ld_qr = [&](int ks) {
-    const int c = 2 * (ks - kH128LatSteps) + g;
-    return *reinterpret_cast<const bf16x8_t*>(smem + qr_base + ((c ^ qr_key) << 4));
-  };
-  // PV A operand (columns 32cb..+31 x tokens 16j..+15), transposing reads
-  // (lo: tokens of the even group 2j, hi: the odd group 2j+1, row pairs swapped)
-  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
-  const int tr_row = 4 * (G >> 1) + e;
-  const int tr_key = swzg(tr_row);
-  const int tr_x = 2 * (G & 1) + (q4 >> 1);
-  const uint32_t tr_lo = tr_row * 128 + 8 * (q4 & 1);
-  const uint32_t tr_hi = kTokGroupBytes + (tr_row ^ 1) * 128 + 8 * (q4 & 1);
-  const uint32_t tr_off[2] = {static_cast<uint32_t>(((0 + tr_x) ^ tr_key) << 4),
-                              static_cast<uint32_t>(((4 + tr_x) ^ tr_key) << 4)};
-  auto ld_pv = [&](const uint8_t* T, int k) {  // PV step k: token half k / 16, column block k % 16
-    const int j = k >> 4, cb = k & 15;
-    const uint8_t* ptr = T + tr_off[cb & 1] + (cb >> 1) * 1024 + 2 * j * kTokGroupBytes;
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + tr_lo));
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + tr_hi));
-    return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-
-  // absorbed queries of the wave's heads: lane (head hl, half g) holds latent
-  // elements 16ks + 8g .. +7 of its head's row (the QK B operand); the RoPE
-  // elements go to LDS by DMA: 4 wave instructions of 8 head positions x 8
-  // slots (the layout of ld_qr below)
-  const uint8_t* qw = static_cast<const uint8_t*>(P.q_abs) + (static_cast<int64_t>(bj) * P.H + hw) * kRowBytes;
-  bf16x8_t q[kH128LatSteps];
-  dma(0);
-  {
-    const int hpos = lane >> 3, slot = lane & 7;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int hr = hpos ^ (k & 1);  // head 8k + hr of the wave sits at position 8k + hpos
-      const uint32_t off = static_cast<uint32_t>((8 * k + hr) * kRowBytes + 2 * kDLatent +
-                                                 ((slot ^ swzg(hr)) << 4));
-      const uint32_t m0 = lds_addr(smem + kQropeOff) + (wave * kHeadsPerWave + 8 * k) * 128;
-      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(qw), "{m0}"(m0) : "memory");
-    }
-  }
-  const uint8_t* qrow = qw + hl * kRowBytes + 16 * g;
-#pragma unroll
-  for (int ks = 0; ks < kH128LatSteps; ++ks) q[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * ks);
-  dma(1);
-  dma(2);
-
-  f32x16_t S;
-  bf16x8_t pb[2];  // probabilities of the tile whose PV runs next, token halves 0 and 1
-  const bf16x8_t zero8 = {};
-
-  auto qk_mfma = [&](int ks, const bf16x8_t& a, const bf16x8_t& qb) {
-    if (ks == 0)
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(S) : "v"(a), "v"(qb));
-    else
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "v"(qb));
-  };
-  auto pv_mfma = [&](auto K, const bf16x8_t& a) {  // PV step K: block K % 16, token half K / 16
-    AccBlock<decltype(K)::value & 15>::mfma(a, pb[decltype(K)::value >> 4]);
-  };
-  constexpr int kRing = 2;   // PV operand reads in flight
-  constexpr int kRingQ = 2;  // QK operand reads in flight
-  // QK of the tile in Tq alone (the first tile of a pass)
-  auto qk_only = [&](const uint8_t* Tq) {
-    bf16x8_t rq[kRingQ], rr[kRingQ];
-#pragma unroll
-    for (int k = 0; k < kRingQ; ++k) rq[k] = ld_qk(Tq, k);
-    static_for<kH128Steps>([&](auto ST) {
-      constexpr int st = decltype(ST)::value;
-      const bf16x8_t a = rq[st % kRingQ];
-      const bf16x8_t qb = st < kH128LatSteps ? q[st < kH128LatSteps ? st : 0] : rr[st % kRingQ];
-      if constexpr (st + kRingQ < kH128Steps) rq[st % kRingQ] = ld_qk(Tq, st + kRingQ);
-      if constexpr (st + kRingQ >= kH128LatSteps && st + kRingQ < kH128Steps)
-        rr[(st + kRingQ) % kRingQ] = ld_qr(st + kRingQ);
-      qk_mfma(st, a, qb);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  auto pv_only = [&](const uint8_t* Tp, const RowsDma& dp) {
-    bf16x8_t rp[kRing];
-#pragma unroll
-    for (int k = 0; k < kRing; ++k) rp[k] = ld_pv(Tp, k);
-    static_for<32>([&](auto ST) {
-      constexpr int st = decltype(ST)::value;
-      const bf16x8_t v = rp[st % kRing];
-      if constexpr (st + kRing < 32) rp[st % kRing] = ld_pv(Tp, st + kRing);
-      pv_mfma(ST, v);
-      if constexpr (st < kDmaPerWave) rows_dma_issue(dp, st);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-
-  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
-  // token of score register r in this lane, kept opaque so that the compiler
-  // does not hoist 16 comparisons per mask out of the loops
-  auto tok0 = [&] {
-    int t = 4 * g;
-    asm volatile("" : "+v"(t));
-    return t;
-  };
-  // scores of `tile` (in S) -> bf16 probabilities in pb, relative to m_ref
-  auto softmax = [&](int tile, int& overflow) {
-    const int nvalid = t_end - (t_begin + tile * kTileTokens);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] *= P.scale_log2;
-    if (nvalid < kTileTokens) {
-      const int t0 = tok0();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = (t0 + 8 * (r >> 2) + (r & 3) < nvalid) ? S[r] : -INFINITY;
-    }
-    float mx = S[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    m_seen = fmaxf(m_seen, mx);
-    overflow |= (mx > m_ref + kRefSlack);
-    uint32_t w[8];
-#pragma unroll
-    for (int r2 = 0; r2 < 8; ++r2) {
-      const float p0 = __builtin_amdgcn_exp2f(S[2 * r2] - m_ref);
-      const float p1 = __builtin_amdgcn_exp2f(S[2 * r2 + 1] - m_ref);
-      l_run += p0;
-      l_run += p1;
-      w[r2] = pack_bf16x2(p0, p1);
-    }
-    const u32x4_t w0{w[0], w[1], w[2], w[3]}, w1{w[4], w[5], w[6], w[7]};
-    __builtin_memcpy(&pb[0], &w0, 16);
-    __builtin_memcpy(&pb[1], &w1, 16);
-  };
-
-  // The softmax of the tile whose QK pass just ended, in steps that can sit
-  // between MFMAs: step 0 scales and masks the scores and takes their maximum,
-  // steps 1..4 turn 4 scores each into probabilities (2 packed words each).
-  auto softmax_step = [&](int c, int tile, int& overflow, uint32_t (&w)[8]) {
-    if (c == 0) {
-      const int nvalid = t_end - (t_begin + tile * kTileTokens);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] *= P.scale_log2;
-      if (nvalid < kTileTokens) {
-        const int t0 = tok0();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = (t0 + 8 * (r >> 2) + (r & 3) < nvalid) ? S[r] : -INFINITY;
-      }
-      float mx = S[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-      m_seen = fmaxf(m_seen, mx);
-      overflow |= (mx > m_ref + kRefSlack);
-      return;
-    }
-#pragma unroll
-    for (int r2 = 2 * (c - 1); r2 < 2 * c; ++r2) {
-      const float p0 = __builtin_amdgcn_exp2f(S[2 * r2] - m_ref);
-      const float p1 = __builtin_amdgcn_exp2f(S[2 * r2 + 1] - m_ref);
-      l_run += p0;
-      l_run += p1;
-      w[r2] = pack_bf16x2(p0, p1);
-    }
-  };
-  // QK of tile `tnext` (in Tq) with the PV of the tile in Tp running kLag
-  // steps behind it, so that the QK product ends first and the softmax of
-  // tnext runs between the last PV MFMAs; its probabilities go to pbn (pb is
-  // still being read).  The DMA of a later tile slot is issued one wave
-  // instruction per step.
-  constexpr int kLag = 10;
-  bf16x8_t pbn[2];
-  auto qk_pv_softmax = [&](const uint8_t* Tq, const uint8_t* Tp, const RowsDma& dp, int tnext,
-                           int& overflow) {
-    bf16x8_t rq[kRingQ], rp[kRing], rr[kRingQ];
-    uint32_t w[8];
-#pragma unroll
-    for (int k = 0; k < kRingQ; ++k) rq[k] = ld_qk(Tq, k);
-#pragma unroll
-    for (int k = 0; k < kRing; ++k) rp[k] = ld_pv(Tp, k);
-    static_for<32 + kLag>([&](auto SL) {
-      constexpr int st = decltype(SL)::value;
-      if constexpr (st < kH128Steps) {
-        const bf16x8_t a = rq[st % kRingQ];
-        const bf16x8_t qb = st < kH128LatSteps ? q[st < kH128LatSteps ? st : 0] : rr[st % kRingQ];
-        if constexpr (st + kRingQ < kH128Steps) rq[st % kRingQ] = ld_qk(Tq, st + kRingQ);
-        if constexpr (st + kRingQ >= kH128LatSteps && st + kRingQ < kH128Steps)
-          rr[(st + kRingQ) % kRingQ] = ld_qr(st + kRingQ);
-        qk_mfma(st, a, qb);
-      }
-      if constexpr (st >= kLag) {
-        constexpr int k = st - kLag;
-        const bf16x8_t v = rp[k % kRing];
-        if constexpr (k + kRing < 32) rp[k % kRing] = ld_pv(Tp, k + kRing);
-        pv_mfma(std::integral_constant<int, k>{}, v);
-      }
-      if constexpr (st < kDmaPerWave) rows_dma_issue(dp, st);
-      if constexpr (st == kH128Steps) {
-        // the last QK MFMA's scores -> VALU reads
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-        softmax_step(0, tnext, overflow, w);
-      }
-      if constexpr (st > kH128Steps && st <= kH128Steps + 4) softmax_step(st - kH128Steps, tnext, overflow, w);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    const u32x4_t w0{w[0], w[1], w[2], w[3]}, w1{w[4], w[5], w[6], w[7]};
-    __builtin_memcpy(&pbn[0], &w0, 16);
-    __builtin_memcpy(&pbn[1], &w1, 16);
-  };
-
-  for (int pass = 0; pass < 2; ++pass) {
-    static_for<16>([&](auto CB) { AccBlock<decltype(CB)::value>::zero(zero8); });
-    if (pass > 0) {
-      dma(0);
-      dma(1);
-      dma(2);
-    }
-    // tile 0 (and on the first pass the RoPE queries and the latent queries,
-    // issued before tiles 1 and 2) landed
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    barrier();
-    qk_only(smem);
-    mfma_drain();
-    if (pass == 0) {  // reference: maximum of the first tile, both lane halves
-      const int nvalid = t_end - t_begin;
-      const int t0 = tok0();
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (t0 + 8 * (r >> 2) + (r & 3) < nvalid) mx = fmaxf(mx, S[r] * P.scale_log2);
-      m_ref = fmaxf(mx, __shfl_xor(mx, 32));
-    }
-    l_run = 0.0f;
-    int overflow = 0;
-    softmax(0, overflow);
-    for (int i = 0; i < ntiles; ++i) {
-      asm volatile("s_nop 4" ::: "memory");  // VALU writes of pb -> MFMA reads
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      barrier();  // tile i+1 landed; tile i-1's buffer released
-      const RowsDma dp = dma_plan(i + 3);
-      const uint8_t* Tp = smem + (i & (kNBuf - 1)) * kTileBytes;
-      if (i + 1 < ntiles) {
-        qk_pv_softmax(smem + ((i + 1) & (kNBuf - 1)) * kTileBytes, Tp, dp, i + 1, overflow);
-        mfma_drain();  // the PV MFMAs still reading pb -> its replacement
-        pb[0] = pbn[0];
-        pb[1] = pbn[1];
-      } else {
-        pv_only(Tp, dp);
-      }
-    }
-    // the slots issued past the range are still in flight
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    barrier();  // every wave is done with the tile buffers
-    int* votes = reinterpret_cast<int*>(smem);
-    const int vote = __any(overflow) ? 1 : 0;  // all lanes, outside the store's branch
-    if (lane == 0) votes[wave] = vote;
-    barrier();
-    int again = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) again |= votes[w];
-    barrier();  // votes read
-    if (!again) break;
-    m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // redo with the range maximum
-  }
-
-  // l and lse per head: the two lane halves
-  l_run += __shfl_xor(l_run, 32);
-  if (g == 0) P.lse_part[row_base + hl] = (m_ref + log2f(l_run)) * kLn2;
-  const float inv = 1.0f / l_run;
-  mfma_drain();  // the last PV MFMAs -> accumulator reads
-  // U^T register r of block cb in lane (hl, g): column 32cb + 8(r/4) + 4g + r%4
-  // of head hw + hl.  Each wave stages its 32 rows in its own LDS region (the
-  // tile buffers are free after the last barrier) and writes whole rows.
-  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
-  constexpr int kColsRound = 1024 / kEsz;  // 512 bf16 / 256 fp32 columns: 1 KB per row
-  constexpr int kBlocksRound = kColsRound / 32;
-  constexpr int kStageRow = 1024 + 16;     // padded: rows start 4 banks apart
-  uint8_t* W = smem + wave * kHeadsPerWave * kStageRow;
-  static_for<kDLatent / kColsRound>([&](auto HALF) {
-    constexpr int half = decltype(HALF)::value;
-    static_for<kBlocksRound / 4>([&](auto QB) {  // 4 blocks at a time
-      constexpr int cb0 = half * kBlocksRound + 4 * decltype(QB)::value;
-      f32x16_t A[4];
-      A[0] = AccBlock<cb0 + 0>::read();
-      A[1] = AccBlock<cb0 + 1>::read();
-      A[2] = AccBlock<cb0 + 2>::read();
-      A[3] = AccBlock<cb0 + 3>::read();
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int c = 32 * (cb0 - half * kBlocksRound + k) + 8 * r4 + 4 * g;
-          const float v0 = A[k][4 * r4 + 0] * inv, v1 = A[k][4 * r4 + 1] * inv;
-          const float v2 = A[k][4 * r4 + 2] * inv, v3 = A[k][4 * r4 + 3] * inv;
-          uint8_t* wp = W + hl * kStageRow + c * kEsz;
-          if constexpr (PART_DT == MLA_F32)
-            *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
-          else
-            *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        }
-      }
-    });
-    // one wave's LDS operations complete in order: no barrier is needed
-    asm volatile("" ::: "memory");
-    uint8_t* dst = static_cast<uint8_t*>(P.u_part) + (row_base * kDLatent + half * kColsRound) * kEsz;
-#pragma unroll 8
-    for (int row = 0; row < kHeadsPerWave; ++row) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + lane * 16);
-      *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) + lane * 16) = v;
-    }
-    asm volatile("" ::: "memory");
-  });
-}
+constexpr int kH128Steps = kRowElems / 16;  // 36 QK k-steps of 16
 
 // ================================================================ decode (128 heads, warp-specialised)
 //
@@ -2899,7 +2439,9 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   const bool h128_ok = !fp8 && H % kH128 == 0;
   const int64_t nblk = static_cast<int64_t>(B) * q_len * num_splits * (H / kH128);
   if ((kernel == MLA_KERNEL_H128 || kernel == MLA_KERNEL_H128_WS) && !h128_ok) return MLA_E_UNSUPPORTED;
-  if (kernel == MLA_KERNEL_H128_WS) {  // bf16 cache: 12-wave workgroups of 128 heads
+  // bf16 cache: 12-wave workgroups of 128 heads (MLA_KERNEL_H128 names the same
+  // decomposition)
+  if (kernel == MLA_KERNEL_H128_WS || kernel == MLA_KERNEL_H128) {
     P.HG = H / kH128;
     if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
     if (part_dt == MLA_F32)
@@ -2911,15 +2453,6 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   // automatic choice: the 64-head kernel, measured as fast or faster than the
   // 128-head one on every bf16 workload and split count tried
   if (kernel == MLA_KERNEL_AUTO) kernel = MLA_KERNEL_H64;
-  if (kernel == MLA_KERNEL_H128) {  // bf16 cache: one workgroup per 128 heads
-    P.HG = H / kH128;
-    if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
-    if (part_dt == MLA_F32)
-      decode_h128_kernel<MLA_F32><<<static_cast<unsigned>(nblk), kH128Threads, 0, s>>>(P, cache->block_table);
-    else
-      decode_h128_kernel<MLA_BF16><<<static_cast<unsigned>(nblk), kH128Threads, 0, s>>>(P, cache->block_table);
-    return launch_status();
-  }
   if (fp8 && part_dt == MLA_F32)
     decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
   else if (fp8)

@@ -1,6 +1,8 @@
-"""The build's guard for the kernel whose accumulators are fixed AGPRs named in
-inline asm: it reads the compiler's resource-usage remarks and rejects a
-build in which the compiler's own registers could reach those AGPRs."""
+"""The build's guard for the decode kernels of the automatic choice, whose
+waits on their own tile loads are counted by hand: it reads the compiler's
+resource-usage remarks and rejects a build in which one of them spills
+registers or uses scratch (scratch traffic inside the tile loop would stall
+those waits)."""
 
 import importlib
 
@@ -8,29 +10,38 @@ import pytest
 
 build = importlib.import_module("mla_latent_kv_15_amd.build")
 
-K = "_ZN3mla12_GLOBAL__N_118decode_h128_kernelILi1EEEvNS0_12DecodeParamsEPKi"
+NAMES = {
+    "decode_ws_kernel": "_ZN3mla12_GLOBAL__N_116decode_ws_kernelILb0ELi1EEEvNS_12DecodeParamsEPKi",
+    "decode_f8q_kernel": "_ZN3mla12_GLOBAL__N_117decode_f8q_kernelILi1EEEvNS_12DecodeParamsEPKii",
+}
 
 
-def remarks(vgprs=221, agprs=256, spill=0, scratch=0):
-    r = "mla_kernels.hip:917:1: remark: {} [-Rpass-analysis=kernel-resource-usage]\n"
-    return "".join(r.format(x) for x in (
-        f"Function Name: {K}", "    TotalSGPRs: 102", f"    VGPRs: {vgprs}", f"    AGPRs: {agprs}",
-        f"    ScratchSize [bytes/lane]: {scratch}", "    Occupancy [waves/SIMD]: 1",
-        f"    VGPRs Spill: {spill}", "    LDS Size [bytes/block]: 163840"))
+def remarks(spill=0, scratch=0, skip=None):
+    r = "mla_kernels.hip:100:1: remark: {} [-Rpass-analysis=kernel-resource-usage]\n"
+    out = []
+    for short, k in NAMES.items():
+        if short == skip:
+            continue
+        out += [f"Function Name: {k}", "    TotalSGPRs: 102", "    VGPRs: 128", "    AGPRs: 128",
+                f"    ScratchSize [bytes/lane]: {scratch}", "    Occupancy [waves/SIMD]: 2",
+                f"    VGPRs Spill: {spill}", "    LDS Size [bytes/block]: 157184"]
+    return "".join(r.format(x) for x in out)
 
 
 def test_parses_the_remarks():
     u = build.resource_usage(remarks())
-    assert u[K]["VGPRs"] == "221" and u[K]["AGPRs"] == "256" and u[K]["VGPRs Spill"] == "0"
-    build.check_fixed_agpr_kernels(u)
+    k = NAMES["decode_f8q_kernel"]
+    assert u[k]["VGPRs"] == "128" and u[k]["AGPRs"] == "128" and u[k]["VGPRs Spill"] == "0"
+    build.check_counted_wait_kernels(u)
 
 
-@pytest.mark.parametrize("kw", [dict(spill=4), dict(scratch=16), dict(vgprs=256), dict(agprs=128)])
-def test_rejects_a_build_that_reaches_the_fixed_agprs(kw):
+@pytest.mark.parametrize("kw", [dict(spill=4), dict(scratch=16)])
+def test_rejects_a_build_with_spills(kw):
     with pytest.raises(RuntimeError):
-        build.check_fixed_agpr_kernels(build.resource_usage(remarks(**kw)))
+        build.check_counted_wait_kernels(build.resource_usage(remarks(**kw)))
 
 
-def test_rejects_missing_remarks():
+@pytest.mark.parametrize("skip", sorted(NAMES))
+def test_rejects_missing_remarks(skip):
     with pytest.raises(RuntimeError):
-        build.check_fixed_agpr_kernels(build.resource_usage(""))
+        build.check_counted_wait_kernels(build.resource_usage(remarks(skip=skip)))
