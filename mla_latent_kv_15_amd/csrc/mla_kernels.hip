@@ -76,25 +76,28 @@ struct Fp8Rows {
 template <bool FP8, int PART_DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads),
                           amdgpu_waves_per_eu(2, 2)))
-void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
+void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, int R_arg) {
+  const int R = FP8 ? 1 : R_arg;  // the fp8 cache runs one range per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kX64Off + (FP8 ? 1536 : 1024)];
   uint8_t* pbuf = smem + kNBuf * kTileBytes;
   float* xch = reinterpret_cast<float*>(smem + kX64Off);  // [2][64] per-head exchange
   int* votes = reinterpret_cast<int*>(smem + kX64Off + 512);
-  float* linv = reinterpret_cast<float*>(smem);  // epilogue: 1 / l per head (tile buffer 0)
+  float* linv = reinterpret_cast<float*>(smem + kX64Off + 768);  // epilogue: 1 / l per head
   float* tscale = reinterpret_cast<float*>(smem + kX64Off + 1024);  // fp8: [kNBuf][32] row scales
 
-  // work id -> (head group, query token j, split p, sequence b), the head
-  // groups and query tokens of one split range adjacent (same XCD, so they
-  // share each tile through L2)
-  const int nwork = P.B * P.QL * P.S * P.HG;
+  // work id -> (head group, query token j, group of R consecutive split
+  // ranges, sequence b), the head groups and query tokens of one range group
+  // adjacent (same XCD, so they share each tile through L2).  R = 1 for the
+  // fp8 cache.
+  const int NG = (P.S + R - 1) / R;
+  const int nwork = P.B * P.QL * NG * P.HG;
   const int wid = xcd_remap(blockIdx.x, nwork);
   const int hg = wid % P.HG;
   const int r1 = wid / P.HG;
   const int qj = r1 % P.QL;
   const int r2 = r1 / P.QL;
-  const int p = r2 % P.S;
-  const int b = r2 / P.S;
+  const int grp = r2 % NG;
+  const int b = r2 / NG;
   const int bj = b * P.QL + qj;  // row of (b, qj) in q_abs, u_part and lse_part
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,27 +111,42 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   // rows up to and including its own: the first L - (QL - 1 - qj)
   const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
                         (P.QL - 1 - qj), 0);
-  const int t_begin = p * P.chunk;
-  const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase;
-
-  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf
-    if (!is_qk) {
-      const int pt = tid - 256;
-      for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
-        store_elem<PART_DT>(P.u_part, row_base * kDLatent + idx, 0.0f);
-      if (pt < nhb * kHeadsPerWave) P.lse_part[row_base + pt] = -INFINITY;
-    }
+  // the workgroup's ranges p_first .. p_end - 1 cover tokens [T0, T1): K
+  // consecutive 32-token tiles (every range is a whole number ntf of tiles),
+  // one pipeline through all of them; ranges from p_live on hold no token
+  const int p_first = grp * R, p_end = min(p_first + R, P.S);
+  const int T0 = p_first * P.chunk;
+  const int T1 = min(p_end * P.chunk, L);
+  const int K = T1 > T0 ? (T1 - T0 + kTileTokens - 1) / kTileTokens : 0;
+  const int ntf = P.chunk / kTileTokens;
+  const int p_live = K > 0 ? (FP8 ? p_first + 1 : p_first + (K - 1) / ntf + 1) : p_first;
+  auto row_base_of = [&](int p) { return (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase; };
+  auto write_empty = [&](int p) {  // a range without tokens: u = 0, lse = -inf (PV waves)
+    const int64_t rb = row_base_of(p);
+    const int pt = tid - 256;
+    for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
+      store_elem<PART_DT>(P.u_part, rb * kDLatent + idx, 0.0f);
+    if (pt < nhb * kHeadsPerWave) P.lse_part[rb + pt] = -INFINITY;
+  };
+  if (K == 0) {
+    if (!is_qk)
+      for (int p = p_first; p < p_end; ++p) write_empty(p);
     return;
   }
-  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-  // fp8: the PV loop runs in pairs of tiles (one register set each), so an odd
-  // range gets one more tile: it is loaded from the range's first rows and all
-  // of its tokens are masked, which adds exact zeros
-  const int ntp = FP8 ? ((ntiles + 1) & ~1) : ntiles;
+  // fp8 (one range): the PV loop runs in pairs of tiles (one register set
+  // each), so an odd range gets one more tile: it is loaded from the range's
+  // first rows and all of its tokens are masked, which adds exact zeros
+  const int ntp = FP8 ? ((K + 1) & ~1) : K;
+  // tiles k0 .. k1 - 1 of the workgroup belong to range p
+  auto range_tiles = [&](int p, int& k0, int& k1) {
+    k0 = (p - p_first) * ntf;
+    k1 = FP8 ? ntp : min(k0 + ntf, K);
+  };
 
   // all s_barriers below are issued by both roles in the same order:
-  //   Q1 Q2 | per pass: T0 [AM AM] B_0..B_{n-1} V1 V2 [AM AM] | E1 E2
+  //   Q1 Q2 T0 | per range: [pass 0: AM AM] B_k0..B_k1-1 V1 V2
+  //   [redo: AM AM T0 B_k0..B_k1-1 V1 V2] E1 E2
+  // E2 of a range also certifies that the next range's first tile landed.
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   if (is_qk) {
@@ -145,8 +163,9 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.0f, 0.0f};
     // B operands: k-steps < kQkAgpr in AGPRs (the PV role's accumulators use
-    // the same 128 AGPRs), the rest in VGPRs
-    constexpr int kQkAgpr = 14;
+    // the same 128 AGPRs), the rest in VGPRs; the fp8 cache's row scales take
+    // VGPRs, so that variant moves two more k-steps to AGPRs
+    constexpr int kQkAgpr = FP8 ? 16 : 14;
     bf16x8_t qa[kQkAgpr][2];
     bf16x8_t qv[kQkSteps - kQkAgpr][2];
 
@@ -202,9 +221,8 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
         for (int r = 0; r < 4; ++r) s[hh][r] *= sc[r];
       return sc;
     };
-    auto softmax_publish = [&](f32x4_t (&s)[2], const f32x4_t& sc, int tile, int& overflow,
+    auto softmax_publish = [&](f32x4_t (&s)[2], const f32x4_t& sc, int nvalid, int& overflow,
                                uint8_t* PB) {
-      const int nvalid = t_end - (t_begin + tile * kTileTokens);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -261,75 +279,84 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
       barrier();  // AM
     };
 
-    for (int pass = 0; pass < 2; ++pass) {
-      l_run[0] = l_run[1] = 0.0f;
-      int overflow = 0;
-      barrier();  // T0: tile 0 landed
-      f32x4_t s[2];
-      f32x4_t sc = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (active) {
-        qk_tile(smem, s);
-        if constexpr (FP8) sc = row_scale(s, 0);
-      }
-      if (pass == 0) {  // reference: maximum of the first tile
-        float mx[2] = {-INFINITY, -INFINITY};
+    barrier();  // T0: the first tile landed
+    for (int p = p_first; p < p_live; ++p) {
+      int k0, k1;
+      range_tiles(p, k0, k1);
+      const int te = min((p + 1) * P.chunk, L);  // the range's end
+      auto nvalid = [&](int k) { return te - (T0 + k * kTileTokens); };
+      m_ref[0] = m_ref[1] = m_seen[0] = m_seen[1] = -INFINITY;
+      for (int pass = 0; pass < 2; ++pass) {
+        l_run[0] = l_run[1] = 0.0f;
+        int overflow = 0;
+        if (pass > 0) barrier();  // T0: the range's first tiles loaded again
+        f32x4_t s[2];
+        f32x4_t sc = {1.0f, 1.0f, 1.0f, 1.0f};
+        const int buf0 = k0 & (kNBuf - 1);
         if (active) {
-          const int nvalid = t_end - t_begin;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (16 * th + 4 * kg + r < nvalid) mx[hh] = fmaxf(mx[hh], s[hh][r] * P.scale_log2);
+          qk_tile(smem + buf0 * kTileBytes, s);
+          if constexpr (FP8) sc = row_scale(s, buf0);
         }
-        agree_max(mx);
-        m_ref[0] = mx[0];
-        m_ref[1] = mx[1];
-      }
-      if (active) softmax_publish(s, sc, 0, overflow, pbuf);
-      for (int i = 0; i < ntp; ++i) {
-        barrier();  // B_i: P(i) published, tile i+1 landed
-        if (active && i + 1 < ntp) {
-          const int buf = (i + 1) & (kNBuf - 1);
-          qk_tile(smem + buf * kTileBytes, s);
-          if constexpr (FP8) sc = row_scale(s, buf);
-          softmax_publish(s, sc, i + 1, overflow, pbuf + ((i + 1) & 1) * kP64Bytes);
+        if (pass == 0) {  // reference: maximum of the range's first tile
+          float mx[2] = {-INFINITY, -INFINITY};
+          if (active) {
+            const int nv = nvalid(k0);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (16 * th + 4 * kg + r < nv) mx[hh] = fmaxf(mx[hh], s[hh][r] * P.scale_log2);
+          }
+          agree_max(mx);
+          m_ref[0] = mx[0];
+          m_ref[1] = mx[1];
         }
+        if (active) softmax_publish(s, sc, nvalid(k0), overflow, pbuf + (k0 & 1) * kP64Bytes);
+        for (int k = k0; k < k1; ++k) {
+          barrier();  // B_k: P(k) published, tile k+1 landed
+          if (active && k + 1 < k1) {
+            const int buf = (k + 1) & (kNBuf - 1);
+            qk_tile(smem + buf * kTileBytes, s);
+            if constexpr (FP8) sc = row_scale(s, buf);
+            softmax_publish(s, sc, nvalid(k + 1), overflow, pbuf + ((k + 1) & 1) * kP64Bytes);
+          }
+        }
+        // the vote over all lanes, taken before the branch that stores it
+        // (inside `lane == 0` it would see lane 0's flag only)
+        const int vote = __any(overflow) ? 1 : 0;
+        if (lane == 0) votes[wave] = vote;
+        barrier();  // V1
+        int again = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) again |= votes[w];
+        barrier();  // V2
+        if (!again) break;
+        agree_max(m_seen);  // redo the range with the range maximum as reference
+        m_ref[0] = m_seen[0];
+        m_ref[1] = m_seen[1];
       }
-      // the vote over all lanes, taken before the branch that stores it
-      // (inside `lane == 0` it would see lane 0's flag only)
-      const int vote = __any(overflow) ? 1 : 0;
-      if (lane == 0) votes[wave] = vote;
-      barrier();  // V1
-      int again = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) again |= votes[w];
-      barrier();  // V2
-      if (!again) break;
-      agree_max(m_seen);  // redo the range with the range maximum as reference
-      m_ref[0] = m_seen[0];
-      m_ref[1] = m_seen[1];
-    }
-    // l per head: lane groups, then the two token halves
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      l_run[hh] += __shfl_xor(l_run[hh], 16);
-      l_run[hh] += __shfl_xor(l_run[hh], 32);
-    }
-    if (active && kg == 0) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) xch[th * 64 + qhb * 32 + 16 * hh + n16] = l_run[hh];
-    }
-    barrier();  // E1
-    if (active && th == 0 && kg == 0) {
+      // l per head: lane groups, then the two token halves
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int hx = qhb * 32 + 16 * hh + n16;
-        const float l_tot = xch[hx] + xch[64 + hx];
-        linv[hx] = 1.0f / l_tot;
-        P.lse_part[row_base + hx] = (m_ref[hh] + log2f(l_tot)) * kLn2;
+        l_run[hh] += __shfl_xor(l_run[hh], 16);
+        l_run[hh] += __shfl_xor(l_run[hh], 32);
       }
+      if (active && kg == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) xch[th * 64 + qhb * 32 + 16 * hh + n16] = l_run[hh];
+      }
+      barrier();  // E1
+      if (active && th == 0 && kg == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int hx = qhb * 32 + 16 * hh + n16;
+          const float l_tot = xch[hx] + xch[64 + hx];
+          linv[hx] = 1.0f / l_tot;
+          P.lse_part[row_base_of(p) + hx] = (m_ref[hh] + log2f(l_tot)) * kLn2;
+        }
+      }
+      barrier();  // E2
     }
-    barrier();  // E2
     return;
   }
 
@@ -391,6 +418,68 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     }
   };
 
+  // the partial of one range: U^T / l, staged per wave (32 rows x 128
+  // columns) in `stage` (a tile buffer no DMA is writing) and written as 256
+  // contiguous bytes per row at rows rb + head
+  auto write_partial = [&](int64_t rb, uint8_t* stage) {
+    // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    // U^T register r of block (hb, cbl) in lane (hl, g) is column
+    // 128*rw + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
+    // wave stages one head block (32 rows x 128 columns) at a time in its own
+    // region of `stage` and writes 256 contiguous bytes per row.
+    constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
+    constexpr int kColsRound = 256 / kEsz;             // 128 bf16 / 64 fp32 columns
+    constexpr int kStageRow = kColsRound * kEsz + 16;  // padded: rows start 4 banks apart
+    // bf16: the lane index recomputed here (volatile), so that the epilogue's
+    // addresses are formed in place rather than held across the range loop
+    int eln = lane;
+    if constexpr (!FP8)
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(eln));
+    const int hl = eln & 31, g = eln >> 5;
+    uint8_t* W = stage + rw * kHeadsPerWave * kStageRow;
+#pragma unroll
+    for (int hb = 0; hb < kH64Blocks; ++hb) {
+      if (hb < nhb) {
+        const float inv = linv[hb * kHeadsPerWave + hl];
+#pragma unroll
+        for (int half = 0; half < 128 / kColsRound; ++half) {
+#pragma unroll
+          for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
+            const int cbl = half * (kColsRound / 32) + cbl2;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int c = 32 * cbl2 + 8 * r4 + 4 * g;
+              const f32x16_t& A = acc[4 * hb + cbl];
+              const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
+              const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
+              uint8_t* wp = W + hl * kStageRow + c * kEsz;
+              if constexpr (PART_DT == MLA_F32) {
+                *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
+              } else {
+                *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+              }
+            }
+          }
+          // one wave's LDS operations complete in order: no barrier is needed
+          asm volatile("" ::: "memory");
+          // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
+          uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
+                         ((rb + hb * kHeadsPerWave) * kDLatent + 128 * rw) * kEsz +
+                         half * (kColsRound * kEsz);
+#pragma unroll
+          for (int i = 0; i < kHeadsPerWave / 4; ++i) {
+            const int row = 4 * i + (eln >> 4);
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (eln & 15) * 16);
+            *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
+                                        (eln & 15) * 16) = v;
+          }
+          asm volatile("" ::: "memory");
+        }
+      }
+    }
+  };
+
   // the queries of both head blocks (32 rows each) go into tile buffers 2 and 3
   const uint8_t* qsrc = static_cast<const uint8_t*>(P.q_abs) +
                         (static_cast<int64_t>(bj) * P.H + hbase) * kRowBytes;
@@ -401,72 +490,95 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   };
 
   if constexpr (!FP8) {
-    auto dma_plan = [&](int tile) {
-      const int tt = t_begin + tile * kTileTokens;
+    // tile k of the workgroup: tokens T0 + 32 k .., all attended (T1 <= L)
+    auto dma_plan = [&](int k) {
+      const int tt = T0 + k * kTileTokens;
       const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
-      return rows_dma_plan(P.rows + row0 * kRowBytes, lds_addr(smem) + (tile & (kNBuf - 1)) * kTileBytes,
-                           min(kTileTokens, t_end - tt), rw);
+      return rows_dma_plan(P.rows + row0 * kRowBytes, lds_addr(smem) + (k & (kNBuf - 1)) * kTileBytes,
+                           min(kTileTokens, T1 - tt), rw);
     };
-    auto dma = [&](int tile) {
-      const RowsDma d = dma_plan(tile);
+    auto dma = [&](int k) {
+      const RowsDma d = dma_plan(k);
 #pragma unroll
       for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
     };
+    // wait until tile k has landed, when tiles up to min(k + 2, K - 1) were
+    // issued (and nothing after them)
+    auto wait_tile = [&](int k) {
+      const int later = min(K - 1, k + 2) - k;
+      if (later >= 2)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
 
-    // queries, then tiles 0 and 1
+    // queries, then tiles 0 and 1 (tile 2 once the staging buffers are free)
     stage_q();
     dma(0);
-    if (ntiles > 1) dma(1);
-    if (ntiles > 1)
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    if (K > 1) dma(1);
+    if (K > 1)
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // the queries landed
     else
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     barrier();  // Q1
     barrier();  // Q2
+    if (K > 2) dma(2);
+    wait_tile(0);
+    barrier();  // T0
 
-    for (int pass = 0; pass < 2; ++pass) {
-      zero_acc();
-      if (pass > 0) {
-        dma(0);
-        if (ntiles > 1) dma(1);
-      }
-      if (ntiles > 2) dma(2);
-      if (ntiles > 2)
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-      else if (ntiles > 1)
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      barrier();  // T0
-      if (pass == 0) {
-        barrier();  // AM
-        barrier();  // AM
-      }
-      for (int i = 0; i < ntiles; ++i) {
-        if (i + 2 < ntiles)
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else
+    for (int p = p_first; p < p_live; ++p) {
+      int k0, k1;
+      range_tiles(p, k0, k1);
+      for (int pass = 0; pass < 2; ++pass) {
+        zero_acc();
+        if (pass > 0) {  // the range again: its first tiles back into the buffers
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        barrier();  // B_i
-        // tile i+3 into tile i-1's buffer, one wave instruction per MFMA
-        const bool dnext = i + 3 < ntiles;  // workgroup-uniform
-        RowsDma dp{};
-        if (dnext) dp = dma_plan(i + 3);
-        pv_tile(i, [&](int st) {
-          if (dnext && st < kDmaPerWave) rows_dma_issue(dp, st);
-        });
-      }
-      if (lane == 0) votes[wave] = 0;
-      barrier();  // V1
-      int again = 0;
+          dma(k0);
+          if (k0 + 1 < K) dma(k0 + 1);
+          if (k0 + 2 < K) dma(k0 + 2);
+          wait_tile(k0);
+          barrier();  // T0
+        } else {
+          barrier();  // AM
+          barrier();  // AM
+        }
+        for (int k = k0; k < k1; ++k) {
+          // tiles up to min(k + 2, K - 1) are issued: tile k + 1 lands
+          if (k + 2 < K)
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          barrier();  // B_k
+          // tile k+3 into tile k-1's buffer, one wave instruction per MFMA
+          const bool dnext = k + 3 < K;  // workgroup-uniform
+          RowsDma dp{};
+          if (dnext) dp = dma_plan(k + 3);
+          pv_tile(k, [&](int st) {
+            if (dnext && st < kDmaPerWave) rows_dma_issue(dp, st);
+          });
+        }
+        if (lane == 0) votes[wave] = 0;
+        barrier();  // V1
+        int again = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) again |= votes[w];
-      barrier();  // V2
-      if (!again) break;
-      barrier();  // AM
-      barrier();  // AM
+        for (int w = 0; w < 4; ++w) again |= votes[w];
+        barrier();  // V2
+        if (!again) break;
+        barrier();  // AM
+        barrier();  // AM
+      }
+      if (k1 < K) wait_tile(k1);  // E2 certifies the next range's first tile
+      barrier();  // E1
+      barrier();  // E2: linv ready
+      // the range's last tile buffer is free until tile k1 + 3 is loaded
+      write_partial(row_base_of(p), smem + ((k1 - 1) & (kNBuf - 1)) * kTileBytes);
     }
+    for (int p = p_live; p < p_end; ++p) write_empty(p);
   } else {
+    // one range per workgroup (R = 1)
+    const int t_begin = T0, t_end = T1, ntiles = K;
     // fp8 rows travel through registers: tile k is loaded two tiles ahead of
     // its conversion, into register set k % 2, and widened to bf16 on its way
     // into the same token-group layout as the bf16 path
@@ -555,60 +667,9 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
       barrier();  // AM
       barrier();  // AM
     }
-  }
-
-  barrier();  // E1
-  barrier();  // E2: linv ready
-  // matrix-core accumulator writes -> VALU reads (the MFMAs are inline asm)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-  // U^T register r of block (hb, cbl) in lane (hl, g) is column
-  // 128*rw + 32*cbl + 8*(r/4) + 4*g + r%4 of head hbase + 32*hb + hl.  Each
-  // wave stages one head block (32 rows x 128 columns) at a time in its own
-  // LDS region (tile buffers 0-1, past linv) and writes 256 contiguous bytes
-  // per row.
-  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
-  constexpr int kColsRound = 256 / kEsz;             // 128 bf16 / 64 fp32 columns
-  constexpr int kStageRow = kColsRound * kEsz + 16;  // padded: rows start 4 banks apart
-  uint8_t* W = smem + 1024 + rw * kHeadsPerWave * kStageRow;
-#pragma unroll
-  for (int hb = 0; hb < kH64Blocks; ++hb) {
-    if (hb < nhb) {
-      const float inv = linv[hb * kHeadsPerWave + hl];
-#pragma unroll
-      for (int half = 0; half < 128 / kColsRound; ++half) {
-#pragma unroll
-        for (int cbl2 = 0; cbl2 < kColsRound / 32; ++cbl2) {
-          const int cbl = half * (kColsRound / 32) + cbl2;
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int c = 32 * cbl2 + 8 * r4 + 4 * g;
-            const f32x16_t& A = acc[4 * hb + cbl];
-            const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
-            const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
-            uint8_t* wp = W + hl * kStageRow + c * kEsz;
-            if constexpr (PART_DT == MLA_F32) {
-              *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
-            } else {
-              *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            }
-          }
-        }
-        // one wave's LDS operations complete in order: no barrier is needed
-        asm volatile("" ::: "memory");
-        // 32 rows x 256 bytes: 4 rows per wave instruction, 16 bytes per lane
-        uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
-                       ((row_base + hb * kHeadsPerWave) * kDLatent + 128 * rw) * kEsz +
-                       half * (kColsRound * kEsz);
-#pragma unroll
-        for (int i = 0; i < kHeadsPerWave / 4; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
-          *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) +
-                                      (lane & 15) * 16) = v;
-        }
-        asm volatile("" ::: "memory");
-      }
-    }
+    barrier();  // E1
+    barrier();  // E2: linv ready
+    write_partial(row_base_of(p_first), smem);  // no tile is in flight in LDS
   }
 }
 
@@ -2453,14 +2514,27 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   // automatic choice: the 64-head kernel, measured as fast or faster than the
   // 128-head one on every bf16 workload and split count tried
   if (kernel == MLA_KERNEL_AUTO) kernel = MLA_KERNEL_H64;
+  // bf16 cache with many splits per sequence (S >= 32): groups of R
+  // consecutive split ranges per workgroup, enough workgroups to fill the 256
+  // CUs once; the workgroup stages its queries once and runs one tile pipeline
+  // through its ranges.  Fewer splits (long ranges, ragged batches) keep one
+  // range per workgroup, so that the dispatcher balances ranges of different
+  // lengths; the fp8 (widening) kernel always runs one.
+  int R = 1;
+  if (!fp8 && num_splits >= 32) {
+    const int64_t per_cu = nblk64 / 256;
+    R = static_cast<int>(per_cu < 1 ? 1 : (per_cu > num_splits ? num_splits : per_cu));
+  }
+  const unsigned gridR = static_cast<unsigned>(
+      static_cast<int64_t>(B) * q_len * ((num_splits + R - 1) / R) * HG64);
   if (fp8 && part_dt == MLA_F32)
-    decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
+    decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table, 1);
   else if (fp8)
-    decode_ws_kernel<true, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
+    decode_ws_kernel<true, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table, 1);
   else if (part_dt == MLA_F32)
-    decode_ws_kernel<false, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
+    decode_ws_kernel<false, MLA_F32><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, R);
   else
-    decode_ws_kernel<false, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
+    decode_ws_kernel<false, MLA_BF16><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, R);
   return launch_status();
 }
 
