@@ -48,8 +48,11 @@ def parse():
     ap.add_argument("--workload", default="paged_b64_ragged")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--decode-kernel", default="auto", choices=["auto", "h64", "h128", "h128ws"],
-                    help="decode work decomposition (mla_decode_ex); auto = mla_decode's choice")
+    ap.add_argument("--decode-kernel", default=None,
+                    choices=["auto", "h64", "h128", "h128ws", "balanced"],
+                    help="decode work decomposition (mla_decode_ex); auto = mla_decode's choice; "
+                         "default: the workload's (balanced for a balanced-partition workload, "
+                         "else auto)")
     ap.add_argument("--query-dtype", default="auto", choices=["auto", "bf16", "fp8"],
                     help="absorbed-query format: fp8 (E4M3 + one factor per sequence and head; "
                          "the decode then runs on the fp8 matrix cores) needs an fp8 cache; "
@@ -139,6 +142,13 @@ def _counter_means(path, counter):
     return {k: v[0] / v[1] for k, v in acc.items()}
 
 
+def decode_kernel_of(args, wl) -> str:
+    """--decode-kernel, else the workload's own: balanced or mla_decode's choice"""
+    if args.decode_kernel:
+        return args.decode_kernel
+    return "balanced" if wl.partition == "balanced" else "auto"
+
+
 def record_traffic(d, args):
     """HBM bytes per mla_decode launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by the factor that maps the same counter onto the
@@ -148,6 +158,7 @@ def record_traffic(d, args):
     the record replaces any earlier one for the same configuration."""
     import synth
     wl = synth.workload(args.workload)
+    args.decode_kernel = decode_kernel_of(args, wl)
     key = traffic_key(args.workload, args.splits or wl.num_splits, args.part_dtype,
                       args.decode_kernel, query_dtype(args, wl))
     f = _counter_means(os.path.join(d, "fetch", "run_counter_collection.csv"), "FETCH_SIZE")
@@ -482,6 +493,7 @@ def main():
 
     wl = synth.workload(args.workload)
     S = args.splits or wl.num_splits
+    args.decode_kernel = decode_kernel_of(args, wl)
     print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(wl)
     dev = DeviceInputs(inp)
@@ -521,7 +533,7 @@ def main():
     fused = step.fused_tail(dev.w_uv) and not args.two_call_tail
 
     kernel = {"auto": mla.KERNEL_AUTO, "h64": mla.KERNEL_H64, "h128": mla.KERNEL_H128,
-              "h128ws": mla.KERNEL_H128_WS}[args.decode_kernel]
+              "h128ws": mla.KERNEL_H128_WS, "balanced": mla.KERNEL_H64_BALANCED}[args.decode_kernel]
 
     def decode(rp, prepare=False):
         if fp8q:

@@ -63,6 +63,9 @@ namespace {
 // and the published probabilities carry them into the PV product.
 
 constexpr int kWsThreads = 512;
+constexpr int kBalancedWorkgroups = 256;  // one 64-head workgroup per CU
+constexpr int kBalancedMaxRows = kWsThreads;  // the plan takes one row per thread
+constexpr int kWalkOff = kX64Off + 1536;  // the balanced piece list, after the exchange area
 
 // fp8 rows in flight in a PV wave's registers: lane (k = lane / 8, j = lane % 8)
 // of PV wave w holds, for i = 0..8, the 8 codes of bf16 chunk 8 i + (j ^ swzg(t))
@@ -73,32 +76,26 @@ struct Fp8Rows {
   float sc;
 };
 
-template <bool FP8, int PART_DT>
+template <bool FP8, int PART_DT, bool BAL = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, int R_arg) {
   const int R = FP8 ? 1 : R_arg;  // the fp8 cache runs one range per workgroup
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kX64Off + (FP8 ? 1536 : 1024)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWalkOff + (FP8 || !BAL ? 0 : 12 * kBalancedMaxRows)];
   uint8_t* pbuf = smem + kNBuf * kTileBytes;
   float* xch = reinterpret_cast<float*>(smem + kX64Off);  // [2][64] per-head exchange
   int* votes = reinterpret_cast<int*>(smem + kX64Off + 512);
   float* linv = reinterpret_cast<float*>(smem + kX64Off + 768);  // epilogue: 1 / l per head
   float* tscale = reinterpret_cast<float*>(smem + kX64Off + 1024);  // fp8: [kNBuf][32] row scales
 
-  // work id -> (head group, query token j, group of R consecutive split
-  // ranges, sequence b), the head groups and query tokens of one range group
-  // adjacent (same XCD, so they share each tile through L2).  R = 1 for the
-  // fp8 cache.
+  // Work id -> head group hg (adjacent work ids, same XCD, share each tile
+  // through L2) and r1: in the fixed partition (query token j, group of R
+  // consecutive split ranges, sequence b); in the balanced one the worker.
+  // R = 1 for the fp8 cache.
   const int NG = (P.S + R - 1) / R;
-  const int nwork = P.B * P.QL * NG * P.HG;
-  const int wid = xcd_remap(blockIdx.x, nwork);
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = wid % P.HG;
   const int r1 = wid / P.HG;
-  const int qj = r1 % P.QL;
-  const int r2 = r1 / P.QL;
-  const int grp = r2 % NG;
-  const int b = r2 / NG;
-  const int bj = b * P.QL + qj;  // row of (b, qj) in q_abs, u_part and lse_part
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
@@ -106,31 +103,39 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   const int rw = wave & 3;                                    // index within the role
   const int hbase = hg * kH64;
   const int nhb = min(kH64Blocks, (P.H - hbase) / kHeadsPerWave);  // 1 or 2
-
-  // query token qj of QL new tokens (the last QL cached rows) sees the cached
-  // rows up to and including its own: the first L - (QL - 1 - qj)
-  const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
-                        (P.QL - 1 - qj), 0);
-  // the workgroup's ranges p_first .. p_end - 1 cover tokens [T0, T1): K
-  // consecutive 32-token tiles (every range is a whole number ntf of tiles),
-  // one pipeline through all of them; ranges from p_live on hold no token
-  const int p_first = grp * R, p_end = min(p_first + R, P.S);
-  const int T0 = p_first * P.chunk;
-  const int T1 = min(p_end * P.chunk, L);
-  const int K = T1 > T0 ? (T1 - T0 + kTileTokens - 1) / kTileTokens : 0;
-  const int ntf = P.chunk / kTileTokens;
-  const int p_live = K > 0 ? (FP8 ? p_first + 1 : p_first + (K - 1) / ntf + 1) : p_first;
-  auto row_base_of = [&](int p) { return (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase; };
-  auto write_empty = [&](int p) {  // a range without tokens: u = 0, lse = -inf (PV waves)
-    const int64_t rb = row_base_of(p);
+  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // first partial row of split p of row bj = b * QL + qj of q_abs / u_part
+  auto row_base = [&](int bj, int p) { return (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase; };
+  auto write_empty = [&](int bj, int p) {  // a split without tokens: u = 0, lse = -inf (PV waves)
+    if (is_qk) return;
+    constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
+    const int64_t rb = row_base(bj, p);
     const int pt = tid - 256;
-    for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
-      store_elem<PART_DT>(P.u_part, rb * kDLatent + idx, 0.0f);
+    // the split's rows of this head group are contiguous: 16-byte stores
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(P.u_part) + rb * kDLatent * kEsz);
+    for (int i = pt; i < nhb * kHeadsPerWave * kDLatent * kEsz / 16; i += 256) dst[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (pt < nhb * kHeadsPerWave) P.lse_part[rb + pt] = -INFINITY;
   };
+  // tokens attended by row v = b * QL + qj: query token qj of QL new tokens
+  // (the last QL cached rows) sees the cached rows up to and including its
+  // own, the first L - (QL - 1 - qj)
+  auto attended = [&](int v) {
+    const int b = v / P.QL, qj = v - (v / P.QL) * P.QL;
+    return max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) - (P.QL - 1 - qj), 0);
+  };
+
+  // One unit of work: row bj's split ranges p_first .. p_end - 1, covering
+  // tokens [T0, T1) of its L attended ones as K consecutive 32-token tiles
+  // (every range but the last a whole number ntf of tiles), one pipeline
+  // through all of them; ranges from p_live on hold no token.
+  auto unit = [&](const int bj, const int L, const int p_first, const int p_end, const int T0,
+                  const int T1, const int ntf, const int lane, const int tid) {
+  const int b = bj / P.QL;
+  const int K = T1 > T0 ? (T1 - T0 + kTileTokens - 1) / kTileTokens : 0;
+  const int p_live = K > 0 ? (FP8 ? p_first + 1 : p_first + (K - 1) / ntf + 1) : p_first;
+  auto row_base_of = [&](int p) { return row_base(bj, p); };
   if (K == 0) {
-    if (!is_qk)
-      for (int p = p_first; p < p_end; ++p) write_empty(p);
+    for (int p = p_first; p < p_end; ++p) write_empty(bj, p);
     return;
   }
   // fp8 (one range): the PV loop runs in pairs of tiles (one register set
@@ -147,7 +152,6 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   //   Q1 Q2 T0 | per range: [pass 0: AM AM] B_k0..B_k1-1 V1 V2
   //   [redo: AM AM T0 B_k0..B_k1-1 V1 V2] E1 E2
   // E2 of a range also certifies that the next range's first tile landed.
-  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   if (is_qk) {
     // ------------------------------------------------------------ QK role
@@ -283,7 +287,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     for (int p = p_first; p < p_live; ++p) {
       int k0, k1;
       range_tiles(p, k0, k1);
-      const int te = min((p + 1) * P.chunk, L);  // the range's end
+      const int te = min(T0 + (p - p_first + 1) * ntf * kTileTokens, T1);  // the range's end
       auto nvalid = [&](int k) { return te - (T0 + k * kTileTokens); };
       m_ref[0] = m_ref[1] = m_seen[0] = m_seen[1] = -INFINITY;
       for (int pass = 0; pass < 2; ++pass) {
@@ -431,11 +435,10 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
     constexpr int kColsRound = 256 / kEsz;             // 128 bf16 / 64 fp32 columns
     constexpr int kStageRow = kColsRound * kEsz + 16;  // padded: rows start 4 banks apart
-    // bf16: the lane index recomputed here (volatile), so that the epilogue's
+    // the lane index recomputed here (volatile), so that the epilogue's
     // addresses are formed in place rather than held across the range loop
-    int eln = lane;
-    if constexpr (!FP8)
-      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(eln));
+    int eln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(eln));
     const int hl = eln & 31, g = eln >> 5;
     uint8_t* W = stage + rw * kHeadsPerWave * kStageRow;
 #pragma unroll
@@ -575,7 +578,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
       // the range's last tile buffer is free until tile k1 + 3 is loaded
       write_partial(row_base_of(p), smem + ((k1 - 1) & (kNBuf - 1)) * kTileBytes);
     }
-    for (int p = p_live; p < p_end; ++p) write_empty(p);
+    for (int p = p_live; p < p_end; ++p) write_empty(bj, p);
   } else {
     // one range per workgroup (R = 1)
     const int t_begin = T0, t_end = T1, ntiles = K;
@@ -670,6 +673,144 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     barrier();  // E1
     barrier();  // E2: linv ready
     write_partial(row_base_of(p_first), smem);  // no tile is in flight in LDS
+  }
+  };  // unit
+
+  // Balanced partition (bf16 cache): the rows' tiles in order (row v's
+  // n_v = ceil(L_v / 32) tiles after those of rows < v, N in all) are cut
+  // into G equal spans [w N / G, (w + 1) N / G), worker w taking span w; G =
+  // min(workers launched, N / ceil(n_max / (S - 1))), so no row meets more
+  // than S spans.  The piece of row v in span w is its split
+  // w - (the span of v's first tile); splits after v's last piece, and every
+  // split of an empty row, are written empty by the worker whose span holds
+  // v's last tile (the span of v's position, the last span if none).
+  constexpr bool balanced = !FP8 && BAL;
+  // the worker's pieces (balanced): kBalancedMaxRows entries of (row |
+  // split << 16, first token, end token), kept in LDS for the whole kernel
+  int* plist = reinterpret_cast<int*>(smem + kWalkOff);
+  int npieces = 1;
+  if constexpr (balanced) {
+    // thread t plans row t (B * QL <= 512, checked on the host)
+    const int V = P.B * P.QL;
+    const int A = tid < V ? attended(tid) : 0;
+    const int n = (A + kTileTokens - 1) / kTileTokens;
+    int* red = reinterpret_cast<int*>(pbuf);  // P buffers: free until the first piece
+    auto wave_scan = [&](int x) {  // inclusive prefix over the wave's lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(x, d);
+        if (lane >= d) x += t;
+      }
+      return x;
+    };
+    // tiles before row t (pre), all tiles (N), the longest row (n_max)
+    const int incl = wave_scan(n);
+    int mx = n;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d));
+    if (lane == 63) red[wave] = incl;
+    if (lane == 0) red[8 + wave] = mx;
+    barrier();
+    int pre = incl - n, N = 0, nmax = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 8; ++w2) {
+      const int t = red[w2];
+      pre += w2 < wave ? t : 0;
+      N += t;
+      nmax = max(nmax, red[8 + w2]);
+    }
+    N = __builtin_amdgcn_readfirstlane(N);
+    nmax = __builtin_amdgcn_readfirstlane(nmax);
+    const int G_launch = static_cast<int>(gridDim.x) / P.HG;
+    const int G = N > 0 ? min(G_launch, max(1, N / ((nmax + P.S - 2) / (P.S - 1)))) : 1;
+    if (r1 >= G) return;  // more workers launched than the spans need
+    const int lo = static_cast<int>(static_cast<int64_t>(r1) * N / G);
+    const int hi = static_cast<int>(static_cast<int64_t>(r1 + 1) * N / G);
+    // row t's piece in this span (its split: this span minus the span of its
+    // first tile), and the empty splits this worker writes for row t
+    bool piece = tid < V && n > 0 && pre < hi && pre + n > lo;
+    int slot = 0, first_empty = P.S;
+    if (piece) {
+      slot = r1 - min(G - 1, static_cast<int>((static_cast<int64_t>(pre + 1) * G - 1) / N));
+      piece = slot < P.S;  // always (G bounds the spans a row meets); keeps writes in bounds
+      if (pre + n <= hi) first_empty = slot + 1;  // the row ends in this span
+    } else if (tid < V && n == 0 && ((pre >= lo && pre < hi) || (r1 == G - 1 && pre == N))) {
+      first_empty = 0;  // an empty row at this span's position
+    }
+    const bool job = first_empty < P.S;
+    // list positions: pieces and empty-split jobs in row order
+    const int pin = wave_scan(piece ? 1 : 0), jin = wave_scan(job ? 1 : 0);
+    if (lane == 63) {
+      red[16 + wave] = pin;
+      red[24 + wave] = jin;
+    }
+    barrier();
+    int pidx = pin - (piece ? 1 : 0), jidx = jin - (job ? 1 : 0), np = 0, nj = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 8; ++w2) {
+      const int tp = red[16 + w2], tj = red[24 + w2];
+      pidx += w2 < wave ? tp : 0;
+      jidx += w2 < wave ? tj : 0;
+      np += tp;
+      nj += tj;
+    }
+    int* jobs = red + 64;  // (row, first empty split)
+    if (piece) {
+      plist[3 * pidx + 0] = tid | (slot << 16);
+      plist[3 * pidx + 1] = kTileTokens * (max(lo, pre) - pre);
+      plist[3 * pidx + 2] = min(kTileTokens * (min(hi, pre + n) - pre), A);
+    }
+    if (job) {
+      jobs[2 * jidx + 0] = tid;
+      jobs[2 * jidx + 1] = first_empty;
+    }
+    barrier();
+    npieces = __builtin_amdgcn_readfirstlane(np);
+    nj = __builtin_amdgcn_readfirstlane(nj);
+    for (int j = 0; j < nj; ++j) {
+      const int v = __builtin_amdgcn_readfirstlane(jobs[2 * j]);
+      const int f = __builtin_amdgcn_readfirstlane(jobs[2 * j + 1]);
+      for (int p = f; p < P.S; ++p) write_empty(v, p);
+    }
+    barrier();  // the P buffers are free again
+  }
+
+  // the pieces of this workgroup: its range group (fixed partition) or the
+  // worker's pieces in row order (balanced); a barrier between two pieces
+  // (the previous one's partial staging vs the next one's first loads)
+  for (int it = 0;; ++it) {
+    int bj, L, pf, pe, T0, T1, ntf;
+    if constexpr (!balanced) {
+      if (it > 0) break;
+      const int qj = r1 % P.QL;
+      const int r2 = r1 / P.QL;
+      const int grp = r2 % NG;
+      const int b = r2 / NG;
+      bj = b * P.QL + qj;
+      L = attended(bj);
+      pf = grp * R;
+      pe = min(pf + R, P.S);
+      T0 = pf * P.chunk;
+      T1 = min(pe * P.chunk, L);
+      ntf = P.chunk / kTileTokens;
+    } else {
+      if (it >= npieces) break;
+      const int e0 = __builtin_amdgcn_readfirstlane(plist[3 * it]);
+      bj = e0 & 0xFFFF;
+      pf = e0 >> 16;
+      pe = pf + 1;
+      T0 = __builtin_amdgcn_readfirstlane(plist[3 * it + 1]);
+      T1 = __builtin_amdgcn_readfirstlane(plist[3 * it + 2]);
+      L = T1;
+      ntf = (T1 - T0 + kTileTokens - 1) / kTileTokens;
+    }
+    if (it > 0) barrier();
+    // balanced: the lane ids pass through an opaque copy per piece, so that
+    // the addresses derived from them are formed inside the piece rather
+    // than held across all of them
+    int lane_i = lane, tid_i = tid;
+    if constexpr (balanced) asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+    unit(bj, L, pf, pe, T0, T1, ntf, lane_i, tid_i);
   }
 }
 
@@ -2461,10 +2602,11 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   const float scale = effective_scale(dims);
   if (cache->ring && q_len != 1) return MLA_E_UNSUPPORTED;
   if (kernel != MLA_KERNEL_AUTO && kernel != MLA_KERNEL_H64 && kernel != MLA_KERNEL_H128 &&
-      kernel != MLA_KERNEL_H128_WS)
+      kernel != MLA_KERNEL_H128_WS && kernel != MLA_KERNEL_H64_BALANCED)
     return MLA_E_ARG;
   if (cache->dtype == MLA_F32) {
-    if (q_len != 1 || kernel == MLA_KERNEL_H128) return MLA_E_UNSUPPORTED;
+    if (q_len != 1 || kernel == MLA_KERNEL_H128 || kernel == MLA_KERNEL_H64_BALANCED)
+      return MLA_E_UNSUPPORTED;
     DecodeF32Params P{static_cast<const float*>(q_abs), static_cast<const float*>(cache->rows),
                       cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                       cache->page_size != 0, B, H, num_splits, chunk, cache->max_seq_len, scale,
@@ -2509,6 +2651,22 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
       decode_w12_kernel<MLA_F32><<<static_cast<unsigned>(nblk), kW12Threads, 0, s>>>(P, cache->block_table);
     else
       decode_w12_kernel<MLA_BF16><<<static_cast<unsigned>(nblk), kW12Threads, 0, s>>>(P, cache->block_table);
+    return launch_status();
+  }
+  // balanced partition (bf16 cache): one worker of HG64 workgroups per two
+  // CUs' worth of 64-head workgroups (256 workgroups of 64 heads in all, one
+  // per CU), each taking an equal share of the batch's tiles
+  if (kernel == MLA_KERNEL_H64_BALANCED) {
+    const int64_t V = static_cast<int64_t>(B) * q_len;
+    const int64_t tiles_max = V * ((static_cast<int64_t>(span) + kTileTokens - 1) / kTileTokens);
+    if (fp8 || num_splits < 2 || V > kBalancedMaxRows || tiles_max > 0x7FFFFFFF)
+      return MLA_E_UNSUPPORTED;
+    if (V == 0) return MLA_OK;
+    const unsigned gridB = static_cast<unsigned>(max(1, kBalancedWorkgroups / HG64) * HG64);
+    if (part_dt == MLA_F32)
+      decode_ws_kernel<false, MLA_F32, true><<<gridB, kWsThreads, 0, s>>>(P, cache->block_table, 1);
+    else
+      decode_ws_kernel<false, MLA_BF16, true><<<gridB, kWsThreads, 0, s>>>(P, cache->block_table, 1);
     return launch_status();
   }
   // automatic choice: the 64-head kernel, measured as fast or faster than the

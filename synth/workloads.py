@@ -48,6 +48,10 @@ class Workload:
     len_range: Optional[tuple] = None  # inclusive (lo, hi) of ragged lengths
     page_size: int = 0  # 0 = contiguous rows, else tokens per page
     num_splits: int = 1
+    # "fixed": mla_decode's split ranges; "balanced": the decode's balanced
+    # partition of the batch (mla_decode_ex, MLA_KERNEL_H64_BALANCED), with
+    # at most num_splits pieces per sequence
+    partition: str = "fixed"
     seed: int = BASE_SEED
     description: str = ""
 
@@ -76,8 +80,9 @@ WORKLOADS = {
         description="long-context bf16 decode: B=4, L=32768, 64 splits"),
     "paged_b64_ragged": Workload(
         "paged_b64_ragged", batch=64, seq_len=None, len_range=(512, 16384),
-        page_size=64, num_splits=8, seed=BASE_SEED + 4,
-        description="paged ragged bf16 decode: B=64, L~U[512,16384], 64-token pages"),
+        page_size=64, num_splits=5, partition="balanced", seed=BASE_SEED + 4,
+        description="paged ragged bf16 decode: B=64, L~U[512,16384], 64-token pages; "
+                    "balanced partition, at most 5 splits per sequence"),
     "fp8_b1_l128k": Workload(
         "fp8_b1_l128k", batch=1, seq_len=131072, cache_dtype="fp8", num_splits=256,
         seed=BASE_SEED + 5,

@@ -70,3 +70,35 @@ def check_against_oracle(dev: DeviceInputs, step: mla.DecodeStep, pairs, tol: fl
     # lse is a log: an absolute error of tol is a relative error of tol in exp(lse)
     assert e_l <= tol, f"lse: max abs err {e_l:.3e} > {tol:g}"
     return e_o, e_u, e_l
+
+
+def balanced_pieces(att, S: int, HG: int, workgroups: int = 256):
+    """The balanced partition of mla_decode_ex(MLA_KERNEL_H64_BALANCED), as the
+    C header states it: rows v (attending att[v] tokens, n_v = ceil(att[v]/32)
+    tiles) laid end to end, N tiles in all, cut into G spans [w N / G,
+    (w+1) N / G) with G = min(workgroups / HG, max(1, N // ceil(n_max / (S-1))))
+    (1 if N = 0).  Returns {(v, split): (t_begin, t_end) or None (empty)} for
+    every row and split."""
+    att = [int(a) for a in att]
+    n = [(a + 31) // 32 for a in att]
+    N, nmax = sum(n), max(n) if n else 0
+    G = 1 if N == 0 else min(max(1, workgroups // HG), max(1, N // -(-nmax // (S - 1))))
+    span_of = lambda x: min(G - 1, ((x + 1) * G - 1) // N) if N else 0  # the span holding tile x
+    out = {}
+    pre = 0
+    for v, (a, nv) in enumerate(zip(att, n)):
+        if nv == 0:
+            for p in range(S):
+                out[(v, p)] = None
+            continue
+        w0, w1 = span_of(pre), span_of(pre + nv - 1)
+        assert w1 - w0 < S
+        for w in range(w0, w1 + 1):
+            lo, hi = w * N // G, (w + 1) * N // G
+            t0 = 32 * (max(lo, pre) - pre)
+            t1 = min(32 * (min(hi, pre + nv) - pre), a)
+            out[(v, w - w0)] = (t0, t1)
+        for p in range(w1 - w0 + 1, S):
+            out[(v, p)] = None
+        pre += nv
+    return out

@@ -266,13 +266,20 @@ def test_decode_ex_kernel_choice_validation():
     launch; the 128-head kernel covers bf16 caches with h a multiple of 128."""
     L = mla.lib()
 
-    def dx(kernel, h=128, c=None, B=2, ql=1):
+    def dx(kernel, h=128, c=None, B=2, ql=1, S=4):
         c = c if c is not None else cache()
-        return L.mla_decode_ex(C.byref(dims(h=h)), B, ql, P, BF16, C.byref(c), 4, P, BF16, P,
+        return L.mla_decode_ex(C.byref(dims(h=h)), B, ql, P, BF16, C.byref(c), S, P, BF16, P,
                                kernel, None)
 
     assert dx(mla.KERNEL_H128, B=0) == OK
-    assert dx(4) == E_ARG
+    assert dx(5) == E_ARG
+    # the balanced partition: bf16 cache, at least 2 splits, at most 512 rows
+    BAL = mla.KERNEL_H64_BALANCED
+    assert dx(BAL, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP
+    assert dx(BAL, S=1) == E_UNSUP
+    assert dx(BAL, B=513) == E_UNSUP
+    assert dx(BAL, B=128, ql=5) == E_UNSUP
+    assert dx(BAL, B=0) == OK
     assert dx(-1) == E_ARG
     assert dx(mla.KERNEL_H128_WS, h=64) == E_UNSUP
     assert dx(mla.KERNEL_H128_WS, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP

@@ -45,3 +45,22 @@ def test_rejects_a_build_with_spills(kw):
 def test_rejects_missing_remarks(skip):
     with pytest.raises(RuntimeError):
         build.check_counted_wait_kernels(build.resource_usage(remarks(skip=skip)))
+
+
+BALANCED = "_ZN3mla12_GLOBAL__N_116decode_ws_kernelILb0ELi1ELb1EEEvNS_12DecodeParamsEPKii"
+
+
+def _with_balanced(spill):
+    r = "mla_kernels.hip:100:1: remark: {} [-Rpass-analysis=kernel-resource-usage]\n"
+    extra = [f"Function Name: {BALANCED}", "    VGPRs: 128", "    ScratchSize [bytes/lane]: 20",
+             f"    VGPRs Spill: {spill}"]
+    return remarks() + "".join(r.format(x) for x in extra)
+
+
+def test_balanced_instances_may_spill_a_little():
+    """the balanced-partition instances carry their piece loop's values and
+    may spill up to the stated bound, not beyond"""
+    build.check_counted_wait_kernels(build.resource_usage(_with_balanced(4)))
+    with pytest.raises(RuntimeError):
+        build.check_counted_wait_kernels(
+            build.resource_usage(_with_balanced(build.BALANCED_MAX_VGPR_SPILLS + 1)))

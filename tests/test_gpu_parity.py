@@ -316,6 +316,7 @@ def test_repeat_is_deterministic():
 # ---------------------------------------------------------------- full sizes
 
 AUTO = mla.KERNEL_AUTO
+BAL = mla.KERNEL_H64_BALANCED
 F8Q = "fp8 query"  # mla.KERNEL_AUTO with the E4M3 absorbed query
 # (workload, tolerance kind, sequences x heads sampled, kernel, parts): the
 # sampled sequences are spread from the first to the last (both ends of the
@@ -330,6 +331,7 @@ FULL = [
     ("long_b4_l32k", "bf16", 4, 8, AUTO, 1),
     ("long_b4_l32k", "bf16", 4, 3, H64, 1),
     ("paged_b64_ragged", "bf16", 8, 8, AUTO, 2),
+    ("paged_b64_ragged", "bf16", 8, 8, BAL, 2),
     ("fp8_b1_l128k", "fp8", 1, 8, AUTO, 1),
     ("fp8_b8_l128k", "fp8", 8, 8, AUTO, 4),
     # the fp8 absorbed query on the fp8 matrix cores
@@ -378,8 +380,9 @@ def test_full_size_sampled(name, kind, nb, nh, kernel, part, parts):
 
 def test_full_size_paged_kernels_agree_on_every_output():
     """The paged ragged workload at full size: the 64-head and the 128-head
-    decode kernels (separate code, separate work decompositions) give the same
-    o, u and lse for all 64 x 128 (b, h) pairs within the bf16 tolerance."""
+    decode kernels (separate code, separate work decompositions) and the
+    balanced partition give the same o, u and lse for all 64 x 128 (b, h)
+    pairs within the bf16 tolerance."""
     wl = synth.workload("paged_b64_ragged")
     dev, a = _full_run("paged_b64_ragged", AUTO)
     o_a, u_a, l_a = a.o.float().clone(), a.u.float().clone(), a.lse.clone()
@@ -389,4 +392,10 @@ def test_full_size_paged_kernels_agree_on_every_output():
         _log(f"  {what}: max rel diff {err:.2e}")
         assert err <= TOL["bf16"], what
     assert (l_a - b.lse).abs().max().item() <= TOL["bf16"]
+    c = run_step(dev, wl.num_splits, kernel=BAL)  # the balanced partition
+    for x, y, what in ((o_a, c.o.float(), "o"), (u_a, c.u.float(), "u")):
+        err = ((x - y).abs().max() / y.abs().max()).item()
+        _log(f"  balanced {what}: max rel diff {err:.2e}")
+        assert err <= TOL["bf16"], what
+    assert (l_a - c.lse).abs().max().item() <= TOL["bf16"]
     _full_cache.clear()
