@@ -75,6 +75,10 @@ def parse():
     ap.add_argument("--gqa", type=int, default=0, metavar="KV_HEADS",
                     help="with --mha: grouped-query attention with this many key/value heads "
                          "(mla_gqa_decode); 0 = one per query head")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="time the decode's tile stream without its arithmetic (mla_stream_probe: "
+                         "256 workgroups x 100 tiles of 36 KB, paired and private) and a torch "
+                         "reduction over 1 GiB; print one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device copy of known size (counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -421,6 +425,50 @@ def prefill_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def stream_ceiling():
+    """The read rate of the decode's tile stream alone (mla_stream_probe), the
+    ceiling the decode's roofline fraction is read against, and a plain torch
+    reduction's read rate.  Two 1 GiB sources alternate so that no launch
+    reads what the previous one left in the 256 MB Infinity Cache; per-launch
+    times from HIP events on the launch stream."""
+    import torch
+
+    import mla_latent_kv_15_amd as mla
+    srcs = [torch.full((1 << 30,), i + 1, dtype=torch.uint8, device="cuda") for i in range(2)]
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
+    wg, tiles, tile_bytes, n = 256, 100, 36864, 40
+    stream = torch.cuda.current_stream()
+    out = {"metric": "decode tile stream without arithmetic (read ceiling), 1 GPU", "unit": "GB/s",
+           "workgroups": wg, "tiles_per_workgroup": tiles, "tile_bytes": tile_bytes}
+
+    def timed(fn):
+        for i in range(4):
+            fn(srcs[i & 1])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record(stream)
+            fn(srcs[i & 1])
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+        return us[n // 2], us[n // 10], us[(9 * n) // 10]
+
+    for paired in (True, False):
+        med, p10, p90 = timed(lambda s: mla.mla_stream_probe(s, wg, tiles, paired, sink, stream=stream))
+        unique = (wg // 2 if paired else wg) * tiles * tile_bytes
+        key = "paired" if paired else "private"
+        out[key] = {"us_median": med, "us_p10": p10, "us_p90": p90, "bytes_unique": unique,
+                    "GBps_unique": unique / med / 1e3, "frac_of_8TBps": unique / med / 8e6,
+                    "GBps_into_CUs": wg * tiles * tile_bytes / med / 1e3}
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    med, p10, p90 = timed(lambda s: torch.sum(s.view(torch.bfloat16), dim=0, dtype=torch.float32,
+                                              out=acc))
+    out["torch_sum_bf16_1GiB"] = {"us_median": med, "GBps": (1 << 30) / med / 1e3,
+                                  "frac_of_8TBps": (1 << 30) / med / 8e6}
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy():
     import torch
     n = 1 << 30
@@ -481,6 +529,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
+    if args.stream_ceiling:
+        stream_ceiling()
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return

@@ -270,6 +270,21 @@ mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t B, int32_t q_len, con
                            void* u_part, int32_t part_dt, float* lse_part, int32_t kernel,
                            void* stream);
 
+/* Measurement: the decode's tile stream without its arithmetic, the ceiling its
+ * HBM fraction is read against ([REV]'s KV-bottleneck introduction: the cache
+ * stream's bandwidth is the quantity).  `workgroups` workgroups of 512 threads
+ * each stream `tiles` consecutive 36,864-byte tiles (32 rows of 1152 bytes) of
+ * `src` (device, 16-byte aligned, src_bytes long) into LDS with the decode's
+ * DMA and waits, 2 tiles in flight, and discard them; with `paired` (an even
+ * number of workgroups) workgroups 2k and 2k+1 of the XCD-aware order read the
+ * same tiles, as the decode's two head groups do; else each its own.  Reads
+ * (paired ? workgroups/2 : workgroups) * tiles * 36864 bytes (more than
+ * src_bytes: MLA_E_SHAPE).  sink: device int32 [workgroups], overwritten.
+ * MLA_E_ARG for a NULL pointer, workgroups or tiles < 1, or an odd paired
+ * count; MLA_E_ALIGN for a misaligned src. */
+mla_status_t mla_stream_probe(const void* src, int64_t src_bytes, int32_t workgroups,
+                              int32_t tiles, int32_t paired, int32_t* sink, void* stream);
+
 /* Merge the split partials of mla_decode with log-sum-exp weights:
  *   lse[b][i] = ln sum_p e^{lse_part[b][p][i]}
  *   u[b][i][:] = sum_p e^{lse_part[b][p][i] - lse[b][i]} * u_part[b][p][i][:]

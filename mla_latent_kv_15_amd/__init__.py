@@ -104,6 +104,8 @@ def lib():
         L.mla_prefill_attn.restype = C.c_int
         L.mla_prefill_attn.argtypes = [C.POINTER(Dims), i32, i32, vp, vp, i32, vp, vp, C.c_int64,
                                        vp, i32, vp, i32, f32p, vp]
+        L.mla_stream_probe.restype = C.c_int
+        L.mla_stream_probe.argtypes = [vp, C.c_int64, i32, i32, i32, vp, vp]
         L.mla_status_str.restype = C.c_char_p
         L.mla_status_str.argtypes = [C.c_int]
         L.mla_version.restype = C.c_int32
@@ -115,7 +117,7 @@ def lib():
 EXPORTED = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_decode_ex", "mla_combine", "mla_up_proj", "mla_combine_up_proj",
             "mla_absorb_q_rope", "mla_cache_append", "mla_mha_decode", "mla_status_str",
             "mla_version", "mla_decode_combine_up_proj_noalloc", "mla_cache_ring_grow",
-            "mla_gqa_decode", "mla_prefill_rebuild_kv", "mla_prefill_attn")
+            "mla_gqa_decode", "mla_prefill_rebuild_kv", "mla_prefill_attn", "mla_stream_probe")
 
 
 def status_str(status: int) -> str:
@@ -306,6 +308,20 @@ def mla_absorb_q_rope(geo: Geometry, q_nope: torch.Tensor, q_rope: torch.Tensor,
     return _launch("mla_absorb_q_rope", (C.byref(d), B, _ptr(q_nope), _ptr(q_rope), dtype_code(q_nope),
                                  _ptr(w_uk), dtype_code(w_uk), _ptr(positions), float(rope_base),
                                  _ptr(q_abs), dtype_code(q_abs), _stream(stream),), (d,), prepare)
+
+
+def mla_stream_probe(src: torch.Tensor, workgroups: int, tiles: int, paired: bool,
+                     sink: torch.Tensor, stream=None, prepare: bool = False):
+    """The decode's tile stream without its arithmetic (a measurement): src any
+    contiguous device tensor (its bytes are streamed), sink int32 [workgroups]."""
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    _need("sink", sink, (int(workgroups),), (torch.int32,))
+    _on_gpu(src, sink)
+    nbytes = src.numel() * src.element_size()
+    return _launch("mla_stream_probe", (_ptr(src), nbytes, int(workgroups), int(tiles),
+                                        1 if paired else 0, _ptr(sink), _stream(stream)), (),
+                   prepare)
 
 
 def mla_gqa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

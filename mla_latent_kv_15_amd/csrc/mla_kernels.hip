@@ -814,6 +814,42 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   }
 }
 
+// ================================================================ stream probe
+//
+// The decode's tile stream alone, the ceiling its HBM fraction is read
+// against: workgroups of 8 waves, 4 of which stream 32-row bf16 tiles (36 KB)
+// into a ring of 4 LDS tile buffers with the decode's DMA plan and counted
+// waits (2 tiles in flight), one barrier per tile, no compute.  With `paired`
+// the two workgroups of adjacent work ids (one XCD) read the same tiles, as the
+// two head groups of a decode range do.
+__global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads)))
+void stream_probe_kernel(const uint8_t* __restrict__ src, int tiles, int paired, int32_t* sink) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNBuf * kTileBytes];
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const uint8_t* base = src + static_cast<int64_t>(paired ? wid >> 1 : wid) * tiles * kTileBytes;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool issuer = wave >= 4;
+  auto dma = [&](int t) {
+    rows_dma_g8(base + static_cast<int64_t>(t) * kTileBytes,
+                lds_addr(smem) + (t & (kNBuf - 1)) * kTileBytes, kTileTokens, wave & 3);
+  };
+  if (issuer) {
+    dma(0);
+    if (tiles > 1) dma(1);
+  }
+  for (int t = 0; t < tiles; ++t) {
+    if (issuer) {  // tile t landed (tile t + 1 may be in flight)
+      if (t + 1 < tiles)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (issuer && t + 2 < tiles) dma(t + 2);  // into the buffer of tile t - 2
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = smem[wid & 1023];
+}
+
 // ================================================================ decode: 128-head tile layout
 //
 // The 12-wave decode below (one workgroup per 128 heads) reads each tile with
@@ -2733,6 +2769,19 @@ extern "C" mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t B, int32_t
   if (static_cast<int64_t>(B) * q_len > 0x7FFFFFFF) return MLA_E_SHAPE;
   return decode_launch(dims, B, q_len, q_abs, q_abs_dt, nullptr, cache, num_splits, u_part,
                        part_dt, lse_part, kernel, static_cast<hipStream_t>(stream));
+}
+
+extern "C" mla_status_t mla_stream_probe(const void* src, int64_t src_bytes, int32_t workgroups,
+                                         int32_t tiles, int32_t paired, int32_t* sink,
+                                         void* stream) {
+  if (!src || !sink || workgroups < 1 || tiles < 1 || (paired && (workgroups & 1)))
+    return MLA_E_ARG;
+  if (reinterpret_cast<uintptr_t>(src) % 16) return MLA_E_ALIGN;
+  const int64_t streams = paired ? workgroups / 2 : workgroups;
+  if (src_bytes < 0 || streams * tiles > src_bytes / kTileBytes) return MLA_E_SHAPE;
+  stream_probe_kernel<<<workgroups, kWsThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(src), tiles, paired ? 1 : 0, sink);
+  return launch_status();
 }
 
 extern "C" mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t num_splits,

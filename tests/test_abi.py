@@ -364,3 +364,22 @@ def test_prefill_validation():
     assert at(q=None) == E_ARG and at(ql=None) == E_ARG and at(S=4000) == E_ARG
     assert at(q_dt=F32) == E_DTYPE and at(o_dt=FP8) == E_DTYPE
     assert at(d=dims(dn=192)) == E_SHAPE and at(o=P + 4) == E_ALIGN
+
+
+def test_stream_probe_validation_before_any_launch():
+    """mla_stream_probe refuses bad arguments on the host: NULL pointers, no
+    workgroups or tiles, an odd paired count, a misaligned source, a source
+    shorter than the tiles it would stream"""
+    L = mla.lib()
+
+    def sp(src=P, nbytes=1 << 30, wg=256, tiles=100, paired=1, sink=P):
+        return L.mla_stream_probe(src, nbytes, wg, tiles, paired, sink, None)
+
+    assert sp(src=None) == E_ARG
+    assert sp(sink=None) == E_ARG
+    assert sp(wg=0) == E_ARG
+    assert sp(tiles=0) == E_ARG
+    assert sp(wg=255) == E_ARG
+    assert sp(src=P + 8) == E_ALIGN
+    assert sp(nbytes=128 * 100 * 36864 - 1) == E_SHAPE
+    assert sp(nbytes=256 * 100 * 36864 - 1, paired=0) == E_SHAPE
