@@ -232,20 +232,23 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
  *   MLA_KERNEL_H64_BALANCED -- the 64-head kernel over a balanced partition
  *                      of the batch instead of the fixed split ranges, for
  *                      ragged batches (split-KV sized to the chip rather than
- *                      to the longest sequence).  Rows v = b * q_len + j in
- *                      order, n_v = ceil(A_v / 32) tiles of the A_v tokens
- *                      row v attends, N = sum n_v; the tiles are cut into G
- *                      spans [floor(w N / G), floor((w+1) N / G)),
+ *                      to the longest sequence).  Rows v = b * q_len + j lie
+ *                      end to end, row v weighing 5 + n_v when it attends
+ *                      A_v > 0 tokens (n_v = ceil(A_v / 32) tiles, placed after
+ *                      its 5 units of start weight) and 0 when it attends none,
+ *                      N = the total weight; the line is cut into G spans
+ *                      [floor(w N / G), floor((w+1) N / G)),
  *                        G = min(256 / ceil(h / 64),
  *                                max(1, floor(N / ceil(n_max / (S - 1)))))
- *                      (G = 1 if N = 0), so no row meets more than S = num_splits
- *                      spans.  Split p of row v is the part of v's tiles in
- *                      span w_v + p, w_v = the span holding v's first tile;
+ *                      with n_max the largest row weight (G = 1 if N = 0), so
+ *                      no row meets more than S = num_splits spans.  Split p of
+ *                      row v is the part of v's tiles in span w_v + p, w_v = the
+ *                      span holding v's first tile;
  *                      splits past v's last span, and all splits of an
  *                      empty row, hold u = 0 and lse = -inf.  mla_combine
  *                      and mla_combine_up_proj merge them as any other
  *                      splits.  BF16 cache and query, 2 <= num_splits, B *
- *                      q_len <= 4096 and B * q_len * ceil(max_seq_len / 32)
+ *                      q_len <= 512 and B * q_len * (ceil(max_seq_len / 32) + 5)
  *                      < 2^31; else MLA_E_UNSUPPORTED.
  *   (an FP8 query always runs its own 64-head kernel: AUTO or H64.)
  *   MLA_KERNEL_AUTO -- what mla_decode and mla_decode_multi use: H64, which

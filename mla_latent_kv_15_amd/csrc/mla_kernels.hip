@@ -65,6 +65,7 @@ namespace {
 constexpr int kWsThreads = 512;
 constexpr int kBalancedWorkgroups = 256;  // one 64-head workgroup per CU
 constexpr int kBalancedMaxRows = kWsThreads;  // the plan takes one row per thread
+constexpr int kRowStartTiles = 5;  // a piece's start, in tiles of streaming (measured ~4.5 us)
 constexpr int kWalkOff = kX64Off + 1536;  // the balanced piece list, after the exchange area
 
 // fp8 rows in flight in a PV wave's registers: lane (k = lane / 8, j = lane % 8)
@@ -676,14 +677,15 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   }
   };  // unit
 
-  // Balanced partition (bf16 cache): the rows' tiles in order (row v's
-  // n_v = ceil(L_v / 32) tiles after those of rows < v, N in all) are cut
-  // into G equal spans [w N / G, (w + 1) N / G), worker w taking span w; G =
-  // min(workers launched, N / ceil(n_max / (S - 1))), so no row meets more
-  // than S spans.  The piece of row v in span w is its split
-  // w - (the span of v's first tile); splits after v's last piece, and every
-  // split of an empty row, are written empty by the worker whose span holds
-  // v's last tile (the span of v's position, the last span if none).
+  // Balanced partition (bf16 cache): the rows laid end to end, row v weighing
+  // kRowStartTiles + n_v (n_v = ceil(L_v / 32) tiles; 0 for an empty row), its
+  // tiles after its start weight, N in all, are cut into G equal spans
+  // [w N / G, (w + 1) N / G), worker w taking span w; G = min(workers
+  // launched, N / ceil(n_max / (S - 1))) with n_max the largest row weight, so
+  // no row meets more than S spans.  The piece of row v in span w is its
+  // split w - (the span of v's first tile); splits after v's last piece, and
+  // every split of an empty row, are written empty by the worker whose span
+  // holds v's last tile (the span of v's position, the last span if none).
   constexpr bool balanced = !FP8 && BAL;
   // the worker's pieces (balanced): kBalancedMaxRows entries of (row |
   // split << 16, first token, end token), kept in LDS for the whole kernel
@@ -694,6 +696,10 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     const int V = P.B * P.QL;
     const int A = tid < V ? attended(tid) : 0;
     const int n = (A + kTileTokens - 1) / kTileTokens;
+    // a row's weight: its tiles plus kRowStartTiles for the start of a piece
+    // (query staging, the first tiles' latency), so that spans holding more
+    // row starts take fewer tiles
+    const int nw = n > 0 ? n + kRowStartTiles : 0;
     int* red = reinterpret_cast<int*>(pbuf);  // P buffers: free until the first piece
     auto wave_scan = [&](int x) {  // inclusive prefix over the wave's lanes
 #pragma unroll
@@ -703,15 +709,15 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
       }
       return x;
     };
-    // tiles before row t (pre), all tiles (N), the longest row (n_max)
-    const int incl = wave_scan(n);
-    int mx = n;
+    // weight before row t (pre), all weight (N), the largest row weight (n_max)
+    const int incl = wave_scan(nw);
+    int mx = nw;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d));
     if (lane == 63) red[wave] = incl;
     if (lane == 0) red[8 + wave] = mx;
     barrier();
-    int pre = incl - n, N = 0, nmax = 0;
+    int pre = incl - nw, N = 0, nmax = 0;
 #pragma unroll
     for (int w2 = 0; w2 < 8; ++w2) {
       const int t = red[w2];
@@ -726,14 +732,16 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     if (r1 >= G) return;  // more workers launched than the spans need
     const int lo = static_cast<int>(static_cast<int64_t>(r1) * N / G);
     const int hi = static_cast<int>(static_cast<int64_t>(r1 + 1) * N / G);
-    // row t's piece in this span (its split: this span minus the span of its
-    // first tile), and the empty splits this worker writes for row t
-    bool piece = tid < V && n > 0 && pre < hi && pre + n > lo;
+    // row t's tiles sit at [f0, f0 + n) after its start weight; its piece in
+    // this span (its split: this span minus the span of its first tile), and
+    // the empty splits this worker writes for row t
+    const int f0 = pre + (n > 0 ? kRowStartTiles : 0);
+    bool piece = tid < V && n > 0 && f0 < hi && f0 + n > lo;
     int slot = 0, first_empty = P.S;
     if (piece) {
-      slot = r1 - min(G - 1, static_cast<int>((static_cast<int64_t>(pre + 1) * G - 1) / N));
+      slot = r1 - min(G - 1, static_cast<int>((static_cast<int64_t>(f0 + 1) * G - 1) / N));
       piece = slot < P.S;  // always (G bounds the spans a row meets); keeps writes in bounds
-      if (pre + n <= hi) first_empty = slot + 1;  // the row ends in this span
+      if (f0 + n <= hi) first_empty = slot + 1;  // the row ends in this span
     } else if (tid < V && n == 0 && ((pre >= lo && pre < hi) || (r1 == G - 1 && pre == N))) {
       first_empty = 0;  // an empty row at this span's position
     }
@@ -757,8 +765,8 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     int* jobs = red + 64;  // (row, first empty split)
     if (piece) {
       plist[3 * pidx + 0] = tid | (slot << 16);
-      plist[3 * pidx + 1] = kTileTokens * (max(lo, pre) - pre);
-      plist[3 * pidx + 2] = min(kTileTokens * (min(hi, pre + n) - pre), A);
+      plist[3 * pidx + 1] = kTileTokens * (max(lo, f0) - f0);
+      plist[3 * pidx + 2] = min(kTileTokens * (min(hi, f0 + n) - f0), A);
     }
     if (job) {
       jobs[2 * jidx + 0] = tid;
@@ -2694,7 +2702,8 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   // per CU), each taking an equal share of the batch's tiles
   if (kernel == MLA_KERNEL_H64_BALANCED) {
     const int64_t V = static_cast<int64_t>(B) * q_len;
-    const int64_t tiles_max = V * ((static_cast<int64_t>(span) + kTileTokens - 1) / kTileTokens);
+    const int64_t tiles_max =
+        V * ((static_cast<int64_t>(span) + kTileTokens - 1) / kTileTokens + kRowStartTiles);
     if (fp8 || num_splits < 2 || V > kBalancedMaxRows || tiles_max > 0x7FFFFFFF)
       return MLA_E_UNSUPPORTED;
     if (V == 0) return MLA_OK;

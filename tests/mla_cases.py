@@ -72,18 +72,23 @@ def check_against_oracle(dev: DeviceInputs, step: mla.DecodeStep, pairs, tol: fl
     return e_o, e_u, e_l
 
 
+ROW_START_WEIGHT = 5
+
+
 def balanced_pieces(att, S: int, HG: int, workgroups: int = 256):
     """The balanced partition of mla_decode_ex(MLA_KERNEL_H64_BALANCED), as the
-    C header states it: rows v (attending att[v] tokens, n_v = ceil(att[v]/32)
-    tiles) laid end to end, N tiles in all, cut into G spans [w N / G,
-    (w+1) N / G) with G = min(workgroups / HG, max(1, N // ceil(n_max / (S-1))))
-    (1 if N = 0).  Returns {(v, split): (t_begin, t_end) or None (empty)} for
-    every row and split."""
+    C header states it: rows v laid end to end, a row attending att[v] > 0
+    tokens weighing 5 + n_v (n_v = ceil(att[v]/32) tiles, after its 5 units of
+    start weight), an empty row 0; the total weight N cut into G spans
+    [w N / G, (w+1) N / G) with G = min(workgroups / HG, max(1, N // ceil(n_max /
+    (S-1)))) (1 if N = 0), n_max the largest row weight.  Returns {(v, split):
+    (t_begin, t_end) or None (empty)} for every row and split."""
     att = [int(a) for a in att]
     n = [(a + 31) // 32 for a in att]
-    N, nmax = sum(n), max(n) if n else 0
+    wt = [ROW_START_WEIGHT + x if x else 0 for x in n]
+    N, nmax = sum(wt), max(wt) if wt else 0
     G = 1 if N == 0 else min(max(1, workgroups // HG), max(1, N // -(-nmax // (S - 1))))
-    span_of = lambda x: min(G - 1, ((x + 1) * G - 1) // N) if N else 0  # the span holding tile x
+    span_of = lambda x: min(G - 1, ((x + 1) * G - 1) // N) if N else 0  # the span holding unit x
     out = {}
     pre = 0
     for v, (a, nv) in enumerate(zip(att, n)):
@@ -91,14 +96,15 @@ def balanced_pieces(att, S: int, HG: int, workgroups: int = 256):
             for p in range(S):
                 out[(v, p)] = None
             continue
-        w0, w1 = span_of(pre), span_of(pre + nv - 1)
+        f0 = pre + ROW_START_WEIGHT  # the row's first tile
+        w0, w1 = span_of(f0), span_of(f0 + nv - 1)
         assert w1 - w0 < S
         for w in range(w0, w1 + 1):
             lo, hi = w * N // G, (w + 1) * N // G
-            t0 = 32 * (max(lo, pre) - pre)
-            t1 = min(32 * (min(hi, pre + nv) - pre), a)
+            t0 = 32 * (max(lo, f0) - f0)
+            t1 = min(32 * (min(hi, f0 + nv) - f0), a)
             out[(v, w - w0)] = (t0, t1)
         for p in range(w1 - w0 + 1, S):
             out[(v, p)] = None
-        pre += nv
+        pre += wt[v]
     return out
