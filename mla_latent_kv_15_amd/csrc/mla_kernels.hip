@@ -1660,20 +1660,28 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
     if (c < 32 * qcpr) *reinterpret_cast<u32x4_t*>(qs + (c / qcpr) * q_stride + 16 * (c % qcpr)) = v;
   };
   bf16x8_t bq[kMaxDHead / 16];
-  u32x4_t qv[2];
+  u32x4_t qv[2], qn[2];
   if (q_lds) {
     qv[0] = q_chunk(0, 0);
     qv[1] = q_chunk(1, 0);
+    if (B > 32) {  // the next tile's rows, staged while this one is multiplied
+      qn[0] = q_chunk(0, 32);
+      qn[1] = q_chunk(1, 32);
+    }
   } else {
     load_q(bq, 0);
   }
-  // RoPE rows: 8 chunks of 16 B per sequence
-  const bool rope_copy = blockIdx.y == 0 && tid < B * (kDRope / 8);
-  u32x4_t rv = u32x4_t{0u, 0u, 0u, 0u};
-  if (rope_copy)
-    rv = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q_rope) +
-                                           (static_cast<int64_t>(tid >> 3) * H + h) * kDRope +
-                                           8 * (tid & 7));
+  // RoPE rows: 8 chunks of 16 B per sequence, chunks tid and tid + 256 loaded
+  // here (all of them for B <= 64), the rest where they are copied
+  u32x4_t rv[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kProjThreads;
+    if (blockIdx.y == 0 && i < B * (kDRope / 8))
+      rv[k] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(q_rope) +
+                                                (static_cast<int64_t>(i >> 3) * H + h) * kDRope +
+                                                8 * (i & 7));
+  }
 #pragma unroll
   for (int i = 0; i < kStage; ++i) {
     const int q = i * kProjThreads + tid;
@@ -1691,12 +1699,14 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
   for (int b0 = 0; b0 < B; b0 += 32) {
     if (q_lds) {
       if (b0 > 0) {  // the next tile of sequences replaces the staged rows
-        qv[0] = q_chunk(0, b0);
-        qv[1] = q_chunk(1, b0);
         __syncthreads();
-        q_store(0, qv[0]);
-        q_store(1, qv[1]);
+        q_store(0, qn[0]);
+        q_store(1, qn[1]);
         __syncthreads();
+        if (b0 + 32 < B) {
+          qn[0] = q_chunk(0, b0 + 32);
+          qn[1] = q_chunk(1, b0 + 32);
+        }
       }
       // B operand: lane (sequence bl, half g) reads elements 16k + 8g .. +7
 #pragma unroll
@@ -1776,7 +1786,9 @@ __global__ __launch_bounds__(kProjThreads) void absorb_mfma_kernel(const uint16_
     for (int i = tid; i < B * (kDRope / 8); i += kProjThreads) {
       const int b = i >> 3, j = 8 * (i & 7);
       const uint16_t* rrow = static_cast<const uint16_t*>(q_rope) + (static_cast<int64_t>(b) * H + h) * kDRope;
-      u32x4_t v = (i == tid && rope_copy) ? rv : *reinterpret_cast<const u32x4_t*>(rrow + j);
+      u32x4_t v = i == tid ? rv[0]
+                  : i == tid + kProjThreads ? rv[1]
+                                            : *reinterpret_cast<const u32x4_t*>(rrow + j);
       if (R.positions) {  // pair with the chunk 32 elements away
         const u32x4_t vp = *reinterpret_cast<const u32x4_t*>(rrow + (j ^ 32));
         const int pos = R.positions[b];
