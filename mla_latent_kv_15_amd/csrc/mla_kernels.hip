@@ -2092,7 +2092,7 @@ constexpr int kCuRows = 16;                // sequences per workgroup
 constexpr int kCuRow = kDLatent * 2 + 16;  // padded LDS row of u (bf16)
 constexpr int kCuBatch = 4;                // splits per batch of partial loads
 
-template <int PART_DT, int O_DT, int VS, int LSE_BLK>
+template <int PART_DT, int O_DT, int VS, int LSE_BLK, bool EARLY_W>
 __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
     const void* u_part, const float* lse_part, const uint16_t* w_uv, void* o, uint16_t* u_out,
     float* lse_out, int B, int H, int S, int d_v, int rows) {
@@ -2147,17 +2147,23 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   auto wrow = [&](int nb) {
     return w_uv + (static_cast<int64_t>(h) * d_v + 16 * nb + n16) * kDLatent + 8 * kg;
   };
+  // EARLY_W: the wave's W_UV rows are loaded with the first loads (64 more
+  // VGPRs: one 512-thread workgroup per CU); else once the partials are
+  // summed, in flight during the merge's LDS steps (two workgroups per CU,
+  // for grids of more workgroups than CUs)
   bf16x8_t wk[kKs];
-  if (VS == 1 || nb0 + wave < nb1) {  // wave-uniform
+  if (EARLY_W && (VS == 1 || nb0 + wave < nb1)) {  // wave-uniform
     const uint16_t* wr = wrow(min(nb0 + wave, nb1 - 1));
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
   }
+  // splits per batch of partial loads: fp32 partials take twice the registers
+  constexpr int kBatch = PART_DT == MLA_F32 ? kCuBatch / 2 : kCuBatch;
   constexpr int kEl = PART_DT == MLA_F32 ? 4 : 8;  // elements per 16-byte load
   constexpr int kLd = 16 / kEl;                     // loads per split
-  auto load_batch = [&](u32x4_t (&v)[kCuBatch][kLd], int k0) {
+  auto load_batch = [&](u32x4_t (&v)[kBatch][kLd], int k0) {
 #pragma unroll
-    for (int q = 0; q < kCuBatch; ++q) {
+    for (int q = 0; q < kBatch; ++q) {
       const int p = ns > 0 ? split(min(k0 + q, ns - 1)) : 0;
       const int64_t e = (prow + static_cast<int64_t>(p) * H) * kDLatent + 16 * cg;
 #pragma unroll
@@ -2169,7 +2175,7 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
       }
     }
   };
-  u32x4_t va[kCuBatch][kLd], vb[kCuBatch][kLd];
+  u32x4_t va[kBatch][kLd], vb[kBatch][kLd];
   load_batch(va, 0);
   // log-sum-exp weights over all splits of the sequence (every group of the
   // sequence computes the same values)
@@ -2215,7 +2221,7 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
 #pragma unroll
   for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
   float wl = 0.0f;  // S > 32: weight of the group's split 32 * (k / 32) + (lane % 32)
-  auto accumulate = [&](const u32x4_t (&v)[kCuBatch][kLd], int k0) {
+  auto accumulate = [&](const u32x4_t (&v)[kBatch][kLd], int k0) {
     if (!lse_reg && (k0 & 31) == 0) {
       const int kl = k0 + cg;
       wl = (kl < ns && mx != -INFINITY)
@@ -2223,7 +2229,7 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
                : 0.0f;
     }
 #pragma unroll
-    for (int q = 0; q < kCuBatch; ++q) {
+    for (int q = 0; q < kBatch; ++q) {
       float w;
       if (lse_reg) {  // split p's weight: lane p % 32, register p / 32
         const int sp = split(k0 + q);
@@ -2249,14 +2255,19 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
       }
     }
   };
-  // batches of kCuBatch splits, the next batch in flight while one is summed
-  for (int k0 = 0; k0 < ns; k0 += 2 * kCuBatch) {
-    if (k0 + kCuBatch < ns) load_batch(vb, k0 + kCuBatch);
+  // batches of kBatch splits, the next batch in flight while one is summed
+  for (int k0 = 0; k0 < ns; k0 += 2 * kBatch) {
+    if (k0 + kBatch < ns) load_batch(vb, k0 + kBatch);
     accumulate(va, k0);
-    if (k0 + kCuBatch < ns) {
-      if (k0 + 2 * kCuBatch < ns) load_batch(va, k0 + 2 * kCuBatch);
-      accumulate(vb, k0 + kCuBatch);
+    if (k0 + kBatch < ns) {
+      if (k0 + 2 * kBatch < ns) load_batch(va, k0 + 2 * kBatch);
+      accumulate(vb, k0 + kBatch);
     }
+  }
+  if (!EARLY_W && (VS == 1 || nb0 + wave < nb1)) {  // wave-uniform
+    const uint16_t* wr = wrow(min(nb0 + wave, nb1 - 1));
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) wk[ks] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * ks);
   }
   if (nph > 1) {  // workgroup-uniform: sum the phases of each sequence
     f32x4_t* red = reinterpret_cast<f32x4_t*>(us + kCuRows * kCuRow);  // [group][4][lane]
@@ -2878,22 +2889,31 @@ static mla_status_t combine_up_launch(const mla_dims_t* dims, int32_t B, int32_t
   const int64_t nblk = static_cast<int64_t>(H) * ((B + rows - 1) / rows) * vsplit;
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid = static_cast<unsigned>(nblk);
+  // one workgroup per CU holds the W_UV rows from the start; a larger grid
+  // runs two per CU with them loaded after the merge (fewer registers)
+  const bool early_w = nblk <= 256;
   uint16_t* ub = static_cast<uint16_t*>(u);
   const uint16_t* w = static_cast<const uint16_t*>(w_uv);
+#define MLA_CU_K(PD, OD, EW)                                                                       \
+  if (vsplit == 2 && num_splits <= 32)                                                             \
+    combine_up_kernel<PD, OD, 2, 1, EW><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, \
+                                                                    B, H, num_splits, dims->d_v, rows); \
+  else if (vsplit == 2)                                                                            \
+    combine_up_kernel<PD, OD, 2, 8, EW><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, \
+                                                                    B, H, num_splits, dims->d_v, rows); \
+  else if (num_splits <= 32)                                                                       \
+    combine_up_kernel<PD, OD, 1, 1, EW><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, \
+                                                                    B, H, num_splits, dims->d_v, rows); \
+  else                                                                                             \
+    combine_up_kernel<PD, OD, 1, 8, EW><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse, \
+                                                                    B, H, num_splits, dims->d_v, rows);
 #define MLA_CU(PD, OD)                                                                             \
   if (part_dt == PD && o_dt == OD) {                                                               \
-    if (vsplit == 2 && num_splits <= 32)                                                           \
-      combine_up_kernel<PD, OD, 2, 1><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
-                                                                  B, H, num_splits, dims->d_v, rows); \
-    else if (vsplit == 2)                                                                          \
-      combine_up_kernel<PD, OD, 2, 8><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
-                                                                  B, H, num_splits, dims->d_v, rows); \
-    else if (num_splits <= 32)                                                                     \
-      combine_up_kernel<PD, OD, 1, 1><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
-                                                                  B, H, num_splits, dims->d_v, rows); \
-    else                                                                                           \
-      combine_up_kernel<PD, OD, 1, 8><<<grid, kCuThreads, 0, s>>>(u_part, lse_part, w, o, ub, lse,  \
-                                                                  B, H, num_splits, dims->d_v, rows); \
+    if (early_w) {                                                                                 \
+      MLA_CU_K(PD, OD, true)                                                                       \
+    } else {                                                                                       \
+      MLA_CU_K(PD, OD, false)                                                                      \
+    }                                                                                              \
     return launch_status();                                                                        \
   }
   MLA_CU(MLA_BF16, MLA_BF16)
@@ -2901,6 +2921,7 @@ static mla_status_t combine_up_launch(const mla_dims_t* dims, int32_t B, int32_t
   MLA_CU(MLA_F32, MLA_BF16)
   MLA_CU(MLA_F32, MLA_F32)
 #undef MLA_CU
+#undef MLA_CU_K
   return MLA_E_DTYPE;
 }
 

@@ -53,6 +53,9 @@ CASES = [  # (batch, lengths or uniform L, splits, partial dtype, output dtype)
     # many splits: fewer sequences per workgroup than the grid alone would need
     (8, 9000, 256, torch.bfloat16, torch.bfloat16),
     (33, 500, 64, torch.bfloat16, torch.float32),
+    # more workgroups than CUs: two per CU, W_UV rows loaded after the merge
+    (70, 1200, 5, torch.float32, torch.bfloat16),
+    (64, 2000, 40, torch.bfloat16, torch.float32),
 ]
 
 
