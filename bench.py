@@ -511,6 +511,51 @@ def cpu_baseline(inp, target_s: float = 15.0):
                       f"{dt:.1f} s; scaled to the whole batch by cached tokens"}
 
 
+# the oracle's one-thread run, in a child process (OpenMP reads its thread
+# count when the library starts); no GPU is touched there
+_ONE_CORE = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import numpy as np
+import oracle, synth
+inp = synth.make_inputs(synth.workload(sys.argv[2]))
+target = float(sys.argv[3])
+wl = inp.wl
+t = time.perf_counter()
+n = 0
+while n < wl.batch and (n == 0 or time.perf_counter() - t < target):
+    oracle.decode_inputs(inp, sel=[(n, h) for h in range(wl.heads)])
+    n += 1
+dt = time.perf_counter() - t
+lens = np.asarray(inp.seq_lens, np.float64)
+print(json.dumps({"seqs": n, "sampled": float(lens[:n].sum()), "total": float(lens.sum()),
+                  "s": dt, "threads": oracle.num_threads()}))
+"""
+
+
+def cpu_baseline_one_core(name: str, target_s: float = 10.0):
+    """The oracle on one host thread (whole sequences, all heads, about
+    target_s seconds), scaled to the whole batch by cached tokens."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _ONE_CORE, os.path.dirname(os.path.abspath(__file__)),
+                        name, str(target_s)], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(r.stderr[-2000:])
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    batch_s = d["s"] * d["total"] / max(d["sampled"], 1.0)
+    import synth
+    wl = synth.workload(name)
+    return {"value": wl.batch / batch_s, "unit": "tokens/s", "cores": d["threads"], "kind": "oracle",
+            "sample": f"{d['seqs']} of {wl.batch} sequences ({int(d['sampled'])} of {int(d['total'])} "
+                      f"cached tokens), all {wl.heads} heads, one host thread, {d['s']:.1f} s; "
+                      f"scaled to the whole batch by cached tokens"}
+
+
+# workloads whose oracle is also timed on one thread
+ONE_CORE_WORKLOADS = ("tiny_f32", "dsv2_b32_l2k")
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -705,6 +750,10 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp)
+    cpu1 = None
+    if not args.no_cpu_baseline and wl.name in ONE_CORE_WORKLOADS:
+        print("[bench] cpu baseline on one thread (oracle)", file=sys.stderr, flush=True)
+        cpu1 = cpu_baseline_one_core(wl.name)
 
     rec = {
         "metric": "MLA decode tokens/s + latent-KV HBM GB/s (% of MI355X peak), 1 GPU",
@@ -741,6 +790,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes},
         "cpu_baseline": cpu,
+        "cpu_baseline_one_thread": cpu1,
     }
     print(json.dumps(rec), flush=True)
 

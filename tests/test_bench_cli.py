@@ -49,3 +49,13 @@ def test_launch_stats():
     st = bench.launch_stats([float(x) for x in range(1, 102)])
     assert st["median"] == 51.0 and st["p10"] == 11.0 and st["p90"] == 91.0
     assert st["mean"] == 51.0 and st["n"] == 101
+
+
+def test_one_thread_oracle_baseline():
+    """the one-thread oracle timing runs in a child process with one OpenMP
+    thread and reports it"""
+    sys.path.insert(0, ROOT)
+    import bench
+    r = bench.cpu_baseline_one_core("tiny_f32", 0.1)
+    assert r["cores"] == 1 and r["kind"] == "oracle" and r["value"] > 0
+    assert "one host thread" in r["sample"]
