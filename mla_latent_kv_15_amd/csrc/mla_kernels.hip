@@ -126,11 +126,11 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   };
 
   // One unit of work: row bj's split ranges p_first .. p_end - 1, covering
-  // tokens [T0, T1) of its L attended ones as K consecutive 32-token tiles
+  // tokens [T0, T1) of its attended ones as K consecutive 32-token tiles
   // (every range but the last a whole number ntf of tiles), one pipeline
   // through all of them; ranges from p_live on hold no token.
-  auto unit = [&](const int bj, const int L, const int p_first, const int p_end, const int T0,
-                  const int T1, const int ntf, const int lane, const int tid) {
+  auto unit = [&](const int bj, const int p_first, const int p_end, const int T0, const int T1,
+                  const int ntf, const int lane, const int tid) {
   const int b = bj / P.QL;
   const int K = T1 > T0 ? (T1 - T0 + kTileTokens - 1) / kTileTokens : 0;
   const int p_live = K > 0 ? (FP8 ? p_first + 1 : p_first + (K - 1) / ntf + 1) : p_first;
@@ -366,7 +366,6 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   }
 
   // -------------------------------------------------------------- PV role
-  const int hl = lane & 31, g = lane >> 5;
   const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
   const int tr_row = 4 * (G >> 1) + e;
   const int tr_key = swzg(tr_row);
@@ -494,7 +493,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   };
 
   if constexpr (!FP8) {
-    // tile k of the workgroup: tokens T0 + 32 k .., all attended (T1 <= L)
+    // tile k of the workgroup: tokens T0 + 32 k .., all attended (T1 is at most the row's length)
     auto dma_plan = [&](int k) {
       const int tt = T0 + k * kTileTokens;
       const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
@@ -787,7 +786,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   // worker's pieces in row order (balanced); a barrier between two pieces
   // (the previous one's partial staging vs the next one's first loads)
   for (int it = 0;; ++it) {
-    int bj, L, pf, pe, T0, T1, ntf;
+    int bj, pf, pe, T0, T1, ntf;
     if constexpr (!balanced) {
       if (it > 0) break;
       const int qj = r1 % P.QL;
@@ -795,11 +794,10 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
       const int grp = r2 % NG;
       const int b = r2 / NG;
       bj = b * P.QL + qj;
-      L = attended(bj);
       pf = grp * R;
       pe = min(pf + R, P.S);
       T0 = pf * P.chunk;
-      T1 = min(pe * P.chunk, L);
+      T1 = min(pe * P.chunk, attended(bj));
       ntf = P.chunk / kTileTokens;
     } else {
       if (it >= npieces) break;
@@ -809,7 +807,6 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
       pe = pf + 1;
       T0 = __builtin_amdgcn_readfirstlane(plist[3 * it + 1]);
       T1 = __builtin_amdgcn_readfirstlane(plist[3 * it + 2]);
-      L = T1;
       ntf = (T1 - T0 + kTileTokens - 1) / kTileTokens;
     }
     if (it > 0) barrier();
@@ -818,7 +815,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     // than held across all of them
     int lane_i = lane, tid_i = tid;
     if constexpr (balanced) asm volatile("" : "+v"(lane_i), "+v"(tid_i));
-    unit(bj, L, pf, pe, T0, T1, ntf, lane_i, tid_i);
+    unit(bj, pf, pe, T0, T1, ntf, lane_i, tid_i);
   }
 }
 
