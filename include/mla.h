@@ -171,8 +171,16 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t B, const void* q_
 /* Attention of every head over the latent cache, split into num_splits token
  * ranges per sequence.  Split p of sequence b covers tokens
  *   [p*C, min((p+1)*C, L_b)),  C = 32 * ceil(max_seq_len / (32*num_splits)),
- * so every range is a whole number of 32-token tiles; empty ranges write
- * u = 0 and lse = -inf.  For each (b, p, i) over that range R:
+ * so every range is a whole number of 32-token tiles; an empty range writes
+ * u = 0 and lse = -inf.  When one workgroup takes R > 1 consecutive ranges
+ * it merges them (one softmax over their tokens, the same log-sum-exp merge
+ * mla_combine does): split g then covers ranges gR .. gR + R - 1, i.e.
+ * tokens [gRC, min((g+1)RC, L_b)), and the splits from ceil(num_splits / R)
+ * on hold lse = -inf with their u_part not written.  That happens with an FP8 query, and
+ * with a BF16 cache when num_splits >= 32, for
+ *   R = min(num_splits, max(1, floor(B * q_len * num_splits * ceil(h/64) / 256)))
+ * (enough workgroups to fill the 256 CUs once); otherwise R = 1.  For each
+ * (b, p, i) over that range R:
  *   s_t  = scale * (q_abs[b][i][0:d_latent]·c_t + q_abs[b][i][d_latent:]·k_R,t)
  *   u_part[b][p][i][:] = sum_{t in R} e^{s_t} c_t / sum_{t in R} e^{s_t}
  *   lse_part[b][p][i]  = ln sum_{t in R} e^{s_t}      (natural log)
@@ -245,7 +253,7 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
  *                      row v is the part of v's tiles in span w_v + p, w_v = the
  *                      span holding v's first tile;
  *                      splits past v's last span, and all splits of an
- *                      empty row, hold u = 0 and lse = -inf.  mla_combine
+ *                      empty row, are empty (lse = -inf, u not written).  mla_combine
  *                      and mla_combine_up_proj merge them as any other
  *                      splits.  BF16 cache and query, 2 <= num_splits, B *
  *                      q_len <= 512 and B * q_len * (ceil(max_seq_len / 32) + 5)
@@ -291,7 +299,8 @@ mla_status_t mla_stream_probe(const void* src, int64_t src_bytes, int32_t workgr
 /* Merge the split partials of mla_decode with log-sum-exp weights:
  *   lse[b][i] = ln sum_p e^{lse_part[b][p][i]}
  *   u[b][i][:] = sum_p e^{lse_part[b][p][i] - lse[b][i]} * u_part[b][p][i][:]
- * Parts with lse = -inf carry no weight; if every part is empty, u = 0 and
+ * Parts with lse = -inf carry no weight and their u_part is not read; if
+ * every part is empty, u = 0 and
  * lse = -inf.  u_part/lse_part as written by mla_decode; u [B][h][d_latent]
  * in u_dt (F32 or BF16); lse [B][h] fp32 or NULL. */
 mla_status_t mla_combine(const mla_dims_t* dims, int32_t B, int32_t num_splits,

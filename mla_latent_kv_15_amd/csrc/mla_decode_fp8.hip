@@ -171,15 +171,21 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table, 
   const int K = T1 > T0 ? (T1 - T0 + kF8Tok - 1) / kF8Tok : 0;
   const int ntf = P.chunk / kF8Tok;
   const int p_live = K > 0 ? p_first + (K - 1) / ntf + 1 : p_first;
-  auto row_base = [&](int p) { return (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase; };
+  auto row_base = [&](int p) { return (static_cast<int64_t>(bj) * P.S_out + p) * P.H + hbase; };
 
-  // ranges without tokens: u = 0, lse = -inf (PV waves)
-  auto write_empty = [&](int p) {
+  // ranges without tokens (PV waves): lse = -inf, and u = 0 unless lse_only
+  // (the slots past merged range groups: mla_combine does not read the u of a
+  // split with lse = -inf)
+  auto write_empty = [&](int p, bool lse_only = false) {
     const int pt = tid - 256;
-    for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
-      store_elem<PART_DT>(P.u_part, row_base(p) * kDLatent + idx, 0.0f);
+    if (!lse_only)
+      for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
+        store_elem<PART_DT>(P.u_part, row_base(p) * kDLatent + idx, 0.0f);
     if (pt < nhb * kHeadsPerWave) P.lse_part[row_base(p) + pt] = -INFINITY;
   };
+  // the workgroup of the last range also marks the slots past the ranges
+  if (!is_qk && p_end == P.S)
+    for (int p = P.S; p < P.S_out; ++p) write_empty(p, true);
   if (K == 0) {
     if (!is_qk)
       for (int p = p_first; p < p_end; ++p) write_empty(p);
@@ -625,19 +631,25 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table, 
 
 }  // namespace
 
-mla_status_t decode_fp8q_launch(const DecodeParams& P, int32_t part_dt, hipStream_t s) {
-  // split ranges per workgroup: enough workgroups to fill the 256 CUs once,
-  // each walking consecutive ranges of one sequence with one pipeline
-  const int64_t units = static_cast<int64_t>(P.B) * P.QL * P.S * P.HG;
+mla_status_t decode_fp8q_launch(const DecodeParams& P0, int32_t part_dt, hipStream_t s) {
+  // R consecutive split ranges per workgroup (enough workgroups to fill the
+  // 256 CUs once), merged into one range: the workgroup streams their tokens
+  // with one softmax and writes one partial, to slot g of its group g; slots
+  // from ceil(S / R) on hold lse = -inf
+  const int64_t units = static_cast<int64_t>(P0.B) * P0.QL * P0.S * P0.HG;
   const int64_t per_cu = units / 256;
-  const int R = static_cast<int>(per_cu < 1 ? 1 : (per_cu > P.S ? P.S : per_cu));
-  const int64_t nblk = static_cast<int64_t>(P.B) * P.QL * ((P.S + R - 1) / R) * P.HG;
+  const int R = static_cast<int>(per_cu < 1 ? 1 : (per_cu > P0.S ? P0.S : per_cu));
+  DecodeParams P = P0;
+  P.S = (P0.S + R - 1) / R;
+  P.chunk = P0.chunk * R;
+  P.S_out = P0.S;
+  const int64_t nblk = static_cast<int64_t>(P.B) * P.QL * P.S * P.HG;
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid = static_cast<unsigned>(nblk);
   if (part_dt == MLA_F32)
-    decode_f8q_kernel<MLA_F32><<<grid, kF8Threads, 0, s>>>(P, P.block_table, R);
+    decode_f8q_kernel<MLA_F32><<<grid, kF8Threads, 0, s>>>(P, P.block_table, 1);
   else
-    decode_f8q_kernel<MLA_BF16><<<grid, kF8Threads, 0, s>>>(P, P.block_table, R);
+    decode_f8q_kernel<MLA_BF16><<<grid, kF8Threads, 0, s>>>(P, P.block_table, 1);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 

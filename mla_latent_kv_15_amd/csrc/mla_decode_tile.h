@@ -30,6 +30,10 @@ struct DecodeParams {
   float* lse_part;
   int32_t ring;  // contiguous rows used as a ring of seq_stride slots
   const float* q_scale;  // E4M3 query: one factor per (b, query token, head)
+  // split slots per row of u_part / lse_part (>= S): when the host merges R
+  // consecutive split ranges into one range per workgroup, S counts the merged
+  // ranges and slots S .. S_out - 1 are empty (lse = -inf)
+  int32_t S_out;
 };
 
 // fp8 cache and fp8 absorbed query, on the fp8 matrix cores (one workgroup

@@ -106,15 +106,20 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   const int nhb = min(kH64Blocks, (P.H - hbase) / kHeadsPerWave);  // 1 or 2
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   // first partial row of split p of row bj = b * QL + qj of q_abs / u_part
-  auto row_base = [&](int bj, int p) { return (static_cast<int64_t>(bj) * P.S + p) * P.H + hbase; };
-  auto write_empty = [&](int bj, int p) {  // a split without tokens: u = 0, lse = -inf (PV waves)
+  auto row_base = [&](int bj, int p) { return (static_cast<int64_t>(bj) * P.S_out + p) * P.H + hbase; };
+  // a split without tokens (PV waves): lse = -inf, and u = 0 unless
+  // lse_only (a slot past merged range groups, an empty split of the balanced
+  // partition: mla_combine does not read the u of a split with lse = -inf)
+  auto write_empty = [&](int bj, int p, bool lse_only = false) {
     if (is_qk) return;
     constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
     const int64_t rb = row_base(bj, p);
     const int pt = tid - 256;
-    // the split's rows of this head group are contiguous: 16-byte stores
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(P.u_part) + rb * kDLatent * kEsz);
-    for (int i = pt; i < nhb * kHeadsPerWave * kDLatent * kEsz / 16; i += 256) dst[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (!lse_only) {  // the split's rows of this head group are contiguous: 16-byte stores
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(P.u_part) + rb * kDLatent * kEsz);
+      for (int i = pt; i < nhb * kHeadsPerWave * kDLatent * kEsz / 16; i += 256)
+        dst[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
     if (pt < nhb * kHeadsPerWave) P.lse_part[rb + pt] = -INFINITY;
   };
   // tokens attended by row v = b * QL + qj: query token qj of QL new tokens
@@ -777,7 +782,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     for (int j = 0; j < nj; ++j) {
       const int v = __builtin_amdgcn_readfirstlane(jobs[2 * j]);
       const int f = __builtin_amdgcn_readfirstlane(jobs[2 * j + 1]);
-      for (int p = f; p < P.S; ++p) write_empty(v, p);
+      for (int p = f; p < P.S; ++p) write_empty(v, p, true);
     }
     barrier();  // the P buffers are free again
   }
@@ -796,6 +801,8 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
       bj = b * P.QL + qj;
       pf = grp * R;
       pe = min(pf + R, P.S);
+      if (pe == P.S)  // the last range's workgroup marks the slots past the ranges
+        for (int p = P.S; p < P.S_out; ++p) write_empty(bj, p, true);
       T0 = pf * P.chunk;
       T1 = min(pe * P.chunk, attended(bj));
       ntf = P.chunk / kTileTokens;
@@ -964,7 +971,7 @@ void decode_w12_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
                         (P.QL - 1 - qj), 0);
   const int t_begin = p * P.chunk;
   const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(bj) * P.S + p) * P.H + hg * kH128;
+  const int64_t row_base = (static_cast<int64_t>(bj) * P.S_out + p) * P.H + hg * kH128;
 
   if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf (no barrier is reached)
     for (int idx = tid; idx < kH128 * kDLatent; idx += kW12Threads)
@@ -1411,36 +1418,47 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(const void* u_par
     return ((static_cast<int64_t>(b) * S + p) * H + h) * kDLatent + c0;
   };
   auto lse_at = [&](int p) { return lse_part[(static_cast<int64_t>(b) * S + p) * H + h]; };
-  PartVec<PART_DT> v[kG];
-#pragma unroll
-  for (int i = 0; i < kG; ++i)
-    if (i < S) v[i] = load_part<PART_DT>(u_part, part_at(i));
-  // log-sum-exp weights (parts with lse = -inf carry no weight)
+  // log-sum-exp weights (parts with lse = -inf carry no weight and their
+  // u is not read: an empty split's u is not written), and the last split
+  // with a finite or NaN log-sum-exp
   float mx = -INFINITY;
-  for (int p = lane; p < S; p += 64) mx = max_nan(mx, lse_at(p));
-  for (int o = 32; o > 0; o >>= 1) mx = max_nan(mx, __shfl_xor(mx, o));
+  int last = -1;
+  for (int p = lane; p < S; p += 64) {
+    const float x = lse_at(p);
+    mx = max_nan(mx, x);
+    last = x != -INFINITY ? p : last;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = max_nan(mx, __shfl_xor(mx, o));
+    last = max(last, __shfl_xor(last, o));
+  }
   float z = 0.0f;
   if (mx != -INFINITY)
     for (int p = lane; p < S; p += 64) z += expf(lse_at(p) - mx);
   for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
   const bool live = z > 0.0f || z != z;  // not every range empty (a NaN sum stays NaN)
   const float inv = live ? 1.0f / z : 0.0f;
+  const int np = last + 1;  // splits that are read
+  PartVec<PART_DT> v[kG];
+#pragma unroll
+  for (int i = 0; i < kG; ++i)
+    if (i < np) v[i] = load_part<PART_DT>(u_part, part_at(i));
   float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  for (int p0 = 0; p0 < S; p0 += kG) {
-    // weight of partial p0 + i sits in lane i; empty ranges hold u = 0
+  for (int p0 = 0; p0 < np; p0 += kG) {
+    // weight of partial p0 + i sits in lane i
     const int pl = p0 + (lane & (kG - 1));
-    const float wl = (pl < S && mx != -INFINITY) ? expf(lse_at(pl) - mx) : 0.0f;
+    const float wl = (pl < np && mx != -INFINITY) ? expf(lse_at(pl) - mx) : 0.0f;
 #pragma unroll
     for (int i = 0; i < kG; ++i) {
       const float w = __shfl(wl, i);
-      if (p0 + i < S) {
+      if (p0 + i < np && w != 0.0f) {  // an empty split before the last: not read
 #pragma unroll
         for (int k = 0; k < 8; ++k) a[k] = fmaf(w, part_elem<PART_DT>(v[i], k), a[k]);
       }
     }
 #pragma unroll
     for (int i = 0; i < kG; ++i)
-      if (p0 + kG + i < S) v[i] = load_part<PART_DT>(u_part, part_at(p0 + kG + i));
+      if (p0 + kG + i < np) v[i] = load_part<PART_DT>(u_part, part_at(p0 + kG + i));
   }
   const int64_t ob = (static_cast<int64_t>(b) * H + h) * kDLatent + c0;
   if constexpr (U_DT == MLA_F32) {
@@ -2212,7 +2230,8 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
   const bool live = z > 0.0f || z != z;  // not every range empty (a NaN sum stays NaN)
   const float inv = live ? 1.0f / z : 0.0f;
   // Splits past the last finite log-sum-exp are empty ranges (the trailing
-  // ranges of a short sequence): weight 0, so their partials are not read.
+  // ranges of a short sequence, the slots past merged range groups): weight 0,
+  // and their partials are not read (an empty split's u is not written).
   ns = min(ns, ph <= last ? (last - ph) / nph + 1 : 0);
   float acc[16];
 #pragma unroll
@@ -2237,7 +2256,7 @@ __global__ __launch_bounds__(kCuThreads) void combine_up_kernel(
       } else {
         w = __shfl(wl, (lane & ~31) | ((k0 + q) & 31));
       }
-      if (k0 + q < ns) {
+      if (k0 + q < ns && w != 0.0f) {  // an empty split before the last: its u is not read
 #pragma unroll
         for (int i = 0; i < kLd; ++i)
 #pragma unroll
@@ -2692,7 +2711,7 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
     DecodeParams Q{q_abs, static_cast<const uint8_t*>(cache->rows), cache->row_scale,
                    cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                    cache->page_size != 0, B, H, num_splits, HG64, chunk64, cache->max_seq_len,
-                   q_len, scale * kLog2e, u_part, lse_part, cache->ring, q_abs_scale};
+                   q_len, scale * kLog2e, u_part, lse_part, cache->ring, q_abs_scale, num_splits};
     return decode_fp8q_launch(Q, part_dt, s);
   }
   const int64_t nblk64 = static_cast<int64_t>(B) * q_len * num_splits * HG64;
@@ -2701,7 +2720,7 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   DecodeParams P{q_abs, static_cast<const uint8_t*>(cache->rows), cache->row_scale,
                  cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                  cache->page_size != 0, B, H, num_splits, HG64, chunk, cache->max_seq_len,
-                 q_len, scale * kLog2e, u_part, lse_part, cache->ring};
+                 q_len, scale * kLog2e, u_part, lse_part, cache->ring, nullptr, num_splits};
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
   const bool h128_ok = !fp8 && H % kH128 == 0;
   const int64_t nblk = static_cast<int64_t>(B) * q_len * num_splits * (H / kH128);
@@ -2737,10 +2756,11 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   // automatic choice: the 64-head kernel, measured as fast or faster than the
   // 128-head one on every bf16 workload and split count tried
   if (kernel == MLA_KERNEL_AUTO) kernel = MLA_KERNEL_H64;
-  // bf16 cache with many splits per sequence (S >= 32): groups of R
-  // consecutive split ranges per workgroup, enough workgroups to fill the 256
-  // CUs once; the workgroup stages its queries once and runs one tile pipeline
-  // through its ranges.  Fewer splits (long ranges, ragged batches) keep one
+  // bf16 cache with many splits per sequence (S >= 32): R consecutive split
+  // ranges per workgroup, enough workgroups to fill the 256 CUs once, merged
+  // into one range: the workgroup streams their tokens with one softmax and
+  // writes one partial, to slot g of its group g; slots from ceil(S / R) on
+  // hold lse = -inf.  Fewer splits (long ranges, ragged batches) keep one
   // range per workgroup, so that the dispatcher balances ranges of different
   // lengths; the fp8 (widening) kernel always runs one.
   int R = 1;
@@ -2748,16 +2768,17 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
     const int64_t per_cu = nblk64 / 256;
     R = static_cast<int>(per_cu < 1 ? 1 : (per_cu > num_splits ? num_splits : per_cu));
   }
-  const unsigned gridR = static_cast<unsigned>(
-      static_cast<int64_t>(B) * q_len * ((num_splits + R - 1) / R) * HG64);
+  P.S = (num_splits + R - 1) / R;
+  P.chunk = chunk * R;
+  const unsigned gridR = static_cast<unsigned>(static_cast<int64_t>(B) * q_len * P.S * HG64);
   if (fp8 && part_dt == MLA_F32)
     decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table, 1);
   else if (fp8)
     decode_ws_kernel<true, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table, 1);
   else if (part_dt == MLA_F32)
-    decode_ws_kernel<false, MLA_F32><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, R);
+    decode_ws_kernel<false, MLA_F32><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, 1);
   else
-    decode_ws_kernel<false, MLA_BF16><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, R);
+    decode_ws_kernel<false, MLA_BF16><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, 1);
   return launch_status();
 }
 

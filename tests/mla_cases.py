@@ -108,3 +108,13 @@ def balanced_pieces(att, S: int, HG: int, workgroups: int = 256):
             out[(v, p)] = None
         pre += wt[v]
     return out
+
+
+def ranges_per_split(B: int, q_len: int, S: int, heads: int, grouped: bool) -> int:
+    """R of mla_decode's merged range groups, as the C header states it: with
+    an FP8 query, or a BF16 cache and S >= 32 (grouped), R = min(S, max(1,
+    floor(B q_len S ceil(h/64) / 256))); else 1.  Split g then covers ranges
+    gR .. gR+R-1 and the splits from ceil(S / R) on are empty."""
+    if not grouped:
+        return 1
+    return min(S, max(1, (B * q_len * S * -(-heads // 64)) // 256))

@@ -115,8 +115,7 @@ def _check_splits(inp, q_rows, up, lp, att, S, HG, heads, ring=False):
         b = v // QL
         for p in range(S):
             rng = pieces[(v, p)]
-            if rng is None:
-                assert np.all(up[v, p, heads] == 0.0), (v, p)
+            if rng is None:  # an empty split: lse = -inf (its u is not written)
                 assert np.all(np.isneginf(lp[v, p, heads])), (v, p)
                 continue
             qb = np.zeros((inp.wl.batch,) + q_rows.shape[1:], q_rows.dtype)
@@ -179,7 +178,7 @@ def test_balanced_every_row_empty():
     q = _query((3, 128), 443)
     _log("balanced: every row empty")
     up, lp = _decode(dev, q, 4, part=torch.bfloat16)
-    assert torch.all(up.float() == 0) and torch.all(torch.isneginf(lp))
+    assert torch.all(torch.isneginf(lp))
 
 
 def test_balanced_several_query_tokens():

@@ -11,11 +11,10 @@ ABI, against the oracle.
   odd lengths (a pair of rows whose second row is past the end), a one-token
   sequence, empty sequences, 32 and 128 heads, several splits;
 * the score-spike redo on this path.
-* workgroups that walk several consecutive split ranges with one pipeline
+* workgroups that take several consecutive split ranges and merge them
   (many splits and few sequences: 256 splits at 2 x 128 heads gives 4 ranges
-  per workgroup), including ranges past the end of a sequence, a range group
-  that straddles it, and a score-spike redo of a range in the middle of a
-  group.
+  per workgroup, merged into one split), including groups past the end of a
+  sequence, a group that straddles it, and a score-spike redo of a group.
 The end-to-end step (absorb -> decode -> tail) at the full 128K sizes is in
 test_gpu_parity.py (the "fp8 query" cases)."""
 
@@ -31,6 +30,7 @@ import oracle
 import synth
 from synth.encode import quantize_rows_e4m3
 from tests.device_inputs import DeviceInputs, bits_to_tensor
+from tests.mla_cases import ranges_per_split
 
 pytestmark = pytest.mark.gpu
 
@@ -173,8 +173,8 @@ def test_fp8_query_partials_every_split():
             codes, "fp8", inp.rows, "fp8", inp.seq_lens, q_scale=scale, row_scale=inp.row_scale,
             seq_stride=inp.seq_stride, sel=pairs, t_begin=tb, t_end=te)
         for k, (b, h) in enumerate(pairs):
-            if not np.isfinite(l_ref[k]):
-                assert np.all(up[b, p, h] == 0) and np.isneginf(lp[b, p, h])
+            if not np.isfinite(l_ref[k]):  # empty: lse = -inf, u not written
+                assert np.isneginf(lp[b, p, h])
                 continue
             assert abs(lp[b, p, h] - l_ref[k]) <= TOL_FP8, (p, b, h)
             assert _rel(up[b, p, h], u_ref[k]) <= TOL_FP8, (p, b, h)
@@ -214,10 +214,11 @@ def test_fp8_query_score_spike_recomputes_range():
 
 
 def test_fp8_query_multi_range_workgroups():
-    """256 splits x 2 sequences x 2 head groups: each workgroup walks 4
-    consecutive ranges of 64 tokens; sequences of 3000 and 700 tokens leave
-    most range groups partly or wholly past the end.  Every split's partial
-    against the oracle over its range."""
+    """256 splits x 2 sequences x 2 head groups: each workgroup takes 4
+    consecutive ranges of 64 tokens and merges them, so split g holds ranges
+    4g .. 4g+3 (tokens [256 g, 256 g + 256)) and splits 64 .. 255 are empty;
+    sequences of 3000 and 700 tokens leave most groups partly or wholly past
+    the end.  Every sampled split against the oracle over its tokens."""
     lens = [3000, 700]
     S = 256
     wl = synth.workload("fp8_b1_l128k").with_(batch=2, heads=128, seq_len=None,
@@ -232,24 +233,28 @@ def test_fp8_query_multi_range_workgroups():
     _log(f"  merged: err u {e_u:.2e} lse {e_l:.2e}")
     assert e_u <= TOL_FP8 and e_l <= TOL_FP8
     up, lp = u_part.cpu().numpy(), lse_part.cpu().numpy()
-    chunk = 64
-    for p in (0, 1, 3, 4, 10, 11, 12, 46, 47, 48, 255):
+    R = ranges_per_split(2, 1, S, 128, grouped=True)
+    assert R == 4
+    chunk = 64 * R
+    assert np.all(np.isneginf(lp[:, S // R:]))  # the slots past the groups
+    for p in (0, 1, 2, 3, 10, 11, 12, 46, 47, 63):
         tb = [min(p * chunk, L) for L in lens]
         te = [min((p + 1) * chunk, L) for L in lens]
         u_ref, l_ref, _ = oracle.absorbed_decode(
             codes, "fp8", inp.rows, "fp8", inp.seq_lens, q_scale=scale, row_scale=inp.row_scale,
             seq_stride=inp.seq_stride, sel=pairs, t_begin=tb, t_end=te)
         for k, (b, h) in enumerate(pairs):
-            if not np.isfinite(l_ref[k]):
-                assert np.all(up[b, p, h] == 0) and np.isneginf(lp[b, p, h]), (p, b, h)
+            if not np.isfinite(l_ref[k]):  # empty: lse = -inf, u not written
+                assert np.isneginf(lp[b, p, h]), (p, b, h)
                 continue
             assert abs(lp[b, p, h] - l_ref[k]) <= TOL_FP8, (p, b, h)
             assert _rel(up[b, p, h], u_ref[k]) <= TOL_FP8, (p, b, h)
 
 
 def test_fp8_query_spike_inside_a_range_group():
-    """A score spike in range 13 of 256 (ranges 12-15 share a workgroup): that
-    range alone is computed again, its neighbours are not disturbed."""
+    """A score spike in range 13 of 256 (ranges 12-15 share a workgroup and
+    are merged into split 3): that group is computed again with its true
+    maximum; its neighbours are not disturbed."""
     lens = [4000, 4000]
     S = 256
     wl = synth.workload("fp8_b1_l128k").with_(batch=2, heads=128, seq_len=None,
@@ -267,8 +272,10 @@ def test_fp8_query_spike_inside_a_range_group():
     u, lse, u_part, lse_part = _decode(dev, codes, scale, S, part=torch.float32)
     pairs = [(b, h) for b in range(2) for h in (0, 77, 127)]
     up, lp = u_part.cpu().numpy(), lse_part.cpu().numpy()
-    for p in (11, 12, 13, 14, 15, 16):
-        tb, te = [p * 64] * 2, [(p + 1) * 64] * 2
+    R = ranges_per_split(2, 1, S, 128, grouped=True)
+    assert R == 4
+    for p in (2, 3, 4):  # ranges 8-11, 12-15 (the spike), 16-19
+        tb, te = [p * 64 * R] * 2, [(p + 1) * 64 * R] * 2
         u_ref, l_ref, _ = oracle.absorbed_decode(
             codes, "fp8", inp.rows, "fp8", inp.seq_lens, q_scale=scale, row_scale=inp.row_scale,
             seq_stride=inp.seq_stride, sel=pairs, t_begin=tb, t_end=te)

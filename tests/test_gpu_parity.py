@@ -132,8 +132,9 @@ def test_paged_matches_contiguous_bitwise(kernel):
     contig = DeviceInputs(synth.make_inputs(base.with_(page_size=0), lengths=lens))
     a = run_step(paged, 3, kernel=kernel)
     b = run_step(contig, 3, kernel=kernel)
-    assert torch.equal(a.u_part.view(torch.int16), b.u_part.view(torch.int16))
     assert torch.equal(a.lse_part, b.lse_part)
+    live = torch.isfinite(a.lse_part)  # an empty split's u is not written
+    assert torch.equal(a.u_part.view(torch.int16)[live], b.u_part.view(torch.int16)[live])
     assert torch.equal(a.o.view(torch.int16), b.o.view(torch.int16))
     pairs = [(bb, h) for bb in range(6) for h in (0, 127)]
     check_against_oracle(paged, a, pairs, TOL["bf16"])
