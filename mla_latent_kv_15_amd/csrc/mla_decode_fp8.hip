@@ -132,17 +132,18 @@ __device__ inline void f8_factor_issue(const float* tile_scale, uint32_t lds_fac
 template <int PART_DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kF8Threads, kF8Threads),
                           amdgpu_waves_per_eu(2, 2)))
-void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table, int R) {
+void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kF8Lds];
   float* rfac = reinterpret_cast<float*>(smem + kF8ROff);  // [kNBuf][64] row factors
   float* xch = reinterpret_cast<float*>(smem + kF8XOff);   // [2][2][64] per-head exchange
   float* linv = xch + 256;                                 // [64] 1 / normaliser per head
   int* votes = reinterpret_cast<int*>(smem + kF8XOff + 1280);
 
-  // work id -> (head group, query token j, group of R split ranges, sequence
-  // b), the head groups and query tokens of one range group adjacent (same
-  // XCD: they share each tile through L2)
-  const int NG = (P.S + R - 1) / R;
+  // work id -> (head group, query token j, split range p, sequence b; the
+  // consecutive ranges that the host merged count as one), the head groups and
+  // query tokens of one range adjacent (same XCD: they share each tile through
+  // L2)
+  const int NG = P.S;
   const int nwork = P.B * P.QL * NG * P.HG;
   const int wid = xcd_remap(blockIdx.x, nwork);
   const int hg = wid % P.HG;
@@ -165,7 +166,7 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table, 
   // the workgroup's ranges p_first .. p_end - 1 cover tokens [T0, T1): K
   // consecutive 64-token tiles (every range is a whole number ntf of tiles),
   // one pipeline through all of them; ranges from p_live on hold no token
-  const int p_first = grp * R, p_end = min(p_first + R, P.S);
+  const int p_first = grp, p_end = grp + 1;
   const int T0 = p_first * P.chunk;
   const int T1 = min(p_end * P.chunk, L);
   const int K = T1 > T0 ? (T1 - T0 + kF8Tok - 1) / kF8Tok : 0;
@@ -647,9 +648,9 @@ mla_status_t decode_fp8q_launch(const DecodeParams& P0, int32_t part_dt, hipStre
   if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
   const unsigned grid = static_cast<unsigned>(nblk);
   if (part_dt == MLA_F32)
-    decode_f8q_kernel<MLA_F32><<<grid, kF8Threads, 0, s>>>(P, P.block_table, 1);
+    decode_f8q_kernel<MLA_F32><<<grid, kF8Threads, 0, s>>>(P, P.block_table);
   else
-    decode_f8q_kernel<MLA_BF16><<<grid, kF8Threads, 0, s>>>(P, P.block_table, 1);
+    decode_f8q_kernel<MLA_BF16><<<grid, kF8Threads, 0, s>>>(P, P.block_table);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_E_HIP;
 }
 

@@ -80,8 +80,7 @@ struct Fp8Rows {
 template <bool FP8, int PART_DT, bool BAL = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWsThreads, kWsThreads),
                           amdgpu_waves_per_eu(2, 2)))
-void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, int R_arg) {
-  const int R = FP8 ? 1 : R_arg;  // the fp8 cache runs one range per workgroup
+void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kWalkOff + (FP8 || !BAL ? 0 : 12 * kBalancedMaxRows)];
   uint8_t* pbuf = smem + kNBuf * kTileBytes;
   float* xch = reinterpret_cast<float*>(smem + kX64Off);  // [2][64] per-head exchange
@@ -90,10 +89,9 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
   float* tscale = reinterpret_cast<float*>(smem + kX64Off + 1024);  // fp8: [kNBuf][32] row scales
 
   // Work id -> head group hg (adjacent work ids, same XCD, share each tile
-  // through L2) and r1: in the fixed partition (query token j, group of R
-  // consecutive split ranges, sequence b); in the balanced one the worker.
-  // R = 1 for the fp8 cache.
-  const int NG = (P.S + R - 1) / R;
+  // through L2) and r1: in the fixed partition (query token j, split range p,
+  // sequence b; consecutive ranges that the host merged count as one); in the
+  // balanced one the worker.
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = wid % P.HG;
   const int r1 = wid / P.HG;
@@ -585,7 +583,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     }
     for (int p = p_live; p < p_end; ++p) write_empty(bj, p);
   } else {
-    // one range per workgroup (R = 1)
+    // one range per workgroup
     const int t_begin = T0, t_end = T1, ntiles = K;
     // fp8 rows travel through registers: tile k is loaded two tiles ahead of
     // its conversion, into register set k % 2, and widened to bf16 on its way
@@ -787,7 +785,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
     barrier();  // the P buffers are free again
   }
 
-  // the pieces of this workgroup: its range group (fixed partition) or the
+  // the pieces of this workgroup: its range (fixed partition) or the
   // worker's pieces in row order (balanced); a barrier between two pieces
   // (the previous one's partial staging vs the next one's first loads)
   for (int it = 0;; ++it) {
@@ -796,11 +794,10 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table, i
       if (it > 0) break;
       const int qj = r1 % P.QL;
       const int r2 = r1 / P.QL;
-      const int grp = r2 % NG;
-      const int b = r2 / NG;
+      const int b = r2 / P.S;
       bj = b * P.QL + qj;
-      pf = grp * R;
-      pe = min(pf + R, P.S);
+      pf = r2 % P.S;
+      pe = pf + 1;
       if (pe == P.S)  // the last range's workgroup marks the slots past the ranges
         for (int p = P.S; p < P.S_out; ++p) write_empty(bj, p, true);
       T0 = pf * P.chunk;
@@ -2748,9 +2745,9 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
     if (V == 0) return MLA_OK;
     const unsigned gridB = static_cast<unsigned>(max(1, kBalancedWorkgroups / HG64) * HG64);
     if (part_dt == MLA_F32)
-      decode_ws_kernel<false, MLA_F32, true><<<gridB, kWsThreads, 0, s>>>(P, cache->block_table, 1);
+      decode_ws_kernel<false, MLA_F32, true><<<gridB, kWsThreads, 0, s>>>(P, cache->block_table);
     else
-      decode_ws_kernel<false, MLA_BF16, true><<<gridB, kWsThreads, 0, s>>>(P, cache->block_table, 1);
+      decode_ws_kernel<false, MLA_BF16, true><<<gridB, kWsThreads, 0, s>>>(P, cache->block_table);
     return launch_status();
   }
   // automatic choice: the 64-head kernel, measured as fast or faster than the
@@ -2772,13 +2769,13 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   P.chunk = chunk * R;
   const unsigned gridR = static_cast<unsigned>(static_cast<int64_t>(B) * q_len * P.S * HG64);
   if (fp8 && part_dt == MLA_F32)
-    decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table, 1);
+    decode_ws_kernel<true, MLA_F32><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
   else if (fp8)
-    decode_ws_kernel<true, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table, 1);
+    decode_ws_kernel<true, MLA_BF16><<<grid64, kWsThreads, 0, s>>>(P, cache->block_table);
   else if (part_dt == MLA_F32)
-    decode_ws_kernel<false, MLA_F32><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, 1);
+    decode_ws_kernel<false, MLA_F32><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table);
   else
-    decode_ws_kernel<false, MLA_BF16><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table, 1);
+    decode_ws_kernel<false, MLA_BF16><<<gridR, kWsThreads, 0, s>>>(P, cache->block_table);
   return launch_status();
 }
 

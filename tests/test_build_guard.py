@@ -11,8 +11,8 @@ import pytest
 build = importlib.import_module("mla_latent_kv_15_amd.build")
 
 NAMES = {
-    "decode_ws_kernel": "_ZN3mla12_GLOBAL__N_116decode_ws_kernelILb0ELi1EEEvNS_12DecodeParamsEPKi",
-    "decode_f8q_kernel": "_ZN3mla12_GLOBAL__N_117decode_f8q_kernelILi1EEEvNS_12DecodeParamsEPKii",
+    "decode_ws_kernel": "_ZN3mla12_GLOBAL__N_116decode_ws_kernelILb0ELi1ELb0EEEvNS_12DecodeParamsEPKi",
+    "decode_f8q_kernel": "_ZN3mla12_GLOBAL__N_117decode_f8q_kernelILi1EEEvNS_12DecodeParamsEPKi",
 }
 
 
@@ -47,7 +47,7 @@ def test_rejects_missing_remarks(skip):
         build.check_counted_wait_kernels(build.resource_usage(remarks(skip=skip)))
 
 
-BALANCED = "_ZN3mla12_GLOBAL__N_116decode_ws_kernelILb0ELi1ELb1EEEvNS_12DecodeParamsEPKii"
+BALANCED = "_ZN3mla12_GLOBAL__N_116decode_ws_kernelILb0ELi1ELb1EEEvNS_12DecodeParamsEPKi"
 
 
 def _with_balanced(spill):
