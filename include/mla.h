@@ -180,10 +180,10 @@ mla_status_t mla_absorb_q_rope(const mla_dims_t* dims, int32_t B, const void* q_
  * with a BF16 cache when num_splits >= 32, for
  *   R = min(num_splits, max(1, floor(B * q_len * num_splits * ceil(h/64) / 256)))
  * (enough workgroups to fill the 256 CUs once); otherwise R = 1.  For each
- * (b, p, i) over that range R:
+ * (b, p, i) over split p's token set T:
  *   s_t  = scale * (q_abs[b][i][0:d_latent]·c_t + q_abs[b][i][d_latent:]·k_R,t)
- *   u_part[b][p][i][:] = sum_{t in R} e^{s_t} c_t / sum_{t in R} e^{s_t}
- *   lse_part[b][p][i]  = ln sum_{t in R} e^{s_t}      (natural log)
+ *   u_part[b][p][i][:] = sum_{t in T} e^{s_t} c_t / sum_{t in T} e^{s_t}
+ *   lse_part[b][p][i]  = ln sum_{t in T} e^{s_t}      (natural log)
  * q_abs [B][h][d_latent+d_rope] (q_abs_dt); q_abs_scale: device fp32 [B][h]
  * for an FP8 query (value = code * q_abs_scale[b][i]), else NULL.  u_part
  * [B][num_splits][h][d_latent] in part_dt (F32 or BF16); lse_part
