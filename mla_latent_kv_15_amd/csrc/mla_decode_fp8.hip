@@ -271,9 +271,8 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
     };
     // scores in the log2 domain: raw x row factor x query factor x scale;
     // tokens past the range end (nvalid tokens in the tile) -> -inf
-    auto scale_scores = [&](f32x16_t& s, int buf, int nvalid) {
-      float rs[16];
-      load_factors(rs, buf);
+    // rs: the tile's row factors (load_factors)
+    auto scale_scores = [&](f32x16_t& s, const float (&rs)[16], int nvalid) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] *= qf * rs[r];
       if (nvalid < kF8Tok) {
@@ -284,9 +283,8 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
           s[r] = (first + 8 * (r >> 2) + (r & 3) < nvalid) ? s[r] : -INFINITY;
       }
     };
-    auto softmax_publish = [&](const f32x16_t& s, int& overflow, int k) {
-      float rs[16];  // reloaded: not held across the MFMAs
-      load_factors(rs, k & (kNBuf - 1));
+    // rs: the row factors scale_scores loaded for the same tile
+    auto softmax_publish = [&](const f32x16_t& s, const float (&rs)[16], int& overflow, int k) {
       uint8_t* PB = smem + kF8POff + (k & 1) * kF8PBytes;
       uint8_t* SB = smem + kF8SOff + (k & 1) * 128;
       float mx = s[0];
@@ -302,7 +300,13 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
         pp[r] = pr * rs[r];  // the value product takes the raw codes
         pmax = fmaxf(pmax, pp[r]);
       }
-      pmax = fmaxf(pmax, __shfl_xor(pmax, 32));  // head n over the wave's 32 tokens
+      {  // head n over the wave's 32 tokens: v_permlane32_swap exchanges the
+         // upper half of pa with the lower half of pb, leaving pa = the lower
+         // half's value and pb = the upper half's in every lane (no LDS trip)
+        float pa = pmax, pb = pmax;
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(pa), "+v"(pb));
+        pmax = fmaxf(pa, pb);
+      }
       // power-of-two factor 2^se putting the largest value in [128, 256)
       const int se = min(max(__builtin_amdgcn_frexp_expf(pmax) - 8, -127), 127);
       const float f = __builtin_ldexpf(1.0f, -se);
@@ -346,9 +350,11 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
         int overflow = 0;
         if (pass > 0) barrier();  // T0: the range's first tile loaded again
         f32x16_t s;
+        float rs[16];
         if (active) {
+          load_factors(rs, k0 & (kNBuf - 1));
           qk_tile(smem + (k0 & (kNBuf - 1)) * kTileBytes, s);
-          scale_scores(s, k0 & (kNBuf - 1), nvalid(k0));
+          scale_scores(s, rs, nvalid(k0));
         }
         if (pass == 0) {  // reference: maximum of the range's first tile
           float mx = -INFINITY;
@@ -359,14 +365,15 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
           agree_max(mx);
           m_ref = mx;
         }
-        if (active) softmax_publish(s, overflow, k0);
+        if (active) softmax_publish(s, rs, overflow, k0);
         for (int k = k0; k < k1; ++k) {
           barrier();  // B_k: P'(k) published, tile k+1 landed
           if (active && k + 1 < k1) {
             const int buf = (k + 1) & (kNBuf - 1);
+            load_factors(rs, buf);  // in flight during the products
             qk_tile(smem + buf * kTileBytes, s);
-            scale_scores(s, buf, nvalid(k + 1));
-            softmax_publish(s, overflow, k + 1);
+            scale_scores(s, rs, nvalid(k + 1));
+            softmax_publish(s, rs, overflow, k + 1);
           }
         }
         const int vote = __any(overflow) ? 1 : 0;
