@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--decode-kernel", default=None,
-                    choices=["auto", "h64", "h128", "h128ws", "balanced"],
+                    choices=["auto", "h64", "balanced"],
                     help="decode work decomposition (mla_decode_ex); auto = mla_decode's choice; "
                          "default: the workload's (balanced for a balanced-partition workload, "
                          "else auto)")
@@ -631,8 +631,8 @@ def main():
     # W_UV product run as one launch (mla_combine_up_proj; u is not stored)
     fused = step.fused_tail(dev.w_uv) and not args.two_call_tail
 
-    kernel = {"auto": mla.KERNEL_AUTO, "h64": mla.KERNEL_H64, "h128": mla.KERNEL_H128,
-              "h128ws": mla.KERNEL_H128_WS, "balanced": mla.KERNEL_H64_BALANCED}[args.decode_kernel]
+    kernel = {"auto": mla.KERNEL_AUTO, "h64": mla.KERNEL_H64,
+              "balanced": mla.KERNEL_H64_BALANCED}[args.decode_kernel]
 
     def decode(rp, prepare=False):
         if fp8q:

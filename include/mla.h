@@ -229,14 +229,6 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
  *   MLA_KERNEL_H64  -- one workgroup per (sequence, split range, 64 heads);
  *                      two workgroups share each cached tile through L2.
  *                      Every cache dtype.
- *   MLA_KERNEL_H128_WS -- one workgroup per (sequence, split range, 128
- *                      heads) of 12 waves: 4 compute the scores and the
- *                      softmax of 32 heads each, 8 the value product of 64
- *                      heads x 128 latent columns each, three waves per SIMD;
- *                      each tile enters one CU once for all of its heads.
- *                      BF16 cache, h a multiple of 128.
- *   MLA_KERNEL_H128 -- the same 128-head decomposition (the name of an
- *                      earlier 4-wave kernel that measured no faster).
  *   MLA_KERNEL_H64_BALANCED -- the 64-head kernel over a balanced partition
  *                      of the batch instead of the fixed split ranges, for
  *                      ragged batches (split-KV sized to the chip rather than
@@ -259,23 +251,21 @@ mla_status_t mla_decode_multi(const mla_dims_t* dims, int32_t B, int32_t q_len,
  *                      q_len <= 512 and B * q_len * (ceil(max_seq_len / 32) + 5)
  *                      < 2^31; else MLA_E_UNSUPPORTED.
  *   (an FP8 query always runs its own 64-head kernel: AUTO or H64.)
- *   MLA_KERNEL_AUTO -- what mla_decode and mla_decode_multi use: H64, which
- *                      measured as fast or faster than the 128-head
- *                      decomposition on the full-size bf16 workloads (with one
- *                      36 KB tile in flight per CU the 128-head stream is
- *                      latency-bound under full load). */
+ *   MLA_KERNEL_AUTO -- what mla_decode and mla_decode_multi use: H64.
+ * Values 2 and 3 named workgroups of 128 heads (each tile entering one CU
+ * once for all heads); they measured slower than H64 on every full-size bf16
+ * workload (with one 36 KB tile in flight per CU their stream is
+ * latency-bound under full load) and are retired: MLA_E_UNSUPPORTED. */
 typedef enum {
   MLA_KERNEL_AUTO = 0,
   MLA_KERNEL_H64 = 1,
-  MLA_KERNEL_H128 = 2,
-  MLA_KERNEL_H128_WS = 3,
   MLA_KERNEL_H64_BALANCED = 4
 } mla_decode_kernel_t;
 
 /* mla_decode_multi with the decode kernel chosen by the caller (`kernel`, an
- * mla_decode_kernel_t).  q_len = 1 is mla_decode.  MLA_KERNEL_H128 for a cache
- * or head count it does not cover returns MLA_E_UNSUPPORTED; an unknown
- * value MLA_E_ARG.  Other arguments, layouts and errors as mla_decode_multi. */
+ * mla_decode_kernel_t).  q_len = 1 is mla_decode.  A kernel for a cache or
+ * shape it does not cover returns MLA_E_UNSUPPORTED, as do the retired values
+ * 2 and 3; an unknown value MLA_E_ARG.  Other arguments, layouts and errors as mla_decode_multi. */
 mla_status_t mla_decode_ex(const mla_dims_t* dims, int32_t B, int32_t q_len, const void* q_abs,
                            int32_t q_abs_dt, const mla_cache_t* cache, int32_t num_splits,
                            void* u_part, int32_t part_dt, float* lse_part, int32_t kernel,

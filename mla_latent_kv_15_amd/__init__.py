@@ -477,7 +477,7 @@ def mla_decode_multi(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_split
                                 _stream(stream),), (d, cd), prepare)
 
 
-KERNEL_AUTO, KERNEL_H64, KERNEL_H128, KERNEL_H128_WS, KERNEL_H64_BALANCED = 0, 1, 2, 3, 4  # mla_decode_kernel_t
+KERNEL_AUTO, KERNEL_H64, KERNEL_H64_BALANCED = 0, 1, 4  # mla_decode_kernel_t (2, 3: retired)
 
 
 def mla_decode_ex(geo: Geometry, q_abs: torch.Tensor, cache: Cache, num_splits: int,

@@ -859,406 +859,6 @@ void stream_probe_kernel(const uint8_t* __restrict__ src, int tiles, int paired,
   if (threadIdx.x == 0) sink[blockIdx.x] = smem[wid & 1023];
 }
 
-// ================================================================ decode: 128-head tile layout
-//
-// The 12-wave decode below (one workgroup per 128 heads) reads each tile with
-// 32x32x16 QK operands, which take 32 rows of one chunk; its tile layout and
-// DMA plan follow.
-
-// calls f(std::integral_constant<int, I>) for I = 0..N-1
-template <int N, int I = 0, class F>
-__device__ inline void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
-// Tile layout of the 128-head kernel (measured with SQ_LDS_BANK_CONFLICT on
-// gfx950: neither of its two operand reads has bank conflicts).  Token t of a
-// 32-token tile, 16-byte chunk c of its row, sits at
-//   (t / 8) * 9216 + (c / 8) * 1024 + ((t % 8) ^ (t / 8 % 2)) * 128 + ((c % 8) ^ swzg(t)) * 16,
-// i.e. the token-group layout above with the row pairs of odd token groups
-// swapped: its 32x32x16 QK read takes 32 rows of one chunk, and rows t and
-// t + 8 would otherwise share banks (4 extra LDS cycles per read).
-
-// DMA plan of 32 rows in that layout: wave w moves token group w; lane
-// (k = lane / 8, j = lane % 8) writes slot j of row position k, i.e. token
-// 8w + (k ^ (w % 2)), chunk j ^ swzg(token % 8) of each 8-chunk group
-__device__ inline RowsDma rows_dma_plan_h128(const uint8_t* base, uint32_t lds_tile, int nvalid, int wave) {
-  int ln;  // volatile: recomputed per call rather than kept live across the loop
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-  const int tr = (ln >> 3) ^ (wave & 1), j = ln & 7;
-  const int t = 8 * wave + tr;
-  RowsDma d;
-  d.base = base;
-  d.off = static_cast<uint32_t>(((t < nvalid) ? t : 0) * kRowBytes + ((j ^ swzg(tr)) << 4));
-  d.m0 = lds_tile + wave * kTokGroupBytes;
-  return d;
-}
-
-constexpr int kH128 = 128;
-constexpr int kH128Steps = kRowElems / 16;  // 36 QK k-steps of 16
-
-// ================================================================ decode (128 heads, warp-specialised)
-//
-// bf16 caches with a multiple of 128 heads: one workgroup per (sequence b,
-// split range p, 128 heads), so each cached tile enters one CU once for all
-// of its heads (the 64-head kernel pulls every tile into two CUs, which caps
-// its unique cache stream at the L2-to-CU rate over two).  12 waves, three
-// per SIMD, in two roles:
-//   * QK waves 0..3 (head block w: 32 heads) hold their heads' 512 latent
-//     query elements in registers and read the 64 RoPE elements from LDS; per
-//     tile S[t][h] = 36 v_mfma_f32_32x32x16_bf16 (tile rows as A), so each
-//     lane owns one head and 16 of the 32 tokens: the softmax against the
-//     fixed reference maximum is lane-local (plus lane l ^ 32), and the bf16
-//     probabilities are published in LDS in the B-operand layout of the value
-//     product.  They also issue the tile DMA (9 one-KB instructions each).
-//   * PV waves 4..11 (column quarter q = (w - 4) % 4: 128 latent columns,
-//     head half (w - 4) / 4: 64 heads) accumulate U^T[128 columns][64 heads]
-//     in 8 blocks with v_mfma_f32_32x32x16_bf16, the tile read with the
-//     transposing reads of the 128-head layout (A) and the published
-//     probabilities (B).
-// One SIMD runs one QK and two PV waves: 1152 + 2 x 512 matrix-core clocks
-// per tile, while any one of them waits on LDS the others can issue.
-// Pipeline (one barrier per tile, 3 tile buffers): in iteration i the QK
-// waves issue the DMA of tile i+2 (into the buffer tile i-1 left), compute
-// QK + softmax of tile i+1 and publish P(i+1); the PV waves run the value
-// product of tile i with P(i); the DMA must land by the end of the iteration.
-// LDS: 3 x 36 KB tiles + 16 KB RoPE queries + 2 x 8 KB probabilities.
-
-constexpr int kW12Threads = 768;
-constexpr int kW12Buf = 3;
-constexpr int kW12P = kTileTokens * kH128 * 2;               // 8 KB of bf16 probabilities
-constexpr int kW12RegSteps = 26;                              // latent query k-steps in registers
-constexpr int kW12TailBytes = (kRowElems - 16 * kW12RegSteps) * 2;  // 320: the rest, per head
-// query tails [128 heads][336 B]: 16 bytes of padding per head put the 16 heads
-// a ds_read_b128 serves at banks 20h mod 64 (16 distinct 4-bank groups), i.e.
-// without conflicts
-constexpr int kW12TailStride = kW12TailBytes + 16;
-constexpr int kW12Qtail = kW12Buf * kTileBytes;
-constexpr int kW12POff = kW12Qtail + kH128 * kW12TailStride;
-constexpr int kW12XOff = kW12POff + kW12P;                    // votes, 1/l per head
-constexpr int kW12Smem = kW12XOff + 64 + kH128 * 4;
-
-template <int PART_DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kW12Threads, kW12Threads),
-                          amdgpu_waves_per_eu(3, 3)))
-void decode_w12_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kW12Smem];
-  int* votes = reinterpret_cast<int*>(smem + kW12XOff);
-  float* linv = reinterpret_cast<float*>(smem + kW12XOff + 64);
-
-  const int nwork = P.B * P.QL * P.S * P.HG;
-  const int wid = xcd_remap(blockIdx.x, nwork);
-  const int hg = wid % P.HG;
-  const int r1 = wid / P.HG;
-  const int qj = r1 % P.QL;
-  const int r2 = r1 / P.QL;
-  const int p = r2 % P.S;
-  const int b = r2 / P.S;
-  const int bj = b * P.QL + qj;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..11
-  const bool is_qk = wave < 4;                                // wave-uniform
-  const int hl = lane & 31, g = lane >> 5;
-
-  const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
-                        (P.QL - 1 - qj), 0);
-  const int t_begin = p * P.chunk;
-  const int t_end = min(t_begin + P.chunk, L);
-  const int64_t row_base = (static_cast<int64_t>(bj) * P.S_out + p) * P.H + hg * kH128;
-
-  if (t_begin >= t_end) {  // empty range: u = 0, lse = -inf (no barrier is reached)
-    for (int idx = tid; idx < kH128 * kDLatent; idx += kW12Threads)
-      store_elem<PART_DT>(P.u_part, row_base * kDLatent + idx, 0.0f);
-    if (tid < kH128) P.lse_part[row_base + tid] = -INFINITY;
-    return;
-  }
-  const int ntiles = (t_end - t_begin + kTileTokens - 1) / kTileTokens;
-  auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  uint8_t* pbuf = smem + kW12POff;
-  // Tile DMA, issued by the PV waves of head half 0 (wave 4 + g moves token
-  // group g, 9 one-KB instructions per tile): slot k goes into buffer k % 3;
-  // a slot past the range reloads the last tile's rows into a buffer no
-  // later tile of the range uses, so every iteration issues the same
-  // instructions and the wait counts stay exact
-  auto dma_plan = [&](int k) {
-    const int kc = min(k, ntiles - 1);
-    const int tt = t_begin + kc * kTileTokens;
-    const int64_t row0 = tile_row0(block_table, P.max_pages, P.seq_stride, P.paged != 0, b, tt);
-    return rows_dma_plan_h128(P.rows + row0 * kRowBytes, lds_addr(smem) + (k % kW12Buf) * kTileBytes,
-                              min(kTileTokens, t_end - tt), wave - 4);
-  };
-  auto dma = [&](int k) {
-    const RowsDma d = dma_plan(k);
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) rows_dma_issue(d, i);
-  };
-
-  // barrier sequence, the same in both roles:
-  //   per pass: T0 B_0 M_0 .. B_{n-1} M_{n-1} V1 V2  |  E1
-  if (is_qk) {
-    // ---------------------------------------------------------------- QK role
-    const int hw = hg * kH128 + wave * kHeadsPerWave;  // first head of this wave
-    // A operand: lane (token hl, half g) reads latent elements 16ks + 8g .. +7
-    // of token row hl (the 128-head tile layout)
-    const uint32_t qk_base = (hl >> 3) * kTokGroupBytes + ((hl & 7) ^ ((hl >> 3) & 1)) * 128;
-    const int qk_key = swzg(hl & 7);
-    auto ld_qk = [&](const uint8_t* T, int ks) {
-      return *reinterpret_cast<const bf16x8_t*>(T + qk_base + (ks >> 2) * 1024 +
-                                                (((2 * (ks & 3) + g) ^ qk_key) << 4));
-    };
-    // query tail (k-steps 26..35) of the B operand, from LDS: head h's 16-byte
-    // chunk c (elements 416 + 8c .. +7) at h * 336 + 16 c
-    const int hq = wave * kHeadsPerWave + hl;
-    const uint8_t* qt = smem + kW12Qtail + hq * kW12TailStride + 16 * g;
-    auto ld_qr = [&](int ks) {
-      return *reinterpret_cast<const bf16x8_t*>(qt + 32 * (ks - kW12RegSteps));
-    };
-
-    // queries: the first 26 k-steps to registers, the tails through
-    // registers to LDS (32 heads x 20 chunks, 10 per lane, in two batches)
-    const uint8_t* qw = static_cast<const uint8_t*>(P.q_abs) + (static_cast<int64_t>(bj) * P.H + hw) * kRowBytes;
-    bf16x8_t q[kW12RegSteps];
-    constexpr int kTailChunks = kW12TailBytes / 16;  // 20
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4_t t[5];
-#pragma unroll
-      for (int k = 0; k < 5; ++k) {
-        const int i = (5 * half + k) * 64 + lane, hr = i / kTailChunks, c = i % kTailChunks;
-        t[k] = *reinterpret_cast<const u32x4_t*>(qw + hr * kRowBytes + 32 * kW12RegSteps + 16 * c);
-      }
-#pragma unroll
-      for (int k = 0; k < 5; ++k) {
-        const int i = (5 * half + k) * 64 + lane, hr = i / kTailChunks, c = i % kTailChunks;
-        *reinterpret_cast<u32x4_t*>(smem + kW12Qtail + (wave * kHeadsPerWave + hr) * kW12TailStride + 16 * c) = t[k];
-      }
-    }
-    const uint8_t* qrow = qw + hl * kRowBytes + 16 * g;
-#pragma unroll
-    for (int ks = 0; ks < kW12RegSteps; ++ks) q[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * ks);
-
-    float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.0f;
-    auto tok0 = [&] {  // opaque, so the masks are not hoisted out of the loops
-      int t = 4 * g;
-      asm volatile("" : "+v"(t));
-      return t;
-    };
-    // QK of the tile in T into S; the 9 DMA instructions of slot `dslot` are
-    // spread over the first MFMAs (dslot < 0: none)
-    auto qk_tile = [&](const uint8_t* T, f32x16_t& S) {
-      constexpr int kR = 3;  // A-operand reads in flight
-      bf16x8_t ra[kR], rr[2];
-#pragma unroll
-      for (int k = 0; k < kR; ++k) ra[k] = ld_qk(T, k);
-      static_for<kH128Steps>([&](auto ST) {
-        constexpr int st = decltype(ST)::value;
-        // both operands of step st are taken before their ring slots are
-        // refilled with later steps
-        const bf16x8_t a = ra[st % kR];
-        const bf16x8_t bq = st < kW12RegSteps ? q[st < kW12RegSteps ? st : 0] : rr[st & 1];
-        if constexpr (st + kR < kH128Steps) ra[st % kR] = ld_qk(T, st + kR);
-        if constexpr (st + 2 >= kW12RegSteps && st + 2 < kH128Steps) rr[st & 1] = ld_qr(st + 2);
-        if constexpr (st == 0)
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, f32x16_t{}, 0, 0, 0);
-        else
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, S, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    };
-    // scores of `tile` -> probabilities relative to m_ref, published for the
-    // value product: k-step j of head block `wave` gets registers 8j..8j+7
-    auto softmax_publish = [&](f32x16_t& S, int tile, int& overflow, uint8_t* PB) {
-      const int nvalid = t_end - (t_begin + tile * kTileTokens);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] *= P.scale_log2;
-      if (nvalid < kTileTokens) {
-        const int t0 = tok0();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = (t0 + 8 * (r >> 2) + (r & 3) < nvalid) ? S[r] : -INFINITY;
-      }
-      float mx = S[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-      m_seen = fmaxf(m_seen, mx);
-      overflow |= (mx > m_ref + kRefSlack);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(S[8 * j + 2 * e] - m_ref);
-          const float p1 = __builtin_amdgcn_exp2f(S[8 * j + 2 * e + 1] - m_ref);
-          l_run += p0;
-          l_run += p1;
-          w[e] = pack_bf16x2(p0, p1);
-        }
-        *reinterpret_cast<u32x4_t*>(PB + ((j * 4 + wave) * 64 + lane) * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
-      }
-    };
-
-    for (int pass = 0; pass < 2; ++pass) {
-      barrier();  // T0: tile 0 landed (and the query tails are in LDS)
-      f32x16_t S;
-      qk_tile(smem, S);
-      if (pass == 0) {  // reference: maximum of the first tile, both lane halves
-        const int nvalid = t_end - t_begin;
-        const int t0 = tok0();
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (t0 + 8 * (r >> 2) + (r & 3) < nvalid) mx = fmaxf(mx, S[r] * P.scale_log2);
-        m_ref = fmaxf(mx, __shfl_xor(mx, 32));
-      }
-      l_run = 0.0f;
-      int overflow = 0;
-      softmax_publish(S, 0, overflow, pbuf);
-      for (int i = 0; i < ntiles; ++i) {
-        barrier();  // B_i: P(i) published; tile i+1 landed; tile i-1's buffer released
-        if (i + 1 < ntiles) qk_tile(smem + ((i + 1) % kW12Buf) * kTileBytes, S);
-        barrier();  // M_i: the PV waves hold P(i) in registers
-        if (i + 1 < ntiles) softmax_publish(S, i + 1, overflow, pbuf);
-      }
-      const int vote = __any(overflow) ? 1 : 0;  // all lanes, outside the store's branch
-      if (lane == 0) votes[wave] = vote;
-      barrier();  // V1
-      int again = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) again |= votes[w];
-      barrier();  // V2
-      if (!again) break;
-      m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // redo with the range maximum
-    }
-    l_run += __shfl_xor(l_run, 32);
-    if (g == 0) {
-      P.lse_part[row_base + wave * kHeadsPerWave + hl] = (m_ref + log2f(l_run)) * kLn2;
-      linv[wave * kHeadsPerWave + hl] = 1.0f / l_run;
-    }
-    barrier();  // E1
-    return;
-  }
-
-  // ------------------------------------------------------------------ PV role
-  const int pw = wave - 4;
-  const int cq = pw & 3, hh = pw >> 2;  // columns 128 cq .. +127, heads 64 hh .. +63
-  // transposing reads of the 128-head layout (tokens of half j, 32 columns of
-  // block cb): the token order of the QK accumulator's registers
-  const int G = lane >> 4, e = (lane >> 2) & 3, q4 = lane & 3;
-  const int tr_row = 4 * (G >> 1) + e;
-  const int tr_key = swzg(tr_row);
-  const int tr_x = 2 * (G & 1) + (q4 >> 1);
-  const uint32_t tr_lo = tr_row * 128 + 8 * (q4 & 1);
-  const uint32_t tr_hi = kTokGroupBytes + (tr_row ^ 1) * 128 + 8 * (q4 & 1);
-  const uint32_t tr_off[2] = {static_cast<uint32_t>(((0 + tr_x) ^ tr_key) << 4),
-                              static_cast<uint32_t>(((4 + tr_x) ^ tr_key) << 4)};
-  auto ld_pv = [&](const uint8_t* T, int j, int cb) {
-    const uint8_t* ptr = T + tr_off[cb & 1] + (cb >> 1) * 1024 + 2 * j * kTokGroupBytes;
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + tr_lo));
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(ptr + tr_hi));
-    return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  };
-  f32x16_t acc[4][2];
-  auto zero_acc = [&] {
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cb][hb][r] = 0.0f;
-  };
-  // the value product of the tile in T with P held in registers: 8 steps
-  // (token half j, column block cb), two MFMAs each (the head blocks)
-  auto pv_tile = [&](const uint8_t* T, const bf16x8_t (&pb)[2][2]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8_t a[2];
-      a[0] = ld_pv(T, j, 4 * cq);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if (cb + 1 < 4) a[(cb + 1) & 1] = ld_pv(T, j, 4 * cq + cb + 1);
-        acc[cb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb & 1], pb[j][0], acc[cb][0], 0, 0, 0);
-        acc[cb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cb & 1], pb[j][1], acc[cb][1], 0, 0, 0);
-      }
-    }
-  };
-  const bool dmaw = hh == 0;  // wave-uniform: this wave moves token group cq of every tile
-  for (int pass = 0; pass < 2; ++pass) {
-    zero_acc();
-    if (dmaw) {
-      dma(0);
-      dma(1);
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0 landed; tile 1 in flight
-    }
-    barrier();  // T0
-    for (int i = 0; i < ntiles; ++i) {
-      if (dmaw) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile i+1 landed
-      barrier();  // B_i
-      bf16x8_t pb[2][2];  // P(i): token half j, head block 2 hh + hb
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          pb[j][hb] = *reinterpret_cast<const bf16x8_t*>(pbuf + ((j * 4 + 2 * hh + hb) * 64 + lane) * 16);
-      if (dmaw) dma(i + 2);
-      pv_tile(smem + (i % kW12Buf) * kTileBytes, pb);
-      barrier();  // M_i
-    }
-    if (dmaw) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the slots issued past the range
-    if (lane == 0) votes[wave] = 0;
-    barrier();  // V1
-    int again = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) again |= votes[w];
-    barrier();  // V2
-    if (!again) break;
-  }
-  barrier();  // E1: 1/l of every head in LDS
-  // U^T register r of block (cb, hb) in lane (hl, g): column 128 cq + 32 cb +
-  // 8 (r/4) + 4 g + r%4 of head 64 hh + 32 hb + hl.  Each wave stages one head
-  // block (32 rows x 128 columns) at a time in its own LDS region (the tile
-  // buffers are free) and writes 256 contiguous bytes per row and instruction.
-  constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
-  constexpr int kColsRound = 256 / kEsz;             // 128 bf16 / 64 fp32 columns
-  constexpr int kStageRow = kColsRound * kEsz + 16;  // padded: rows start 4 banks apart
-  uint8_t* W = smem + pw * kHeadsPerWave * kStageRow;
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const float inv = linv[64 * hh + 32 * hb + hl];
-#pragma unroll
-    for (int half = 0; half < 128 / kColsRound; ++half) {
-#pragma unroll
-      for (int cb2 = 0; cb2 < kColsRound / 32; ++cb2) {
-        const int cb = half * (kColsRound / 32) + cb2;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int c = 32 * cb2 + 8 * r4 + 4 * g;
-          const f32x16_t& A = acc[cb][hb];
-          const float v0 = A[4 * r4 + 0] * inv, v1 = A[4 * r4 + 1] * inv;
-          const float v2 = A[4 * r4 + 2] * inv, v3 = A[4 * r4 + 3] * inv;
-          uint8_t* wp = W + hl * kStageRow + c * kEsz;
-          if constexpr (PART_DT == MLA_F32)
-            *reinterpret_cast<f32x4_t*>(wp) = f32x4_t{v0, v1, v2, v3};
-          else
-            *reinterpret_cast<u32x2_t*>(wp) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        }
-      }
-      asm volatile("" ::: "memory");  // one wave's LDS operations complete in order
-      uint8_t* dst = static_cast<uint8_t*>(P.u_part) +
-                     ((row_base + 64 * hh + 32 * hb) * kDLatent + 128 * cq) * kEsz + half * (kColsRound * kEsz);
-#pragma unroll
-      for (int i = 0; i < kHeadsPerWave / 4; ++i) {
-        const int row = 4 * i + (lane >> 4);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + row * kStageRow + (lane & 15) * 16);
-        *reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(row) * (kDLatent * kEsz) + (lane & 15) * 16) = v;
-      }
-      asm volatile("" ::: "memory");
-    }
-  }
-}
-
 // ================================================================ decode (fp32)
 //
 // Plain fp32 path for fp32 caches: one workgroup per (b, split, head), 256
@@ -2681,12 +2281,12 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
   const int32_t chunk = max(split_chunk(span, num_splits), kTileTokens);
   const float scale = effective_scale(dims);
   if (cache->ring && q_len != 1) return MLA_E_UNSUPPORTED;
-  if (kernel != MLA_KERNEL_AUTO && kernel != MLA_KERNEL_H64 && kernel != MLA_KERNEL_H128 &&
-      kernel != MLA_KERNEL_H128_WS && kernel != MLA_KERNEL_H64_BALANCED)
+  // values 2 and 3 named the retired 128-head workgroups
+  if (kernel == 2 || kernel == 3) return MLA_E_UNSUPPORTED;
+  if (kernel != MLA_KERNEL_AUTO && kernel != MLA_KERNEL_H64 && kernel != MLA_KERNEL_H64_BALANCED)
     return MLA_E_ARG;
   if (cache->dtype == MLA_F32) {
-    if (q_len != 1 || kernel == MLA_KERNEL_H128 || kernel == MLA_KERNEL_H64_BALANCED)
-      return MLA_E_UNSUPPORTED;
+    if (q_len != 1 || kernel == MLA_KERNEL_H64_BALANCED) return MLA_E_UNSUPPORTED;
     DecodeF32Params P{static_cast<const float*>(q_abs), static_cast<const float*>(cache->rows),
                       cache->block_table, cache->seq_lens, cache->seq_stride, cache->max_pages,
                       cache->page_size != 0, B, H, num_splits, chunk, cache->max_seq_len, scale,
@@ -2719,20 +2319,6 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
                  cache->page_size != 0, B, H, num_splits, HG64, chunk, cache->max_seq_len,
                  q_len, scale * kLog2e, u_part, lse_part, cache->ring, nullptr, num_splits};
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
-  const bool h128_ok = !fp8 && H % kH128 == 0;
-  const int64_t nblk = static_cast<int64_t>(B) * q_len * num_splits * (H / kH128);
-  if ((kernel == MLA_KERNEL_H128 || kernel == MLA_KERNEL_H128_WS) && !h128_ok) return MLA_E_UNSUPPORTED;
-  // bf16 cache: 12-wave workgroups of 128 heads (MLA_KERNEL_H128 names the same
-  // decomposition)
-  if (kernel == MLA_KERNEL_H128_WS || kernel == MLA_KERNEL_H128) {
-    P.HG = H / kH128;
-    if (nblk > 0x7FFFFFFF) return MLA_E_SHAPE;
-    if (part_dt == MLA_F32)
-      decode_w12_kernel<MLA_F32><<<static_cast<unsigned>(nblk), kW12Threads, 0, s>>>(P, cache->block_table);
-    else
-      decode_w12_kernel<MLA_BF16><<<static_cast<unsigned>(nblk), kW12Threads, 0, s>>>(P, cache->block_table);
-    return launch_status();
-  }
   // balanced partition (bf16 cache): one worker of HG64 workgroups per two
   // CUs' worth of 64-head workgroups (256 workgroups of 64 heads in all, one
   // per CU), each taking an equal share of the batch's tiles

@@ -263,7 +263,7 @@ def test_decode_multi_validation():
 
 def test_decode_ex_kernel_choice_validation():
     """mla_decode_ex: the kernel argument is checked on the host before any
-    launch; the 128-head kernel covers bf16 caches with h a multiple of 128."""
+    launch; the balanced partition's limits, the retired values, unknown ones."""
     L = mla.lib()
 
     def dx(kernel, h=128, c=None, B=2, ql=1, S=4):
@@ -271,7 +271,7 @@ def test_decode_ex_kernel_choice_validation():
         return L.mla_decode_ex(C.byref(dims(h=h)), B, ql, P, BF16, C.byref(c), S, P, BF16, P,
                                kernel, None)
 
-    assert dx(mla.KERNEL_H128, B=0) == OK
+    assert dx(mla.KERNEL_H64, B=0) == OK
     assert dx(5) == E_ARG
     # the balanced partition: bf16 cache, at least 2 splits, at most 512 rows
     BAL = mla.KERNEL_H64_BALANCED
@@ -281,11 +281,9 @@ def test_decode_ex_kernel_choice_validation():
     assert dx(BAL, B=128, ql=5) == E_UNSUP
     assert dx(BAL, B=0) == OK
     assert dx(-1) == E_ARG
-    assert dx(mla.KERNEL_H128_WS, h=64) == E_UNSUP
-    assert dx(mla.KERNEL_H128_WS, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP
-    assert dx(mla.KERNEL_H128, h=64) == E_UNSUP
-    assert dx(mla.KERNEL_H128, h=160) == E_UNSUP
-    assert dx(mla.KERNEL_H128, c=cache(dtype=FP8, row_scale=P)) == E_UNSUP
+    # values 2 and 3: the retired 128-head workgroups
+    assert dx(2) == E_UNSUP
+    assert dx(3) == E_UNSUP
     assert dx(mla.KERNEL_H64, ql=0) == E_ARG
     assert dx(mla.KERNEL_H64, ql=17) == E_ARG
 

@@ -37,7 +37,7 @@ def test_counter_record_applies_only_to_its_source_and_launch(monkeypatch, tmp_p
     monkeypatch.setattr(bench, "source_hash", lambda: "1" * 16)
     assert bench.stored_counters(a)["hbm_bytes_per_launch"] == 7.0
     assert bench.stored_counters(b)["hbm_bytes_per_launch"] == 9.0
-    assert bench.stored_counters(dict(a, decode_kernel="h128")) is None
+    assert bench.stored_counters(dict(a, decode_kernel="h64")) is None
     assert bench.stored_counters(dict(a, splits=16)) is None
     monkeypatch.setattr(bench, "source_hash", lambda: "0" * 16)
     assert bench.stored_counters(a) is None

@@ -30,9 +30,9 @@ def _bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-AUTO, H128, W12 = mla.KERNEL_AUTO, mla.KERNEL_H128, mla.KERNEL_H128_WS
+AUTO, H64 = mla.KERNEL_AUTO, mla.KERNEL_H64
 CASES = [("dsv2_b32_l2k", 2, 3, AUTO), ("dsv2_b32_l2k", 4, 1, AUTO), ("paged_b64_ragged", 3, 4, AUTO),
-         ("fp8_b1_l128k", 4, 3, AUTO), ("dsv2_b32_l2k", 2, 3, H128), ("paged_b64_ragged", 3, 4, H128), ("dsv2_b32_l2k", 4, 3, W12), ("paged_b64_ragged", 2, 4, W12),
+         ("fp8_b1_l128k", 4, 3, AUTO), ("dsv2_b32_l2k", 4, 3, H64), ("paged_b64_ragged", 2, 4, H64),
          ("dsv2_b32_l2k", 16, 2, AUTO)]  # the largest q_len the ABI takes
 
 

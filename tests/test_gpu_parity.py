@@ -47,16 +47,17 @@ def test_tiny_f32_every_output(splits):
 RAGGED = [0, 1, 31, 32, 45, 300, 257]
 
 
-H64, H128, W12 = mla.KERNEL_H64, mla.KERNEL_H128, mla.KERNEL_H128_WS
+H64, BAL = mla.KERNEL_H64, mla.KERNEL_H64_BALANCED
+# the balanced partition takes 2 splits or more
+RAGGED_CASES = ([(h, H64, s) for h in (32, 128, 160, 256) for s in (1, 3, 7)] +
+                [(h, BAL, s) for h in (32, 128, 160, 256) for s in (3, 7)])
 
 
-@pytest.mark.parametrize("heads,kernel", [(32, H64), (128, H64), (128, H128), (160, H64),
-                                          (256, H64), (256, H128), (128, W12), (256, W12)])
-@pytest.mark.parametrize("splits", [1, 3, 7])
+@pytest.mark.parametrize("heads,kernel,splits", RAGGED_CASES)
 def test_ragged_bf16(heads, kernel, splits):
     """bf16, several tiles plus ragged tails, empty and 1-token sequences, on
-    both decode kernels: a partial head group (160 = 128 + 32), waves without
-    heads (32), two head groups of either kernel (256)."""
+    the fixed split ranges and on the balanced partition: a partial head group
+    (160 = 128 + 32), waves without heads (32), several head groups (256)."""
     wl = synth.workload("dsv2_b32_l2k").with_(batch=len(RAGGED), heads=heads, seq_len=None,
                                              seed=synth.workloads.BASE_SEED + 101)
     dev = DeviceInputs(synth.make_inputs(wl, lengths=RAGGED))
@@ -67,7 +68,7 @@ def test_ragged_bf16(heads, kernel, splits):
     _log(f"  err o/u/lse = {e}")
 
 
-@pytest.mark.parametrize("kernel", [H64, H128, W12])
+@pytest.mark.parametrize("kernel", [H64, BAL])
 @pytest.mark.parametrize("part", ["f32", "bf16"])
 def test_ragged_fp32_partials(part, kernel):
     """The same bf16 problem with fp32 or bf16 split partials."""
@@ -122,7 +123,7 @@ def test_fp8_codes_exact():
         assert np.array_equal(got, np.broadcast_to(want[b], got.shape)), b
 
 
-@pytest.mark.parametrize("kernel", [H64, H128, W12])
+@pytest.mark.parametrize("kernel", [H64, BAL])
 def test_paged_matches_contiguous_bitwise(kernel):
     """The same tokens in a shuffled paged pool and in contiguous rows give
     bit-identical partials (the tiles see the same rows in the same order)."""
@@ -140,7 +141,7 @@ def test_paged_matches_contiguous_bitwise(kernel):
     check_against_oracle(paged, a, pairs, TOL["bf16"])
 
 
-@pytest.mark.parametrize("kernel", [H64, H128, W12])
+@pytest.mark.parametrize("kernel", [H64, BAL])
 def test_split_count_invariance(kernel):
     """Different split counts give the same result.  With a zero query every
     score is 0, so every probability is exactly 1 in bf16 and u is the plain
@@ -153,7 +154,8 @@ def test_split_count_invariance(kernel):
     dev.q_nope.zero_()
     dev.q_rope.zero_()
     f32 = torch.float32
-    ref = run_step(dev, 1, part_dtype=f32, out_dtype=f32, kernel=kernel)
+    # one split (the balanced partition takes 2 or more: the fixed ranges' result)
+    ref = run_step(dev, 1, part_dtype=f32, out_dtype=f32, kernel=H64)
     ref_u = ref.u.clone()
     # u equals the column mean of the cached latents
     rows = dev.cache.rows.float()
@@ -182,7 +184,7 @@ def test_split_count_random_inputs():
         assert err < 1e-2, (s, err)
 
 
-@pytest.mark.parametrize("kernel", [H64, H128, W12])
+@pytest.mark.parametrize("kernel", [H64, BAL])
 def test_max_splits(kernel):
     """The largest split count the ABI takes (1024): 64-token ranges over a
     40,000-token sequence, most ranges of the short and the empty sequence
@@ -198,8 +200,7 @@ def test_max_splits(kernel):
     _log(f"  err o/u/lse = {e}")
 
 
-SPIKE_CASES = [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("dsv2_b32_l2k", W12),
-               ("fp8_b1_l128k", H64)]
+SPIKE_CASES = [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", BAL), ("fp8_b1_l128k", H64)]
 
 
 @pytest.mark.parametrize("name,kernel", SPIKE_CASES)
@@ -231,15 +232,14 @@ def test_score_spike_recomputes_range(name, kernel):
     dev = DeviceInputs(inp)
     _log(f"score spike {name} kernel={kernel}")
     kind = "fp8" if wl.cache_dtype == "fp8" else "bf16"
-    for splits in (1, 3):
+    for splits in ((3,) if kernel == BAL else (1, 3)):
         step = run_step(dev, splits, kernel=kernel)
         pairs = [(b, h) for b in range(len(lens)) for h in (0, 1, 77, 127)]
         e = check_against_oracle(dev, step, pairs, TOL[kind])
         _log(f"  S={splits}: err o/u/lse = {e}")
 
 
-@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("dsv2_b32_l2k", W12),
-                                         ("tiny_f32", H64)])
+@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", BAL), ("tiny_f32", H64)])
 def test_custom_softmax_scale(name, kernel):
     """A caller-given softmax scale (0.05) replaces 1/sqrt(d_nope + d_rope)."""
     wl = synth.workload(name).with_(batch=3, seq_len=None, seed=synth.workloads.BASE_SEED + 110)
@@ -256,8 +256,7 @@ def test_custom_softmax_scale(name, kernel):
     assert np.abs(np.array([lse[b, h] for b, h in pairs]) - lse_ref).max() <= TOL[kind]
 
 
-@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", H128), ("dsv2_b32_l2k", W12),
-                                         ("fp8_b1_l128k", H64)])
+@pytest.mark.parametrize("name,kernel", [("dsv2_b32_l2k", H64), ("dsv2_b32_l2k", BAL), ("fp8_b1_l128k", H64)])
 def test_nan_in_a_read_row_propagates(name, kernel):
     """A NaN in a cached row that is attended (a bf16 NaN, or the E4M3 NaN
     code) makes every output of that sequence NaN (o, u, lse), with one range
@@ -268,7 +267,7 @@ def test_nan_in_a_read_row_propagates(name, kernel):
     # sequence 0, token 150, latent element 3
     inp.rows[150, 3] = 0x7F if wl.cache_dtype == "fp8" else 0x7FC0
     dev = DeviceInputs(inp)
-    for splits in (1, 3):
+    for splits in ((3,) if kernel == BAL else (1, 3)):
         step = run_step(dev, splits, kernel=kernel)
         o = step.o.float().cpu().numpy()
         u = step.u.float().cpu().numpy()
@@ -288,7 +287,7 @@ def test_nan_in_a_read_row_propagates(name, kernel):
         assert np.abs(got - o_ref).max() <= tol * np.abs(o_ref).max()
 
 
-@pytest.mark.parametrize("kernel", [H64, H128, W12])
+@pytest.mark.parametrize("kernel", [H64, BAL])
 def test_large_batch_of_short_sequences(kernel):
     """300 sequences of 0-120 tokens: many 32-sequence tiles in the absorb (the
     staged query rows are replaced tile after tile), many merge workgroups,
@@ -317,7 +316,6 @@ def test_repeat_is_deterministic():
 # ---------------------------------------------------------------- full sizes
 
 AUTO = mla.KERNEL_AUTO
-BAL = mla.KERNEL_H64_BALANCED
 F8Q = "fp8 query"  # mla.KERNEL_AUTO with the E4M3 absorbed query
 # (workload, tolerance kind, sequences x heads sampled, kernel, parts): the
 # sampled sequences are spread from the first to the last (both ends of the
@@ -325,10 +323,7 @@ F8Q = "fp8 query"  # mla.KERNEL_AUTO with the E4M3 absorbed query
 # oracle run is long is checked in parts, one test each, on the same run
 FULL = [
     ("dsv2_b32_l2k", "bf16", 8, 8, AUTO, 1),
-    ("dsv2_b32_l2k", "bf16", 4, 4, H128, 1),
-    ("dsv2_b32_l2k", "bf16", 8, 8, W12, 1),
-    ("long_b4_l32k", "bf16", 4, 8, W12, 1),
-    ("paged_b64_ragged", "bf16", 8, 8, W12, 2),
+    ("dsv2_b32_l2k", "bf16", 8, 8, BAL, 1),
     ("long_b4_l32k", "bf16", 4, 8, AUTO, 1),
     ("long_b4_l32k", "bf16", 4, 3, H64, 1),
     ("paged_b64_ragged", "bf16", 8, 8, AUTO, 2),
@@ -380,14 +375,14 @@ def test_full_size_sampled(name, kind, nb, nh, kernel, part, parts):
 
 
 def test_full_size_paged_kernels_agree_on_every_output():
-    """The paged ragged workload at full size: the 64-head and the 128-head
-    decode kernels (separate code, separate work decompositions) and the
+    """The paged ragged workload at full size: the fixed split ranges at the
+    workload's split count and at 8 (separate work decompositions) and the
     balanced partition give the same o, u and lse for all 64 x 128 (b, h)
     pairs within the bf16 tolerance."""
     wl = synth.workload("paged_b64_ragged")
     dev, a = _full_run("paged_b64_ragged", AUTO)
     o_a, u_a, l_a = a.o.float().clone(), a.u.float().clone(), a.lse.clone()
-    b = run_step(dev, wl.num_splits, kernel=H128)
+    b = run_step(dev, 8, kernel=H64)
     for x, y, what in ((o_a, b.o.float(), "o"), (u_a, b.u.float(), "u")):
         err = ((x - y).abs().max() / y.abs().max()).item()
         _log(f"  {what}: max rel diff {err:.2e}")
