@@ -30,10 +30,10 @@ HIPFLAGS = [
 # no VGPR spill and no scratch for them.  The balanced-partition instances of
 # decode_ws_kernel (template argument BAL = true) carry their piece loop's
 # values across each piece and are allowed a few spill slots, reloaded at
-# piece boundaries (BALANCED_MAX_VGPR_SPILLS); the 12-wave 128-head kernel,
-# an option of mla_decode_ex, has a few spills and is not checked.
+# piece boundaries (BALANCED_MAX_VGPR_SPILLS; the fp32-partial instance
+# spills 4, the bf16 one none).
 COUNTED_WAIT_KERNELS = ("decode_ws_kernel", "decode_f8q_kernel")
-BALANCED_MAX_VGPR_SPILLS = 16
+BALANCED_MAX_VGPR_SPILLS = 8
 
 
 def resource_usage(remarks: str) -> dict:

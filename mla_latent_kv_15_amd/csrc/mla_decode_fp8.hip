@@ -143,15 +143,14 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
   // consecutive ranges that the host merged count as one), the head groups and
   // query tokens of one range adjacent (same XCD: they share each tile through
   // L2)
-  const int NG = P.S;
-  const int nwork = P.B * P.QL * NG * P.HG;
+  const int nwork = P.B * P.QL * P.S * P.HG;
   const int wid = xcd_remap(blockIdx.x, nwork);
   const int hg = wid % P.HG;
   const int r1 = wid / P.HG;
   const int qj = r1 % P.QL;
   const int r2 = r1 / P.QL;
-  const int grp = r2 % NG;
-  const int b = r2 / NG;
+  const int p = r2 % P.S;  // the split (a range the host merged from several is one)
+  const int b = r2 / P.S;
   const int bj = b * P.QL + qj;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,40 +162,34 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
 
   const int L = max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) -
                         (P.QL - 1 - qj), 0);
-  // the workgroup's ranges p_first .. p_end - 1 cover tokens [T0, T1): K
-  // consecutive 64-token tiles (every range is a whole number ntf of tiles),
-  // one pipeline through all of them; ranges from p_live on hold no token
-  const int p_first = grp, p_end = grp + 1;
-  const int T0 = p_first * P.chunk;
-  const int T1 = min(p_end * P.chunk, L);
+  // the workgroup's range covers tokens [T0, T1): K consecutive 64-token tiles
+  const int T0 = p * P.chunk;
+  const int T1 = min((p + 1) * P.chunk, L);
   const int K = T1 > T0 ? (T1 - T0 + kF8Tok - 1) / kF8Tok : 0;
-  const int ntf = P.chunk / kF8Tok;
-  const int p_live = K > 0 ? p_first + (K - 1) / ntf + 1 : p_first;
-  auto row_base = [&](int p) { return (static_cast<int64_t>(bj) * P.S_out + p) * P.H + hbase; };
+  const int k0 = 0, k1 = K;  // the range's tiles
+  auto row_base = [&](int sp) { return (static_cast<int64_t>(bj) * P.S_out + sp) * P.H + hbase; };
 
-  // ranges without tokens (PV waves): lse = -inf, and u = 0 unless lse_only
+  // splits without tokens (PV waves): lse = -inf, and u = 0 unless lse_only
   // (the slots past merged range groups: mla_combine does not read the u of a
   // split with lse = -inf)
-  auto write_empty = [&](int p, bool lse_only = false) {
+  auto write_empty = [&](int sp, bool lse_only = false) {
     const int pt = tid - 256;
     if (!lse_only)
       for (int idx = pt; idx < nhb * kHeadsPerWave * kDLatent; idx += 256)
-        store_elem<PART_DT>(P.u_part, row_base(p) * kDLatent + idx, 0.0f);
-    if (pt < nhb * kHeadsPerWave) P.lse_part[row_base(p) + pt] = -INFINITY;
+        store_elem<PART_DT>(P.u_part, row_base(sp) * kDLatent + idx, 0.0f);
+    if (pt < nhb * kHeadsPerWave) P.lse_part[row_base(sp) + pt] = -INFINITY;
   };
   // the workgroup of the last range also marks the slots past the ranges
-  if (!is_qk && p_end == P.S)
-    for (int p = P.S; p < P.S_out; ++p) write_empty(p, true);
+  if (!is_qk && p + 1 == P.S)
+    for (int q = P.S; q < P.S_out; ++q) write_empty(q, true);
   if (K == 0) {
-    if (!is_qk)
-      for (int p = p_first; p < p_end; ++p) write_empty(p);
+    if (!is_qk) write_empty(p);
     return;
   }
 
   // s_barriers, issued by both roles in the same order:
-  //   Q1 Q2 T0 | per range: [pass 0: AM AM] B_k0 .. B_k1-1 V1 V2
-  //   [redo: AM AM T0 B_k0 .. B_k1-1 V1 V2] E1 E2
-  // E2 of a range also certifies that the next range's first tile landed.
+  //   Q1 Q2 T0 | [pass 0: AM AM] B_0 .. B_K-1 V1 V2
+  //   [redo: AM AM T0 B_0 .. B_K-1 V1 V2] E1 E2
   auto barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   if (is_qk) {
@@ -338,10 +331,8 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
     };
 
     barrier();  // T0: the first tile landed
-    for (int p = p_first; p < p_live; ++p) {
-      const int k0 = (p - p_first) * ntf, k1 = min(k0 + ntf, K);
-      const int te = min((p + 1) * P.chunk, L);  // the range's end
-      auto nvalid = [&](int k) { return te - (T0 + k * kF8Tok); };
+    {
+      auto nvalid = [&](int k) { return T1 - (T0 + k * kF8Tok); };
       m_ref = -INFINITY;
       m_seen = -INFINITY;
       for (int pass = 0; pass < 2; ++pass) {
@@ -529,8 +520,7 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
   wait_tile(0);
   barrier();  // T0
 
-  for (int p = p_first; p < p_live; ++p) {
-    const int k0 = (p - p_first) * ntf, k1 = min(k0 + ntf, K);
+  {
     for (int pass = 0; pass < 2; ++pass) {
       zero_acc();
       if (pass > 0) {  // the range again: its first tiles back into the buffers
@@ -576,7 +566,6 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
       barrier();  // AM
       barrier();  // AM
     }
-    if (k1 < K) wait_tile(k1);  // E2 certifies the next range's first tile
     barrier();  // E1
     barrier();  // E2: linv ready
     // matrix-core accumulator writes -> VALU reads
@@ -584,8 +573,8 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
     // U^T register r of block (hb, cbl) in lane (hl, g) is column
     // 128 rw + 32 cbl + 8 (r / 4) + 4 g + r % 4 of head hbase + 32 hb + hl;
     // each wave stages one head block (32 rows x 128 columns) at a time in its
-    // own region of the range's last tile buffer (free: its next tile is
-    // loaded only after B_k1) and writes 256 contiguous bytes per row.
+    // own region of the range's last tile buffer (free: no tile is loaded
+    // after it) and writes 256 contiguous bytes per row.
     constexpr int kEsz = PART_DT == MLA_F32 ? 4 : 2;
     constexpr int kColsRound = 256 / kEsz;
     constexpr int kStageRow = kColsRound * kEsz + 16;
@@ -634,7 +623,6 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
       }
     }
   }
-  for (int p = p_live; p < p_end; ++p) write_empty(p);
 }
 
 }  // namespace

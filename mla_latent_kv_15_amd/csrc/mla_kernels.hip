@@ -128,34 +128,26 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     return max(attended_len(P.seq_lens, b, P.max_seq_len, P.ring, P.seq_stride) - (P.QL - 1 - qj), 0);
   };
 
-  // One unit of work: row bj's split ranges p_first .. p_end - 1, covering
-  // tokens [T0, T1) of its attended ones as K consecutive 32-token tiles
-  // (every range but the last a whole number ntf of tiles), one pipeline
-  // through all of them; ranges from p_live on hold no token.
-  auto unit = [&](const int bj, const int p_first, const int p_end, const int T0, const int T1,
-                  const int ntf, const int lane, const int tid) {
+  // One unit of work: split p of row bj, tokens [T0, T1) of its attended ones
+  // as K consecutive 32-token tiles (a range the host merged from several
+  // split ranges is one range here).
+  auto unit = [&](const int bj, const int p, const int T0, const int T1, const int lane,
+                  const int tid) {
   const int b = bj / P.QL;
   const int K = T1 > T0 ? (T1 - T0 + kTileTokens - 1) / kTileTokens : 0;
-  const int p_live = K > 0 ? (FP8 ? p_first + 1 : p_first + (K - 1) / ntf + 1) : p_first;
-  auto row_base_of = [&](int p) { return row_base(bj, p); };
   if (K == 0) {
-    for (int p = p_first; p < p_end; ++p) write_empty(bj, p);
+    write_empty(bj, p);
     return;
   }
-  // fp8 (one range): the PV loop runs in pairs of tiles (one register set
-  // each), so an odd range gets one more tile: it is loaded from the range's
-  // first rows and all of its tokens are masked, which adds exact zeros
+  // fp8: the PV loop runs in pairs of tiles (one register set each), so an
+  // odd range gets one more tile: it is loaded from the range's first rows
+  // and all of its tokens are masked, which adds exact zeros
   const int ntp = FP8 ? ((K + 1) & ~1) : K;
-  // tiles k0 .. k1 - 1 of the workgroup belong to range p
-  auto range_tiles = [&](int p, int& k0, int& k1) {
-    k0 = (p - p_first) * ntf;
-    k1 = FP8 ? ntp : min(k0 + ntf, K);
-  };
+  const int k1 = ntp;  // the range's tiles 0 .. k1 - 1
 
   // all s_barriers below are issued by both roles in the same order:
-  //   Q1 Q2 T0 | per range: [pass 0: AM AM] B_k0..B_k1-1 V1 V2
-  //   [redo: AM AM T0 B_k0..B_k1-1 V1 V2] E1 E2
-  // E2 of a range also certifies that the next range's first tile landed.
+  //   Q1 Q2 T0 | [pass 0: AM AM] B_0..B_k1-1 V1 V2
+  //   [redo: AM AM T0 B_0..B_k1-1 V1 V2] E1 E2
 
   if (is_qk) {
     // ------------------------------------------------------------ QK role
@@ -288,11 +280,9 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     };
 
     barrier();  // T0: the first tile landed
-    for (int p = p_first; p < p_live; ++p) {
-      int k0, k1;
-      range_tiles(p, k0, k1);
-      const int te = min(T0 + (p - p_first + 1) * ntf * kTileTokens, T1);  // the range's end
-      auto nvalid = [&](int k) { return te - (T0 + k * kTileTokens); };
+    {
+      const int k0 = 0;
+      auto nvalid = [&](int k) { return T1 - (T0 + k * kTileTokens); };
       m_ref[0] = m_ref[1] = m_seen[0] = m_seen[1] = -INFINITY;
       for (int pass = 0; pass < 2; ++pass) {
         l_run[0] = l_run[1] = 0.0f;
@@ -360,7 +350,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
           const int hx = qhb * 32 + 16 * hh + n16;
           const float l_tot = xch[hx] + xch[64 + hx];
           linv[hx] = 1.0f / l_tot;
-          P.lse_part[row_base_of(p) + hx] = (m_ref[hh] + log2f(l_tot)) * kLn2;
+          P.lse_part[row_base(bj, p) + hx] = (m_ref[hh] + log2f(l_tot)) * kLn2;
         }
       }
       barrier();  // E2
@@ -534,9 +524,8 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     wait_tile(0);
     barrier();  // T0
 
-    for (int p = p_first; p < p_live; ++p) {
-      int k0, k1;
-      range_tiles(p, k0, k1);
+    {
+      const int k0 = 0;
       for (int pass = 0; pass < 2; ++pass) {
         zero_acc();
         if (pass > 0) {  // the range again: its first tiles back into the buffers
@@ -575,13 +564,11 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
         barrier();  // AM
         barrier();  // AM
       }
-      if (k1 < K) wait_tile(k1);  // E2 certifies the next range's first tile
       barrier();  // E1
       barrier();  // E2: linv ready
-      // the range's last tile buffer is free until tile k1 + 3 is loaded
-      write_partial(row_base_of(p), smem + ((k1 - 1) & (kNBuf - 1)) * kTileBytes);
+      // the range's last tile buffer: no tile is loaded after it
+      write_partial(row_base(bj, p), smem + ((k1 - 1) & (kNBuf - 1)) * kTileBytes);
     }
-    for (int p = p_live; p < p_end; ++p) write_empty(bj, p);
   } else {
     // one range per workgroup
     const int t_begin = T0, t_end = T1, ntiles = K;
@@ -675,7 +662,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     }
     barrier();  // E1
     barrier();  // E2: linv ready
-    write_partial(row_base_of(p_first), smem);  // no tile is in flight in LDS
+    write_partial(row_base(bj, p), smem);  // no tile is in flight in LDS
   }
   };  // unit
 
@@ -789,7 +776,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
   // worker's pieces in row order (balanced); a barrier between two pieces
   // (the previous one's partial staging vs the next one's first loads)
   for (int it = 0;; ++it) {
-    int bj, pf, pe, T0, T1, ntf;
+    int bj, pf, T0, T1;
     if constexpr (!balanced) {
       if (it > 0) break;
       const int qj = r1 % P.QL;
@@ -797,21 +784,17 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
       const int b = r2 / P.S;
       bj = b * P.QL + qj;
       pf = r2 % P.S;
-      pe = pf + 1;
-      if (pe == P.S)  // the last range's workgroup marks the slots past the ranges
+      if (pf + 1 == P.S)  // the last range's workgroup marks the slots past the ranges
         for (int p = P.S; p < P.S_out; ++p) write_empty(bj, p, true);
       T0 = pf * P.chunk;
-      T1 = min(pe * P.chunk, attended(bj));
-      ntf = P.chunk / kTileTokens;
+      T1 = min((pf + 1) * P.chunk, attended(bj));
     } else {
       if (it >= npieces) break;
       const int e0 = __builtin_amdgcn_readfirstlane(plist[3 * it]);
       bj = e0 & 0xFFFF;
       pf = e0 >> 16;
-      pe = pf + 1;
       T0 = __builtin_amdgcn_readfirstlane(plist[3 * it + 1]);
       T1 = __builtin_amdgcn_readfirstlane(plist[3 * it + 2]);
-      ntf = (T1 - T0 + kTileTokens - 1) / kTileTokens;
     }
     if (it > 0) barrier();
     // balanced: the lane ids pass through an opaque copy per piece, so that
@@ -819,7 +802,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     // than held across all of them
     int lane_i = lane, tid_i = tid;
     if constexpr (balanced) asm volatile("" : "+v"(lane_i), "+v"(tid_i));
-    unit(bj, pf, pe, T0, T1, ntf, lane_i, tid_i);
+    unit(bj, pf, T0, T1, lane_i, tid_i);
   }
 }
 
