@@ -337,12 +337,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(AttnParams P) 
     const float m_new = fmaxf(m, mx);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // nothing attended yet
     const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    // the accumulators are rescaled only when some query's maximum moved: an
+    // unchanged maximum gives alpha = 1 (and a query with nothing attended yet
+    // has nothing accumulated), so skipping is exact
+    if (__any(m_new != m)) {
+      l *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+    }
     m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
