@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="paged_b64_ragged")
+    ap.add_argument("--events-every", type=int, default=4, metavar="N",
+                    help="per-launch HIP events around the launches of every N-th timed step "
+                         "(the event markers lengthen the steps they bracket by ~9 us; 1 = all)")
     ap.add_argument("--splits", type=int, default=0, help="0: the workload's own split count")
     ap.add_argument("--part-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--decode-kernel", default=None,
@@ -667,21 +670,30 @@ def main():
             call()
     torch.cuda.synchronize()
 
-    # the timed region: K steps between two synchronisations; an event on
-    # the launch stream before the first launch of each step and after each
-    # launch gives every kernel's per-launch duration
+    # the timed region: K steps between two synchronisations; in every N-th
+    # step an event on the launch stream before its first launch and after
+    # each launch gives each kernel's per-launch duration (a sample of K / N
+    # launches per kernel; the markers are left out of the other steps, which
+    # a serving loop would run without them)
+    every = max(1, args.events_every)
+    n_inst = (args.steps + every - 1) // every
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(args.steps)]
+          for _ in range(n_inst)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        for j, call in enumerate(prepared[i % R]):
-            call()
-            ev[i][j + 1].record(stream)
+        if i % every == 0:
+            e = ev[i // every]
+            e[0].record(stream)
+            for j, call in enumerate(prepared[i % R]):
+                call()
+                e[j + 1].record(stream)
+        else:
+            for call in prepared[i % R]:
+                call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    per_launch = {name: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(args.steps)]
+    per_launch = {name: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(n_inst)]
                   for j, (name, _) in enumerate(stages)}
     kernel_stats = {name: launch_stats(us) for name, us in per_launch.items()}
     kernel_us = {name: st["mean"] for name, st in kernel_stats.items()}
@@ -792,6 +804,8 @@ def main():
         "cache_pct_hbm_peak": 100.0 * cache_bytes / (t_decode + t_tail) / 1e9 / HBM_PEAK_GBPS,
         "cache_GBps_decode_only": achieved,
         "kernel_us": kernel_stats,
+        # per-launch durations: events around the launches of every N-th timed step
+        "launch_events": {"every_nth_step": every, "samples_per_kernel": n_inst},
         "outside_step_us_mean": outside_us,
         "mfma": mfma,
         "roofline": {"kernel": "mla_decode", "bound": "hbm", "achieved": achieved,
