@@ -86,7 +86,8 @@ struct RebuildParams {
   int64_t kv_stride;
 };
 
-__global__ __launch_bounds__(kPfThreads) void rebuild_kv_kernel(RebuildParams P) {
+__global__ __attribute__((amdgpu_flat_work_group_size(kPfThreads, kPfThreads), amdgpu_waves_per_eu(2, 2)))
+void rebuild_kv_kernel(RebuildParams P) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int L = min(max(P.seq_lens[b], 0), P.max_seq_len);
   const int from = P.rebuild_from ? max(P.rebuild_from[b], 0) : 0;
@@ -233,7 +234,8 @@ struct AttnParams {
 };
 
 template <int O_DT>
-__global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(AttnParams P) {
+__global__ __attribute__((amdgpu_flat_work_group_size(kPfThreads, kPfThreads), amdgpu_waves_per_eu(2, 2)))
+void prefill_attn_kernel(AttnParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kKBuf + kVBuf)];
   const int b = blockIdx.z, h = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;  // the longest query tiles first
