@@ -579,7 +579,7 @@ void decode_f8q_kernel(DecodeParams P, const int32_t* __restrict__ block_table) 
     constexpr int kColsRound = 256 / kEsz;
     constexpr int kStageRow = kColsRound * kEsz + 16;
     // the lane index recomputed here (volatile), so that the epilogue's
-    // addresses are formed in place rather than held across the range loop
+    // addresses are formed in place rather than held across the tile loop
     int eln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(eln));
     const int hl = eln & 31, g = eln >> 5;

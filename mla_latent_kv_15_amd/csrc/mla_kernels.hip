@@ -429,7 +429,7 @@ void decode_ws_kernel(DecodeParams P, const int32_t* __restrict__ block_table) {
     constexpr int kColsRound = 256 / kEsz;             // 128 bf16 / 64 fp32 columns
     constexpr int kStageRow = kColsRound * kEsz + 16;  // padded: rows start 4 banks apart
     // the lane index recomputed here (volatile), so that the epilogue's
-    // addresses are formed in place rather than held across the range loop
+    // addresses are formed in place rather than held across the tile loop
     int eln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(eln));
     const int hl = eln & 31, g = eln >> 5;
@@ -2319,8 +2319,7 @@ static mla_status_t decode_launch(const mla_dims_t* dims, int32_t B, int32_t q_l
       decode_ws_kernel<false, MLA_BF16, true><<<gridB, kWsThreads, 0, s>>>(P, cache->block_table);
     return launch_status();
   }
-  // automatic choice: the 64-head kernel, measured as fast or faster than the
-  // 128-head one on every bf16 workload and split count tried
+  // automatic choice: the 64-head kernel over the fixed split ranges
   if (kernel == MLA_KERNEL_AUTO) kernel = MLA_KERNEL_H64;
   // bf16 cache with many splits per sequence (S >= 32): R consecutive split
   // ranges per workgroup, enough workgroups to fill the 256 CUs once, merged
